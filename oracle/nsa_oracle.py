@@ -1,0 +1,518 @@
+"""Plain fp64 CPU oracle of Native Sparse Attention (NSA).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg may import or run this module; the GPU library
+never routes through it and shares no code with it.
+
+It writes out, step by step and in float64 numpy, what the NSA operator
+computes: the gate, token compression phi, compressed attention, the remap of
+its probabilities onto selection blocks, the GQA head reduction, top-n block
+selection, selected-block attention, sliding-window attention, the gated sum,
+the single-token decode step and the backward pass with the selected blocks
+held fixed.  Nothing is blocked, fused or reordered beyond the definitions, so
+each function can be checked against the pages by eye.
+
+Sources (web pages about the NSA paper "Native Sparse Attention:
+Hardware-Aligned and Natively Trainable Sparse Attention"):
+
+* [YLY] m.youleyou.com, "硬件对齐+原生训练！DeepSeek NSA打造高效稀疏Attention",
+  section 二 (NSA核心工作): 整体框架, 令牌压缩, 重要性分数计算, Top-n块选择,
+  滑动窗口, 最终输出计算; and 效率分析/解码速度.
+* [XK] xookee.cn, "NSA（Natively Sparse Attention）论文原理解析" and its
+  follow-on explainers: 压缩注意力机制解析 §2.1-2.4 (mean-pool / MLP
+  compression, softmax(QK^T/sqrt(d_k))V), 滑动窗口注意力 §2 (window key set,
+  gated sum), 三种注意力如何组合 §2 (gates g = sigmoid(MLP(X))).
+
+Where the pages leave a step open the reading taken is stated at the step
+("Reading:").  Pins: every function here is checked by tests against brute
+force, closed forms or library routines (tests/test_oracle_*.py), except the
+two conventions marked "parity unpinned" below: the exact architecture of the
+MLP compressor phi and the remap weights for l != l' (the pages strip both
+formulas; the readings are pinned only by their invariants).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+from scipy.special import erf
+
+__all__ = [
+    "Params", "gate", "compress", "remap_matrix", "attend", "n_cmp_visible",
+    "candidate_blocks", "forced_blocks", "top_n", "is_near_tie", "forward",
+    "decode", "backward", "round_io", "gelu", "gelu_grad", "sigmoid",
+    "cmp_keys", "slc_keys", "win_keys", "decode_token_count",
+]
+
+
+@dataclasses.dataclass(frozen=True)
+class Params:
+    """NSA hyper-parameters as the oracle reads them.
+
+    l: compression block length; d: compression stride; l_sel: selection block
+    length; n: number of selected blocks, the forced ones included; w: window;
+    phi: "mean" (mean-pool) or "mlp"; io: rounding applied to the stored
+    compressed keys/values ("bf16", "fp32" or None for exact fp64);
+    scale: softmax scale (None means 1/sqrt(d_k)).
+    """
+    l: int = 32
+    d: int = 16
+    l_sel: int = 64
+    n: int = 16
+    w: int = 512
+    phi: str = "mlp"
+    io: Optional[str] = "bf16"
+    scale: Optional[float] = None
+
+
+# ---------------------------------------------------------------------------
+# Elementary functions
+# ---------------------------------------------------------------------------
+
+def sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def gelu(a):
+    """Exact (erf) GELU: a * Phi(a)."""
+    return 0.5 * a * (1.0 + erf(a / math.sqrt(2.0)))
+
+
+def gelu_grad(a):
+    """d/da [a Phi(a)] = Phi(a) + a * phi(a)."""
+    return 0.5 * (1.0 + erf(a / math.sqrt(2.0))) + a * np.exp(-0.5 * a * a) / math.sqrt(2.0 * math.pi)
+
+
+def round_io(x, io: Optional[str]):
+    """Round float64 values once, to nearest-even, to the I/O dtype.
+
+    bf16 keeps 8 significant bits; fp32 keeps 24.  Reading: the compressed keys
+    and values are stored tensors (the decode cache holds them), so they are
+    rounded to the I/O dtype like every other stored tensor.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if io is None:
+        return x.copy()
+    if io == "fp32":
+        return x.astype(np.float32).astype(np.float64)
+    if io == "bf16":
+        m, e = np.frexp(x)                  # x = m * 2**e, 0.5 <= |m| < 1
+        return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+    raise ValueError(io)
+
+
+def _scale(p: Params, d_k: int) -> float:
+    return p.scale if p.scale is not None else 1.0 / math.sqrt(d_k)
+
+
+# ---------------------------------------------------------------------------
+# Gate  [YLY 整体框架: gate scores from the input features through an MLP and a
+# sigmoid; XK 三种注意力如何组合 §2: g = sigmoid(MLP(X))]
+# Reading: one gate per (token, query head, branch), a single linear layer
+# without bias: g[b,t,h,c] = sigmoid(x[b,t,:] . W_g[:,h,c]); c = (cmp, slc, win).
+# ---------------------------------------------------------------------------
+
+def gate(x, w_gate):
+    """x [B,T,C], w_gate [C,Hq,3] -> g [B,T,Hq,3]."""
+    z = np.einsum("btc,chk->bthk", x, w_gate)
+    return sigmoid(z)
+
+
+# ---------------------------------------------------------------------------
+# Token compression  [YLY 令牌压缩: blocks of length l slid with stride d, each
+# mapped by a learnable MLP with intra-block position encoding to one
+# compressed key; likewise values.  XK 压缩注意力 §2.2-2.3: mean pooling or MLP]
+# Reading: block i covers tokens [i*d, i*d + l); only complete blocks exist.
+# ---------------------------------------------------------------------------
+
+def n_cmp_visible(t: int, l: int, d: int) -> int:
+    """Number of complete compression blocks whose last token is <= t."""
+    s = t + 1
+    return 0 if s < l else (s - l) // d + 1
+
+
+def compress(kv, phi: Dict[str, np.ndarray], p: Params):
+    """kv [B,T,H,D] -> [B,N,H,D] with N = n_cmp_visible(T-1).
+
+    mean: (1/l) * sum_j kv[i*d + j].
+    mlp (parity unpinned as an architecture: the pages name only "MLP with
+    intra-block position encoding"): u = concat_j (kv[i*d+j] + pe[j]) (token j
+    major, feature minor), out = W2^T gelu(W1^T u + b1) + b2 with w1 [l*D, hidden],
+    w2 [hidden, D].  The same phi serves every KV head.
+    The result is rounded to the I/O dtype.
+    """
+    B, T, H, D = kv.shape
+    N = n_cmp_visible(T - 1, p.l, p.d)
+    out = np.zeros((B, N, H, D))
+    for i in range(N):
+        blk = kv[:, i * p.d: i * p.d + p.l]           # [B,l,H,D]
+        if p.phi == "mean":
+            out[:, i] = blk.mean(axis=1)
+        else:
+            u = (blk + phi["pe"][None, :, None, :])    # [B,l,H,D]
+            u = np.transpose(u, (0, 2, 1, 3)).reshape(B, H, p.l * D)
+            a = u @ phi["w1"] + phi["b1"]
+            out[:, i] = gelu(a) @ phi["w2"] + phi["b2"]
+    return round_io(out, p.io)
+
+
+# ---------------------------------------------------------------------------
+# Attention over one key set  [XK 压缩注意力 §2.4, 滑动窗口 §2: softmax(q K^T /
+# sqrt(d_k)) V].  An empty key set yields O = 0 and lse = -inf.
+# ---------------------------------------------------------------------------
+
+def attend(qh, K, V, scale: float):
+    """qh [H,dk], K [N,dk], V [N,dv] -> (O [H,dv], lse [H], P [H,N])."""
+    H = qh.shape[0]
+    if K.shape[0] == 0:
+        return np.zeros((H, V.shape[1])), np.full(H, -np.inf), np.zeros((H, 0))
+    z = scale * (qh @ K.T)
+    m = z.max(axis=1, keepdims=True)
+    e = np.exp(z - m)
+    s = e.sum(axis=1, keepdims=True)
+    P = e / s
+    return P @ V, (m + np.log(s))[:, 0], P
+
+
+# ---------------------------------------------------------------------------
+# Key sets of the three branches at query position t.
+# ---------------------------------------------------------------------------
+
+def cmp_keys(t: int, p: Params) -> np.ndarray:
+    """Compressed blocks visible at t: those complete at or before t."""
+    return np.arange(n_cmp_visible(t, p.l, p.d))
+
+
+def slc_keys(t: int, blocks: Sequence[int], p: Params) -> np.ndarray:
+    """Tokens of the selected blocks, concatenated, with a token-level causal mask.
+
+    [YLY Top-n块选择: the selected keys are the concatenation of the chosen
+    blocks' tokens].  Reading: tokens after t are masked.
+    """
+    toks = [np.arange(j * p.l_sel, min((j + 1) * p.l_sel, t + 1)) for j in sorted(blocks)]
+    return np.concatenate(toks) if toks else np.zeros(0, dtype=np.int64)
+
+
+def win_keys(t: int, p: Params) -> np.ndarray:
+    """[YLY 滑动窗口; XK 滑动窗口 §2: only the most recent w tokens].
+
+    Reading: w keys, positions [max(0, t-w+1), t].
+    """
+    return np.arange(max(0, t - p.w + 1), t + 1)
+
+
+# ---------------------------------------------------------------------------
+# Importance scores  [YLY 重要性分数计算]: the compressed branch's softmax
+# probabilities are reused.  When compression and selection blocking differ
+# (l <= l', d | l, d | l') they are remapped onto selection blocks.
+# Reading (remap weights parity unpinned: the formula is stripped from the
+# page): selection block j receives from compression block i the overlap of
+# their token ranges in units of d,
+#     W[i, j] = |[i*d, i*d+l) ∩ [j*l', (j+1)*l')| / d,
+# which is the double sum over m < l'/d and r < l/d of p_cmp[(l'/d) j + m - r],
+# and the identity when l = l' = d.
+# ---------------------------------------------------------------------------
+
+def remap_matrix(n_cmp: int, n_sel: int, p: Params) -> np.ndarray:
+    W = np.zeros((n_cmp, n_sel))
+    for i in range(n_cmp):
+        a0, a1 = i * p.d, i * p.d + p.l
+        for j in range(n_sel):
+            b0, b1 = j * p.l_sel, (j + 1) * p.l_sel
+            ov = max(0, min(a1, b1) - max(a0, b0))
+            W[i, j] = ov / p.d
+    return W
+
+
+# ---------------------------------------------------------------------------
+# Top-n block selection  [YLY Top-n块选择: keep the blocks ranked highest by
+# the group-shared importance score; the n selected blocks include 1 initial
+# block and 2 local blocks that are always active (实验设置)].
+# Readings: candidates are the causal blocks j <= floor(t/l'); the forced set is
+# {0, floor(t/l'), floor(t/l') - 1} among the candidates; the remaining slots
+# go to the best other candidates ranked by (-score, j), so the lower block
+# index wins a tie; when there are at most n candidates all are selected.
+# ---------------------------------------------------------------------------
+
+def candidate_blocks(t: int, p: Params) -> List[int]:
+    return list(range(t // p.l_sel + 1))
+
+
+def forced_blocks(t: int, p: Params) -> List[int]:
+    jc = t // p.l_sel
+    return sorted({j for j in (0, jc, jc - 1) if 0 <= j <= jc})
+
+
+def _ranked_rest(scores, t: int, p: Params) -> List[int]:
+    F = set(forced_blocks(t, p))
+    rest = [j for j in candidate_blocks(t, p) if j not in F]
+    return sorted(rest, key=lambda j: (-scores[j], j))
+
+
+def top_n(scores, t: int, p: Params) -> List[int]:
+    """Selected block set at position t (ascending) from one group's score row."""
+    J = candidate_blocks(t, p)
+    if len(J) <= p.n:
+        return J
+    F = forced_blocks(t, p)
+    r = p.n - len(F)
+    return sorted(F + _ranked_rest(scores, t, p)[:r])
+
+
+def is_near_tie(scores, t: int, p: Params, rel: float = 1e-3) -> bool:
+    """True when the last selected and first unselected ranked scores are within
+    ``rel`` of the larger one, so that rounding may legitimately swap them."""
+    J = candidate_blocks(t, p)
+    if len(J) <= p.n:
+        return False
+    r = p.n - len(forced_blocks(t, p))
+    rest = _ranked_rest(scores, t, p)
+    if r <= 0 or len(rest) <= r:
+        return False
+    a, b = scores[rest[r - 1]], scores[rest[r]]
+    return abs(a - b) <= rel * max(abs(a), abs(b))
+
+
+def decode_token_count(s: int, p: Params) -> int:
+    """Tokens one decode step loads per KV group in the pages' memory model
+    [YLY 效率分析/解码速度]: floor((s-l)/d) compressed + n*l' selected + w window."""
+    return (s - p.l) // p.d + p.n * p.l_sel + p.w
+
+
+# ---------------------------------------------------------------------------
+# One query position, all heads  [YLY 整体框架 and 最终输出计算:
+# o_t = sum over c in {cmp, slc, win} of g_t^c * Attn(q_t, K_t^c, V_t^c)]
+# ---------------------------------------------------------------------------
+
+def _row(p: Params, t: int, q_t, k, v, kc, vc, g_t, n_sel: int,
+         sel: Optional[List[List[int]]] = None, tie_scores=None):
+    """All NSA quantities at position t of one sequence.
+
+    q_t [Hq,dk]; k [*,Hkv,dk], v [*,Hkv,dv] raw keys/values (positions <= t used);
+    kc, vc compressed keys/values [*,Hkv,*]; g_t [Hq,3] gates.
+    sel: optional fixed block sets per KV head.  tie_scores: optional [Hkv,n_sel]
+    score rows used for selection instead of the oracle's own where the oracle's
+    own row is a near tie.
+    """
+    Hq, dk = q_t.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    dv = v.shape[2]
+    sc = _scale(p, dk)
+    ic = cmp_keys(t, p)
+    W = remap_matrix(len(ic), n_sel, p)
+    o_br = np.zeros((3, Hq, dv))
+    lse = np.zeros((3, Hq))
+    p_slc = np.zeros((Hkv, n_sel))
+    sets, retied = [], []
+    for g in range(Hkv):
+        hs = slice(g * G, (g + 1) * G)
+        # compressed branch; its probabilities are the importance scores
+        o_br[0, hs], lse[0, hs], P = attend(q_t[hs], kc[ic, g], vc[ic, g], sc)
+        # remap onto selection blocks, then sum over the group's query heads
+        p_slc[g] = (P @ W).sum(axis=0)
+        if sel is not None:
+            S = [j for j in sel[g] if j >= 0]
+            retied.append(False)
+        elif tie_scores is not None and is_near_tie(p_slc[g], t, p):
+            S = top_n(tie_scores[g], t, p)
+            retied.append(True)
+        else:
+            S = top_n(p_slc[g], t, p)
+            retied.append(False)
+        sets.append(S)
+        ks = slc_keys(t, S, p)
+        o_br[1, hs], lse[1, hs], _ = attend(q_t[hs], k[ks, g], v[ks, g], sc)
+        kw = win_keys(t, p)
+        o_br[2, hs], lse[2, hs], _ = attend(q_t[hs], k[kw, g], v[kw, g], sc)
+    o = (g_t[:, :, None] * np.transpose(o_br, (1, 0, 2))).sum(axis=1)
+    return o, o_br, lse, p_slc, sets, retied
+
+
+def _sets_to_idx(sets: List[List[int]], n: int) -> np.ndarray:
+    out = np.full((len(sets), n), -1, dtype=np.int64)
+    for g, S in enumerate(sets):
+        out[g, :len(S)] = sorted(S)
+    return out
+
+
+def forward(p: Params, q, k, v, x, w_gate, phi_k=None, phi_v=None, rows=None,
+            idx=None, tie_scores=None, kc=None, vc=None) -> Dict[str, np.ndarray]:
+    """NSA prefill forward.
+
+    q [B,T,Hq,dk], k [B,T,Hkv,dk], v [B,T,Hkv,dv], x [B,T,C], w_gate [C,Hq,3].
+    rows: query positions to evaluate (default all).  idx: optional fixed block
+    indices [B,T,Hkv,n] (-1 padded), used instead of top-n.  tie_scores: optional
+    [B,T,Hkv,N_sel] score rows consulted only where the oracle's own row is a near
+    tie.  kc, vc: optional precomputed compressed keys/values.
+
+    Returns o [B,R,Hq,dv], o_branch [3,B,R,Hq,dv], lse [3,B,R,Hq],
+    p_slc [B,R,Hkv,N_sel], idx [B,R,Hkv,n], retied [B,R,Hkv], gates [B,R,Hq,3],
+    k_cmp, v_cmp, rows.
+    """
+    B, T, Hq, dk = q.shape
+    Hkv, dv = k.shape[2], v.shape[3]
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    R = len(rows)
+    n_sel = -(-T // p.l_sel)
+    if kc is None:
+        kc = compress(k, phi_k, p)
+    if vc is None:
+        vc = compress(v, phi_v, p)
+    g_all = gate(x[:, rows], w_gate)
+    out = {
+        "o": np.zeros((B, R, Hq, dv)), "o_branch": np.zeros((3, B, R, Hq, dv)),
+        "lse": np.zeros((3, B, R, Hq)), "p_slc": np.zeros((B, R, Hkv, n_sel)),
+        "idx": np.full((B, R, Hkv, p.n), -1, dtype=np.int64),
+        "retied": np.zeros((B, R, Hkv), dtype=bool), "gates": g_all,
+        "k_cmp": kc, "v_cmp": vc, "rows": rows,
+    }
+    for b in range(B):
+        for r, t in enumerate(rows):
+            sel = None if idx is None else [list(idx[b, t, g]) for g in range(Hkv)]
+            ts = None if tie_scores is None else tie_scores[b, t]
+            o, o_br, lse, ps, sets, ret = _row(p, int(t), q[b, t], k[b], v[b], kc[b], vc[b],
+                                               g_all[b, r], n_sel, sel, ts)
+            out["o"][b, r] = o
+            out["o_branch"][:, b, r] = o_br
+            out["lse"][:, b, r] = lse
+            out["p_slc"][b, r] = ps
+            out["idx"][b, r] = _sets_to_idx(sets, p.n)
+            out["retied"][b, r] = ret
+    return out
+
+
+def decode(p: Params, q, k_cache, v_cache, kc_cache, vc_cache, x, w_gate,
+           tie_scores=None) -> Dict[str, np.ndarray]:
+    """One decode step: the query token sits at position S-1 of a length-S cache,
+    its own key/value already stored there; compressed blocks come from the
+    given compressed cache (complete blocks only), not from phi.
+
+    q [B,Hq,dk], k_cache [B,S,Hkv,dk], v_cache [B,S,Hkv,dv], kc_cache [B,>=N,Hkv,dk],
+    vc_cache [B,>=N,Hkv,dv], x [B,C].  Returns o [B,Hq,dv], o_branch [3,B,Hq,dv],
+    lse [3,B,Hq], p_slc [B,Hkv,N_sel], idx [B,Hkv,n], retied [B,Hkv].
+    """
+    B, S = k_cache.shape[:2]
+    Hq, dv = q.shape[1], v_cache.shape[3]
+    Hkv = k_cache.shape[2]
+    t = S - 1
+    n_sel = -(-S // p.l_sel)
+    g_all = gate(x[:, None], w_gate)[:, 0]
+    out = {"o": np.zeros((B, Hq, dv)), "o_branch": np.zeros((3, B, Hq, dv)),
+           "lse": np.zeros((3, B, Hq)), "p_slc": np.zeros((B, Hkv, n_sel)),
+           "idx": np.full((B, Hkv, p.n), -1, dtype=np.int64),
+           "retied": np.zeros((B, Hkv), dtype=bool), "gates": g_all}
+    for b in range(B):
+        ts = None if tie_scores is None else tie_scores[b]
+        o, o_br, lse, ps, sets, ret = _row(p, t, q[b], k_cache[b], v_cache[b], kc_cache[b],
+                                           vc_cache[b], g_all[b], n_sel, None, ts)
+        out["o"][b], out["o_branch"][:, b], out["lse"][:, b] = o, o_br, lse
+        out["p_slc"][b], out["idx"][b], out["retied"][b] = ps, _sets_to_idx(sets, p.n), ret
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Backward with the selected blocks held fixed (no gradient flows through the
+# scores or the discrete selection).  Per branch c, with dO_c = g_c * dO:
+#   dV += P^T dO_c;  dP = dO_c V^T;  D = rowsum(dO_c * O_c);  dS = P * (dP - D)
+#   dq += scale * dS K;  dK += scale * dS^T q
+# Gate: dg_c = <dO, O_c>, dW_g = sum_{b,t} x (x) (dg * g * (1 - g)).
+# Compressed-branch dK_cmp / dV_cmp flow back through phi to k / v and to the
+# phi parameters.  Rounding of the stored compressed tensors is not
+# differentiated (use io=None when comparing with finite differences).
+# ---------------------------------------------------------------------------
+
+def _attend_bwd(qh, K, V, P, O, dOc, scale):
+    dV = P.T @ dOc
+    dP = dOc @ V.T
+    D = (dOc * O).sum(axis=1, keepdims=True)
+    dS = P * (dP - D)
+    return scale * dS @ K, scale * dS.T @ qh, dV
+
+
+def _phi_bwd(kv, phi, dout, p: Params):
+    """Gradients of compress() w.r.t. its input and parameters (no rounding)."""
+    B, T, H, D = kv.shape
+    N = dout.shape[1]
+    dkv = np.zeros_like(kv)
+    grads = {}
+    if p.phi == "mean":
+        for i in range(N):
+            dkv[:, i * p.d: i * p.d + p.l] += dout[:, i][:, None] / p.l
+        return dkv, grads
+    for key in ("pe", "w1", "b1", "w2", "b2"):
+        grads[key] = np.zeros_like(phi[key])
+    for i in range(N):
+        blk = kv[:, i * p.d: i * p.d + p.l] + phi["pe"][None, :, None, :]
+        u = np.transpose(blk, (0, 2, 1, 3)).reshape(B * H, p.l * D)
+        a = u @ phi["w1"] + phi["b1"]
+        hh = gelu(a)
+        do = dout[:, i].reshape(B * H, D)
+        grads["b2"] += do.sum(axis=0)
+        grads["w2"] += hh.T @ do
+        da = (do @ phi["w2"].T) * gelu_grad(a)
+        grads["w1"] += u.T @ da
+        grads["b1"] += da.sum(axis=0)
+        du = (da @ phi["w1"].T).reshape(B, H, p.l, D)
+        du = np.transpose(du, (0, 2, 1, 3))           # [B,l,H,D]
+        dkv[:, i * p.d: i * p.d + p.l] += du
+        grads["pe"] += du.sum(axis=(0, 2))
+    return dkv, grads
+
+
+def backward(p: Params, q, k, v, x, w_gate, phi_k, phi_v, d_o, idx) -> Dict[str, object]:
+    """Gradients of L = sum(d_o * O) with block indices idx [B,T,Hkv,n] fixed.
+
+    Returns dq, dk, dv, dw_gate, dphi_k, dphi_v (dicts keyed like phi).
+    """
+    B, T, Hq, dk_ = q.shape
+    Hkv, dv_ = k.shape[2], v.shape[3]
+    G = Hq // Hkv
+    sc = _scale(p, dk_)
+    kc = compress(k, phi_k, p)
+    vc = compress(v, phi_v, p)
+    g_all = gate(x, w_gate)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dkc = np.zeros_like(kc)
+    dvc = np.zeros_like(vc)
+    dz = np.zeros_like(g_all)
+    for b in range(B):
+        for t in range(T):
+            for g in range(Hkv):
+                hs = slice(g * G, (g + 1) * G)
+                qh = q[b, t, hs]
+                dO = d_o[b, t, hs]
+                gg = g_all[b, t, hs]
+                branches = [
+                    ("cmp", cmp_keys(t, p)),
+                    ("slc", slc_keys(t, [j for j in idx[b, t, g] if j >= 0], p)),
+                    ("win", win_keys(t, p)),
+                ]
+                for c, (name, keys) in enumerate(branches):
+                    if len(keys) == 0:
+                        continue
+                    if name == "cmp":
+                        K, V = kc[b, keys, g], vc[b, keys, g]
+                    else:
+                        K, V = k[b, keys, g], v[b, keys, g]
+                    O, _, P = attend(qh, K, V, sc)
+                    dg = (dO * O).sum(axis=1)
+                    dz[b, t, hs, c] = dg * gg[:, c] * (1.0 - gg[:, c])
+                    dOc = gg[:, c:c + 1] * dO
+                    dqh, dK, dV = _attend_bwd(qh, K, V, P, O, dOc, sc)
+                    dq[b, t, hs] += dqh
+                    if name == "cmp":
+                        dkc[b, keys, g] += dK
+                        dvc[b, keys, g] += dV
+                    else:
+                        np.add.at(dk[b, :, g], keys, dK)
+                        np.add.at(dv[b, :, g], keys, dV)
+    dk_phi, dphi_k = _phi_bwd(k, phi_k, dkc, p)
+    dv_phi, dphi_v = _phi_bwd(v, phi_v, dvc, p)
+    dw_gate = np.einsum("btc,bthk->chk", x, dz)
+    return {"dq": dq, "dk": dk + dk_phi, "dv": dv + dv_phi, "dw_gate": dw_gate,
+            "dphi_k": dphi_k, "dphi_v": dphi_v, "dk_cmp": dkc, "dv_cmp": dvc}
