@@ -1,0 +1,178 @@
+/*
+ * nsa.h - C ABI of the MI355X (gfx950) Native Sparse Attention library.
+ *
+ * The operator (web pages on the NSA paper: youleyou "硬件对齐+原生训练！DeepSeek
+ * NSA打造高效稀疏Attention", section 二 整体框架 .. 最终输出计算) replaces the
+ * keys/values of each query t by three remapped sets and mixes the three
+ * attention outputs with sigmoid gates:
+ *     o_t = g_cmp * Attn(q_t, K_cmp, V_cmp) + g_slc * Attn(q_t, K_slc, V_slc)
+ *         + g_win * Attn(q_t, K_win, V_win)
+ *   cmp: keys/values compressed block-wise by phi over blocks of l tokens
+ *        taken every d tokens (令牌压缩), only blocks complete at t;
+ *   slc: the tokens (<= t) of the n selection blocks of l' tokens ranked
+ *        highest by the compressed branch's probabilities, remapped to
+ *        selection blocks and summed over the G query heads of a GQA group
+ *        (重要性分数计算, Top-n块选择); block 0 and the two blocks holding
+ *        t and the block before are always selected and count inside n;
+ *        the lower block index wins a tie;
+ *   win: the last w tokens [t-w+1, t] (滑动窗口).
+ * Scores use scale / sqrt(d_k) (xookee "NSA论文原理解析", 压缩注意力 §2.4).
+ *
+ * Conventions shared by every entry point
+ * - All tensor pointers are device pointers owned by the caller; the library
+ *   never allocates or frees device memory.  Extra device memory the kernels
+ *   need is the caller's workspace of nsa_workspace_size() bytes.
+ * - Tensors are dense, row-major, in the order their shapes are written.
+ *   Query head h belongs to KV head h / group_size.
+ * - io_dtype (NSA_BF16 or NSA_FP32) is the element type of every input and
+ *   of o / k_cmp / v_cmp / o_branch.  lse, p_slc, gates and all gradients are
+ *   fp32; idx is int32.  Arithmetic accumulates in fp32.
+ * - Calls enqueue work on `stream` (a hipStream_t; NULL = default stream)
+ *   and return without synchronising.  Results are valid when the stream
+ *   reaches that point.
+ * - Validation runs before anything is enqueued: on NSA_ERR_INVALID_ARG,
+ *   NSA_ERR_UNSUPPORTED or NSA_ERR_WORKSPACE nothing was launched and no
+ *   output was touched.  NSA_ERR_HIP reports a failed launch; outputs are
+ *   then undefined.  No C++ exception crosses this interface.
+ * - Every pointer must be 16-byte aligned.
+ * - The device is the caller's current HIP device; it must be gfx950.
+ * - No global mutable state: calls on different streams may run
+ *   concurrently as long as their buffers do not overlap.
+ */
+#ifndef NSA_H_
+#define NSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NSA_ABI_VERSION 1
+
+typedef enum nsa_status {
+  NSA_OK = 0,
+  NSA_ERR_INVALID_ARG = 1,  /* bad shape, hyper-parameter or NULL pointer */
+  NSA_ERR_UNSUPPORTED = 2,  /* valid but not built: device, dtype, head dims */
+  NSA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
+  NSA_ERR_HIP = 4,          /* a HIP runtime call failed */
+  NSA_ERR_INTERNAL = 5
+} nsa_status;
+
+typedef enum nsa_dtype { NSA_BF16 = 0, NSA_FP32 = 1 } nsa_dtype;
+typedef enum nsa_phi_kind { NSA_PHI_MEANPOOL = 0, NSA_PHI_MLP = 1 } nsa_phi_kind;
+typedef enum nsa_op { NSA_OP_FWD_PREFILL = 0, NSA_OP_FWD_DECODE = 1, NSA_OP_BWD = 2 } nsa_op;
+
+/* Shapes and hyper-parameters.
+ *   batch B; seqlen T (prefill/backward) or cache length S (decode);
+ *   n_kv_heads H_kv; group_size G (query heads per KV head, H_q = H_kv*G,
+ *   G in {1,2,4,8,16}); d_k, d_v head dims ((64,64), (128,128), (192,128));
+ *   cmp_block l, cmp_stride d (d | l), sel_block l' (d | l', l <= l',
+ *   l' | 32*d, 31*d + l <= 32*l'); n_select n (3 <= n <= 32);
+ *   window w >= 1; gate_dim C (gate input width); phi_hidden (MLP width,
+ *   multiple of 64); phi (nsa_phi_kind); io_dtype (nsa_dtype);
+ *   scale: 0 selects 1/sqrt(d_k). */
+typedef struct nsa_params {
+  int32_t batch, seqlen, n_kv_heads, group_size, d_k, d_v;
+  int32_t cmp_block, cmp_stride, sel_block, n_select, window;
+  int32_t gate_dim, phi_hidden;
+  int32_t phi;
+  int32_t io_dtype;
+  float scale;
+} nsa_params;
+
+/* Compression MLP phi for keys (D = d_k) or values (D = d_v), io_dtype:
+ *   pe [l, D], w1 [l*D, hidden], b1 [hidden], w2 [hidden, D], b2 [D];
+ *   block i (tokens i*d .. i*d+l-1): u = concat_j (x[i*d+j] + pe[j]),
+ *   phi = gelu_erf(u w1 + b1) w2 + b2.  Ignored for NSA_PHI_MEANPOOL
+ *   (phi = mean of the block's l tokens). */
+typedef struct nsa_phi_weights {
+  const void *pe, *w1, *b1, *w2, *b2;
+} nsa_phi_weights;
+
+/* Prefill / training forward.
+ * Inputs: q [B,T,Hq,dk], k [B,T,Hkv,dk], v [B,T,Hkv,dv], x [B,T,C],
+ *         w_gate [C,Hq,3] (gates g = sigmoid(x w_gate), branch order
+ *         cmp, slc, win), phi_k, phi_v.
+ * Output: o [B,T,Hq,dv] (required).
+ * Optional outputs (NULL = not written; the backward pass needs k_cmp,
+ * v_cmp, lse, idx and o_branch):
+ *   k_cmp [B,Ncmp,Hkv,dk], v_cmp [B,Ncmp,Hkv,dv] with Ncmp = (T-l)/d+1
+ *     (0 when T < l), rounded to io_dtype;
+ *   lse [3,B,T,Hq] fp32 log-sum-exp per branch (-inf for an empty set);
+ *   idx [B,T,Hkv,n] int32 selected blocks, ascending, -1 padded;
+ *   o_branch [3,B,T,Hq,dv] io_dtype per-branch outputs;
+ *   p_slc [B,T,Hkv,Nsel] fp32 group importance scores, Nsel = ceil(T/l');
+ *   gates [B,T,Hq,3] fp32. */
+typedef struct nsa_prefill_args {
+  const void *q, *k, *v, *x, *w_gate;
+  nsa_phi_weights phi_k, phi_v;
+  void *o;
+  void *k_cmp, *v_cmp, *lse, *idx, *o_branch, *p_slc, *gates;
+} nsa_prefill_args;
+
+/* One decode step per sequence; the new token's key/value are already stored
+ * at cache slot S-1 and its query sits at position S-1.
+ * Inputs: q [B,Hq,dk], k_cache [B,S,Hkv,dk], v_cache [B,S,Hkv,dv],
+ *   k_cmp_cache [B,Ncmp_cap,Hkv,dk], v_cmp_cache [B,Ncmp_cap,Hkv,dv] holding
+ *   at least the Ncmp(S) = (S-l)/d+1 complete compressed blocks in their
+ *   first rows (cmp_cache_cap = Ncmp_cap >= Ncmp(S)), x [B,C], w_gate.
+ * Output: o [B,Hq,dv] io_dtype.
+ * Optional: idx [B,Hkv,n] int32, p_slc [B,Hkv,Nsel] fp32,
+ *   lse [3,B,Hq] fp32, o_branch [3,B,Hq,dv] io_dtype. */
+typedef struct nsa_decode_args {
+  const void *q, *k_cache, *v_cache, *k_cmp_cache, *v_cmp_cache, *x, *w_gate;
+  int32_t cmp_cache_cap;
+  void *o;
+  void *idx, *p_slc, *lse, *o_branch;
+} nsa_decode_args;
+
+/* Backward with the selected blocks held fixed (no gradient through the
+ * scores or the selection).  Inputs as the prefill forward plus the forward's
+ * saved k_cmp, v_cmp, lse, idx, o_branch and the upstream gradient
+ * d_o [B,T,Hq,dv] (io_dtype).
+ * Outputs (fp32, overwritten): dq [B,T,Hq,dk], dk [B,T,Hkv,dk],
+ *   dv [B,T,Hkv,dv], dw_gate [C,Hq,3]; for NSA_PHI_MLP also d_phi_k and
+ *   d_phi_v laid out like the phi weights (pe, w1, b1, w2, b2) in fp32. */
+typedef struct nsa_phi_grads {
+  void *pe, *w1, *b1, *w2, *b2;
+} nsa_phi_grads;
+
+typedef struct nsa_bwd_args {
+  const void *q, *k, *v, *x, *w_gate;
+  nsa_phi_weights phi_k, phi_v;
+  const void *k_cmp, *v_cmp, *lse, *idx, *o_branch, *d_o;
+  void *dq, *dk, *dv, *dw_gate;
+  nsa_phi_grads d_phi_k, d_phi_v;
+} nsa_bwd_args;
+
+/* Version of this header the library was built from (NSA_ABI_VERSION). */
+int nsa_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char* nsa_status_str(nsa_status s);
+
+/* Workspace bytes entry point `op` needs for `p` (a pure function of p). */
+nsa_status nsa_workspace_size(const nsa_params* p, nsa_op op, size_t* bytes);
+
+/* Compress a key or value sequence with phi, as the forward does internally:
+ *   x [B,T,Hkv,D] -> out [B,Ncmp,Hkv,D] (io_dtype, Ncmp = (T-l)/d+1).
+ * D must equal p->d_k (is_value = 0) or p->d_v (is_value = 1).  Used to
+ * build or extend the compressed decode cache.  Workspace as for
+ * NSA_OP_FWD_PREFILL. */
+nsa_status nsa_compress(const nsa_params* p, int is_value, const void* x,
+                        const nsa_phi_weights* phi, void* out, void* ws,
+                        size_t ws_bytes, void* stream);
+
+nsa_status nsa_fwd_prefill(const nsa_params* p, const nsa_prefill_args* a, void* ws,
+                           size_t ws_bytes, void* stream);
+nsa_status nsa_fwd_decode(const nsa_params* p, const nsa_decode_args* a, void* ws,
+                          size_t ws_bytes, void* stream);
+nsa_status nsa_bwd(const nsa_params* p, const nsa_bwd_args* a, void* ws,
+                   size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NSA_H_ */

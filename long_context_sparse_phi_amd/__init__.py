@@ -1,0 +1,270 @@
+"""MI355X (gfx950) Native Sparse Attention: Python binding of libnsa.so.
+
+The functions here take torch tensors that already live on the GPU, check
+their dtypes and shapes, and pass raw pointers and the current HIP stream to
+the C ABI (include/nsa.h).  torch provides device memory and streams only;
+every step of the operator runs in the library's HIP kernels.  Output tensors
+are allocated with torch when the caller does not pass them.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+from typing import Dict, Optional
+
+import torch
+
+from . import _lib
+from ._lib import (NSA_BF16, NSA_FP32, NSA_OP_BWD, NSA_OP_FWD_DECODE, NSA_OP_FWD_PREFILL,
+                   NSA_PHI_MEANPOOL, NSA_PHI_MLP, NSAError)
+
+__all__ = ["Config", "workspace_size", "nsa_compress", "nsa_fwd_prefill", "nsa_fwd_decode",
+           "nsa_bwd", "load_library", "NSAError"]
+
+load_library = _lib.load
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    """Shapes and hyper-parameters (mirrors nsa_params)."""
+    B: int
+    T: int
+    H_kv: int
+    G: int
+    d_k: int
+    d_v: int
+    l: int = 32
+    d: int = 16
+    l_sel: int = 64
+    n: int = 16
+    w: int = 512
+    gate_dim: int = 256
+    hidden: int = 256
+    phi: str = "mlp"          # "mlp" | "mean"
+    dtype: str = "bf16"       # "bf16" | "fp32"
+    scale: float = 0.0        # 0 => 1/sqrt(d_k)
+
+    @property
+    def H_q(self) -> int:
+        return self.H_kv * self.G
+
+    @property
+    def n_cmp(self) -> int:
+        return 0 if self.T < self.l else (self.T - self.l) // self.d + 1
+
+    @property
+    def n_sel(self) -> int:
+        return -(-self.T // self.l_sel)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def params(self) -> _lib.nsa_params:
+        return _lib.nsa_params(
+            batch=self.B, seqlen=self.T, n_kv_heads=self.H_kv, group_size=self.G,
+            d_k=self.d_k, d_v=self.d_v, cmp_block=self.l, cmp_stride=self.d,
+            sel_block=self.l_sel, n_select=self.n, window=self.w, gate_dim=self.gate_dim,
+            phi_hidden=self.hidden if self.phi == "mlp" else 0,
+            phi=NSA_PHI_MLP if self.phi == "mlp" else NSA_PHI_MEANPOOL,
+            io_dtype=NSA_BF16 if self.dtype == "bf16" else NSA_FP32, scale=self.scale)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check(t: torch.Tensor, name: str, shape, dtype: torch.dtype, dev: torch.device):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda or t.device != dev:
+        raise ValueError(f"{name} must live on {dev}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def workspace_size(cfg: Config, op: int) -> int:
+    n = ctypes.c_size_t(0)
+    p = cfg.params()
+    st = _lib.load().nsa_workspace_size(ctypes.byref(p), op, ctypes.byref(n))
+    if st != 0:
+        raise NSAError("nsa_workspace_size", st)
+    return int(n.value)
+
+
+def _workspace(cfg: Config, op: int, dev, ws: Optional[torch.Tensor]) -> torch.Tensor:
+    need = workspace_size(cfg, op)
+    if ws is None:
+        return torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace of {need} bytes needed")
+    return ws
+
+
+def _phi_struct(cfg: Config, phi: Optional[Dict[str, torch.Tensor]], D: int, dev) -> _lib.nsa_phi_weights:
+    w = _lib.nsa_phi_weights()
+    if cfg.phi != "mlp":
+        return w
+    shapes = {"pe": (cfg.l, D), "w1": (cfg.l * D, cfg.hidden), "b1": (cfg.hidden,),
+              "w2": (cfg.hidden, D), "b2": (D,)}
+    for k, shp in shapes.items():
+        _check(phi[k], f"phi.{k}", shp, cfg.torch_dtype, dev)
+        setattr(w, k, phi[k].data_ptr())
+    return w
+
+
+def nsa_compress(cfg: Config, x: torch.Tensor, phi: Optional[Dict[str, torch.Tensor]], is_value: bool,
+                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Compressed keys (is_value=False) or values of x [B,T,Hkv,D] -> [B,Ncmp,Hkv,D]."""
+    dev = x.device
+    D = cfg.d_v if is_value else cfg.d_k
+    _check(x, "x", (cfg.B, cfg.T, cfg.H_kv, D), cfg.torch_dtype, dev)
+    if out is None:
+        out = torch.empty(cfg.B, cfg.n_cmp, cfg.H_kv, D, dtype=cfg.torch_dtype, device=dev)
+    _check(out, "out", (cfg.B, cfg.n_cmp, cfg.H_kv, D), cfg.torch_dtype, dev)
+    ws = _workspace(cfg, NSA_OP_FWD_PREFILL, dev, workspace)
+    p = cfg.params()
+    w = _phi_struct(cfg, phi, D, dev)
+    st = _lib.load().nsa_compress(ctypes.byref(p), int(is_value), x.data_ptr(), ctypes.byref(w),
+                                  out.data_ptr() if out.numel() else x.data_ptr(), ws.data_ptr(),
+                                  ws.numel(), _stream(dev))
+    if st != 0:
+        raise NSAError("nsa_compress", st)
+    return out
+
+
+def nsa_fwd_prefill(cfg: Config, q, k, v, x, w_gate, phi_k=None, phi_v=None, *, out=None,
+                    save_for_backward: bool = False, debug: bool = False,
+                    workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """NSA prefill forward.  Returns {"o": ...} plus, when save_for_backward,
+    k_cmp, v_cmp, lse, idx, o_branch, and, when debug, also p_slc and gates."""
+    dev = q.device
+    dt = cfg.torch_dtype
+    B, T, Hq, Hkv = cfg.B, cfg.T, cfg.H_q, cfg.H_kv
+    _check(q, "q", (B, T, Hq, cfg.d_k), dt, dev)
+    _check(k, "k", (B, T, Hkv, cfg.d_k), dt, dev)
+    _check(v, "v", (B, T, Hkv, cfg.d_v), dt, dev)
+    _check(x, "x", (B, T, cfg.gate_dim), dt, dev)
+    _check(w_gate, "w_gate", (cfg.gate_dim, Hq, 3), dt, dev)
+    res = {"o": out if out is not None else torch.empty(B, T, Hq, cfg.d_v, dtype=dt, device=dev)}
+    _check(res["o"], "o", (B, T, Hq, cfg.d_v), dt, dev)
+    if save_for_backward or debug:
+        res["k_cmp"] = torch.empty(B, cfg.n_cmp, Hkv, cfg.d_k, dtype=dt, device=dev)
+        res["v_cmp"] = torch.empty(B, cfg.n_cmp, Hkv, cfg.d_v, dtype=dt, device=dev)
+        res["lse"] = torch.empty(3, B, T, Hq, dtype=torch.float32, device=dev)
+        res["idx"] = torch.empty(B, T, Hkv, cfg.n, dtype=torch.int32, device=dev)
+        res["o_branch"] = torch.empty(3, B, T, Hq, cfg.d_v, dtype=dt, device=dev)
+    if debug:
+        res["p_slc"] = torch.empty(B, T, Hkv, cfg.n_sel, dtype=torch.float32, device=dev)
+        res["gates"] = torch.empty(B, T, Hq, 3, dtype=torch.float32, device=dev)
+    a = _lib.nsa_prefill_args()
+    for name, t in (("q", q), ("k", k), ("v", v), ("x", x), ("w_gate", w_gate)):
+        setattr(a, name, t.data_ptr())
+    a.phi_k = _phi_struct(cfg, phi_k, cfg.d_k, dev)
+    a.phi_v = _phi_struct(cfg, phi_v, cfg.d_v, dev)
+    for name in ("o", "k_cmp", "v_cmp", "lse", "idx", "o_branch", "p_slc", "gates"):
+        t = res.get(name)
+        setattr(a, name, t.data_ptr() if (t is not None and t.numel()) else None)
+    ws = _workspace(cfg, NSA_OP_FWD_PREFILL, dev, workspace)
+    p = cfg.params()
+    st = _lib.load().nsa_fwd_prefill(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(), _stream(dev))
+    if st != 0:
+        raise NSAError("nsa_fwd_prefill", st)
+    res["_workspace"] = ws
+    return res
+
+
+def nsa_fwd_decode(cfg: Config, q, k_cache, v_cache, k_cmp_cache, v_cmp_cache, x, w_gate, *,
+                   out=None, debug: bool = False, workspace: Optional[torch.Tensor] = None):
+    """One decode step; cfg.T is the cache length S (query at position S-1)."""
+    dev = q.device
+    dt = cfg.torch_dtype
+    B, S, Hq, Hkv = cfg.B, cfg.T, cfg.H_q, cfg.H_kv
+    _check(q, "q", (B, Hq, cfg.d_k), dt, dev)
+    _check(k_cache, "k_cache", (B, S, Hkv, cfg.d_k), dt, dev)
+    _check(v_cache, "v_cache", (B, S, Hkv, cfg.d_v), dt, dev)
+    cap = k_cmp_cache.shape[1]
+    _check(k_cmp_cache, "k_cmp_cache", (B, cap, Hkv, cfg.d_k), dt, dev)
+    _check(v_cmp_cache, "v_cmp_cache", (B, cap, Hkv, cfg.d_v), dt, dev)
+    _check(x, "x", (B, cfg.gate_dim), dt, dev)
+    _check(w_gate, "w_gate", (cfg.gate_dim, Hq, 3), dt, dev)
+    res = {"o": out if out is not None else torch.empty(B, Hq, cfg.d_v, dtype=dt, device=dev)}
+    if debug:
+        res["idx"] = torch.empty(B, Hkv, cfg.n, dtype=torch.int32, device=dev)
+        res["p_slc"] = torch.empty(B, Hkv, cfg.n_sel, dtype=torch.float32, device=dev)
+        res["lse"] = torch.empty(3, B, Hq, dtype=torch.float32, device=dev)
+        res["o_branch"] = torch.empty(3, B, Hq, cfg.d_v, dtype=dt, device=dev)
+    a = _lib.nsa_decode_args()
+    for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("x", x), ("w_gate", w_gate)):
+        setattr(a, name, t.data_ptr())
+    a.k_cmp_cache = k_cmp_cache.data_ptr() if k_cmp_cache.numel() else None
+    a.v_cmp_cache = v_cmp_cache.data_ptr() if v_cmp_cache.numel() else None
+    a.cmp_cache_cap = cap
+    for name in ("o", "idx", "p_slc", "lse", "o_branch"):
+        t = res.get(name)
+        setattr(a, name, t.data_ptr() if t is not None else None)
+    ws = _workspace(cfg, NSA_OP_FWD_DECODE, dev, workspace)
+    p = cfg.params()
+    st = _lib.load().nsa_fwd_decode(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(), _stream(dev))
+    if st != 0:
+        raise NSAError("nsa_fwd_decode", st)
+    res["_workspace"] = ws
+    return res
+
+
+def nsa_bwd(cfg: Config, q, k, v, x, w_gate, phi_k, phi_v, saved: Dict[str, torch.Tensor], d_o, *,
+            workspace: Optional[torch.Tensor] = None) -> Dict[str, object]:
+    """Backward with the forward's selected blocks fixed.  `saved` is the dict
+    nsa_fwd_prefill returned with save_for_backward=True.  Gradients are fp32."""
+    dev = q.device
+    dt = cfg.torch_dtype
+    B, T, Hq, Hkv = cfg.B, cfg.T, cfg.H_q, cfg.H_kv
+    _check(d_o, "d_o", (B, T, Hq, cfg.d_v), dt, dev)
+    f32 = torch.float32
+    res = {"dq": torch.empty(B, T, Hq, cfg.d_k, dtype=f32, device=dev),
+           "dk": torch.empty(B, T, Hkv, cfg.d_k, dtype=f32, device=dev),
+           "dv": torch.empty(B, T, Hkv, cfg.d_v, dtype=f32, device=dev),
+           "dw_gate": torch.empty(cfg.gate_dim, Hq, 3, dtype=f32, device=dev)}
+    a = _lib.nsa_bwd_args()
+    for name, t in (("q", q), ("k", k), ("v", v), ("x", x), ("w_gate", w_gate), ("d_o", d_o)):
+        setattr(a, name, t.data_ptr())
+    for name in ("k_cmp", "v_cmp", "lse", "idx", "o_branch"):
+        t = saved[name]
+        setattr(a, name, t.data_ptr() if t.numel() else None)
+    a.phi_k = _phi_struct(cfg, phi_k, cfg.d_k, dev)
+    a.phi_v = _phi_struct(cfg, phi_v, cfg.d_v, dev)
+    for name in ("dq", "dk", "dv", "dw_gate"):
+        setattr(a, name, res[name].data_ptr())
+    if cfg.phi == "mlp":
+        for tag, D in (("d_phi_k", cfg.d_k), ("d_phi_v", cfg.d_v)):
+            g = {"pe": torch.empty(cfg.l, D, dtype=f32, device=dev),
+                 "w1": torch.empty(cfg.l * D, cfg.hidden, dtype=f32, device=dev),
+                 "b1": torch.empty(cfg.hidden, dtype=f32, device=dev),
+                 "w2": torch.empty(cfg.hidden, D, dtype=f32, device=dev),
+                 "b2": torch.empty(D, dtype=f32, device=dev)}
+            gs = _lib.nsa_phi_grads(**{kk: vv.data_ptr() for kk, vv in g.items()})
+            setattr(a, tag, gs)
+            res[tag] = g
+    ws = _workspace(cfg, NSA_OP_BWD, dev, workspace)
+    p = cfg.params()
+    st = _lib.load().nsa_bwd(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(), _stream(dev))
+    if st != 0:
+        raise NSAError("nsa_bwd", st)
+    res["_workspace"] = ws
+    return res
+
+
+def config_from_workload(w, **over) -> Config:
+    """Config for a workload description of the shared input generator."""
+    c = Config(B=w.B, T=w.T, H_kv=w.H_kv, G=w.G, d_k=w.d_k, d_v=w.d_v, l=w.l, d=w.d, l_sel=w.l_sel,
+               n=w.n, w=w.w, gate_dim=w.gate_dim, hidden=w.hidden, phi=w.phi, dtype=w.dtype)
+    return dataclasses.replace(c, **over) if over else c

@@ -1,0 +1,101 @@
+"""ctypes mirror of include/nsa.h and loader of the in-tree libnsa.so.
+
+Argument marshalling only: every computation happens in the HIP library.
+The library is never built or replaced here; a missing library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnsa.so")
+
+NSA_OK, NSA_ERR_INVALID_ARG, NSA_ERR_UNSUPPORTED, NSA_ERR_WORKSPACE, NSA_ERR_HIP, NSA_ERR_INTERNAL = range(6)
+NSA_BF16, NSA_FP32 = 0, 1
+NSA_PHI_MEANPOOL, NSA_PHI_MLP = 0, 1
+NSA_OP_FWD_PREFILL, NSA_OP_FWD_DECODE, NSA_OP_BWD = 0, 1, 2
+ABI_VERSION = 1
+
+_vp = ctypes.c_void_p
+
+
+class nsa_params(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "seqlen", "n_kv_heads", "group_size", "d_k", "d_v",
+        "cmp_block", "cmp_stride", "sel_block", "n_select", "window",
+        "gate_dim", "phi_hidden", "phi", "io_dtype")] + [("scale", ctypes.c_float)]
+
+
+class nsa_phi_weights(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("pe", "w1", "b1", "w2", "b2")]
+
+
+class nsa_phi_grads(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("pe", "w1", "b1", "w2", "b2")]
+
+
+class nsa_prefill_args(ctypes.Structure):
+    _fields_ = ([(n, _vp) for n in ("q", "k", "v", "x", "w_gate")] +
+                [("phi_k", nsa_phi_weights), ("phi_v", nsa_phi_weights)] +
+                [(n, _vp) for n in ("o", "k_cmp", "v_cmp", "lse", "idx", "o_branch", "p_slc", "gates")])
+
+
+class nsa_decode_args(ctypes.Structure):
+    _fields_ = ([(n, _vp) for n in ("q", "k_cache", "v_cache", "k_cmp_cache", "v_cmp_cache", "x", "w_gate")] +
+                [("cmp_cache_cap", ctypes.c_int32)] +
+                [(n, _vp) for n in ("o", "idx", "p_slc", "lse", "o_branch")])
+
+
+class nsa_bwd_args(ctypes.Structure):
+    _fields_ = ([(n, _vp) for n in ("q", "k", "v", "x", "w_gate")] +
+                [("phi_k", nsa_phi_weights), ("phi_v", nsa_phi_weights)] +
+                [(n, _vp) for n in ("k_cmp", "v_cmp", "lse", "idx", "o_branch", "d_o",
+                                    "dq", "dk", "dv", "dw_gate")] +
+                [("d_phi_k", nsa_phi_grads), ("d_phi_v", nsa_phi_grads)])
+
+
+EXPORTS = ("nsa_abi_version", "nsa_status_str", "nsa_workspace_size", "nsa_compress",
+           "nsa_fwd_prefill", "nsa_fwd_decode", "nsa_bwd")
+
+_LIB = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libnsa.so (once) and declare the signatures of its exports."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise RuntimeError(f"NSA HIP library not built: {path} is missing "
+                           "(run python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    lib.nsa_abi_version.restype = ctypes.c_int
+    lib.nsa_abi_version.argtypes = []
+    lib.nsa_status_str.restype = ctypes.c_char_p
+    lib.nsa_status_str.argtypes = [ctypes.c_int]
+    lib.nsa_workspace_size.restype = ctypes.c_int
+    lib.nsa_workspace_size.argtypes = [P(nsa_params), ctypes.c_int, P(ctypes.c_size_t)]
+    lib.nsa_compress.restype = ctypes.c_int
+    lib.nsa_compress.argtypes = [P(nsa_params), ctypes.c_int, _vp, P(nsa_phi_weights), _vp, _vp,
+                                 ctypes.c_size_t, _vp]
+    for name, argt in (("nsa_fwd_prefill", nsa_prefill_args), ("nsa_fwd_decode", nsa_decode_args),
+                       ("nsa_bwd", nsa_bwd_args)):
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int
+        fn.argtypes = [P(nsa_params), P(argt), _vp, ctypes.c_size_t, _vp]
+    if lib.nsa_abi_version() != ABI_VERSION:
+        raise RuntimeError("libnsa.so ABI version mismatch")
+    _LIB = lib
+    return lib
+
+
+def status_str(code: int) -> str:
+    return load().nsa_status_str(code).decode()
+
+
+class NSAError(RuntimeError):
+    def __init__(self, where: str, code: int):
+        super().__init__(f"{where}: {status_str(code)} (status {code})")
+        self.code = code

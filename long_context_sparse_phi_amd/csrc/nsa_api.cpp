@@ -1,0 +1,318 @@
+// C ABI of the NSA library: argument validation, workspace layout and the
+// launch sequence of each entry point.  Nothing is enqueued until every check
+// has passed.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstring>
+
+#include "../../include/nsa.h"
+#include "nsa_kernels.hpp"
+
+namespace nsa {
+bool cmp_out_fits(const Dims& dm);
+hipError_t launch_decode(const Dims& dm, const nsa_decode_args* a, void* ws, hipStream_t s);
+size_t decode_ws_bytes(const Dims& dm);
+hipError_t launch_bwd(const Dims& dm, const nsa_bwd_args* a, void* ws, hipStream_t s);
+size_t bwd_ws_bytes(const Dims& dm);
+}  // namespace nsa
+
+using namespace nsa;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t al(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+// Bump allocator over the caller's workspace.
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* b) : base((char*)b) {}
+  void* take(size_t bytes) {
+    void* p = base ? base + off : nullptr;
+    off += al(bytes);
+    return p;
+  }
+};
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Device check: gfx950 only.  Cached per device id; the cache holds no state
+// that changes results.
+nsa_status check_device() {
+  static std::atomic<int> ok[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return NSA_ERR_HIP;
+  if (dev < 0 || dev >= 64) return NSA_ERR_UNSUPPORTED;
+  int v = ok[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return NSA_ERR_HIP;
+    v = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    ok[dev].store(v, std::memory_order_relaxed);
+  }
+  return v == 1 ? NSA_OK : NSA_ERR_UNSUPPORTED;
+}
+
+// Validates p and fills the derived sizes.  T_override: sequence length to
+// use (the cache length for decode).
+nsa_status make_dims(const nsa_params* p, Dims* dm) {
+  if (!p || !dm) return NSA_ERR_INVALID_ARG;
+  if (p->batch < 1 || p->seqlen < 1 || p->n_kv_heads < 1 || p->group_size < 1) return NSA_ERR_INVALID_ARG;
+  const int G = p->group_size;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return NSA_ERR_UNSUPPORTED;
+  if (p->d_k < 1 || p->d_v < 1) return NSA_ERR_INVALID_ARG;
+  if (!shapes_supported(p->d_k, p->d_v)) return NSA_ERR_UNSUPPORTED;
+  const int l = p->cmp_block, d = p->cmp_stride, ls = p->sel_block;
+  if (l < 1 || d < 1 || ls < 1 || l % d != 0 || ls % d != 0 || l > ls) return NSA_ERR_INVALID_ARG;
+  if (ls % 8 != 0 || (32 * d) % ls != 0) return NSA_ERR_UNSUPPORTED;
+  if ((31 * d + l - 1) / ls + 1 > 32) return NSA_ERR_UNSUPPORTED;
+  if (p->n_select < 3 || p->n_select > 32) return NSA_ERR_INVALID_ARG;
+  if (p->window < 1) return NSA_ERR_INVALID_ARG;
+  if (p->gate_dim < 1) return NSA_ERR_INVALID_ARG;
+  if (p->gate_dim > 1024) return NSA_ERR_UNSUPPORTED;
+  if (p->phi != NSA_PHI_MEANPOOL && p->phi != NSA_PHI_MLP) return NSA_ERR_INVALID_ARG;
+  if (p->phi == NSA_PHI_MLP && (p->phi_hidden < 64 || p->phi_hidden % 64 != 0)) return NSA_ERR_INVALID_ARG;
+  if (p->io_dtype != NSA_BF16 && p->io_dtype != NSA_FP32) return NSA_ERR_UNSUPPORTED;
+  if (!(p->scale >= 0.f) || std::isinf(p->scale)) return NSA_ERR_INVALID_ARG;
+  const long long tokens = (long long)p->batch * p->seqlen * p->n_kv_heads * G;
+  if (tokens * (p->d_k > p->d_v ? p->d_k : p->d_v) >= (1ll << 40)) return NSA_ERR_UNSUPPORTED;
+  Dims& D = *dm;
+  D.B = p->batch; D.T = p->seqlen; D.Hkv = p->n_kv_heads; D.G = G; D.Hq = p->n_kv_heads * G;
+  D.dk = p->d_k; D.dv = p->d_v; D.l = l; D.d = d; D.ls = ls; D.n = p->n_select; D.w = p->window;
+  D.ncmp = D.T < l ? 0 : (D.T - l) / d + 1;
+  D.ncmp_pad = ((D.ncmp + 63) & ~63) + 64;
+  D.nsel = (D.T + ls - 1) / ls;
+  D.Tp = ((D.T + 63) & ~63) + 64;
+  D.C = p->gate_dim;
+  D.hidden = p->phi == NSA_PHI_MLP ? p->phi_hidden : 0;
+  D.scale = p->scale > 0.f ? p->scale : 1.f / std::sqrt((float)p->d_k);
+  D.io = p->io_dtype == NSA_BF16 ? IO_BF16 : IO_F32;
+  if (!cmp_out_fits(D)) return NSA_ERR_UNSUPPORTED;
+  return NSA_OK;
+}
+
+size_t esize(const Dims& dm) { return dm.io == IO_BF16 ? 2 : 4; }
+
+// Workspace plan of the prefill forward.  Every optional output the caller
+// leaves NULL is placed in the workspace; sizes assume all are NULL.
+struct PrefillWs {
+  void *gates, *kc, *vc, *vct, *vt, *lse, *idx, *ob, *phi;
+};
+
+size_t phi_ws(const Dims& dm) {
+  if (dm.hidden == 0) return 0;
+  size_t a = phi_mlp_ws_bytes(dm, dm.dk), b = phi_mlp_ws_bytes(dm, dm.dv);
+  return a > b ? a : b;
+}
+
+size_t plan_prefill(const Dims& dm, void* ws, PrefillWs* w) {
+  Carve c(ws);
+  const size_t BTH = (size_t)dm.B * dm.T * dm.Hq;
+  const size_t es = esize(dm);
+  w->gates = c.take(BTH * 3 * 4);
+  w->kc = c.take((size_t)dm.B * dm.ncmp * dm.Hkv * dm.dk * es);
+  w->vc = c.take((size_t)dm.B * dm.ncmp * dm.Hkv * dm.dv * es);
+  w->vct = c.take((size_t)dm.B * dm.Hkv * dm.dv * dm.ncmp_pad * es);
+  w->vt = c.take((size_t)dm.B * dm.Hkv * dm.dv * dm.Tp * es);
+  w->lse = c.take(3 * BTH * 4);
+  w->idx = c.take((size_t)dm.B * dm.T * dm.Hkv * dm.n * 4);
+  w->ob = c.take(2 * BTH * dm.dv * es);
+  w->phi = c.take(phi_ws(dm));
+  return c.off;
+}
+
+nsa_status hip_status(hipError_t e) { return e == hipSuccess ? NSA_OK : NSA_ERR_HIP; }
+
+// Compress one tensor (keys: D = dk, values: D = dv) into out (and outT).
+hipError_t run_compress(const Dims& dm, int D, const void* x, const nsa_phi_weights* phi, void* out,
+                        void* outT, void* phi_ws_ptr, hipStream_t s) {
+  if (dm.hidden == 0) return launch_meanpool(dm, D, x, out, outT, s);
+  PhiMlpArgs a;
+  a.D = D; a.x = x; a.pe = phi->pe; a.w1 = phi->w1; a.b1 = phi->b1; a.w2 = phi->w2; a.b2 = phi->b2;
+  Carve c(phi_ws_ptr);
+  const size_t es = esize(dm);
+  const int R = dm.l / dm.d;
+  const int nsub = dm.ncmp > 0 ? dm.ncmp + R - 1 : 0;
+  a.w1t = c.take((size_t)dm.hidden * dm.l * D * es);
+  a.w2t = c.take((size_t)D * dm.hidden * es);
+  a.cvec = (float*)c.take((size_t)dm.hidden * 4);
+  a.y = (float*)c.take(((size_t)dm.B * dm.Hkv * nsub + R) * R * dm.hidden * 4);
+  a.h = c.take((size_t)dm.B * dm.Hkv * dm.ncmp * dm.hidden * 4);
+  a.out = out; a.outT = outT;
+  return launch_phi_mlp(dm, a, s);
+}
+
+bool phi_ok(const nsa_phi_weights& w) {
+  const void* ps[5] = {w.pe, w.w1, w.b1, w.w2, w.b2};
+  for (const void* p : ps)
+    if (!p || !aligned16(p)) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nsa_abi_version(void) { return NSA_ABI_VERSION; }
+
+const char* nsa_status_str(nsa_status s) {
+  switch (s) {
+    case NSA_OK: return "ok";
+    case NSA_ERR_INVALID_ARG: return "invalid argument";
+    case NSA_ERR_UNSUPPORTED: return "unsupported configuration or device";
+    case NSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case NSA_ERR_HIP: return "HIP runtime error";
+    case NSA_ERR_INTERNAL: return "internal error";
+  }
+  return "unknown status";
+}
+
+nsa_status nsa_workspace_size(const nsa_params* p, nsa_op op, size_t* bytes) {
+  try {
+    if (!bytes) return NSA_ERR_INVALID_ARG;
+    Dims dm;
+    nsa_status st = make_dims(p, &dm);
+    if (st != NSA_OK) return st;
+    PrefillWs w;
+    switch (op) {
+      case NSA_OP_FWD_PREFILL: *bytes = plan_prefill(dm, nullptr, &w); return NSA_OK;
+      case NSA_OP_FWD_DECODE: *bytes = decode_ws_bytes(dm); return NSA_OK;
+      case NSA_OP_BWD: *bytes = bwd_ws_bytes(dm); return NSA_OK;
+    }
+    return NSA_ERR_INVALID_ARG;
+  } catch (...) {
+    return NSA_ERR_INTERNAL;
+  }
+}
+
+nsa_status nsa_compress(const nsa_params* p, int is_value, const void* x, const nsa_phi_weights* phi,
+                        void* out, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    Dims dm;
+    nsa_status st = make_dims(p, &dm);
+    if (st != NSA_OK) return st;
+    if (!x || !out || !aligned16(x) || !aligned16(out)) return NSA_ERR_INVALID_ARG;
+    if (dm.hidden && (!phi || !phi_ok(*phi))) return NSA_ERR_INVALID_ARG;
+    PrefillWs w;
+    const size_t need = plan_prefill(dm, nullptr, &w);
+    if (ws_bytes < need || (need && !ws) || !aligned16(ws)) return NSA_ERR_WORKSPACE;
+    if ((st = check_device()) != NSA_OK) return st;
+    plan_prefill(dm, ws, &w);
+    const int D = is_value ? dm.dv : dm.dk;
+    return hip_status(run_compress(dm, D, x, phi, out, nullptr, w.phi, (hipStream_t)stream));
+  } catch (...) {
+    return NSA_ERR_INTERNAL;
+  }
+}
+
+nsa_status nsa_fwd_prefill(const nsa_params* p, const nsa_prefill_args* a, void* ws, size_t ws_bytes,
+                           void* stream) {
+  try {
+    Dims dm;
+    nsa_status st = make_dims(p, &dm);
+    if (st != NSA_OK) return st;
+    if (!a) return NSA_ERR_INVALID_ARG;
+    const void* req[] = {a->q, a->k, a->v, a->x, a->w_gate, a->o};
+    for (const void* r : req)
+      if (!r || !aligned16(r)) return NSA_ERR_INVALID_ARG;
+    const void* opt[] = {a->k_cmp, a->v_cmp, a->lse, a->idx, a->o_branch, a->p_slc, a->gates};
+    for (const void* r : opt)
+      if (r && !aligned16(r)) return NSA_ERR_INVALID_ARG;
+    if (dm.hidden && (!phi_ok(a->phi_k) || !phi_ok(a->phi_v))) return NSA_ERR_INVALID_ARG;
+    PrefillWs w;
+    const size_t need = plan_prefill(dm, nullptr, &w);
+    if (ws_bytes < need || !ws || !aligned16(ws)) return NSA_ERR_WORKSPACE;
+    if ((st = check_device()) != NSA_OK) return st;
+    plan_prefill(dm, ws, &w);
+    hipStream_t s = (hipStream_t)stream;
+    const size_t BTH = (size_t)dm.B * dm.T * dm.Hq;
+    const size_t es = esize(dm);
+    float* gates = a->gates ? (float*)a->gates : (float*)w.gates;
+    void* kc = a->k_cmp ? a->k_cmp : w.kc;
+    void* vc = a->v_cmp ? a->v_cmp : w.vc;
+    float* lse = a->lse ? (float*)a->lse : (float*)w.lse;
+    int* idx = a->idx ? (int*)a->idx : (int*)w.idx;
+    char* ob = a->o_branch ? (char*)a->o_branch : (char*)w.ob;
+    void* o_cmp = ob;
+    void* o_slc = ob + BTH * dm.dv * es;
+    void* o_win = a->o_branch ? ob + 2 * BTH * dm.dv * es : nullptr;
+    hipError_t e;
+    if ((e = launch_gate(dm, dm.B * dm.T, a->x, a->w_gate, gates, s)) != hipSuccess) return NSA_ERR_HIP;
+    if ((e = run_compress(dm, dm.dk, a->k, &a->phi_k, kc, nullptr, w.phi, s)) != hipSuccess) return NSA_ERR_HIP;
+    if ((e = run_compress(dm, dm.dv, a->v, &a->phi_v, vc, w.vct, w.phi, s)) != hipSuccess) return NSA_ERR_HIP;
+    if ((e = launch_transpose_seq(dm, dm.B, dm.T, dm.Hkv, dm.dv, dm.Tp, a->v, w.vt, s)) != hipSuccess)
+      return NSA_ERR_HIP;
+    CmpArgs ca;
+    ca.q = a->q; ca.kc = kc; ca.vct = w.vct; ca.lse = lse; ca.o = o_cmp; ca.p_slc = (float*)a->p_slc; ca.idx = idx;
+    if ((e = launch_cmp_lse(dm, ca, s)) != hipSuccess) return NSA_ERR_HIP;
+    if ((e = launch_cmp_out_topn(dm, ca, s)) != hipSuccess) return NSA_ERR_HIP;
+    SlcArgs sa;
+    sa.q = a->q; sa.k = a->k; sa.vt = w.vt; sa.idx = idx; sa.o = o_slc; sa.lse = lse + BTH;
+    if ((e = launch_slc(dm, sa, s)) != hipSuccess) return NSA_ERR_HIP;
+    WinArgs wa;
+    wa.q = a->q; wa.k = a->k; wa.vt = w.vt; wa.o_cmp = o_cmp; wa.o_slc = o_slc; wa.gates = gates;
+    wa.o_win = o_win; wa.lse = lse + 2 * BTH; wa.o = a->o;
+    if ((e = launch_win_combine(dm, wa, s)) != hipSuccess) return NSA_ERR_HIP;
+    return NSA_OK;
+  } catch (...) {
+    return NSA_ERR_INTERNAL;
+  }
+}
+
+nsa_status nsa_fwd_decode(const nsa_params* p, const nsa_decode_args* a, void* ws, size_t ws_bytes,
+                          void* stream) {
+  try {
+    Dims dm;
+    nsa_status st = make_dims(p, &dm);
+    if (st != NSA_OK) return st;
+    if (!a) return NSA_ERR_INVALID_ARG;
+    const void* req[] = {a->q, a->k_cache, a->v_cache, a->x, a->w_gate, a->o};
+    for (const void* r : req)
+      if (!r || !aligned16(r)) return NSA_ERR_INVALID_ARG;
+    if (dm.ncmp > 0 && (!a->k_cmp_cache || !a->v_cmp_cache || !aligned16(a->k_cmp_cache) ||
+                        !aligned16(a->v_cmp_cache) || a->cmp_cache_cap < dm.ncmp))
+      return NSA_ERR_INVALID_ARG;
+    const void* opt[] = {a->idx, a->p_slc, a->lse, a->o_branch};
+    for (const void* r : opt)
+      if (r && !aligned16(r)) return NSA_ERR_INVALID_ARG;
+    const size_t need = decode_ws_bytes(dm);
+    if (ws_bytes < need || !ws || !aligned16(ws)) return NSA_ERR_WORKSPACE;
+    if ((st = check_device()) != NSA_OK) return st;
+    return hip_status(launch_decode(dm, a, ws, (hipStream_t)stream));
+  } catch (...) {
+    return NSA_ERR_INTERNAL;
+  }
+}
+
+nsa_status nsa_bwd(const nsa_params* p, const nsa_bwd_args* a, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    Dims dm;
+    nsa_status st = make_dims(p, &dm);
+    if (st != NSA_OK) return st;
+    if (!a) return NSA_ERR_INVALID_ARG;
+    const void* req[] = {a->q, a->k, a->v, a->x, a->w_gate, a->lse, a->idx, a->o_branch, a->d_o,
+                         a->dq, a->dk, a->dv, a->dw_gate};
+    for (const void* r : req)
+      if (!r || !aligned16(r)) return NSA_ERR_INVALID_ARG;
+    if (dm.ncmp > 0 && (!a->k_cmp || !a->v_cmp || !aligned16(a->k_cmp) || !aligned16(a->v_cmp)))
+      return NSA_ERR_INVALID_ARG;
+    if (dm.hidden) {
+      if (!phi_ok(a->phi_k) || !phi_ok(a->phi_v)) return NSA_ERR_INVALID_ARG;
+      const void* g[] = {a->d_phi_k.pe, a->d_phi_k.w1, a->d_phi_k.b1, a->d_phi_k.w2, a->d_phi_k.b2,
+                         a->d_phi_v.pe, a->d_phi_v.w1, a->d_phi_v.b1, a->d_phi_v.w2, a->d_phi_v.b2};
+      for (const void* r : g)
+        if (!r || !aligned16(r)) return NSA_ERR_INVALID_ARG;
+    }
+    const size_t need = bwd_ws_bytes(dm);
+    if (ws_bytes < need || !ws || !aligned16(ws)) return NSA_ERR_WORKSPACE;
+    if ((st = check_device()) != NSA_OK) return st;
+    return hip_status(launch_bwd(dm, a, ws, (hipStream_t)stream));
+  } catch (...) {
+    return NSA_ERR_INTERNAL;
+  }
+}
+
+}  // extern "C"

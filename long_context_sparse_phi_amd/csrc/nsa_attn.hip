@@ -1,0 +1,256 @@
+// Selected-block attention and sliding-window attention + gated combine.
+//
+// Selected branch (youleyou NSA page, Top-n块选择 and 内核设计): the query of
+// position t attends to the tokens <= t of its n selected blocks.  All G query
+// heads of a GQA group share the block set, so one wave takes the G heads of
+// one position as the 16 columns of its MFMA tiles and streams each selected
+// block's keys and values through them once (group-centric loading; every
+// 64-token block fetched feeds all G heads).  Online softmax across blocks.
+//
+// Window branch (滑动窗口): keys [t-w+1, t].  A wave owns several consecutive
+// positions x G heads; the keys of its band are streamed once for all of
+// them.  The epilogue reads the other two branch outputs and the gates and
+// writes o = g_cmp O_cmp + g_slc O_slc + g_win O_win (最终输出计算).
+//
+// MFMA layout as in the compressed branch: S^T = K Q^T with keys permuted so
+// lane group qd holds keys 8*qd..8*qd+7, then O^T += V^T P^T with V^T read
+// from a transposed copy of V ([B, Hkv, dv, Tp]).
+#include "nsa_common.hpp"
+#include "nsa_kernels.hpp"
+
+namespace nsa {
+
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(256) void k_slc(Dims dm, SlcArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c16 = lane & 15, qd = lane >> 4;
+  const int ntiles = (dm.T + 3) / 4;
+  int unit, tile;
+  xcd_map(blockIdx.x, dm.B * dm.Hkv, ntiles, unit, tile);
+  const int b = unit / dm.Hkv, g = unit % dm.Hkv;
+  const int t = tile * 4 + wave;
+  if (t >= dm.T) return;
+  const int G = dm.G;
+  const bool cv = c16 < G;
+  const int hq = g * G + (cv ? c16 : 0);
+  const size_t qrow = (size_t)(b * dm.T + t) * dm.Hq + hq;
+  Frag8<T> qf[DK / 32];
+  {
+    const T* qp = (const T*)a.q + qrow * DK + qd * 8;
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) qf[ks] = cv ? load_frag(qp + ks * 32) : zero_frag<T>();
+  }
+  const int* ids = a.idx + ((size_t)(b * dm.T + t) * dm.Hkv + g) * dm.n;
+  const float sc2 = dm.scale * kLog2e;
+  float m = kNegInf, ls = 0.f;
+  f32x4 oacc[DV / 16];
+#pragma unroll
+  for (int dt = 0; dt < DV / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const size_t kstride = (size_t)dm.Hkv * DK;
+  const T* kbase = (const T*)a.k + ((size_t)b * dm.T * dm.Hkv + g) * DK + qd * 8;
+  const T* vtb = (const T*)a.vt + (size_t)(b * dm.Hkv + g) * DV * dm.Tp + qd * 8;
+  const int krow = (c16 >> 2) * 8 + (c16 & 3);
+  for (int si = 0; si < dm.n; ++si) {
+    const int j = ids[si];
+    if (j < 0) break;
+    const int kend = min((j + 1) * dm.ls, t + 1);
+    for (int kt = j * dm.ls; kt < kend; kt += 32) {
+      f32x4 s[2];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        s[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int key = min(kt + krow + sub * 4, dm.T - 1);
+        const T* kp = kbase + (size_t)key * kstride;
+#pragma unroll
+        for (int ks = 0; ks < DK / 32; ++ks) mma(s[sub], load_frag(kp + ks * 32), qf[ks]);
+      }
+      Frag8<T> vf[DV / 16];
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt) vf[dt] = load_frag(vtb + (size_t)(dt * 16 + c16) * dm.Tp + kt);
+      float v[8], mx = kNegInf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = kt + qd * 8 + e;
+        v[e] = key < kend ? s[e >> 2][e & 3] * sc2 : kNegInf;
+        mx = fmaxf(mx, v[e]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m, mx);
+      const float mref = mn == kNegInf ? 0.f : mn;
+      const float alpha = fast_exp2(m - mref);
+      float p[8], psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { p[e] = fast_exp2(v[e] - mref); psum += p[e]; }
+      ls = ls * alpha + psum;
+      m = mn;
+      Frag8<T> pf = to_frag<T>(p);
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt) {
+        oacc[dt] *= alpha;
+        mma(oacc[dt], vf[dt], pf);
+      }
+    }
+  }
+  float tot = ls + __shfl_xor(ls, 16);
+  tot += __shfl_xor(tot, 32);
+  const float inv = 1.f / tot;
+  if (cv) {
+    T* op = (T*)a.o + qrow * DV + qd * 4;
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt)
+      store4(op + dt * 16, oacc[dt][0] * inv, oacc[dt][1] * inv, oacc[dt][2] * inv, oacc[dt][3] * inv);
+    if (qd == 0) a.lse[qrow] = (m + __log2f(tot)) * kLn2;
+  }
+}
+
+hipError_t launch_slc(const Dims& dm, const SlcArgs& a, hipStream_t s) {
+  const int ntiles = (dm.T + 3) / 4;
+  dim3 grid(ntiles * dm.B * dm.Hkv);
+  const bool bf = dm.io == IO_BF16;
+  if (dm.dk == 64 && dm.dv == 64) {
+    if (bf) k_slc<bf16, 64, 64><<<grid, 256, 0, s>>>(dm, a); else k_slc<float, 64, 64><<<grid, 256, 0, s>>>(dm, a);
+  } else if (dm.dk == 128 && dm.dv == 128) {
+    if (bf) k_slc<bf16, 128, 128><<<grid, 256, 0, s>>>(dm, a); else k_slc<float, 128, 128><<<grid, 256, 0, s>>>(dm, a);
+  } else if (dm.dk == 192 && dm.dv == 128) {
+    if (bf) k_slc<bf16, 192, 128><<<grid, 256, 0, s>>>(dm, a); else k_slc<float, 192, 128><<<grid, 256, 0, s>>>(dm, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int DK, int DV, int NCT>
+__global__ __launch_bounds__(256) void k_win(Dims dm, WinArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c16 = lane & 15, qd = lane >> 4;
+  const int G = dm.G, PW = 16 * NCT / G, PWG = 4 * PW;
+  const int ntiles = (dm.T + PWG - 1) / PWG;
+  int unit, tile;
+  xcd_map(blockIdx.x, dm.B * dm.Hkv, ntiles, unit, tile);
+  const int b = unit / dm.Hkv, g = unit % dm.Hkv;
+  const int t0 = tile * PWG + wave * PW;
+  if (t0 >= dm.T) return;
+  const int tl = min(dm.T - 1, t0 + PW - 1);
+  Frag8<T> qf[NCT][DK / 32];
+  int pos[NCT], hq[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int col = ct * 16 + c16;
+    pos[ct] = t0 + col / G;
+    hq[ct] = g * G + col % G;
+    const bool v = pos[ct] < dm.T;
+    const T* qp = (const T*)a.q + ((size_t)(b * dm.T + min(pos[ct], dm.T - 1)) * dm.Hq + hq[ct]) * DK + qd * 8;
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) qf[ct][ks] = v ? load_frag(qp + ks * 32) : zero_frag<T>();
+  }
+  const float sc2 = dm.scale * kLog2e;
+  float m[NCT], ls[NCT];
+  f32x4 oacc[DV / 16][NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    m[ct] = kNegInf;
+    ls[ct] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt) oacc[dt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const size_t kstride = (size_t)dm.Hkv * DK;
+  const T* kbase = (const T*)a.k + ((size_t)b * dm.T * dm.Hkv + g) * DK + qd * 8;
+  const T* vtb = (const T*)a.vt + (size_t)(b * dm.Hkv + g) * DV * dm.Tp + qd * 8;
+  const int krow = (c16 >> 2) * 8 + (c16 & 3);
+  const int kstart = max(0, t0 - dm.w + 1) & ~31;
+  for (int kt = kstart; kt <= tl; kt += 32) {
+    f32x4 s[2][NCT];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) s[sub][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int key = min(kt + krow + sub * 4, dm.T - 1);
+      const T* kp = kbase + (size_t)key * kstride;
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks) {
+        Frag8<T> kf = load_frag(kp + ks * 32);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) mma(s[sub][ct], kf, qf[ct][ks]);
+      }
+    }
+    Frag8<T> vf[DV / 16];
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt) vf[dt] = load_frag(vtb + (size_t)(dt * 16 + c16) * dm.Tp + kt);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      float v[8], mx = kNegInf;
+      const int lo = pos[ct] - dm.w + 1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = kt + qd * 8 + e;
+        v[e] = (key >= lo && key <= pos[ct]) ? s[e >> 2][ct][e & 3] * sc2 : kNegInf;
+        mx = fmaxf(mx, v[e]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m[ct], mx);
+      const float mref = mn == kNegInf ? 0.f : mn;
+      const float alpha = fast_exp2(m[ct] - mref);
+      float p[8], psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { p[e] = fast_exp2(v[e] - mref); psum += p[e]; }
+      ls[ct] = ls[ct] * alpha + psum;
+      m[ct] = mn;
+      Frag8<T> pf = to_frag<T>(p);
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt) {
+        oacc[dt][ct] *= alpha;
+        mma(oacc[dt][ct], vf[dt], pf);
+      }
+    }
+  }
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    float tot = ls[ct] + __shfl_xor(ls[ct], 16);
+    tot += __shfl_xor(tot, 32);
+    if (pos[ct] >= dm.T) continue;
+    const float inv = 1.f / tot;
+    const size_t row = (size_t)(b * dm.T + pos[ct]) * dm.Hq + hq[ct];
+    if (a.lse && qd == 0) a.lse[row] = (m[ct] + __log2f(tot)) * kLn2;
+    const float g0 = a.gates[row * 3 + 0], g1 = a.gates[row * 3 + 1], g2 = a.gates[row * 3 + 2];
+    const size_t ob = row * DV + qd * 4;
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt) {
+      float ow[4], oc[4], os[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ow[r] = oacc[dt][ct][r] * inv;
+      if (a.o_win) {
+        // the stored branch output is what the combine uses
+        store4((T*)a.o_win + ob + dt * 16, ow[0], ow[1], ow[2], ow[3]);
+      }
+      load4((const T*)a.o_cmp + ob + dt * 16, oc);
+      load4((const T*)a.o_slc + ob + dt * 16, os);
+      store4((T*)a.o + ob + dt * 16, g0 * oc[0] + g1 * os[0] + g2 * ow[0], g0 * oc[1] + g1 * os[1] + g2 * ow[1],
+             g0 * oc[2] + g1 * os[2] + g2 * ow[2], g0 * oc[3] + g1 * os[3] + g2 * ow[3]);
+    }
+  }
+}
+
+template <typename T, int DK, int DV>
+static hipError_t win_impl(const Dims& dm, const WinArgs& a, hipStream_t s) {
+  constexpr int NCT = 4;
+  const int PWG = 4 * 16 * NCT / dm.G;
+  const int ntiles = (dm.T + PWG - 1) / PWG;
+  k_win<T, DK, DV, NCT><<<ntiles * dm.B * dm.Hkv, 256, 0, s>>>(dm, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_win_combine(const Dims& dm, const WinArgs& a, hipStream_t s) {
+  const bool bf = dm.io == IO_BF16;
+  if (dm.dk == 64 && dm.dv == 64) return bf ? win_impl<bf16, 64, 64>(dm, a, s) : win_impl<float, 64, 64>(dm, a, s);
+  if (dm.dk == 128 && dm.dv == 128) return bf ? win_impl<bf16, 128, 128>(dm, a, s) : win_impl<float, 128, 128>(dm, a, s);
+  if (dm.dk == 192 && dm.dv == 128) return bf ? win_impl<bf16, 192, 128>(dm, a, s) : win_impl<float, 192, 128>(dm, a, s);
+  return hipErrorInvalidValue;
+}
+
+bool shapes_supported(int dk, int dv) {
+  return (dk == 64 && dv == 64) || (dk == 128 && dv == 128) || (dk == 192 && dv == 128);
+}
+
+}  // namespace nsa

@@ -1,0 +1,142 @@
+// Device helpers shared by the gfx950 NSA kernels: MFMA fragments, conversions,
+// wave reductions and the workgroup -> XCD work mapping.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nsa {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// ---------------------------------------------------------------------------
+// One lane's share of an MFMA operand: 8 consecutive elements along the
+// contraction index.  For v_mfma_f32_16x16x32_bf16 lane l holds row (or
+// column) l%16 and contraction indices 8*(l/16) .. 8*(l/16)+7.  The fp32
+// variant issues eight v_mfma_f32_16x16x4_f32, the e-th contracting element e
+// of every lane, which sums the same 32 products.
+// ---------------------------------------------------------------------------
+template <typename T> struct Frag8;
+template <> struct Frag8<bf16> { bf16x8 v; };
+template <> struct Frag8<float> { f32x4 lo, hi; };
+
+__device__ __forceinline__ Frag8<bf16> load_frag(const bf16* p) {
+  Frag8<bf16> f;
+  f.v = *reinterpret_cast<const bf16x8*>(p);
+  return f;
+}
+__device__ __forceinline__ Frag8<float> load_frag(const float* p) {
+  Frag8<float> f;
+  f.lo = *reinterpret_cast<const f32x4*>(p);
+  f.hi = *reinterpret_cast<const f32x4*>(p + 4);
+  return f;
+}
+template <typename T> __device__ __forceinline__ Frag8<T> zero_frag();
+template <> __device__ __forceinline__ Frag8<bf16> zero_frag<bf16>() {
+  Frag8<bf16> f;
+  for (int e = 0; e < 8; ++e) f.v[e] = (bf16)0.0f;
+  return f;
+}
+template <> __device__ __forceinline__ Frag8<float> zero_frag<float>() {
+  Frag8<float> f;
+  for (int e = 0; e < 4; ++e) { f.lo[e] = 0.f; f.hi[e] = 0.f; }
+  return f;
+}
+
+__device__ __forceinline__ void mma(f32x4& c, const Frag8<bf16>& a, const Frag8<bf16>& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& c, const Frag8<float>& a, const Frag8<float>& b) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[e], b.lo[e], c, 0, 0, 0);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[e], b.hi[e], c, 0, 0, 0);
+}
+
+// 8 fp32 values -> operand fragment of element type T (round to nearest even).
+__device__ __forceinline__ Frag8<bf16> to_frag_bf16(const float* x) {
+  Frag8<bf16> f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = (bf16)x[e];
+  return f;
+}
+template <typename T> __device__ __forceinline__ Frag8<T> to_frag(const float* x);
+template <> __device__ __forceinline__ Frag8<bf16> to_frag<bf16>(const float* x) { return to_frag_bf16(x); }
+template <> __device__ __forceinline__ Frag8<float> to_frag<float>(const float* x) {
+  Frag8<float> f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { f.lo[e] = x[e]; f.hi[e] = x[4 + e]; }
+  return f;
+}
+// x = hi + lo with hi, lo in bf16: the pair carries ~16 significant bits.
+__device__ __forceinline__ void split_bf16(const float* x, Frag8<bf16>& hi, Frag8<bf16>& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    bf16 h = (bf16)x[e];
+    hi.v[e] = h;
+    lo.v[e] = (bf16)(x[e] - (float)h);
+  }
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+
+// Store 4 consecutive values.
+__device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
+  bf16x4 v;
+  v[0] = (bf16)a; v[1] = (bf16)b; v[2] = (bf16)c; v[3] = (bf16)d;
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  f32x4 v;
+  v[0] = a; v[1] = b; v[2] = c; v[3] = d;
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+__device__ __forceinline__ void load4(const bf16* p, float* o) {
+  bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  o[0] = (float)v[0]; o[1] = (float)v[1]; o[2] = (float)v[2]; o[3] = (float)v[3];
+}
+__device__ __forceinline__ void load4(const float* p, float* o) {
+  f32x4 v = *reinterpret_cast<const f32x4*>(p);
+  o[0] = v[0]; o[1] = v[1]; o[2] = v[2]; o[3] = v[3];
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Number of complete compression blocks [i*d, i*d+l) whose last token is <= t.
+__device__ __forceinline__ int ncmp_visible(int t, int l, int d) {
+  int s = t + 1;
+  return s < l ? 0 : (s - l) / d + 1;
+}
+
+// ---------------------------------------------------------------------------
+// Workgroup -> (batch*kv-head unit, tile) mapping.  Workgroups are handed to
+// the 8 XCDs round-robin by id; this keeps every XCD on one (batch, kv head)
+// unit when there are at most 8 units (so that unit's keys stay in that
+// XCD's L2), and hands out the most expensive tiles (late positions) first.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void xcd_map(int id, int units, int ntiles, int& unit, int& tile) {
+  if (units <= 8 && 8 % units == 0 && ntiles % (8 / units) == 0) {
+    int per = 8 / units, x = id & 7, k = id >> 3;
+    unit = x / per;
+    tile = ntiles - 1 - (k * per + x % per);
+  } else if (units % 8 == 0) {
+    int x = id & 7, k = id >> 3;
+    unit = x + 8 * (k / ntiles);
+    tile = ntiles - 1 - k % ntiles;
+  } else {
+    unit = id / ntiles;
+    tile = ntiles - 1 - id % ntiles;
+  }
+}
+
+}  // namespace nsa

@@ -1,0 +1,12 @@
+// Decode step kernels (placeholder until the decode path lands).
+#include "nsa_common.hpp"
+#include "nsa_kernels.hpp"
+#include "../../include/nsa.h"
+
+namespace nsa {
+size_t decode_ws_bytes(const Dims& dm) { (void)dm; return 0; }
+hipError_t launch_decode(const Dims& dm, const nsa_decode_args* a, void* ws, hipStream_t s) {
+  (void)dm; (void)a; (void)ws; (void)s;
+  return hipErrorNotSupported;
+}
+}  // namespace nsa

@@ -1,0 +1,102 @@
+// Internal interface between the C ABI layer (nsa_api.cpp) and the kernel
+// translation units.  Plain structs of device pointers and sizes; every
+// launch_* returns the hipError_t of its launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nsa {
+
+enum IoType { IO_BF16 = 0, IO_F32 = 1 };
+
+struct Dims {
+  int B, T, Hkv, G, Hq, dk, dv;
+  int l, d, ls, n, w;
+  int ncmp;       // complete compressed blocks of the whole sequence
+  int ncmp_pad;   // ncmp rounded up to a multiple of 64 (+64): row stride of V_cmp^T
+  int nsel;       // ceil(T / ls)
+  int Tp;         // row stride of V^T: T rounded up to 64, plus 64
+  int C;          // gate input width
+  int hidden;     // phi MLP width
+  float scale;    // softmax scale
+  int io;         // IoType
+};
+
+// ---- gate: gates[b,t,h,c] = sigmoid(sum_i x[b,t,i] w[i,h,c]) ----
+hipError_t launch_gate(const Dims& dm, int ntok, const void* x, const void* w, float* gates,
+                       hipStream_t s);
+
+// ---- transposes ----
+// src [B, n, H, D] -> dst [B, H, D, ldd] with zeros in columns n..ldd-1.
+hipError_t launch_transpose_seq(const Dims& dm, int B, int n, int H, int D, int ldd,
+                                const void* src, void* dst, hipStream_t s);
+// src [R, Cc] -> dst [Cc, R]  (element type = io type)
+hipError_t launch_transpose_2d(const Dims& dm, int R, int Cc, const void* src, void* dst,
+                               hipStream_t s);
+
+// ---- compression phi ----
+// mean-pool: x [B,T,Hkv,D] -> out [B,ncmp,Hkv,D]; outT (optional) [B,Hkv,D,ncmp_pad]
+hipError_t launch_meanpool(const Dims& dm, int D, const void* x, void* out, void* outT,
+                           hipStream_t s);
+// MLP phi, in four launches; see nsa_phi.hip.
+struct PhiMlpArgs {
+  int D;                 // feature dim of this tensor (dk or dv)
+  const void* x;         // [B,T,Hkv,D]
+  const void* pe;        // [l, D]
+  const void* w1;        // [l*D, hidden]
+  const void* b1;        // [hidden]
+  const void* w2;        // [hidden, D]
+  const void* b2;        // [D]
+  void* w1t;             // ws: [hidden, l*D]   (io type)
+  void* w2t;             // ws: [D, hidden]     (io type)
+  float* cvec;           // ws: [hidden]  b1 + sum_j pe[j] . w1[j]
+  float* y;              // ws: [B*Hkv*nsub, (l/d)*hidden] sub-block products
+  void* h;               // ws: hidden activations [B*Hkv*ncmp, hidden]: bf16 hi,lo pair or fp32
+  void* out;             // [B,ncmp,Hkv,D]
+  void* outT;            // optional [B,Hkv,D,ncmp_pad]
+};
+hipError_t launch_phi_mlp(const Dims& dm, const PhiMlpArgs& a, hipStream_t s);
+size_t phi_mlp_ws_bytes(const Dims& dm, int D);
+
+// ---- compressed attention ----
+struct CmpArgs {
+  const void* q;    // [B,T,Hq,dk]
+  const void* kc;   // [B,ncmp,Hkv,dk]
+  const void* vct;  // [B,Hkv,dv,ncmp_pad]
+  float* lse;       // [B,T,Hq]  natural-log lse of the compressed branch
+  void* o;          // [B,T,Hq,dv]
+  float* p_slc;     // optional [B,T,Hkv,nsel]
+  int* idx;         // [B,T,Hkv,n]
+};
+hipError_t launch_cmp_lse(const Dims& dm, const CmpArgs& a, hipStream_t s);
+hipError_t launch_cmp_out_topn(const Dims& dm, const CmpArgs& a, hipStream_t s);
+
+// ---- selected attention ----
+struct SlcArgs {
+  const void* q;    // [B,T,Hq,dk]
+  const void* k;    // [B,T,Hkv,dk]
+  const void* vt;   // [B,Hkv,dv,Tp]
+  const int* idx;   // [B,T,Hkv,n]
+  void* o;          // [B,T,Hq,dv]
+  float* lse;       // [B,T,Hq]
+};
+hipError_t launch_slc(const Dims& dm, const SlcArgs& a, hipStream_t s);
+
+// ---- sliding window + gated combine ----
+struct WinArgs {
+  const void* q;       // [B,T,Hq,dk]
+  const void* k;       // [B,T,Hkv,dk]
+  const void* vt;      // [B,Hkv,dv,Tp]
+  const void* o_cmp;   // [B,T,Hq,dv]
+  const void* o_slc;   // [B,T,Hq,dv]
+  const float* gates;  // [B,T,Hq,3]
+  void* o_win;         // optional [B,T,Hq,dv]
+  float* lse;          // optional [B,T,Hq]
+  void* o;             // [B,T,Hq,dv]
+};
+hipError_t launch_win_combine(const Dims& dm, const WinArgs& a, hipStream_t s);
+
+bool shapes_supported(int dk, int dv);
+
+}  // namespace nsa

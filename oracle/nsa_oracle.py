@@ -216,14 +216,12 @@ def win_keys(t: int, p: Params) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def remap_matrix(n_cmp: int, n_sel: int, p: Params) -> np.ndarray:
-    W = np.zeros((n_cmp, n_sel))
-    for i in range(n_cmp):
-        a0, a1 = i * p.d, i * p.d + p.l
-        for j in range(n_sel):
-            b0, b1 = j * p.l_sel, (j + 1) * p.l_sel
-            ov = max(0, min(a1, b1) - max(a0, b0))
-            W[i, j] = ov / p.d
-    return W
+    i = np.arange(n_cmp)[:, None]
+    j = np.arange(n_sel)[None, :]
+    a0, a1 = i * p.d, i * p.d + p.l                 # compression block token range
+    b0, b1 = j * p.l_sel, (j + 1) * p.l_sel         # selection block token range
+    ov = np.maximum(0, np.minimum(a1, b1) - np.maximum(a0, b0))
+    return ov / p.d
 
 
 # ---------------------------------------------------------------------------
@@ -287,7 +285,7 @@ def decode_token_count(s: int, p: Params) -> int:
 # ---------------------------------------------------------------------------
 
 def _row(p: Params, t: int, q_t, k, v, kc, vc, g_t, n_sel: int,
-         sel: Optional[List[List[int]]] = None, tie_scores=None):
+         sel: Optional[List[List[int]]] = None, tie_scores=None, W_full=None):
     """All NSA quantities at position t of one sequence.
 
     q_t [Hq,dk]; k [*,Hkv,dk], v [*,Hkv,dv] raw keys/values (positions <= t used);
@@ -302,7 +300,7 @@ def _row(p: Params, t: int, q_t, k, v, kc, vc, g_t, n_sel: int,
     dv = v.shape[2]
     sc = _scale(p, dk)
     ic = cmp_keys(t, p)
-    W = remap_matrix(len(ic), n_sel, p)
+    W = (W_full if W_full is not None else remap_matrix(len(ic), n_sel, p))[:len(ic)]
     o_br = np.zeros((3, Hq, dv))
     lse = np.zeros((3, Hq))
     p_slc = np.zeros((Hkv, n_sel))
@@ -362,6 +360,7 @@ def forward(p: Params, q, k, v, x, w_gate, phi_k=None, phi_v=None, rows=None,
     if vc is None:
         vc = compress(v, phi_v, p)
     g_all = gate(x[:, rows], w_gate)
+    W_full = remap_matrix(kc.shape[1], n_sel, p)
     out = {
         "o": np.zeros((B, R, Hq, dv)), "o_branch": np.zeros((3, B, R, Hq, dv)),
         "lse": np.zeros((3, B, R, Hq)), "p_slc": np.zeros((B, R, Hkv, n_sel)),
@@ -374,7 +373,7 @@ def forward(p: Params, q, k, v, x, w_gate, phi_k=None, phi_v=None, rows=None,
             sel = None if idx is None else [list(idx[b, t, g]) for g in range(Hkv)]
             ts = None if tie_scores is None else tie_scores[b, t]
             o, o_br, lse, ps, sets, ret = _row(p, int(t), q[b, t], k[b], v[b], kc[b], vc[b],
-                                               g_all[b, r], n_sel, sel, ts)
+                                               g_all[b, r], n_sel, sel, ts, W_full)
             out["o"][b, r] = o
             out["o_branch"][:, b, r] = o_br
             out["lse"][:, b, r] = lse

@@ -1,0 +1,38 @@
+"""Helpers shared by the GPU parity tests: move seeded inputs to the GPU and
+run the oracle on the same values."""
+import numpy as np
+import torch
+
+import nsa_inputs as NI
+
+ATOL, RTOL = 2e-2, 1e-2   # |gpu - oracle| <= ATOL + RTOL * |oracle|
+
+
+def oracle_params(w):
+    import oracle as O
+    return O.Params(l=w.l, d=w.d, l_sel=w.l_sel, n=w.n, w=w.w, phi=w.phi,
+                    io="bf16" if w.dtype == "bf16" else "fp32")
+
+
+def to_dev(d, dev="cuda:0"):
+    if isinstance(d, dict):
+        return {k: to_dev(v, dev) for k, v in d.items()}
+    return d.to(dev)
+
+
+def np64(t):
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def assert_close(gpu, ref, name, atol=ATOL, rtol=RTOL):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (name, gpu.shape, ref.shape)
+    both_inf = np.isinf(gpu) & np.isinf(ref) & (np.sign(gpu) == np.sign(ref))
+    err = np.where(both_inf, 0.0, np.abs(gpu - ref))
+    bad = ~(err <= atol + rtol * np.abs(np.where(both_inf, 0.0, ref)))
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(f"{name}: {bad.sum()} of {bad.size} elements out of tolerance; first at "
+                             f"{tuple(i)}: gpu={gpu[tuple(i)]} oracle={ref[tuple(i)]} max err={err.max():.3e}")
+    return float(err.max()) if err.size else 0.0

@@ -1,0 +1,65 @@
+"""The C-ABI library loads and exports every entry point include/nsa.h declares.
+CPU only: no compute call is made."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "long_context_sparse_phi_amd", "libnsa.so")
+HEADER = os.path.join(ROOT, "include", "nsa.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nsa_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libnsa.so is not built (run __graft_entry__.build())")
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_three_entry_points():
+    fns = declared_functions()
+    for f in ("nsa_fwd_prefill", "nsa_fwd_decode", "nsa_bwd", "nsa_workspace_size"):
+        assert f in fns
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings(lib):
+    lib.nsa_abi_version.restype = ctypes.c_int
+    assert lib.nsa_abi_version() == 1
+    lib.nsa_status_str.restype = ctypes.c_char_p
+    lib.nsa_status_str.argtypes = [ctypes.c_int]
+    assert lib.nsa_status_str(0) == b"ok"
+    assert lib.nsa_status_str(3).startswith(b"workspace")
+
+
+def test_ctypes_mirror_matches_header_and_validation_runs_on_host():
+    import long_context_sparse_phi_amd as nsa
+    from long_context_sparse_phi_amd import _lib
+    # nsa_params: 15 int32 + 1 float
+    assert ctypes.sizeof(_lib.nsa_params) == 64
+    cfg = nsa.Config(B=1, T=1024, H_kv=1, G=4, d_k=64, d_v=64, n=4, w=128, phi="mean", dtype="fp32")
+    assert nsa.workspace_size(cfg, _lib.NSA_OP_FWD_PREFILL) > 0
+    bad = nsa.Config(B=1, T=1024, H_kv=1, G=3, d_k=64, d_v=64)
+    with pytest.raises(nsa.NSAError) as e:
+        nsa.workspace_size(bad, _lib.NSA_OP_FWD_PREFILL)
+    assert e.value.code == _lib.NSA_ERR_UNSUPPORTED
+    bad = nsa.Config(B=1, T=1024, H_kv=1, G=4, d_k=64, d_v=64, l=24, d=16)
+    with pytest.raises(nsa.NSAError) as e:
+        nsa.workspace_size(bad, _lib.NSA_OP_FWD_PREFILL)
+    assert e.value.code == _lib.NSA_ERR_INVALID_ARG
+    bad = nsa.Config(B=1, T=1024, H_kv=1, G=4, d_k=64, d_v=64, n=2)
+    with pytest.raises(nsa.NSAError) as e:
+        nsa.workspace_size(bad, _lib.NSA_OP_FWD_PREFILL)
+    assert e.value.code == _lib.NSA_ERR_INVALID_ARG
