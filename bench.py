@@ -1,0 +1,290 @@
+"""Benchmark of the NSA hot path on one MI355X.
+
+A step is one NSA prefill forward (gates, compression, compressed attention
+with scores and top-n, selected attention, window attention and the gated
+combine) over the 64K-token workload (B=1, T=65536, 4 KV x 16 query heads,
+d_k=192, d_v=128, bf16), inputs resident in HBM.  The JSON line reports
+tokens/s for that step, the per-stage times measured with HIP events on the
+launch stream inside the timed region, the roofline of the dominant kernel,
+the decode and backward legs when available, and the fp64 CPU oracle timed
+on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "NSA prefill fwd tokens/s at 64K (MFMA % peak); decode HBM GB/s at 64K KV"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+PREFILL_STAGES = [
+    ("gates", "k_gate"), ("compress_k", "k_phi_gemm1"), ("compress_v", "k_phi_gemm1"),
+    ("transpose_v", "k_transpose_seq"), ("cmp_lse", "k_cmp_lse"), ("cmp_out_topn", "k_cmp_out"),
+    ("selected", "k_slc"), ("window_combine", "k_win"),
+]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- work model
+
+def key_counts(w):
+    """Per-position key counts of the three branches (numpy int64 arrays)."""
+    import numpy as np
+    t = np.arange(w.T, dtype=np.int64)
+    s = t + 1
+    n_cmp = np.where(s < w.l, 0, (s - w.l) // w.d + 1)
+    all_blocks = (t // w.l_sel + 1) <= w.n
+    n_slc = np.where(all_blocks, s, (w.n - 1) * w.l_sel + (t % w.l_sel) + 1)
+    n_win = np.minimum(s, w.w)
+    return n_cmp, n_slc, n_win
+
+
+def useful_flops(w):
+    """Algorithmic FLOPs of the prefill forward (2 per multiply-add, unmasked
+    query-key pairs only; the log-sum-exp recompute is not counted)."""
+    n_cmp, n_slc, n_win = key_counts(w)
+    per_pair = 2 * (w.d_k + w.d_v) * w.B * w.H_q
+    ncmp_tot = 0 if w.T < w.l else (w.T - w.l) // w.d + 1
+    phi = 0
+    if w.phi == "mlp":
+        phi = 2 * w.B * w.H_kv * ncmp_tot * (w.l * w.d_k * w.hidden + w.hidden * w.d_k +
+                                             w.l * w.d_v * w.hidden + w.hidden * w.d_v)
+    gate = 2 * w.B * w.T * w.gate_dim * 3 * w.H_q
+    return {"cmp": per_pair * int(n_cmp.sum()), "slc": per_pair * int(n_slc.sum()),
+            "win": per_pair * int(n_win.sum()), "phi": phi, "gate": gate,
+            "cmp_lse": 2 * w.d_k * w.B * w.H_q * int(n_cmp.sum())}
+
+
+# ---------------------------------------------------------------- HIP events
+
+class HipEvents:
+    def __init__(self, lib):
+        self.lib = lib
+        lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        lib.hipEventCreate.restype = ctypes.c_int
+        lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        lib.hipEventElapsedTime.restype = ctypes.c_int
+        lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, src_files):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 PMC summary,
+    when it was taken from the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel)
+    if not rec or rec.get("source_sha") != source_hash(src_files):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------- prefill leg
+
+def run_prefill(steps, warmup, wname="prefill_64k"):
+    import torch
+    import long_context_sparse_phi_amd as nsa
+    from long_context_sparse_phi_amd import _lib
+    import nsa_inputs as NI
+
+    w = NI.workload(wname)
+    cfg = nsa.config_from_workload(w)
+    log(f"generating inputs for {wname}")
+    inp = NI.make_prefill_inputs(w, 0)
+    dev = torch.device("cuda:0")
+    d = {k: ({kk: vv.to(dev) for kk, vv in v.items()} if isinstance(v, dict) else v.to(dev))
+         for k, v in inp.items()}
+    del inp
+    o = torch.empty(w.B, w.T, w.H_q, w.d_v, dtype=cfg.torch_dtype, device=dev)
+    ws = torch.empty(nsa.workspace_size(cfg, _lib.NSA_OP_FWD_PREFILL), dtype=torch.uint8, device=dev)
+    lib = _lib.load()
+    lib.nsa_fwd_prefill_timed.restype = ctypes.c_int
+    lib.nsa_fwd_prefill_timed.argtypes = [ctypes.POINTER(_lib.nsa_params), ctypes.POINTER(_lib.nsa_prefill_args),
+                                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                          ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+    p = cfg.params()
+    a = _lib.nsa_prefill_args()
+    for name in ("q", "k", "v", "x", "w_gate"):
+        setattr(a, name, d[name].data_ptr())
+    a.phi_k = nsa._phi_struct(cfg, d["phi_k"], w.d_k, dev)
+    a.phi_v = nsa._phi_struct(cfg, d["phi_v"], w.d_v, dev)
+    a.o = o.data_ptr()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    nst = len(PREFILL_STAGES)
+    ev = HipEvents(lib)
+    events = [ev.create(nst + 1) for _ in range(steps)]
+
+    def step(evs=None):
+        if evs is None:
+            st = lib.nsa_fwd_prefill(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(), stream)
+        else:
+            arr = (ctypes.c_void_p * len(evs))(*evs)
+            st = lib.nsa_fwd_prefill_timed(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(), stream,
+                                           arr, len(evs))
+        if st != 0:
+            raise RuntimeError(f"nsa_fwd_prefill failed: {_lib.status_str(st)}")
+
+    log(f"prefill warmup {warmup}")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"prefill timed {steps}")
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = [sum(ev.elapsed_ms(events[i][s], events[i][s + 1]) for i in range(steps)) / steps
+                for s in range(nst)]
+    gpu_ms = sum(ev.elapsed_ms(events[i][0], events[i][nst]) for i in range(steps)) / steps
+    return w, wall, stage_ms, gpu_ms
+
+
+def prefill_roofline(w, stage_ms):
+    fl = useful_flops(w)
+    work = {"gates": fl["gate"], "compress_k": fl["phi"] * w.d_k / (w.d_k + w.d_v),
+            "compress_v": fl["phi"] * w.d_v / (w.d_k + w.d_v), "transpose_v": 0, "cmp_lse": fl["cmp_lse"],
+            "cmp_out_topn": fl["cmp"], "selected": fl["slc"], "window_combine": fl["win"]}
+    i = max(range(len(stage_ms)), key=lambda s: stage_ms[s])
+    name, kern = PREFILL_STAGES[i]
+    achieved = work[name] / (stage_ms[i] * 1e-3) / 1e12
+    src = {"k_cmp_out": ["long_context_sparse_phi_amd/csrc/nsa_cmp.hip"],
+           "k_cmp_lse": ["long_context_sparse_phi_amd/csrc/nsa_cmp.hip"],
+           "k_slc": ["long_context_sparse_phi_amd/csrc/nsa_attn.hip"],
+           "k_win": ["long_context_sparse_phi_amd/csrc/nsa_attn.hip"]}.get(kern, [])
+    return {"kernel": kern, "stage": name, "bound": "mfma", "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_for(kern, src) if src else None,
+            "launch_ms": round(stage_ms[i], 4), "algorithmic_flops_per_launch": work[name]}
+
+
+# ---------------------------------------------------------------- CPU oracle leg
+
+class _SampledRows:
+    """q holding only the sampled positions, indexed by absolute position."""
+
+    def __init__(self, data, rows, T):
+        self.data = data
+        self.pos = {int(t): i for i, t in enumerate(rows)}
+        self.shape = (data.shape[0], T) + tuple(data.shape[2:])
+
+    def __getitem__(self, idx):
+        b, t = idx
+        return self.data[b, self.pos[int(t)]]
+
+
+def cpu_baseline(wname="prefill_64k", nrows=192):
+    """fp64 oracle on a bounded sample of the workload: the compression of the
+    whole sequence plus `nrows` query positions spread evenly over [0, T);
+    tokens/s = T / (t_compress + t_rows * T / nrows)."""
+    import numpy as np
+    import torch
+    import nsa_inputs as NI
+    import oracle as O
+
+    w = NI.workload(wname)
+    cores = len(os.sched_getaffinity(0))
+    torch.set_num_threads(cores)
+    inp = NI.make_prefill_inputs(w, 0)
+    rows = np.linspace(0, w.T - 1, nrows).astype(np.int64)
+    a = {"q": inp["q"][:, rows].double().numpy(), "k": inp["k"].double().numpy(),
+         "v": inp["v"].double().numpy(), "x": inp["x"].double().numpy(), "w_gate": inp["w_gate"].double().numpy(),
+         "phi_k": NI.to_numpy64(inp["phi_k"]), "phi_v": NI.to_numpy64(inp["phi_v"])}
+    del inp
+    p = O.Params(l=w.l, d=w.d, l_sel=w.l_sel, n=w.n, w=w.w, phi=w.phi, io="bf16")
+    t0 = time.perf_counter()
+    kc = O.compress(a["k"], a["phi_k"], p)
+    vc = O.compress(a["v"], a["phi_v"], p)
+    t_cmp = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.forward(p, _SampledRows(a["q"], rows, w.T), a["k"], a["v"], a["x"], a["w_gate"], a["phi_k"], a["phi_v"],
+              rows=rows, kc=kc, vc=vc)
+    t_rows = time.perf_counter() - t0
+    est = t_cmp + t_rows * w.T / nrows
+    return {"value": round(w.B * w.T / est, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{wname}: phi compression of all {kc.shape[1]} blocks ({t_cmp:.1f} s) + {nrows} query "
+                      f"rows evenly spaced over [0,{w.T}) ({t_rows:.1f} s), scaled to {w.T} rows"}
+
+
+# ---------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="prefill_64k")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this NSA build runs on exactly one GPU; multi-GPU runs are not supported",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    w, wall, stage_ms, gpu_ms = run_prefill(args.steps, args.warmup, args.workload)
+    ms_per_step = wall * 1e3 / args.steps
+    fl = useful_flops(w)
+    useful = fl["cmp"] + fl["slc"] + fl["win"] + fl["phi"] + fl["gate"]
+    out = {
+        "metric": METRIC,
+        "value": round(w.B * w.T / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "B": w.B, "T": w.T, "H_kv": w.H_kv, "G": w.G, "d_k": w.d_k,
+                   "d_v": w.d_v, "l": w.l, "d": w.d, "l_sel": w.l_sel, "n": w.n, "w": w.w, "phi": w.phi},
+        "gpu_ms_per_step": round(gpu_ms, 4),
+        "useful_tflop_per_step": round(useful / 1e12, 4),
+        "mfma_frac_useful": round(useful / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "stages_ms": {name: round(ms, 4) for (name, _), ms in zip(PREFILL_STAGES, stage_ms)},
+        "roofline": prefill_roofline(w, stage_ms),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on a sample")
+        out["cpu_baseline"] = cpu_baseline(args.workload)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

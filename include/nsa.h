@@ -172,6 +172,28 @@ nsa_status nsa_fwd_decode(const nsa_params* p, const nsa_decode_args* a, void* w
 nsa_status nsa_bwd(const nsa_params* p, const nsa_bwd_args* a, void* ws,
                    size_t ws_bytes, void* stream);
 
+/* Timed variants, for measurement.  Identical work to the entry points
+ * above; in addition hipEventRecord(events[i], stream) is issued before stage
+ * i and events[n_stages] after the last stage, so that
+ * hipEventElapsedTime(events[i], events[i+1]) is the duration of stage i.
+ * `events` holds n_events hipEvent_t created by the caller; n_events must be
+ * at least the stage count + 1 (NSA_ERR_INVALID_ARG otherwise).
+ * Prefill stages (8): 0 gates, 1 compress K, 2 compress V, 3 transpose V,
+ *   4 compressed log-sum-exp, 5 compressed output + scores + top-n,
+ *   6 selected attention, 7 window attention + gated combine.
+ * Decode stages (3): 0 compressed partials + gates, 1 combine + top-n,
+ *   2 selected/window attention + merge.
+ * Backward stages: see nsa_bwd_stage_count(). */
+int nsa_prefill_stage_count(void);
+int nsa_decode_stage_count(void);
+int nsa_bwd_stage_count(void);
+nsa_status nsa_fwd_prefill_timed(const nsa_params* p, const nsa_prefill_args* a, void* ws,
+                                 size_t ws_bytes, void* stream, void* const* events, int n_events);
+nsa_status nsa_fwd_decode_timed(const nsa_params* p, const nsa_decode_args* a, void* ws,
+                                size_t ws_bytes, void* stream, void* const* events, int n_events);
+nsa_status nsa_bwd_timed(const nsa_params* p, const nsa_bwd_args* a, void* ws, size_t ws_bytes,
+                         void* stream, void* const* events, int n_events);
+
 #ifdef __cplusplus
 }
 #endif

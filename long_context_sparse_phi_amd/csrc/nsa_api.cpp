@@ -11,10 +11,14 @@
 #include "nsa_kernels.hpp"
 
 namespace nsa {
+constexpr int kPrefillStages = 8;
+constexpr int kDecodeStages = 3;
+int bwd_stage_count();
 bool cmp_out_fits(const Dims& dm);
-hipError_t launch_decode(const Dims& dm, const nsa_decode_args* a, void* ws, hipStream_t s);
+hipError_t launch_decode(const Dims& dm, const nsa_decode_args* a, void* ws, hipStream_t s,
+                         void* const* events);
 size_t decode_ws_bytes(const Dims& dm);
-hipError_t launch_bwd(const Dims& dm, const nsa_bwd_args* a, void* ws, hipStream_t s);
+hipError_t launch_bwd(const Dims& dm, const nsa_bwd_args* a, void* ws, hipStream_t s, void* const* events);
 size_t bwd_ws_bytes(const Dims& dm);
 }  // namespace nsa
 
@@ -145,6 +149,16 @@ hipError_t run_compress(const Dims& dm, int D, const void* x, const nsa_phi_weig
   return launch_phi_mlp(dm, a, s);
 }
 
+// Records caller-provided events between stages (no-op without events).
+struct Stages {
+  void* const* ev;
+  hipStream_t s;
+  int i = 0;
+  Stages(void* const* e, hipStream_t st) : ev(e), s(st) {}
+  // true on failure
+  bool mark() { return ev ? hipEventRecord((hipEvent_t)ev[i++], s) != hipSuccess : false; }
+};
+
 bool phi_ok(const nsa_phi_weights& w) {
   const void* ps[5] = {w.pe, w.w1, w.b1, w.w2, w.b2};
   for (const void* p : ps)
@@ -208,13 +222,14 @@ nsa_status nsa_compress(const nsa_params* p, int is_value, const void* x, const 
   }
 }
 
-nsa_status nsa_fwd_prefill(const nsa_params* p, const nsa_prefill_args* a, void* ws, size_t ws_bytes,
-                           void* stream) {
+static nsa_status prefill_impl(const nsa_params* p, const nsa_prefill_args* a, void* ws, size_t ws_bytes,
+                               void* stream, void* const* events, int n_events) {
   try {
     Dims dm;
     nsa_status st = make_dims(p, &dm);
     if (st != NSA_OK) return st;
     if (!a) return NSA_ERR_INVALID_ARG;
+    if (events && n_events < kPrefillStages + 1) return NSA_ERR_INVALID_ARG;
     const void* req[] = {a->q, a->k, a->v, a->x, a->w_gate, a->o};
     for (const void* r : req)
       if (!r || !aligned16(r)) return NSA_ERR_INVALID_ARG;
@@ -228,6 +243,7 @@ nsa_status nsa_fwd_prefill(const nsa_params* p, const nsa_prefill_args* a, void*
     if ((st = check_device()) != NSA_OK) return st;
     plan_prefill(dm, ws, &w);
     hipStream_t s = (hipStream_t)stream;
+    Stages sg(events, s);
     const size_t BTH = (size_t)dm.B * dm.T * dm.Hq;
     const size_t es = esize(dm);
     float* gates = a->gates ? (float*)a->gates : (float*)w.gates;
@@ -239,36 +255,54 @@ nsa_status nsa_fwd_prefill(const nsa_params* p, const nsa_prefill_args* a, void*
     void* o_cmp = ob;
     void* o_slc = ob + BTH * dm.dv * es;
     void* o_win = a->o_branch ? ob + 2 * BTH * dm.dv * es : nullptr;
-    hipError_t e;
-    if ((e = launch_gate(dm, dm.B * dm.T, a->x, a->w_gate, gates, s)) != hipSuccess) return NSA_ERR_HIP;
-    if ((e = run_compress(dm, dm.dk, a->k, &a->phi_k, kc, nullptr, w.phi, s)) != hipSuccess) return NSA_ERR_HIP;
-    if ((e = run_compress(dm, dm.dv, a->v, &a->phi_v, vc, w.vct, w.phi, s)) != hipSuccess) return NSA_ERR_HIP;
-    if ((e = launch_transpose_seq(dm, dm.B, dm.T, dm.Hkv, dm.dv, dm.Tp, a->v, w.vt, s)) != hipSuccess)
+    if (sg.mark() || launch_gate(dm, dm.B * dm.T, a->x, a->w_gate, gates, s) != hipSuccess) return NSA_ERR_HIP;
+    if (sg.mark() || run_compress(dm, dm.dk, a->k, &a->phi_k, kc, nullptr, w.phi, s) != hipSuccess)
+      return NSA_ERR_HIP;
+    if (sg.mark() || run_compress(dm, dm.dv, a->v, &a->phi_v, vc, w.vct, w.phi, s) != hipSuccess)
+      return NSA_ERR_HIP;
+    if (sg.mark() || launch_transpose_seq(dm, dm.B, dm.T, dm.Hkv, dm.dv, dm.Tp, a->v, w.vt, s) != hipSuccess)
       return NSA_ERR_HIP;
     CmpArgs ca;
     ca.q = a->q; ca.kc = kc; ca.vct = w.vct; ca.lse = lse; ca.o = o_cmp; ca.p_slc = (float*)a->p_slc; ca.idx = idx;
-    if ((e = launch_cmp_lse(dm, ca, s)) != hipSuccess) return NSA_ERR_HIP;
-    if ((e = launch_cmp_out_topn(dm, ca, s)) != hipSuccess) return NSA_ERR_HIP;
+    if (sg.mark() || launch_cmp_lse(dm, ca, s) != hipSuccess) return NSA_ERR_HIP;
+    if (sg.mark() || launch_cmp_out_topn(dm, ca, s) != hipSuccess) return NSA_ERR_HIP;
     SlcArgs sa;
     sa.q = a->q; sa.k = a->k; sa.vt = w.vt; sa.idx = idx; sa.o = o_slc; sa.lse = lse + BTH;
-    if ((e = launch_slc(dm, sa, s)) != hipSuccess) return NSA_ERR_HIP;
+    if (sg.mark() || launch_slc(dm, sa, s) != hipSuccess) return NSA_ERR_HIP;
     WinArgs wa;
     wa.q = a->q; wa.k = a->k; wa.vt = w.vt; wa.o_cmp = o_cmp; wa.o_slc = o_slc; wa.gates = gates;
     wa.o_win = o_win; wa.lse = lse + 2 * BTH; wa.o = a->o;
-    if ((e = launch_win_combine(dm, wa, s)) != hipSuccess) return NSA_ERR_HIP;
+    if (sg.mark() || launch_win_combine(dm, wa, s) != hipSuccess) return NSA_ERR_HIP;
+    if (sg.mark()) return NSA_ERR_HIP;
     return NSA_OK;
   } catch (...) {
     return NSA_ERR_INTERNAL;
   }
 }
 
-nsa_status nsa_fwd_decode(const nsa_params* p, const nsa_decode_args* a, void* ws, size_t ws_bytes,
-                          void* stream) {
+nsa_status nsa_fwd_prefill(const nsa_params* p, const nsa_prefill_args* a, void* ws, size_t ws_bytes,
+                           void* stream) {
+  return prefill_impl(p, a, ws, ws_bytes, stream, nullptr, 0);
+}
+
+nsa_status nsa_fwd_prefill_timed(const nsa_params* p, const nsa_prefill_args* a, void* ws, size_t ws_bytes,
+                                 void* stream, void* const* events, int n_events) {
+  if (!events) return NSA_ERR_INVALID_ARG;
+  return prefill_impl(p, a, ws, ws_bytes, stream, events, n_events);
+}
+
+int nsa_prefill_stage_count(void) { return kPrefillStages; }
+int nsa_decode_stage_count(void) { return kDecodeStages; }
+int nsa_bwd_stage_count(void) { return bwd_stage_count(); }
+
+static nsa_status decode_impl(const nsa_params* p, const nsa_decode_args* a, void* ws, size_t ws_bytes,
+                              void* stream, void* const* events, int n_events) {
   try {
     Dims dm;
     nsa_status st = make_dims(p, &dm);
     if (st != NSA_OK) return st;
     if (!a) return NSA_ERR_INVALID_ARG;
+    if (events && n_events < kDecodeStages + 1) return NSA_ERR_INVALID_ARG;
     const void* req[] = {a->q, a->k_cache, a->v_cache, a->x, a->w_gate, a->o};
     for (const void* r : req)
       if (!r || !aligned16(r)) return NSA_ERR_INVALID_ARG;
@@ -281,18 +315,31 @@ nsa_status nsa_fwd_decode(const nsa_params* p, const nsa_decode_args* a, void* w
     const size_t need = decode_ws_bytes(dm);
     if (ws_bytes < need || !ws || !aligned16(ws)) return NSA_ERR_WORKSPACE;
     if ((st = check_device()) != NSA_OK) return st;
-    return hip_status(launch_decode(dm, a, ws, (hipStream_t)stream));
+    return hip_status(launch_decode(dm, a, ws, (hipStream_t)stream, events));
   } catch (...) {
     return NSA_ERR_INTERNAL;
   }
 }
 
-nsa_status nsa_bwd(const nsa_params* p, const nsa_bwd_args* a, void* ws, size_t ws_bytes, void* stream) {
+nsa_status nsa_fwd_decode(const nsa_params* p, const nsa_decode_args* a, void* ws, size_t ws_bytes,
+                          void* stream) {
+  return decode_impl(p, a, ws, ws_bytes, stream, nullptr, 0);
+}
+
+nsa_status nsa_fwd_decode_timed(const nsa_params* p, const nsa_decode_args* a, void* ws, size_t ws_bytes,
+                                void* stream, void* const* events, int n_events) {
+  if (!events) return NSA_ERR_INVALID_ARG;
+  return decode_impl(p, a, ws, ws_bytes, stream, events, n_events);
+}
+
+static nsa_status bwd_impl(const nsa_params* p, const nsa_bwd_args* a, void* ws, size_t ws_bytes, void* stream,
+                           void* const* events, int n_events) {
   try {
     Dims dm;
     nsa_status st = make_dims(p, &dm);
     if (st != NSA_OK) return st;
     if (!a) return NSA_ERR_INVALID_ARG;
+    if (events && n_events < bwd_stage_count() + 1) return NSA_ERR_INVALID_ARG;
     const void* req[] = {a->q, a->k, a->v, a->x, a->w_gate, a->lse, a->idx, a->o_branch, a->d_o,
                          a->dq, a->dk, a->dv, a->dw_gate};
     for (const void* r : req)
@@ -309,10 +356,20 @@ nsa_status nsa_bwd(const nsa_params* p, const nsa_bwd_args* a, void* ws, size_t 
     const size_t need = bwd_ws_bytes(dm);
     if (ws_bytes < need || !ws || !aligned16(ws)) return NSA_ERR_WORKSPACE;
     if ((st = check_device()) != NSA_OK) return st;
-    return hip_status(launch_bwd(dm, a, ws, (hipStream_t)stream));
+    return hip_status(launch_bwd(dm, a, ws, (hipStream_t)stream, events));
   } catch (...) {
     return NSA_ERR_INTERNAL;
   }
+}
+
+nsa_status nsa_bwd(const nsa_params* p, const nsa_bwd_args* a, void* ws, size_t ws_bytes, void* stream) {
+  return bwd_impl(p, a, ws, ws_bytes, stream, nullptr, 0);
+}
+
+nsa_status nsa_bwd_timed(const nsa_params* p, const nsa_bwd_args* a, void* ws, size_t ws_bytes, void* stream,
+                         void* const* events, int n_events) {
+  if (!events) return NSA_ERR_INVALID_ARG;
+  return bwd_impl(p, a, ws, ws_bytes, stream, events, n_events);
 }
 
 }  // extern "C"

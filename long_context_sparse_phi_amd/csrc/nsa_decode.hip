@@ -5,8 +5,9 @@
 
 namespace nsa {
 size_t decode_ws_bytes(const Dims& dm) { (void)dm; return 0; }
-hipError_t launch_decode(const Dims& dm, const nsa_decode_args* a, void* ws, hipStream_t s) {
-  (void)dm; (void)a; (void)ws; (void)s;
+hipError_t launch_decode(const Dims& dm, const nsa_decode_args* a, void* ws, hipStream_t s,
+                         void* const* events) {
+  (void)dm; (void)a; (void)ws; (void)s; (void)events;
   return hipErrorNotSupported;
 }
 }  // namespace nsa
