@@ -181,8 +181,9 @@ nsa_status nsa_bwd(const nsa_params* p, const nsa_bwd_args* a, void* ws,
  * Prefill stages (8): 0 gates, 1 compress K, 2 compress V, 3 transpose V,
  *   4 compressed log-sum-exp, 5 compressed output + scores + top-n,
  *   6 selected attention, 7 window attention + gated combine.
- * Decode stages (3): 0 compressed partials + gates, 1 combine + top-n,
- *   2 selected/window attention + merge.
+ * Decode stages (3): 0 compressed-cache partial softmax states and scores,
+ *   1 combine + group scores + top-n + gates, 2 selected/window attention +
+ *   merge + gated combine.
  * Backward stages: see nsa_bwd_stage_count(). */
 int nsa_prefill_stage_count(void);
 int nsa_decode_stage_count(void);

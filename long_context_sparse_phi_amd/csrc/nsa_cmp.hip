@@ -105,14 +105,6 @@ __global__ __launch_bounds__(256) void k_cmp_lse(Dims dm, CmpArgs a) {
   }
 }
 
-// Weight of compression block (row kr of a 32-key tile) in selection block
-// (column jc of the tile's window), in units of d.
-__device__ __forceinline__ float remap_weight(int kr, int jc, int l, int d, int ls) {
-  const int a0 = kr * d, a1 = a0 + l, b0 = jc * ls, b1 = b0 + ls;
-  const int ov = min(a1, b1) - max(a0, b0);
-  return ov > 0 ? (float)(ov / d) : 0.f;
-}
-
 template <typename T, int DK, int DV, int NCT>
 __global__ __launch_bounds__(256) void k_cmp_out(Dims dm, CmpArgs a, int nselp, int njt) {
   extern __shared__ float smem[];
@@ -243,42 +235,12 @@ __global__ __launch_bounds__(256) void k_cmp_out(Dims dm, CmpArgs a, int nselp, 
     const int t = t0 + pl;
     if (t >= dm.T) break;
     float* row = prow + pl * nselp;
-    const int jc = t / dm.ls;
     const size_t rbase = (size_t)(b * dm.T + t) * dm.Hkv + g;
     if (a.p_slc) {
       float* ps = a.p_slc + rbase * dm.nsel;
       for (int j = lane; j < dm.nsel; j += 64) ps[j] = row[j];
     }
-    int* out = a.idx + rbase * n;
-    if (jc + 1 <= n) {
-      for (int e = lane; e < n; e += 64) out[e] = e <= jc ? e : -1;
-      continue;
-    }
-    if (lane == 0) { row[0] = -1.f; row[jc - 1] = -1.f; row[jc] = -1.f; }
-    for (int it = 0; it < n - 3; ++it) {
-      float bv = -2.f;
-      int bj = 0x7fffffff;
-      for (int j = lane; j <= jc; j += 64) {
-        const float v = row[j];
-        if (v > bv) { bv = v; bj = j; }
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oj = __shfl_xor(bj, off);
-        if (ov > bv || (ov == bv && oj < bj)) { bv = ov; bj = oj; }
-      }
-      if (lane == 0) row[bj] = -1.f;
-    }
-    int cnt = 0;
-    for (int jb = 0; jb <= jc; jb += 64) {
-      const int j = jb + lane;
-      const bool sel = j <= jc && row[j] < 0.f;
-      const uint64_t mk = __ballot(sel);
-      if (sel) out[cnt + __popcll(mk & ((1ull << lane) - 1ull))] = j;
-      cnt += __popcll(mk);
-    }
-    for (int e = cnt + lane; e < n; e += 64) out[e] = -1;
+    wave_topn(row, t, dm.ls, n, a.idx + rbase * n, lane);
   }
 }
 

@@ -139,4 +139,53 @@ __device__ __forceinline__ void xcd_map(int id, int units, int ntiles, int& unit
   }
 }
 
+// Weight of compression block kr (row of a 32-key tile) in selection block jc
+// (column of the tile's window), in units of d: the overlap of their token
+// ranges [kr*d, kr*d+l) and [jc*ls, (jc+1)*ls), divided by d.
+__device__ __forceinline__ float remap_weight(int kr, int jc, int l, int d, int ls) {
+  const int a0 = kr * d, a1 = a0 + l, b0 = jc * ls, b1 = b0 + ls;
+  const int ov = min(a1, b1) - max(a0, b0);
+  return ov > 0 ? (float)(ov / d) : 0.f;
+}
+
+// Top-n block selection for query position t from one group's score row
+// (LDS, nsel entries, scores >= 0), executed by one whole wave.  Block 0 and
+// blocks floor(t/ls) and floor(t/ls)-1 are always selected; the remaining
+// n-3 slots go to the highest scores among the other causal blocks
+// j <= floor(t/ls), the lower index winning a tie.  When at most n blocks
+// are causal all are selected.  Writes n indices ascending, -1 padded.  The
+// row is overwritten (selected entries marked -1).
+__device__ inline void wave_topn(float* row, int t, int ls, int n, int* out, int lane) {
+  const int jc = t / ls;
+  if (jc + 1 <= n) {
+    for (int e = lane; e < n; e += 64) out[e] = e <= jc ? e : -1;
+    return;
+  }
+  if (lane == 0) { row[0] = -1.f; row[jc - 1] = -1.f; row[jc] = -1.f; }
+  for (int it = 0; it < n - 3; ++it) {
+    float bv = -2.f;
+    int bj = 0x7fffffff;
+    for (int j = lane; j <= jc; j += 64) {
+      const float v = row[j];
+      if (v > bv) { bv = v; bj = j; }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oj = __shfl_xor(bj, off);
+      if (ov > bv || (ov == bv && oj < bj)) { bv = ov; bj = oj; }
+    }
+    if (lane == 0) row[bj] = -1.f;
+  }
+  int cnt = 0;
+  for (int jb = 0; jb <= jc; jb += 64) {
+    const int j = jb + lane;
+    const bool sel = j <= jc && row[j] < 0.f;
+    const uint64_t mk = __ballot(sel);
+    if (sel) out[cnt + __popcll(mk & ((1ull << lane) - 1ull))] = j;
+    cnt += __popcll(mk);
+  }
+  for (int e = cnt + lane; e < n; e += 64) out[e] = -1;
+}
+
 }  // namespace nsa
