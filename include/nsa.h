@@ -25,7 +25,7 @@
  * - Tensors are dense, row-major, in the order their shapes are written.
  *   Query head h belongs to KV head h / group_size.
  * - io_dtype (NSA_BF16 or NSA_FP32) is the element type of every input and
- *   of o / k_cmp / v_cmp / o_branch.  lse, p_slc, gates and all gradients are
+ *   of o / k_cmp / v_cmp.  o_branch, lse, p_slc, gates and all gradients are
  *   fp32; idx is int32.  Arithmetic accumulates in fp32.
  * - Calls enqueue work on `stream` (a hipStream_t; NULL = default stream)
  *   and return without synchronising.  Results are valid when the stream
@@ -69,7 +69,7 @@ typedef enum nsa_op { NSA_OP_FWD_PREFILL = 0, NSA_OP_FWD_DECODE = 1, NSA_OP_BWD 
  *   n_kv_heads H_kv; group_size G (query heads per KV head, H_q = H_kv*G,
  *   G in {1,2,4,8,16}); d_k, d_v head dims ((64,64), (128,128), (192,128));
  *   cmp_block l, cmp_stride d (d | l), sel_block l' (d | l', l <= l',
- *   l' | 32*d, 31*d + l <= 32*l'); n_select n (3 <= n <= 32);
+ *   16 | l', l' | 32*d, 31*d + l <= 32*l'); n_select n (3 <= n <= 32);
  *   window w >= 1; gate_dim C (gate input width); phi_hidden (MLP width,
  *   multiple of 64); phi (nsa_phi_kind); io_dtype (nsa_dtype);
  *   scale: 0 selects 1/sqrt(d_k). */
@@ -97,12 +97,12 @@ typedef struct nsa_phi_weights {
  *         cmp, slc, win), phi_k, phi_v.
  * Output: o [B,T,Hq,dv] (required).
  * Optional outputs (NULL = not written; the backward pass needs k_cmp,
- * v_cmp, lse, idx and o_branch):
+ * v_cmp, lse and idx):
  *   k_cmp [B,Ncmp,Hkv,dk], v_cmp [B,Ncmp,Hkv,dv] with Ncmp = (T-l)/d+1
  *     (0 when T < l), rounded to io_dtype;
  *   lse [3,B,T,Hq] fp32 log-sum-exp per branch (-inf for an empty set);
  *   idx [B,T,Hkv,n] int32 selected blocks, ascending, -1 padded;
- *   o_branch [3,B,T,Hq,dv] io_dtype per-branch outputs;
+ *   o_branch [3,B,T,Hq,dv] fp32 per-branch outputs;
  *   p_slc [B,T,Hkv,Nsel] fp32 group importance scores, Nsel = ceil(T/l');
  *   gates [B,T,Hq,3] fp32. */
 typedef struct nsa_prefill_args {
@@ -120,7 +120,7 @@ typedef struct nsa_prefill_args {
  *   first rows (cmp_cache_cap = Ncmp_cap >= Ncmp(S)), x [B,C], w_gate.
  * Output: o [B,Hq,dv] io_dtype.
  * Optional: idx [B,Hkv,n] int32, p_slc [B,Hkv,Nsel] fp32,
- *   lse [3,B,Hq] fp32, o_branch [3,B,Hq,dv] io_dtype. */
+ *   lse [3,B,Hq] fp32, o_branch [3,B,Hq,dv] fp32. */
 typedef struct nsa_decode_args {
   const void *q, *k_cache, *v_cache, *k_cmp_cache, *v_cmp_cache, *x, *w_gate;
   int32_t cmp_cache_cap;
@@ -130,8 +130,9 @@ typedef struct nsa_decode_args {
 
 /* Backward with the selected blocks held fixed (no gradient through the
  * scores or the selection).  Inputs as the prefill forward plus the forward's
- * saved k_cmp, v_cmp, lse, idx, o_branch and the upstream gradient
- * d_o [B,T,Hq,dv] (io_dtype).
+ * saved k_cmp, v_cmp, lse, idx and the upstream gradient d_o [B,T,Hq,dv]
+ * (io_dtype).  o_branch is not read (may be NULL): <dO, O_c> is recomputed
+ * from the probabilities.
  * Outputs (fp32, overwritten): dq [B,T,Hq,dk], dk [B,T,Hkv,dk],
  *   dv [B,T,Hkv,dv], dw_gate [C,Hq,3]; for NSA_PHI_MLP also d_phi_k and
  *   d_phi_v laid out like the phi weights (pe, w1, b1, w2, b2) in fp32. */
@@ -184,7 +185,9 @@ nsa_status nsa_bwd(const nsa_params* p, const nsa_bwd_args* a, void* ws,
  * Decode stages (3): 0 compressed-cache partial softmax states and scores,
  *   1 combine + group scores + top-n + gates, 2 selected/window attention +
  *   merge + gated combine.
- * Backward stages: see nsa_bwd_stage_count(). */
+ * Backward stages (8): 0 gates, 1 transposed copies of k, k_cmp, q, dO,
+ *   2 row terms <dO, O_c> + dq, 3 compressed-key dK/dV, 4 window-key dK/dV,
+ *   5 selected-block reverse index + dK/dV, 6 phi backward, 7 dW_g. */
 int nsa_prefill_stage_count(void);
 int nsa_decode_stage_count(void);
 int nsa_bwd_stage_count(void);

@@ -162,7 +162,7 @@ def nsa_fwd_prefill(cfg: Config, q, k, v, x, w_gate, phi_k=None, phi_v=None, *, 
         res["v_cmp"] = torch.empty(B, cfg.n_cmp, Hkv, cfg.d_v, dtype=dt, device=dev)
         res["lse"] = torch.empty(3, B, T, Hq, dtype=torch.float32, device=dev)
         res["idx"] = torch.empty(B, T, Hkv, cfg.n, dtype=torch.int32, device=dev)
-        res["o_branch"] = torch.empty(3, B, T, Hq, cfg.d_v, dtype=dt, device=dev)
+        res["o_branch"] = torch.empty(3, B, T, Hq, cfg.d_v, dtype=torch.float32, device=dev)
     if debug:
         res["p_slc"] = torch.empty(B, T, Hkv, cfg.n_sel, dtype=torch.float32, device=dev)
         res["gates"] = torch.empty(B, T, Hq, 3, dtype=torch.float32, device=dev)
@@ -202,7 +202,7 @@ def nsa_fwd_decode(cfg: Config, q, k_cache, v_cache, k_cmp_cache, v_cmp_cache, x
         res["idx"] = torch.empty(B, Hkv, cfg.n, dtype=torch.int32, device=dev)
         res["p_slc"] = torch.empty(B, Hkv, cfg.n_sel, dtype=torch.float32, device=dev)
         res["lse"] = torch.empty(3, B, Hq, dtype=torch.float32, device=dev)
-        res["o_branch"] = torch.empty(3, B, Hq, cfg.d_v, dtype=dt, device=dev)
+        res["o_branch"] = torch.empty(3, B, Hq, cfg.d_v, dtype=torch.float32, device=dev)
     a = _lib.nsa_decode_args()
     for name, t in (("q", q), ("k_cache", k_cache), ("v_cache", v_cache), ("x", x), ("w_gate", w_gate)):
         setattr(a, name, t.data_ptr())
@@ -237,7 +237,7 @@ def nsa_bwd(cfg: Config, q, k, v, x, w_gate, phi_k, phi_v, saved: Dict[str, torc
     a = _lib.nsa_bwd_args()
     for name, t in (("q", q), ("k", k), ("v", v), ("x", x), ("w_gate", w_gate), ("d_o", d_o)):
         setattr(a, name, t.data_ptr())
-    for name in ("k_cmp", "v_cmp", "lse", "idx", "o_branch"):
+    for name in ("k_cmp", "v_cmp", "lse", "idx"):
         t = saved[name]
         setattr(a, name, t.data_ptr() if t.numel() else None)
     a.phi_k = _phi_struct(cfg, phi_k, cfg.d_k, dev)

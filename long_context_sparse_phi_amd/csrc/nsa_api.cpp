@@ -71,7 +71,7 @@ nsa_status make_dims(const nsa_params* p, Dims* dm) {
   if (!shapes_supported(p->d_k, p->d_v)) return NSA_ERR_UNSUPPORTED;
   const int l = p->cmp_block, d = p->cmp_stride, ls = p->sel_block;
   if (l < 1 || d < 1 || ls < 1 || l % d != 0 || ls % d != 0 || l > ls) return NSA_ERR_INVALID_ARG;
-  if (ls % 8 != 0 || (32 * d) % ls != 0) return NSA_ERR_UNSUPPORTED;
+  if (ls % 16 != 0 || (32 * d) % ls != 0) return NSA_ERR_UNSUPPORTED;
   if ((31 * d + l - 1) / ls + 1 > 32) return NSA_ERR_UNSUPPORTED;
   if (p->n_select < 3 || p->n_select > 32) return NSA_ERR_INVALID_ARG;
   if (p->window < 1) return NSA_ERR_INVALID_ARG;
@@ -251,10 +251,13 @@ static nsa_status prefill_impl(const nsa_params* p, const nsa_prefill_args* a, v
     void* vc = a->v_cmp ? a->v_cmp : w.vc;
     float* lse = a->lse ? (float*)a->lse : (float*)w.lse;
     int* idx = a->idx ? (int*)a->idx : (int*)w.idx;
+    // branch outputs: fp32 when saved for the backward, else I/O type in the workspace
+    const int o_f32 = a->o_branch ? 1 : 0;
+    const size_t obs = o_f32 ? 4 : es;
     char* ob = a->o_branch ? (char*)a->o_branch : (char*)w.ob;
     void* o_cmp = ob;
-    void* o_slc = ob + BTH * dm.dv * es;
-    void* o_win = a->o_branch ? ob + 2 * BTH * dm.dv * es : nullptr;
+    void* o_slc = ob + BTH * dm.dv * obs;
+    void* o_win = a->o_branch ? ob + 2 * BTH * dm.dv * obs : nullptr;
     if (sg.mark() || launch_gate(dm, dm.B * dm.T, a->x, a->w_gate, gates, s) != hipSuccess) return NSA_ERR_HIP;
     if (sg.mark() || run_compress(dm, dm.dk, a->k, &a->phi_k, kc, nullptr, w.phi, s) != hipSuccess)
       return NSA_ERR_HIP;
@@ -264,14 +267,15 @@ static nsa_status prefill_impl(const nsa_params* p, const nsa_prefill_args* a, v
       return NSA_ERR_HIP;
     CmpArgs ca;
     ca.q = a->q; ca.kc = kc; ca.vct = w.vct; ca.lse = lse; ca.o = o_cmp; ca.p_slc = (float*)a->p_slc; ca.idx = idx;
+    ca.o_f32 = o_f32;
     if (sg.mark() || launch_cmp_lse(dm, ca, s) != hipSuccess) return NSA_ERR_HIP;
     if (sg.mark() || launch_cmp_out_topn(dm, ca, s) != hipSuccess) return NSA_ERR_HIP;
     SlcArgs sa;
-    sa.q = a->q; sa.k = a->k; sa.vt = w.vt; sa.idx = idx; sa.o = o_slc; sa.lse = lse + BTH;
+    sa.q = a->q; sa.k = a->k; sa.vt = w.vt; sa.idx = idx; sa.o = o_slc; sa.lse = lse + BTH; sa.o_f32 = o_f32;
     if (sg.mark() || launch_slc(dm, sa, s) != hipSuccess) return NSA_ERR_HIP;
     WinArgs wa;
     wa.q = a->q; wa.k = a->k; wa.vt = w.vt; wa.o_cmp = o_cmp; wa.o_slc = o_slc; wa.gates = gates;
-    wa.o_win = o_win; wa.lse = lse + 2 * BTH; wa.o = a->o;
+    wa.o_win = o_win; wa.lse = lse + 2 * BTH; wa.o = a->o; wa.o_f32 = o_f32;
     if (sg.mark() || launch_win_combine(dm, wa, s) != hipSuccess) return NSA_ERR_HIP;
     if (sg.mark()) return NSA_ERR_HIP;
     return NSA_OK;
@@ -340,7 +344,7 @@ static nsa_status bwd_impl(const nsa_params* p, const nsa_bwd_args* a, void* ws,
     if (st != NSA_OK) return st;
     if (!a) return NSA_ERR_INVALID_ARG;
     if (events && n_events < bwd_stage_count() + 1) return NSA_ERR_INVALID_ARG;
-    const void* req[] = {a->q, a->k, a->v, a->x, a->w_gate, a->lse, a->idx, a->o_branch, a->d_o,
+    const void* req[] = {a->q, a->k, a->v, a->x, a->w_gate, a->lse, a->idx, a->d_o,
                          a->dq, a->dk, a->dv, a->dw_gate};
     for (const void* r : req)
       if (!r || !aligned16(r)) return NSA_ERR_INVALID_ARG;

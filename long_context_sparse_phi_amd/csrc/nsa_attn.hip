@@ -20,7 +20,7 @@
 
 namespace nsa {
 
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, typename OT>
 __global__ __launch_bounds__(256) void k_slc(Dims dm, SlcArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, qd = lane >> 4;
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void k_slc(Dims dm, SlcArgs a) {
   tot += __shfl_xor(tot, 32);
   const float inv = 1.f / tot;
   if (cv) {
-    T* op = (T*)a.o + qrow * DV + qd * 4;
+    OT* op = (OT*)a.o + qrow * DV + qd * 4;
 #pragma unroll
     for (int dt = 0; dt < DV / 16; ++dt)
       store4(op + dt * 16, oacc[dt][0] * inv, oacc[dt][1] * inv, oacc[dt][2] * inv, oacc[dt][3] * inv);
@@ -104,23 +104,23 @@ __global__ __launch_bounds__(256) void k_slc(Dims dm, SlcArgs a) {
   }
 }
 
-hipError_t launch_slc(const Dims& dm, const SlcArgs& a, hipStream_t s) {
-  const int ntiles = (dm.T + 3) / 4;
-  dim3 grid(ntiles * dm.B * dm.Hkv);
-  const bool bf = dm.io == IO_BF16;
-  if (dm.dk == 64 && dm.dv == 64) {
-    if (bf) k_slc<bf16, 64, 64><<<grid, 256, 0, s>>>(dm, a); else k_slc<float, 64, 64><<<grid, 256, 0, s>>>(dm, a);
-  } else if (dm.dk == 128 && dm.dv == 128) {
-    if (bf) k_slc<bf16, 128, 128><<<grid, 256, 0, s>>>(dm, a); else k_slc<float, 128, 128><<<grid, 256, 0, s>>>(dm, a);
-  } else if (dm.dk == 192 && dm.dv == 128) {
-    if (bf) k_slc<bf16, 192, 128><<<grid, 256, 0, s>>>(dm, a); else k_slc<float, 192, 128><<<grid, 256, 0, s>>>(dm, a);
-  } else {
-    return hipErrorInvalidValue;
-  }
+template <typename T, int DK, int DV>
+static hipError_t slc_impl(const Dims& dm, const SlcArgs& a, hipStream_t s) {
+  dim3 grid(((dm.T + 3) / 4) * dm.B * dm.Hkv);
+  if (a.o_f32) k_slc<T, DK, DV, float><<<grid, 256, 0, s>>>(dm, a);
+  else k_slc<T, DK, DV, T><<<grid, 256, 0, s>>>(dm, a);
   return hipGetLastError();
 }
 
-template <typename T, int DK, int DV, int NCT>
+hipError_t launch_slc(const Dims& dm, const SlcArgs& a, hipStream_t s) {
+  const bool bf = dm.io == IO_BF16;
+  if (dm.dk == 64 && dm.dv == 64) return bf ? slc_impl<bf16, 64, 64>(dm, a, s) : slc_impl<float, 64, 64>(dm, a, s);
+  if (dm.dk == 128 && dm.dv == 128) return bf ? slc_impl<bf16, 128, 128>(dm, a, s) : slc_impl<float, 128, 128>(dm, a, s);
+  if (dm.dk == 192 && dm.dv == 128) return bf ? slc_impl<bf16, 192, 128>(dm, a, s) : slc_impl<float, 192, 128>(dm, a, s);
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int DK, int DV, int NCT, typename OT>
 __global__ __launch_bounds__(256) void k_win(Dims dm, WinArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, qd = lane >> 4;
@@ -222,10 +222,10 @@ __global__ __launch_bounds__(256) void k_win(Dims dm, WinArgs a) {
       for (int r = 0; r < 4; ++r) ow[r] = oacc[dt][ct][r] * inv;
       if (a.o_win) {
         // the stored branch output is what the combine uses
-        store4((T*)a.o_win + ob + dt * 16, ow[0], ow[1], ow[2], ow[3]);
+        store4((OT*)a.o_win + ob + dt * 16, ow[0], ow[1], ow[2], ow[3]);
       }
-      load4((const T*)a.o_cmp + ob + dt * 16, oc);
-      load4((const T*)a.o_slc + ob + dt * 16, os);
+      load4((const OT*)a.o_cmp + ob + dt * 16, oc);
+      load4((const OT*)a.o_slc + ob + dt * 16, os);
       store4((T*)a.o + ob + dt * 16, g0 * oc[0] + g1 * os[0] + g2 * ow[0], g0 * oc[1] + g1 * os[1] + g2 * ow[1],
              g0 * oc[2] + g1 * os[2] + g2 * ow[2], g0 * oc[3] + g1 * os[3] + g2 * ow[3]);
     }
@@ -237,7 +237,8 @@ static hipError_t win_impl(const Dims& dm, const WinArgs& a, hipStream_t s) {
   constexpr int NCT = 4;
   const int PWG = 4 * 16 * NCT / dm.G;
   const int ntiles = (dm.T + PWG - 1) / PWG;
-  k_win<T, DK, DV, NCT><<<ntiles * dm.B * dm.Hkv, 256, 0, s>>>(dm, a);
+  if (a.o_f32) k_win<T, DK, DV, NCT, float><<<ntiles * dm.B * dm.Hkv, 256, 0, s>>>(dm, a);
+  else k_win<T, DK, DV, NCT, T><<<ntiles * dm.B * dm.Hkv, 256, 0, s>>>(dm, a);
   return hipGetLastError();
 }
 

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void k_cmp_lse(Dims dm, CmpArgs a) {
   }
 }
 
-template <typename T, int DK, int DV, int NCT>
+template <typename T, int DK, int DV, int NCT, typename OT>
 __global__ __launch_bounds__(256) void k_cmp_out(Dims dm, CmpArgs a, int nselp, int njt) {
   extern __shared__ float smem[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -220,11 +220,11 @@ __global__ __launch_bounds__(256) void k_cmp_out(Dims dm, CmpArgs a, int nselp, 
     }
   }
   // O_cmp (rows with no visible block stay 0)
-  T* o = (T*)a.o;
+  OT* o = (OT*)a.o;
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
     if (pos[ct] >= dm.T) continue;
-    T* op = o + ((size_t)(b * dm.T + pos[ct]) * dm.Hq + hq[ct]) * DV + qd * 4;
+    OT* op = o + ((size_t)(b * dm.T + pos[ct]) * dm.Hq + hq[ct]) * DV + qd * 4;
 #pragma unroll
     for (int dt = 0; dt < DV / 16; ++dt)
       store4(op + dt * 16, oacc[dt][ct][0], oacc[dt][ct][1], oacc[dt][ct][2], oacc[dt][ct][3]);
@@ -282,11 +282,11 @@ static hipError_t cmp_out_impl(const Dims& dm, const CmpArgs& a, hipStream_t s) 
   const int PWG = 4 * 16 * nct / dm.G;
   const int ntiles = (dm.T + PWG - 1) / PWG;
   if (nct == 4) {
-    auto kfn = k_cmp_out<T, DK, DV, 4>;
+    auto kfn = a.o_f32 ? k_cmp_out<T, DK, DV, 4, float> : k_cmp_out<T, DK, DV, 4, T>;
     if (lds > 64 * 1024) hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     kfn<<<ntiles * dm.B * dm.Hkv, 256, lds, s>>>(dm, a, nselp, njt);
   } else {
-    auto kfn = k_cmp_out<T, DK, DV, 1>;
+    auto kfn = a.o_f32 ? k_cmp_out<T, DK, DV, 1, float> : k_cmp_out<T, DK, DV, 1, T>;
     if (lds > 64 * 1024) hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     kfn<<<ntiles * dm.B * dm.Hkv, 256, lds, s>>>(dm, a, nselp, njt);
   }

@@ -424,9 +424,9 @@ __global__ __launch_bounds__(256) void k_dec_merge(Dims dm, DecArgs a, DecPlan p
     ((T*)a.o)[row * dm.dv + e] = from_f32<T>(o);
     if (a.o_branch) {
       const size_t plane = (size_t)dm.B * dm.Hq * dm.dv;
-      ((T*)a.o_branch)[row * dm.dv + e] = from_f32<T>(oc);
-      ((T*)a.o_branch)[plane + row * dm.dv + e] = from_f32<T>(ob[0]);
-      ((T*)a.o_branch)[2 * plane + row * dm.dv + e] = from_f32<T>(ob[1]);
+      ((float*)a.o_branch)[row * dm.dv + e] = oc;
+      ((float*)a.o_branch)[plane + row * dm.dv + e] = ob[0];
+      ((float*)a.o_branch)[2 * plane + row * dm.dv + e] = ob[1];
     }
   }
 }

@@ -57,6 +57,9 @@ struct PhiMlpArgs {
   void* outT;            // optional [B,Hkv,D,ncmp_pad]
 };
 hipError_t launch_phi_mlp(const Dims& dm, const PhiMlpArgs& a, hipStream_t s);
+// First phi GEMM alone (sub-block products y, see nsa_phi.hip); w1t = w1 transposed.
+hipError_t launch_phi_gemm1(const Dims& dm, int D, int nsub, const void* x, const void* pe, const void* w1t,
+                            float* y, hipStream_t s);
 size_t phi_mlp_ws_bytes(const Dims& dm, int D);
 
 // ---- compressed attention ----
@@ -68,6 +71,7 @@ struct CmpArgs {
   void* o;          // [B,T,Hq,dv]
   float* p_slc;     // optional [B,T,Hkv,nsel]
   int* idx;         // [B,T,Hkv,n]
+  int o_f32;        // o is fp32 (saved for the backward) instead of the I/O type
 };
 hipError_t launch_cmp_lse(const Dims& dm, const CmpArgs& a, hipStream_t s);
 hipError_t launch_cmp_out_topn(const Dims& dm, const CmpArgs& a, hipStream_t s);
@@ -80,6 +84,7 @@ struct SlcArgs {
   const int* idx;   // [B,T,Hkv,n]
   void* o;          // [B,T,Hq,dv]
   float* lse;       // [B,T,Hq]
+  int o_f32;        // o is fp32 instead of the I/O type
 };
 hipError_t launch_slc(const Dims& dm, const SlcArgs& a, hipStream_t s);
 
@@ -94,6 +99,7 @@ struct WinArgs {
   void* o_win;         // optional [B,T,Hq,dv]
   float* lse;          // optional [B,T,Hq]
   void* o;             // [B,T,Hq,dv]
+  int o_f32;           // o_cmp / o_slc / o_win are fp32 instead of the I/O type
 };
 hipError_t launch_win_combine(const Dims& dm, const WinArgs& a, hipStream_t s);
 

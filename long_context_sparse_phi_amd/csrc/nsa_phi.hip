@@ -383,6 +383,27 @@ static hipError_t phi_mlp_impl(const Dims& dm, const PhiMlpArgs& a, hipStream_t 
   return hipSuccess;
 }
 
+template <typename T, int D>
+static hipError_t gemm1_impl(const Dims& dm, int nsub, const void* x, const void* pe, const void* w1t, float* y,
+                             hipStream_t s) {
+  const int R = dm.l / dm.d;
+  const int M = dm.B * dm.Hkv * nsub + R, N = R * dm.hidden;
+  dim3 grid(N / 64, (M + 63) / 64);
+  k_phi_gemm1<T, D><<<grid, 256, 0, s>>>(dm, nsub, (const T*)x, (const T*)pe, (const T*)w1t, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_phi_gemm1(const Dims& dm, int D, int nsub, const void* x, const void* pe, const void* w1t,
+                            float* y, hipStream_t s) {
+  const bool bf = dm.io == IO_BF16;
+  switch (D) {
+    case 64: return bf ? gemm1_impl<bf16, 64>(dm, nsub, x, pe, w1t, y, s) : gemm1_impl<float, 64>(dm, nsub, x, pe, w1t, y, s);
+    case 128: return bf ? gemm1_impl<bf16, 128>(dm, nsub, x, pe, w1t, y, s) : gemm1_impl<float, 128>(dm, nsub, x, pe, w1t, y, s);
+    case 192: return bf ? gemm1_impl<bf16, 192>(dm, nsub, x, pe, w1t, y, s) : gemm1_impl<float, 192>(dm, nsub, x, pe, w1t, y, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_phi_mlp(const Dims& dm, const PhiMlpArgs& a, hipStream_t s) {
   if (dm.ncmp == 0) return hipSuccess;
   const bool bf = dm.io == IO_BF16;
