@@ -5,9 +5,11 @@ with scores and top-n, selected attention, window attention and the gated
 combine) over the 64K-token workload (B=1, T=65536, 4 KV x 16 query heads,
 d_k=192, d_v=128, bf16), inputs resident in HBM.  The JSON line reports
 tokens/s for that step, the per-stage times measured with HIP events on the
-launch stream inside the timed region, the roofline of the dominant kernel,
-the decode and backward legs when available, and the fp64 CPU oracle timed
-on a bounded sample of the same workload.
+launch stream inside the timed region, and the roofline of the dominant
+kernel.  Two further legs are measured the same way: one decode step of 32
+sequences over a 64K cache (HBM GB/s, caches cold), and the backward pass of
+the 16K training shape (MFMA fraction).  The fp64 CPU oracle is timed on a
+bounded sample of the prefill workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -197,6 +199,193 @@ def prefill_roofline(w, stage_ms):
             "launch_ms": round(stage_ms[i], 4), "algorithmic_flops_per_launch": work[name]}
 
 
+# ---------------------------------------------------------------- decode leg
+
+DECODE_STAGES = [("cmp_partials", "k_dec_cmp"), ("combine_topn", "k_dec_combine"),
+                 ("sel_win_merge", "k_dec_sw")]
+
+
+def decode_bytes(w, idx):
+    """Algorithmic HBM bytes of one decode step: the compressed cache, the union
+    of selected-block and window tokens of every (sequence, KV head), q, o, x, W_g."""
+    import numpy as np
+    S = w.T
+    t = S - 1
+    ncmp = 0 if S < w.l else (S - w.l) // w.d + 1
+    row = (w.d_k + w.d_v) * 2
+    total = w.B * w.H_kv * ncmp * row
+    win = set(range(max(0, t - w.w + 1), t + 1))
+    for b in range(w.B):
+        for g in range(w.H_kv):
+            u = set(win)
+            for j in idx[b, g]:
+                if j >= 0:
+                    u.update(range(j * w.l_sel, min((j + 1) * w.l_sel, S)))
+            total += len(u) * row
+    total += w.B * w.H_q * (w.d_k + w.d_v) * 2 + w.B * w.gate_dim * 2 + w.gate_dim * w.H_q * 3 * 2
+    return int(total)
+
+
+def run_decode(steps, warmup, wname="decode_64k"):
+    import numpy as np
+    import torch
+    import long_context_sparse_phi_amd as nsa
+    from long_context_sparse_phi_amd import _lib
+    import nsa_inputs as NI
+
+    w = NI.workload(wname)
+    cfg = nsa.config_from_workload(w)
+    log(f"generating inputs for {wname}")
+    inp = NI.make_decode_inputs(w, 0)
+    dev = torch.device("cuda:0")
+    d = {k: ({kk: vv.to(dev) for kk, vv in v.items()} if isinstance(v, dict) else v.to(dev))
+         for k, v in inp.items()}
+    del inp
+    # compressed caches: phi over the raw caches (cache maintenance, untimed)
+    kc = nsa.nsa_compress(cfg, d["k_cache"], d["phi_k"], False)
+    vc = nsa.nsa_compress(cfg, d["v_cache"], d["phi_v"], True)
+    dbg = nsa.nsa_fwd_decode(cfg, d["q"], d["k_cache"], d["v_cache"], kc, vc, d["x"], d["w_gate"], debug=True)
+    torch.cuda.synchronize()
+    idx = dbg["idx"].cpu().numpy()
+    del dbg
+    o = torch.empty(w.B, w.H_q, w.d_v, dtype=cfg.torch_dtype, device=dev)
+    ws = torch.empty(nsa.workspace_size(cfg, _lib.NSA_OP_FWD_DECODE), dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)   # evicts L2 and the 256 MB MALL
+    lib = _lib.load()
+    lib.nsa_fwd_decode_timed.restype = ctypes.c_int
+    lib.nsa_fwd_decode_timed.argtypes = [ctypes.POINTER(_lib.nsa_params), ctypes.POINTER(_lib.nsa_decode_args),
+                                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                         ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+    p = cfg.params()
+    a = _lib.nsa_decode_args()
+    for name in ("q", "k_cache", "v_cache", "x", "w_gate"):
+        setattr(a, name, d[name].data_ptr())
+    a.k_cmp_cache, a.v_cmp_cache, a.cmp_cache_cap = kc.data_ptr(), vc.data_ptr(), kc.shape[1]
+    a.o = o.data_ptr()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    nst = len(DECODE_STAGES)
+    ev = HipEvents(lib)
+    events = [ev.create(nst + 1) for _ in range(steps)]
+
+    def step(evs=None):
+        flush.zero_()
+        if evs is None:
+            st = lib.nsa_fwd_decode(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(), stream)
+        else:
+            arr = (ctypes.c_void_p * len(evs))(*evs)
+            st = lib.nsa_fwd_decode_timed(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(), stream,
+                                          arr, len(evs))
+        if st != 0:
+            raise RuntimeError(f"nsa_fwd_decode failed: {_lib.status_str(st)}")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"decode timed {steps}")
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = [sum(ev.elapsed_ms(events[i][s], events[i][s + 1]) for i in range(steps)) / steps
+                for s in range(nst)]
+    step_ms = sum(ev.elapsed_ms(events[i][0], events[i][nst]) for i in range(steps)) / steps
+    nbytes = decode_bytes(w, idx)
+    ncmp = (w.T - w.l) // w.d + 1
+    cmp_bytes = w.B * w.H_kv * ncmp * (w.d_k + w.d_v) * 2 + w.B * w.H_q * w.d_k * 2
+    gbs = cmp_bytes / (stage_ms[0] * 1e-3) / 1e9
+    return {
+        "workload": wname, "B": w.B, "cache_len": w.T, "steps": steps, "warmup": warmup,
+        "us_per_step": round(step_ms * 1e3, 2), "wall_ms_incl_cache_flush": round(wall * 1e3 / steps, 3),
+        "algorithmic_bytes": nbytes, "GB_per_s": round(nbytes / (step_ms * 1e-3) / 1e9, 1),
+        "frac_hbm_peak": round(nbytes / (step_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "stages_us": {n: round(ms * 1e3, 2) for (n, _), ms in zip(DECODE_STAGES, stage_ms)},
+        "roofline": {"kernel": "k_dec_cmp", "stage": "cmp_partials", "bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_for("k_dec_cmp", ["long_context_sparse_phi_amd/csrc/nsa_decode.hip"]),
+                     "algorithmic_bytes_per_launch": cmp_bytes, "launch_us": round(stage_ms[0] * 1e3, 2)},
+        "cold_cache": "512 MB buffer written before every step (outside the timed events)",
+    }
+
+
+# ---------------------------------------------------------------- backward leg
+
+BWD_STAGES = ["gates", "transposes", "rowterms_dq", "cmp_dkdv", "win_dkdv", "slc_dkdv", "phi", "dw_gate"]
+
+
+def run_backward(steps, warmup, wname="train_16k"):
+    import torch
+    import long_context_sparse_phi_amd as nsa
+    from long_context_sparse_phi_amd import _lib
+    import nsa_inputs as NI
+
+    w = NI.workload(wname)
+    cfg = nsa.config_from_workload(w)
+    log(f"generating inputs for {wname}")
+    inp = NI.make_prefill_inputs(w, 0)
+    dev = torch.device("cuda:0")
+    d = {k: ({kk: vv.to(dev) for kk, vv in v.items()} if isinstance(v, dict) else v.to(dev))
+         for k, v in inp.items()}
+    d_o = NI.make_grad_output(w, 0).to(dev)
+    fwd = nsa.nsa_fwd_prefill(cfg, d["q"], d["k"], d["v"], d["x"], d["w_gate"], d["phi_k"], d["phi_v"],
+                              save_for_backward=True)
+    res = nsa.nsa_bwd(cfg, d["q"], d["k"], d["v"], d["x"], d["w_gate"], d["phi_k"], d["phi_v"], fwd, d_o)
+    torch.cuda.synchronize()
+    lib = _lib.load()
+    lib.nsa_bwd_timed.restype = ctypes.c_int
+    lib.nsa_bwd_timed.argtypes = [ctypes.POINTER(_lib.nsa_params), ctypes.POINTER(_lib.nsa_bwd_args),
+                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                  ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+    p = cfg.params()
+    a = _lib.nsa_bwd_args()
+    for name in ("q", "k", "v", "x", "w_gate"):
+        setattr(a, name, d[name].data_ptr())
+    a.d_o = d_o.data_ptr()
+    for name in ("k_cmp", "v_cmp", "lse", "idx"):
+        setattr(a, name, fwd[name].data_ptr())
+    a.phi_k = nsa._phi_struct(cfg, d["phi_k"], w.d_k, dev)
+    a.phi_v = nsa._phi_struct(cfg, d["phi_v"], w.d_v, dev)
+    for name in ("dq", "dk", "dv", "dw_gate"):
+        setattr(a, name, res[name].data_ptr())
+    a.d_phi_k = _lib.nsa_phi_grads(**{k: v.data_ptr() for k, v in res["d_phi_k"].items()})
+    a.d_phi_v = _lib.nsa_phi_grads(**{k: v.data_ptr() for k, v in res["d_phi_v"].items()})
+    ws = res["_workspace"]
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    nst = len(BWD_STAGES)
+    ev = HipEvents(lib)
+    events = [ev.create(nst + 1) for _ in range(steps)]
+
+    def step(evs=None):
+        if evs is None:
+            st = lib.nsa_bwd(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(), stream)
+        else:
+            arr = (ctypes.c_void_p * len(evs))(*evs)
+            st = lib.nsa_bwd_timed(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(), stream, arr,
+                                   len(evs))
+        if st != 0:
+            raise RuntimeError(f"nsa_bwd failed: {_lib.status_str(st)}")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"backward timed {steps}")
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = [sum(ev.elapsed_ms(events[i][s], events[i][s + 1]) for i in range(steps)) / steps
+                for s in range(nst)]
+    fl = useful_flops(w)
+    useful = 2 * (fl["cmp"] + fl["slc"] + fl["win"]) + 2 * fl["phi"] + fl["gate"]
+    ms = wall * 1e3 / steps
+    return {"workload": wname, "B": w.B, "T": w.T, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 4),
+            "useful_tflop_per_step": round(useful / 1e12, 4),
+            "tflops": round(useful / (ms * 1e-3) / 1e12, 2),
+            "mfma_frac_useful": round(useful / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "stages_ms": {n: round(x, 4) for n, x in zip(BWD_STAGES, stage_ms)}}
+
+
 # ---------------------------------------------------------------- CPU oracle leg
 
 class _SampledRows:
@@ -254,6 +443,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="prefill_64k")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--bwd-steps", type=int, default=5)
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this NSA build runs on exactly one GPU; multi-GPU runs are not supported",
@@ -280,6 +473,10 @@ def main():
         "stages_ms": {name: round(ms, 4) for (name, _), ms in zip(PREFILL_STAGES, stage_ms)},
         "roofline": prefill_roofline(w, stage_ms),
     }
+    if not args.no_decode:
+        out["decode"] = run_decode(args.decode_steps, 3)
+    if not args.no_backward:
+        out["backward"] = run_backward(args.bwd_steps, 2)
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(args.workload)

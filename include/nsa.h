@@ -62,7 +62,9 @@ typedef enum nsa_status {
 
 typedef enum nsa_dtype { NSA_BF16 = 0, NSA_FP32 = 1 } nsa_dtype;
 typedef enum nsa_phi_kind { NSA_PHI_MEANPOOL = 0, NSA_PHI_MLP = 1 } nsa_phi_kind;
-typedef enum nsa_op { NSA_OP_FWD_PREFILL = 0, NSA_OP_FWD_DECODE = 1, NSA_OP_BWD = 2 } nsa_op;
+typedef enum nsa_op {
+  NSA_OP_FWD_PREFILL = 0, NSA_OP_FWD_DECODE = 1, NSA_OP_BWD = 2, NSA_OP_COMPRESS = 3
+} nsa_op;
 
 /* Shapes and hyper-parameters.
  *   batch B; seqlen T (prefill/backward) or cache length S (decode);
@@ -160,8 +162,7 @@ nsa_status nsa_workspace_size(const nsa_params* p, nsa_op op, size_t* bytes);
 /* Compress a key or value sequence with phi, as the forward does internally:
  *   x [B,T,Hkv,D] -> out [B,Ncmp,Hkv,D] (io_dtype, Ncmp = (T-l)/d+1).
  * D must equal p->d_k (is_value = 0) or p->d_v (is_value = 1).  Used to
- * build or extend the compressed decode cache.  Workspace as for
- * NSA_OP_FWD_PREFILL. */
+ * build or extend the compressed decode cache.  Workspace: NSA_OP_COMPRESS. */
 nsa_status nsa_compress(const nsa_params* p, int is_value, const void* x,
                         const nsa_phi_weights* phi, void* out, void* ws,
                         size_t ws_bytes, void* stream);

@@ -16,7 +16,7 @@ from typing import Dict, Optional
 import torch
 
 from . import _lib
-from ._lib import (NSA_BF16, NSA_FP32, NSA_OP_BWD, NSA_OP_FWD_DECODE, NSA_OP_FWD_PREFILL,
+from ._lib import (NSA_BF16, NSA_FP32, NSA_OP_BWD, NSA_OP_COMPRESS, NSA_OP_FWD_DECODE, NSA_OP_FWD_PREFILL,
                    NSA_PHI_MEANPOOL, NSA_PHI_MLP, NSAError)
 
 __all__ = ["Config", "workspace_size", "nsa_compress", "nsa_fwd_prefill", "nsa_fwd_decode",
@@ -131,7 +131,7 @@ def nsa_compress(cfg: Config, x: torch.Tensor, phi: Optional[Dict[str, torch.Ten
     if out is None:
         out = torch.empty(cfg.B, cfg.n_cmp, cfg.H_kv, D, dtype=cfg.torch_dtype, device=dev)
     _check(out, "out", (cfg.B, cfg.n_cmp, cfg.H_kv, D), cfg.torch_dtype, dev)
-    ws = _workspace(cfg, NSA_OP_FWD_PREFILL, dev, workspace)
+    ws = _workspace(cfg, NSA_OP_COMPRESS, dev, workspace)
     p = cfg.params()
     w = _phi_struct(cfg, phi, D, dev)
     st = _lib.load().nsa_compress(ctypes.byref(p), int(is_value), x.data_ptr(), ctypes.byref(w),

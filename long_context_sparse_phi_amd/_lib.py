@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(_PKG, "libnsa.so")
 NSA_OK, NSA_ERR_INVALID_ARG, NSA_ERR_UNSUPPORTED, NSA_ERR_WORKSPACE, NSA_ERR_HIP, NSA_ERR_INTERNAL = range(6)
 NSA_BF16, NSA_FP32 = 0, 1
 NSA_PHI_MEANPOOL, NSA_PHI_MLP = 0, 1
-NSA_OP_FWD_PREFILL, NSA_OP_FWD_DECODE, NSA_OP_BWD = 0, 1, 2
+NSA_OP_FWD_PREFILL, NSA_OP_FWD_DECODE, NSA_OP_BWD, NSA_OP_COMPRESS = 0, 1, 2, 3
 ABI_VERSION = 1
 
 _vp = ctypes.c_void_p

@@ -195,6 +195,7 @@ nsa_status nsa_workspace_size(const nsa_params* p, nsa_op op, size_t* bytes) {
       case NSA_OP_FWD_PREFILL: *bytes = plan_prefill(dm, nullptr, &w); return NSA_OK;
       case NSA_OP_FWD_DECODE: *bytes = decode_ws_bytes(dm); return NSA_OK;
       case NSA_OP_BWD: *bytes = bwd_ws_bytes(dm); return NSA_OK;
+      case NSA_OP_COMPRESS: *bytes = phi_ws(dm) > 0 ? phi_ws(dm) : 256; return NSA_OK;
     }
     return NSA_ERR_INVALID_ARG;
   } catch (...) {
@@ -210,13 +211,11 @@ nsa_status nsa_compress(const nsa_params* p, int is_value, const void* x, const 
     if (st != NSA_OK) return st;
     if (!x || !out || !aligned16(x) || !aligned16(out)) return NSA_ERR_INVALID_ARG;
     if (dm.hidden && (!phi || !phi_ok(*phi))) return NSA_ERR_INVALID_ARG;
-    PrefillWs w;
-    const size_t need = plan_prefill(dm, nullptr, &w);
+    const size_t need = phi_ws(dm);
     if (ws_bytes < need || (need && !ws) || !aligned16(ws)) return NSA_ERR_WORKSPACE;
     if ((st = check_device()) != NSA_OK) return st;
-    plan_prefill(dm, ws, &w);
     const int D = is_value ? dm.dv : dm.dk;
-    return hip_status(run_compress(dm, D, x, phi, out, nullptr, w.phi, (hipStream_t)stream));
+    return hip_status(run_compress(dm, D, x, phi, out, nullptr, ws, (hipStream_t)stream));
   } catch (...) {
     return NSA_ERR_INTERNAL;
   }
