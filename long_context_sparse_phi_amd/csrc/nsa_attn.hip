@@ -17,6 +17,7 @@
 // from a transposed copy of V ([B, Hkv, dv, Tp]).
 #include "nsa_common.hpp"
 #include "nsa_kernels.hpp"
+#include "nsa_tiles.hpp"
 
 namespace nsa {
 
@@ -74,8 +75,8 @@ __global__ __launch_bounds__(256) void k_slc(Dims dm, SlcArgs a) {
         v[e] = key < kend ? s[e >> 2][e & 3] * sc2 : kNegInf;
         mx = fmaxf(mx, v[e]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = fmaxf(mx, xor16f(mx, lane));
+      mx = fmaxf(mx, xor32f(mx, lane));
       const float mn = fmaxf(m, mx);
       const float mref = mn == kNegInf ? 0.f : mn;
       const float alpha = fast_exp2(m - mref);
@@ -92,8 +93,8 @@ __global__ __launch_bounds__(256) void k_slc(Dims dm, SlcArgs a) {
       }
     }
   }
-  float tot = ls + __shfl_xor(ls, 16);
-  tot += __shfl_xor(tot, 32);
+  float tot = ls + xor16f(ls, lane);
+  tot += xor32f(tot, lane);
   const float inv = 1.f / tot;
   if (cv) {
     OT* op = (OT*)a.o + qrow * DV + qd * 4;
@@ -122,6 +123,9 @@ hipError_t launch_slc(const Dims& dm, const SlcArgs& a, hipStream_t s) {
 
 template <typename T, int DK, int DV, int NCT, typename OT>
 __global__ __launch_bounds__(256) void k_win(Dims dm, WinArgs a) {
+  using Tile = KVTile<T, DK, DV, true>;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* tiles = (T*)smem_raw;                              // [2][Tile::elems]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, qd = lane >> 4;
   const int G = dm.G, PW = 16 * NCT / G, PWG = 4 * PW;
@@ -129,8 +133,9 @@ __global__ __launch_bounds__(256) void k_win(Dims dm, WinArgs a) {
   int unit, tile;
   xcd_map(blockIdx.x, dm.B * dm.Hkv, ntiles, unit, tile);
   const int b = unit / dm.Hkv, g = unit % dm.Hkv;
-  const int t0 = tile * PWG + wave * PW;
-  if (t0 >= dm.T) return;
+  const int twg = tile * PWG;
+  const int t0 = twg + wave * PW;
+  const bool wave_live = t0 < dm.T;
   const int tl = min(dm.T - 1, t0 + PW - 1);
   Frag8<T> qf[NCT][DK / 32];
   int pos[NCT], hq[NCT];
@@ -155,60 +160,77 @@ __global__ __launch_bounds__(256) void k_win(Dims dm, WinArgs a) {
     for (int dt = 0; dt < DV / 16; ++dt) oacc[dt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const size_t kstride = (size_t)dm.Hkv * DK;
-  const T* kbase = (const T*)a.k + ((size_t)b * dm.T * dm.Hkv + g) * DK + qd * 8;
-  const T* vtb = (const T*)a.vt + (size_t)(b * dm.Hkv + g) * DV * dm.Tp + qd * 8;
+  const T* kbase = (const T*)a.k + ((size_t)b * dm.T * dm.Hkv + g) * DK;
+  const T* vtb = (const T*)a.vt + (size_t)(b * dm.Hkv + g) * DV * dm.Tp;
   const int krow = (c16 >> 2) * 8 + (c16 & 3);
-  const int kstart = max(0, t0 - dm.w + 1) & ~31;
-  for (int kt = kstart; kt <= tl; kt += 32) {
-    f32x4 s[2][NCT];
+  // keys of the workgroup's band, in 64-key tiles; each wave computes the 32-key halves of its own band
+  const int kwg0 = max(0, twg - dm.w + 1) & ~63;
+  const int kwg1 = min(dm.T - 1, twg + PWG - 1);
+  const int nkt = (kwg1 - kwg0) / kTileKeys + 1;
+  const int klo = wave_live ? (max(0, t0 - dm.w + 1) & ~31) : 0x7fffffff;
+  const int khi = wave_live ? tl : -1;
+  Tile ld;
+  ld.gload(kbase, kstride, dm.T, vtb, dm.Tp, kwg0);
+  ld.lstore(tiles);
+  __syncthreads();
+  for (int it = 0; it < nkt; ++it) {
+    const int kt0 = kwg0 + it * kTileKeys;
+    if (it + 1 < nkt) ld.gload(kbase, kstride, dm.T, vtb, dm.Tp, kt0 + kTileKeys);
+    const T* tl_ = tiles + (size_t)(it & 1) * Tile::elems;
+    for (int h = 0; h < 2; ++h) {
+      const int kt = kt0 + h * 32;
+      if (kt + 31 < klo || kt > khi) continue;
+      f32x4 s[2][NCT];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+      for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) s[sub][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int key = min(kt + krow + sub * 4, dm.T - 1);
-      const T* kp = kbase + (size_t)key * kstride;
+        for (int ct = 0; ct < NCT; ++ct) s[sub][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < DK / 32; ++ks) {
-        Frag8<T> kf = load_frag(kp + ks * 32);
+        for (int ks = 0; ks < DK / 32; ++ks) {
+          const Frag8<T> kf = Tile::kfrag(tl_, h * 32 + krow + sub * 4, ks, qd);
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) mma(s[sub][ct], kf, qf[ct][ks]);
+          for (int ct = 0; ct < NCT; ++ct) mma(s[sub][ct], kf, qf[ct][ks]);
+        }
+      }
+      Frag8<T> vf[DV / 16];
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt) vf[dt] = Tile::vfrag(tl_, dt * 16 + c16, h * 32, qd);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        float v[8], mx = kNegInf;
+        const int lo = pos[ct] - dm.w + 1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = kt + qd * 8 + e;
+          v[e] = (key >= lo && key <= pos[ct]) ? s[e >> 2][ct][e & 3] * sc2 : kNegInf;
+          mx = fmaxf(mx, v[e]);
+        }
+        mx = fmaxf(mx, xor16f(mx, lane));
+        mx = fmaxf(mx, xor32f(mx, lane));
+        const float mn = fmaxf(m[ct], mx);
+        const float mref = mn == kNegInf ? 0.f : mn;
+        const float alpha = fast_exp2(m[ct] - mref);
+        float p[8], psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { p[e] = fast_exp2(v[e] - mref); psum += p[e]; }
+        ls[ct] = ls[ct] * alpha + psum;
+        m[ct] = mn;
+        const Frag8<T> pf = to_frag<T>(p);
+#pragma unroll
+        for (int dt = 0; dt < DV / 16; ++dt) {
+          oacc[dt][ct] *= alpha;
+          mma(oacc[dt][ct], vf[dt], pf);
+        }
       }
     }
-    Frag8<T> vf[DV / 16];
-#pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt) vf[dt] = load_frag(vtb + (size_t)(dt * 16 + c16) * dm.Tp + kt);
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      float v[8], mx = kNegInf;
-      const int lo = pos[ct] - dm.w + 1;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = kt + qd * 8 + e;
-        v[e] = (key >= lo && key <= pos[ct]) ? s[e >> 2][ct][e & 3] * sc2 : kNegInf;
-        mx = fmaxf(mx, v[e]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(m[ct], mx);
-      const float mref = mn == kNegInf ? 0.f : mn;
-      const float alpha = fast_exp2(m[ct] - mref);
-      float p[8], psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { p[e] = fast_exp2(v[e] - mref); psum += p[e]; }
-      ls[ct] = ls[ct] * alpha + psum;
-      m[ct] = mn;
-      Frag8<T> pf = to_frag<T>(p);
-#pragma unroll
-      for (int dt = 0; dt < DV / 16; ++dt) {
-        oacc[dt][ct] *= alpha;
-        mma(oacc[dt][ct], vf[dt], pf);
-      }
-    }
+    if (it + 1 < nkt) ld.lstore(tiles + (size_t)((it + 1) & 1) * Tile::elems);
+    __syncthreads();
   }
+  if (!wave_live) return;
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
-    float tot = ls[ct] + __shfl_xor(ls[ct], 16);
-    tot += __shfl_xor(tot, 32);
+    float tot = ls[ct] + xor16f(ls[ct], lane);
+    tot += xor32f(tot, lane);
     if (pos[ct] >= dm.T) continue;
     const float inv = 1.f / tot;
     const size_t row = (size_t)(b * dm.T + pos[ct]) * dm.Hq + hq[ct];
@@ -220,10 +242,7 @@ __global__ __launch_bounds__(256) void k_win(Dims dm, WinArgs a) {
       float ow[4], oc[4], os[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) ow[r] = oacc[dt][ct][r] * inv;
-      if (a.o_win) {
-        // the stored branch output is what the combine uses
-        store4((OT*)a.o_win + ob + dt * 16, ow[0], ow[1], ow[2], ow[3]);
-      }
+      if (a.o_win) store4((OT*)a.o_win + ob + dt * 16, ow[0], ow[1], ow[2], ow[3]);
       load4((const OT*)a.o_cmp + ob + dt * 16, oc);
       load4((const OT*)a.o_slc + ob + dt * 16, os);
       store4((T*)a.o + ob + dt * 16, g0 * oc[0] + g1 * os[0] + g2 * ow[0], g0 * oc[1] + g1 * os[1] + g2 * ow[1],
@@ -237,8 +256,10 @@ static hipError_t win_impl(const Dims& dm, const WinArgs& a, hipStream_t s) {
   constexpr int NCT = 4;
   const int PWG = 4 * 16 * NCT / dm.G;
   const int ntiles = (dm.T + PWG - 1) / PWG;
-  if (a.o_f32) k_win<T, DK, DV, NCT, float><<<ntiles * dm.B * dm.Hkv, 256, 0, s>>>(dm, a);
-  else k_win<T, DK, DV, NCT, T><<<ntiles * dm.B * dm.Hkv, 256, 0, s>>>(dm, a);
+  const size_t lds = 2 * KVTile<T, DK, DV, true>::elems * sizeof(T);
+  auto kfn = a.o_f32 ? k_win<T, DK, DV, NCT, float> : k_win<T, DK, DV, NCT, T>;
+  if (lds > 64 * 1024) hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  kfn<<<ntiles * dm.B * dm.Hkv, 256, lds, s>>>(dm, a);
   return hipGetLastError();
 }
 

@@ -292,8 +292,8 @@ __global__ __launch_bounds__(256) void k_bwd_dq(Dims dm, BwdArgs a) {
   if (ROWSUM) {
 #pragma unroll
     for (int c = 0; c < 3; ++c) {
-      float v = rsum[c] + __shfl_xor(rsum[c], 16);
-      v += __shfl_xor(v, 32);
+      float v = rsum[c] + xor16f(rsum[c], lane);
+      v += xor32f(v, lane);
       if (cv && qd == 0) {
         a.w.Dc[c * BTH + row] = gc[c] * v;
         a.w.dz[row * 3 + c] = v * gc[c] * (1.f - gc[c]);

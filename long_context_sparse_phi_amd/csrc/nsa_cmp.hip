@@ -27,87 +27,29 @@
 
 namespace nsa {
 
-template <typename T, int DK, int NCT>
-__global__ __launch_bounds__(256) void k_cmp_lse(Dims dm, CmpArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c16 = lane & 15, qd = lane >> 4;
-  const int G = dm.G, PW = 16 * NCT / G, PWG = 4 * PW;
-  const int ntiles = (dm.T + PWG - 1) / PWG;
-  int unit, tile;
-  xcd_map(blockIdx.x, dm.B * dm.Hkv, ntiles, unit, tile);
-  const int b = unit / dm.Hkv, g = unit % dm.Hkv;
-  const int t0 = tile * PWG + wave * PW;
-  if (t0 >= dm.T) return;
-  const int tl = min(dm.T - 1, t0 + PW - 1);
-  const int nmax = ncmp_visible(tl, dm.l, dm.d);
-  const T* q = (const T*)a.q;
-  Frag8<T> qf[NCT][DK / 32];
-  int pos[NCT], hq[NCT], nvis[NCT];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const int col = ct * 16 + c16;
-    pos[ct] = t0 + col / G;
-    hq[ct] = g * G + col % G;
-    const bool v = pos[ct] < dm.T;
-    nvis[ct] = v ? ncmp_visible(pos[ct], dm.l, dm.d) : 0;
-    const T* qp = q + ((size_t)(b * dm.T + min(pos[ct], dm.T - 1)) * dm.Hq + hq[ct]) * DK + qd * 8;
-#pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) qf[ct][ks] = v ? load_frag(qp + ks * 32) : zero_frag<T>();
-  }
-  const float sc2 = dm.scale * kLog2e;
-  float m[NCT], ls[NCT];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) { m[ct] = kNegInf; ls[ct] = 0.f; }
-  const size_t kstride = (size_t)dm.Hkv * DK;
-  const T* kbase = (const T*)a.kc + ((size_t)b * dm.ncmp * dm.Hkv + g) * DK + qd * 8;
-  const int krow = (c16 >> 2) * 8 + (c16 & 3);
-  for (int kt = 0; kt < nmax; kt += 32) {
-    f32x4 s[2][NCT];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) s[sub][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int key = min(kt + krow + sub * 4, dm.ncmp - 1);
-      const T* kp = kbase + (size_t)key * kstride;
-#pragma unroll
-      for (int ks = 0; ks < DK / 32; ++ks) {
-        Frag8<T> kf = load_frag(kp + ks * 32);
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) mma(s[sub][ct], kf, qf[ct][ks]);
-      }
-    }
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      float v[8], mx = kNegInf;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = kt + qd * 8 + e;
-        v[e] = key < nvis[ct] ? s[e >> 2][ct][e & 3] * sc2 : kNegInf;
-        mx = fmaxf(mx, v[e]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(m[ct], mx);
-      const float mref = mn == kNegInf ? 0.f : mn;
-      float acc = ls[ct] * fast_exp2(m[ct] - mref);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc += fast_exp2(v[e] - mref);
-      ls[ct] = acc;
-      m[ct] = mn;
-    }
-  }
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    float tot = ls[ct] + __shfl_xor(ls[ct], 16);
-    tot += __shfl_xor(tot, 32);
-    const float lse = m[ct] == kNegInf ? kNegInf : (m[ct] + __log2f(tot)) * kLn2;
-    if (qd == 0 && pos[ct] < dm.T) a.lse[(size_t)(b * dm.T + pos[ct]) * dm.Hq + hq[ct]] = lse;
-  }
+// ---------------------------------------------------------------------------
+// One kernel for both passes.  A workgroup of 4 waves owns PWG consecutive
+// positions of one (batch, KV head); all waves need the same compressed keys,
+// so 64-key tiles of K_cmp (and, in pass B, of V_cmp^T) are staged once in LDS
+// per workgroup, double-buffered: the next tile's global loads are in flight
+// (in registers) while the current tile is computed from LDS.
+// ---------------------------------------------------------------------------
+constexpr int kCmpKT = 64;               // keys per LDS tile
+constexpr int kCmpVS = kCmpKT + 8;       // LDS row stride of the V^T tile (elements)
+
+template <int DK> constexpr int cmp_ks() { return DK + 8; }   // LDS row stride of the K tile
+
+template <typename T, int DK, int DV, bool PB>
+constexpr size_t cmp_tile_elems() {
+  return (size_t)kCmpKT * cmp_ks<DK>() + (PB ? (size_t)DV * kCmpVS : 0);
 }
 
-template <typename T, int DK, int DV, int NCT, typename OT>
-__global__ __launch_bounds__(256) void k_cmp_out(Dims dm, CmpArgs a, int nselp, int njt) {
-  extern __shared__ float smem[];
+template <typename T, int DK, int DV, int NCT, bool PB, typename OT>
+__global__ __launch_bounds__(256) void k_cmp(Dims dm, CmpArgs a, int nselp, int njt) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  constexpr int KS = cmp_ks<DK>();
+  constexpr size_t TE = cmp_tile_elems<T, DK, DV, PB>();
+  T* tiles = (T*)smem_raw;                                  // [2][TE]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, qd = lane >> 4;
   const int G = dm.G, PW = 16 * NCT / G, PWG = 4 * PW;
@@ -115,13 +57,15 @@ __global__ __launch_bounds__(256) void k_cmp_out(Dims dm, CmpArgs a, int nselp, 
   int unit, tile;
   xcd_map(blockIdx.x, dm.B * dm.Hkv, ntiles, unit, tile);
   const int b = unit / dm.Hkv, g = unit % dm.Hkv;
-  const int t0 = tile * PWG + wave * PW;
-  if (t0 >= dm.T) return;
-  float* prow = smem + (size_t)wave * PW * nselp;
-  for (int i = lane; i < PW * nselp; i += 64) prow[i] = 0.f;
+  const int twg = tile * PWG;
+  const int t0 = twg + wave * PW;
+  const bool wave_live = t0 < dm.T;
+  const int nmax_wg = ncmp_visible(min(dm.T - 1, twg + PWG - 1), dm.l, dm.d);
+  const int nmax = wave_live ? ncmp_visible(min(dm.T - 1, t0 + PW - 1), dm.l, dm.d) : 0;
+  float* prow = (float*)(smem_raw + 2 * TE * sizeof(T)) + (size_t)wave * PW * nselp;
+  if (PB)
+    for (int i = lane; i < PW * nselp; i += 64) prow[i] = 0.f;
 
-  const int tl = min(dm.T - 1, t0 + PW - 1);
-  const int nmax = ncmp_visible(tl, dm.l, dm.d);
   const T* q = (const T*)a.q;
   Frag8<T> qf[NCT][DK / 32];
   int pos[NCT], hq[NCT], nvis[NCT];
@@ -134,175 +78,273 @@ __global__ __launch_bounds__(256) void k_cmp_out(Dims dm, CmpArgs a, int nselp, 
     const bool v = pos[ct] < dm.T;
     nvis[ct] = v ? ncmp_visible(pos[ct], dm.l, dm.d) : 0;
     const size_t row = (size_t)(b * dm.T + min(pos[ct], dm.T - 1)) * dm.Hq + hq[ct];
-    lse2[ct] = (v && nvis[ct] > 0) ? a.lse[row] * kLog2e : 0.f;
+    lse2[ct] = (PB && v && nvis[ct] > 0) ? a.lse[row] * kLog2e : 0.f;
     const T* qp = q + row * DK + qd * 8;
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) qf[ct][ks] = v ? load_frag(qp + ks * 32) : zero_frag<T>();
   }
-  // remap matrix fragments (constant over tiles since l' divides 32*d)
   Frag8<T> wf[2];
+  if (PB) {
 #pragma unroll
-  for (int jt = 0; jt < 2; ++jt) {
-    float w[8];
+    for (int jt = 0; jt < 2; ++jt) {
+      float w[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) w[e] = jt < njt ? remap_weight(qd * 8 + e, jt * 16 + c16, dm.l, dm.d, dm.ls) : 0.f;
-    wf[jt] = to_frag<T>(w);
+      for (int e = 0; e < 8; ++e) w[e] = jt < njt ? remap_weight(qd * 8 + e, jt * 16 + c16, dm.l, dm.d, dm.ls) : 0.f;
+      wf[jt] = to_frag<T>(w);
+    }
   }
   const float sc2 = dm.scale * kLog2e;
-  f32x4 oacc[DV / 16][NCT];
+  float m[NCT], ls[NCT];
+  f32x4 oacc[PB ? DV / 16 : 1][NCT];
 #pragma unroll
-  for (int dt = 0; dt < DV / 16; ++dt)
+  for (int ct = 0; ct < NCT; ++ct) {
+    m[ct] = kNegInf;
+    ls[ct] = 0.f;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) oacc[dt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const size_t kstride = (size_t)dm.Hkv * DK;
-  const T* kbase = (const T*)a.kc + ((size_t)b * dm.ncmp * dm.Hkv + g) * DK + qd * 8;
-  const T* vtb = (const T*)a.vct + (size_t)(b * dm.Hkv + g) * DV * dm.ncmp_pad + qd * 8;
+    for (int dt = 0; dt < (PB ? DV / 16 : 1); ++dt) oacc[dt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // cooperative tile loader
+  constexpr int KCH = kCmpKT * DK / 8 / 256;        // 16-byte chunks per thread (K)
+  constexpr int VCH = PB ? DV * kCmpKT / 8 / 256 : 0;
+  Frag8<T> kr[KCH], vr[VCH > 0 ? VCH : 1];
+  const T* kcb = (const T*)a.kc + ((size_t)b * dm.ncmp * dm.Hkv + g) * DK;
+  const T* vtb = (const T*)a.vct + (size_t)(b * dm.Hkv + g) * DV * dm.ncmp_pad;
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+      const int idx = threadIdx.x + 256 * c, row = idx / (DK / 8), c8 = idx % (DK / 8);
+      const int key = min(kt + row, dm.ncmp - 1);
+      kr[c] = load_frag(kcb + (size_t)key * dm.Hkv * DK + c8 * 8);
+    }
+#pragma unroll
+    for (int c = 0; c < VCH; ++c) {
+      const int idx = threadIdx.x + 256 * c, row = idx / (kCmpKT / 8), c8 = idx % (kCmpKT / 8);
+      vr[c] = load_frag(vtb + (size_t)row * dm.ncmp_pad + kt + c8 * 8);
+    }
+  };
+  auto lstore = [&](int buf) {
+    T* kt_ = tiles + (size_t)buf * TE;
+    T* vt_ = kt_ + (size_t)kCmpKT * KS;
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+      const int idx = threadIdx.x + 256 * c, row = idx / (DK / 8), c8 = idx % (DK / 8);
+      *reinterpret_cast<Frag8<T>*>(kt_ + row * KS + c8 * 8) = kr[c];
+    }
+#pragma unroll
+    for (int c = 0; c < VCH; ++c) {
+      const int idx = threadIdx.x + 256 * c, row = idx / (kCmpKT / 8), c8 = idx % (kCmpKT / 8);
+      *reinterpret_cast<Frag8<T>*>(vt_ + row * kCmpVS + c8 * 8) = vr[c];
+    }
+  };
+
   const int krow = (c16 >> 2) * 8 + (c16 & 3);
   const int jstep = 32 * dm.d / dm.ls;
-  for (int kt = 0; kt < nmax; kt += 32) {
-    f32x4 s[2][NCT];
+  const int nkt = (nmax_wg + kCmpKT - 1) / kCmpKT;
+  if (nkt > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int it = 0; it < nkt; ++it) {
+    const int kt0 = it * kCmpKT;
+    if (it + 1 < nkt) gload(kt0 + kCmpKT);
+    const T* ktile = tiles + (size_t)(it & 1) * TE;
+    const T* vtile = ktile + (size_t)kCmpKT * KS;
+    for (int h = 0; h < 2; ++h) {
+      const int kt = kt0 + h * 32;
+      if (kt >= nmax) break;
+      f32x4 s[2][NCT];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+      for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) s[sub][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int key = min(kt + krow + sub * 4, dm.ncmp - 1);
-      const T* kp = kbase + (size_t)key * kstride;
+        for (int ct = 0; ct < NCT; ++ct) s[sub][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const T* kp = ktile + (h * 32 + krow + sub * 4) * KS + qd * 8;
 #pragma unroll
-      for (int ks = 0; ks < DK / 32; ++ks) {
-        Frag8<T> kf = load_frag(kp + ks * 32);
+        for (int ks = 0; ks < DK / 32; ++ks) {
+          const Frag8<T> kf = *reinterpret_cast<const Frag8<T>*>(kp + ks * 32);
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) mma(s[sub][ct], kf, qf[ct][ks]);
+          for (int ct = 0; ct < NCT; ++ct) mma(s[sub][ct], kf, qf[ct][ks]);
+        }
       }
-    }
-    Frag8<T> vf[DV / 16];
+      if constexpr (!PB) {
 #pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt) vf[dt] = load_frag(vtb + (size_t)(dt * 16 + c16) * dm.ncmp_pad + kt);
-    const int j0 = (kt / 32) * jstep;
+        for (int ct = 0; ct < NCT; ++ct) {
+          float v[8], mx = kNegInf;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      float p[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = kt + qd * 8 + e;
-        p[e] = key < nvis[ct] ? fast_exp2(s[e >> 2][ct][e & 3] * sc2 - lse2[ct]) : 0.f;
-      }
-      Frag8<T> pf = to_frag<T>(p);
-#pragma unroll
-      for (int dt = 0; dt < DV / 16; ++dt) mma(oacc[dt][ct], vf[dt], pf);
-      // remap onto selection blocks and sum over the group's heads
-      Frag8<T> phi = pf, plo;
-      if constexpr (sizeof(T) == 2) split_bf16(p, phi, plo);
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        if (jt >= njt) break;
-        f32x4 cr = f32x4{0.f, 0.f, 0.f, 0.f};
-        mma(cr, phi, wf[jt]);
-        if constexpr (sizeof(T) == 2) mma(cr, plo, wf[jt]);
-        const int j = j0 + jt * 16 + c16;
-        const int col = ct * 16 + qd * 4;
-        if (G >= 4) {
-          float v = cr[0] + cr[1] + cr[2] + cr[3];
-          if (G >= 8) v += __shfl_xor(v, 16);
-          if (G >= 16) v += __shfl_xor(v, 32);
-          const bool writer = G == 4 || (G == 8 && (qd & 1) == 0) || (G >= 16 && qd == 0);
-          if (writer && j < dm.nsel) prow[(col / G) * nselp + j] += v;
-        } else if (G == 2) {
-          if (j < dm.nsel) {
-            prow[(col / 2) * nselp + j] += cr[0] + cr[1];
-            prow[(col / 2 + 1) * nselp + j] += cr[2] + cr[3];
+          for (int e = 0; e < 8; ++e) {
+            const int key = kt + qd * 8 + e;
+            v[e] = key < nvis[ct] ? s[e >> 2][ct][e & 3] * sc2 : kNegInf;
+            mx = fmaxf(mx, v[e]);
           }
-        } else {
-          if (j < dm.nsel)
+          mx = fmaxf(mx, xor16f(mx, lane));
+          mx = fmaxf(mx, xor32f(mx, lane));
+          const float mn = fmaxf(m[ct], mx);
+          const float mref = mn == kNegInf ? 0.f : mn;
+          float acc = ls[ct] * fast_exp2(m[ct] - mref);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) prow[(col + r) * nselp + j] += cr[r];
+          for (int e = 0; e < 8; ++e) acc += fast_exp2(v[e] - mref);
+          ls[ct] = acc;
+          m[ct] = mn;
+        }
+      } else {
+        const int j0 = (kt / 32) * jstep;
+        // value tile fragments, shared by all column tiles
+        Frag8<T> vf[DV / 16];
+#pragma unroll
+        for (int dt = 0; dt < DV / 16; ++dt)
+          vf[dt] = *reinterpret_cast<const Frag8<T>*>(vtile + (dt * 16 + c16) * kCmpVS + h * 32 + qd * 8);
+        f32x4 cr[NCT][2];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          float p[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int key = kt + qd * 8 + e;
+            p[e] = key < nvis[ct] ? fast_exp2(s[e >> 2][ct][e & 3] * sc2 - lse2[ct]) : 0.f;
+          }
+          const Frag8<T> pf = to_frag<T>(p);
+#pragma unroll
+          for (int dt = 0; dt < DV / 16; ++dt) mma(oacc[dt][ct], vf[dt], pf);
+          // remap onto selection blocks: P (hi + lo) times the overlap weights
+          Frag8<T> phi = pf, plo;
+          if constexpr (sizeof(T) == 2) split_bf16(p, phi, plo);
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt) {
+            cr[ct][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (jt < njt) {
+              mma(cr[ct][jt], phi, wf[jt]);
+              if constexpr (sizeof(T) == 2) mma(cr[ct][jt], plo, wf[jt]);
+            }
+          }
+        }
+        // sum over the group's heads and accumulate the score rows in LDS
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+          if (jt >= njt) break;
+          const int j = j0 + jt * 16 + c16;
+          if (G >= 4) {
+            float v[NCT];
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) v[ct] = cr[ct][jt][0] + cr[ct][jt][1] + cr[ct][jt][2] + cr[ct][jt][3];
+            if (G >= 8) {
+#pragma unroll
+              for (int ct = 0; ct < NCT; ++ct) v[ct] += xor16f(v[ct], lane);
+            }
+            if (G >= 16) {
+#pragma unroll
+              for (int ct = 0; ct < NCT; ++ct) v[ct] += xor32f(v[ct], lane);
+            }
+            const bool writer = G == 4 || (G == 8 && (qd & 1) == 0) || (G >= 16 && qd == 0);
+            if (writer && j < dm.nsel) {
+#pragma unroll
+              for (int ct = 0; ct < NCT; ++ct) prow[((ct * 16 + qd * 4) / G) * nselp + j] += v[ct];
+            }
+          } else if (j < dm.nsel) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+              const int col = ct * 16 + qd * 4;
+              if (G == 2) {
+                prow[(col / 2) * nselp + j] += cr[ct][jt][0] + cr[ct][jt][1];
+                prow[(col / 2 + 1) * nselp + j] += cr[ct][jt][2] + cr[ct][jt][3];
+              } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) prow[(col + r) * nselp + j] += cr[ct][jt][r];
+              }
+            }
+          }
         }
       }
     }
+    if (it + 1 < nkt) lstore((it + 1) & 1);
+    __syncthreads();
   }
-  // O_cmp (rows with no visible block stay 0)
-  OT* o = (OT*)a.o;
+  if (!wave_live) return;
+  if constexpr (!PB) {
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    if (pos[ct] >= dm.T) continue;
-    OT* op = o + ((size_t)(b * dm.T + pos[ct]) * dm.Hq + hq[ct]) * DV + qd * 4;
-#pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt)
-      store4(op + dt * 16, oacc[dt][ct][0], oacc[dt][ct][1], oacc[dt][ct][2], oacc[dt][ct][3]);
-  }
-  // top-n per position of this wave
-  const int n = dm.n;
-  for (int pl = 0; pl < PW; ++pl) {
-    const int t = t0 + pl;
-    if (t >= dm.T) break;
-    float* row = prow + pl * nselp;
-    const size_t rbase = (size_t)(b * dm.T + t) * dm.Hkv + g;
-    if (a.p_slc) {
-      float* ps = a.p_slc + rbase * dm.nsel;
-      for (int j = lane; j < dm.nsel; j += 64) ps[j] = row[j];
+    for (int ct = 0; ct < NCT; ++ct) {
+      float tot = ls[ct] + xor16f(ls[ct], lane);
+      tot += xor32f(tot, lane);
+      const float lse = m[ct] == kNegInf ? kNegInf : (m[ct] + __log2f(tot)) * kLn2;
+      if (qd == 0 && pos[ct] < dm.T) a.lse[(size_t)(b * dm.T + pos[ct]) * dm.Hq + hq[ct]] = lse;
     }
-    wave_topn(row, t, dm.ls, n, a.idx + rbase * n, lane);
+  } else {
+    // O_cmp (rows with no visible block stay 0)
+    OT* o = (OT*)a.o;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      if (pos[ct] >= dm.T) continue;
+      OT* op = o + ((size_t)(b * dm.T + pos[ct]) * dm.Hq + hq[ct]) * DV + qd * 4;
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt)
+        store4(op + dt * 16, oacc[dt][ct][0], oacc[dt][ct][1], oacc[dt][ct][2], oacc[dt][ct][3]);
+    }
+    // top-n per position of this wave
+    for (int pl = 0; pl < PW; ++pl) {
+      const int t = t0 + pl;
+      if (t >= dm.T) break;
+      float* row = prow + pl * nselp;
+      const size_t rbase = (size_t)(b * dm.T + t) * dm.Hkv + g;
+      if (a.p_slc) {
+        float* ps = a.p_slc + rbase * dm.nsel;
+        for (int j = lane; j < dm.nsel; j += 64) ps[j] = row[j];
+      }
+      wave_topn(row, t, dm.ls, dm.n, a.idx + rbase * dm.n, lane);
+    }
   }
-}
-
-template <typename T, int DK>
-static hipError_t cmp_lse_impl(const Dims& dm, const CmpArgs& a, hipStream_t s) {
-  constexpr int NCT = 4;
-  const int PWG = 4 * 16 * NCT / dm.G;
-  const int ntiles = (dm.T + PWG - 1) / PWG;
-  k_cmp_lse<T, DK, NCT><<<ntiles * dm.B * dm.Hkv, 256, 0, s>>>(dm, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_cmp_lse(const Dims& dm, const CmpArgs& a, hipStream_t s) {
-  const bool bf = dm.io == IO_BF16;
-  switch (dm.dk) {
-    case 64: return bf ? cmp_lse_impl<bf16, 64>(dm, a, s) : cmp_lse_impl<float, 64>(dm, a, s);
-    case 128: return bf ? cmp_lse_impl<bf16, 128>(dm, a, s) : cmp_lse_impl<float, 128>(dm, a, s);
-    case 192: return bf ? cmp_lse_impl<bf16, 192>(dm, a, s) : cmp_lse_impl<float, 192>(dm, a, s);
-  }
-  return hipErrorInvalidValue;
-}
-
-// LDS bytes pass B needs with NCT column tiles per wave.
-static size_t cmp_out_lds(const Dims& dm, int nct, int nselp) {
-  return (size_t)4 * (16 * nct / dm.G) * nselp * sizeof(float);
 }
 
 int cmp_out_nselp(const Dims& dm) { return (dm.nsel + 15) & ~15; }
 
-template <typename T, int DK, int DV>
-static hipError_t cmp_out_impl(const Dims& dm, const CmpArgs& a, hipStream_t s) {
-  const int nselp = cmp_out_nselp(dm);
-  const int nblk = (31 * dm.d + dm.l - 1) / dm.ls + 1;   // selection blocks one key tile touches
-  const int njt = (nblk + 15) / 16;
-  const size_t lim = 160 * 1024;
-  int nct = cmp_out_lds(dm, 4, nselp) <= lim ? 4 : 1;
-  const size_t lds = cmp_out_lds(dm, nct, nselp);
-  if (lds > lim) return hipErrorInvalidValue;
-  const int PWG = 4 * 16 * nct / dm.G;
+template <typename T, int DK, int DV, bool PB>
+static size_t cmp_lds(const Dims& dm, int nct, int nselp) {
+  size_t b = 2 * cmp_tile_elems<T, DK, DV, PB>() * sizeof(T);
+  if (PB) b += (size_t)4 * (16 * nct / dm.G) * nselp * sizeof(float);
+  return b;
+}
+
+template <typename T, int DK, int DV, int NCT, bool PB, typename OT>
+static hipError_t cmp_launch(const Dims& dm, const CmpArgs& a, int nselp, int njt, size_t lds, hipStream_t s) {
+  auto kfn = k_cmp<T, DK, DV, NCT, PB, OT>;
+  if (lds > 64 * 1024) hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const int PWG = 4 * 16 * NCT / dm.G;
   const int ntiles = (dm.T + PWG - 1) / PWG;
-  if (nct == 4) {
-    auto kfn = a.o_f32 ? k_cmp_out<T, DK, DV, 4, float> : k_cmp_out<T, DK, DV, 4, T>;
-    if (lds > 64 * 1024) hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    kfn<<<ntiles * dm.B * dm.Hkv, 256, lds, s>>>(dm, a, nselp, njt);
-  } else {
-    auto kfn = a.o_f32 ? k_cmp_out<T, DK, DV, 1, float> : k_cmp_out<T, DK, DV, 1, T>;
-    if (lds > 64 * 1024) hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    kfn<<<ntiles * dm.B * dm.Hkv, 256, lds, s>>>(dm, a, nselp, njt);
-  }
+  kfn<<<ntiles * dm.B * dm.Hkv, 256, lds, s>>>(dm, a, nselp, njt);
   return hipGetLastError();
 }
 
-hipError_t launch_cmp_out_topn(const Dims& dm, const CmpArgs& a, hipStream_t s) {
+template <typename T, int DK, int DV, bool PB>
+static hipError_t cmp_impl(const Dims& dm, const CmpArgs& a, hipStream_t s) {
+  const int nselp = cmp_out_nselp(dm);
+  const int nblk = (31 * dm.d + dm.l - 1) / dm.ls + 1;   // selection blocks one 32-key tile touches
+  const int njt = (nblk + 15) / 16;
+  const size_t lim = 160 * 1024;
+  const int nct = cmp_lds<T, DK, DV, PB>(dm, 4, nselp) <= lim ? 4 : 1;
+  const size_t lds = cmp_lds<T, DK, DV, PB>(dm, nct, nselp);
+  if (lds > lim) return hipErrorInvalidValue;
+  if (nct == 4)
+    return a.o_f32 ? cmp_launch<T, DK, DV, 4, PB, float>(dm, a, nselp, njt, lds, s)
+                   : cmp_launch<T, DK, DV, 4, PB, T>(dm, a, nselp, njt, lds, s);
+  return a.o_f32 ? cmp_launch<T, DK, DV, 1, PB, float>(dm, a, nselp, njt, lds, s)
+                 : cmp_launch<T, DK, DV, 1, PB, T>(dm, a, nselp, njt, lds, s);
+}
+
+template <bool PB>
+static hipError_t cmp_dispatch(const Dims& dm, const CmpArgs& a, hipStream_t s) {
   const bool bf = dm.io == IO_BF16;
-  if (dm.dk == 64 && dm.dv == 64) return bf ? cmp_out_impl<bf16, 64, 64>(dm, a, s) : cmp_out_impl<float, 64, 64>(dm, a, s);
-  if (dm.dk == 128 && dm.dv == 128) return bf ? cmp_out_impl<bf16, 128, 128>(dm, a, s) : cmp_out_impl<float, 128, 128>(dm, a, s);
-  if (dm.dk == 192 && dm.dv == 128) return bf ? cmp_out_impl<bf16, 192, 128>(dm, a, s) : cmp_out_impl<float, 192, 128>(dm, a, s);
+  if (dm.dk == 64 && dm.dv == 64) return bf ? cmp_impl<bf16, 64, 64, PB>(dm, a, s) : cmp_impl<float, 64, 64, PB>(dm, a, s);
+  if (dm.dk == 128 && dm.dv == 128) return bf ? cmp_impl<bf16, 128, 128, PB>(dm, a, s) : cmp_impl<float, 128, 128, PB>(dm, a, s);
+  if (dm.dk == 192 && dm.dv == 128) return bf ? cmp_impl<bf16, 192, 128, PB>(dm, a, s) : cmp_impl<float, 192, 128, PB>(dm, a, s);
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_cmp_lse(const Dims& dm, const CmpArgs& a, hipStream_t s) { return cmp_dispatch<false>(dm, a, s); }
+hipError_t launch_cmp_out_topn(const Dims& dm, const CmpArgs& a, hipStream_t s) { return cmp_dispatch<true>(dm, a, s); }
+
 bool cmp_out_fits(const Dims& dm) {
-  return cmp_out_lds(dm, 1, cmp_out_nselp(dm)) <= 160 * 1024;
+  // pass B with one column tile per wave: tiles (largest case: fp32, 192/128) + score rows
+  const size_t tiles = 2 * ((size_t)kCmpKT * (dm.dk + 8) + (size_t)dm.dv * kCmpVS) * (dm.io == IO_BF16 ? 2 : 4);
+  return tiles + (size_t)4 * (16 / dm.G) * cmp_out_nselp(dm) * sizeof(float) <= 160 * 1024;
 }
 
 }  // namespace nsa

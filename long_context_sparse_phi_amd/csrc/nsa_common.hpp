@@ -148,6 +148,53 @@ __device__ __forceinline__ float remap_weight(int kr, int jc, int l, int d, int 
   return ov > 0 ? (float)(ov / d) : 0.f;
 }
 
+// ---------------------------------------------------------------------------
+// Cross-lane exchanges without the LDS crossbar (gfx950 permlane swaps, DPP).
+// xor16 / xor32 return the value of lane ^ 16 / lane ^ 32.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float xor16f(float v, int lane) {
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((lane & 16) ? q[0] : q[1]);
+}
+__device__ __forceinline__ float xor32f(float v, int lane) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((lane & 32) ? p[0] : p[1]);
+}
+// Reductions over the 4 lanes that share lane % 16 (one MFMA column).
+__device__ __forceinline__ float colmax4(float v, int lane) {
+  v = fmaxf(v, xor16f(v, lane));
+  return fmaxf(v, xor32f(v, lane));
+}
+__device__ __forceinline__ float colsum4(float v, int lane) {
+  v += xor16f(v, lane);
+  return v + xor32f(v, lane);
+}
+
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROWMASK, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROWMASK, 0xf, false);
+  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+// Maximum of a 64-bit key over the wave (DPP prefix max ends in lane 63), broadcast.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+  uint64_t t;
+  t = dpp_u64<0x111, 0xf>(k); k = t > k ? t : k;   // row_shr:1
+  t = dpp_u64<0x112, 0xf>(k); k = t > k ? t : k;   // row_shr:2
+  t = dpp_u64<0x114, 0xf>(k); k = t > k ? t : k;   // row_shr:4
+  t = dpp_u64<0x118, 0xf>(k); k = t > k ? t : k;   // row_shr:8
+  t = dpp_u64<0x142, 0xa>(k); k = t > k ? t : k;   // row_bcast:15
+  t = dpp_u64<0x143, 0xc>(k); k = t > k ? t : k;   // row_bcast:31
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)k, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+// Order key of candidate block j with score v >= 0: larger score first, then
+// lower index.  Taken (marked, v < 0) entries map to 0, below every candidate.
+__device__ __forceinline__ uint64_t topn_key(float v, int j) {
+  return v < 0.f ? 0ull : ((uint64_t)__float_as_uint(v) << 32) | (uint32_t)(0xffffffffu - (uint32_t)j);
+}
+
 // Top-n block selection for query position t from one group's score row
 // (LDS, nsel entries, scores >= 0), executed by one whole wave.  Block 0 and
 // blocks floor(t/ls) and floor(t/ls)-1 are always selected; the remaining
@@ -162,20 +209,23 @@ __device__ inline void wave_topn(float* row, int t, int ls, int n, int* out, int
     return;
   }
   if (lane == 0) { row[0] = -1.f; row[jc - 1] = -1.f; row[jc] = -1.f; }
-  for (int it = 0; it < n - 3; ++it) {
-    float bv = -2.f;
-    int bj = 0x7fffffff;
+  // each lane keeps the best key among its candidates j = lane (mod 64)
+  auto lane_best = [&]() {
+    uint64_t best = 0;
     for (int j = lane; j <= jc; j += 64) {
-      const float v = row[j];
-      if (v > bv) { bv = v; bj = j; }
+      const uint64_t k = topn_key(row[j], j);
+      best = k > best ? k : best;
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oj = __shfl_xor(bj, off);
-      if (ov > bv || (ov == bv && oj < bj)) { bv = ov; bj = oj; }
+    return best;
+  };
+  uint64_t mine = lane_best();
+  for (int it = 0; it < n - 3; ++it) {
+    const uint64_t win = wave_max_u64(mine);
+    const int bj = (int)(0xffffffffu - (uint32_t)win);
+    if ((bj & 63) == lane) {
+      row[bj] = -1.f;
+      mine = lane_best();
     }
-    if (lane == 0) row[bj] = -1.f;
   }
   int cnt = 0;
   for (int jb = 0; jb <= jc; jb += 64) {

@@ -9,13 +9,14 @@
 //      its chunk, its partial softmax state (max m, sum l, unnormalised P V)
 //      and its per-head partial importance scores remapped onto selection
 //      blocks (same remap MFMA as the prefill).
-//   2. k_dec_combine: merges the chunks into the compressed-branch output and
-//      exact per-head probabilities, sums the group's heads into the block
-//      scores, runs top-n and evaluates the gates.
-//   3. k_dec_sw: selected blocks (two per wave) and 128-token window chunks,
+//   2. k_dec_combine: merges the chunks' softmax states into exact per-head
+//      probabilities, sums the group's heads into the block scores and runs
+//      top-n.
+//   3. k_dec_sw: one selected block or one 64-token window chunk per wave,
 //      each a partial softmax state.
-//   4. k_dec_merge: merges the partial states of the selected and window
-//      branches and writes o = g_cmp O_cmp + g_slc O_slc + g_win O_win.
+//   4. k_dec_merge: evaluates the gates, merges the compressed chunks and the
+//      selected and window partial states, and writes
+//      o = g_cmp O_cmp + g_slc O_slc + g_win O_win.
 // The raw caches are stored [key][feature]; the value operand of P V needs
 // eight consecutive keys per lane, so each 32-key value tile passes through
 // LDS and is read transposed.
@@ -25,10 +26,10 @@
 
 namespace nsa {
 
-constexpr int kDecCK = 512;     // compressed blocks per chunk
+constexpr int kDecCK = 256;     // compressed blocks per chunk (one wave)
 constexpr int kDecTPC = kDecCK / 32;
-constexpr int kDecSlcPer = 2;   // selected blocks per wave
-constexpr int kDecWinChunk = 128;
+constexpr int kDecSlcPer = 1;   // selected blocks per wave
+constexpr int kDecWinChunk = 64;
 
 struct DecPlan {
   int S, t, ncmp, nc, nb, jstep, nis, niw, ni, wlen, ws0;
@@ -53,8 +54,8 @@ static DecPlan dec_plan(const Dims& dm) {
 struct DecBufs {
   float* part_o;    // [B,Hkv,nc,16,dv]
   float* part_ml;   // [B,Hkv,nc,16,2]
-  float* part_ps;   // [B,Hkv,nc,16,TPC,nb]
-  float* o_cmp;     // [B,Hq,dv]
+  float* part_ps;   // [B,Hkv,nc,TPC,nb,16]
+  float* cmp_scl;   // [B,Hkv,nc,16] exp2(m_chunk - lse) per chunk and head
   float* lse_cmp;   // [B,Hq] (log2 units)
   float* gates;     // [B,Hq,3]
   int* idx;         // [B,Hkv,n]
@@ -73,7 +74,7 @@ static size_t dec_carve(const Dims& dm, void* ws, DecBufs* b) {
   b->part_o = (float*)take(BG * p.nc * 16 * dm.dv * 4);
   b->part_ml = (float*)take(BG * p.nc * 16 * 2 * 4);
   b->part_ps = (float*)take(BG * p.nc * 16 * kDecTPC * p.nb * 4);
-  b->o_cmp = (float*)take((size_t)dm.B * dm.Hq * dm.dv * 4);
+  b->cmp_scl = (float*)take(BG * (p.nc > 0 ? p.nc : 1) * 16 * 4);
   b->lse_cmp = (float*)take((size_t)dm.B * dm.Hq * 4);
   b->gates = (float*)take((size_t)dm.B * dm.Hq * 3 * 4);
   b->idx = (int*)take(BG * dm.n * 4);
@@ -145,9 +146,52 @@ __device__ __forceinline__ void score_tile(f32x4 (&s)[2], const T* kbase, size_t
   }
 }
 
+template <typename T, int DK>
+__device__ __forceinline__ void load_k_tile(Frag8<T> (&kf)[2][DK / 32], const T* kbase, size_t kstride, int kt,
+                                            int klim, int krow) {
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    const T* kp = kbase + (size_t)min(kt + krow + sub * 4, klim - 1) * kstride;
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) kf[sub][ks] = load_frag(kp + ks * 32);
+  }
+}
+
+template <typename T, int DK>
+__device__ __forceinline__ void score_from(f32x4 (&s)[2], const Frag8<T> (&kf)[2][DK / 32],
+                                           const Frag8<T> (&qf)[DK / 32]) {
+#pragma unroll
+  for (int sub = 0; sub < 2; ++sub) {
+    s[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) mma(s[sub], kf[sub][ks], qf[ks]);
+  }
+}
+
+// 32-key value tile in registers (row r = key, 8 features per chunk) and its LDS image.
+template <typename T, int DV>
+struct VTileRegs {
+  static constexpr int CH = 32 * DV / 8 / 64;   // chunks per lane
+  Frag8<T> r[CH];
+  __device__ __forceinline__ void gload(const T* vbase, size_t kstride, int key0, int klim, int lane) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int i = lane + 64 * c, row = i / (DV / 8), c8 = i % (DV / 8);
+      r[c] = load_frag(vbase + (size_t)min(key0 + row, klim - 1) * kstride + c8 * 8);
+    }
+  }
+  __device__ __forceinline__ void lstore(T* vs, int lane) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int i = lane + 64 * c, row = i / (DV / 8), c8 = i % (DV / 8);
+      *reinterpret_cast<Frag8<T>*>(vs + row * (DV + 8) + c8 * 8) = r[c];
+    }
+  }
+};
+
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(64) void k_dec_cmp(Dims dm, DecArgs a, DecPlan pl) {
-  extern __shared__ float smem[];
+  extern __shared__ __align__(16) float smem[];
   float* sb = smem;                                   // [TPC][64][8] scores
   T* vs = (T*)(smem + kDecTPC * 64 * 8);              // [32][DV+8]
   const int lane = threadIdx.x, c16 = lane & 15, qd = lane >> 4;
@@ -167,11 +211,10 @@ __global__ __launch_bounds__(64) void k_dec_cmp(Dims dm, DecArgs a, DecPlan pl) 
   const T* kbase = (const T*)a.kc + ((size_t)b * a.cap * dm.Hkv + g) * DK + qd * 8;
   const T* vbase = (const T*)a.vc + ((size_t)b * a.cap * dm.Hkv + g) * DV;
   const int krow = (c16 >> 2) * 8 + (c16 & 3);
+  // phase 1: scores of the chunk, two key tiles in flight
   float mloc = kNegInf;
-  for (int i = 0; i < ntile; ++i) {
+  auto keep = [&](const f32x4 (&s)[2], int i) {
     const int kt = k0 + 32 * i;
-    f32x4 s[2];
-    score_tile<T, DK>(s, kbase, kstride, kt, pl.ncmp, qf, krow);
     float* dst = sb + (i * 64 + lane) * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -179,9 +222,24 @@ __global__ __launch_bounds__(64) void k_dec_cmp(Dims dm, DecArgs a, DecPlan pl) 
       dst[e] = v;
       mloc = fmaxf(mloc, v);
     }
+  };
+  {
+    Frag8<T> ka[2][DK / 32], kb[2][DK / 32];
+    load_k_tile<T, DK>(ka, kbase, kstride, k0, pl.ncmp, krow);
+    for (int i = 0; i < ntile; i += 2) {
+      if (i + 1 < ntile) load_k_tile<T, DK>(kb, kbase, kstride, k0 + 32 * (i + 1), pl.ncmp, krow);
+      f32x4 s[2];
+      score_from<T, DK>(s, ka, qf);
+      keep(s, i);
+      if (i + 2 < ntile) load_k_tile<T, DK>(ka, kbase, kstride, k0 + 32 * (i + 2), pl.ncmp, krow);
+      if (i + 1 < ntile) {
+        score_from<T, DK>(s, kb, qf);
+        keep(s, i + 1);
+      }
+    }
   }
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 16));
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+  mloc = fmaxf(mloc, xor16f(mloc, lane));
+  mloc = fmaxf(mloc, xor32f(mloc, lane));
   const float mref = mloc == kNegInf ? 0.f : mloc;
   Frag8<T> wf[2];
 #pragma unroll
@@ -195,11 +253,15 @@ __global__ __launch_bounds__(64) void k_dec_cmp(Dims dm, DecArgs a, DecPlan pl) 
 #pragma unroll
   for (int dt = 0; dt < DV / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float lsum = 0.f;
-  float* ps = a.w.part_ps + (((size_t)bg * pl.nc + c) * 16) * kDecTPC * pl.nb;
+  float* ps = a.w.part_ps + ((size_t)bg * pl.nc + c) * kDecTPC * pl.nb * 16;
+  // phase 2: probabilities, P V and remapped scores; the next value tile is in flight
+  VTileRegs<T, DV> vr;
+  vr.gload(vbase, vstride, k0, pl.ncmp, lane);
   for (int i = 0; i < ntile; ++i) {
-    const int kt = k0 + 32 * i;
     __syncthreads();
-    stage_v_tile<T, DV>(vs, vbase, vstride, kt, pl.ncmp, lane);
+    vr.lstore(vs, lane);
+    __syncthreads();
+    if (i + 1 < ntile) vr.gload(vbase, vstride, k0 + 32 * (i + 1), pl.ncmp, lane);
     float p[8];
     const float* src = sb + (i * 64 + lane) * 8;
 #pragma unroll
@@ -216,14 +278,11 @@ __global__ __launch_bounds__(64) void k_dec_cmp(Dims dm, DecArgs a, DecPlan pl) 
       mma(cr, phi, wf[jt]);
       if constexpr (sizeof(T) == 2) mma(cr, plo, wf[jt]);
       const int jj = jt * 16 + c16;
-      if (jj < pl.nb) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ps[((size_t)(qd * 4 + r) * kDecTPC + i) * pl.nb + jj] = cr[r];
-      }
+      if (jj < pl.nb) store4(ps + ((size_t)i * pl.nb + jj) * 16 + qd * 4, cr[0], cr[1], cr[2], cr[3]);
     }
   }
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  lsum += xor16f(lsum, lane);
+  lsum += xor32f(lsum, lane);
   const size_t hb = ((size_t)bg * pl.nc + c) * 16 + c16;
   if (qd == 0) {
     a.w.part_ml[hb * 2 + 0] = mloc;
@@ -234,67 +293,65 @@ __global__ __launch_bounds__(64) void k_dec_cmp(Dims dm, DecArgs a, DecPlan pl) 
   for (int dt = 0; dt < DV / 16; ++dt) store4(op + dt * 16, oacc[dt][0], oacc[dt][1], oacc[dt][2], oacc[dt][3]);
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void k_dec_combine(Dims dm, DecArgs a, DecPlan pl) {
+// One workgroup (1024 threads) per (sequence, KV head): per-head log-sum-exp
+// of the compressed branch, per-chunk scales, block scores and top-n.
+__global__ __launch_bounds__(1024) void k_dec_combine(Dims dm, DecArgs a, DecPlan pl) {
   extern __shared__ float smem[];
   float* row = smem;                          // [nsel]
   float* scl = row + ((dm.nsel + 3) & ~3);    // [nc][16]
   float* lse2 = scl + pl.nc * 16;             // [16]
+  float* mls = lse2 + 16;                     // [nc][16] chunk maxima
+  float* lsl = mls + pl.nc * 16;              // [nc][16] chunk sums
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bg = blockIdx.x, b = bg / dm.Hkv, g = bg % dm.Hkv;
   const int G = dm.G;
+  for (int i = tid; i < pl.nc * 16; i += 1024) {
+    const size_t hb = (size_t)bg * pl.nc * 16 + i;
+    mls[i] = a.w.part_ml[hb * 2];
+    lsl[i] = a.w.part_ml[hb * 2 + 1];
+  }
+  __syncthreads();
   if (tid < 16) {
     float M = kNegInf;
-    for (int c = 0; c < pl.nc; ++c) M = fmaxf(M, a.w.part_ml[(((size_t)bg * pl.nc + c) * 16 + tid) * 2]);
+    for (int c = 0; c < pl.nc; ++c) M = fmaxf(M, mls[c * 16 + tid]);
     float L = 0.f;
     const float Mr = M == kNegInf ? 0.f : M;
-    for (int c = 0; c < pl.nc; ++c) {
-      const size_t hb = ((size_t)bg * pl.nc + c) * 16 + tid;
-      L += a.w.part_ml[hb * 2 + 1] * fast_exp2(a.w.part_ml[hb * 2] - Mr);
-    }
+    for (int c = 0; c < pl.nc; ++c) L += lsl[c * 16 + tid] * fast_exp2(mls[c * 16 + tid] - Mr);
     const float l2 = M == kNegInf ? kNegInf : M + __log2f(L);
     lse2[tid] = l2;
-    for (int c = 0; c < pl.nc; ++c) {
-      const float mc = a.w.part_ml[(((size_t)bg * pl.nc + c) * 16 + tid) * 2];
-      scl[c * 16 + tid] = (mc == kNegInf || l2 == kNegInf) ? 0.f : fast_exp2(mc - l2);
-    }
     if (tid < G) a.w.lse_cmp[(size_t)b * dm.Hq + g * G + tid] = l2;
   }
   __syncthreads();
-  // compressed-branch output
-  for (int i = tid; i < G * dm.dv; i += 256) {
-    const int h = i / dm.dv, e = i % dm.dv;
-    float acc = 0.f;
-    for (int c = 0; c < pl.nc; ++c)
-      acc += a.w.part_o[(((size_t)bg * pl.nc + c) * 16 + h) * dm.dv + e] * scl[c * 16 + h];
-    a.w.o_cmp[((size_t)b * dm.Hq + g * G + h) * dm.dv + e] = acc;
+  for (int i = tid; i < pl.nc * 16; i += 1024) {
+    const float mc = mls[i], l2 = lse2[i % 16];
+    const float v = (mc == kNegInf || l2 == kNegInf) ? 0.f : fast_exp2(mc - l2);
+    scl[i] = v;
+    a.w.cmp_scl[(size_t)bg * pl.nc * 16 + i] = v;
   }
+  __syncthreads();
   // block scores: sum over heads of exact probabilities remapped to blocks
   const int ntiles = (pl.ncmp + 31) / 32;
-  for (int j = tid; j < dm.nsel; j += 256) {
+  for (int j = tid; j < dm.nsel; j += 1024) {
     float val = 0.f;
     int klo = j - pl.nb + 1;
     klo = klo <= 0 ? 0 : (klo + pl.jstep - 1) / pl.jstep;
     const int khi = min(j / pl.jstep, ntiles - 1);
     for (int kg = klo; kg <= khi; ++kg) {
       const int c = kg / kDecTPC, i = kg % kDecTPC, jj = j - kg * pl.jstep;
-      if (jj >= pl.nb) continue;
-      const float* ps = a.w.part_ps + (((size_t)bg * pl.nc + c) * 16) * kDecTPC * pl.nb;
-      for (int h = 0; h < G; ++h) val += ps[((size_t)h * kDecTPC + i) * pl.nb + jj] * scl[c * 16 + h];
+      const float* ps = a.w.part_ps + ((((size_t)bg * pl.nc + c) * kDecTPC + i) * pl.nb + jj) * 16;
+      for (int h4 = 0; h4 < G; h4 += 4) {
+        float x[4];
+        load4(ps + h4, x);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (h4 + r < G) val += x[r] * scl[c * 16 + h4 + r];
+      }
     }
     row[j] = val;
   }
-  // gates for the group's heads
-  for (int i = tid; i < G * 3; i += 256) {
-    const int h = g * G + i / 3, cc = i % 3;
-    float z = 0.f;
-    for (int k = 0; k < dm.C; ++k)
-      z += to_f32(((const T*)a.x)[(size_t)b * dm.C + k]) * to_f32(((const T*)a.wg)[((size_t)k * dm.Hq + h) * 3 + cc]);
-    a.w.gates[((size_t)b * dm.Hq + h) * 3 + cc] = 1.f / (1.f + expf(-z));
-  }
   __syncthreads();
   if (a.p_slc)
-    for (int j = tid; j < dm.nsel; j += 256) a.p_slc[(size_t)bg * dm.nsel + j] = row[j];
+    for (int j = tid; j < dm.nsel; j += 1024) a.p_slc[(size_t)bg * dm.nsel + j] = row[j];
   __syncthreads();
   if (wave == 0) wave_topn(row, pl.t, dm.ls, dm.n, a.w.idx + (size_t)bg * dm.n, lane);
 }
@@ -347,8 +404,8 @@ __global__ __launch_bounds__(64) void k_dec_sw(Dims dm, DecArgs a, DecPlan pl) {
         v[e] = (kt + qd * 8 + e < r1[r]) ? s[e >> 2][e & 3] * sc2 : kNegInf;
         mx = fmaxf(mx, v[e]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = fmaxf(mx, xor16f(mx, lane));
+      mx = fmaxf(mx, xor32f(mx, lane));
       const float mn = fmaxf(m, mx);
       const float mref = mn == kNegInf ? 0.f : mn;
       const float alpha = fast_exp2(m - mref);
@@ -365,8 +422,8 @@ __global__ __launch_bounds__(64) void k_dec_sw(Dims dm, DecArgs a, DecPlan pl) {
       }
     }
   }
-  ls += __shfl_xor(ls, 16);
-  ls += __shfl_xor(ls, 32);
+  ls += xor16f(ls, lane);
+  ls += xor32f(ls, lane);
   const size_t hb = ((size_t)bg * pl.ni + it) * 16 + c16;
   if (qd == 0) {
     a.w.sw_ml[hb * 2 + 0] = m;
@@ -377,57 +434,79 @@ __global__ __launch_bounds__(64) void k_dec_sw(Dims dm, DecArgs a, DecPlan pl) {
   for (int dt = 0; dt < DV / 16; ++dt) store4(op + dt * 16, oacc[dt][0], oacc[dt][1], oacc[dt][2], oacc[dt][3]);
 }
 
-template <typename T>
+// One workgroup per (sequence, KV head, pair of query heads): gates, merge of
+// the compressed chunks and of the selected/window partial states, output.
+template <typename T, int DV>
 __global__ __launch_bounds__(256) void k_dec_merge(Dims dm, DecArgs a, DecPlan pl) {
-  __shared__ float st[2][16][2];   // per branch, head: (max, 1/sum)
-  const int tid = threadIdx.x;
-  const int bg = blockIdx.x, b = bg / dm.Hkv, g = bg % dm.Hkv;
+  extern __shared__ float sm[];
+  float* swscl = sm;                  // [ni][2]
+  float* cscl = swscl + pl.ni * 2;    // [nc][2]
+  float* gts = cscl + pl.nc * 2;      // [2][3]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hp = blockIdx.x % 8, bg = blockIdx.x / 8;
+  const int b = bg / dm.Hkv, g = bg % dm.Hkv;
   const int G = dm.G;
-  if (tid < 32) {
-    const int br = tid / 16, h = tid % 16;
+  const int h0 = hp * 2;
+  if (h0 >= G) return;
+  // gates of the two heads: one wave per dot product
+  for (int o = wave; o < 6; o += 4) {
+    const int hh = h0 + o / 3, cc = o % 3;
+    float z = 0.f;
+    if (hh < G) {
+      const int h = g * G + hh;
+      for (int k = lane; k < dm.C; k += 64)
+        z += to_f32(((const T*)a.x)[(size_t)b * dm.C + k]) * to_f32(((const T*)a.wg)[((size_t)k * dm.Hq + h) * 3 + cc]);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
+    if (lane == 0) gts[o] = 1.f / (1.f + expf(-z));
+  }
+  // selected / window merge scales: exp2(m_i - M_branch) / L_branch
+  if (tid < 4) {
+    const int hh = h0 + tid / 2, br = tid % 2;
     const int i0 = br == 0 ? 0 : pl.nis, i1 = br == 0 ? pl.nis : pl.ni;
     float M = kNegInf;
-    for (int i = i0; i < i1; ++i) M = fmaxf(M, a.w.sw_ml[(((size_t)bg * pl.ni + i) * 16 + h) * 2]);
+    for (int i = i0; i < i1; ++i) M = fmaxf(M, a.w.sw_ml[(((size_t)bg * pl.ni + i) * 16 + hh) * 2]);
     const float Mr = M == kNegInf ? 0.f : M;
     float L = 0.f;
     for (int i = i0; i < i1; ++i) {
-      const size_t hb = ((size_t)bg * pl.ni + i) * 16 + h;
+      const size_t hb = ((size_t)bg * pl.ni + i) * 16 + hh;
       L += a.w.sw_ml[hb * 2 + 1] * fast_exp2(a.w.sw_ml[hb * 2] - Mr);
     }
-    st[br][h][0] = Mr;
-    st[br][h][1] = L > 0.f ? 1.f / L : 0.f;
-    if (a.lse && h < G) a.lse[(size_t)(1 + br) * dm.B * dm.Hq + (size_t)b * dm.Hq + g * G + h] = (M + __log2f(L)) * kLn2;
-    if (a.lse && br == 0 && h < G) {
-      const float l2 = a.w.lse_cmp[(size_t)b * dm.Hq + g * G + h];
-      a.lse[(size_t)b * dm.Hq + g * G + h] = l2 == kNegInf ? kNegInf : l2 * kLn2;
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    for (int i = i0; i < i1; ++i) {
+      const float mi = a.w.sw_ml[(((size_t)bg * pl.ni + i) * 16 + hh) * 2];
+      swscl[i * 2 + tid / 2] = mi == kNegInf ? 0.f : fast_exp2(mi - Mr) * inv;
+    }
+    if (a.lse && hh < G) {
+      const size_t rr = (size_t)b * dm.Hq + g * G + hh;
+      a.lse[(size_t)(1 + br) * dm.B * dm.Hq + rr] = (M + __log2f(L)) * kLn2;
+      if (br == 0) {
+        const float l2 = a.w.lse_cmp[rr];
+        a.lse[rr] = l2 == kNegInf ? kNegInf : l2 * kLn2;
+      }
     }
   }
+  for (int i = tid; i < pl.nc * 2; i += 256) cscl[i] = a.w.cmp_scl[((size_t)bg * pl.nc + i / 2) * 16 + h0 + i % 2];
   __syncthreads();
-  for (int i = tid; i < G * dm.dv; i += 256) {
-    const int h = i / dm.dv, e = i % dm.dv;
-    float ob[2];
-    for (int br = 0; br < 2; ++br) {
-      const int i0 = br == 0 ? 0 : pl.nis, i1 = br == 0 ? pl.nis : pl.ni;
-      float acc = 0.f;
-      for (int it = i0; it < i1; ++it) {
-        const size_t hb = ((size_t)bg * pl.ni + it) * 16 + h;
-        const float mi = a.w.sw_ml[hb * 2];
-        if (mi == kNegInf) continue;
-        acc += a.w.sw_o[hb * dm.dv + e] * fast_exp2(mi - st[br][h][0]);
-      }
-      ob[br] = acc * st[br][h][1];
-    }
-    const size_t row = (size_t)b * dm.Hq + g * G + h;
-    const float oc = a.w.o_cmp[row * dm.dv + e];
-    const float* gt = a.w.gates + row * 3;
-    const float o = gt[0] * oc + gt[1] * ob[0] + gt[2] * ob[1];
-    ((T*)a.o)[row * dm.dv + e] = from_f32<T>(o);
-    if (a.o_branch) {
-      const size_t plane = (size_t)dm.B * dm.Hq * dm.dv;
-      ((float*)a.o_branch)[row * dm.dv + e] = oc;
-      ((float*)a.o_branch)[plane + row * dm.dv + e] = ob[0];
-      ((float*)a.o_branch)[2 * plane + row * dm.dv + e] = ob[1];
-    }
+  const int hh = h0 + tid / DV, e = tid % DV;   // 2 heads x DV features (DV <= 128)
+  if (tid >= 2 * DV || hh >= G) return;
+  const int hl = hh - h0;
+  float oc = 0.f;
+  for (int c = 0; c < pl.nc; ++c) oc += a.w.part_o[(((size_t)bg * pl.nc + c) * 16 + hh) * DV + e] * cscl[c * 2 + hl];
+  float ob[2] = {0.f, 0.f};
+  for (int it = 0; it < pl.ni; ++it) {
+    const float v = a.w.sw_o[(((size_t)bg * pl.ni + it) * 16 + hh) * DV + e] * swscl[it * 2 + hl];
+    if (it < pl.nis) ob[0] += v; else ob[1] += v;
+  }
+  const size_t row = (size_t)b * dm.Hq + g * G + hh;
+  const float o = gts[hl * 3 + 0] * oc + gts[hl * 3 + 1] * ob[0] + gts[hl * 3 + 2] * ob[1];
+  ((T*)a.o)[row * DV + e] = from_f32<T>(o);
+  if (a.o_branch) {
+    const size_t plane = (size_t)dm.B * dm.Hq * DV;
+    ((float*)a.o_branch)[row * DV + e] = oc;
+    ((float*)a.o_branch)[plane + row * DV + e] = ob[0];
+    ((float*)a.o_branch)[2 * plane + row * DV + e] = ob[1];
   }
 }
 
@@ -446,16 +525,16 @@ static hipError_t decode_impl(const Dims& dm, const DecArgs& a, const DecPlan& p
   }
   if ((e = mark()) != hipSuccess) return e;
   {
-    const size_t lds = (((size_t)dm.nsel + 3) & ~(size_t)3) * 4 + (size_t)pl.nc * 16 * 4 + 16 * 4;
+    const size_t lds = (((size_t)dm.nsel + 3) & ~(size_t)3) * 4 + (size_t)pl.nc * 16 * 4 * 3 + 16 * 4;
     if (lds > 64 * 1024)
-      hipFuncSetAttribute((const void*)k_dec_combine<T>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    k_dec_combine<T><<<BG, 256, lds, s>>>(dm, a, pl);
+      hipFuncSetAttribute((const void*)k_dec_combine, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    k_dec_combine<<<BG, 1024, lds, s>>>(dm, a, pl);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = mark()) != hipSuccess) return e;
   k_dec_sw<T, DK, DV><<<BG * pl.ni, 64, 0, s>>>(dm, a, pl);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  k_dec_merge<T><<<BG, 256, 0, s>>>(dm, a, pl);
+  k_dec_merge<T, DV><<<BG * 8, 256, ((size_t)pl.ni * 2 + (size_t)pl.nc * 2 + 8) * sizeof(float), s>>>(dm, a, pl);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return mark();
 }
