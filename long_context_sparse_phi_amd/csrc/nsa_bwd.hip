@@ -35,24 +35,25 @@ int bwd_stage_count() { return 8; }
 constexpr int kSegCmp = 1024;    // query positions per compressed-key segment
 constexpr int kSegSlc = 1024;    // list entries per selected-block segment
 constexpr int kRevChunk = 256;   // positions per reverse-index chunk
+constexpr int kMaxSplit = 64;    // split-K factor bound of the reduction GEMMs
 
 struct BwdPlan {
-  int nkt_cmp;     // 16-key tiles of the compressed keys
-  int nseg_cmp;    // segments per compressed key tile (upper bound)
+  int nkg_cmp;     // 64-key groups of the compressed keys
+  int nseg_cmp;    // position segments per compressed key group (upper bound)
   int nchunk;      // reverse-index chunks
+  int nkc_slc;     // 64-key chunks per selection block
   int nseg_slc;    // segments per selected block (upper bound)
   int max_slc_seg; // segment slots per (b, g)
-  int Ts;          // stride of the padded transposed q / dO: T*16
 };
 
 static BwdPlan bwd_plan(const Dims& dm) {
   BwdPlan p;
-  p.nkt_cmp = (dm.ncmp + 15) / 16;
+  p.nkg_cmp = (dm.ncmp + 63) / 64;
   p.nseg_cmp = (dm.T + kSegCmp - 1) / kSegCmp;
   p.nchunk = (dm.T + kRevChunk - 1) / kRevChunk;
+  p.nkc_slc = (dm.ls + 63) / 64;
   p.nseg_slc = (dm.T + kSegSlc - 1) / kSegSlc;
   p.max_slc_seg = dm.nsel + (int)(((long long)dm.T * dm.n + kSegSlc - 1) / kSegSlc);
-  p.Ts = dm.T * 16;
   return p;
 }
 
@@ -62,18 +63,18 @@ struct BwdBufs {
   float* dz;       // [B,T,Hq,3]
   void* kt;        // [B,Hkv,dk,Tp]
   void* kct;       // [B,Hkv,dk,ncmp_pad]
-  void* qt;        // [B,Hkv,dk,T*16]
-  void* dot;       // [B,Hkv,dv,T*16]
   float* dkc;      // [B,Hkv,ncmp,dk]
   float* dvc;      // [B,Hkv,ncmp,dv]
-  float* part_cmp; // [B*Hkv*nkt*nseg][16][dk+dv]
+  float* part_cmp; // [B*Hkv*nkg*nseg][64][dk+dv]
   int* hist;       // [B*Hkv][nchunk][nsel]
   int* offc;       // [B*Hkv][nchunk][nsel]
   int* cnt;        // [B*Hkv][nsel]
   int* lstart;     // [B*Hkv][nsel]
   int* segoff;     // [B*Hkv][nsel]
+  int* task;       // [B*Hkv][max_slc_seg] segment slot -> j * nseg_slc + seg, or -1
   int* list;       // [B*Hkv][T*n]
   float* part_slc; // [B*Hkv*max_slc_seg][ls][dk+dv]
+  float* gpart;    // split-K GEMM / column-sum partials
   // phi
   void* w1t;       // [H, l*D]   io
   void* w2t;       // [D, H]     io
@@ -98,18 +99,24 @@ static size_t bwd_carve(const Dims& dm, void* ws, BwdBufs* w) {
   w->dz = (float*)take(BTH * 3 * 4);
   w->kt = take(BG * dm.dk * dm.Tp * es);
   w->kct = take(BG * dm.dk * dm.ncmp_pad * es);
-  w->qt = take(BG * dm.dk * p.Ts * es);
-  w->dot = take(BG * dm.dv * p.Ts * es);
   w->dkc = (float*)take(BG * dm.ncmp * dm.dk * 4);
   w->dvc = (float*)take(BG * dm.ncmp * dm.dv * 4);
-  w->part_cmp = (float*)take(BG * p.nkt_cmp * p.nseg_cmp * 16 * (dm.dk + dm.dv) * 4);
+  w->part_cmp = (float*)take(BG * p.nkg_cmp * p.nseg_cmp * 64 * (dm.dk + dm.dv) * 4);
   w->hist = (int*)take(BG * p.nchunk * dm.nsel * 4);
   w->offc = (int*)take(BG * p.nchunk * dm.nsel * 4);
   w->cnt = (int*)take(BG * dm.nsel * 4);
   w->lstart = (int*)take(BG * dm.nsel * 4);
   w->segoff = (int*)take(BG * dm.nsel * 4);
+  w->task = (int*)take(BG * p.max_slc_seg * 4);
   w->list = (int*)take(BG * dm.T * dm.n * 4);
   w->part_slc = (float*)take(BG * p.max_slc_seg * dm.ls * (dm.dk + dm.dv) * 4);
+  {
+    const size_t Dm = dm.dk > dm.dv ? dm.dk : dm.dv;
+    size_t mn = (size_t)dm.C * 3 * dm.Hq;
+    mn = mn > (size_t)dm.hidden * Dm ? mn : (size_t)dm.hidden * Dm;
+    mn = mn > (size_t)dm.l * Dm ? mn : (size_t)dm.l * Dm;
+    w->gpart = (float*)take(kMaxSplit * mn * 4);
+  }
   if (dm.hidden) {
     const int D = dm.dk > dm.dv ? dm.dk : dm.dv;
     const int R = dm.l / dm.d;
@@ -139,29 +146,6 @@ struct BwdArgs {
   BwdBufs w;
   BwdPlan pl;
 };
-
-// q / dO [B,T,Hq,D] -> [B,Hkv,D,T,16] with heads >= G zero-filled.
-template <typename T>
-__global__ __launch_bounds__(256) void k_transpose_heads(Dims dm, int D, const T* __restrict__ src,
-                                                         T* __restrict__ dst) {
-  __shared__ float tile[64][65];
-  const int bg = blockIdx.z, b = bg / dm.Hkv, g = bg % dm.Hkv;
-  const int r0 = blockIdx.x * 64;   // flattened (t, h16) index
-  const int f0 = blockIdx.y * 64;
-  const int Ts = dm.T * 16;
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int rr = i >> 6, ff = i & 63, rf = r0 + rr, f = f0 + ff;
-    const int t = rf >> 4, h = rf & 15;
-    float v = 0.f;
-    if (rf < Ts && f < D && h < dm.G) v = to_f32(src[((size_t)(b * dm.T + t) * dm.Hq + g * dm.G + h) * D + f]);
-    tile[rr][ff] = v;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int ff = i >> 6, rr = i & 63, rf = r0 + rr, f = f0 + ff;
-    if (f < D && rf < Ts) dst[((size_t)bg * D + f) * Ts + rf] = from_f32<T>(tile[rr][ff]);
-  }
-}
 
 // ---------------------------------------------------------------------------
 // dq: one wave per (b, t, g); columns = the G heads.
@@ -315,66 +299,137 @@ __global__ __launch_bounds__(256) void k_bwd_dq(Dims dm, BwdArgs a) {
 // ---------------------------------------------------------------------------
 enum KvMode { KV_CMP = 0, KV_WIN = 1, KV_SLC = 2 };
 
-template <typename T, int DK, int DV, int MODE>
-__global__ __launch_bounds__(64) void k_bwd_kv(Dims dm, BwdArgs a) {
-  const int lane = threadIdx.x, c16 = lane & 15, qd = lane >> 4;
+// Task of one workgroup: 64 keys [k0, k0+64) (klim bounds valid keys), query
+// positions p0..p1-1 (cmp, win) or plist[0..npos) (slc), partial output row
+// base (cmp, slc).  Returns false when the task has no positions.
+template <int MODE>
+__device__ __forceinline__ bool kv_task(const Dims& dm, const BwdArgs& a, int& bg, int& k0, int& klim, int& p0,
+                                        int& npos, const int*& plist, float*& outp, int W) {
   const BwdPlan& pl = a.pl;
-  const int G = dm.G;
-  const size_t BTH = (size_t)dm.B * dm.T * dm.Hq;
-  int bg, k0, klim;            // keys k0 .. k0+15, valid below klim
-  int p0 = 0, p1 = 0;          // position range (cmp, win)
-  const int* plist = nullptr;  // position list (slc)
-  int nlist = 0;
-  float* outp = nullptr;       // partial output [16][DK+DV] (cmp, slc)
-  int jblk = 0;
+  plist = nullptr;
+  outp = nullptr;
+  // Consecutive workgroups go to different XCDs, so the (b, g) index runs
+  // fastest: every XCD then receives an even share of the heavy tasks.
+  const int BG = dm.B * dm.Hkv;
   if (MODE == KV_CMP) {
-    const int seg = blockIdx.x % pl.nseg_cmp;
-    const int r = blockIdx.x / pl.nseg_cmp;
-    const int kt = r % pl.nkt_cmp;
-    bg = r / pl.nkt_cmp;
-    k0 = kt * 16;
+    bg = blockIdx.x % BG;
+    const int r = blockIdx.x / BG;
+    const int kg = r % pl.nkg_cmp;
+    const int seg = r / pl.nkg_cmp;
+    k0 = kg * 64;
     klim = dm.ncmp;
-    const int pf = k0 * dm.d + dm.l - 1;
-    p0 = pf + seg * kSegCmp;
-    p1 = min(dm.T, p0 + kSegCmp);
-    outp = a.w.part_cmp + ((size_t)blockIdx.x) * 16 * (DK + DV);
+    p0 = k0 * dm.d + dm.l - 1 + seg * kSegCmp;
+    npos = max(0, min(dm.T, p0 + kSegCmp) - p0);
+    outp = a.w.part_cmp + (((size_t)bg * pl.nkg_cmp + kg) * pl.nseg_cmp + seg) * 64 * W;
   } else if (MODE == KV_WIN) {
-    const int ntk = (dm.T + 15) / 16;
-    const int kt = blockIdx.x % ntk;
-    bg = blockIdx.x / ntk;
-    k0 = kt * 16;
+    const int nkg = (dm.T + 63) / 64;
+    const int kg = blockIdx.x % nkg;
+    bg = blockIdx.x / nkg;
+    k0 = kg * 64;
     klim = dm.T;
     p0 = k0;
-    p1 = min(dm.T, k0 + 15 + dm.w);
+    npos = min(dm.T, k0 + 63 + dm.w) - p0;
   } else {
-    const int nsub = dm.ls / 16;
-    const int seg = blockIdx.x % pl.nseg_slc;
-    int r = blockIdx.x / pl.nseg_slc;
-    const int sub = r % nsub;
-    r /= nsub;
-    jblk = r % dm.nsel;
-    bg = r / dm.nsel;
-    const int cnt = a.w.cnt[(size_t)bg * dm.nsel + jblk];
-    if (seg * kSegSlc >= cnt) return;
-    nlist = min(kSegSlc, cnt - seg * kSegSlc);
-    plist = a.w.list + (size_t)bg * dm.T * dm.n + a.w.lstart[(size_t)bg * dm.nsel + jblk] + seg * kSegSlc;
-    k0 = jblk * dm.ls + sub * 16;
-    klim = min(dm.T, (jblk + 1) * dm.ls);
-    const int slot = a.w.segoff[(size_t)bg * dm.nsel + jblk] + seg;
-    outp = a.w.part_slc + ((size_t)bg * pl.max_slc_seg + slot) * dm.ls * (DK + DV) + (size_t)sub * 16 * (DK + DV);
+    // segment slots of all (b, g) interleaved; unused slots hold -1
+    const int kc = blockIdx.x % pl.nkc_slc;
+    const int r = blockIdx.x / pl.nkc_slc;
+    bg = r % BG;
+    const int slot_i = r / BG;
+    const int tk = a.w.task[(size_t)bg * pl.max_slc_seg + slot_i];
+    if (tk < 0) return false;
+    const int j = tk / pl.nseg_slc, seg = tk % pl.nseg_slc;
+    const int cnt = a.w.cnt[(size_t)bg * dm.nsel + j];
+    npos = min(kSegSlc, cnt - seg * kSegSlc);
+    plist = a.w.list + (size_t)bg * dm.T * dm.n + a.w.lstart[(size_t)bg * dm.nsel + j] + seg * kSegSlc;
+    k0 = j * dm.ls + kc * 64;
+    klim = min(dm.T, (j + 1) * dm.ls);
+    p0 = 0;
+    const int slot = a.w.segoff[(size_t)bg * dm.nsel + j] + seg;
+    outp = a.w.part_slc + ((size_t)bg * pl.max_slc_seg + slot) * dm.ls * W + (size_t)kc * 64 * W;
   }
+  return npos > 0;
+}
+
+// dK / dV: one workgroup of four waves per 64 keys (16 keys per wave).  For
+// every pair of query positions the workgroup stages the 2 x 16 query rows of
+// q and dO in LDS, both row-major (A operand of S = Q K^T and dP = dO V^T) and
+// transposed (A operand of dK^T += Q^T dS and dV^T += dO^T P), plus the rows'
+// log-sum-exp, D_c and gate.  Staging is double-buffered: the next pair's
+// rows are loaded into registers while the current pair is computed.  The
+// positions of a selected-block list segment are read into LDS up front.
+template <typename T, int DK, int DV>
+struct KvStage {
+  // Row strides: RS keeps 16-byte rows; TS (a multiple of 4) keeps the
+  // transposed 4-row groups 8-byte aligned and spreads them over the banks.
+  static constexpr int QS = DK + 8, DS = DV + 8, TS = 32 + 4;
+  // A staging task is 4 consecutive rows x 8 features of q or dO.
+  static constexpr int NTASK = DK + DV, NCH = (NTASK + 255) / 256;
+  static constexpr size_t elems = (size_t)32 * QS + (size_t)DK * TS + (size_t)32 * DS + (size_t)DV * TS;
+  static constexpr size_t bytes = elems * sizeof(T) + 3 * 32 * sizeof(float);
+  Frag8<T> r[NCH][4];
+  float l2, Dv, gv;
+};
+
+__device__ __forceinline__ bf16 frag_at(const Frag8<bf16>& f, int e) { return f.v[e]; }
+__device__ __forceinline__ float frag_at(const Frag8<float>& f, int e) { return e < 4 ? f.lo[e] : f.hi[e - 4]; }
+typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_col4(bf16* p, bf16 a, bf16 b, bf16 c, bf16 d) {
+  *reinterpret_cast<bf16x4v*>(p) = bf16x4v{a, b, c, d};
+}
+__device__ __forceinline__ void store_col4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+}
+
+// Staging task u -> tensor (q or dO), feature chunk c8 and row quad rq.  Lanes
+// vary the low two bits of c8 fastest (64 contiguous bytes of a row per lane
+// quad), then rq, so the transposed 8-byte stores of a wave hit distinct banks.
+struct KvTaskMap {
+  bool is_q;
+  int c8, rq;
+};
+template <int DK, int DV>
+__device__ __forceinline__ KvTaskMap kv_task_map(int u) {
+  KvTaskMap m;
+  m.is_q = u < DK;
+  const int v = m.is_q ? u : u - DK;
+  m.c8 = (v & 3) + 4 * (v >> 5);
+  m.rq = (v >> 2) & 7;
+  return m;
+}
+
+template <typename T, int DK, int DV, int MODE>
+__global__ __launch_bounds__(256) void k_bwd_kv(Dims dm, BwdArgs a) {
+  using St = KvStage<T, DK, DV>;
+  constexpr int QS = St::QS, DS = St::DS, TS = St::TS;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  int* lpos = (int*)(smem_raw + 2 * St::bytes);        // [kSegSlc] list positions (slc)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15, qd = lane >> 4;
+  const int W = DK + DV;
+  int bg, k0, klim, p0, npos;
+  const int* plist;
+  float* outp;
+  if (!kv_task<MODE>(dm, a, bg, k0, klim, p0, npos, plist, outp, W)) return;
   const int b = bg / dm.Hkv, g = bg % dm.Hkv;
+  const int G = dm.G;
   const int c = MODE == KV_CMP ? 0 : (MODE == KV_SLC ? 1 : 2);
-  const int key = k0 + c16;   // this lane's key column
+  const size_t BTH = (size_t)dm.B * dm.T * dm.Hq;
+  if (MODE == KV_SLC) {
+    for (int i = tid; i < npos; i += 256) lpos[i] = plist[i];
+    __syncthreads();
+  }
+  auto position = [&](int ii) { return ii < npos ? (MODE == KV_SLC ? lpos[ii] : p0 + ii) : -1; };
+  const int key = k0 + wave * 16 + c16;
+  const bool wave_live = k0 + wave * 16 < klim;
   const bool kvalid = key < klim;
-  // B operands: K^T and V^T columns = this tile's 16 keys
+  const int kcl = min(key, klim - 1);
   const T *kr, *vr;
   if (MODE == KV_CMP) {
-    kr = (const T*)a.kc + ((size_t)(b * dm.ncmp + min(key, klim - 1)) * dm.Hkv + g) * DK;
-    vr = (const T*)a.vc + ((size_t)(b * dm.ncmp + min(key, klim - 1)) * dm.Hkv + g) * DV;
+    kr = (const T*)a.kc + ((size_t)(b * dm.ncmp + kcl) * dm.Hkv + g) * DK;
+    vr = (const T*)a.vc + ((size_t)(b * dm.ncmp + kcl) * dm.Hkv + g) * DV;
   } else {
-    kr = (const T*)a.k + ((size_t)(b * dm.T + min(key, klim - 1)) * dm.Hkv + g) * DK;
-    vr = (const T*)a.v + ((size_t)(b * dm.T + min(key, klim - 1)) * dm.Hkv + g) * DV;
+    kr = (const T*)a.k + ((size_t)(b * dm.T + kcl) * dm.Hkv + g) * DK;
+    vr = (const T*)a.v + ((size_t)(b * dm.T + kcl) * dm.Hkv + g) * DV;
   }
   Frag8<T> kf[DK / 32], vf[DV / 32];
 #pragma unroll
@@ -387,87 +442,149 @@ __global__ __launch_bounds__(64) void k_bwd_kv(Dims dm, BwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DV / 16; ++dt) dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float sc2 = dm.scale * kLog2e;
-  const T* qtb = (const T*)a.w.qt + (size_t)bg * DK * pl.Ts;
-  const T* dotb = (const T*)a.w.dot + (size_t)bg * DV * pl.Ts;
-  const int npos = (MODE == KV_SLC) ? nlist : max(0, p1 - p0);
-  for (int pi = 0; pi < npos; pi += 2) {
-    int pos[2];
-    bool pv[2];
+
+  St reg;
+  // global -> registers for the position pair (pp0, pp1): rows r = i*16 + h
+  auto gload = [&](int pp0, int pp1) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      pv[i] = pi + i < npos;
-      const int ii = pv[i] ? pi + i : pi;
-      pos[i] = (MODE == KV_SLC) ? plist[ii] : p0 + ii;
+    for (int cc = 0; cc < St::NCH; ++cc) {
+      const int u = tid + 256 * cc;
+      const KvTaskMap m = kv_task_map<DK, DV>(u);
+      const int pp = (m.rq >> 2) ? pp1 : pp0;
+      const int h0 = (m.rq & 3) * 4;
+      const int D = m.is_q ? DK : DV;
+      const T* src = (const T*)(m.is_q ? a.q : a.d_o);
+      const bool ok = u < St::NTASK && pp >= 0;
+      const size_t rb = ((size_t)(b * dm.T + (ok ? pp : 0)) * dm.Hq + g * G + h0) * D + m.c8 * 8;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        reg.r[cc][k] = (ok && h0 + k < G) ? load_frag(src + rb + (size_t)k * D) : zero_frag<T>();
     }
-    float pg[2][4], dsv[2][4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      // rows of this query tile: heads c16 (A operand) / 4qd + r (accumulator)
-      const bool hv = c16 < G && pv[i];
-      const size_t arow = (size_t)(b * dm.T + pos[i]) * dm.Hq + g * G + (c16 < G ? c16 : 0);
-      f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
-      const T* qp = (const T*)a.q + arow * DK + qd * 8;
-      const T* dp_ = (const T*)a.d_o + arow * DV + qd * 8;
-#pragma unroll
-      for (int ks = 0; ks < DK / 32; ++ks) mma(s, hv ? load_frag(qp + ks * 32) : zero_frag<T>(), kf[ks]);
-#pragma unroll
-      for (int ks = 0; ks < DV / 32; ++ks) mma(dp, hv ? load_frag(dp_ + ks * 32) : zero_frag<T>(), vf[ks]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int hh = qd * 4 + r;
-        bool v = hh < G && pv[i] && kvalid;
-        const int t = pos[i];
-        if (MODE == KV_CMP) v = v && key < ncmp_visible(t, dm.l, dm.d);
-        else if (MODE == KV_WIN) v = v && key <= t && t <= key + dm.w - 1;
-        else v = v && key <= t;
-        const size_t rr = (size_t)(b * dm.T + t) * dm.Hq + g * G + (hh < G ? hh : 0);
-        float p = 0.f, ds = 0.f;
-        if (v) {
-          const float gcv = a.w.gates[rr * 3 + c];
-          p = fast_exp2(s[r] * sc2 - a.lse[c * BTH + rr] * kLog2e);
-          ds = p * (gcv * dp[r] - a.w.Dc[c * BTH + rr]);
-          p *= gcv;
-        }
-        pg[i][r] = p;
-        dsv[i][r] = ds;
+    if (tid < 32) {
+      const int h = tid & 15, pp = (tid >> 4) ? pp1 : pp0;
+      reg.l2 = 0.f; reg.Dv = 0.f; reg.gv = 0.f;
+      if (pp >= 0 && h < G) {
+        const size_t rr = (size_t)(b * dm.T + pp) * dm.Hq + g * G + h;
+        const float l = a.lse[c * BTH + rr];
+        reg.l2 = l == kNegInf ? 0.f : l * kLog2e;
+        reg.Dv = a.w.Dc[c * BTH + rr];
+        reg.gv = a.w.gates[rr * 3 + c];
       }
     }
-    float pv8[8], ds8[8];
+  };
+  // registers -> LDS buffer: row-major and transposed copies
+  auto lstore = [&](int buf) {
+    T* Qr = (T*)(smem_raw + (size_t)buf * St::bytes);
+    T* Qt = Qr + 32 * QS;
+    T* Dr = Qt + DK * TS;
+    T* Dt = Dr + 32 * DS;
+    float* sst = (float*)(Dt + DV * TS);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      pv8[e] = pg[0][e]; pv8[4 + e] = pg[1][e];
-      ds8[e] = dsv[0][e]; ds8[4 + e] = dsv[1][e];
-    }
-    // P and dS enter sums over up to T*G query rows: carry them as bf16 hi + lo
-    // pairs (about 16 significant bits) so the key gradients stay accurate.
-    Frag8<T> pfr = to_frag<T>(pv8), dsf = to_frag<T>(ds8), plo, dslo;
-    if constexpr (sizeof(T) == 2) {
-      split_bf16(pv8, pfr, plo);
-      split_bf16(ds8, dsf, dslo);
-    }
-    // A operands from the transposed q / dO: row = feature, k = (position, head) pairs
-    const size_t f0 = (size_t)pos[0] * 16 + qd * 4, f1 = (size_t)pos[1] * 16 + qd * 4;
+    for (int cc = 0; cc < St::NCH; ++cc) {
+      const int u = tid + 256 * cc;
+      if (u >= St::NTASK) break;
+      const KvTaskMap m = kv_task_map<DK, DV>(u);
+      T* R = m.is_q ? Qr : Dr;
+      T* Tt = m.is_q ? Qt : Dt;
+      const int RS = m.is_q ? QS : DS;
 #pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt) {
-      const T* src = dotb + (size_t)(dt * 16 + c16) * pl.Ts;
-      float x[8];
-      load4(src + f0, x);
-      load4(src + f1, x + 4);
-      const Frag8<T> xf = to_frag<T>(x);
-      mma(dv[dt], xf, pfr);
-      if constexpr (sizeof(T) == 2) mma(dv[dt], xf, plo);
-    }
+      for (int k = 0; k < 4; ++k)
+        *reinterpret_cast<Frag8<T>*>(R + (4 * m.rq + k) * RS + m.c8 * 8) = reg.r[cc][k];
 #pragma unroll
-    for (int dt = 0; dt < DK / 16; ++dt) {
-      const T* src = qtb + (size_t)(dt * 16 + c16) * pl.Ts;
-      float x[8];
-      load4(src + f0, x);
-      load4(src + f1, x + 4);
-      const Frag8<T> xf = to_frag<T>(x);
-      mma(dk[dt], xf, dsf);
-      if constexpr (sizeof(T) == 2) mma(dk[dt], xf, dslo);
+      for (int e = 0; e < 8; ++e)
+        store_col4(Tt + (m.c8 * 8 + e) * TS + 4 * m.rq, frag_at(reg.r[cc][0], e), frag_at(reg.r[cc][1], e),
+                   frag_at(reg.r[cc][2], e), frag_at(reg.r[cc][3], e));
     }
+    if (tid < 32) {
+      sst[tid] = reg.l2;
+      sst[32 + tid] = reg.Dv;
+      sst[64 + tid] = reg.gv;
+    }
+  };
+
+  gload(position(0), position(1));
+  lstore(0);
+  __syncthreads();
+  for (int pi = 0; pi < npos; pi += 2) {
+    const int buf = (pi >> 1) & 1;
+    int pos[2] = {position(pi), position(pi + 1)};
+    const bool more = pi + 2 < npos;
+    if (more) gload(position(pi + 2), position(pi + 3));
+    const T* Qr = (const T*)(smem_raw + (size_t)buf * St::bytes);
+    const T* Qt = Qr + 32 * QS;
+    const T* Dr = Qt + DK * TS;
+    const T* Dt = Dr + 32 * DS;
+    const float* slse = (const float*)(Dt + DV * TS);
+    const float* sD = slse + 32;
+    const float* sg = sD + 32;
+    if (wave_live) {
+      float pg[2][4], dsv[2][4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f}, dpacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < DK / 32; ++ks)
+          mma(sacc, *reinterpret_cast<const Frag8<T>*>(Qr + (i * 16 + c16) * QS + ks * 32 + qd * 8), kf[ks]);
+#pragma unroll
+        for (int ks = 0; ks < DV / 32; ++ks)
+          mma(dpacc, *reinterpret_cast<const Frag8<T>*>(Dr + (i * 16 + c16) * DS + ks * 32 + qd * 8), vf[ks]);
+        const int t = pos[i];
+        bool pv = t >= 0 && kvalid;
+        if (MODE == KV_CMP) pv = pv && key < ncmp_visible(t, dm.l, dm.d);
+        else if (MODE == KV_WIN) pv = pv && key <= t && t <= key + dm.w - 1;
+        else pv = pv && key <= t;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rr = i * 16 + qd * 4 + r;
+          const bool v = pv && (qd * 4 + r) < G;
+          float p = 0.f, ds = 0.f;
+          if (v) {
+            p = fast_exp2(sacc[r] * sc2 - slse[rr]);
+            ds = p * (sg[rr] * dpacc[r] - sD[rr]);
+            p *= sg[rr];
+          }
+          pg[i][r] = p;
+          dsv[i][r] = ds;
+        }
+      }
+      float pv8[8], ds8[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pv8[e] = pg[0][e]; pv8[4 + e] = pg[1][e];
+        ds8[e] = dsv[0][e]; ds8[4 + e] = dsv[1][e];
+      }
+      // P and dS enter sums over up to T*G query rows: carry them as bf16 hi + lo
+      // pairs (about 16 significant bits) so the key gradients stay accurate.
+      Frag8<T> pfr = to_frag<T>(pv8), dsf = to_frag<T>(ds8), plo, dslo;
+      if constexpr (sizeof(T) == 2) {
+        split_bf16(pv8, pfr, plo);
+        split_bf16(ds8, dsf, dslo);
+      }
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt) {
+        const T* src = Dt + (dt * 16 + c16) * TS + qd * 4;
+        float x[8];
+        load4(src, x);
+        load4(src + 16, x + 4);
+        const Frag8<T> xf = to_frag<T>(x);
+        mma(dv[dt], xf, pfr);
+        if constexpr (sizeof(T) == 2) mma(dv[dt], xf, plo);
+      }
+#pragma unroll
+      for (int dt = 0; dt < DK / 16; ++dt) {
+        const T* src = Qt + (dt * 16 + c16) * TS + qd * 4;
+        float x[8];
+        load4(src, x);
+        load4(src + 16, x + 4);
+        const Frag8<T> xf = to_frag<T>(x);
+        mma(dk[dt], xf, dsf);
+        if constexpr (sizeof(T) == 2) mma(dk[dt], xf, dslo);
+      }
+    }
+    if (more) lstore(buf ^ 1);
+    __syncthreads();
   }
+  if (!wave_live) return;
   // write: lane holds key column c16, features dt*16 + 4qd + r
   if (MODE == KV_WIN) {
     if (!kvalid) return;
@@ -479,7 +596,7 @@ __global__ __launch_bounds__(64) void k_bwd_kv(Dims dm, BwdArgs a) {
 #pragma unroll
     for (int dt = 0; dt < DV / 16; ++dt) store4(dvp + dt * 16, dv[dt][0], dv[dt][1], dv[dt][2], dv[dt][3]);
   } else {
-    float* op = outp + (size_t)c16 * (DK + DV) + qd * 4;
+    float* op = outp + (size_t)(wave * 16 + c16) * W + qd * 4;
 #pragma unroll
     for (int dt = 0; dt < DK / 16; ++dt)
       store4(op + dt * 16, dm.scale * dk[dt][0], dm.scale * dk[dt][1], dm.scale * dk[dt][2], dm.scale * dk[dt][3]);
@@ -488,21 +605,26 @@ __global__ __launch_bounds__(64) void k_bwd_kv(Dims dm, BwdArgs a) {
   }
 }
 
+template <typename T, int DK, int DV>
+static size_t kv_lds() {
+  return 2 * KvStage<T, DK, DV>::bytes + kSegSlc * sizeof(int);
+}
+
 // Sum the compressed-key segments in order: dkc/dvc [B,Hkv,ncmp,D].
 __global__ __launch_bounds__(256) void k_reduce_cmp(Dims dm, BwdArgs a) {
   const BwdPlan& pl = a.pl;
   const int W = dm.dk + dm.dv;
-  const int r = blockIdx.x;              // (bg, kt)
-  const int kt = r % pl.nkt_cmp, bg = r / pl.nkt_cmp;
-  for (int i = threadIdx.x; i < 16 * W; i += 256) {
-    const int kk = i / W, e = i % W, key = kt * 16 + kk;
+  const int r = blockIdx.x;              // (bg, kg)
+  const int kg = r % pl.nkg_cmp, bg = r / pl.nkg_cmp;
+  // segments of this key group start at its first key's first visible position
+  const int pf = (kg * 64) * dm.d + dm.l - 1;
+  for (int i = threadIdx.x; i < 64 * W; i += 256) {
+    const int kk = i / W, e = i % W, key = kg * 64 + kk;
     if (key >= dm.ncmp) continue;
-    // segments of this key tile start at its first visible position
-    const int pf = (kt * 16) * dm.d + dm.l - 1;
     float s = 0.f;
     for (int seg = 0; seg < pl.nseg_cmp; ++seg) {
       if (pf + seg * kSegCmp >= dm.T) break;
-      s += a.w.part_cmp[(((size_t)r * pl.nseg_cmp + seg) * 16 + kk) * W + e];
+      s += a.w.part_cmp[(((size_t)r * pl.nseg_cmp + seg) * 64 + kk) * W + e];
     }
     if (e < dm.dk) a.w.dkc[((size_t)bg * dm.ncmp + key) * dm.dk + e] = s;
     else a.w.dvc[((size_t)bg * dm.ncmp + key) * dm.dv + e - dm.dk] = s;
@@ -561,17 +683,23 @@ __global__ __launch_bounds__(256) void k_rev_scan(Dims dm, BwdArgs a) {
     a.w.cnt[(size_t)bg * dm.nsel + j] = tot;
   }
   __syncthreads();
+  __shared__ int nslots;
+  int* task = a.w.task + (size_t)bg * pl.max_slc_seg;
   if (threadIdx.x == 0) {
     int run = 0, srun = 0;
     for (int j = 0; j < dm.nsel; ++j) {
       const int c = a.w.cnt[(size_t)bg * dm.nsel + j];
+      const int ns = (c + kSegSlc - 1) / kSegSlc;
       a.w.lstart[(size_t)bg * dm.nsel + j] = run;
       a.w.segoff[(size_t)bg * dm.nsel + j] = srun;
+      for (int sg = 0; sg < ns; ++sg) task[srun + sg] = j * pl.nseg_slc + sg;
       run += c;
-      srun += (c + kSegSlc - 1) / kSegSlc;
+      srun += ns;
     }
+    nslots = srun;
   }
   __syncthreads();
+  for (int i = nslots + threadIdx.x; i < pl.max_slc_seg; i += 256) task[i] = -1;
   for (int j = threadIdx.x; j < dm.nsel; j += 256) {
     int run = a.w.lstart[(size_t)bg * dm.nsel + j];
     for (int ch = 0; ch < pl.nchunk; ++ch) {
@@ -612,29 +740,32 @@ struct Gemm {
   int accumulate;
 };
 
+// blockIdx.z = split index: k range [z*kc, (z+1)*kc); with a split the result
+// goes to part[z][M][N] and is summed afterwards in split order.
 template <typename TA, typename TB>
-__global__ __launch_bounds__(256) void k_gemm(Gemm gm) {
+__global__ __launch_bounds__(256) void k_gemm(Gemm gm, int kc, float* part) {
   __shared__ float As[32][64 + 4];
   __shared__ float Bs[32][64 + 4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, kq = lane >> 4;
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int kbeg = blockIdx.z * kc, kend = min(gm.K, kbeg + kc);
   const TA* A = (const TA*)gm.A;
   const TB* B = (const TB*)gm.B;
   f32x4 acc[2][2];
   for (int i = 0; i < 2; ++i)
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const bool a_k_fast = gm.sak == 1, b_n_fast = gm.sbn == 1;
-  for (int k0 = 0; k0 < gm.K; k0 += 32) {
+  for (int k0 = kbeg; k0 < kend; k0 += 32) {
     for (int i = tid; i < 64 * 32; i += 256) {
       int mm, kk;
       if (a_k_fast) { kk = i & 31; mm = i >> 5; } else { mm = i & 63; kk = i >> 6; }
       const int m = m0 + mm, k = k0 + kk;
-      As[kk][mm] = (m < gm.M && k < gm.K) ? to_f32(A[m * gm.sam + k * gm.sak]) : 0.f;
+      As[kk][mm] = (m < gm.M && k < kend) ? to_f32(A[m * gm.sam + k * gm.sak]) : 0.f;
       int nn, kb;
       if (b_n_fast) { nn = i & 63; kb = i >> 6; } else { kb = i & 31; nn = i >> 5; }
       const int n = n0 + nn, k2 = k0 + kb;
-      Bs[kb][nn] = (n < gm.N && k2 < gm.K) ? to_f32(B[k2 * gm.sbk + n * gm.sbn]) : 0.f;
+      Bs[kb][nn] = (n < gm.N && k2 < kend) ? to_f32(B[k2 * gm.sbk + n * gm.sbn]) : 0.f;
     }
     __syncthreads();
 #pragma unroll
@@ -654,34 +785,72 @@ __global__ __launch_bounds__(256) void k_gemm(Gemm gm) {
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + (wave >> 1) * 32 + i * 16 + kq * 4 + r;
         if (m >= gm.M) continue;
-        float* cp = gm.C + (long long)m * gm.ldc + n;
-        *cp = gm.accumulate ? *cp + acc[i][j][r] : acc[i][j][r];
+        if (part) {
+          part[((size_t)blockIdx.z * gm.M + m) * gm.N + n] = acc[i][j][r];
+        } else {
+          float* cp = gm.C + (long long)m * gm.ldc + n;
+          *cp = gm.accumulate ? *cp + acc[i][j][r] : acc[i][j][r];
+        }
       }
     }
 }
 
+__global__ __launch_bounds__(256) void k_gemm_reduce(Gemm gm, int nsplit, const float* __restrict__ part) {
+  const size_t id = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= (size_t)gm.M * gm.N) return;
+  const int m = id / gm.N, n = id % gm.N;
+  float s = 0.f;
+  for (int z = 0; z < nsplit; ++z) s += part[(size_t)z * gm.M * gm.N + id];
+  float* cp = gm.C + (long long)m * gm.ldc + n;
+  *cp = gm.accumulate ? *cp + s : s;
+}
+
+// Splits K so that about 512 workgroups run; partials need nsplit*M*N floats of part.
 template <typename TA, typename TB>
-static hipError_t gemm(const Gemm& g, hipStream_t s) {
+static hipError_t gemm(const Gemm& g, float* part, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
-  dim3 grid((g.N + 63) / 64, (g.M + 63) / 64);
-  k_gemm<TA, TB><<<grid, 256, 0, s>>>(g);
+  const int tiles = ((g.N + 63) / 64) * ((g.M + 63) / 64);
+  int nsplit = part ? (512 + tiles - 1) / tiles : 1;
+  nsplit = min(nsplit, min(kMaxSplit, max(1, g.K / 256)));
+  const int kc = ((g.K + nsplit - 1) / nsplit + 31) & ~31;
+  nsplit = (g.K + kc - 1) / kc;
+  dim3 grid((g.N + 63) / 64, (g.M + 63) / 64, nsplit);
+  if (nsplit == 1) {
+    k_gemm<TA, TB><<<grid, 256, 0, s>>>(g, kc, nullptr);
+    return hipGetLastError();
+  }
+  k_gemm<TA, TB><<<grid, 256, 0, s>>>(g, kc, part);
+  const size_t mn = (size_t)g.M * g.N;
+  k_gemm_reduce<<<(unsigned)((mn + 255) / 256), 256, 0, s>>>(g, nsplit, part);
   return hipGetLastError();
 }
 
-// Column sums: out[c] (+)= sum_r in[r*ld + c].  Fixed order per column.
-__global__ __launch_bounds__(256) void k_colsum(int R, int Cn, long long ld, const float* __restrict__ in,
-                                                float* __restrict__ out, int accumulate) {
-  __shared__ float part[4][64];
-  const int c = blockIdx.x * 64 + (threadIdx.x & 63), rg = threadIdx.x >> 6;
+// Column sums out[c] = sum_r in[r*ld + c] in two stages with a fixed order:
+// row split z sums rows z, z + nsplit, ...; then the splits are added in order.
+__global__ __launch_bounds__(256) void k_colsum_part(int R, int Cn, long long ld, int nsplit,
+                                                     const float* __restrict__ in, float* __restrict__ part) {
+  const int c = blockIdx.x * 256 + threadIdx.x, z = blockIdx.y;
+  if (c >= Cn) return;
   float s = 0.f;
-  if (c < Cn)
-    for (int r = rg; r < R; r += 4) s += in[(long long)r * ld + c];
-  part[rg][threadIdx.x & 63] = s;
-  __syncthreads();
-  if (rg == 0 && c < Cn) {
-    const float v = part[0][threadIdx.x] + part[1][threadIdx.x] + part[2][threadIdx.x] + part[3][threadIdx.x];
-    out[c] = accumulate ? out[c] + v : v;
-  }
+  for (int r = z; r < R; r += nsplit) s += in[(long long)r * ld + c];
+  part[(size_t)z * Cn + c] = s;
+}
+
+__global__ __launch_bounds__(256) void k_colsum_fin(int Cn, int nsplit, const float* __restrict__ part,
+                                                    float* __restrict__ out) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= Cn) return;
+  float s = 0.f;
+  for (int z = 0; z < nsplit; ++z) s += part[(size_t)z * Cn + c];
+  out[c] = s;
+}
+
+static hipError_t colsum(int R, int Cn, long long ld, const float* in, float* out, float* part, hipStream_t s) {
+  const int nsplit = min(kMaxSplit, max(1, R / 64));
+  dim3 g1((Cn + 255) / 256, nsplit);
+  k_colsum_part<<<g1, 256, 0, s>>>(R, Cn, ld, nsplit, in, part);
+  k_colsum_fin<<<(Cn + 255) / 256, 256, 0, s>>>(Cn, nsplit, part, out);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -813,21 +982,19 @@ static hipError_t phi_bwd(const Dims& dm, const BwdArgs& a, const nsa_phi_weight
   k_phi_act<T><<<(unsigned)((rows * H + 255) / 256), 256, 0, s>>>(dm, a.w.y, (const T*)w.b1, a.w.act, a.w.hid);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // db2 = colsum(dout); dW2 = hid^T dout
-  k_colsum<<<(D + 63) / 64, 256, 0, s>>>((int)rows, D, D, dcmp, (float*)gr.b2, 0);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = colsum((int)rows, D, D, dcmp, (float*)gr.b2, a.w.gpart, s)) != hipSuccess) return e;
   {
     Gemm g{H, D, (int)rows, a.w.hid, 1, H, dcmp, D, 1, (float*)gr.w2, D, 0};
-    if ((e = gemm<float, float>(g, s)) != hipSuccess) return e;
+    if ((e = gemm<float, float>(g, a.w.gpart, s)) != hipSuccess) return e;
   }
   // dh = dout W2^T; da = dh * gelu'(act)
   {
     Gemm g{(int)rows, H, D, dcmp, D, 1, w.w2, 1, D, a.w.dh, H, 0};
-    if ((e = gemm<float, T>(g, s)) != hipSuccess) return e;
+    if ((e = gemm<float, T>(g, nullptr, s)) != hipSuccess) return e;
   }
   k_phi_dact<<<(unsigned)((rows * H + 255) / 256), 256, 0, s>>>(rows * H, a.w.act, a.w.dh);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  k_colsum<<<(H + 63) / 64, 256, 0, s>>>((int)rows, H, H, a.w.dh, (float*)gr.b1, 0);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = colsum((int)rows, H, H, a.w.dh, (float*)gr.b1, a.w.gpart, s)) != hipSuccess) return e;
   // dW1 chunks
   {
     dim3 grid((H + 63) / 64, (dm.d * D + 63) / 64, R);
@@ -837,10 +1004,10 @@ static hipError_t phi_bwd(const Dims& dm, const BwdArgs& a, const nsa_phi_weight
   // du = da W1^T -> token gradient and dpe
   {
     Gemm g{(int)rows, dm.l * D, H, a.w.dh, H, 1, w.w1, 1, H, a.w.du, (long long)dm.l * D, 0};
-    if ((e = gemm<float, T>(g, s)) != hipSuccess) return e;
+    if ((e = gemm<float, T>(g, nullptr, s)) != hipSuccess) return e;
   }
-  k_colsum<<<(dm.l * D + 63) / 64, 256, 0, s>>>((int)rows, dm.l * D, (long long)dm.l * D, a.w.du, (float*)gr.pe, 0);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = colsum((int)rows, dm.l * D, (long long)dm.l * D, a.w.du, (float*)gr.pe, a.w.gpart, s)) != hipSuccess)
+    return e;
   const size_t total = (size_t)dm.B * dm.T * dm.Hkv * D;
   k_phi_dx<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(dm, D, a.w.du, 1, dx);
   return hipGetLastError();
@@ -868,40 +1035,40 @@ static hipError_t bwd_impl(const Dims& dm, const nsa_bwd_args* args, BwdArgs& a,
   // stage 0: gates, gate backward, row terms
   if ((e = mark()) != hipSuccess) return e;
   if ((e = launch_gate(dm, dm.B * dm.T, a.x, a.wg, a.w.gates, s)) != hipSuccess) return e;
-  // stage 1: transposed copies
+  // stage 1: transposed copies of k and k_cmp (A operand of dq^T += K^T dS^T)
   if ((e = mark()) != hipSuccess) return e;
   if ((e = launch_transpose_seq(dm, dm.B, dm.T, dm.Hkv, DK, dm.Tp, a.k, a.w.kt, s)) != hipSuccess) return e;
   if (dm.ncmp > 0 &&
       (e = launch_transpose_seq(dm, dm.B, dm.ncmp, dm.Hkv, DK, dm.ncmp_pad, a.kc, a.w.kct, s)) != hipSuccess)
     return e;
-  {
-    dim3 gq((pl.Ts + 63) / 64, (DK + 63) / 64, BG), gd((pl.Ts + 63) / 64, (DV + 63) / 64, BG);
-    k_transpose_heads<T><<<gq, 256, 0, s>>>(dm, DK, (const T*)a.q, (T*)a.w.qt);
-    k_transpose_heads<T><<<gd, 256, 0, s>>>(dm, DV, (const T*)a.d_o, (T*)a.w.dot);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
   // stage 2: row terms D_c, dz, then dq
   if ((e = mark()) != hipSuccess) return e;
   k_bwd_dq<T, DK, DV, true><<<((dm.T + 3) / 4) * BG, 256, 0, s>>>(dm, a);
   k_bwd_dq<T, DK, DV, false><<<((dm.T + 3) / 4) * BG, 256, 0, s>>>(dm, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // stage 3: compressed keys
+  const size_t klds = kv_lds<T, DK, DV>();
+  if (klds > 64 * 1024) {
+    hipFuncSetAttribute((const void*)k_bwd_kv<T, DK, DV, KV_CMP>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)klds);
+    hipFuncSetAttribute((const void*)k_bwd_kv<T, DK, DV, KV_WIN>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)klds);
+    hipFuncSetAttribute((const void*)k_bwd_kv<T, DK, DV, KV_SLC>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)klds);
+  }
   if ((e = mark()) != hipSuccess) return e;
   if (dm.ncmp > 0) {
-    k_bwd_kv<T, DK, DV, KV_CMP><<<BG * pl.nkt_cmp * pl.nseg_cmp, 64, 0, s>>>(dm, a);
-    k_reduce_cmp<<<BG * pl.nkt_cmp, 256, 0, s>>>(dm, a);
+    k_bwd_kv<T, DK, DV, KV_CMP><<<BG * pl.nkg_cmp * pl.nseg_cmp, 256, klds, s>>>(dm, a);
+    k_reduce_cmp<<<BG * pl.nkg_cmp, 256, 0, s>>>(dm, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // stage 4: window keys (writes dk, dv)
   if ((e = mark()) != hipSuccess) return e;
-  k_bwd_kv<T, DK, DV, KV_WIN><<<BG * ((dm.T + 15) / 16), 64, 0, s>>>(dm, a);
+  k_bwd_kv<T, DK, DV, KV_WIN><<<BG * ((dm.T + 63) / 64), 256, klds, s>>>(dm, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // stage 5: selected blocks (adds into dk, dv)
   if ((e = mark()) != hipSuccess) return e;
   k_rev_hist<<<BG * pl.nchunk, 64, dm.nsel * sizeof(int), s>>>(dm, a);
   k_rev_scan<<<BG, 256, 0, s>>>(dm, a);
   k_rev_fill<<<BG * pl.nchunk, 64, dm.nsel * sizeof(int), s>>>(dm, a);
-  k_bwd_kv<T, DK, DV, KV_SLC><<<BG * dm.nsel * (dm.ls / 16) * pl.nseg_slc, 64, 0, s>>>(dm, a);
+  k_bwd_kv<T, DK, DV, KV_SLC><<<BG * pl.max_slc_seg * pl.nkc_slc, 256, klds, s>>>(dm, a);
   k_reduce_slc<<<BG * dm.nsel, 256, 0, s>>>(dm, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // stage 6: phi
@@ -924,7 +1091,7 @@ static hipError_t bwd_impl(const Dims& dm, const nsa_bwd_args* args, BwdArgs& a,
   if ((e = mark()) != hipSuccess) return e;
   {
     Gemm g{dm.C, 3 * dm.Hq, dm.B * dm.T, a.x, 1, dm.C, a.w.dz, 3 * dm.Hq, 1, a.dwg, 3 * dm.Hq, 0};
-    if ((e = gemm<T, float>(g, s)) != hipSuccess) return e;
+    if ((e = gemm<T, float>(g, a.w.gpart, s)) != hipSuccess) return e;
   }
   return mark();
 }
