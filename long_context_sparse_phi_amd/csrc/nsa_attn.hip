@@ -21,6 +21,19 @@
 
 namespace nsa {
 
+// One 32-key tile of a selected block, held in registers: the K rows of the
+// permuted key order (two MFMA sub-tiles) and the V^T fragments.
+template <typename T, int DK, int DV>
+struct SlcTile {
+  Frag8<T> k[2][DK / 32];
+  Frag8<T> v[DV / 16];
+};
+
+// Walks the (block, 32-key tile) sequence of one position's selection.
+struct SlcCursor {
+  int si, kt, kend;
+};
+
 template <typename T, int DK, int DV, typename OT>
 __global__ __launch_bounds__(256) void k_slc(Dims dm, SlcArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -41,7 +54,9 @@ __global__ __launch_bounds__(256) void k_slc(Dims dm, SlcArgs a) {
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) qf[ks] = cv ? load_frag(qp + ks * 32) : zero_frag<T>();
   }
+  // the n block indices of this position, one per lane (n <= 32)
   const int* ids = a.idx + ((size_t)(b * dm.T + t) * dm.Hkv + g) * dm.n;
+  const int myid = lane < dm.n ? ids[lane] : -1;
   const float sc2 = dm.scale * kLog2e;
   float m = kNegInf, ls = 0.f;
   f32x4 oacc[DV / 16];
@@ -51,51 +66,89 @@ __global__ __launch_bounds__(256) void k_slc(Dims dm, SlcArgs a) {
   const T* kbase = (const T*)a.k + ((size_t)b * dm.T * dm.Hkv + g) * DK + qd * 8;
   const T* vtb = (const T*)a.vt + (size_t)(b * dm.Hkv + g) * DV * dm.Tp + qd * 8;
   const int krow = (c16 >> 2) * 8 + (c16 & 3);
-  for (int si = 0; si < dm.n; ++si) {
-    const int j = ids[si];
-    if (j < 0) break;
-    const int kend = min((j + 1) * dm.ls, t + 1);
-    for (int kt = j * dm.ls; kt < kend; kt += 32) {
-      f32x4 s[2];
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        s[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int key = min(kt + krow + sub * 4, dm.T - 1);
-        const T* kp = kbase + (size_t)key * kstride;
-#pragma unroll
-        for (int ks = 0; ks < DK / 32; ++ks) mma(s[sub], load_frag(kp + ks * 32), qf[ks]);
-      }
-      Frag8<T> vf[DV / 16];
-#pragma unroll
-      for (int dt = 0; dt < DV / 16; ++dt) vf[dt] = load_frag(vtb + (size_t)(dt * 16 + c16) * dm.Tp + kt);
-      float v[8], mx = kNegInf;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int key = kt + qd * 8 + e;
-        v[e] = key < kend ? s[e >> 2][e & 3] * sc2 : kNegInf;
-        mx = fmaxf(mx, v[e]);
-      }
-      mx = fmaxf(mx, xor16f(mx, lane));
-      mx = fmaxf(mx, xor32f(mx, lane));
-      const float mn = fmaxf(m, mx);
-      const float mref = mn == kNegInf ? 0.f : mn;
-      const float alpha = fast_exp2(m - mref);
-      float p[8], psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { p[e] = fast_exp2(v[e] - mref); psum += p[e]; }
-      ls = ls * alpha + psum;
-      m = mn;
-      Frag8<T> pf = to_frag<T>(p);
-#pragma unroll
-      for (int dt = 0; dt < DV / 16; ++dt) {
-        oacc[dt] *= alpha;
-        mma(oacc[dt], vf[dt], pf);
-      }
+
+  // first tile of block slot si at or after it, or si = n when none is left
+  auto open_block = [&](SlcCursor& c) {
+    for (; c.si < dm.n; ++c.si) {
+      const int j = __builtin_amdgcn_readlane(myid, c.si);
+      if (j < 0) { c.si = dm.n; return; }
+      c.kt = j * dm.ls;
+      c.kend = min((j + 1) * dm.ls, t + 1);
+      if (c.kt < c.kend) return;
     }
+  };
+  auto advance = [&](SlcCursor& c) {
+    c.kt += 32;
+    if (c.kt < c.kend) return;
+    ++c.si;
+    open_block(c);
+  };
+  auto load_tile = [&](SlcTile<T, DK, DV>& tl, const SlcCursor& c) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const int key = min(c.kt + krow + sub * 4, dm.T - 1);
+      const T* kp = kbase + (size_t)key * kstride;
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks) tl.k[sub][ks] = load_frag(kp + ks * 32);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt) tl.v[dt] = load_frag(vtb + (size_t)(dt * 16 + c16) * dm.Tp + c.kt);
+  };
+  auto compute_tile = [&](const SlcTile<T, DK, DV>& tl, const SlcCursor& c) {
+    f32x4 sacc[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      sacc[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks) mma(sacc[sub], tl.k[sub][ks], qf[ks]);
+    }
+    float v[8], mx = kNegInf;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int key = c.kt + qd * 8 + e;
+      v[e] = key < c.kend ? sacc[e >> 2][e & 3] * sc2 : kNegInf;
+      mx = fmaxf(mx, v[e]);
+    }
+    mx = fmaxf(mx, xor16f(mx, lane));
+    mx = fmaxf(mx, xor32f(mx, lane));
+    const float mn = fmaxf(m, mx);
+    const float mref = mn == kNegInf ? 0.f : mn;
+    const float alpha = fast_exp2(m - mref);
+    float p[8], psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { p[e] = fast_exp2(v[e] - mref); psum += p[e]; }
+    ls = ls * alpha + psum;
+    m = mn;
+    const Frag8<T> pf = to_frag<T>(p);
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt) {
+      oacc[dt] *= alpha;
+      mma(oacc[dt], tl.v[dt], pf);
+    }
+  };
+
+  // Two register tiles in flight: the next tile's loads are issued before the
+  // current tile is computed, so memory latency overlaps the MFMA work.
+  SlcTile<T, DK, DV> ta, tb;
+  SlcCursor ca{0, 0, 0};
+  open_block(ca);
+  if (ca.si < dm.n) load_tile(ta, ca);
+  while (ca.si < dm.n) {
+    SlcCursor cb = ca;
+    advance(cb);
+    if (cb.si < dm.n) load_tile(tb, cb);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_tile(ta, ca);
+    if (cb.si >= dm.n) break;
+    ca = cb;
+    advance(ca);
+    if (ca.si < dm.n) load_tile(ta, ca);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_tile(tb, cb);
   }
   float tot = ls + xor16f(ls, lane);
   tot += xor32f(tot, lane);
-  const float inv = 1.f / tot;
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
   if (cv) {
     OT* op = (OT*)a.o + qrow * DV + qd * 4;
 #pragma unroll

@@ -22,6 +22,8 @@
 // that every lane holds one column's scores for 8 keys, which is directly the
 // B operand of O^T = V^T P^T.  Keys inside a 32-key tile are permuted so that
 // lane group qd (= lane/16) ends up holding keys 8*qd .. 8*qd+7.
+#include <type_traits>
+
 #include "nsa_common.hpp"
 #include "nsa_kernels.hpp"
 
@@ -44,15 +46,16 @@ constexpr size_t cmp_tile_elems() {
   return (size_t)kCmpKT * cmp_ks<DK>() + (PB ? (size_t)DV * kCmpVS : 0);
 }
 
-template <typename T, int DK, int DV, int NCT, bool PB, typename OT>
-__global__ __launch_bounds__(256) void k_cmp(Dims dm, CmpArgs a, int nselp, int njt) {
+template <typename T, int DK, int DV, int NCT, int NW, bool PB, typename OT>
+__global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nselp, int njt) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   constexpr int KS = cmp_ks<DK>();
   constexpr size_t TE = cmp_tile_elems<T, DK, DV, PB>();
+  constexpr int NT = NW * 64;
   T* tiles = (T*)smem_raw;                                  // [2][TE]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, qd = lane >> 4;
-  const int G = dm.G, PW = 16 * NCT / G, PWG = 4 * PW;
+  const int G = dm.G, PW = 16 * NCT / G, PWG = NW * PW;
   const int ntiles = (dm.T + PWG - 1) / PWG;
   int unit, tile;
   xcd_map(blockIdx.x, dm.B * dm.Hkv, ntiles, unit, tile);
@@ -62,6 +65,8 @@ __global__ __launch_bounds__(256) void k_cmp(Dims dm, CmpArgs a, int nselp, int 
   const bool wave_live = t0 < dm.T;
   const int nmax_wg = ncmp_visible(min(dm.T - 1, twg + PWG - 1), dm.l, dm.d);
   const int nmax = wave_live ? ncmp_visible(min(dm.T - 1, t0 + PW - 1), dm.l, dm.d) : 0;
+  // keys below nfull are visible to every column of the wave (no masking)
+  const int nfull = (wave_live && t0 + PW - 1 < dm.T) ? ncmp_visible(t0, dm.l, dm.d) : 0;
   float* prow = (float*)(smem_raw + 2 * TE * sizeof(T)) + (size_t)wave * PW * nselp;
   if (PB)
     for (int i = lane; i < PW * nselp; i += 64) prow[i] = 0.f;
@@ -105,21 +110,23 @@ __global__ __launch_bounds__(256) void k_cmp(Dims dm, CmpArgs a, int nselp, int 
   }
 
   // cooperative tile loader
-  constexpr int KCH = kCmpKT * DK / 8 / 256;        // 16-byte chunks per thread (K)
-  constexpr int VCH = PB ? DV * kCmpKT / 8 / 256 : 0;
+  constexpr int KCH = kCmpKT * DK / 8 / NT;        // 16-byte chunks per thread (K)
+  constexpr int VCH = PB ? DV * kCmpKT / 8 / NT : 0;
+  static_assert(KCH * NT == kCmpKT * DK / 8, "K tile must split evenly over the workgroup");
+  static_assert(!PB || VCH * NT == DV * kCmpKT / 8, "V tile must split evenly over the workgroup");
   Frag8<T> kr[KCH], vr[VCH > 0 ? VCH : 1];
   const T* kcb = (const T*)a.kc + ((size_t)b * dm.ncmp * dm.Hkv + g) * DK;
   const T* vtb = (const T*)a.vct + (size_t)(b * dm.Hkv + g) * DV * dm.ncmp_pad;
   auto gload = [&](int kt) {
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
-      const int idx = threadIdx.x + 256 * c, row = idx / (DK / 8), c8 = idx % (DK / 8);
+      const int idx = threadIdx.x + NT * c, row = idx / (DK / 8), c8 = idx % (DK / 8);
       const int key = min(kt + row, dm.ncmp - 1);
       kr[c] = load_frag(kcb + (size_t)key * dm.Hkv * DK + c8 * 8);
     }
 #pragma unroll
     for (int c = 0; c < VCH; ++c) {
-      const int idx = threadIdx.x + 256 * c, row = idx / (kCmpKT / 8), c8 = idx % (kCmpKT / 8);
+      const int idx = threadIdx.x + NT * c, row = idx / (kCmpKT / 8), c8 = idx % (kCmpKT / 8);
       vr[c] = load_frag(vtb + (size_t)row * dm.ncmp_pad + kt + c8 * 8);
     }
   };
@@ -128,18 +135,133 @@ __global__ __launch_bounds__(256) void k_cmp(Dims dm, CmpArgs a, int nselp, int 
     T* vt_ = kt_ + (size_t)kCmpKT * KS;
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
-      const int idx = threadIdx.x + 256 * c, row = idx / (DK / 8), c8 = idx % (DK / 8);
+      const int idx = threadIdx.x + NT * c, row = idx / (DK / 8), c8 = idx % (DK / 8);
       *reinterpret_cast<Frag8<T>*>(kt_ + row * KS + c8 * 8) = kr[c];
     }
 #pragma unroll
     for (int c = 0; c < VCH; ++c) {
-      const int idx = threadIdx.x + 256 * c, row = idx / (kCmpKT / 8), c8 = idx % (kCmpKT / 8);
+      const int idx = threadIdx.x + NT * c, row = idx / (kCmpKT / 8), c8 = idx % (kCmpKT / 8);
       *reinterpret_cast<Frag8<T>*>(vt_ + row * kCmpVS + c8 * 8) = vr[c];
     }
   };
 
   const int krow = (c16 >> 2) * 8 + (c16 & 3);
   const int jstep = 32 * dm.d / dm.ls;
+
+  // scores of one 32-key half tile: S^T = K Q^T for all column tiles
+  auto scores = [&](const T* ktile, int h, f32x4 (&s)[2][NCT]) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      const T* kp = ktile + (h * 32 + krow + sub * 4) * KS + qd * 8;
+      Frag8<T> kf[DK / 32];
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks) kf[ks] = *reinterpret_cast<const Frag8<T>*>(kp + ks * 32);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) s[sub][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) mma(s[sub][ct], kf[ks], qf[ct][ks]);
+    }
+  };
+
+  // pass A: online max / sum of exp2 per column
+  auto pass_a = [&](const f32x4 (&s)[2][NCT], int kt, auto masked) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      float v[8], mx = kNegInf;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[e] = s[e >> 2][ct][e & 3] * sc2;
+        if (masked) v[e] = kt + qd * 8 + e < nvis[ct] ? v[e] : kNegInf;
+        mx = fmaxf(mx, v[e]);
+      }
+      mx = fmaxf(mx, xor16f(mx, lane));
+      mx = fmaxf(mx, xor32f(mx, lane));
+      const float mn = fmaxf(m[ct], mx);
+      const float mref = mn == kNegInf ? 0.f : mn;
+      float acc = ls[ct] * fast_exp2(m[ct] - mref);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += fast_exp2(v[e] - mref);
+      ls[ct] = acc;
+      m[ct] = mn;
+    }
+  };
+
+  // pass B: exact probabilities, O += P V, remapped scores into prow
+  auto pass_b = [&](const f32x4 (&s)[2][NCT], const T* vtile, int h, int kt, auto masked) {
+    const int j0 = (kt / 32) * jstep;
+    f32x4 cr[NCT][2];
+    Frag8<T> pf[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = fast_exp2(s[e >> 2][ct][e & 3] * sc2 - lse2[ct]);
+        if (masked) p[e] = kt + qd * 8 + e < nvis[ct] ? p[e] : 0.f;
+      }
+      pf[ct] = to_frag<T>(p);
+      // remap onto selection blocks: P (hi + lo) times the overlap weights
+      Frag8<T> plo;
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) plo.v[e] = (bf16)(p[e] - (float)pf[ct].v[e]);
+      }
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        cr[ct][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (jt < njt) {
+          mma(cr[ct][jt], pf[ct], wf[jt]);
+          if constexpr (sizeof(T) == 2) mma(cr[ct][jt], plo, wf[jt]);
+        }
+      }
+    }
+    // O^T += V^T P^T, value fragments shared by the column tiles
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt) {
+      const Frag8<T> vf = *reinterpret_cast<const Frag8<T>*>(vtile + (dt * 16 + c16) * kCmpVS + h * 32 + qd * 8);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) mma(oacc[dt][ct], vf, pf[ct]);
+    }
+    // sum over the group's heads and accumulate the score rows in LDS
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) {
+      if (jt >= njt) break;
+      const int j = j0 + jt * 16 + c16;
+      if (G >= 4) {
+        float v[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) v[ct] = cr[ct][jt][0] + cr[ct][jt][1] + cr[ct][jt][2] + cr[ct][jt][3];
+        if (G >= 8) {
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) v[ct] += xor16f(v[ct], lane);
+        }
+        if (G >= 16) {
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) v[ct] += xor32f(v[ct], lane);
+        }
+        const bool writer = G == 4 || (G == 8 && (qd & 1) == 0) || (G >= 16 && qd == 0);
+        if (writer && j < dm.nsel) {
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) prow[((ct * 16 + qd * 4) / G) * nselp + j] += v[ct];
+        }
+      } else if (j < dm.nsel) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          const int col = ct * 16 + qd * 4;
+          if (G == 2) {
+            prow[(col / 2) * nselp + j] += cr[ct][jt][0] + cr[ct][jt][1];
+            prow[(col / 2 + 1) * nselp + j] += cr[ct][jt][2] + cr[ct][jt][3];
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) prow[(col + r) * nselp + j] += cr[ct][jt][r];
+          }
+        }
+      }
+    }
+  };
+
   const int nkt = (nmax_wg + kCmpKT - 1) / kCmpKT;
   if (nkt > 0) {
     gload(0);
@@ -155,105 +277,14 @@ __global__ __launch_bounds__(256) void k_cmp(Dims dm, CmpArgs a, int nselp, int 
       const int kt = kt0 + h * 32;
       if (kt >= nmax) break;
       f32x4 s[2][NCT];
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) s[sub][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const T* kp = ktile + (h * 32 + krow + sub * 4) * KS + qd * 8;
-#pragma unroll
-        for (int ks = 0; ks < DK / 32; ++ks) {
-          const Frag8<T> kf = *reinterpret_cast<const Frag8<T>*>(kp + ks * 32);
-#pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) mma(s[sub][ct], kf, qf[ct][ks]);
-        }
-      }
+      scores(ktile, h, s);
+      const bool full = kt + 32 <= nfull;
       if constexpr (!PB) {
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          float v[8], mx = kNegInf;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int key = kt + qd * 8 + e;
-            v[e] = key < nvis[ct] ? s[e >> 2][ct][e & 3] * sc2 : kNegInf;
-            mx = fmaxf(mx, v[e]);
-          }
-          mx = fmaxf(mx, xor16f(mx, lane));
-          mx = fmaxf(mx, xor32f(mx, lane));
-          const float mn = fmaxf(m[ct], mx);
-          const float mref = mn == kNegInf ? 0.f : mn;
-          float acc = ls[ct] * fast_exp2(m[ct] - mref);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc += fast_exp2(v[e] - mref);
-          ls[ct] = acc;
-          m[ct] = mn;
-        }
+        if (full) pass_a(s, kt, std::false_type{});
+        else pass_a(s, kt, std::true_type{});
       } else {
-        const int j0 = (kt / 32) * jstep;
-        // value tile fragments, shared by all column tiles
-        Frag8<T> vf[DV / 16];
-#pragma unroll
-        for (int dt = 0; dt < DV / 16; ++dt)
-          vf[dt] = *reinterpret_cast<const Frag8<T>*>(vtile + (dt * 16 + c16) * kCmpVS + h * 32 + qd * 8);
-        f32x4 cr[NCT][2];
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          float p[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int key = kt + qd * 8 + e;
-            p[e] = key < nvis[ct] ? fast_exp2(s[e >> 2][ct][e & 3] * sc2 - lse2[ct]) : 0.f;
-          }
-          const Frag8<T> pf = to_frag<T>(p);
-#pragma unroll
-          for (int dt = 0; dt < DV / 16; ++dt) mma(oacc[dt][ct], vf[dt], pf);
-          // remap onto selection blocks: P (hi + lo) times the overlap weights
-          Frag8<T> phi = pf, plo;
-          if constexpr (sizeof(T) == 2) split_bf16(p, phi, plo);
-#pragma unroll
-          for (int jt = 0; jt < 2; ++jt) {
-            cr[ct][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (jt < njt) {
-              mma(cr[ct][jt], phi, wf[jt]);
-              if constexpr (sizeof(T) == 2) mma(cr[ct][jt], plo, wf[jt]);
-            }
-          }
-        }
-        // sum over the group's heads and accumulate the score rows in LDS
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          if (jt >= njt) break;
-          const int j = j0 + jt * 16 + c16;
-          if (G >= 4) {
-            float v[NCT];
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) v[ct] = cr[ct][jt][0] + cr[ct][jt][1] + cr[ct][jt][2] + cr[ct][jt][3];
-            if (G >= 8) {
-#pragma unroll
-              for (int ct = 0; ct < NCT; ++ct) v[ct] += xor16f(v[ct], lane);
-            }
-            if (G >= 16) {
-#pragma unroll
-              for (int ct = 0; ct < NCT; ++ct) v[ct] += xor32f(v[ct], lane);
-            }
-            const bool writer = G == 4 || (G == 8 && (qd & 1) == 0) || (G >= 16 && qd == 0);
-            if (writer && j < dm.nsel) {
-#pragma unroll
-              for (int ct = 0; ct < NCT; ++ct) prow[((ct * 16 + qd * 4) / G) * nselp + j] += v[ct];
-            }
-          } else if (j < dm.nsel) {
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-              const int col = ct * 16 + qd * 4;
-              if (G == 2) {
-                prow[(col / 2) * nselp + j] += cr[ct][jt][0] + cr[ct][jt][1];
-                prow[(col / 2 + 1) * nselp + j] += cr[ct][jt][2] + cr[ct][jt][3];
-              } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) prow[(col + r) * nselp + j] += cr[ct][jt][r];
-              }
-            }
-          }
-        }
+        if (full) pass_b(s, vtile, h, kt, std::false_type{});
+        else pass_b(s, vtile, h, kt, std::true_type{});
       }
     }
     if (it + 1 < nkt) lstore((it + 1) & 1);
@@ -297,36 +328,46 @@ __global__ __launch_bounds__(256) void k_cmp(Dims dm, CmpArgs a, int nselp, int 
 int cmp_out_nselp(const Dims& dm) { return (dm.nsel + 15) & ~15; }
 
 template <typename T, int DK, int DV, bool PB>
-static size_t cmp_lds(const Dims& dm, int nct, int nselp) {
+static size_t cmp_lds(const Dims& dm, int nw, int nct, int nselp) {
   size_t b = 2 * cmp_tile_elems<T, DK, DV, PB>() * sizeof(T);
-  if (PB) b += (size_t)4 * (16 * nct / dm.G) * nselp * sizeof(float);
+  if (PB) b += (size_t)nw * (16 * nct / dm.G) * nselp * sizeof(float);
   return b;
 }
 
-template <typename T, int DK, int DV, int NCT, bool PB, typename OT>
+template <typename T, int DK, int DV, int NCT, int NW, bool PB, typename OT>
 static hipError_t cmp_launch(const Dims& dm, const CmpArgs& a, int nselp, int njt, size_t lds, hipStream_t s) {
-  auto kfn = k_cmp<T, DK, DV, NCT, PB, OT>;
+  auto kfn = k_cmp<T, DK, DV, NCT, NW, PB, OT>;
   if (lds > 64 * 1024) hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  const int PWG = 4 * 16 * NCT / dm.G;
+  const int PWG = NW * 16 * NCT / dm.G;
   const int ntiles = (dm.T + PWG - 1) / PWG;
-  kfn<<<ntiles * dm.B * dm.Hkv, 256, lds, s>>>(dm, a, nselp, njt);
+  kfn<<<ntiles * dm.B * dm.Hkv, NW * 64, lds, s>>>(dm, a, nselp, njt);
   return hipGetLastError();
 }
 
+// Pass A: 4 waves x 4 column tiles.  Pass B: 8 waves x 2 column tiles, so two
+// waves share each SIMD; with the score rows it falls back to 4 waves x 1
+// column tile when LDS is short.
 template <typename T, int DK, int DV, bool PB>
 static hipError_t cmp_impl(const Dims& dm, const CmpArgs& a, hipStream_t s) {
   const int nselp = cmp_out_nselp(dm);
   const int nblk = (31 * dm.d + dm.l - 1) / dm.ls + 1;   // selection blocks one 32-key tile touches
   const int njt = (nblk + 15) / 16;
   const size_t lim = 160 * 1024;
-  const int nct = cmp_lds<T, DK, DV, PB>(dm, 4, nselp) <= lim ? 4 : 1;
-  const size_t lds = cmp_lds<T, DK, DV, PB>(dm, nct, nselp);
+  if constexpr (!PB) {
+    const size_t lds = cmp_lds<T, DK, DV, PB>(dm, 4, 4, nselp);
+    return a.o_f32 ? cmp_launch<T, DK, DV, 4, 4, PB, float>(dm, a, nselp, njt, lds, s)
+                   : cmp_launch<T, DK, DV, 4, 4, PB, T>(dm, a, nselp, njt, lds, s);
+  } else {
+  if (cmp_lds<T, DK, DV, PB>(dm, 8, 2, nselp) <= lim) {
+    const size_t lds = cmp_lds<T, DK, DV, PB>(dm, 8, 2, nselp);
+    return a.o_f32 ? cmp_launch<T, DK, DV, 2, 8, PB, float>(dm, a, nselp, njt, lds, s)
+                   : cmp_launch<T, DK, DV, 2, 8, PB, T>(dm, a, nselp, njt, lds, s);
+  }
+  const size_t lds = cmp_lds<T, DK, DV, PB>(dm, 4, 1, nselp);
   if (lds > lim) return hipErrorInvalidValue;
-  if (nct == 4)
-    return a.o_f32 ? cmp_launch<T, DK, DV, 4, PB, float>(dm, a, nselp, njt, lds, s)
-                   : cmp_launch<T, DK, DV, 4, PB, T>(dm, a, nselp, njt, lds, s);
-  return a.o_f32 ? cmp_launch<T, DK, DV, 1, PB, float>(dm, a, nselp, njt, lds, s)
-                 : cmp_launch<T, DK, DV, 1, PB, T>(dm, a, nselp, njt, lds, s);
+  return a.o_f32 ? cmp_launch<T, DK, DV, 1, 4, PB, float>(dm, a, nselp, njt, lds, s)
+                 : cmp_launch<T, DK, DV, 1, 4, PB, T>(dm, a, nselp, njt, lds, s);
+  }
 }
 
 template <bool PB>
