@@ -103,7 +103,7 @@ size_t esize(const Dims& dm) { return dm.io == IO_BF16 ? 2 : 4; }
 // Workspace plan of the prefill forward.  Every optional output the caller
 // leaves NULL is placed in the workspace; sizes assume all are NULL.
 struct PrefillWs {
-  void *gates, *kc, *vc, *vct, *vt, *lse, *idx, *ob, *phi;
+  void *gates, *kc, *vc, *vct, *vt, *kvf, *lse, *idx, *ob, *phi;
 };
 
 size_t phi_ws(const Dims& dm) {
@@ -121,6 +121,7 @@ size_t plan_prefill(const Dims& dm, void* ws, PrefillWs* w) {
   w->vc = c.take((size_t)dm.B * dm.ncmp * dm.Hkv * dm.dv * es);
   w->vct = c.take((size_t)dm.B * dm.Hkv * dm.dv * dm.ncmp_pad * es);
   w->vt = c.take((size_t)dm.B * dm.Hkv * dm.dv * dm.Tp * es);
+  w->kvf = c.take(kv_frag_elems(dm) * es);
   w->lse = c.take(3 * BTH * 4);
   w->idx = c.take((size_t)dm.B * dm.T * dm.Hkv * dm.n * 4);
   w->ob = c.take(2 * BTH * dm.dv * es);
@@ -262,7 +263,8 @@ static nsa_status prefill_impl(const nsa_params* p, const nsa_prefill_args* a, v
       return NSA_ERR_HIP;
     if (sg.mark() || run_compress(dm, dm.dv, a->v, &a->phi_v, vc, w.vct, w.phi, s) != hipSuccess)
       return NSA_ERR_HIP;
-    if (sg.mark() || launch_transpose_seq(dm, dm.B, dm.T, dm.Hkv, dm.dv, dm.Tp, a->v, w.vt, s) != hipSuccess)
+    if (sg.mark() || launch_transpose_seq(dm, dm.B, dm.T, dm.Hkv, dm.dv, dm.Tp, a->v, w.vt, s) != hipSuccess ||
+        launch_kv_frag(dm, a->k, a->v, w.kvf, s) != hipSuccess)
       return NSA_ERR_HIP;
     CmpArgs ca;
     ca.q = a->q; ca.kc = kc; ca.vct = w.vct; ca.lse = lse; ca.o = o_cmp; ca.p_slc = (float*)a->p_slc; ca.idx = idx;
@@ -270,7 +272,7 @@ static nsa_status prefill_impl(const nsa_params* p, const nsa_prefill_args* a, v
     if (sg.mark() || launch_cmp_lse(dm, ca, s) != hipSuccess) return NSA_ERR_HIP;
     if (sg.mark() || launch_cmp_out_topn(dm, ca, s) != hipSuccess) return NSA_ERR_HIP;
     SlcArgs sa;
-    sa.q = a->q; sa.k = a->k; sa.vt = w.vt; sa.idx = idx; sa.o = o_slc; sa.lse = lse + BTH; sa.o_f32 = o_f32;
+    sa.q = a->q; sa.kvf = w.kvf; sa.idx = idx; sa.o = o_slc; sa.lse = lse + BTH; sa.o_f32 = o_f32;
     if (sg.mark() || launch_slc(dm, sa, s) != hipSuccess) return NSA_ERR_HIP;
     WinArgs wa;
     wa.q = a->q; wa.k = a->k; wa.vt = w.vt; wa.o_cmp = o_cmp; wa.o_slc = o_slc; wa.gates = gates;

@@ -21,21 +21,95 @@
 
 namespace nsa {
 
-// One 32-key tile of a selected block, held in registers: the K rows of the
-// permuted key order (two MFMA sub-tiles) and the V^T fragments.
+// ---------------------------------------------------------------------------
+// Fragment-ordered copy of K and V.  A selected block is gathered by one wave;
+// in the natural [T, Hkv, d] layout each fragment load touches 16 key rows of
+// 64 bytes, and such fragmented requests cap the load rate well below what
+// contiguous requests reach.  After this re-layout every load instruction of
+// the selected branch reads 1 KB (bf16) of contiguous memory, and one 32-key
+// tile is a single contiguous run of 32 * (dk + dv) elements.
+// ---------------------------------------------------------------------------
+template <int DK, int DV> constexpr int kvf_nk() { return 2 * DK / 32; }
+template <int DK, int DV> constexpr int kvf_ni() { return 2 * DK / 32 + DV / 16; }
+
+size_t kv_frag_elems(const Dims& dm) {
+  return (size_t)dm.B * dm.Hkv * ((dm.T + 31) / 32) * 32 * (dm.dk + dm.dv);
+}
+
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(256) void k_kv_frag(Dims dm, const T* k, const T* v, T* kvf) {
+  constexpr int KS = DK + 8, VS = DV + 8;
+  constexpr int NK = kvf_nk<DK, DV>(), NI = kvf_ni<DK, DV>();
+  __shared__ __align__(16) T sk[32 * KS];
+  __shared__ __align__(16) T sv[32 * VS];
+  const int nt = (dm.T + 31) / 32;
+  const int tile = blockIdx.x % nt, bg = blockIdx.x / nt;
+  const int b = bg / dm.Hkv, g = bg % dm.Hkv;
+  const int k0 = tile * 32;
+  for (int i = threadIdx.x; i < 32 * DK / 8; i += 256) {
+    const int r = i / (DK / 8), c8 = i % (DK / 8), key = k0 + r;
+    *reinterpret_cast<Frag8<T>*>(sk + r * KS + c8 * 8) =
+        key < dm.T ? load_frag(k + ((size_t)(b * dm.T + key) * dm.Hkv + g) * DK + c8 * 8) : zero_frag<T>();
+  }
+  for (int i = threadIdx.x; i < 32 * DV / 8; i += 256) {
+    const int r = i / (DV / 8), c8 = i % (DV / 8), key = k0 + r;
+    *reinterpret_cast<Frag8<T>*>(sv + r * VS + c8 * 8) =
+        key < dm.T ? load_frag(v + ((size_t)(b * dm.T + key) * dm.Hkv + g) * DV + c8 * 8) : zero_frag<T>();
+  }
+  __syncthreads();
+  T* out = kvf + ((size_t)bg * nt + tile) * NI * 512;
+  for (int i = threadIdx.x; i < NI * 64; i += 256) {
+    const int ins = i / 64, L = i % 64, c16 = L & 15, qd = L >> 4;
+    Frag8<T> f;
+    if (ins < NK) {
+      // key fragment: key row (c16 permuted, + 4 for the second sub-tile), features ks*32 + qd*8 ..
+      const int sub = ins / (DK / 32), ks = ins % (DK / 32);
+      const int r = (c16 >> 2) * 8 + (c16 & 3) + sub * 4;
+      f = *reinterpret_cast<const Frag8<T>*>(sk + r * KS + ks * 32 + qd * 8);
+    } else {
+      // value fragment of V^T: feature dt*16 + c16, keys qd*8 ..
+      const int dt = ins - NK;
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = (float)sv[(qd * 8 + e) * VS + dt * 16 + c16];
+      f = to_frag<T>(x);
+    }
+    *reinterpret_cast<Frag8<T>*>(out + (size_t)ins * 512 + L * 8) = f;
+  }
+}
+
+template <typename T, int DK, int DV>
+static hipError_t kv_frag_impl(const Dims& dm, const void* k, const void* v, void* kvf, hipStream_t s) {
+  const int nt = (dm.T + 31) / 32;
+  k_kv_frag<T, DK, DV><<<dm.B * dm.Hkv * nt, 256, 0, s>>>(dm, (const T*)k, (const T*)v, (T*)kvf);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_frag(const Dims& dm, const void* k, const void* v, void* kvf, hipStream_t s) {
+  const bool bf = dm.io == IO_BF16;
+  if (dm.dk == 64 && dm.dv == 64) return bf ? kv_frag_impl<bf16, 64, 64>(dm, k, v, kvf, s) : kv_frag_impl<float, 64, 64>(dm, k, v, kvf, s);
+  if (dm.dk == 128 && dm.dv == 128) return bf ? kv_frag_impl<bf16, 128, 128>(dm, k, v, kvf, s) : kv_frag_impl<float, 128, 128>(dm, k, v, kvf, s);
+  if (dm.dk == 192 && dm.dv == 128) return bf ? kv_frag_impl<bf16, 192, 128>(dm, k, v, kvf, s) : kv_frag_impl<float, 192, 128>(dm, k, v, kvf, s);
+  return hipErrorInvalidValue;
+}
+
+// One 32-key tile of a selected block, held in registers: the key fragments
+// of the two MFMA sub-tiles and the V^T fragments.
 template <typename T, int DK, int DV>
 struct SlcTile {
   Frag8<T> k[2][DK / 32];
   Frag8<T> v[DV / 16];
 };
 
-// Walks the (block, 32-key tile) sequence of one position's selection.
+// Walks the (block, 32-key tile) sequence of one position's selection: keys
+// kt .. kt+31 of the fragment tile, of which lo <= key < kend are the block's.
 struct SlcCursor {
-  int si, kt, kend;
+  int si, kt, lo, kend;
 };
 
 template <typename T, int DK, int DV, typename OT>
-__global__ __launch_bounds__(256) void k_slc(Dims dm, SlcArgs a) {
+__global__ __launch_bounds__(256, 2) void k_slc(Dims dm, SlcArgs a) {
+  constexpr int NK = kvf_nk<DK, DV>(), NI = kvf_ni<DK, DV>();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, qd = lane >> 4;
   const int ntiles = (dm.T + 3) / 4;
@@ -62,19 +136,18 @@ __global__ __launch_bounds__(256) void k_slc(Dims dm, SlcArgs a) {
   f32x4 oacc[DV / 16];
 #pragma unroll
   for (int dt = 0; dt < DV / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const size_t kstride = (size_t)dm.Hkv * DK;
-  const T* kbase = (const T*)a.k + ((size_t)b * dm.T * dm.Hkv + g) * DK + qd * 8;
-  const T* vtb = (const T*)a.vt + (size_t)(b * dm.Hkv + g) * DV * dm.Tp + qd * 8;
-  const int krow = (c16 >> 2) * 8 + (c16 & 3);
+  const int nt = (dm.T + 31) / 32;
+  const T* kvt = (const T*)a.kvf + (size_t)(b * dm.Hkv + g) * nt * NI * 512 + lane * 8;
 
   // first tile of block slot si at or after it, or si = n when none is left
   auto open_block = [&](SlcCursor& c) {
     for (; c.si < dm.n; ++c.si) {
       const int j = __builtin_amdgcn_readlane(myid, c.si);
       if (j < 0) { c.si = dm.n; return; }
-      c.kt = j * dm.ls;
+      c.lo = j * dm.ls;
+      c.kt = c.lo & ~31;
       c.kend = min((j + 1) * dm.ls, t + 1);
-      if (c.kt < c.kend) return;
+      if (c.lo < c.kend) return;
     }
   };
   auto advance = [&](SlcCursor& c) {
@@ -84,15 +157,13 @@ __global__ __launch_bounds__(256) void k_slc(Dims dm, SlcArgs a) {
     open_block(c);
   };
   auto load_tile = [&](SlcTile<T, DK, DV>& tl, const SlcCursor& c) {
+    const T* base = kvt + (size_t)(c.kt / 32) * NI * 512;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int key = min(c.kt + krow + sub * 4, dm.T - 1);
-      const T* kp = kbase + (size_t)key * kstride;
+    for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-      for (int ks = 0; ks < DK / 32; ++ks) tl.k[sub][ks] = load_frag(kp + ks * 32);
-    }
+      for (int ks = 0; ks < DK / 32; ++ks) tl.k[sub][ks] = load_frag(base + (sub * (DK / 32) + ks) * 512);
 #pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt) tl.v[dt] = load_frag(vtb + (size_t)(dt * 16 + c16) * dm.Tp + c.kt);
+    for (int dt = 0; dt < DV / 16; ++dt) tl.v[dt] = load_frag(base + (NK + dt) * 512);
   };
   auto compute_tile = [&](const SlcTile<T, DK, DV>& tl, const SlcCursor& c) {
     f32x4 sacc[2];
@@ -106,7 +177,7 @@ __global__ __launch_bounds__(256) void k_slc(Dims dm, SlcArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int key = c.kt + qd * 8 + e;
-      v[e] = key < c.kend ? sacc[e >> 2][e & 3] * sc2 : kNegInf;
+      v[e] = (key >= c.lo && key < c.kend) ? sacc[e >> 2][e & 3] * sc2 : kNegInf;
       mx = fmaxf(mx, v[e]);
     }
     mx = fmaxf(mx, xor16f(mx, lane));
@@ -130,7 +201,7 @@ __global__ __launch_bounds__(256) void k_slc(Dims dm, SlcArgs a) {
   // Two register tiles in flight: the next tile's loads are issued before the
   // current tile is computed, so memory latency overlaps the MFMA work.
   SlcTile<T, DK, DV> ta, tb;
-  SlcCursor ca{0, 0, 0};
+  SlcCursor ca{0, 0, 0, 0};
   open_block(ca);
   if (ca.si < dm.n) load_tile(ta, ca);
   while (ca.si < dm.n) {

@@ -77,10 +77,15 @@ hipError_t launch_cmp_lse(const Dims& dm, const CmpArgs& a, hipStream_t s);
 hipError_t launch_cmp_out_topn(const Dims& dm, const CmpArgs& a, hipStream_t s);
 
 // ---- selected attention ----
+// K and V in MFMA-fragment order: for every (b, g) and 32-key tile, the
+// 2*dk/32 key fragments and dv/16 value fragments a wave loads, each as 64
+// lanes x 8 contiguous elements (keys past T are zero).
+size_t kv_frag_elems(const Dims& dm);
+hipError_t launch_kv_frag(const Dims& dm, const void* k, const void* v, void* kvf, hipStream_t s);
+
 struct SlcArgs {
   const void* q;    // [B,T,Hq,dk]
-  const void* k;    // [B,T,Hkv,dk]
-  const void* vt;   // [B,Hkv,dv,Tp]
+  const void* kvf;  // fragment-ordered K|V tiles (launch_kv_frag)
   const int* idx;   // [B,T,Hkv,n]
   void* o;          // [B,T,Hq,dv]
   float* lse;       // [B,T,Hq]
