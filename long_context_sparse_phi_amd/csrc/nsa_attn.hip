@@ -15,6 +15,8 @@
 // MFMA layout as in the compressed branch: S^T = K Q^T with keys permuted so
 // lane group qd holds keys 8*qd..8*qd+7, then O^T += V^T P^T with V^T read
 // from a transposed copy of V ([B, Hkv, dv, Tp]).
+#include <type_traits>
+
 #include "nsa_common.hpp"
 #include "nsa_kernels.hpp"
 #include "nsa_tiles.hpp"
@@ -245,14 +247,14 @@ hipError_t launch_slc(const Dims& dm, const SlcArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-template <typename T, int DK, int DV, int NCT, typename OT>
-__global__ __launch_bounds__(256) void k_win(Dims dm, WinArgs a) {
-  using Tile = KVTile<T, DK, DV, true>;
+template <typename T, int DK, int DV, int NCT, int NW, typename OT>
+__global__ __launch_bounds__(NW * 64, 2) void k_win(Dims dm, WinArgs a) {
+  using Tile = KVTile<T, DK, DV, true, NW * 64>;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* tiles = (T*)smem_raw;                              // [2][Tile::elems]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, qd = lane >> 4;
-  const int G = dm.G, PW = 16 * NCT / G, PWG = 4 * PW;
+  const int G = dm.G, PW = 16 * NCT / G, PWG = NW * PW;
   const int ntiles = (dm.T + PWG - 1) / PWG;
   int unit, tile;
   xcd_map(blockIdx.x, dm.B * dm.Hkv, ntiles, unit, tile);
@@ -293,6 +295,60 @@ __global__ __launch_bounds__(256) void k_win(Dims dm, WinArgs a) {
   const int nkt = (kwg1 - kwg0) / kTileKeys + 1;
   const int klo = wave_live ? (max(0, t0 - dm.w + 1) & ~31) : 0x7fffffff;
   const int khi = wave_live ? tl : -1;
+  // keys in [kfull0, kfull1] are inside the window of every column of the wave
+  const int kfull0 = (wave_live && t0 + PW - 1 < dm.T) ? max(0, t0 + PW - 1 - dm.w + 1) : 0x7fffffff;
+  const int kfull1 = t0;
+
+  auto half_tile = [&](const T* tl_, int h, int kt, auto masked) {
+    f32x4 s[2][NCT];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      Frag8<T> kf[DK / 32];
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks) kf[ks] = Tile::kfrag(tl_, h * 32 + krow + sub * 4, ks, qd);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) s[sub][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) mma(s[sub][ct], kf[ks], qf[ct][ks]);
+    }
+    Frag8<T> pf[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      float v[8], mx = kNegInf;
+      const int lo = pos[ct] - dm.w + 1;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        v[e] = s[e >> 2][ct][e & 3] * sc2;
+        if (masked) {
+          const int key = kt + qd * 8 + e;
+          v[e] = (key >= lo && key <= pos[ct]) ? v[e] : kNegInf;
+        }
+        mx = fmaxf(mx, v[e]);
+      }
+      mx = fmaxf(mx, xor16f(mx, lane));
+      mx = fmaxf(mx, xor32f(mx, lane));
+      const float mn = fmaxf(m[ct], mx);
+      const float mref = mn == kNegInf ? 0.f : mn;
+      const float alpha = fast_exp2(m[ct] - mref);
+      float p[8], psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { p[e] = fast_exp2(v[e] - mref); psum += p[e]; }
+      ls[ct] = ls[ct] * alpha + psum;
+      m[ct] = mn;
+      pf[ct] = to_frag<T>(p);
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt) oacc[dt][ct] *= alpha;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt) {
+      const Frag8<T> vf = Tile::vfrag(tl_, dt * 16 + c16, h * 32, qd);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) mma(oacc[dt][ct], vf, pf[ct]);
+    }
+  };
+
   Tile ld;
   ld.gload(kbase, kstride, dm.T, vtb, dm.Tp, kwg0);
   ld.lstore(tiles);
@@ -304,48 +360,8 @@ __global__ __launch_bounds__(256) void k_win(Dims dm, WinArgs a) {
     for (int h = 0; h < 2; ++h) {
       const int kt = kt0 + h * 32;
       if (kt + 31 < klo || kt > khi) continue;
-      f32x4 s[2][NCT];
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) s[sub][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < DK / 32; ++ks) {
-          const Frag8<T> kf = Tile::kfrag(tl_, h * 32 + krow + sub * 4, ks, qd);
-#pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) mma(s[sub][ct], kf, qf[ct][ks]);
-        }
-      }
-      Frag8<T> vf[DV / 16];
-#pragma unroll
-      for (int dt = 0; dt < DV / 16; ++dt) vf[dt] = Tile::vfrag(tl_, dt * 16 + c16, h * 32, qd);
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        float v[8], mx = kNegInf;
-        const int lo = pos[ct] - dm.w + 1;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int key = kt + qd * 8 + e;
-          v[e] = (key >= lo && key <= pos[ct]) ? s[e >> 2][ct][e & 3] * sc2 : kNegInf;
-          mx = fmaxf(mx, v[e]);
-        }
-        mx = fmaxf(mx, xor16f(mx, lane));
-        mx = fmaxf(mx, xor32f(mx, lane));
-        const float mn = fmaxf(m[ct], mx);
-        const float mref = mn == kNegInf ? 0.f : mn;
-        const float alpha = fast_exp2(m[ct] - mref);
-        float p[8], psum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { p[e] = fast_exp2(v[e] - mref); psum += p[e]; }
-        ls[ct] = ls[ct] * alpha + psum;
-        m[ct] = mn;
-        const Frag8<T> pf = to_frag<T>(p);
-#pragma unroll
-        for (int dt = 0; dt < DV / 16; ++dt) {
-          oacc[dt][ct] *= alpha;
-          mma(oacc[dt][ct], vf[dt], pf);
-        }
-      }
+      if (kt >= kfull0 && kt + 31 <= kfull1) half_tile(tl_, h, kt, std::false_type{});
+      else half_tile(tl_, h, kt, std::true_type{});
     }
     if (it + 1 < nkt) ld.lstore(tiles + (size_t)((it + 1) & 1) * Tile::elems);
     __syncthreads();
@@ -375,15 +391,17 @@ __global__ __launch_bounds__(256) void k_win(Dims dm, WinArgs a) {
   }
 }
 
+// 8 waves x 2 column tiles per workgroup: two waves share each SIMD and the
+// staged key tiles feed 16 positions x G heads.
 template <typename T, int DK, int DV>
 static hipError_t win_impl(const Dims& dm, const WinArgs& a, hipStream_t s) {
-  constexpr int NCT = 4;
-  const int PWG = 4 * 16 * NCT / dm.G;
+  constexpr int NCT = 2, NW = 8;
+  const int PWG = NW * 16 * NCT / dm.G;
   const int ntiles = (dm.T + PWG - 1) / PWG;
-  const size_t lds = 2 * KVTile<T, DK, DV, true>::elems * sizeof(T);
-  auto kfn = a.o_f32 ? k_win<T, DK, DV, NCT, float> : k_win<T, DK, DV, NCT, T>;
+  const size_t lds = 2 * KVTile<T, DK, DV, true, NW * 64>::elems * sizeof(T);
+  auto kfn = a.o_f32 ? k_win<T, DK, DV, NCT, NW, float> : k_win<T, DK, DV, NCT, NW, T>;
   if (lds > 64 * 1024) hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  kfn<<<ntiles * dm.B * dm.Hkv, 256, lds, s>>>(dm, a);
+  kfn<<<ntiles * dm.B * dm.Hkv, NW * 64, lds, s>>>(dm, a);
   return hipGetLastError();
 }
 

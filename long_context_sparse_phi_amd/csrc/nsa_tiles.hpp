@@ -1,5 +1,5 @@
-// Cooperative staging of 64-key attention tiles in LDS for a 256-thread
-// workgroup: a K tile [64 keys][DK] (rows padded to DK+8 elements) and a V^T
+// Cooperative staging of 64-key attention tiles in LDS for a workgroup of NT
+// threads: a K tile [64 keys][DK] (rows padded to DK+8 elements) and a V^T
 // tile [DV][64 keys] (rows padded to 72 elements).  Global loads go to
 // registers first (gload) so they can be in flight while the previous tile is
 // computed, then to LDS (lstore).  Row paddings keep the 16-byte fragment reads
@@ -13,13 +13,15 @@ constexpr int kTileKeys = 64;
 constexpr int kTileVS = kTileKeys + 8;
 template <int DK> constexpr int tile_ks() { return DK + 8; }
 
-template <typename T, int DK, int DV, bool WITH_V>
+template <typename T, int DK, int DV, bool WITH_V, int NT = 256>
 struct KVTile {
   static constexpr int KS = tile_ks<DK>();
   static constexpr size_t kElems = (size_t)kTileKeys * KS;
   static constexpr size_t elems = kElems + (WITH_V ? (size_t)DV * kTileVS : 0);
-  static constexpr int KCH = kTileKeys * DK / 8 / 256;
-  static constexpr int VCH = WITH_V ? DV * kTileKeys / 8 / 256 : 0;
+  static constexpr int KCH = kTileKeys * DK / 8 / NT;
+  static constexpr int VCH = WITH_V ? DV * kTileKeys / 8 / NT : 0;
+  static_assert(KCH * NT == kTileKeys * DK / 8, "K tile must split evenly over the workgroup");
+  static_assert(!WITH_V || VCH * NT == DV * kTileKeys / 8, "V tile must split evenly over the workgroup");
   Frag8<T> kr[KCH];
   Frag8<T> vr[VCH > 0 ? VCH : 1];
 
@@ -28,26 +30,26 @@ struct KVTile {
                                         int kt) {
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
-      const int idx = threadIdx.x + 256 * c, row = idx / (DK / 8), c8 = idx % (DK / 8);
+      const int idx = threadIdx.x + NT * c, row = idx / (DK / 8), c8 = idx % (DK / 8);
       const int key = min(kt + row, klim - 1);
       kr[c] = load_frag(kbase + (size_t)key * kstride + c8 * 8);
     }
 #pragma unroll
     for (int c = 0; c < VCH; ++c) {
-      const int idx = threadIdx.x + 256 * c, row = idx / (kTileKeys / 8), c8 = idx % (kTileKeys / 8);
+      const int idx = threadIdx.x + NT * c, row = idx / (kTileKeys / 8), c8 = idx % (kTileKeys / 8);
       vr[c] = load_frag(vtbase + (size_t)row * vld + kt + c8 * 8);
     }
   }
   __device__ __forceinline__ void lstore(T* tile) {
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
-      const int idx = threadIdx.x + 256 * c, row = idx / (DK / 8), c8 = idx % (DK / 8);
+      const int idx = threadIdx.x + NT * c, row = idx / (DK / 8), c8 = idx % (DK / 8);
       *reinterpret_cast<Frag8<T>*>(tile + row * KS + c8 * 8) = kr[c];
     }
     T* vt = tile + kElems;
 #pragma unroll
     for (int c = 0; c < VCH; ++c) {
-      const int idx = threadIdx.x + 256 * c, row = idx / (kTileKeys / 8), c8 = idx % (kTileKeys / 8);
+      const int idx = threadIdx.x + NT * c, row = idx / (kTileKeys / 8), c8 = idx % (kTileKeys / 8);
       *reinterpret_cast<Frag8<T>*>(vt + row * kTileVS + c8 * 8) = vr[c];
     }
   }
