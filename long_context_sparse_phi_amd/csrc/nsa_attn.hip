@@ -400,7 +400,7 @@ static hipError_t win_impl(const Dims& dm, const WinArgs& a, hipStream_t s) {
   const int ntiles = (dm.T + PWG - 1) / PWG;
   const size_t lds = 2 * KVTile<T, DK, DV, true, NW * 64>::elems * sizeof(T);
   auto kfn = a.o_f32 ? k_win<T, DK, DV, NCT, NW, float> : k_win<T, DK, DV, NCT, NW, T>;
-  if (lds > 64 * 1024) hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   kfn<<<ntiles * dm.B * dm.Hkv, NW * 64, lds, s>>>(dm, a);
   return hipGetLastError();
 }

@@ -26,6 +26,7 @@
 
 #include "nsa_common.hpp"
 #include "nsa_kernels.hpp"
+#include "nsa_tiles.hpp"
 
 namespace nsa {
 
@@ -39,17 +40,15 @@ namespace nsa {
 constexpr int kCmpKT = 64;               // keys per LDS tile
 constexpr int kCmpVS = kCmpKT + 8;       // LDS row stride of the V^T tile (elements)
 
-template <int DK> constexpr int cmp_ks() { return DK + 8; }   // LDS row stride of the K tile
-
+// K tile rows are unpadded with XOR-swizzled 16-byte chunks (kchunk_off).
 template <typename T, int DK, int DV, bool PB>
 constexpr size_t cmp_tile_elems() {
-  return (size_t)kCmpKT * cmp_ks<DK>() + (PB ? (size_t)DV * kCmpVS : 0);
+  return (size_t)kCmpKT * DK + (PB ? (size_t)DV * kCmpVS : 0);
 }
 
 template <typename T, int DK, int DV, int NCT, int NW, bool PB, typename OT>
 __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nselp, int njt) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  constexpr int KS = cmp_ks<DK>();
   constexpr size_t TE = cmp_tile_elems<T, DK, DV, PB>();
   constexpr int NT = NW * 64;
   T* tiles = (T*)smem_raw;                                  // [2][TE]
@@ -132,11 +131,11 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
   };
   auto lstore = [&](int buf) {
     T* kt_ = tiles + (size_t)buf * TE;
-    T* vt_ = kt_ + (size_t)kCmpKT * KS;
+    T* vt_ = kt_ + (size_t)kCmpKT * DK;
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
       const int idx = threadIdx.x + NT * c, row = idx / (DK / 8), c8 = idx % (DK / 8);
-      *reinterpret_cast<Frag8<T>*>(kt_ + row * KS + c8 * 8) = kr[c];
+      *reinterpret_cast<Frag8<T>*>(kt_ + kchunk_off<DK>(row, c8)) = kr[c];
     }
 #pragma unroll
     for (int c = 0; c < VCH; ++c) {
@@ -147,15 +146,25 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
 
   const int krow = (c16 >> 2) * 8 + (c16 & 3);
   const int jstep = 32 * dm.d / dm.ls;
+  // score-row offsets of the MFMA output rows 4*qd + r of each column tile
+  // (row = position within the wave), and whether this lane writes the head
+  // sum (one lane group per position once the group's heads are reduced)
+  int rowoff[NCT][4];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rowoff[ct][r] = ((ct * 16 + qd * 4 + r) / G) * nselp;
+  const bool writer = G == 4 || (G == 8 && (qd & 1) == 0) || (G >= 16 && qd == 0);
 
   // scores of one 32-key half tile: S^T = K Q^T for all column tiles
   auto scores = [&](const T* ktile, int h, f32x4 (&s)[2][NCT]) {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-      const T* kp = ktile + (h * 32 + krow + sub * 4) * KS + qd * 8;
+      const int r = h * 32 + krow + sub * 4;
       Frag8<T> kf[DK / 32];
 #pragma unroll
-      for (int ks = 0; ks < DK / 32; ++ks) kf[ks] = *reinterpret_cast<const Frag8<T>*>(kp + ks * 32);
+      for (int ks = 0; ks < DK / 32; ++ks)
+        kf[ks] = *reinterpret_cast<const Frag8<T>*>(ktile + kchunk_off<DK>(r, ks * 4 + qd));
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) s[sub][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -229,6 +238,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
     for (int jt = 0; jt < 2; ++jt) {
       if (jt >= njt) break;
       const int j = j0 + jt * 16 + c16;
+      if (j >= dm.nsel) continue;
       if (G >= 4) {
         float v[NCT];
 #pragma unroll
@@ -241,23 +251,21 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct) v[ct] += xor32f(v[ct], lane);
         }
-        const bool writer = G == 4 || (G == 8 && (qd & 1) == 0) || (G >= 16 && qd == 0);
-        if (writer && j < dm.nsel) {
+        if (writer) {
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) prow[((ct * 16 + qd * 4) / G) * nselp + j] += v[ct];
+          for (int ct = 0; ct < NCT; ++ct) prow[rowoff[ct][0] + j] += v[ct];
         }
-      } else if (j < dm.nsel) {
+      } else if (G == 2) {
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-          const int col = ct * 16 + qd * 4;
-          if (G == 2) {
-            prow[(col / 2) * nselp + j] += cr[ct][jt][0] + cr[ct][jt][1];
-            prow[(col / 2 + 1) * nselp + j] += cr[ct][jt][2] + cr[ct][jt][3];
-          } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) prow[(col + r) * nselp + j] += cr[ct][jt][r];
-          }
+          prow[rowoff[ct][0] + j] += cr[ct][jt][0] + cr[ct][jt][1];
+          prow[rowoff[ct][2] + j] += cr[ct][jt][2] + cr[ct][jt][3];
         }
+      } else {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) prow[rowoff[ct][r] + j] += cr[ct][jt][r];
       }
     }
   };
@@ -272,7 +280,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
     const int kt0 = it * kCmpKT;
     if (it + 1 < nkt) gload(kt0 + kCmpKT);
     const T* ktile = tiles + (size_t)(it & 1) * TE;
-    const T* vtile = ktile + (size_t)kCmpKT * KS;
+    const T* vtile = ktile + (size_t)kCmpKT * DK;
     for (int h = 0; h < 2; ++h) {
       const int kt = kt0 + h * 32;
       if (kt >= nmax) break;
@@ -337,7 +345,7 @@ static size_t cmp_lds(const Dims& dm, int nw, int nct, int nselp) {
 template <typename T, int DK, int DV, int NCT, int NW, bool PB, typename OT>
 static hipError_t cmp_launch(const Dims& dm, const CmpArgs& a, int nselp, int njt, size_t lds, hipStream_t s) {
   auto kfn = k_cmp<T, DK, DV, NCT, NW, PB, OT>;
-  if (lds > 64 * 1024) hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   const int PWG = NW * 16 * NCT / dm.G;
   const int ntiles = (dm.T + PWG - 1) / PWG;
   kfn<<<ntiles * dm.B * dm.Hkv, NW * 64, lds, s>>>(dm, a, nselp, njt);
@@ -384,7 +392,7 @@ hipError_t launch_cmp_out_topn(const Dims& dm, const CmpArgs& a, hipStream_t s) 
 
 bool cmp_out_fits(const Dims& dm) {
   // pass B with one column tile per wave: tiles (largest case: fp32, 192/128) + score rows
-  const size_t tiles = 2 * ((size_t)kCmpKT * (dm.dk + 8) + (size_t)dm.dv * kCmpVS) * (dm.io == IO_BF16 ? 2 : 4);
+  const size_t tiles = 2 * ((size_t)kCmpKT * dm.dk + (size_t)dm.dv * kCmpVS) * (dm.io == IO_BF16 ? 2 : 4);
   return tiles + (size_t)4 * (16 / dm.G) * cmp_out_nselp(dm) * sizeof(float) <= 160 * 1024;
 }
 

@@ -1,9 +1,13 @@
 // Cooperative staging of 64-key attention tiles in LDS for a workgroup of NT
-// threads: a K tile [64 keys][DK] (rows padded to DK+8 elements) and a V^T
-// tile [DV][64 keys] (rows padded to 72 elements).  Global loads go to
-// registers first (gload) so they can be in flight while the previous tile is
-// computed, then to LDS (lstore).  Row paddings keep the 16-byte fragment reads
-// of the MFMA operands aligned and spread over the LDS banks.
+// threads: a K tile [64 keys][DK] and a V^T tile [DV][64 keys] (rows padded
+// to 72 elements).  Global loads go to registers first (gload) so they can be
+// in flight while the previous tile is computed, then to LDS (lstore).
+//
+// K rows are unpadded; their 16-byte chunks are XOR-swizzled by row
+// (kswz) so that the 16 key rows one MFMA fragment read touches land in 16
+// different 4-bank groups.  The rows read together are the permuted key rows
+// (c/4)*8 + c%4 (+4), c = 0..15; kswz is a bijection on the chunks of a row.
+// The V^T rows are padded to 72 elements, which already spreads them.
 #pragma once
 #include "nsa_common.hpp"
 
@@ -11,12 +15,25 @@ namespace nsa {
 
 constexpr int kTileKeys = 64;
 constexpr int kTileVS = kTileKeys + 8;
-template <int DK> constexpr int tile_ks() { return DK + 8; }
+
+// XOR pattern of K-tile row r.  With a row length of 128 elements (256 bytes)
+// every row starts in the same bank group, so 16 distinct 4-bit patterns are
+// needed; with 64 or 192 elements odd rows are offset by half the banks and a
+// 3-bit pattern distinct within each row parity suffices (and stays inside
+// aligned groups of 8 chunks).
+template <int DK>
+__device__ __forceinline__ int kswz(int r) {
+  if constexpr (DK == 128) return (r & 3) | ((r >> 3 & 3) << 2);
+  else return (r >> 1 & 1) | (r >> 2 & 6);
+}
+template <int DK>
+__device__ __forceinline__ int kchunk_off(int r, int chunk) {
+  return r * DK + ((chunk ^ kswz<DK>(r)) << 3);
+}
 
 template <typename T, int DK, int DV, bool WITH_V, int NT = 256>
 struct KVTile {
-  static constexpr int KS = tile_ks<DK>();
-  static constexpr size_t kElems = (size_t)kTileKeys * KS;
+  static constexpr size_t kElems = (size_t)kTileKeys * DK;
   static constexpr size_t elems = kElems + (WITH_V ? (size_t)DV * kTileVS : 0);
   static constexpr int KCH = kTileKeys * DK / 8 / NT;
   static constexpr int VCH = WITH_V ? DV * kTileKeys / 8 / NT : 0;
@@ -44,7 +61,7 @@ struct KVTile {
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
       const int idx = threadIdx.x + NT * c, row = idx / (DK / 8), c8 = idx % (DK / 8);
-      *reinterpret_cast<Frag8<T>*>(tile + row * KS + c8 * 8) = kr[c];
+      *reinterpret_cast<Frag8<T>*>(tile + kchunk_off<DK>(row, c8)) = kr[c];
     }
     T* vt = tile + kElems;
 #pragma unroll
@@ -55,7 +72,7 @@ struct KVTile {
   }
   // MFMA A operand from the staged K tile: row r of the tile, features ks*32 + qd*8 ..
   static __device__ __forceinline__ Frag8<T> kfrag(const T* tile, int r, int ks, int qd) {
-    return *reinterpret_cast<const Frag8<T>*>(tile + r * KS + ks * 32 + qd * 8);
+    return *reinterpret_cast<const Frag8<T>*>(tile + kchunk_off<DK>(r, ks * 4 + qd));
   }
   // MFMA A operand of O^T += V^T P^T: V^T row dv, keys k0 + qd*8 ..
   static __device__ __forceinline__ Frag8<T> vfrag(const T* tile, int dv, int k0, int qd) {
