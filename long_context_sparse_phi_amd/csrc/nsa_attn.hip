@@ -24,75 +24,93 @@
 namespace nsa {
 
 // ---------------------------------------------------------------------------
-// Fragment-ordered copy of K and V.  A selected block is gathered by one wave;
-// in the natural [T, Hkv, d] layout each fragment load touches 16 key rows of
-// 64 bytes, and such fragmented requests cap the load rate well below what
-// contiguous requests reach.  After this re-layout every load instruction of
-// the selected branch reads 1 KB (bf16) of contiguous memory, and one 32-key
-// tile is a single contiguous run of 32 * (dk + dv) elements.
+// Fragment-ordered copies of K and V.  A selected block is gathered by one
+// wave; in the natural [T, Hkv, d] layout each fragment load touches 16 key
+// rows of 64 bytes, and such fragmented requests cap the load rate well below
+// what contiguous requests reach.  After this re-layout every load
+// instruction reads 64 lanes x 16 bytes (bf16) of contiguous memory, and one
+// 32-key tile is a single contiguous run.
+//
+// A packed tile holds tile_ins "instructions" of 64 lanes x 8 elements.  A
+// tensor [B, N, Hkv, D] contributes, per 32-key tile, either
+//   key-row fragments (2*D/32): (sub, ks) -> lane (c, q) holds row
+//     (c/4)*8 + c%4 + 4*sub, features ks*32 + q*8 .. +7 (A operand of K Q^T),
+//   or transposed fragments (D/16): dt -> lane (c, q) holds feature
+//     dt*16 + c, rows q*8 .. +7 (A operand of V^T P^T or K^T dS^T),
+// starting at instruction ins0.  Rows past N are zero.
 // ---------------------------------------------------------------------------
-template <int DK, int DV> constexpr int kvf_nk() { return 2 * DK / 32; }
-template <int DK, int DV> constexpr int kvf_ni() { return 2 * DK / 32 + DV / 16; }
-
-size_t kv_frag_elems(const Dims& dm) {
-  return (size_t)dm.B * dm.Hkv * ((dm.T + 31) / 32) * 32 * (dm.dk + dm.dv);
+size_t frag_tiles_elems(const Dims& dm, int N, int tile_ins) {
+  return (size_t)dm.B * dm.Hkv * ((N + 31) / 32) * tile_ins * 512;
 }
 
-template <typename T, int DK, int DV>
-__global__ __launch_bounds__(256) void k_kv_frag(Dims dm, const T* k, const T* v, T* kvf) {
-  constexpr int KS = DK + 8, VS = DV + 8;
-  constexpr int NK = kvf_nk<DK, DV>(), NI = kvf_ni<DK, DV>();
-  __shared__ __align__(16) T sk[32 * KS];
-  __shared__ __align__(16) T sv[32 * VS];
-  const int nt = (dm.T + 31) / 32;
+template <typename T, int D, bool TRANS>
+__global__ __launch_bounds__(256) void k_frag_pack(Dims dm, int N, const T* src, T* dst, int tile_ins, int ins0) {
+  constexpr int RS = D + 8;
+  constexpr int NI = TRANS ? D / 16 : 2 * D / 32;
+  __shared__ __align__(16) T sr[32 * RS];
+  const int nt = (N + 31) / 32;
   const int tile = blockIdx.x % nt, bg = blockIdx.x / nt;
   const int b = bg / dm.Hkv, g = bg % dm.Hkv;
   const int k0 = tile * 32;
-  for (int i = threadIdx.x; i < 32 * DK / 8; i += 256) {
-    const int r = i / (DK / 8), c8 = i % (DK / 8), key = k0 + r;
-    *reinterpret_cast<Frag8<T>*>(sk + r * KS + c8 * 8) =
-        key < dm.T ? load_frag(k + ((size_t)(b * dm.T + key) * dm.Hkv + g) * DK + c8 * 8) : zero_frag<T>();
-  }
-  for (int i = threadIdx.x; i < 32 * DV / 8; i += 256) {
-    const int r = i / (DV / 8), c8 = i % (DV / 8), key = k0 + r;
-    *reinterpret_cast<Frag8<T>*>(sv + r * VS + c8 * 8) =
-        key < dm.T ? load_frag(v + ((size_t)(b * dm.T + key) * dm.Hkv + g) * DV + c8 * 8) : zero_frag<T>();
+  for (int i = threadIdx.x; i < 32 * D / 8; i += 256) {
+    const int r = i / (D / 8), c8 = i % (D / 8), key = k0 + r;
+    *reinterpret_cast<Frag8<T>*>(sr + r * RS + c8 * 8) =
+        key < N ? load_frag(src + ((size_t)(b * N + key) * dm.Hkv + g) * D + c8 * 8) : zero_frag<T>();
   }
   __syncthreads();
-  T* out = kvf + ((size_t)bg * nt + tile) * NI * 512;
+  T* out = dst + ((size_t)bg * nt + tile) * tile_ins * 512 + (size_t)ins0 * 512;
   for (int i = threadIdx.x; i < NI * 64; i += 256) {
     const int ins = i / 64, L = i % 64, c16 = L & 15, qd = L >> 4;
     Frag8<T> f;
-    if (ins < NK) {
-      // key fragment: key row (c16 permuted, + 4 for the second sub-tile), features ks*32 + qd*8 ..
-      const int sub = ins / (DK / 32), ks = ins % (DK / 32);
+    if constexpr (!TRANS) {
+      const int sub = ins / (D / 32), ks = ins % (D / 32);
       const int r = (c16 >> 2) * 8 + (c16 & 3) + sub * 4;
-      f = *reinterpret_cast<const Frag8<T>*>(sk + r * KS + ks * 32 + qd * 8);
+      f = *reinterpret_cast<const Frag8<T>*>(sr + r * RS + ks * 32 + qd * 8);
     } else {
-      // value fragment of V^T: feature dt*16 + c16, keys qd*8 ..
-      const int dt = ins - NK;
       float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = (float)sv[(qd * 8 + e) * VS + dt * 16 + c16];
+      for (int e = 0; e < 8; ++e) x[e] = (float)sr[(qd * 8 + e) * RS + ins * 16 + c16];
       f = to_frag<T>(x);
     }
     *reinterpret_cast<Frag8<T>*>(out + (size_t)ins * 512 + L * 8) = f;
   }
 }
 
-template <typename T, int DK, int DV>
-static hipError_t kv_frag_impl(const Dims& dm, const void* k, const void* v, void* kvf, hipStream_t s) {
-  const int nt = (dm.T + 31) / 32;
-  k_kv_frag<T, DK, DV><<<dm.B * dm.Hkv * nt, 256, 0, s>>>(dm, (const T*)k, (const T*)v, (T*)kvf);
+template <typename T, int D>
+static hipError_t frag_pack_impl(const Dims& dm, int N, const void* src, void* dst, int tile_ins, int ins0,
+                                 bool trans, hipStream_t s) {
+  const int grid = dm.B * dm.Hkv * ((N + 31) / 32);
+  if (grid == 0) return hipSuccess;
+  if (trans) k_frag_pack<T, D, true><<<grid, 256, 0, s>>>(dm, N, (const T*)src, (T*)dst, tile_ins, ins0);
+  else k_frag_pack<T, D, false><<<grid, 256, 0, s>>>(dm, N, (const T*)src, (T*)dst, tile_ins, ins0);
   return hipGetLastError();
 }
 
-hipError_t launch_kv_frag(const Dims& dm, const void* k, const void* v, void* kvf, hipStream_t s) {
+hipError_t launch_frag_pack(const Dims& dm, int D, int N, const void* src, void* dst, int tile_ins, int ins0,
+                            bool trans, hipStream_t s) {
   const bool bf = dm.io == IO_BF16;
-  if (dm.dk == 64 && dm.dv == 64) return bf ? kv_frag_impl<bf16, 64, 64>(dm, k, v, kvf, s) : kv_frag_impl<float, 64, 64>(dm, k, v, kvf, s);
-  if (dm.dk == 128 && dm.dv == 128) return bf ? kv_frag_impl<bf16, 128, 128>(dm, k, v, kvf, s) : kv_frag_impl<float, 128, 128>(dm, k, v, kvf, s);
-  if (dm.dk == 192 && dm.dv == 128) return bf ? kv_frag_impl<bf16, 192, 128>(dm, k, v, kvf, s) : kv_frag_impl<float, 192, 128>(dm, k, v, kvf, s);
+  switch (D) {
+    case 64: return bf ? frag_pack_impl<bf16, 64>(dm, N, src, dst, tile_ins, ins0, trans, s)
+                       : frag_pack_impl<float, 64>(dm, N, src, dst, tile_ins, ins0, trans, s);
+    case 128: return bf ? frag_pack_impl<bf16, 128>(dm, N, src, dst, tile_ins, ins0, trans, s)
+                        : frag_pack_impl<float, 128>(dm, N, src, dst, tile_ins, ins0, trans, s);
+    case 192: return bf ? frag_pack_impl<bf16, 192>(dm, N, src, dst, tile_ins, ins0, trans, s)
+                        : frag_pack_impl<float, 192>(dm, N, src, dst, tile_ins, ins0, trans, s);
+  }
   return hipErrorInvalidValue;
+}
+
+// Selected-branch tiles: key-row K fragments, then transposed V fragments.
+template <int DK, int DV> constexpr int kvf_nk() { return 2 * DK / 32; }
+template <int DK, int DV> constexpr int kvf_ni() { return 2 * DK / 32 + DV / 16; }
+
+size_t kv_frag_elems(const Dims& dm) { return frag_tiles_elems(dm, dm.T, 2 * dm.dk / 32 + dm.dv / 16); }
+
+hipError_t launch_kv_frag(const Dims& dm, const void* k, const void* v, void* kvf, hipStream_t s) {
+  const int ni = 2 * dm.dk / 32 + dm.dv / 16;
+  hipError_t e = launch_frag_pack(dm, dm.dk, dm.T, k, kvf, ni, 0, false, s);
+  if (e != hipSuccess) return e;
+  return launch_frag_pack(dm, dm.dv, dm.T, v, kvf, ni, 2 * dm.dk / 32, true, s);
 }
 
 // One 32-key tile of a selected block, held in registers: the key fragments

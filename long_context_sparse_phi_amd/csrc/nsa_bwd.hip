@@ -61,8 +61,8 @@ struct BwdBufs {
   float* gates;    // [B,T,Hq,3]
   float* Dc;       // [3,B,T,Hq]
   float* dz;       // [B,T,Hq,3]
-  void* kt;        // [B,Hkv,dk,Tp]
-  void* kct;       // [B,Hkv,dk,ncmp_pad]
+  void* fkv;       // fragment tiles of (k, v, k^T) over T (bwd_tile_ins instructions per 32 keys)
+  void* fckv;      // the same over the compressed keys (k_cmp, v_cmp, k_cmp^T)
   float* dkc;      // [B,Hkv,ncmp,dk]
   float* dvc;      // [B,Hkv,ncmp,dv]
   float* part_cmp; // [B*Hkv*nkg*nseg][64][dk+dv]
@@ -87,6 +87,10 @@ struct BwdBufs {
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Fragment tile of the dq passes: key-row fragments of k (2*dk/32) and of v
+// (2*dv/32), then transposed fragments of k (dk/16).
+static int bwd_tile_ins(const Dims& dm) { return 2 * dm.dk / 32 + 2 * dm.dv / 32 + dm.dk / 16; }
+
 static size_t bwd_carve(const Dims& dm, void* ws, BwdBufs* w) {
   const BwdPlan p = bwd_plan(dm);
   char* base = (char*)ws;
@@ -97,8 +101,8 @@ static size_t bwd_carve(const Dims& dm, void* ws, BwdBufs* w) {
   w->gates = (float*)take(BTH * 3 * 4);
   w->Dc = (float*)take(3 * BTH * 4);
   w->dz = (float*)take(BTH * 3 * 4);
-  w->kt = take(BG * dm.dk * dm.Tp * es);
-  w->kct = take(BG * dm.dk * dm.ncmp_pad * es);
+  w->fkv = take(frag_tiles_elems(dm, dm.T, bwd_tile_ins(dm)) * es);
+  w->fckv = take(frag_tiles_elems(dm, dm.ncmp, bwd_tile_ins(dm)) * es);
   w->dkc = (float*)take(BG * dm.ncmp * dm.dk * 4);
   w->dvc = (float*)take(BG * dm.ncmp * dm.dv * 4);
   w->part_cmp = (float*)take(BG * p.nkg_cmp * p.nseg_cmp * 64 * (dm.dk + dm.dv) * 4);
@@ -158,27 +162,24 @@ struct DqState {
   float rs;   // row-sum pass: this lane's part of sum_k P_k (dO . v_k)
 };
 
-// One 32-key tile of one branch.  kbase/vbase: row pointers of key/value
-// rows (row stride kstr/vstr, already offset by qd*8); ktb: transposed keys
-// (row stride ld, already offset by qd*8).  Keys kt .. kt+31, valid when
-// lo <= key < hi.  ROWSUM: accumulate sum_k P_k dP_k (dP = dO v^T, no gate),
-// which equals <dO, O_c> exactly; otherwise accumulate dq^T += K^T dS^T.
+// One 32-key tile of one branch.  tb: the packed fragment tile of keys
+// kt .. kt+31 (already offset by lane*8); keys lo <= key < hi are valid.
+// ROWSUM: accumulate sum_k P_k dP_k (dP = dO v^T, no gate), which equals
+// <dO, O_c> exactly; otherwise accumulate dq^T += K^T dS^T.
 template <typename T, int DK, int DV, bool ROWSUM>
-__device__ __forceinline__ void dq_tile(DqState<T, DK, DV>& st, const T* kbase, size_t kstr, const T* vbase,
-                                        size_t vstr, const T* ktb, size_t ld, int kt, int lo, int hi, int klim,
-                                        int krow, int c16, int qd, float sc2, float lse2, float gc, float Dc) {
+__device__ __forceinline__ void dq_tile(DqState<T, DK, DV>& st, const T* tb, int kt, int lo, int hi, int c16,
+                                        int qd, float sc2, float lse2, float gc, float Dc) {
+  constexpr int NKK = 2 * DK / 32, NKV = 2 * DV / 32;
   f32x4 s[2], dp[2];
 #pragma unroll
   for (int sub = 0; sub < 2; ++sub) {
     s[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
     dp[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int key = min(kt + krow + sub * 4, klim - 1);
-    const T* kp = kbase + (size_t)key * kstr;
-    const T* vp = vbase + (size_t)key * vstr;
 #pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) mma(s[sub], load_frag(kp + ks * 32), st.qf[ks]);
+    for (int ks = 0; ks < DK / 32; ++ks) mma(s[sub], load_frag(tb + (sub * (DK / 32) + ks) * 512), st.qf[ks]);
 #pragma unroll
-    for (int ks = 0; ks < DV / 32; ++ks) mma(dp[sub], load_frag(vp + ks * 32), st.dof[ks]);
+    for (int ks = 0; ks < DV / 32; ++ks)
+      mma(dp[sub], load_frag(tb + (NKK + sub * (DV / 32) + ks) * 512), st.dof[ks]);
   }
   float ds[8];
 #pragma unroll
@@ -192,7 +193,7 @@ __device__ __forceinline__ void dq_tile(DqState<T, DK, DV>& st, const T* kbase, 
   if (!ROWSUM) {
     Frag8<T> dsf = to_frag<T>(ds);
 #pragma unroll
-    for (int dt = 0; dt < DK / 16; ++dt) mma(st.dq[dt], load_frag(ktb + (size_t)(dt * 16 + c16) * ld + kt), dsf);
+    for (int dt = 0; dt < DK / 16; ++dt) mma(st.dq[dt], load_frag(tb + (NKK + NKV + dt) * 512), dsf);
   }
 }
 
@@ -226,7 +227,6 @@ __global__ __launch_bounds__(256) void k_bwd_dq(Dims dm, BwdArgs a) {
     st.rs = 0.f;
   }
   const float sc2 = dm.scale * kLog2e;
-  const int krow = (c16 >> 2) * 8 + (c16 & 3);
   float lse2[3], gc[3], Dc[3];
 #pragma unroll
   for (int c = 0; c < 3; ++c) {
@@ -236,31 +236,28 @@ __global__ __launch_bounds__(256) void k_bwd_dq(Dims dm, BwdArgs a) {
     Dc[c] = (cv && !ROWSUM) ? a.w.Dc[c * BTH + row] : 0.f;
   }
   float rsum[3] = {0.f, 0.f, 0.f};
+  const int TI = 2 * DK / 32 + 2 * DV / 32 + DK / 16;
   // compressed branch
   {
     const int nv = ncmp_visible(t, dm.l, dm.d);
-    const T* kb = (const T*)a.kc + ((size_t)b * dm.ncmp * dm.Hkv + g) * DK + qd * 8;
-    const T* vb = (const T*)a.vc + ((size_t)b * dm.ncmp * dm.Hkv + g) * DV + qd * 8;
-    const T* ktb = (const T*)a.w.kct + (size_t)(b * dm.Hkv + g) * DK * dm.ncmp_pad + qd * 8;
+    const T* fb = (const T*)a.w.fckv + (size_t)(b * dm.Hkv + g) * ((dm.ncmp + 31) / 32) * TI * 512 + lane * 8;
     for (int kt = 0; kt < nv; kt += 32)
-      dq_tile<T, DK, DV, ROWSUM>(st, kb, (size_t)dm.Hkv * DK, vb, (size_t)dm.Hkv * DV, ktb, dm.ncmp_pad, kt, 0,
-                                 nv, dm.ncmp, krow, c16, qd, sc2, lse2[0], gc[0], Dc[0]);
+      dq_tile<T, DK, DV, ROWSUM>(st, fb + (size_t)(kt / 32) * TI * 512, kt, 0, nv, c16, qd, sc2, lse2[0], gc[0],
+                                 Dc[0]);
     rsum[0] = st.rs;
     st.rs = 0.f;
   }
-  const T* kb = (const T*)a.k + ((size_t)b * dm.T * dm.Hkv + g) * DK + qd * 8;
-  const T* vb = (const T*)a.v + ((size_t)b * dm.T * dm.Hkv + g) * DV + qd * 8;
-  const T* ktb = (const T*)a.w.kt + (size_t)(b * dm.Hkv + g) * DK * dm.Tp + qd * 8;
+  const T* fb = (const T*)a.w.fkv + (size_t)(b * dm.Hkv + g) * ((dm.T + 31) / 32) * TI * 512 + lane * 8;
   // selected branch
   {
     const int* ids = a.idx + ((size_t)(b * dm.T + t) * dm.Hkv + g) * dm.n;
     for (int si = 0; si < dm.n; ++si) {
       const int j = ids[si];
       if (j < 0) break;
-      const int kend = min((j + 1) * dm.ls, t + 1);
-      for (int kt = j * dm.ls; kt < kend; kt += 32)
-        dq_tile<T, DK, DV, ROWSUM>(st, kb, (size_t)dm.Hkv * DK, vb, (size_t)dm.Hkv * DV, ktb, dm.Tp, kt,
-                                   j * dm.ls, kend, dm.T, krow, c16, qd, sc2, lse2[1], gc[1], Dc[1]);
+      const int lo = j * dm.ls, kend = min((j + 1) * dm.ls, t + 1);
+      for (int kt = lo & ~31; kt < kend; kt += 32)
+        dq_tile<T, DK, DV, ROWSUM>(st, fb + (size_t)(kt / 32) * TI * 512, kt, lo, kend, c16, qd, sc2, lse2[1],
+                                   gc[1], Dc[1]);
     }
     rsum[1] = st.rs;
     st.rs = 0.f;
@@ -269,8 +266,8 @@ __global__ __launch_bounds__(256) void k_bwd_dq(Dims dm, BwdArgs a) {
   {
     const int lo = max(0, t - dm.w + 1);
     for (int kt = lo & ~31; kt <= t; kt += 32)
-      dq_tile<T, DK, DV, ROWSUM>(st, kb, (size_t)dm.Hkv * DK, vb, (size_t)dm.Hkv * DV, ktb, dm.Tp, kt, lo, t + 1,
-                                 dm.T, krow, c16, qd, sc2, lse2[2], gc[2], Dc[2]);
+      dq_tile<T, DK, DV, ROWSUM>(st, fb + (size_t)(kt / 32) * TI * 512, kt, lo, t + 1, c16, qd, sc2, lse2[2],
+                                 gc[2], Dc[2]);
     rsum[2] = st.rs;
   }
   if (ROWSUM) {
@@ -1035,12 +1032,21 @@ static hipError_t bwd_impl(const Dims& dm, const nsa_bwd_args* args, BwdArgs& a,
   // stage 0: gates, gate backward, row terms
   if ((e = mark()) != hipSuccess) return e;
   if ((e = launch_gate(dm, dm.B * dm.T, a.x, a.wg, a.w.gates, s)) != hipSuccess) return e;
-  // stage 1: transposed copies of k and k_cmp (A operand of dq^T += K^T dS^T)
+  // stage 1: fragment tiles of (k, v, k^T) and (k_cmp, v_cmp, k_cmp^T) for the dq passes
   if ((e = mark()) != hipSuccess) return e;
-  if ((e = launch_transpose_seq(dm, dm.B, dm.T, dm.Hkv, DK, dm.Tp, a.k, a.w.kt, s)) != hipSuccess) return e;
-  if (dm.ncmp > 0 &&
-      (e = launch_transpose_seq(dm, dm.B, dm.ncmp, dm.Hkv, DK, dm.ncmp_pad, a.kc, a.w.kct, s)) != hipSuccess)
-    return e;
+  {
+    const int ti = bwd_tile_ins(dm);
+    const int n1 = 2 * DK / 32, n2 = n1 + 2 * DV / 32;
+    if ((e = launch_frag_pack(dm, DK, dm.T, a.k, a.w.fkv, ti, 0, false, s)) != hipSuccess ||
+        (e = launch_frag_pack(dm, DV, dm.T, a.v, a.w.fkv, ti, n1, false, s)) != hipSuccess ||
+        (e = launch_frag_pack(dm, DK, dm.T, a.k, a.w.fkv, ti, n2, true, s)) != hipSuccess)
+      return e;
+    if (dm.ncmp > 0 &&
+        ((e = launch_frag_pack(dm, DK, dm.ncmp, a.kc, a.w.fckv, ti, 0, false, s)) != hipSuccess ||
+         (e = launch_frag_pack(dm, DV, dm.ncmp, a.vc, a.w.fckv, ti, n1, false, s)) != hipSuccess ||
+         (e = launch_frag_pack(dm, DK, dm.ncmp, a.kc, a.w.fckv, ti, n2, true, s)) != hipSuccess))
+      return e;
+  }
   // stage 2: row terms D_c, dz, then dq
   if ((e = mark()) != hipSuccess) return e;
   k_bwd_dq<T, DK, DV, true><<<((dm.T + 3) / 4) * BG, 256, 0, s>>>(dm, a);

@@ -82,6 +82,12 @@ hipError_t launch_cmp_out_topn(const Dims& dm, const CmpArgs& a, hipStream_t s);
 // lanes x 8 contiguous elements (keys past T are zero).
 size_t kv_frag_elems(const Dims& dm);
 hipError_t launch_kv_frag(const Dims& dm, const void* k, const void* v, void* kvf, hipStream_t s);
+// General form: pack src [B, N, Hkv, D] into tiles of tile_ins instructions,
+// as key-row (trans = false, 2*D/32 instructions) or transposed (D/16)
+// fragments starting at instruction ins0.
+size_t frag_tiles_elems(const Dims& dm, int N, int tile_ins);
+hipError_t launch_frag_pack(const Dims& dm, int D, int N, const void* src, void* dst, int tile_ins, int ins0,
+                            bool trans, hipStream_t s);
 
 struct SlcArgs {
   const void* q;    // [B,T,Hq,dk]
