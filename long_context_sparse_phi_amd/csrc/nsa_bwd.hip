@@ -367,15 +367,6 @@ struct KvStage {
   float l2, Dv, gv;
 };
 
-__device__ __forceinline__ bf16 frag_at(const Frag8<bf16>& f, int e) { return f.v[e]; }
-__device__ __forceinline__ float frag_at(const Frag8<float>& f, int e) { return e < 4 ? f.lo[e] : f.hi[e - 4]; }
-typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void store_col4(bf16* p, bf16 a, bf16 b, bf16 c, bf16 d) {
-  *reinterpret_cast<bf16x4v*>(p) = bf16x4v{a, b, c, d};
-}
-__device__ __forceinline__ void store_col4(float* p, float a, float b, float c, float d) {
-  *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
-}
 
 // Staging task u -> tensor (q or dO), feature chunk c8 and row quad rq.  Lanes
 // vary the low two bits of c8 fastest (64 contiguous bytes of a row per lane

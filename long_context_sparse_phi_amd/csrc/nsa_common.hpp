@@ -37,6 +37,43 @@ __device__ __forceinline__ Frag8<float> load_frag(const float* p) {
   f.hi = *reinterpret_cast<const f32x4*>(p + 4);
   return f;
 }
+// Element e of a fragment in its own type, and a store of four such elements
+// as one 8-byte (bf16) or 16-byte (fp32) vector.
+__device__ __forceinline__ bf16 frag_at(const Frag8<bf16>& f, int e) { return f.v[e]; }
+__device__ __forceinline__ float frag_at(const Frag8<float>& f, int e) { return e < 4 ? f.lo[e] : f.hi[e - 4]; }
+typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_col4(bf16* p, bf16 a, bf16 b, bf16 c, bf16 d) {
+  *reinterpret_cast<bf16x4v*>(p) = bf16x4v{a, b, c, d};
+}
+__device__ __forceinline__ void store_col4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+}
+
+// Transposed store of a 4-row x 8-element block: element e of rows 0..3 goes
+// to dst[e * stride + 0..3].  The bf16 form pairs half-words with byte
+// permutes, so no element is extracted through memory.
+__device__ __forceinline__ void store_cols4x8(bf16* dst, int stride, const Frag8<bf16> (&r)[4]) {
+  typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+  typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
+  u32x4v w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w[k] = __builtin_bit_cast(u32x4v, r[k].v);
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const unsigned lo01 = __builtin_amdgcn_perm(w[1][m], w[0][m], 0x05040100u);
+    const unsigned lo23 = __builtin_amdgcn_perm(w[3][m], w[2][m], 0x05040100u);
+    const unsigned hi01 = __builtin_amdgcn_perm(w[1][m], w[0][m], 0x07060302u);
+    const unsigned hi23 = __builtin_amdgcn_perm(w[3][m], w[2][m], 0x07060302u);
+    *reinterpret_cast<u32x2v*>(dst + (2 * m) * stride) = u32x2v{lo01, lo23};
+    *reinterpret_cast<u32x2v*>(dst + (2 * m + 1) * stride) = u32x2v{hi01, hi23};
+  }
+}
+__device__ __forceinline__ void store_cols4x8(float* dst, int stride, const Frag8<float> (&r)[4]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    store_col4(dst + e * stride, frag_at(r[0], e), frag_at(r[1], e), frag_at(r[2], e), frag_at(r[3], e));
+}
+
 template <typename T> __device__ __forceinline__ Frag8<T> zero_frag();
 template <> __device__ __forceinline__ Frag8<bf16> zero_frag<bf16>() {
   Frag8<bf16> f;
@@ -189,10 +226,45 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
   const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 63);
   return ((uint64_t)hi << 32) | lo;
 }
-// Order key of candidate block j with score v >= 0: larger score first, then
-// lower index.  Taken (marked, v < 0) entries map to 0, below every candidate.
-__device__ __forceinline__ uint64_t topn_key(float v, int j) {
-  return v < 0.f ? 0ull : ((uint64_t)__float_as_uint(v) << 32) | (uint32_t)(0xffffffffu - (uint32_t)j);
+// Wave-wide max (float) and min (int) by the same DPP pattern, broadcast.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_f32(float v, float ident) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(ident), __float_as_int(v), CTRL, ROWMASK, 0xf,
+                                                    false));
+}
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ int dpp_i32(int v, int ident) {
+  return __builtin_amdgcn_update_dpp(ident, v, CTRL, ROWMASK, 0xf, false);
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+  const float ni = -__builtin_inff();
+  v = fmaxf(v, dpp_f32<0x111, 0xf>(v, ni));
+  v = fmaxf(v, dpp_f32<0x112, 0xf>(v, ni));
+  v = fmaxf(v, dpp_f32<0x114, 0xf>(v, ni));
+  v = fmaxf(v, dpp_f32<0x118, 0xf>(v, ni));
+  v = fmaxf(v, dpp_f32<0x142, 0xa>(v, ni));
+  v = fmaxf(v, dpp_f32<0x143, 0xc>(v, ni));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ int wave_min_i32(int v) {
+  const int id = 0x7fffffff;
+  v = min(v, dpp_i32<0x111, 0xf>(v, id));
+  v = min(v, dpp_i32<0x112, 0xf>(v, id));
+  v = min(v, dpp_i32<0x114, 0xf>(v, id));
+  v = min(v, dpp_i32<0x118, 0xf>(v, id));
+  v = min(v, dpp_i32<0x142, 0xa>(v, id));
+  v = min(v, dpp_i32<0x143, 0xc>(v, id));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+// Selection order: larger score first, the lower index winning a tie.  Each
+// lane offers its best (s, j); the wave's best is returned in every lane
+// (s = -inf when no lane has a candidate).
+__device__ __forceinline__ void wave_argmax(float s, int j, float& bs, int& bj) {
+  bs = wave_max_f32(s);
+  bj = wave_min_i32(s == bs ? j : 0x7fffffff);
+}
+__device__ __forceinline__ bool topn_better(float s, int j, float bs, int bj) {
+  return s > bs || (s == bs && j < bj);
 }
 
 // Top-n block selection for query position t from one group's score row
@@ -209,22 +281,26 @@ __device__ inline void wave_topn(float* row, int t, int ls, int n, int* out, int
     return;
   }
   if (lane == 0) { row[0] = -1.f; row[jc - 1] = -1.f; row[jc] = -1.f; }
-  // each lane keeps the best key among its candidates j = lane (mod 64)
+  // each lane keeps its best candidate among j = lane (mod 64)
+  float ms;
+  int mj;
   auto lane_best = [&]() {
-    uint64_t best = 0;
+    ms = -__builtin_inff();
+    mj = 0x7fffffff;
     for (int j = lane; j <= jc; j += 64) {
-      const uint64_t k = topn_key(row[j], j);
-      best = k > best ? k : best;
+      const float v = row[j];
+      if (v >= 0.f && v > ms) { ms = v; mj = j; }
     }
-    return best;
   };
-  uint64_t mine = lane_best();
+  lane_best();
   for (int it = 0; it < n - 3; ++it) {
-    const uint64_t win = wave_max_u64(mine);
-    const int bj = (int)(0xffffffffu - (uint32_t)win);
-    if ((bj & 63) == lane) {
+    float bs;
+    int bj;
+    wave_argmax(ms, mj, bs, bj);
+    if (bs < 0.f) break;
+    if (mj == bj) {
       row[bj] = -1.f;
-      mine = lane_best();
+      lane_best();
     }
   }
   int cnt = 0;
@@ -236,6 +312,115 @@ __device__ inline void wave_topn(float* row, int t, int ls, int n, int* out, int
     cnt += __popcll(mk);
   }
   for (int e = cnt + lane; e < n; e += 64) out[e] = -1;
+}
+
+// The same selection by a whole workgroup of NW waves (NW*64 threads).
+// Stage 1: each wave keeps a contiguous slice of the candidates in registers
+// (KPL per lane) and extracts its local top (n-3) by repeated wave argmax;
+// stage 2: wave 0 takes the top (n-3) of the NW*(n-3) finalists (FPL per
+// lane).  The order is total (score, then index), so the result equals
+// wave_topn's.  fs/fj: LDS scratch of NW*(n-3) finalists.  The caller
+// synchronises the workgroup before (row complete) and after.
+template <int NW, int KPL, int FPL>
+__device__ inline void block_topn_impl(float* row, int jc, int n, int* out, float* fs, int* fj, int tid) {
+  const int lane = tid & 63, wave = tid >> 6;
+  const int R = (jc + 1 + NW - 1) / NW;
+  const int m = n - 3;
+  {
+    const int j0 = wave * R, j1 = min(jc + 1, j0 + R);
+    float ks[KPL];
+    int kj[KPL];
+    float ms = -__builtin_inff();
+    int mj = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const int j = j0 + lane + 64 * i;
+      const bool ok = j < j1 && j != 0 && j != jc - 1 && j != jc;
+      ks[i] = ok ? row[j] : -__builtin_inff();
+      kj[i] = j;
+      if (topn_better(ks[i], kj[i], ms, mj)) { ms = ks[i]; mj = kj[i]; }
+    }
+    for (int r = 0; r < m; ++r) {
+      float bs;
+      int bj;
+      wave_argmax(ms, mj, bs, bj);
+      if (lane == 0) { fs[wave * m + r] = bs; fj[wave * m + r] = bj; }
+      if (bs == -__builtin_inff()) continue;
+      if (mj == bj) {
+        ms = -__builtin_inff();
+        mj = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+          if (kj[i] == bj) ks[i] = -__builtin_inff();
+          if (topn_better(ks[i], kj[i], ms, mj)) { ms = ks[i]; mj = kj[i]; }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  const int F = NW * m;
+  float gs[FPL];
+  int gj[FPL];
+  float ms = -__builtin_inff();
+  int mj = 0x7fffffff;
+#pragma unroll
+  for (int i = 0; i < FPL; ++i) {
+    const int e = lane + 64 * i;
+    gs[i] = e < F ? fs[e] : -__builtin_inff();
+    gj[i] = e < F ? fj[e] : 0x7fffffff;
+    if (topn_better(gs[i], gj[i], ms, mj)) { ms = gs[i]; mj = gj[i]; }
+  }
+  if (lane == 0) { row[0] = -1.f; row[jc - 1] = -1.f; row[jc] = -1.f; }
+  for (int r = 0; r < m; ++r) {
+    float bs;
+    int bj;
+    wave_argmax(ms, mj, bs, bj);
+    if (bs == -__builtin_inff()) break;
+    if (mj == bj) {
+      row[bj] = -1.f;
+      ms = -__builtin_inff();
+      mj = 0x7fffffff;
+#pragma unroll
+      for (int i = 0; i < FPL; ++i) {
+        if (gj[i] == bj) gs[i] = -__builtin_inff();
+        if (topn_better(gs[i], gj[i], ms, mj)) { ms = gs[i]; mj = gj[i]; }
+      }
+    }
+  }
+  int cnt = 0;
+  for (int jb = 0; jb <= jc; jb += 64) {
+    const int j = jb + lane;
+    const bool sel = j <= jc && row[j] < 0.f;
+    const uint64_t mk = __ballot(sel);
+    if (sel) out[cnt + __popcll(mk & ((1ull << lane) - 1ull))] = j;
+    cnt += __popcll(mk);
+  }
+  for (int e = cnt + lane; e < n; e += 64) out[e] = -1;
+}
+
+// fs / fj: LDS scratch of NW*29 floats and ints (n <= 32).
+template <int NW>
+__device__ inline void block_topn(float* row, int t, int ls, int n, int* out, float* fs, int* fj, int tid) {
+  const int jc = t / ls;
+  if (jc + 1 <= n) {
+    for (int e = tid; e < n; e += NW * 64) out[e] = e <= jc ? e : -1;
+    return;
+  }
+  const int R = (jc + 1 + NW - 1) / NW;
+  const bool f4 = NW * (n - 3) <= 4 * 64;
+  constexpr int FMAX = (NW * 29 + 63) / 64;
+  if (R <= 64) {
+    if (f4) block_topn_impl<NW, 1, 4>(row, jc, n, out, fs, fj, tid);
+    else block_topn_impl<NW, 1, FMAX>(row, jc, n, out, fs, fj, tid);
+  } else if (R <= 4 * 64) {
+    if (f4) block_topn_impl<NW, 4, 4>(row, jc, n, out, fs, fj, tid);
+    else block_topn_impl<NW, 4, FMAX>(row, jc, n, out, fs, fj, tid);
+  } else if (R <= 16 * 64) {
+    block_topn_impl<NW, 16, FMAX>(row, jc, n, out, fs, fj, tid);
+  } else if ((tid >> 6) == 0) {
+    wave_topn(row, t, ls, n, out, tid & 63);
+  }
 }
 
 }  // namespace nsa

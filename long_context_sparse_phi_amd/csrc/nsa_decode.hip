@@ -17,19 +17,23 @@
 //   4. k_dec_merge: evaluates the gates, merges the compressed chunks and the
 //      selected and window partial states, and writes
 //      o = g_cmp O_cmp + g_slc O_slc + g_win O_win.
-// The raw caches are stored [key][feature]; the value operand of P V needs
-// eight consecutive keys per lane, so each 32-key value tile passes through
-// LDS and is read transposed.
+// All caches are stored [key][Hkv][feature].  A wave reads each 32-key tile of
+// its KV head as whole rows (64 lanes x 16 contiguous bytes per load, the
+// request pattern that streams at full rate) into registers, one tile ahead,
+// then writes it to LDS: keys row-major with XOR-swizzled chunks, values
+// transposed ([feature][key]) so both MFMA operands are single 16-byte reads.
 #include "../../include/nsa.h"
 #include "nsa_common.hpp"
 #include "nsa_kernels.hpp"
+#include "nsa_tiles.hpp"
 
 namespace nsa {
 
 constexpr int kDecCK = 256;     // compressed blocks per chunk (one wave)
 constexpr int kDecTPC = kDecCK / 32;
-constexpr int kDecSlcPer = 1;   // selected blocks per wave
 constexpr int kDecWinChunk = 64;
+// tiles in flight per wave (one wave per SIMD; the ring takes most registers)
+template <int DK, int DV> constexpr int dec_depth() { return DK + DV >= 320 ? 3 : 4; }
 
 struct DecPlan {
   int S, t, ncmp, nc, nb, jstep, nis, niw, ni, wlen, ws0;
@@ -43,7 +47,7 @@ static DecPlan dec_plan(const Dims& dm) {
   p.nc = (dm.ncmp + kDecCK - 1) / kDecCK;
   p.nb = (31 * dm.d + dm.l - 1) / dm.ls + 1;
   p.jstep = 32 * dm.d / dm.ls;
-  p.nis = (dm.n + kDecSlcPer - 1) / kDecSlcPer;
+  p.nis = dm.n;
   p.wlen = dm.w < dm.T ? dm.w : dm.T;
   p.ws0 = dm.T - p.wlen;
   p.niw = (p.wlen + kDecWinChunk - 1) / kDecWinChunk;
@@ -54,7 +58,8 @@ static DecPlan dec_plan(const Dims& dm) {
 struct DecBufs {
   float* part_o;    // [B,Hkv,nc,16,dv]
   float* part_ml;   // [B,Hkv,nc,16,2]
-  float* part_ps;   // [B,Hkv,nc,TPC,nb,16]
+  float* part_ps;   // [B,Hkv,nc,TPC,nb,16] remapped scores, relative to the tile's running max
+  float* part_tm;   // [B,Hkv,nc,TPC,16] running max (log2 units) after each tile
   float* cmp_scl;   // [B,Hkv,nc,16] exp2(m_chunk - lse) per chunk and head
   float* lse_cmp;   // [B,Hq] (log2 units)
   float* gates;     // [B,Hq,3]
@@ -74,6 +79,7 @@ static size_t dec_carve(const Dims& dm, void* ws, DecBufs* b) {
   b->part_o = (float*)take(BG * p.nc * 16 * dm.dv * 4);
   b->part_ml = (float*)take(BG * p.nc * 16 * 2 * 4);
   b->part_ps = (float*)take(BG * p.nc * 16 * kDecTPC * p.nb * 4);
+  b->part_tm = (float*)take(BG * p.nc * 16 * kDecTPC * 4);
   b->cmp_scl = (float*)take(BG * (p.nc > 0 ? p.nc : 1) * 16 * 4);
   b->lse_cmp = (float*)take((size_t)dm.B * dm.Hq * 4);
   b->gates = (float*)take((size_t)dm.B * dm.Hq * 3 * 4);
@@ -104,96 +110,78 @@ struct DecArgs {
   DecBufs w;
 };
 
-// Loads a 32-key x DV value tile (rows key0..key0+31, clamped to klim-1) of
-// one KV head into LDS [32][DV+8] and returns after the wave can read it.
-template <typename T, int DV>
-__device__ __forceinline__ void stage_v_tile(T* vs, const T* vbase, size_t kstride, int key0, int klim, int lane) {
-  constexpr int CH = DV / 8;             // 16-byte chunks per row
-  for (int i = lane; i < 32 * CH; i += 64) {
-    const int r = i / CH, c = i % CH;
-    const int key = min(key0 + r, klim - 1);
-    Frag8<T> f = load_frag(vbase + (size_t)key * kstride + c * 8);
-    if constexpr (sizeof(T) == 2) {
-      *reinterpret_cast<bf16x8*>(vs + r * (DV + 8) + c * 8) = f.v;
-    } else {
-      *reinterpret_cast<f32x4*>(vs + r * (DV + 8) + c * 8) = f.lo;
-      *reinterpret_cast<f32x4*>(vs + r * (DV + 8) + c * 8 + 4) = f.hi;
+// 32-key tile of one KV head: global -> registers (gload, one tile ahead of
+// the compute) -> LDS (lstore).  Keys: 32 rows x DK, chunks swizzled by
+// kchunk_off.  Values: V^T [DV][kVS]; a lane moves 4 consecutive key rows x 8
+// features and writes them as 8-byte columns.  Lanes vary the feature chunk
+// fastest within groups of 4, then the row quad, which spreads both the
+// global requests (64 contiguous bytes per lane quad) and the LDS banks.
+template <typename T, int DK, int DV>
+struct DecTile {
+  static constexpr int kVS = 40;                     // V^T row stride (elements)
+  static constexpr int KCH = 32 * DK / 8 / 64;       // key chunks per lane
+  static constexpr int VTK = DV / 64;                // value tasks (4 rows x 8 features) per lane
+  static constexpr size_t kElems = (size_t)32 * DK;
+  static constexpr size_t elems = kElems + (size_t)DV * kVS;
+  Frag8<T> kr[KCH];
+  Frag8<T> vr[VTK][4];
+
+  __device__ __forceinline__ void gload(const T* kbase, const T* vbase, size_t kstride, size_t vstride, int key0,
+                                        int klim, int lane) {
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+      const int i = lane + 64 * c, row = i / (DK / 8), c8 = i % (DK / 8);
+      kr[c] = load_frag(kbase + (size_t)min(key0 + row, klim - 1) * kstride + c8 * 8);
+    }
+#pragma unroll
+    for (int c = 0; c < VTK; ++c) {
+      const int u = lane + 64 * c, c8 = (u & 3) + 4 * (u >> 5), rq = (u >> 2) & 7;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        vr[c][k] = load_frag(vbase + (size_t)min(key0 + 4 * rq + k, klim - 1) * vstride + c8 * 8);
     }
   }
-  __syncthreads();
-}
-
-// A operand of O^T += V^T P^T from the staged tile: row dv = dt*16 + c16,
-// keys 8*qd .. 8*qd+7.
-template <typename T, int DV>
-__device__ __forceinline__ Frag8<T> vt_frag(const T* vs, int dt, int c16, int qd) {
-  float x[8];
+  __device__ __forceinline__ void lstore(T* tile, int lane) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) x[e] = to_f32(vs[(qd * 8 + e) * (DV + 8) + dt * 16 + c16]);
-  return to_frag<T>(x);
-}
-
-template <typename T, int DK>
-__device__ __forceinline__ void score_tile(f32x4 (&s)[2], const T* kbase, size_t kstride, int kt, int klim,
-                                           const Frag8<T> (&qf)[DK / 32], int krow) {
+    for (int c = 0; c < KCH; ++c) {
+      const int i = lane + 64 * c, row = i / (DK / 8), c8 = i % (DK / 8);
+      *reinterpret_cast<Frag8<T>*>(tile + kchunk_off<DK>(row, c8)) = kr[c];
+    }
+    T* vt = tile + kElems;
 #pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
-    s[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int key = min(kt + krow + sub * 4, klim - 1);
-    const T* kp = kbase + (size_t)key * kstride;
-#pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) mma(s[sub], load_frag(kp + ks * 32), qf[ks]);
-  }
-}
-
-template <typename T, int DK>
-__device__ __forceinline__ void load_k_tile(Frag8<T> (&kf)[2][DK / 32], const T* kbase, size_t kstride, int kt,
-                                            int klim, int krow) {
-#pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
-    const T* kp = kbase + (size_t)min(kt + krow + sub * 4, klim - 1) * kstride;
-#pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) kf[sub][ks] = load_frag(kp + ks * 32);
-  }
-}
-
-template <typename T, int DK>
-__device__ __forceinline__ void score_from(f32x4 (&s)[2], const Frag8<T> (&kf)[2][DK / 32],
-                                           const Frag8<T> (&qf)[DK / 32]) {
-#pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
-    s[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) mma(s[sub], kf[sub][ks], qf[ks]);
-  }
-}
-
-// 32-key value tile in registers (row r = key, 8 features per chunk) and its LDS image.
-template <typename T, int DV>
-struct VTileRegs {
-  static constexpr int CH = 32 * DV / 8 / 64;   // chunks per lane
-  Frag8<T> r[CH];
-  __device__ __forceinline__ void gload(const T* vbase, size_t kstride, int key0, int klim, int lane) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int i = lane + 64 * c, row = i / (DV / 8), c8 = i % (DV / 8);
-      r[c] = load_frag(vbase + (size_t)min(key0 + row, klim - 1) * kstride + c8 * 8);
+    for (int c = 0; c < VTK; ++c) {
+      const int u = lane + 64 * c, c8 = (u & 3) + 4 * (u >> 5), rq = (u >> 2) & 7;
+      store_cols4x8(vt + (c8 * 8) * kVS + 4 * rq, kVS, vr[c]);
     }
   }
-  __device__ __forceinline__ void lstore(T* vs, int lane) {
+  // S^T = K Q^T for the tile's permuted key rows (two 16-key sub-tiles)
+  static __device__ __forceinline__ void scores(f32x4 (&s)[2], const T* tile, const Frag8<T> (&qf)[DK / 32],
+                                                int krow, int qd) {
 #pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int i = lane + 64 * c, row = i / (DV / 8), c8 = i % (DV / 8);
-      *reinterpret_cast<Frag8<T>*>(vs + row * (DV + 8) + c8 * 8) = r[c];
+    for (int sub = 0; sub < 2; ++sub) {
+      Frag8<T> kf[DK / 32];
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks)
+        kf[ks] = *reinterpret_cast<const Frag8<T>*>(tile + kchunk_off<DK>(krow + sub * 4, ks * 4 + qd));
+      s[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks) mma(s[sub], kf[ks], qf[ks]);
     }
+  }
+  // A operand of O^T += V^T P^T: feature dt*16 + c16, keys 8*qd .. 8*qd+7
+  static __device__ __forceinline__ Frag8<T> vfrag(const T* tile, int dt, int c16, int qd) {
+    return *reinterpret_cast<const Frag8<T>*>(tile + kElems + (dt * 16 + c16) * kVS + qd * 8);
   }
 };
 
+// Chunk of CK compressed keys per wave, one pass with an online softmax: per
+// tile the scores, the running per-head maximum, P V, and the remapped block
+// scores relative to that running maximum, stored with it; the combine scales
+// each tile's scores by exp2(max - lse).
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__(64) void k_dec_cmp(Dims dm, DecArgs a, DecPlan pl) {
-  extern __shared__ __align__(16) float smem[];
-  float* sb = smem;                                   // [TPC][64][8] scores
-  T* vs = (T*)(smem + kDecTPC * 64 * 8);              // [32][DV+8]
+__global__ __launch_bounds__(64, 1) void k_dec_cmp(Dims dm, DecArgs a, DecPlan pl) {
+  using Tile = DecTile<T, DK, DV>;
+  __shared__ __align__(16) T tile[Tile::elems];
   const int lane = threadIdx.x, c16 = lane & 15, qd = lane >> 4;
   const int c = blockIdx.x % pl.nc, bg = blockIdx.x / pl.nc;
   const int b = bg / dm.Hkv, g = bg % dm.Hkv;
@@ -206,41 +194,6 @@ __global__ __launch_bounds__(64) void k_dec_cmp(Dims dm, DecArgs a, DecPlan pl) 
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) qf[ks] = cv ? load_frag(qp + ks * 32) : zero_frag<T>();
   }
-  const float sc2 = dm.scale * kLog2e;
-  const size_t kstride = (size_t)dm.Hkv * DK, vstride = (size_t)dm.Hkv * DV;
-  const T* kbase = (const T*)a.kc + ((size_t)b * a.cap * dm.Hkv + g) * DK + qd * 8;
-  const T* vbase = (const T*)a.vc + ((size_t)b * a.cap * dm.Hkv + g) * DV;
-  const int krow = (c16 >> 2) * 8 + (c16 & 3);
-  // phase 1: scores of the chunk, two key tiles in flight
-  float mloc = kNegInf;
-  auto keep = [&](const f32x4 (&s)[2], int i) {
-    const int kt = k0 + 32 * i;
-    float* dst = sb + (i * 64 + lane) * 8;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float v = (kt + qd * 8 + e < k1) ? s[e >> 2][e & 3] * sc2 : kNegInf;
-      dst[e] = v;
-      mloc = fmaxf(mloc, v);
-    }
-  };
-  {
-    Frag8<T> ka[2][DK / 32], kb[2][DK / 32];
-    load_k_tile<T, DK>(ka, kbase, kstride, k0, pl.ncmp, krow);
-    for (int i = 0; i < ntile; i += 2) {
-      if (i + 1 < ntile) load_k_tile<T, DK>(kb, kbase, kstride, k0 + 32 * (i + 1), pl.ncmp, krow);
-      f32x4 s[2];
-      score_from<T, DK>(s, ka, qf);
-      keep(s, i);
-      if (i + 2 < ntile) load_k_tile<T, DK>(ka, kbase, kstride, k0 + 32 * (i + 2), pl.ncmp, krow);
-      if (i + 1 < ntile) {
-        score_from<T, DK>(s, kb, qf);
-        keep(s, i + 1);
-      }
-    }
-  }
-  mloc = fmaxf(mloc, xor16f(mloc, lane));
-  mloc = fmaxf(mloc, xor32f(mloc, lane));
-  const float mref = mloc == kNegInf ? 0.f : mloc;
   Frag8<T> wf[2];
 #pragma unroll
   for (int jt = 0; jt < 2; ++jt) {
@@ -249,26 +202,45 @@ __global__ __launch_bounds__(64) void k_dec_cmp(Dims dm, DecArgs a, DecPlan pl) 
     for (int e = 0; e < 8; ++e) w[e] = remap_weight(qd * 8 + e, jt * 16 + c16, dm.l, dm.d, dm.ls);
     wf[jt] = to_frag<T>(w);
   }
+  const float sc2 = dm.scale * kLog2e;
+  const size_t kstride = (size_t)dm.Hkv * DK, vstride = (size_t)dm.Hkv * DV;
+  const T* kbase = (const T*)a.kc + ((size_t)b * a.cap * dm.Hkv + g) * DK;
+  const T* vbase = (const T*)a.vc + ((size_t)b * a.cap * dm.Hkv + g) * DV;
+  const int krow = (c16 >> 2) * 8 + (c16 & 3);
   f32x4 oacc[DV / 16];
 #pragma unroll
   for (int dt = 0; dt < DV / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float lsum = 0.f;
+  float m = kNegInf, lsum = 0.f;
   float* ps = a.w.part_ps + ((size_t)bg * pl.nc + c) * kDecTPC * pl.nb * 16;
-  // phase 2: probabilities, P V and remapped scores; the next value tile is in flight
-  VTileRegs<T, DV> vr;
-  vr.gload(vbase, vstride, k0, pl.ncmp, lane);
-  for (int i = 0; i < ntile; ++i) {
-    __syncthreads();
-    vr.lstore(vs, lane);
-    __syncthreads();
-    if (i + 1 < ntile) vr.gload(vbase, vstride, k0 + 32 * (i + 1), pl.ncmp, lane);
-    float p[8];
-    const float* src = sb + (i * 64 + lane) * 8;
+  float* tm = a.w.part_tm + ((size_t)bg * pl.nc + c) * kDecTPC * 16;
+  // two tiles in flight in registers while the current one is computed from LDS
+  auto compute = [&](int i) {
+    const int kt = k0 + 32 * i;
+    f32x4 s[2];
+    Tile::scores(s, tile, qf, krow, qd);
+    float v[8], mx = kNegInf;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) { p[e] = fast_exp2(src[e] - mref); lsum += p[e]; }
-    Frag8<T> pf = to_frag<T>(p);
+    for (int e = 0; e < 8; ++e) {
+      v[e] = (kt + qd * 8 + e < k1) ? s[e >> 2][e & 3] * sc2 : kNegInf;
+      mx = fmaxf(mx, v[e]);
+    }
+    mx = fmaxf(mx, xor16f(mx, lane));
+    mx = fmaxf(mx, xor32f(mx, lane));
+    const float mn = fmaxf(m, mx);
+    const float mref = mn == kNegInf ? 0.f : mn;
+    const float alpha = fast_exp2(m - mref);
+    float p[8], psum = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt) mma(oacc[dt], vt_frag<T, DV>(vs, dt, c16, qd), pf);
+    for (int e = 0; e < 8; ++e) { p[e] = fast_exp2(v[e] - mref); psum += p[e]; }
+    lsum = lsum * alpha + psum;
+    m = mn;
+    if (qd == 0) tm[i * 16 + c16] = mn;
+    const Frag8<T> pf = to_frag<T>(p);
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt) {
+      oacc[dt] *= alpha;
+      mma(oacc[dt], Tile::vfrag(tile, dt, c16, qd), pf);
+    }
     Frag8<T> phi = pf, plo;
     if constexpr (sizeof(T) == 2) split_bf16(p, phi, plo);
 #pragma unroll
@@ -280,17 +252,41 @@ __global__ __launch_bounds__(64) void k_dec_cmp(Dims dm, DecArgs a, DecPlan pl) 
       const int jj = jt * 16 + c16;
       if (jj < pl.nb) store4(ps + ((size_t)i * pl.nb + jj) * 16 + qd * 4, cr[0], cr[1], cr[2], cr[3]);
     }
+  };
+  // a ring of kDecDepth tiles in flight in registers while the current one is
+  // computed from LDS (one wave per SIMD, most of its registers hold loads)
+  constexpr int DEPTH = dec_depth<DK, DV>();
+  auto step = [&](Tile& cur, int i) {
+    __syncthreads();
+    cur.lstore(tile, lane);
+    __syncthreads();
+    if (i + DEPTH < ntile) cur.gload(kbase, vbase, kstride, vstride, k0 + 32 * (i + DEPTH), pl.ncmp, lane);
+    compute(i);
+  };
+  Tile ring[DEPTH];
+#pragma unroll
+  for (int r = 0; r < DEPTH; ++r)
+    if (r < ntile) ring[r].gload(kbase, vbase, kstride, vstride, k0 + 32 * r, pl.ncmp, lane);
+  for (int i = 0; i < ntile; i += DEPTH) {
+#pragma unroll
+    for (int r = 0; r < DEPTH; ++r)
+      if (i + r < ntile) step(ring[r], i + r);
   }
   lsum += xor16f(lsum, lane);
   lsum += xor32f(lsum, lane);
   const size_t hb = ((size_t)bg * pl.nc + c) * 16 + c16;
   if (qd == 0) {
-    a.w.part_ml[hb * 2 + 0] = mloc;
+    a.w.part_ml[hb * 2 + 0] = m;
     a.w.part_ml[hb * 2 + 1] = lsum;
   }
   float* op = a.w.part_o + hb * DV + qd * 4;
 #pragma unroll
   for (int dt = 0; dt < DV / 16; ++dt) store4(op + dt * 16, oacc[dt][0], oacc[dt][1], oacc[dt][2], oacc[dt][3]);
+}
+
+// Element i of an I/O tensor as float.
+__device__ __forceinline__ float load_elem(const void* p, int io, size_t i) {
+  return io == IO_BF16 ? (float)((const bf16*)p)[i] : ((const float*)p)[i];
 }
 
 // One workgroup (1024 threads) per (sequence, KV head): per-head log-sum-exp
@@ -302,24 +298,47 @@ __global__ __launch_bounds__(1024) void k_dec_combine(Dims dm, DecArgs a, DecPla
   float* lse2 = scl + pl.nc * 16;             // [16]
   float* mls = lse2 + 16;                     // [nc][16] chunk maxima
   float* lsl = mls + pl.nc * 16;              // [nc][16] chunk sums
+  float* fs = lsl + pl.nc * 16;               // [16*29] top-n finalists: scores
+  int* fj = (int*)(fs + 16 * 29);             // [16*29] and indices
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bg = blockIdx.x, b = bg / dm.Hkv, g = bg % dm.Hkv;
   const int G = dm.G;
+  // gate inputs of head `wave`, requested now and used at the end
+  float gx[4], gw[4][3];
+  auto gate_load = [&](int k0) {
+    const int h = g * G + min(wave, G - 1);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = k0 + u * 64 + lane;
+      gx[u] = k < dm.C ? load_elem(a.x, dm.io, (size_t)b * dm.C + k) : 0.f;
+#pragma unroll
+      for (int c = 0; c < 3; ++c) gw[u][c] = k < dm.C ? load_elem(a.wg, dm.io, ((size_t)k * dm.Hq + h) * 3 + c) : 0.f;
+    }
+  };
+  gate_load(0);
   for (int i = tid; i < pl.nc * 16; i += 1024) {
     const size_t hb = (size_t)bg * pl.nc * 16 + i;
     mls[i] = a.w.part_ml[hb * 2];
     lsl[i] = a.w.part_ml[hb * 2 + 1];
   }
   __syncthreads();
-  if (tid < 16) {
+  // per-head log-sum-exp: wave h reduces head h over the chunks
+  {
+    const int h = wave;
     float M = kNegInf;
-    for (int c = 0; c < pl.nc; ++c) M = fmaxf(M, mls[c * 16 + tid]);
-    float L = 0.f;
+    for (int c = lane; c < pl.nc; c += 64) M = fmaxf(M, mls[c * 16 + h]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     const float Mr = M == kNegInf ? 0.f : M;
-    for (int c = 0; c < pl.nc; ++c) L += lsl[c * 16 + tid] * fast_exp2(mls[c * 16 + tid] - Mr);
-    const float l2 = M == kNegInf ? kNegInf : M + __log2f(L);
-    lse2[tid] = l2;
-    if (tid < G) a.w.lse_cmp[(size_t)b * dm.Hq + g * G + tid] = l2;
+    float L = 0.f;
+    for (int c = lane; c < pl.nc; c += 64) L += lsl[c * 16 + h] * fast_exp2(mls[c * 16 + h] - Mr);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
+    if (lane == 0) {
+      const float l2 = M == kNegInf ? kNegInf : M + __log2f(L);
+      lse2[h] = l2;
+      if (h < G) a.w.lse_cmp[(size_t)b * dm.Hq + g * G + h] = l2;
+    }
   }
   __syncthreads();
   for (int i = tid; i < pl.nc * 16; i += 1024) {
@@ -336,15 +355,28 @@ __global__ __launch_bounds__(1024) void k_dec_combine(Dims dm, DecArgs a, DecPla
     int klo = j - pl.nb + 1;
     klo = klo <= 0 ? 0 : (klo + pl.jstep - 1) / pl.jstep;
     const int khi = min(j / pl.jstep, ntiles - 1);
-    for (int kg = klo; kg <= khi; ++kg) {
-      const int c = kg / kDecTPC, i = kg % kDecTPC, jj = j - kg * pl.jstep;
-      const float* ps = a.w.part_ps + ((((size_t)bg * pl.nc + c) * kDecTPC + i) * pl.nb + jj) * 16;
-      for (int h4 = 0; h4 < G; h4 += 4) {
-        float x[4];
-        load4(ps + h4, x);
+    // at most a few tiles touch a block; all their loads are issued together
+    for (int kb = klo; kb <= khi; kb += 2) {
+      float x[2][16], mt[2][16];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (h4 + r < G) val += x[r] * scl[c * 16 + h4 + r];
+      for (int q = 0; q < 2; ++q) {
+        const int kg = kb + q;
+        if (kg > khi) break;
+        const int c = kg / kDecTPC, i = kg % kDecTPC, jj = j - kg * pl.jstep;
+        const float* ps = a.w.part_ps + ((((size_t)bg * pl.nc + c) * kDecTPC + i) * pl.nb + jj) * 16;
+        const float* tm = a.w.part_tm + (((size_t)bg * pl.nc + c) * kDecTPC + i) * 16;
+#pragma unroll
+        for (int h4 = 0; h4 < 16; h4 += 4) {
+          load4(ps + h4, x[q] + h4);
+          load4(tm + h4, mt[q] + h4);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        if (kb + q > khi) break;
+#pragma unroll
+        for (int h = 0; h < 16; ++h)
+          if (h < G && mt[q][h] != kNegInf && lse2[h] != kNegInf) val += x[q][h] * fast_exp2(mt[q][h] - lse2[h]);
       }
     }
     row[j] = val;
@@ -353,12 +385,35 @@ __global__ __launch_bounds__(1024) void k_dec_combine(Dims dm, DecArgs a, DecPla
   if (a.p_slc)
     for (int j = tid; j < dm.nsel; j += 1024) a.p_slc[(size_t)bg * dm.nsel + j] = row[j];
   __syncthreads();
-  if (wave == 0) wave_topn(row, pl.t, dm.ls, dm.n, a.w.idx + (size_t)bg * dm.n, lane);
+  block_topn<16>(row, pl.t, dm.ls, dm.n, a.w.idx + (size_t)bg * dm.n, fs, fj, tid);
+  // gates of the group's heads: wave h, lanes over the gate input, the three
+  // branches together; the first 256 inputs were loaded at the start
+  if (wave < G) {
+    const int h = g * G + wave;
+    float z[3] = {0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < dm.C; k0 += 4 * 64) {
+      if (k0 > 0) gate_load(k0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int c = 0; c < 3; ++c) z[c] += gx[u] * gw[u][c];
+    }
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) z[c] += __shfl_xor(z[c], off);
+    }
+    if (lane < 3) {
+      const float zz = lane == 0 ? z[0] : (lane == 1 ? z[1] : z[2]);
+      a.w.gates[((size_t)b * dm.Hq + h) * 3 + lane] = 1.f / (1.f + expf(-zz));
+    }
+  }
 }
 
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(64) void k_dec_sw(Dims dm, DecArgs a, DecPlan pl) {
-  __shared__ T vs[32 * (DV + 8)];
+  using Tile = DecTile<T, DK, DV>;
+  __shared__ __align__(16) T tile[Tile::elems];
   const int lane = threadIdx.x, c16 = lane & 15, qd = lane >> 4;
   const int it = blockIdx.x % pl.ni, bg = blockIdx.x / pl.ni;
   const int b = bg / dm.Hkv, g = bg % dm.Hkv;
@@ -369,58 +424,71 @@ __global__ __launch_bounds__(64) void k_dec_sw(Dims dm, DecArgs a, DecPlan pl) {
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) qf[ks] = cv ? load_frag(qp + ks * 32) : zero_frag<T>();
   }
-  // key ranges of this work item
-  int r0[kDecSlcPer], r1[kDecSlcPer], nr = 0;
+  // key range of this work item: one selected block or one window chunk
+  int r0 = 0, r1 = 0;
   if (it < pl.nis) {
-    for (int s = 0; s < kDecSlcPer; ++s) {
-      const int si = it * kDecSlcPer + s;
-      const int j = si < dm.n ? a.w.idx[(size_t)bg * dm.n + si] : -1;
-      if (j >= 0) { r0[nr] = j * dm.ls; r1[nr] = min((j + 1) * dm.ls, pl.S); ++nr; }
-    }
+    const int j = it < dm.n ? a.w.idx[(size_t)bg * dm.n + it] : -1;
+    if (j >= 0) { r0 = j * dm.ls; r1 = min((j + 1) * dm.ls, pl.S); }
   } else {
-    const int wi = it - pl.nis;
-    r0[0] = pl.ws0 + wi * kDecWinChunk;
-    r1[0] = min(r0[0] + kDecWinChunk, pl.S);
-    nr = 1;
+    r0 = pl.ws0 + (it - pl.nis) * kDecWinChunk;
+    r1 = min(r0 + kDecWinChunk, pl.S);
   }
+  const int kt0 = r0 & ~31;
+  const int ntile = r1 > r0 ? (r1 - kt0 + 31) / 32 : 0;
   const float sc2 = dm.scale * kLog2e;
   const size_t kstride = (size_t)dm.Hkv * DK, vstride = (size_t)dm.Hkv * DV;
-  const T* kbase = (const T*)a.kcache + ((size_t)b * pl.S * dm.Hkv + g) * DK + qd * 8;
+  const T* kbase = (const T*)a.kcache + ((size_t)b * pl.S * dm.Hkv + g) * DK;
   const T* vbase = (const T*)a.vcache + ((size_t)b * pl.S * dm.Hkv + g) * DV;
   const int krow = (c16 >> 2) * 8 + (c16 & 3);
   float m = kNegInf, ls = 0.f;
   f32x4 oacc[DV / 16];
 #pragma unroll
   for (int dt = 0; dt < DV / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int r = 0; r < nr; ++r) {
-    for (int kt = r0[r]; kt < r1[r]; kt += 32) {
-      f32x4 s[2];
-      score_tile<T, DK>(s, kbase, kstride, kt, pl.S, qf, krow);
-      __syncthreads();
-      stage_v_tile<T, DV>(vs, vbase, vstride, kt, pl.S, lane);
-      float v[8], mx = kNegInf;
+  auto compute = [&](int i) {
+    const int kt = kt0 + 32 * i;
+    f32x4 s[2];
+    Tile::scores(s, tile, qf, krow, qd);
+    float v[8], mx = kNegInf;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        v[e] = (kt + qd * 8 + e < r1[r]) ? s[e >> 2][e & 3] * sc2 : kNegInf;
-        mx = fmaxf(mx, v[e]);
-      }
-      mx = fmaxf(mx, xor16f(mx, lane));
-      mx = fmaxf(mx, xor32f(mx, lane));
-      const float mn = fmaxf(m, mx);
-      const float mref = mn == kNegInf ? 0.f : mn;
-      const float alpha = fast_exp2(m - mref);
-      float p[8], psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { p[e] = fast_exp2(v[e] - mref); psum += p[e]; }
-      ls = ls * alpha + psum;
-      m = mn;
-      Frag8<T> pf = to_frag<T>(p);
-#pragma unroll
-      for (int dt = 0; dt < DV / 16; ++dt) {
-        oacc[dt] *= alpha;
-        mma(oacc[dt], vt_frag<T, DV>(vs, dt, c16, qd), pf);
-      }
+    for (int e = 0; e < 8; ++e) {
+      const int key = kt + qd * 8 + e;
+      v[e] = (key >= r0 && key < r1) ? s[e >> 2][e & 3] * sc2 : kNegInf;
+      mx = fmaxf(mx, v[e]);
     }
+    mx = fmaxf(mx, xor16f(mx, lane));
+    mx = fmaxf(mx, xor32f(mx, lane));
+    const float mn = fmaxf(m, mx);
+    const float mref = mn == kNegInf ? 0.f : mn;
+    const float alpha = fast_exp2(m - mref);
+    float p[8], psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { p[e] = fast_exp2(v[e] - mref); psum += p[e]; }
+    ls = ls * alpha + psum;
+    m = mn;
+    const Frag8<T> pf = to_frag<T>(p);
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt) {
+      oacc[dt] *= alpha;
+      mma(oacc[dt], Tile::vfrag(tile, dt, c16, qd), pf);
+    }
+  };
+  // a ring of two tiles in flight (a 64-token block or aligned window chunk
+  // is two tiles, so all of it is requested up front)
+  auto step = [&](Tile& cur, int i) {
+    __syncthreads();
+    cur.lstore(tile, lane);
+    __syncthreads();
+    if (i + 2 < ntile) cur.gload(kbase, vbase, kstride, vstride, kt0 + 32 * (i + 2), pl.S, lane);
+    compute(i);
+  };
+  Tile ring[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+    if (r < ntile) ring[r].gload(kbase, vbase, kstride, vstride, kt0 + 32 * r, pl.S, lane);
+  for (int i = 0; i < ntile; i += 2) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+      if (i + r < ntile) step(ring[r], i + r);
   }
   ls += xor16f(ls, lane);
   ls += xor32f(ls, lane);
@@ -448,37 +516,34 @@ __global__ __launch_bounds__(256) void k_dec_merge(Dims dm, DecArgs a, DecPlan p
   const int G = dm.G;
   const int h0 = hp * 2;
   if (h0 >= G) return;
-  // gates of the two heads: one wave per dot product
-  for (int o = wave; o < 6; o += 4) {
-    const int hh = h0 + o / 3, cc = o % 3;
-    float z = 0.f;
-    if (hh < G) {
-      const int h = g * G + hh;
-      for (int k = lane; k < dm.C; k += 64)
-        z += to_f32(((const T*)a.x)[(size_t)b * dm.C + k]) * to_f32(((const T*)a.wg)[((size_t)k * dm.Hq + h) * 3 + cc]);
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
-    if (lane == 0) gts[o] = 1.f / (1.f + expf(-z));
+  // gates of the two heads (evaluated by the combine)
+  if (tid < 6) {
+    const int hh = h0 + tid / 3;
+    gts[tid] = hh < G ? a.w.gates[((size_t)b * dm.Hq + g * G + hh) * 3 + tid % 3] : 0.f;
   }
-  // selected / window merge scales: exp2(m_i - M_branch) / L_branch
-  if (tid < 4) {
-    const int hh = h0 + tid / 2, br = tid % 2;
+  // selected / window merge scales exp2(m_i - M_branch) / L_branch: one wave
+  // per (head, branch) with the lanes over the items
+  for (int o = wave; o < 4; o += 4) {
+    const int hh = h0 + o / 2, br = o % 2;
     const int i0 = br == 0 ? 0 : pl.nis, i1 = br == 0 ? pl.nis : pl.ni;
     float M = kNegInf;
-    for (int i = i0; i < i1; ++i) M = fmaxf(M, a.w.sw_ml[(((size_t)bg * pl.ni + i) * 16 + hh) * 2]);
+    for (int i = i0 + lane; i < i1; i += 64) M = fmaxf(M, a.w.sw_ml[(((size_t)bg * pl.ni + i) * 16 + hh) * 2]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     const float Mr = M == kNegInf ? 0.f : M;
     float L = 0.f;
-    for (int i = i0; i < i1; ++i) {
+    for (int i = i0 + lane; i < i1; i += 64) {
       const size_t hb = ((size_t)bg * pl.ni + i) * 16 + hh;
       L += a.w.sw_ml[hb * 2 + 1] * fast_exp2(a.w.sw_ml[hb * 2] - Mr);
     }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    for (int i = i0; i < i1; ++i) {
+    for (int i = i0 + lane; i < i1; i += 64) {
       const float mi = a.w.sw_ml[(((size_t)bg * pl.ni + i) * 16 + hh) * 2];
-      swscl[i * 2 + tid / 2] = mi == kNegInf ? 0.f : fast_exp2(mi - Mr) * inv;
+      swscl[i * 2 + o / 2] = mi == kNegInf ? 0.f : fast_exp2(mi - Mr) * inv;
     }
-    if (a.lse && hh < G) {
+    if (a.lse && hh < G && lane == 0) {
       const size_t rr = (size_t)b * dm.Hq + g * G + hh;
       a.lse[(size_t)(1 + br) * dm.B * dm.Hq + rr] = (M + __log2f(L)) * kLn2;
       if (br == 0) {
@@ -493,12 +558,15 @@ __global__ __launch_bounds__(256) void k_dec_merge(Dims dm, DecArgs a, DecPlan p
   if (tid >= 2 * DV || hh >= G) return;
   const int hl = hh - h0;
   float oc = 0.f;
+#pragma unroll 8
   for (int c = 0; c < pl.nc; ++c) oc += a.w.part_o[(((size_t)bg * pl.nc + c) * 16 + hh) * DV + e] * cscl[c * 2 + hl];
   float ob[2] = {0.f, 0.f};
-  for (int it = 0; it < pl.ni; ++it) {
-    const float v = a.w.sw_o[(((size_t)bg * pl.ni + it) * 16 + hh) * DV + e] * swscl[it * 2 + hl];
-    if (it < pl.nis) ob[0] += v; else ob[1] += v;
-  }
+#pragma unroll 8
+  for (int it = 0; it < pl.nis; ++it)
+    ob[0] += a.w.sw_o[(((size_t)bg * pl.ni + it) * 16 + hh) * DV + e] * swscl[it * 2 + hl];
+#pragma unroll 8
+  for (int it = pl.nis; it < pl.ni; ++it)
+    ob[1] += a.w.sw_o[(((size_t)bg * pl.ni + it) * 16 + hh) * DV + e] * swscl[it * 2 + hl];
   const size_t row = (size_t)b * dm.Hq + g * G + hh;
   const float o = gts[hl * 3 + 0] * oc + gts[hl * 3 + 1] * ob[0] + gts[hl * 3 + 2] * ob[1];
   ((T*)a.o)[row * DV + e] = from_f32<T>(o);
@@ -519,13 +587,13 @@ static hipError_t decode_impl(const Dims& dm, const DecArgs& a, const DecPlan& p
   const int BG = dm.B * dm.Hkv;
   if ((e = mark()) != hipSuccess) return e;
   if (pl.nc > 0) {
-    const size_t lds = (size_t)kDecTPC * 64 * 8 * 4 + 32 * (DV + 8) * sizeof(T);
-    k_dec_cmp<T, DK, DV><<<BG * pl.nc, 64, lds, s>>>(dm, a, pl);
+    k_dec_cmp<T, DK, DV><<<BG * pl.nc, 64, 0, s>>>(dm, a, pl);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = mark()) != hipSuccess) return e;
   {
-    const size_t lds = (((size_t)dm.nsel + 3) & ~(size_t)3) * 4 + (size_t)pl.nc * 16 * 4 * 3 + 16 * 4;
+    const size_t lds = (((size_t)dm.nsel + 3) & ~(size_t)3) * 4 + (size_t)pl.nc * 16 * 4 * 3 + 16 * 4 +
+                       2 * 16 * 29 * 4;
     if (lds > 64 * 1024)
       hipFuncSetAttribute((const void*)k_dec_combine, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     k_dec_combine<<<BG, 1024, lds, s>>>(dm, a, pl);
