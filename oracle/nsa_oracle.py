@@ -42,7 +42,7 @@ from scipy.special import erf
 __all__ = [
     "Params", "gate", "compress", "remap_matrix", "attend", "n_cmp_visible",
     "candidate_blocks", "forced_blocks", "top_n", "is_near_tie", "forward",
-    "decode", "backward", "round_io", "gelu", "gelu_grad", "sigmoid",
+    "decode", "backward", "dq_rows", "round_io", "gelu", "gelu_grad", "sigmoid",
     "cmp_keys", "slc_keys", "win_keys", "decode_token_count",
 ]
 
@@ -459,6 +459,39 @@ def _phi_bwd(kv, phi, dout, p: Params):
         dkv[:, i * p.d: i * p.d + p.l] += du
         grads["pe"] += du.sum(axis=(0, 2))
     return dkv, grads
+
+
+def dq_rows(p: Params, q_rows, k, v, kc, vc, g_rows, d_o_rows, idx_rows, rows) -> np.ndarray:
+    """dq of the given query positions only (the same per-row arithmetic as
+    backward(): dq_t depends on row t and the keys/values it attends).
+
+    q_rows [B,R,Hq,dk], d_o_rows [B,R,Hq,dv], g_rows [B,R,Hq,3] gates, idx_rows
+    [B,R,Hkv,n]; k, v raw and kc, vc compressed keys/values of whole sequences.
+    """
+    B, R, Hq, dk_ = q_rows.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    sc = _scale(p, dk_)
+    dq = np.zeros_like(q_rows)
+    for b in range(B):
+        for r, t in enumerate(rows):
+            t = int(t)
+            for g in range(Hkv):
+                hs = slice(g * G, (g + 1) * G)
+                qh, dO, gg = q_rows[b, r, hs], d_o_rows[b, r, hs], g_rows[b, r, hs]
+                branches = [
+                    (kc[b, :, g], vc[b, :, g], cmp_keys(t, p)),
+                    (k[b, :, g], v[b, :, g], slc_keys(t, [j for j in idx_rows[b, r, g] if j >= 0], p)),
+                    (k[b, :, g], v[b, :, g], win_keys(t, p)),
+                ]
+                for c, (KK, VV, keys) in enumerate(branches):
+                    if len(keys) == 0:
+                        continue
+                    K, V = KK[keys], VV[keys]
+                    O, _, P = attend(qh, K, V, sc)
+                    dqh, _, _ = _attend_bwd(qh, K, V, P, O, gg[:, c:c + 1] * dO, sc)
+                    dq[b, r, hs] += dqh
+    return dq
 
 
 def backward(p: Params, q, k, v, x, w_gate, phi_k, phi_v, d_o, idx) -> Dict[str, object]:

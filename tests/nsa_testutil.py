@@ -36,3 +36,19 @@ def assert_close(gpu, ref, name, atol=ATOL, rtol=RTOL):
         raise AssertionError(f"{name}: {bad.sum()} of {bad.size} elements out of tolerance; first at "
                              f"{tuple(i)}: gpu={gpu[tuple(i)]} oracle={ref[tuple(i)]} max err={err.max():.3e}")
     return float(err.max()) if err.size else 0.0
+
+
+class SampledRows:
+    """Stand-in for a [B, T, ...] array of which only some positions are held
+    (rows R, data [B, R, ...]); indexing [b, t] returns position t's data.
+    Lets the oracle evaluate sampled rows of a full-size sequence without the
+    whole query tensor in float64."""
+
+    def __init__(self, data, rows, T):
+        self.data = np.asarray(data)
+        self.pos = {int(t): i for i, t in enumerate(rows)}
+        self.shape = (self.data.shape[0], T) + tuple(self.data.shape[2:])
+
+    def __getitem__(self, idx):
+        b, t = idx
+        return self.data[b, self.pos[int(t)]]

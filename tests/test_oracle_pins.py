@@ -446,6 +446,34 @@ def test_backward_matches_finite_differences(phi):
             check(inp["phi_v"][key], gr["dphi_v"][key])
 
 
+def test_dq_rows_matches_finite_differences():
+    """Per-row dq (used where the whole backward is too large for the oracle)
+    against central differences of the loss in q at those rows."""
+    p, inp = small_problem(B=1, T=26, Hkv=2, G=2, dk=3, dv=2, C=4, phi="mlp", l=4, d=2,
+                           l_sel=8, n=2, w=5, hidden=4, seed=13)
+    p = O.Params(l=4, d=2, l_sel=8, n=3, w=5, phi="mlp", io=None)
+    rng = np.random.default_rng(17)
+    d_o = rng.standard_normal((1, 26, 4, 2))
+    idx = O.forward(p, **inp)["idx"]
+    rows = np.array([3, 17, 25])
+    kc = O.compress(inp["k"], inp["phi_k"], p)
+    vc = O.compress(inp["v"], inp["phi_v"], p)
+    g_rows = O.gate(inp["x"][:, rows], inp["w_gate"])
+    dq = O.dq_rows(p, inp["q"][:, rows], inp["k"], inp["v"], kc, vc, g_rows, d_o[:, rows], idx[:, rows], rows)
+    eps = 1e-6
+    for r, t in enumerate(rows):
+        for h in range(4):
+            for e in range(3):
+                old = inp["q"][0, t, h, e]
+                inp["q"][0, t, h, e] = old + eps
+                lp = _loss(p, inp, d_o, idx)
+                inp["q"][0, t, h, e] = old - eps
+                lm = _loss(p, inp, d_o, idx)
+                inp["q"][0, t, h, e] = old
+                fd = (lp - lm) / (2 * eps)
+                assert abs(fd - dq[0, r, h, e]) < 1e-6 + 1e-6 * abs(fd), (t, h, e, fd, dq[0, r, h, e])
+
+
 def test_backward_dense_case_matches_torch_autograd():
     T = 40
     p, inp = small_problem(B=1, T=T, Hkv=2, G=2, dk=6, dv=5, C=5, l=1, d=1, l_sel=8,
