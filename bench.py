@@ -107,17 +107,85 @@ def source_hash(paths):
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel, src_files):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 PMC summary,
-    when it was taken from the current kernel sources; else None."""
+_CSRC = "long_context_sparse_phi_amd/csrc/"
+_HDRS = [_CSRC + h for h in ("nsa_common.hpp", "nsa_kernels.hpp", "nsa_tiles.hpp")]
+# kernels whose HBM traffic is reported: name pattern in the profiler's kernel
+# names, and the sources their code comes from
+TRAFFIC_KERNELS = {
+    "k_slc": (r"k_slcI", [_CSRC + "nsa_attn.hip"] + _HDRS),
+    "k_dec_cmp": (r"k_dec_cmpI", [_CSRC + "nsa_decode.hip"] + _HDRS),
+    "k_cmp_out": (r"k_cmpI.*Lb1E", [_CSRC + "nsa_cmp.hip"] + _HDRS),
+    "k_cmp_lse": (r"k_cmpI.*Lb0E", [_CSRC + "nsa_cmp.hip"] + _HDRS),
+    "k_win": (r"k_winI", [_CSRC + "nsa_attn.hip"] + _HDRS),
+}
+COPY_BYTES = 1 << 30     # calibration: read 1 GiB, write 1 GiB
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 PMC summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel of known size), when it
+    was taken from the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
+    if not os.path.exists(path) or kernel not in TRAFFIC_KERNELS:
         return None
     with open(path) as f:
-        rec = json.load(f).get(kernel)
-    if not rec or rec.get("source_sha") != source_hash(src_files):
+        rec = json.load(f).get("kernels", {}).get(kernel)
+    if not rec or rec.get("source_sha") != source_hash(TRAFFIC_KERNELS[kernel][1]):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def calibrate_copy():
+    """A plain elementwise kernel that reads and writes COPY_BYTES (the PMC
+    calibration: its FETCH_SIZE / WRITE_SIZE give the counters' byte scale)."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 2.0, out=dst)
+    torch.cuda.synchronize()
+    log("copy calibration done")
+
+
+def _pmc_per_kernel(csv_path, counter):
+    """Median value of `counter` per dispatch, keyed by kernel name."""
+    import csv
+    import statistics
+    vals = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: statistics.median(v) for k, v in vals.items()}
+
+
+def write_traffic(cal_fetch, cal_write, run_fetch, run_write, out_path, command):
+    """profiles/traffic.json from four rocprofv3 --pmc runs (FETCH_SIZE and
+    WRITE_SIZE of the copy calibration and of the benchmark)."""
+    import re
+    cf, cw = _pmc_per_kernel(cal_fetch, "FETCH_SIZE"), _pmc_per_kernel(cal_write, "WRITE_SIZE")
+    kf = max(cf, key=cf.get)                     # the 1 GiB elementwise kernel
+    f_fetch = COPY_BYTES / (cf[kf] * 1024.0)
+    f_write = COPY_BYTES / (cw[kf] * 1024.0)
+    rf, rw = _pmc_per_kernel(run_fetch, "FETCH_SIZE"), _pmc_per_kernel(run_write, "WRITE_SIZE")
+    kernels = {}
+    for name, (pat, srcs) in TRAFFIC_KERNELS.items():
+        hits = [k for k in rf if re.search(pat, k)]
+        if not hits:
+            continue
+        k = max(hits, key=lambda x: rf[x])
+        fetch = rf[k] * 1024.0 * f_fetch
+        write = rw.get(k, 0.0) * 1024.0 * f_write
+        kernels[name] = {"kernel_name": k, "fetch_kib_per_dispatch": rf[k], "write_kib_per_dispatch": rw.get(k),
+                         "hbm_read_bytes": round(fetch), "hbm_write_bytes": round(write),
+                         "hbm_bytes_per_launch": round(fetch + write), "source_sha": source_hash(srcs)}
+    rec = {"command": command, "calibration": {"kernel_name": kf, "bytes_each_way": COPY_BYTES,
+                                               "fetch_kib": cf[kf], "write_kib": cw[kf],
+                                               "fetch_scale": f_fetch, "write_scale": f_write},
+           "kernels": kernels}
+    with open(out_path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
 
 
 # ---------------------------------------------------------------- prefill leg
@@ -189,14 +257,21 @@ def prefill_roofline(w, stage_ms):
     i = max(range(len(stage_ms)), key=lambda s: stage_ms[s])
     name, kern = PREFILL_STAGES[i]
     achieved = work[name] / (stage_ms[i] * 1e-3) / 1e12
-    src = {"k_cmp_out": ["long_context_sparse_phi_amd/csrc/nsa_cmp.hip"],
-           "k_cmp_lse": ["long_context_sparse_phi_amd/csrc/nsa_cmp.hip"],
-           "k_slc": ["long_context_sparse_phi_amd/csrc/nsa_attn.hip"],
-           "k_win": ["long_context_sparse_phi_amd/csrc/nsa_attn.hip"]}.get(kern, [])
     return {"kernel": kern, "stage": name, "bound": "mfma", "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic_for(kern, src) if src else None,
+            "traffic": traffic_for(kern),
             "launch_ms": round(stage_ms[i], 4), "algorithmic_flops_per_launch": work[name]}
+
+
+def selected_gather(w, stage_ms):
+    """The selected branch as a gather: K/V bytes of every (position, KV head)'s
+    selected tokens (16 FLOP/B at G = 16, served mostly by L2 and MALL), per
+    second of the selected-attention stage."""
+    _, n_slc, _ = key_counts(w)
+    nbytes = int(n_slc.sum()) * w.B * w.H_kv * (w.d_k + w.d_v) * 2
+    i = [n for n, _ in PREFILL_STAGES].index("selected")
+    return {"kernel": "k_slc", "block_fetch_bytes": nbytes,
+            "TB_per_s": round(nbytes / (stage_ms[i] * 1e-3) / 1e12, 2)}
 
 
 # ---------------------------------------------------------------- decode leg
@@ -306,7 +381,7 @@ def run_decode(steps, warmup, wname="decode_64k"):
         "stages_us": {n: round(ms * 1e3, 2) for (n, _), ms in zip(DECODE_STAGES, stage_ms)},
         "roofline": {"kernel": "k_dec_cmp", "stage": "cmp_partials", "bound": "hbm", "achieved": round(gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                     "traffic": traffic_for("k_dec_cmp", ["long_context_sparse_phi_amd/csrc/nsa_decode.hip"]),
+                     "traffic": traffic_for("k_dec_cmp"),
                      "algorithmic_bytes_per_launch": cmp_bytes, "launch_us": round(stage_ms[0] * 1e3, 2)},
         "cold_cache": "512 MB buffer written then read before every step (outside the timed events)",
     }
@@ -451,7 +526,19 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--bwd-steps", type=int, default=5)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run the 1 GiB elementwise kernel used to scale the PMC byte counters")
+    ap.add_argument("--traffic-from", nargs=4, metavar=("CAL_FETCH", "CAL_WRITE", "RUN_FETCH", "RUN_WRITE"),
+                    help="rocprofv3 counter CSVs; writes the traffic summary and exits (no GPU use)")
+    ap.add_argument("--traffic-out", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    ap.add_argument("--traffic-command", default="")
     args = ap.parse_args()
+    if args.traffic_from:
+        write_traffic(*args.traffic_from, args.traffic_out, args.traffic_command)
+        return
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this NSA build runs on exactly one GPU; multi-GPU runs are not supported",
                           "n_gpus": args.gpus}))
@@ -476,6 +563,7 @@ def main():
         "mfma_frac_useful": round(useful / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "stages_ms": {name: round(ms, 4) for (name, _), ms in zip(PREFILL_STAGES, stage_ms)},
         "roofline": prefill_roofline(w, stage_ms),
+        "selected_gather": selected_gather(w, stage_ms),
     }
     if not args.no_decode:
         out["decode"] = run_decode(args.decode_steps, 3)

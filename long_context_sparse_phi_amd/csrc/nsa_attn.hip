@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256, 2) void k_slc(Dims dm, SlcArgs a) {
   {
     const T* qp = (const T*)a.q + qrow * DK + qd * 8;
 #pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) qf[ks] = cv ? load_frag(qp + ks * 32) : zero_frag<T>();
+    for (int ks = 0; ks < DK / 32; ++ks) qf[ks] = cv ? load_frag_nt(qp + ks * 32) : zero_frag<T>();
   }
   // the n block indices of this position, one per lane (n <= 32)
   const int* ids = a.idx + ((size_t)(b * dm.T + t) * dm.Hkv + g) * dm.n;
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256, 2) void k_slc(Dims dm, SlcArgs a) {
     OT* op = (OT*)a.o + qrow * DV + qd * 4;
 #pragma unroll
     for (int dt = 0; dt < DV / 16; ++dt)
-      store4(op + dt * 16, oacc[dt][0] * inv, oacc[dt][1] * inv, oacc[dt][2] * inv, oacc[dt][3] * inv);
+      store4_nt(op + dt * 16, oacc[dt][0] * inv, oacc[dt][1] * inv, oacc[dt][2] * inv, oacc[dt][3] * inv);
     if (qd == 0) a.lse[qrow] = (m + __log2f(tot)) * kLn2;
   }
 }

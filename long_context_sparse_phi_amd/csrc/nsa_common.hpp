@@ -74,6 +74,21 @@ __device__ __forceinline__ void store_cols4x8(float* dst, int stride, const Frag
     store_col4(dst + e * stride, frag_at(r[0], e), frag_at(r[1], e), frag_at(r[2], e), frag_at(r[3], e));
 }
 
+// Streaming variants: data read or written once per kernel (query rows,
+// outputs) carry the non-temporal hint so they do not displace reused data
+// (key/value tiles) from L2 and the MALL.
+__device__ __forceinline__ Frag8<bf16> load_frag_nt(const bf16* p) {
+  Frag8<bf16> f;
+  f.v = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p));
+  return f;
+}
+__device__ __forceinline__ Frag8<float> load_frag_nt(const float* p) {
+  Frag8<float> f;
+  f.lo = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  f.hi = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
+  return f;
+}
+
 template <typename T> __device__ __forceinline__ Frag8<T> zero_frag();
 template <> __device__ __forceinline__ Frag8<bf16> zero_frag<bf16>() {
   Frag8<bf16> f;
@@ -132,6 +147,14 @@ __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float
   bf16x4 v;
   v[0] = (bf16)a; v[1] = (bf16)b; v[2] = (bf16)c; v[3] = (bf16)d;
   *reinterpret_cast<bf16x4*>(p) = v;
+}
+__device__ __forceinline__ void store4_nt(bf16* p, float a, float b, float c, float d) {
+  bf16x4 v;
+  v[0] = (bf16)a; v[1] = (bf16)b; v[2] = (bf16)c; v[3] = (bf16)d;
+  __builtin_nontemporal_store(v, reinterpret_cast<bf16x4*>(p));
+}
+__device__ __forceinline__ void store4_nt(float* p, float a, float b, float c, float d) {
+  __builtin_nontemporal_store(f32x4{a, b, c, d}, reinterpret_cast<f32x4*>(p));
 }
 __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
   f32x4 v;
