@@ -465,6 +465,55 @@ def run_backward(steps, warmup, wname="train_16k"):
             "stages_ms": {n: round(x, 4) for n, x in zip(BWD_STAGES, stage_ms)}}
 
 
+# ---------------------------------------------------------------- dense baseline
+
+def run_dense_comparison(lengths=(8192, 16384, 32768, 65536), wname="prefill_64k", reps=2):
+    """NSA prefill forward against dense causal attention on the same inputs
+    (the comparison the pages' kernel-speed figures make), per sequence length:
+    milliseconds of each (HIP events around the call, after one warmup) and the
+    ratio."""
+    import torch
+    import long_context_sparse_phi_amd as nsa
+    import nsa_inputs as NI
+
+    w = NI.workload(wname)
+    log(f"generating inputs for the dense comparison ({wname})")
+    inp = NI.make_prefill_inputs(w, 0)
+    dev = torch.device("cuda:0")
+    full = {k: ({kk: vv.to(dev) for kk, vv in v.items()} if isinstance(v, dict) else v.to(dev))
+            for k, v in inp.items()}
+    del inp
+    out = []
+    for T in lengths:
+        wt = w.replace(T=T)
+        cfg = nsa.config_from_workload(wt)
+        d = {k: (v if isinstance(v, dict) or k == "w_gate" else v[:, :T].contiguous()) for k, v in full.items()}
+
+        def timed(fn):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        ws_n = torch.empty(nsa.workspace_size(cfg, nsa.NSA_OP_FWD_PREFILL), dtype=torch.uint8, device=dev)
+        o_n = torch.empty(1, T, wt.H_q, wt.d_v, dtype=cfg.torch_dtype, device=dev)
+        t_nsa = timed(lambda: nsa.nsa_fwd_prefill(cfg, d["q"], d["k"], d["v"], d["x"], d["w_gate"], d["phi_k"],
+                                                  d["phi_v"], out=o_n, workspace=ws_n))
+        del ws_n
+        ws_d = torch.empty(nsa.workspace_size(cfg, nsa.NSA_OP_DENSE), dtype=torch.uint8, device=dev)
+        t_dense = timed(lambda: nsa.nsa_dense_fwd(cfg, d["q"], d["k"], d["v"], out=o_n, workspace=ws_d))
+        del ws_d, d
+        log(f"T={T}: NSA {t_nsa:.2f} ms, dense {t_dense:.2f} ms")
+        out.append({"T": T, "nsa_ms": round(t_nsa, 3), "dense_ms": round(t_dense, 3),
+                    "speedup": round(t_dense / t_nsa, 2)})
+    return {"workload": wname, "pass": "forward", "per_length": out}
+
+
 # ---------------------------------------------------------------- CPU oracle leg
 
 class _SampledRows:
@@ -526,6 +575,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--bwd-steps", type=int, default=5)
+    ap.add_argument("--no-dense", action="store_true", help="skip the NSA-vs-dense comparison")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the 1 GiB elementwise kernel used to scale the PMC byte counters")
     ap.add_argument("--traffic-from", nargs=4, metavar=("CAL_FETCH", "CAL_WRITE", "RUN_FETCH", "RUN_WRITE"),
@@ -569,6 +619,8 @@ def main():
         out["decode"] = run_decode(args.decode_steps, 3)
     if not args.no_backward:
         out["backward"] = run_backward(args.bwd_steps, 2)
+    if not args.no_dense:
+        out["dense_baseline"] = run_dense_comparison()
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(args.workload)

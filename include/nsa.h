@@ -63,7 +63,8 @@ typedef enum nsa_status {
 typedef enum nsa_dtype { NSA_BF16 = 0, NSA_FP32 = 1 } nsa_dtype;
 typedef enum nsa_phi_kind { NSA_PHI_MEANPOOL = 0, NSA_PHI_MLP = 1 } nsa_phi_kind;
 typedef enum nsa_op {
-  NSA_OP_FWD_PREFILL = 0, NSA_OP_FWD_DECODE = 1, NSA_OP_BWD = 2, NSA_OP_COMPRESS = 3
+  NSA_OP_FWD_PREFILL = 0, NSA_OP_FWD_DECODE = 1, NSA_OP_BWD = 2, NSA_OP_COMPRESS = 3,
+  NSA_OP_DENSE = 4
 } nsa_op;
 
 /* Shapes and hyper-parameters.
@@ -150,6 +151,20 @@ typedef struct nsa_bwd_args {
   nsa_phi_grads d_phi_k, d_phi_v;
 } nsa_bwd_args;
 
+/* Dense causal attention, the baseline the pages measure NSA against
+ * (kernel speed comparison of the youleyou page, 效率分析): for every query
+ * head h of KV head h/G,
+ *   o[b,t,h] = sum_{j<=t} softmax_j(scale q[b,t,h].k[b,j,h/G]) v[b,j,h/G].
+ * Uses batch, seqlen, n_kv_heads, group_size, d_k, d_v, io_dtype and scale of
+ * p; the NSA hyper-parameters must still be valid but do not matter.
+ * Inputs q [B,T,Hq,dk], k [B,T,Hkv,dk], v [B,T,Hkv,dv]; output o [B,T,Hq,dv]
+ * io_dtype; optional lse [B,T,Hq] fp32 natural-log log-sum-exp.  All device
+ * pointers, caller-owned, 16-byte aligned.  Workspace: NSA_OP_DENSE. */
+typedef struct nsa_dense_args {
+  const void *q, *k, *v;
+  void *o, *lse;
+} nsa_dense_args;
+
 /* Version of this header the library was built from (NSA_ABI_VERSION). */
 int nsa_abi_version(void);
 
@@ -173,6 +188,8 @@ nsa_status nsa_fwd_decode(const nsa_params* p, const nsa_decode_args* a, void* w
                           size_t ws_bytes, void* stream);
 nsa_status nsa_bwd(const nsa_params* p, const nsa_bwd_args* a, void* ws,
                    size_t ws_bytes, void* stream);
+nsa_status nsa_dense_fwd(const nsa_params* p, const nsa_dense_args* a, void* ws,
+                         size_t ws_bytes, void* stream);
 
 /* Timed variants, for measurement.  Identical work to the entry points
  * above; in addition hipEventRecord(events[i], stream) is issued before stage
@@ -180,13 +197,15 @@ nsa_status nsa_bwd(const nsa_params* p, const nsa_bwd_args* a, void* ws,
  * hipEventElapsedTime(events[i], events[i+1]) is the duration of stage i.
  * `events` holds n_events hipEvent_t created by the caller; n_events must be
  * at least the stage count + 1 (NSA_ERR_INVALID_ARG otherwise).
- * Prefill stages (8): 0 gates, 1 compress K, 2 compress V, 3 transpose V,
+ * Prefill stages (8): 0 gates, 1 compress K, 2 compress V, 3 transposed V
+ *   and fragment-ordered K/V copies,
  *   4 compressed log-sum-exp, 5 compressed output + scores + top-n,
  *   6 selected attention, 7 window attention + gated combine.
  * Decode stages (3): 0 compressed-cache partial softmax states and scores,
  *   1 combine + group scores + top-n + gates, 2 selected/window attention +
  *   merge + gated combine.
- * Backward stages (8): 0 gates, 1 transposed copies of k, k_cmp, q, dO,
+ * Backward stages (8): 0 gates, 1 fragment-ordered copies of (k, v, k^T)
+ *   and (k_cmp, v_cmp, k_cmp^T),
  *   2 row terms <dO, O_c> + dq, 3 compressed-key dK/dV, 4 window-key dK/dV,
  *   5 selected-block reverse index + dK/dV, 6 phi backward, 7 dW_g. */
 int nsa_prefill_stage_count(void);

@@ -16,11 +16,12 @@ from typing import Dict, Optional
 import torch
 
 from . import _lib
-from ._lib import (NSA_BF16, NSA_FP32, NSA_OP_BWD, NSA_OP_COMPRESS, NSA_OP_FWD_DECODE, NSA_OP_FWD_PREFILL,
+from ._lib import (NSA_BF16, NSA_FP32, NSA_OP_BWD, NSA_OP_COMPRESS, NSA_OP_DENSE, NSA_OP_FWD_DECODE,
+                   NSA_OP_FWD_PREFILL,
                    NSA_PHI_MEANPOOL, NSA_PHI_MLP, NSAError)
 
 __all__ = ["Config", "workspace_size", "nsa_compress", "nsa_fwd_prefill", "nsa_fwd_decode",
-           "nsa_bwd", "load_library", "NSAError"]
+           "nsa_bwd", "nsa_dense_fwd", "load_library", "NSAError"]
 
 load_library = _lib.load
 
@@ -259,6 +260,30 @@ def nsa_bwd(cfg: Config, q, k, v, x, w_gate, phi_k, phi_v, saved: Dict[str, torc
     st = _lib.load().nsa_bwd(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(), _stream(dev))
     if st != 0:
         raise NSAError("nsa_bwd", st)
+    res["_workspace"] = ws
+    return res
+
+
+def nsa_dense_fwd(cfg: Config, q, k, v, *, out=None, want_lse: bool = False,
+                  workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Dense causal attention (the baseline NSA is measured against): every query
+    attends to all keys at or before its position.  Uses cfg's shapes only."""
+    dev = q.device
+    dt = cfg.torch_dtype
+    B, T, Hq, Hkv = cfg.B, cfg.T, cfg.H_q, cfg.H_kv
+    _check(q, "q", (B, T, Hq, cfg.d_k), dt, dev)
+    _check(k, "k", (B, T, Hkv, cfg.d_k), dt, dev)
+    _check(v, "v", (B, T, Hkv, cfg.d_v), dt, dev)
+    res = {"o": out if out is not None else torch.empty(B, T, Hq, cfg.d_v, dtype=dt, device=dev)}
+    if want_lse:
+        res["lse"] = torch.empty(B, T, Hq, dtype=torch.float32, device=dev)
+    a = _lib.nsa_dense_args(q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(), o=res["o"].data_ptr(),
+                            lse=res["lse"].data_ptr() if want_lse else None)
+    ws = _workspace(cfg, NSA_OP_DENSE, dev, workspace)
+    p = cfg.params()
+    st = _lib.load().nsa_dense_fwd(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(), _stream(dev))
+    if st != 0:
+        raise NSAError("nsa_dense_fwd", st)
     res["_workspace"] = ws
     return res
 

@@ -131,6 +131,9 @@ size_t plan_prefill(const Dims& dm, void* ws, PrefillWs* w) {
 
 nsa_status hip_status(hipError_t e) { return e == hipSuccess ? NSA_OK : NSA_ERR_HIP; }
 
+// Dense baseline workspace: the transposed V the window kernel reads.
+size_t dense_ws_bytes(const Dims& dm) { return (size_t)dm.B * dm.Hkv * dm.dv * dm.Tp * esize(dm) + 256; }
+
 // Compress one tensor (keys: D = dk, values: D = dv) into out (and outT).
 hipError_t run_compress(const Dims& dm, int D, const void* x, const nsa_phi_weights* phi, void* out,
                         void* outT, void* phi_ws_ptr, hipStream_t s) {
@@ -197,6 +200,7 @@ nsa_status nsa_workspace_size(const nsa_params* p, nsa_op op, size_t* bytes) {
       case NSA_OP_FWD_DECODE: *bytes = decode_ws_bytes(dm); return NSA_OK;
       case NSA_OP_BWD: *bytes = bwd_ws_bytes(dm); return NSA_OK;
       case NSA_OP_COMPRESS: *bytes = phi_ws(dm) > 0 ? phi_ws(dm) : 256; return NSA_OK;
+      case NSA_OP_DENSE: *bytes = dense_ws_bytes(dm); return NSA_OK;
     }
     return NSA_ERR_INVALID_ARG;
   } catch (...) {
@@ -274,7 +278,7 @@ static nsa_status prefill_impl(const nsa_params* p, const nsa_prefill_args* a, v
     SlcArgs sa;
     sa.q = a->q; sa.kvf = w.kvf; sa.idx = idx; sa.o = o_slc; sa.lse = lse + BTH; sa.o_f32 = o_f32;
     if (sg.mark() || launch_slc(dm, sa, s) != hipSuccess) return NSA_ERR_HIP;
-    WinArgs wa;
+    WinArgs wa{};
     wa.q = a->q; wa.k = a->k; wa.vt = w.vt; wa.o_cmp = o_cmp; wa.o_slc = o_slc; wa.gates = gates;
     wa.o_win = o_win; wa.lse = lse + 2 * BTH; wa.o = a->o; wa.o_f32 = o_f32;
     if (sg.mark() || launch_win_combine(dm, wa, s) != hipSuccess) return NSA_ERR_HIP;
@@ -294,6 +298,32 @@ nsa_status nsa_fwd_prefill_timed(const nsa_params* p, const nsa_prefill_args* a,
                                  void* stream, void* const* events, int n_events) {
   if (!events) return NSA_ERR_INVALID_ARG;
   return prefill_impl(p, a, ws, ws_bytes, stream, events, n_events);
+}
+
+// Dense causal attention: the window kernel with a window covering every key
+// and no gated combine.
+nsa_status nsa_dense_fwd(const nsa_params* p, const nsa_dense_args* a, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    Dims dm;
+    nsa_status st = make_dims(p, &dm);
+    if (st != NSA_OK) return st;
+    if (!a) return NSA_ERR_INVALID_ARG;
+    const void* req[] = {a->q, a->k, a->v, a->o};
+    for (const void* r : req)
+      if (!r || !aligned16(r)) return NSA_ERR_INVALID_ARG;
+    if (a->lse && !aligned16(a->lse)) return NSA_ERR_INVALID_ARG;
+    if (ws_bytes < dense_ws_bytes(dm) || !ws || !aligned16(ws)) return NSA_ERR_WORKSPACE;
+    if ((st = check_device()) != NSA_OK) return st;
+    dm.w = dm.T;
+    hipStream_t s = (hipStream_t)stream;
+    if (launch_transpose_seq(dm, dm.B, dm.T, dm.Hkv, dm.dv, dm.Tp, a->v, ws, s) != hipSuccess) return NSA_ERR_HIP;
+    WinArgs wa{};
+    wa.q = a->q; wa.k = a->k; wa.vt = ws; wa.o = a->o; wa.lse = (float*)a->lse; wa.dense = 1;
+    if (launch_win_combine(dm, wa, s) != hipSuccess) return NSA_ERR_HIP;
+    return NSA_OK;
+  } catch (...) {
+    return NSA_ERR_INTERNAL;
+  }
 }
 
 int nsa_prefill_stage_count(void) { return kPrefillStages; }

@@ -393,8 +393,15 @@ __global__ __launch_bounds__(NW * 64, 2) void k_win(Dims dm, WinArgs a) {
     const float inv = 1.f / tot;
     const size_t row = (size_t)(b * dm.T + pos[ct]) * dm.Hq + hq[ct];
     if (a.lse && qd == 0) a.lse[row] = (m[ct] + __log2f(tot)) * kLn2;
-    const float g0 = a.gates[row * 3 + 0], g1 = a.gates[row * 3 + 1], g2 = a.gates[row * 3 + 2];
     const size_t ob = row * DV + qd * 4;
+    if (a.dense) {
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt)
+        store4((T*)a.o + ob + dt * 16, oacc[dt][ct][0] * inv, oacc[dt][ct][1] * inv, oacc[dt][ct][2] * inv,
+               oacc[dt][ct][3] * inv);
+      continue;
+    }
+    const float g0 = a.gates[row * 3 + 0], g1 = a.gates[row * 3 + 1], g2 = a.gates[row * 3 + 2];
 #pragma unroll
     for (int dt = 0; dt < DV / 16; ++dt) {
       float ow[4], oc[4], os[4];

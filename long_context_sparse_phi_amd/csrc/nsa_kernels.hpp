@@ -111,6 +111,7 @@ struct WinArgs {
   float* lse;          // optional [B,T,Hq]
   void* o;             // [B,T,Hq,dv]
   int o_f32;           // o_cmp / o_slc / o_win are fp32 instead of the I/O type
+  int dense;           // o = window output alone (dense causal attention when w >= T)
 };
 hipError_t launch_win_combine(const Dims& dm, const WinArgs& a, hipStream_t s);
 

@@ -42,7 +42,7 @@ from scipy.special import erf
 __all__ = [
     "Params", "gate", "compress", "remap_matrix", "attend", "n_cmp_visible",
     "candidate_blocks", "forced_blocks", "top_n", "is_near_tie", "forward",
-    "decode", "backward", "dq_rows", "round_io", "gelu", "gelu_grad", "sigmoid",
+    "decode", "backward", "dq_rows", "dense_causal", "round_io", "gelu", "gelu_grad", "sigmoid",
     "cmp_keys", "slc_keys", "win_keys", "decode_token_count",
 ]
 
@@ -459,6 +459,33 @@ def _phi_bwd(kv, phi, dout, p: Params):
         dkv[:, i * p.d: i * p.d + p.l] += du
         grads["pe"] += du.sum(axis=(0, 2))
     return dkv, grads
+
+
+def dense_causal(q, k, v, scale=None):
+    """Dense causal attention, the baseline NSA's speed is measured against
+    [YLY 效率分析]: query head h of KV head h // G attends to every key j <= t.
+
+    q [B,T,Hq,dk], k [B,T,Hkv,dk], v [B,T,Hkv,dv] -> o [B,T,Hq,dv], lse [B,T,Hq]
+    (natural log).
+    """
+    B, T, Hq, dk = q.shape
+    Hkv, dv = k.shape[2], v.shape[3]
+    G = Hq // Hkv
+    sc = 1.0 / np.sqrt(dk) if scale is None else scale
+    o = np.zeros((B, T, Hq, dv))
+    lse = np.zeros((B, T, Hq))
+    causal = np.tril(np.ones((T, T), dtype=bool))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            s = sc * (q[b, :, h] @ k[b, :, g].T)
+            s = np.where(causal, s, -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            e = np.exp(s - m)
+            l_ = e.sum(axis=1, keepdims=True)
+            o[b, :, h] = (e @ v[b, :, g]) / l_
+            lse[b, :, h] = (m + np.log(l_))[:, 0]
+    return o, lse
 
 
 def dq_rows(p: Params, q_rows, k, v, kc, vc, g_rows, d_o_rows, idx_rows, rows) -> np.ndarray:

@@ -494,3 +494,21 @@ def test_backward_dense_case_matches_torch_autograd():
     np.testing.assert_allclose(gr["dk"], tk.grad.numpy(), rtol=1e-10, atol=1e-11)
     np.testing.assert_allclose(gr["dv"], tv.grad.numpy(), rtol=1e-10, atol=1e-11)
     np.testing.assert_allclose(gr["dw_gate"], tw.grad.numpy(), rtol=1e-10, atol=1e-11)
+
+
+def test_dense_causal_matches_torch_sdpa():
+    """The dense baseline against torch's fp64 scaled-dot-product attention
+    (causal, GQA by repeating the KV heads)."""
+    rng = np.random.default_rng(23)
+    B, T, Hkv, G, dk, dv = 2, 37, 2, 3, 5, 4
+    q = rng.standard_normal((B, T, Hkv * G, dk))
+    k = rng.standard_normal((B, T, Hkv, dk))
+    v = rng.standard_normal((B, T, Hkv, dv))
+    o, lse = O.dense_causal(q, k, v)
+    tq, tk, tv = (torch.from_numpy(a).permute(0, 2, 1, 3) for a in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk.repeat_interleave(G, 1), tv.repeat_interleave(G, 1), is_causal=True).permute(0, 2, 1, 3)
+    np.testing.assert_allclose(o, ref.numpy(), rtol=1e-12, atol=1e-12)
+    s = np.einsum("bthd,bjhd->bhtj", q, np.repeat(k, G, axis=2)) / np.sqrt(dk)
+    s = np.where(np.tril(np.ones((T, T), dtype=bool)), s, -np.inf)
+    np.testing.assert_allclose(lse, np.transpose(np.log(np.exp(s).sum(-1)), (0, 2, 1)), rtol=1e-12)
