@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define NSA_ABI_VERSION 1
+#define NSA_ABI_VERSION 2
 
 typedef enum nsa_status {
   NSA_OK = 0,
@@ -64,7 +64,7 @@ typedef enum nsa_dtype { NSA_BF16 = 0, NSA_FP32 = 1 } nsa_dtype;
 typedef enum nsa_phi_kind { NSA_PHI_MEANPOOL = 0, NSA_PHI_MLP = 1 } nsa_phi_kind;
 typedef enum nsa_op {
   NSA_OP_FWD_PREFILL = 0, NSA_OP_FWD_DECODE = 1, NSA_OP_BWD = 2, NSA_OP_COMPRESS = 3,
-  NSA_OP_DENSE = 4
+  NSA_OP_DENSE = 4, NSA_OP_APPEND = 5
 } nsa_op;
 
 /* Shapes and hyper-parameters.
@@ -116,20 +116,55 @@ typedef struct nsa_prefill_args {
 } nsa_prefill_args;
 
 /* One decode step per sequence; the new token's key/value are already stored
- * at cache slot S-1 and its query sits at position S-1.
- * Inputs: q [B,Hq,dk], k_cache [B,S,Hkv,dk], v_cache [B,S,Hkv,dv],
- *   k_cmp_cache [B,Ncmp_cap,Hkv,dk], v_cmp_cache [B,Ncmp_cap,Hkv,dv] holding
- *   at least the Ncmp(S) = (S-l)/d+1 complete compressed blocks in their
- *   first rows (cmp_cache_cap = Ncmp_cap >= Ncmp(S)), x [B,C], w_gate.
+ * at cache slot S_b-1 and its query sits at position S_b-1, where S_b is the
+ * number of tokens sequence b holds (youleyou page, 效率分析/解码速度: a step
+ * reads the compressed blocks, the selected blocks and the window of the
+ * cache).
+ * Inputs: q [B,Hq,dk], k_cache [B,S,Hkv,dk], v_cache [B,S,Hkv,dv] with
+ *   S = p->seqlen (the cache capacity), k_cmp_cache [B,Ncmp_cap,Hkv,dk],
+ *   v_cmp_cache [B,Ncmp_cap,Hkv,dv] holding the Ncmp(S_b) = (S_b-l)/d+1
+ *   complete compressed blocks of each sequence in their first rows
+ *   (cmp_cache_cap = Ncmp_cap >= Ncmp(S)), x [B,C], w_gate.
+ *   seq_lens: optional device int32 [B]; NULL means S_b = S for every
+ *   sequence.  Values are clamped into [1, S].  Cache rows at or beyond a
+ *   sequence's own length (raw rows >= S_b, compressed rows >= Ncmp(S_b))
+ *   are never read.
  * Output: o [B,Hq,dv] io_dtype.
- * Optional: idx [B,Hkv,n] int32, p_slc [B,Hkv,Nsel] fp32,
- *   lse [3,B,Hq] fp32, o_branch [3,B,Hq,dv] fp32. */
+ * Optional: idx [B,Hkv,n] int32, p_slc [B,Hkv,Nsel(S)] fp32 (columns at or
+ *   beyond Nsel(S_b) = ceil(S_b/l') are written as 0), lse [3,B,Hq] fp32,
+ *   o_branch [3,B,Hq,dv] fp32. */
 typedef struct nsa_decode_args {
   const void *q, *k_cache, *v_cache, *k_cmp_cache, *v_cmp_cache, *x, *w_gate;
   int32_t cmp_cache_cap;
   void *o;
   void *idx, *p_slc, *lse, *o_branch;
+  const int32_t *seq_lens;
 } nsa_decode_args;
+
+/* Decode-time cache maintenance: append one token per sequence to the raw
+ * caches and keep the compressed caches complete (youleyou page, 令牌压缩:
+ * block i covers tokens i*d .. i*d+l-1; it exists once its last token does).
+ * For sequence b with L = seq_lens[b] tokens before the call:
+ *   k_cache[b, L] = k_new[b], v_cache[b, L] = v_new[b];
+ *   if L+1 >= l and (L+1-l) % d == 0, block i = (L+1-l)/d has just become
+ *   complete: k_cmp_cache[b, i] = phi_k(k_cache[b, i*d .. i*d+l-1]) and
+ *   v_cmp_cache[b, i] = phi_v(...), rounded to io_dtype, exactly as
+ *   nsa_compress computes that block.
+ * Inputs: k_new [B,Hkv,dk], v_new [B,Hkv,dv] io_dtype; seq_lens device int32
+ *   [B] (read only: the caller advances it by one afterwards); phi_k, phi_v
+ *   (NSA_PHI_MLP only).
+ * In/out: k_cache [B,S,Hkv,dk], v_cache [B,S,Hkv,dv] (S = p->seqlen),
+ *   k_cmp_cache [B,cmp_cache_cap,Hkv,dk], v_cmp_cache [B,cmp_cache_cap,Hkv,dv]
+ *   with cmp_cache_cap >= Ncmp(S) (NSA_ERR_INVALID_ARG otherwise).
+ * A sequence whose L is outside [0, S-1] (full cache) is left untouched.
+ * No other cache row is written.  Workspace: NSA_OP_APPEND. */
+typedef struct nsa_append_args {
+  const void *k_new, *v_new;
+  const int32_t *seq_lens;
+  void *k_cache, *v_cache, *k_cmp_cache, *v_cmp_cache;
+  int32_t cmp_cache_cap;
+  nsa_phi_weights phi_k, phi_v;
+} nsa_append_args;
 
 /* Backward with the selected blocks held fixed (no gradient through the
  * scores or the selection).  Inputs as the prefill forward plus the forward's
@@ -190,6 +225,8 @@ nsa_status nsa_bwd(const nsa_params* p, const nsa_bwd_args* a, void* ws,
                    size_t ws_bytes, void* stream);
 nsa_status nsa_dense_fwd(const nsa_params* p, const nsa_dense_args* a, void* ws,
                          size_t ws_bytes, void* stream);
+nsa_status nsa_decode_append(const nsa_params* p, const nsa_append_args* a, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /* Timed variants, for measurement.  Identical work to the entry points
  * above; in addition hipEventRecord(events[i], stream) is issued before stage

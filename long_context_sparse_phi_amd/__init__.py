@@ -16,12 +16,12 @@ from typing import Dict, Optional
 import torch
 
 from . import _lib
-from ._lib import (NSA_BF16, NSA_FP32, NSA_OP_BWD, NSA_OP_COMPRESS, NSA_OP_DENSE, NSA_OP_FWD_DECODE,
-                   NSA_OP_FWD_PREFILL,
+from ._lib import (NSA_BF16, NSA_FP32, NSA_OP_APPEND, NSA_OP_BWD, NSA_OP_COMPRESS, NSA_OP_DENSE,
+                   NSA_OP_FWD_DECODE, NSA_OP_FWD_PREFILL,
                    NSA_PHI_MEANPOOL, NSA_PHI_MLP, NSAError)
 
 __all__ = ["Config", "workspace_size", "nsa_compress", "nsa_fwd_prefill", "nsa_fwd_decode",
-           "nsa_bwd", "nsa_dense_fwd", "load_library", "NSAError"]
+           "nsa_decode_append", "nsa_bwd", "nsa_dense_fwd", "load_library", "NSAError"]
 
 load_library = _lib.load
 
@@ -185,8 +185,11 @@ def nsa_fwd_prefill(cfg: Config, q, k, v, x, w_gate, phi_k=None, phi_v=None, *, 
 
 
 def nsa_fwd_decode(cfg: Config, q, k_cache, v_cache, k_cmp_cache, v_cmp_cache, x, w_gate, *,
-                   out=None, debug: bool = False, workspace: Optional[torch.Tensor] = None):
-    """One decode step; cfg.T is the cache length S (query at position S-1)."""
+                   out=None, debug: bool = False, seq_lens: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None):
+    """One decode step; cfg.T is the cache length S (query at position S-1).
+    With seq_lens (int32 [B] on the device), cfg.T is the cache capacity and
+    sequence b holds seq_lens[b] tokens, its query at position seq_lens[b]-1."""
     dev = q.device
     dt = cfg.torch_dtype
     B, S, Hq, Hkv = cfg.B, cfg.T, cfg.H_q, cfg.H_kv
@@ -213,6 +216,9 @@ def nsa_fwd_decode(cfg: Config, q, k_cache, v_cache, k_cmp_cache, v_cmp_cache, x
     for name in ("o", "idx", "p_slc", "lse", "o_branch"):
         t = res.get(name)
         setattr(a, name, t.data_ptr() if t is not None else None)
+    if seq_lens is not None:
+        _check(seq_lens, "seq_lens", (B,), torch.int32, dev)
+        a.seq_lens = seq_lens.data_ptr()
     ws = _workspace(cfg, NSA_OP_FWD_DECODE, dev, workspace)
     p = cfg.params()
     st = _lib.load().nsa_fwd_decode(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(), _stream(dev))
@@ -220,6 +226,39 @@ def nsa_fwd_decode(cfg: Config, q, k_cache, v_cache, k_cmp_cache, v_cmp_cache, x
         raise NSAError("nsa_fwd_decode", st)
     res["_workspace"] = ws
     return res
+
+
+def nsa_decode_append(cfg: Config, k_new, v_new, seq_lens, k_cache, v_cache, k_cmp_cache, v_cmp_cache,
+                      phi_k=None, phi_v=None, *, workspace: Optional[torch.Tensor] = None) -> None:
+    """Append one token per sequence at slot seq_lens[b] of the raw caches
+    (cfg.T = their capacity) and write the compressed block it completes, if
+    any.  seq_lens (int32 [B], device) is read only; advance it afterwards."""
+    dev = k_cache.device
+    dt = cfg.torch_dtype
+    B, S, Hkv = cfg.B, cfg.T, cfg.H_kv
+    _check(k_new, "k_new", (B, Hkv, cfg.d_k), dt, dev)
+    _check(v_new, "v_new", (B, Hkv, cfg.d_v), dt, dev)
+    _check(seq_lens, "seq_lens", (B,), torch.int32, dev)
+    _check(k_cache, "k_cache", (B, S, Hkv, cfg.d_k), dt, dev)
+    _check(v_cache, "v_cache", (B, S, Hkv, cfg.d_v), dt, dev)
+    cap = k_cmp_cache.shape[1]
+    _check(k_cmp_cache, "k_cmp_cache", (B, cap, Hkv, cfg.d_k), dt, dev)
+    _check(v_cmp_cache, "v_cmp_cache", (B, cap, Hkv, cfg.d_v), dt, dev)
+    a = _lib.nsa_append_args()
+    for name, t in (("k_new", k_new), ("v_new", v_new), ("seq_lens", seq_lens), ("k_cache", k_cache),
+                    ("v_cache", v_cache)):
+        setattr(a, name, t.data_ptr())
+    a.k_cmp_cache = k_cmp_cache.data_ptr() if k_cmp_cache.numel() else None
+    a.v_cmp_cache = v_cmp_cache.data_ptr() if v_cmp_cache.numel() else None
+    a.cmp_cache_cap = cap
+    a.phi_k = _phi_struct(cfg, phi_k, cfg.d_k, dev)
+    a.phi_v = _phi_struct(cfg, phi_v, cfg.d_v, dev)
+    ws = _workspace(cfg, NSA_OP_APPEND, dev, workspace)
+    p = cfg.params()
+    st = _lib.load().nsa_decode_append(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(),
+                                       _stream(dev))
+    if st != 0:
+        raise NSAError("nsa_decode_append", st)
 
 
 def nsa_bwd(cfg: Config, q, k, v, x, w_gate, phi_k, phi_v, saved: Dict[str, torch.Tensor], d_o, *,

@@ -14,8 +14,8 @@ LIB_PATH = os.path.join(_PKG, "libnsa.so")
 NSA_OK, NSA_ERR_INVALID_ARG, NSA_ERR_UNSUPPORTED, NSA_ERR_WORKSPACE, NSA_ERR_HIP, NSA_ERR_INTERNAL = range(6)
 NSA_BF16, NSA_FP32 = 0, 1
 NSA_PHI_MEANPOOL, NSA_PHI_MLP = 0, 1
-NSA_OP_FWD_PREFILL, NSA_OP_FWD_DECODE, NSA_OP_BWD, NSA_OP_COMPRESS, NSA_OP_DENSE = 0, 1, 2, 3, 4
-ABI_VERSION = 1
+NSA_OP_FWD_PREFILL, NSA_OP_FWD_DECODE, NSA_OP_BWD, NSA_OP_COMPRESS, NSA_OP_DENSE, NSA_OP_APPEND = range(6)
+ABI_VERSION = 2
 
 _vp = ctypes.c_void_p
 
@@ -44,7 +44,14 @@ class nsa_prefill_args(ctypes.Structure):
 class nsa_decode_args(ctypes.Structure):
     _fields_ = ([(n, _vp) for n in ("q", "k_cache", "v_cache", "k_cmp_cache", "v_cmp_cache", "x", "w_gate")] +
                 [("cmp_cache_cap", ctypes.c_int32)] +
-                [(n, _vp) for n in ("o", "idx", "p_slc", "lse", "o_branch")])
+                [(n, _vp) for n in ("o", "idx", "p_slc", "lse", "o_branch", "seq_lens")])
+
+
+class nsa_append_args(ctypes.Structure):
+    _fields_ = ([(n, _vp) for n in ("k_new", "v_new", "seq_lens", "k_cache", "v_cache",
+                                    "k_cmp_cache", "v_cmp_cache")] +
+                [("cmp_cache_cap", ctypes.c_int32)] +
+                [("phi_k", nsa_phi_weights), ("phi_v", nsa_phi_weights)])
 
 
 class nsa_bwd_args(ctypes.Structure):
@@ -60,7 +67,8 @@ class nsa_dense_args(ctypes.Structure):
 
 
 EXPORTS = ("nsa_abi_version", "nsa_status_str", "nsa_workspace_size", "nsa_compress",
-           "nsa_fwd_prefill", "nsa_fwd_decode", "nsa_bwd", "nsa_dense_fwd")
+           "nsa_fwd_prefill", "nsa_fwd_decode", "nsa_bwd", "nsa_dense_fwd",
+           "nsa_decode_append")
 
 _LIB = None
 
@@ -85,7 +93,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.nsa_compress.argtypes = [P(nsa_params), ctypes.c_int, _vp, P(nsa_phi_weights), _vp, _vp,
                                  ctypes.c_size_t, _vp]
     for name, argt in (("nsa_fwd_prefill", nsa_prefill_args), ("nsa_fwd_decode", nsa_decode_args),
-                       ("nsa_bwd", nsa_bwd_args), ("nsa_dense_fwd", nsa_dense_args)):
+                       ("nsa_bwd", nsa_bwd_args), ("nsa_dense_fwd", nsa_dense_args),
+                       ("nsa_decode_append", nsa_append_args)):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [P(nsa_params), P(argt), _vp, ctypes.c_size_t, _vp]

@@ -201,6 +201,7 @@ nsa_status nsa_workspace_size(const nsa_params* p, nsa_op op, size_t* bytes) {
       case NSA_OP_BWD: *bytes = bwd_ws_bytes(dm); return NSA_OK;
       case NSA_OP_COMPRESS: *bytes = phi_ws(dm) > 0 ? phi_ws(dm) : 256; return NSA_OK;
       case NSA_OP_DENSE: *bytes = dense_ws_bytes(dm); return NSA_OK;
+      case NSA_OP_APPEND: *bytes = append_ws_bytes(dm) > 0 ? append_ws_bytes(dm) : 256; return NSA_OK;
     }
     return NSA_ERR_INVALID_ARG;
   } catch (...) {
@@ -321,6 +322,35 @@ nsa_status nsa_dense_fwd(const nsa_params* p, const nsa_dense_args* a, void* ws,
     wa.q = a->q; wa.k = a->k; wa.vt = ws; wa.o = a->o; wa.lse = (float*)a->lse; wa.dense = 1;
     if (launch_win_combine(dm, wa, s) != hipSuccess) return NSA_ERR_HIP;
     return NSA_OK;
+  } catch (...) {
+    return NSA_ERR_INTERNAL;
+  }
+}
+
+nsa_status nsa_decode_append(const nsa_params* p, const nsa_append_args* a, void* ws, size_t ws_bytes,
+                             void* stream) {
+  try {
+    Dims dm;
+    nsa_status st = make_dims(p, &dm);
+    if (st != NSA_OK) return st;
+    if (!a) return NSA_ERR_INVALID_ARG;
+    const void* req[] = {a->k_new, a->v_new, a->seq_lens, a->k_cache, a->v_cache};
+    for (const void* r : req)
+      if (!r || !aligned16(r)) return NSA_ERR_INVALID_ARG;
+    if (dm.ncmp > 0 && (!a->k_cmp_cache || !a->v_cmp_cache || !aligned16(a->k_cmp_cache) ||
+                        !aligned16(a->v_cmp_cache) || a->cmp_cache_cap < dm.ncmp))
+      return NSA_ERR_INVALID_ARG;
+    if (dm.hidden && (!phi_ok(a->phi_k) || !phi_ok(a->phi_v))) return NSA_ERR_INVALID_ARG;
+    const size_t need = append_ws_bytes(dm);
+    if (ws_bytes < need || (need && !ws) || !aligned16(ws)) return NSA_ERR_WORKSPACE;
+    if ((st = check_device()) != NSA_OK) return st;
+    AppendArgs aa;
+    aa.lens = a->seq_lens; aa.kn = a->k_new; aa.vn = a->v_new; aa.kc = a->k_cache; aa.vc = a->v_cache;
+    aa.kcmp = a->k_cmp_cache; aa.vcmp = a->v_cmp_cache; aa.cap = a->cmp_cache_cap;
+    aa.phi_k = {a->phi_k.pe, a->phi_k.w1, a->phi_k.b1, a->phi_k.w2, a->phi_k.b2};
+    aa.phi_v = {a->phi_v.pe, a->phi_v.w1, a->phi_v.b1, a->phi_v.w2, a->phi_v.b2};
+    aa.h = (float*)ws;
+    return hip_status(launch_append(dm, aa, (hipStream_t)stream));
   } catch (...) {
     return NSA_ERR_INTERNAL;
   }

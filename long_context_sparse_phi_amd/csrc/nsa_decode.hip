@@ -35,6 +35,8 @@ constexpr int kDecWinChunk = 64;
 // tiles in flight per wave (one wave per SIMD; the ring takes most registers)
 template <int DK, int DV> constexpr int dec_depth() { return DK + DV >= 320 ? 3 : 4; }
 
+// Launch plan for the cache capacity S (grid sizes, workspace layout); every
+// sequence then works within its own length (DecSeq).
 struct DecPlan {
   int S, t, ncmp, nc, nb, jstep, nis, niw, ni, wlen, ws0;
 };
@@ -107,8 +109,28 @@ struct DecArgs {
   float* p_slc;       // optional [B,Hkv,nsel]
   float* lse;         // optional [3,B,Hq]
   void* o_branch;     // optional [3,B,Hq,dv]
+  const int* lens;    // optional [B] tokens per sequence (NULL: S each)
   DecBufs w;
 };
+
+// Extent of sequence b: S tokens (clamped into [1, capacity]), query at t,
+// ncmp complete compressed blocks, nsel selection blocks, the window's first
+// token ws0 and its 64-token chunk count niw.
+struct DecSeq {
+  int S, t, ncmp, nsel, ws0, niw;
+};
+
+__device__ __forceinline__ DecSeq dec_seq(const Dims& dm, const DecArgs& a, int b) {
+  DecSeq q;
+  q.S = a.lens ? min(max(a.lens[b], 1), dm.T) : dm.T;
+  q.t = q.S - 1;
+  q.ncmp = q.S < dm.l ? 0 : (q.S - dm.l) / dm.d + 1;
+  q.nsel = (q.S + dm.ls - 1) / dm.ls;
+  const int wlen = min(dm.w, q.S);
+  q.ws0 = q.S - wlen;
+  q.niw = (wlen + kDecWinChunk - 1) / kDecWinChunk;
+  return q;
+}
 
 // 32-key tile of one KV head: global -> registers (gload, one tile ahead of
 // the compute) -> LDS (lstore).  Keys: 32 rows x DK, chunks swizzled by
@@ -185,8 +207,9 @@ __global__ __launch_bounds__(64, 1) void k_dec_cmp(Dims dm, DecArgs a, DecPlan p
   const int lane = threadIdx.x, c16 = lane & 15, qd = lane >> 4;
   const int c = blockIdx.x % pl.nc, bg = blockIdx.x / pl.nc;
   const int b = bg / dm.Hkv, g = bg % dm.Hkv;
-  const int k0 = c * kDecCK, k1 = min(k0 + kDecCK, pl.ncmp);
-  const int ntile = (k1 - k0 + 31) / 32;
+  const int ncmp = dec_seq(dm, a, b).ncmp;
+  const int k0 = c * kDecCK, k1 = min(k0 + kDecCK, ncmp);
+  const int ntile = k1 > k0 ? (k1 - k0 + 31) / 32 : 0;
   const bool cv = c16 < dm.G;
   Frag8<T> qf[DK / 32];
   {
@@ -260,13 +283,13 @@ __global__ __launch_bounds__(64, 1) void k_dec_cmp(Dims dm, DecArgs a, DecPlan p
     __syncthreads();
     cur.lstore(tile, lane);
     __syncthreads();
-    if (i + DEPTH < ntile) cur.gload(kbase, vbase, kstride, vstride, k0 + 32 * (i + DEPTH), pl.ncmp, lane);
+    if (i + DEPTH < ntile) cur.gload(kbase, vbase, kstride, vstride, k0 + 32 * (i + DEPTH), ncmp, lane);
     compute(i);
   };
   Tile ring[DEPTH];
 #pragma unroll
   for (int r = 0; r < DEPTH; ++r)
-    if (r < ntile) ring[r].gload(kbase, vbase, kstride, vstride, k0 + 32 * r, pl.ncmp, lane);
+    if (r < ntile) ring[r].gload(kbase, vbase, kstride, vstride, k0 + 32 * r, ncmp, lane);
   for (int i = 0; i < ntile; i += DEPTH) {
 #pragma unroll
     for (int r = 0; r < DEPTH; ++r)
@@ -303,6 +326,7 @@ __global__ __launch_bounds__(1024) void k_dec_combine(Dims dm, DecArgs a, DecPla
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bg = blockIdx.x, b = bg / dm.Hkv, g = bg % dm.Hkv;
   const int G = dm.G;
+  const DecSeq sq = dec_seq(dm, a, b);
   // gate inputs of head `wave`, requested now and used at the end
   float gx[4], gw[4][3];
   auto gate_load = [&](int k0) {
@@ -349,12 +373,12 @@ __global__ __launch_bounds__(1024) void k_dec_combine(Dims dm, DecArgs a, DecPla
   }
   __syncthreads();
   // block scores: sum over heads of exact probabilities remapped to blocks
-  const int ntiles = (pl.ncmp + 31) / 32;
+  const int ntiles = (sq.ncmp + 31) / 32;
   for (int j = tid; j < dm.nsel; j += 1024) {
     float val = 0.f;
     int klo = j - pl.nb + 1;
     klo = klo <= 0 ? 0 : (klo + pl.jstep - 1) / pl.jstep;
-    const int khi = min(j / pl.jstep, ntiles - 1);
+    const int khi = j < sq.nsel ? min(j / pl.jstep, ntiles - 1) : -1;
     // at most a few tiles touch a block; all their loads are issued together
     for (int kb = klo; kb <= khi; kb += 2) {
       float x[2][16], mt[2][16];
@@ -385,7 +409,7 @@ __global__ __launch_bounds__(1024) void k_dec_combine(Dims dm, DecArgs a, DecPla
   if (a.p_slc)
     for (int j = tid; j < dm.nsel; j += 1024) a.p_slc[(size_t)bg * dm.nsel + j] = row[j];
   __syncthreads();
-  block_topn<16>(row, pl.t, dm.ls, dm.n, a.w.idx + (size_t)bg * dm.n, fs, fj, tid);
+  block_topn<16>(row, sq.t, dm.ls, dm.n, a.w.idx + (size_t)bg * dm.n, fs, fj, tid);
   // gates of the group's heads: wave h, lanes over the gate input, the three
   // branches together; the first 256 inputs were loaded at the start
   if (wave < G) {
@@ -425,13 +449,14 @@ __global__ __launch_bounds__(64) void k_dec_sw(Dims dm, DecArgs a, DecPlan pl) {
     for (int ks = 0; ks < DK / 32; ++ks) qf[ks] = cv ? load_frag(qp + ks * 32) : zero_frag<T>();
   }
   // key range of this work item: one selected block or one window chunk
+  const DecSeq sq = dec_seq(dm, a, b);
   int r0 = 0, r1 = 0;
   if (it < pl.nis) {
     const int j = it < dm.n ? a.w.idx[(size_t)bg * dm.n + it] : -1;
-    if (j >= 0) { r0 = j * dm.ls; r1 = min((j + 1) * dm.ls, pl.S); }
-  } else {
-    r0 = pl.ws0 + (it - pl.nis) * kDecWinChunk;
-    r1 = min(r0 + kDecWinChunk, pl.S);
+    if (j >= 0) { r0 = j * dm.ls; r1 = min((j + 1) * dm.ls, sq.S); }
+  } else if (it - pl.nis < sq.niw) {
+    r0 = sq.ws0 + (it - pl.nis) * kDecWinChunk;
+    r1 = min(r0 + kDecWinChunk, sq.S);
   }
   const int kt0 = r0 & ~31;
   const int ntile = r1 > r0 ? (r1 - kt0 + 31) / 32 : 0;
@@ -478,13 +503,13 @@ __global__ __launch_bounds__(64) void k_dec_sw(Dims dm, DecArgs a, DecPlan pl) {
     __syncthreads();
     cur.lstore(tile, lane);
     __syncthreads();
-    if (i + 2 < ntile) cur.gload(kbase, vbase, kstride, vstride, kt0 + 32 * (i + 2), pl.S, lane);
+    if (i + 2 < ntile) cur.gload(kbase, vbase, kstride, vstride, kt0 + 32 * (i + 2), sq.S, lane);
     compute(i);
   };
   Tile ring[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r)
-    if (r < ntile) ring[r].gload(kbase, vbase, kstride, vstride, kt0 + 32 * r, pl.S, lane);
+    if (r < ntile) ring[r].gload(kbase, vbase, kstride, vstride, kt0 + 32 * r, sq.S, lane);
   for (int i = 0; i < ntile; i += 2) {
 #pragma unroll
     for (int r = 0; r < 2; ++r)
@@ -614,6 +639,7 @@ hipError_t launch_decode(const Dims& dm, const nsa_decode_args* args, void* ws, 
   a.kc = args->k_cmp_cache; a.vc = args->v_cmp_cache; a.cap = args->cmp_cache_cap;
   a.x = args->x; a.wg = args->w_gate; a.o = args->o;
   a.p_slc = (float*)args->p_slc; a.lse = (float*)args->lse; a.o_branch = args->o_branch;
+  a.lens = args->seq_lens;
   dec_carve(dm, ws, &a.w);
   if (args->idx) a.w.idx = (int*)args->idx;
   const DecPlan pl = dec_plan(dm);

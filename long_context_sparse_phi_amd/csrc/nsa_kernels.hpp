@@ -115,6 +115,23 @@ struct WinArgs {
 };
 hipError_t launch_win_combine(const Dims& dm, const WinArgs& a, hipStream_t s);
 
+// Decode-time cache maintenance (nsa_append.hip).  dm.T is the raw cache
+// capacity; lens[b] the tokens sequence b held before the call.
+struct AppendPhi {
+  const void *pe, *w1, *b1, *w2, *b2;
+};
+struct AppendArgs {
+  const int* lens;         // [B]
+  const void *kn, *vn;     // [B,Hkv,dk], [B,Hkv,dv]
+  void *kc, *vc;           // [B,T,Hkv,dk], [B,T,Hkv,dv]
+  void *kcmp, *vcmp;       // [B,cap,Hkv,dk], [B,cap,Hkv,dv]
+  int cap;
+  AppendPhi phi_k, phi_v;
+  float* h;                // workspace [B*Hkv, hidden]
+};
+hipError_t launch_append(const Dims& dm, const AppendArgs& a, hipStream_t s);
+size_t append_ws_bytes(const Dims& dm);
+
 bool shapes_supported(int dk, int dv);
 
 }  // namespace nsa

@@ -42,7 +42,7 @@ from scipy.special import erf
 __all__ = [
     "Params", "gate", "compress", "remap_matrix", "attend", "n_cmp_visible",
     "candidate_blocks", "forced_blocks", "top_n", "is_near_tie", "forward",
-    "decode", "backward", "dq_rows", "dense_causal", "round_io", "gelu", "gelu_grad", "sigmoid",
+    "decode", "append_token", "backward", "dq_rows", "dense_causal", "round_io", "gelu", "gelu_grad", "sigmoid",
     "cmp_keys", "slc_keys", "win_keys", "decode_token_count",
 ]
 
@@ -384,7 +384,7 @@ def forward(p: Params, q, k, v, x, w_gate, phi_k=None, phi_v=None, rows=None,
 
 
 def decode(p: Params, q, k_cache, v_cache, kc_cache, vc_cache, x, w_gate,
-           tie_scores=None) -> Dict[str, np.ndarray]:
+           tie_scores=None, seq_lens=None) -> Dict[str, np.ndarray]:
     """One decode step: the query token sits at position S-1 of a length-S cache,
     its own key/value already stored there; compressed blocks come from the
     given compressed cache (complete blocks only), not from phi.
@@ -392,11 +392,13 @@ def decode(p: Params, q, k_cache, v_cache, kc_cache, vc_cache, x, w_gate,
     q [B,Hq,dk], k_cache [B,S,Hkv,dk], v_cache [B,S,Hkv,dv], kc_cache [B,>=N,Hkv,dk],
     vc_cache [B,>=N,Hkv,dv], x [B,C].  Returns o [B,Hq,dv], o_branch [3,B,Hq,dv],
     lse [3,B,Hq], p_slc [B,Hkv,N_sel], idx [B,Hkv,n], retied [B,Hkv].
+    seq_lens [B] (optional): sequence b holds only its first seq_lens[b] cache
+    rows, and its query sits at seq_lens[b]-1; p_slc keeps the width of the full
+    cache, zero beyond the sequence's own blocks.
     """
     B, S = k_cache.shape[:2]
     Hq, dv = q.shape[1], v_cache.shape[3]
     Hkv = k_cache.shape[2]
-    t = S - 1
     n_sel = -(-S // p.l_sel)
     g_all = gate(x[:, None], w_gate)[:, 0]
     out = {"o": np.zeros((B, Hq, dv)), "o_branch": np.zeros((3, B, Hq, dv)),
@@ -404,12 +406,43 @@ def decode(p: Params, q, k_cache, v_cache, kc_cache, vc_cache, x, w_gate,
            "idx": np.full((B, Hkv, p.n), -1, dtype=np.int64),
            "retied": np.zeros((B, Hkv), dtype=bool), "gates": g_all}
     for b in range(B):
+        Sb = S if seq_lens is None else int(seq_lens[b])
+        nb = -(-Sb // p.l_sel)
         ts = None if tie_scores is None else tie_scores[b]
-        o, o_br, lse, ps, sets, ret = _row(p, t, q[b], k_cache[b], v_cache[b], kc_cache[b],
-                                           vc_cache[b], g_all[b], n_sel, None, ts)
+        o, o_br, lse, ps, sets, ret = _row(p, Sb - 1, q[b], k_cache[b, :Sb], v_cache[b, :Sb], kc_cache[b],
+                                           vc_cache[b], g_all[b], nb, None, ts)
         out["o"][b], out["o_branch"][:, b], out["lse"][:, b] = o, o_br, lse
-        out["p_slc"][b], out["idx"][b], out["retied"][b] = ps, _sets_to_idx(sets, p.n), ret
+        out["p_slc"][b, :, :nb], out["idx"][b], out["retied"][b] = ps, _sets_to_idx(sets, p.n), ret
     return out
+
+
+def append_token(p: Params, k_cache, v_cache, kc_cache, vc_cache, k_new, v_new, seq_lens,
+                 phi_k=None, phi_v=None):
+    """Decode-time cache maintenance [YLY 令牌压缩: block i covers tokens
+    i*d .. i*d+l-1 and exists once its last token does].
+
+    For every sequence b with L = seq_lens[b] < capacity: the new token's key and
+    value go to cache row L; if that token completes block i (L+1 >= l and
+    (L+1-l) % d == 0, i = (L+1-l)/d), row i of the compressed caches becomes
+    phi of that block, computed by compress() on the block's l tokens.
+    Returns updated copies of the four caches; seq_lens is not advanced.
+    """
+    k_cache, v_cache = k_cache.copy(), v_cache.copy()
+    kc_cache, vc_cache = kc_cache.copy(), vc_cache.copy()
+    S = k_cache.shape[1]
+    for b in range(k_cache.shape[0]):
+        L = int(seq_lens[b])
+        if not 0 <= L < S:
+            continue
+        k_cache[b, L], v_cache[b, L] = k_new[b], v_new[b]
+        n = L + 1 - p.l
+        if n < 0 or n % p.d:
+            continue
+        i = n // p.d
+        blk = slice(i * p.d, i * p.d + p.l)
+        kc_cache[b, i] = compress(k_cache[b:b + 1, blk], phi_k, p)[0, 0]
+        vc_cache[b, i] = compress(v_cache[b:b + 1, blk], phi_v, p)[0, 0]
+    return k_cache, v_cache, kc_cache, vc_cache
 
 
 # ---------------------------------------------------------------------------

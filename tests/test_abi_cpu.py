@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_abi_version_and_status_strings(lib):
     lib.nsa_abi_version.restype = ctypes.c_int
-    assert lib.nsa_abi_version() == 1
+    assert lib.nsa_abi_version() == 2
     lib.nsa_status_str.restype = ctypes.c_char_p
     lib.nsa_status_str.argtypes = [ctypes.c_int]
     assert lib.nsa_status_str(0) == b"ok"

@@ -393,6 +393,67 @@ def test_decode_equals_prefill_last_row():
         np.testing.assert_array_equal(dec["idx"], full["idx"][:, 0])
 
 
+def test_decode_seq_lens_equals_prefill_rows_of_each_prefix():
+    # sequence b holds only its first S_b tokens: its decode row must be the
+    # prefill forward's row S_b-1 over that prefix alone; rows beyond it are
+    # NaN and must never be read
+    S, lens = 150, [150, 61, 9]
+    p, inp = small_problem(B=3, T=S, phi="mlp", seed=21)
+    kc = O.compress(inp["k"], inp["phi_k"], p)
+    vc = O.compress(inp["v"], inp["phi_v"], p)
+    kcache, vcache = inp["k"].copy(), inp["v"].copy()
+    q = np.stack([inp["q"][b, L - 1] for b, L in enumerate(lens)])
+    x = np.stack([inp["x"][b, L - 1] for b, L in enumerate(lens)])
+    for b, L in enumerate(lens):
+        kcache[b, L:] = vcache[b, L:] = np.nan
+        kc[b, O.n_cmp_visible(L - 1, p.l, p.d):] = np.nan
+        vc[b, O.n_cmp_visible(L - 1, p.l, p.d):] = np.nan
+    dec = O.decode(p, q, kcache, vcache, kc, vc, x, inp["w_gate"], seq_lens=lens)
+    for b, L in enumerate(lens):
+        sub = {k: (v[b:b + 1, :L] if k in ("q", "k", "v", "x") else v) for k, v in inp.items()}
+        full = O.forward(p, **sub, rows=[L - 1])
+        np.testing.assert_allclose(dec["o"][b], full["o"][0, 0], rtol=1e-13, atol=1e-13)
+        np.testing.assert_array_equal(dec["idx"][b], full["idx"][0, 0])
+        nb = -(-L // p.l_sel)
+        np.testing.assert_allclose(dec["p_slc"][b, :, :nb], full["p_slc"][0, 0], rtol=1e-13, atol=1e-15)
+        assert not dec["p_slc"][b, :, nb:].any()
+
+
+@pytest.mark.parametrize("phi", ["mean", "mlp"])
+def test_append_token_maintains_the_one_shot_compression(phi):
+    # appending tokens one at a time from ragged starting lengths must rebuild
+    # exactly the compressed cache that compress() gives for the whole sequence
+    S, B = 64, 3
+    p, inp = small_problem(B=B, T=S, phi=phi, seed=5)
+    k, v = inp["k"], inp["v"]
+    ncap = O.n_cmp_visible(S - 1, p.l, p.d)
+    kcache, vcache = np.full_like(k, np.nan), np.full_like(v, np.nan)
+    kc = np.full((B, ncap) + k.shape[2:], np.nan)
+    vc = np.full((B, ncap) + v.shape[2:], np.nan)
+    lens = np.array([0, 13, 61])
+    for b, L in enumerate(lens):
+        kcache[b, :L], vcache[b, :L] = k[b, :L], v[b, :L]
+        n = O.n_cmp_visible(L - 1, p.l, p.d)
+        if n:
+            kc[b, :n] = O.compress(k[b:b + 1, :L], inp["phi_k"], p)[0]
+            vc[b, :n] = O.compress(v[b:b + 1, :L], inp["phi_v"], p)[0]
+    for _ in range(S + 2):   # the last sequences reach the capacity and stay there
+        kn = np.stack([k[b, min(L, S - 1)] for b, L in enumerate(lens)])
+        vn = np.stack([v[b, min(L, S - 1)] for b, L in enumerate(lens)])
+        before = kc.copy()
+        kcache, vcache, kc, vc = O.append_token(p, kcache, vcache, kc, vc, kn, vn, lens,
+                                                inp["phi_k"], inp["phi_v"])
+        for b, L in enumerate(lens):
+            done = L < S and L + 1 >= p.l and (L + 1 - p.l) % p.d == 0
+            changed = ~np.all((kc[b] == before[b]) | (np.isnan(kc[b]) & np.isnan(before[b])), axis=(1, 2))
+            assert changed.sum() == (1 if done else 0)
+        lens = np.minimum(lens + 1, S)
+    np.testing.assert_array_equal(kcache, k)
+    np.testing.assert_array_equal(vcache, v)
+    np.testing.assert_allclose(kc, O.compress(k, inp["phi_k"], p), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(vc, O.compress(v, inp["phi_v"], p), rtol=1e-12, atol=1e-12)
+
+
 def test_decode_token_model_reproduces_pages():
     with open(os.path.join(GOLDEN, "decode_token_model.json")) as f:
         g = json.load(f)
