@@ -369,6 +369,7 @@ def run_decode(steps, warmup, wname="decode_64k"):
     stage_ms = [sum(ev.elapsed_ms(events[i][s], events[i][s + 1]) for i in range(steps)) / steps
                 for s in range(nst)]
     step_ms = sum(ev.elapsed_ms(events[i][0], events[i][nst]) for i in range(steps)) / steps
+    append = run_append(w, cfg, d, kc, vc)
     nbytes = decode_bytes(w, idx)
     ncmp = (w.T - w.l) // w.d + 1
     cmp_bytes = w.B * w.H_kv * ncmp * (w.d_k + w.d_v) * 2 + w.B * w.H_q * w.d_k * 2
@@ -384,7 +385,60 @@ def run_decode(steps, warmup, wname="decode_64k"):
                      "traffic": traffic_for("k_dec_cmp"),
                      "algorithmic_bytes_per_launch": cmp_bytes, "launch_us": round(stage_ms[0] * 1e3, 2)},
         "cold_cache": "512 MB buffer written then read before every step (outside the timed events)",
+        "append": append,
     }
+
+
+def run_append(w, cfg, d, kc, vc, reps=3):
+    """Decode-time cache maintenance: one nsa_decode_append per step appends a
+    token to every sequence; over d = 16 consecutive steps exactly one (here the
+    first) completes a compression block in every sequence and runs phi.  Each
+    call is timed alone with HIP events; the lengths are set so the appended
+    rows rewrite the cache's own last rows (the caches keep their contents)."""
+    import torch
+    from long_context_sparse_phi_amd import _lib
+    dev = torch.device("cuda:0")
+    lib = _lib.load()
+    p = cfg.params()
+    lens = torch.empty(w.B, dtype=torch.int32, device=dev)
+    start = w.T - 1 - w.d
+    kn = [d["k_cache"][:, start + i].contiguous() for i in range(w.d)]
+    vn = [d["v_cache"][:, start + i].contiguous() for i in range(w.d)]
+    a = _lib.nsa_append_args()
+    a.seq_lens = lens.data_ptr()
+    a.k_cache, a.v_cache = d["k_cache"].data_ptr(), d["v_cache"].data_ptr()
+    a.k_cmp_cache, a.v_cmp_cache, a.cmp_cache_cap = kc.data_ptr(), vc.data_ptr(), kc.shape[1]
+    for name, ph in (("phi_k", d["phi_k"]), ("phi_v", d["phi_v"])):
+        st = getattr(a, name)
+        for f in ("pe", "w1", "b1", "w2", "b2"):
+            if f in ph:
+                setattr(st, f, ph[f].data_ptr())
+    ws = torch.empty(max(256, nsa_ws(cfg, _lib.NSA_OP_APPEND)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    times = [[] for _ in range(w.d)]
+    for r in range(reps + 1):
+        lens.fill_(start)
+        for i in range(w.d):
+            a.k_new, a.v_new = kn[i].data_ptr(), vn[i].data_ptr()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            st = lib.nsa_decode_append(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(), stream)
+            e1.record()
+            if st != 0:
+                raise RuntimeError(f"nsa_decode_append failed: {_lib.status_str(st)}")
+            lens.add_(1)
+            if r > 0:
+                times[i].append((e0, e1))
+    torch.cuda.synchronize()
+    us = [sum(x.elapsed_time(y) for x, y in t) / len(t) * 1e3 for t in times]
+    return {"calls_per_stride": w.d, "us_block_completing": round(us[0], 2),
+            "us_other_mean": round(sum(us[1:]) / (len(us) - 1), 2),
+            "us_mean_per_token": round(sum(us) / len(us), 2)}
+
+
+def nsa_ws(cfg, op):
+    import long_context_sparse_phi_amd as nsa
+    return nsa.workspace_size(cfg, op)
 
 
 # ---------------------------------------------------------------- backward leg
@@ -420,7 +474,7 @@ def run_backward(steps, warmup, wname="train_16k"):
     for name in ("q", "k", "v", "x", "w_gate"):
         setattr(a, name, d[name].data_ptr())
     a.d_o = d_o.data_ptr()
-    for name in ("k_cmp", "v_cmp", "lse", "idx"):
+    for name in ("k_cmp", "v_cmp", "lse", "idx", "o_branch"):
         setattr(a, name, fwd[name].data_ptr())
     a.phi_k = nsa._phi_struct(cfg, d["phi_k"], w.d_k, dev)
     a.phi_v = nsa._phi_struct(cfg, d["phi_v"], w.d_v, dev)
@@ -455,6 +509,18 @@ def run_backward(steps, warmup, wname="train_16k"):
     wall = time.perf_counter() - t0
     stage_ms = [sum(ev.elapsed_ms(events[i][s], events[i][s + 1]) for i in range(steps)) / steps
                 for s in range(nst)]
+    # the training-mode forward that saves the fp32 branch outputs (and with
+    # them the softmax row terms) for this backward
+    fwd_ms = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        nsa.nsa_fwd_prefill(cfg, d["q"], d["k"], d["v"], d["x"], d["w_gate"], d["phi_k"], d["phi_v"],
+                            save_for_backward=True, workspace=fwd["_workspace"])
+        e1.record()
+        fwd_ms.append((e0, e1))
+    torch.cuda.synchronize()
+    fwd_ms = sum(x.elapsed_time(y) for x, y in fwd_ms) / steps
     fl = useful_flops(w)
     useful = 2 * (fl["cmp"] + fl["slc"] + fl["win"]) + 2 * fl["phi"] + fl["gate"]
     ms = wall * 1e3 / steps
@@ -462,7 +528,9 @@ def run_backward(steps, warmup, wname="train_16k"):
             "useful_tflop_per_step": round(useful / 1e12, 4),
             "tflops": round(useful / (ms * 1e-3) / 1e12, 2),
             "mfma_frac_useful": round(useful / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "stages_ms": {n: round(x, 4) for n, x in zip(BWD_STAGES, stage_ms)}}
+            "stages_ms": {n: round(x, 4) for n, x in zip(BWD_STAGES, stage_ms)},
+            "row_terms": "read from the forward's saved fp32 branch outputs",
+            "training_forward_ms": round(fwd_ms, 4)}
 
 
 # ---------------------------------------------------------------- dense baseline
@@ -492,6 +560,7 @@ def run_dense_comparison(lengths=(8192, 16384, 32768, 65536), wname="prefill_64k
         def timed(fn):
             fn()
             torch.cuda.synchronize()
+            a.k_new, a.v_new = kn[i].data_ptr(), vn[i].data_ptr()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             for _ in range(reps):

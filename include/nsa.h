@@ -107,12 +107,18 @@ typedef struct nsa_phi_weights {
  *   idx [B,T,Hkv,n] int32 selected blocks, ascending, -1 padded;
  *   o_branch [3,B,T,Hq,dv] fp32 per-branch outputs;
  *   p_slc [B,T,Hkv,Nsel] fp32 group importance scores, Nsel = ceil(T/l');
- *   gates [B,T,Hq,3] fp32. */
+ *   gates [B,T,Hq,3] fp32.
+ * Independent keys/values per branch (youleyou page, 滑动窗口: each branch
+ * gets its own keys and values so that their gradients do not interfere):
+ *   k_slc, v_slc [B,T,Hkv,dk|dv] for the selected branch and k_win, v_win for
+ *   the window branch, all four set or all NULL.  When set, k and v feed the
+ *   compressed branch (phi) only.  NULL: one k, v for all three branches. */
 typedef struct nsa_prefill_args {
   const void *q, *k, *v, *x, *w_gate;
   nsa_phi_weights phi_k, phi_v;
   void *o;
   void *k_cmp, *v_cmp, *lse, *idx, *o_branch, *p_slc, *gates;
+  const void *k_slc, *v_slc, *k_win, *v_win;
 } nsa_prefill_args;
 
 /* One decode step per sequence; the new token's key/value are already stored
@@ -132,13 +138,17 @@ typedef struct nsa_prefill_args {
  * Output: o [B,Hq,dv] io_dtype.
  * Optional: idx [B,Hkv,n] int32, p_slc [B,Hkv,Nsel(S)] fp32 (columns at or
  *   beyond Nsel(S_b) = ceil(S_b/l') are written as 0), lse [3,B,Hq] fp32,
- *   o_branch [3,B,Hq,dv] fp32. */
+ *   o_branch [3,B,Hq,dv] fp32.
+ * k_win_cache, v_win_cache: the window branch's own caches [B,S,Hkv,dk|dv]
+ *   when each branch has independent keys/values (both set or both NULL);
+ *   k_cache, v_cache then serve the selected branch only. */
 typedef struct nsa_decode_args {
   const void *q, *k_cache, *v_cache, *k_cmp_cache, *v_cmp_cache, *x, *w_gate;
   int32_t cmp_cache_cap;
   void *o;
   void *idx, *p_slc, *lse, *o_branch;
   const int32_t *seq_lens;
+  const void *k_win_cache, *v_win_cache;
 } nsa_decode_args;
 
 /* Decode-time cache maintenance: append one token per sequence to the raw
@@ -169,11 +179,18 @@ typedef struct nsa_append_args {
 /* Backward with the selected blocks held fixed (no gradient through the
  * scores or the selection).  Inputs as the prefill forward plus the forward's
  * saved k_cmp, v_cmp, lse, idx and the upstream gradient d_o [B,T,Hq,dv]
- * (io_dtype).  o_branch is not read (may be NULL): <dO, O_c> is recomputed
- * from the probabilities.
+ * (io_dtype).  o_branch (optional): the forward's fp32 branch outputs
+ * [3,B,T,Hq,dv]; when given, the row terms <dO, O_c> of the softmax backward
+ * are read from it (one pass over 3*B*T*Hq*dv floats), otherwise they are
+ * recomputed from the probabilities (a second pass over every key).
  * Outputs (fp32, overwritten): dq [B,T,Hq,dk], dk [B,T,Hkv,dk],
  *   dv [B,T,Hkv,dv], dw_gate [C,Hq,3]; for NSA_PHI_MLP also d_phi_k and
- *   d_phi_v laid out like the phi weights (pe, w1, b1, w2, b2) in fp32. */
+ *   d_phi_v laid out like the phi weights (pe, w1, b1, w2, b2) in fp32.
+ * Independent keys/values per branch: with k_slc, v_slc, k_win, v_win set
+ *   (as in the forward), dk_slc, dv_slc, dk_win, dv_win [B,T,Hkv,dk|dv] fp32
+ *   are required and receive those tensors' gradients, and dk, dv hold only
+ *   the gradient through the compressed branch (phi).  Without them dk, dv
+ *   are the sum over the three branches. */
 typedef struct nsa_phi_grads {
   void *pe, *w1, *b1, *w2, *b2;
 } nsa_phi_grads;
@@ -184,6 +201,8 @@ typedef struct nsa_bwd_args {
   const void *k_cmp, *v_cmp, *lse, *idx, *o_branch, *d_o;
   void *dq, *dk, *dv, *dw_gate;
   nsa_phi_grads d_phi_k, d_phi_v;
+  const void *k_slc, *v_slc, *k_win, *v_win;
+  void *dk_slc, *dv_slc, *dk_win, *dv_win;
 } nsa_bwd_args;
 
 /* Dense causal attention, the baseline the pages measure NSA against

@@ -143,11 +143,24 @@ def nsa_compress(cfg: Config, x: torch.Tensor, phi: Optional[Dict[str, torch.Ten
     return out
 
 
+def _branch_kv(cfg: Config, kv, tag: str, dev):
+    """Pointers of a branch's own (k, v) pair, or (None, None)."""
+    if kv is None:
+        return None, None
+    k, v = kv
+    _check(k, f"k_{tag}", (cfg.B, cfg.T, cfg.H_kv, cfg.d_k), cfg.torch_dtype, dev)
+    _check(v, f"v_{tag}", (cfg.B, cfg.T, cfg.H_kv, cfg.d_v), cfg.torch_dtype, dev)
+    return k.data_ptr(), v.data_ptr()
+
+
 def nsa_fwd_prefill(cfg: Config, q, k, v, x, w_gate, phi_k=None, phi_v=None, *, out=None,
-                    save_for_backward: bool = False, debug: bool = False,
+                    save_for_backward: bool = False, debug: bool = False, kv_slc=None, kv_win=None,
                     workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
     """NSA prefill forward.  Returns {"o": ...} plus, when save_for_backward,
-    k_cmp, v_cmp, lse, idx, o_branch, and, when debug, also p_slc and gates."""
+    k_cmp, v_cmp, lse, idx, o_branch, and, when debug, also p_slc and gates.
+    kv_slc, kv_win: (k, v) pairs of the selected and window branches when each
+    branch has its own keys and values (both or neither); k, v then feed the
+    compressed branch only."""
     dev = q.device
     dt = cfg.torch_dtype
     B, T, Hq, Hkv = cfg.B, cfg.T, cfg.H_q, cfg.H_kv
@@ -175,6 +188,10 @@ def nsa_fwd_prefill(cfg: Config, q, k, v, x, w_gate, phi_k=None, phi_v=None, *, 
     for name in ("o", "k_cmp", "v_cmp", "lse", "idx", "o_branch", "p_slc", "gates"):
         t = res.get(name)
         setattr(a, name, t.data_ptr() if (t is not None and t.numel()) else None)
+    if (kv_slc is None) != (kv_win is None):
+        raise ValueError("kv_slc and kv_win go together")
+    a.k_slc, a.v_slc = _branch_kv(cfg, kv_slc, "slc", dev)
+    a.k_win, a.v_win = _branch_kv(cfg, kv_win, "win", dev)
     ws = _workspace(cfg, NSA_OP_FWD_PREFILL, dev, workspace)
     p = cfg.params()
     st = _lib.load().nsa_fwd_prefill(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(), _stream(dev))
@@ -186,10 +203,12 @@ def nsa_fwd_prefill(cfg: Config, q, k, v, x, w_gate, phi_k=None, phi_v=None, *, 
 
 def nsa_fwd_decode(cfg: Config, q, k_cache, v_cache, k_cmp_cache, v_cmp_cache, x, w_gate, *,
                    out=None, debug: bool = False, seq_lens: Optional[torch.Tensor] = None,
-                   workspace: Optional[torch.Tensor] = None):
+                   kv_win_cache=None, workspace: Optional[torch.Tensor] = None):
     """One decode step; cfg.T is the cache length S (query at position S-1).
     With seq_lens (int32 [B] on the device), cfg.T is the cache capacity and
-    sequence b holds seq_lens[b] tokens, its query at position seq_lens[b]-1."""
+    sequence b holds seq_lens[b] tokens, its query at position seq_lens[b]-1.
+    kv_win_cache: the window branch's own (k, v) caches when each branch has
+    independent keys and values (k_cache, v_cache then serve the selected one)."""
     dev = q.device
     dt = cfg.torch_dtype
     B, S, Hq, Hkv = cfg.B, cfg.T, cfg.H_q, cfg.H_kv
@@ -219,6 +238,10 @@ def nsa_fwd_decode(cfg: Config, q, k_cache, v_cache, k_cmp_cache, v_cmp_cache, x
     if seq_lens is not None:
         _check(seq_lens, "seq_lens", (B,), torch.int32, dev)
         a.seq_lens = seq_lens.data_ptr()
+    if kv_win_cache is not None:
+        _check(kv_win_cache[0], "k_win_cache", (B, S, Hkv, cfg.d_k), dt, dev)
+        _check(kv_win_cache[1], "v_win_cache", (B, S, Hkv, cfg.d_v), dt, dev)
+        a.k_win_cache, a.v_win_cache = kv_win_cache[0].data_ptr(), kv_win_cache[1].data_ptr()
     ws = _workspace(cfg, NSA_OP_FWD_DECODE, dev, workspace)
     p = cfg.params()
     st = _lib.load().nsa_fwd_decode(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(), _stream(dev))
@@ -262,9 +285,14 @@ def nsa_decode_append(cfg: Config, k_new, v_new, seq_lens, k_cache, v_cache, k_c
 
 
 def nsa_bwd(cfg: Config, q, k, v, x, w_gate, phi_k, phi_v, saved: Dict[str, torch.Tensor], d_o, *,
+            kv_slc=None, kv_win=None, recompute_row_terms: bool = False,
             workspace: Optional[torch.Tensor] = None) -> Dict[str, object]:
     """Backward with the forward's selected blocks fixed.  `saved` is the dict
-    nsa_fwd_prefill returned with save_for_backward=True.  Gradients are fp32."""
+    nsa_fwd_prefill returned with save_for_backward=True.  Gradients are fp32.
+    With kv_slc, kv_win (as passed to the forward) the result also holds
+    dk_slc, dv_slc, dk_win, dv_win, and dk, dv are the compressed branch's part.
+    The softmax row terms <dO, O_c> are read from saved["o_branch"] when it is
+    there, unless recompute_row_terms asks for them to be recomputed."""
     dev = q.device
     dt = cfg.torch_dtype
     B, T, Hq, Hkv = cfg.B, cfg.T, cfg.H_q, cfg.H_kv
@@ -280,10 +308,23 @@ def nsa_bwd(cfg: Config, q, k, v, x, w_gate, phi_k, phi_v, saved: Dict[str, torc
     for name in ("k_cmp", "v_cmp", "lse", "idx"):
         t = saved[name]
         setattr(a, name, t.data_ptr() if t.numel() else None)
+    if saved.get("o_branch") is not None and not recompute_row_terms:
+        _check(saved["o_branch"], "o_branch", (3, B, T, Hq, cfg.d_v), torch.float32, dev)
+        a.o_branch = saved["o_branch"].data_ptr()
     a.phi_k = _phi_struct(cfg, phi_k, cfg.d_k, dev)
     a.phi_v = _phi_struct(cfg, phi_v, cfg.d_v, dev)
     for name in ("dq", "dk", "dv", "dw_gate"):
         setattr(a, name, res[name].data_ptr())
+    if (kv_slc is None) != (kv_win is None):
+        raise ValueError("kv_slc and kv_win go together")
+    if kv_slc is not None:
+        a.k_slc, a.v_slc = _branch_kv(cfg, kv_slc, "slc", dev)
+        a.k_win, a.v_win = _branch_kv(cfg, kv_win, "win", dev)
+        for tag in ("slc", "win"):
+            res["dk_" + tag] = torch.empty(B, T, Hkv, cfg.d_k, dtype=f32, device=dev)
+            res["dv_" + tag] = torch.empty(B, T, Hkv, cfg.d_v, dtype=f32, device=dev)
+            setattr(a, "dk_" + tag, res["dk_" + tag].data_ptr())
+            setattr(a, "dv_" + tag, res["dv_" + tag].data_ptr())
     if cfg.phi == "mlp":
         for tag, D in (("d_phi_k", cfg.d_k), ("d_phi_v", cfg.d_v)):
             g = {"pe": torch.empty(cfg.l, D, dtype=f32, device=dev),

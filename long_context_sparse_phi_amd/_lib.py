@@ -38,13 +38,15 @@ class nsa_phi_grads(ctypes.Structure):
 class nsa_prefill_args(ctypes.Structure):
     _fields_ = ([(n, _vp) for n in ("q", "k", "v", "x", "w_gate")] +
                 [("phi_k", nsa_phi_weights), ("phi_v", nsa_phi_weights)] +
-                [(n, _vp) for n in ("o", "k_cmp", "v_cmp", "lse", "idx", "o_branch", "p_slc", "gates")])
+                [(n, _vp) for n in ("o", "k_cmp", "v_cmp", "lse", "idx", "o_branch", "p_slc", "gates",
+                                    "k_slc", "v_slc", "k_win", "v_win")])
 
 
 class nsa_decode_args(ctypes.Structure):
     _fields_ = ([(n, _vp) for n in ("q", "k_cache", "v_cache", "k_cmp_cache", "v_cmp_cache", "x", "w_gate")] +
                 [("cmp_cache_cap", ctypes.c_int32)] +
-                [(n, _vp) for n in ("o", "idx", "p_slc", "lse", "o_branch", "seq_lens")])
+                [(n, _vp) for n in ("o", "idx", "p_slc", "lse", "o_branch", "seq_lens",
+                                    "k_win_cache", "v_win_cache")])
 
 
 class nsa_append_args(ctypes.Structure):
@@ -59,7 +61,9 @@ class nsa_bwd_args(ctypes.Structure):
                 [("phi_k", nsa_phi_weights), ("phi_v", nsa_phi_weights)] +
                 [(n, _vp) for n in ("k_cmp", "v_cmp", "lse", "idx", "o_branch", "d_o",
                                     "dq", "dk", "dv", "dw_gate")] +
-                [("d_phi_k", nsa_phi_grads), ("d_phi_v", nsa_phi_grads)])
+                [("d_phi_k", nsa_phi_grads), ("d_phi_v", nsa_phi_grads)] +
+                [(n, _vp) for n in ("k_slc", "v_slc", "k_win", "v_win",
+                                    "dk_slc", "dv_slc", "dk_win", "dv_win")])
 
 
 class nsa_dense_args(ctypes.Structure):

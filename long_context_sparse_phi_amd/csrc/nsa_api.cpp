@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <initializer_list>
 #include <cmath>
 #include <cstring>
 
@@ -163,6 +164,20 @@ struct Stages {
   bool mark() { return ev ? hipEventRecord((hipEvent_t)ev[i++], s) != hipSuccess : false; }
 };
 
+// The optional per-branch tensors are either all absent or all present and aligned.
+bool all_or_none(std::initializer_list<const void*> ps, bool* present) {
+  int n = 0, k = 0;
+  for (const void* p : ps) {
+    ++k;
+    if (p) {
+      if (!aligned16(p)) return false;
+      ++n;
+    }
+  }
+  *present = n > 0;
+  return n == 0 || n == k;
+}
+
 bool phi_ok(const nsa_phi_weights& w) {
   const void* ps[5] = {w.pe, w.w1, w.b1, w.w2, w.b2};
   for (const void* p : ps)
@@ -242,6 +257,8 @@ static nsa_status prefill_impl(const nsa_params* p, const nsa_prefill_args* a, v
     for (const void* r : opt)
       if (r && !aligned16(r)) return NSA_ERR_INVALID_ARG;
     if (dm.hidden && (!phi_ok(a->phi_k) || !phi_ok(a->phi_v))) return NSA_ERR_INVALID_ARG;
+    bool split = false;
+    if (!all_or_none({a->k_slc, a->v_slc, a->k_win, a->v_win}, &split)) return NSA_ERR_INVALID_ARG;
     PrefillWs w;
     const size_t need = plan_prefill(dm, nullptr, &w);
     if (ws_bytes < need || !ws || !aligned16(ws)) return NSA_ERR_WORKSPACE;
@@ -268,8 +285,12 @@ static nsa_status prefill_impl(const nsa_params* p, const nsa_prefill_args* a, v
       return NSA_ERR_HIP;
     if (sg.mark() || run_compress(dm, dm.dv, a->v, &a->phi_v, vc, w.vct, w.phi, s) != hipSuccess)
       return NSA_ERR_HIP;
-    if (sg.mark() || launch_transpose_seq(dm, dm.B, dm.T, dm.Hkv, dm.dv, dm.Tp, a->v, w.vt, s) != hipSuccess ||
-        launch_kv_frag(dm, a->k, a->v, w.kvf, s) != hipSuccess)
+    const void* ks = split ? a->k_slc : a->k;
+    const void* vs = split ? a->v_slc : a->v;
+    const void* kw = split ? a->k_win : a->k;
+    const void* vw = split ? a->v_win : a->v;
+    if (sg.mark() || launch_transpose_seq(dm, dm.B, dm.T, dm.Hkv, dm.dv, dm.Tp, vw, w.vt, s) != hipSuccess ||
+        launch_kv_frag(dm, ks, vs, w.kvf, s) != hipSuccess)
       return NSA_ERR_HIP;
     CmpArgs ca;
     ca.q = a->q; ca.kc = kc; ca.vct = w.vct; ca.lse = lse; ca.o = o_cmp; ca.p_slc = (float*)a->p_slc; ca.idx = idx;
@@ -280,7 +301,7 @@ static nsa_status prefill_impl(const nsa_params* p, const nsa_prefill_args* a, v
     sa.q = a->q; sa.kvf = w.kvf; sa.idx = idx; sa.o = o_slc; sa.lse = lse + BTH; sa.o_f32 = o_f32;
     if (sg.mark() || launch_slc(dm, sa, s) != hipSuccess) return NSA_ERR_HIP;
     WinArgs wa{};
-    wa.q = a->q; wa.k = a->k; wa.vt = w.vt; wa.o_cmp = o_cmp; wa.o_slc = o_slc; wa.gates = gates;
+    wa.q = a->q; wa.k = kw; wa.vt = w.vt; wa.o_cmp = o_cmp; wa.o_slc = o_slc; wa.gates = gates;
     wa.o_win = o_win; wa.lse = lse + 2 * BTH; wa.o = a->o; wa.o_f32 = o_f32;
     if (sg.mark() || launch_win_combine(dm, wa, s) != hipSuccess) return NSA_ERR_HIP;
     if (sg.mark()) return NSA_ERR_HIP;
@@ -374,9 +395,11 @@ static nsa_status decode_impl(const nsa_params* p, const nsa_decode_args* a, voi
     if (dm.ncmp > 0 && (!a->k_cmp_cache || !a->v_cmp_cache || !aligned16(a->k_cmp_cache) ||
                         !aligned16(a->v_cmp_cache) || a->cmp_cache_cap < dm.ncmp))
       return NSA_ERR_INVALID_ARG;
-    const void* opt[] = {a->idx, a->p_slc, a->lse, a->o_branch};
+    const void* opt[] = {a->idx, a->p_slc, a->lse, a->o_branch, a->seq_lens};
     for (const void* r : opt)
       if (r && !aligned16(r)) return NSA_ERR_INVALID_ARG;
+    bool split = false;
+    if (!all_or_none({a->k_win_cache, a->v_win_cache}, &split)) return NSA_ERR_INVALID_ARG;
     const size_t need = decode_ws_bytes(dm);
     if (ws_bytes < need || !ws || !aligned16(ws)) return NSA_ERR_WORKSPACE;
     if ((st = check_device()) != NSA_OK) return st;
@@ -418,6 +441,10 @@ static nsa_status bwd_impl(const nsa_params* p, const nsa_bwd_args* a, void* ws,
       for (const void* r : g)
         if (!r || !aligned16(r)) return NSA_ERR_INVALID_ARG;
     }
+    bool split = false, split_out = false;
+    if (!all_or_none({a->k_slc, a->v_slc, a->k_win, a->v_win}, &split) ||
+        !all_or_none({a->dk_slc, a->dv_slc, a->dk_win, a->dv_win}, &split_out) || split != split_out)
+      return NSA_ERR_INVALID_ARG;
     const size_t need = bwd_ws_bytes(dm);
     if (ws_bytes < need || !ws || !aligned16(ws)) return NSA_ERR_WORKSPACE;
     if ((st = check_device()) != NSA_OK) return st;

@@ -7,11 +7,13 @@
 // when its last token arrives, i.e. when the sequence length L+1 satisfies
 // L+1 >= l and (L+1-l) % d == 0; it is then block (L+1-l)/d.
 //
-// Work per call is tiny (at most one block per (sequence, KV head)): the MLP
-// phi runs as a 16-row MFMA GEMM over the l*D block features of the rows that
-// complete a block, with W1 column tiles staged through LDS, then a GELU, and
-// the second layer in fp32 with one thread per output feature.  Rows that do
-// not complete a block skip all work.
+// Work per call is tiny (at most one block per (sequence, KV head)) and bound
+// by latency: the MLP phi's first layer runs as a 16-row MFMA GEMM over the
+// l*D block features of the rows that complete a block, split over the
+// feature axis into 256-wide slices so that hundreds of workgroups each do a
+// few steps (W1 column tiles staged through LDS); the second kernel sums the
+// slices, applies the GELU and evaluates the second layer in fp32 with one
+// thread per output feature.  Rows that do not complete a block skip all work.
 #include "nsa_common.hpp"
 #include "nsa_kernels.hpp"
 
@@ -61,15 +63,19 @@ __global__ __launch_bounds__(64) void k_append_mean(Dims dm, int D, int cap, con
   }
 }
 
-// MLP phi, first layer: h[r, n] = gelu(sum_x u_r[x] w1[x, n] + b1[n]) for the
-// rows r = (b, g) that complete a block, u_r = concat_j (x[i*d+j] + pe[j]).
-// The pe term is a second MFMA on the same W1 fragment, so both operands stay
-// exact in the I/O type.  Workgroup: 16 rows x 64 hidden units, one wave per
-// 16 units; W1[kk .. kk+31][n0 .. n0+63] is staged transposed in LDS.
+constexpr int kAppendKS = 256;   // first-layer features per workgroup (split-K slice)
+
+// MLP phi, first layer, one feature slice: part[z, r, n] = sum over x in slice z
+// of u_r[x] w1[x, n] for the rows r = (b, g) that complete a block,
+// u_r = concat_j (x[i*d+j] + pe[j]).  The pe term is a second MFMA on the
+// same W1 fragment, so both operands stay exact in the I/O type.  Workgroup:
+// 16 rows x 64 hidden units x one slice, one wave per 16 units;
+// W1[kk .. kk+31][n0 .. n0+63] is staged transposed in LDS, the next step's
+// global loads are issued before the current step's MFMAs.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_append_h(Dims dm, const int* __restrict__ lens, const T* __restrict__ x,
                                                   const T* __restrict__ pe, const T* __restrict__ w1,
-                                                  const T* __restrict__ b1, float* __restrict__ h) {
+                                                  float* __restrict__ part) {
   constexpr int WS = 32 + 8;              // LDS row stride (elements) of the transposed W1 tile
   __shared__ __align__(16) T ws[64 * WS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -85,57 +91,69 @@ __global__ __launch_bounds__(256) void k_append_h(Dims dm, const int* __restrict
   }
   if (!__syncthreads_or(src != nullptr)) return;
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int KK = dm.l * D;
+  const int k0 = blockIdx.z * kAppendKS, k1 = min(k0 + kAppendKS, dm.l * D);
   const int lr = tid >> 3, lc = (tid & 7) * 8;   // loader: W1 row kk+lr, columns n0+lc .. +7
-  for (int kk = 0; kk < KK; kk += 32) {
-    {
-      const Frag8<T> f = load_frag(w1 + (size_t)(kk + lr) * H + n0 + lc);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ws[(lc + e) * WS + lr] = frag_at(f, e);
-    }
-    __syncthreads();
+  auto gload = [&](int kk, Frag8<T>& f, Frag8<T>& a, Frag8<T>& ap) {
+    f = load_frag(w1 + (size_t)(kk + lr) * H + n0 + lc);
     const int xx = kk + qd * 8, j = xx / D, e = xx % D;
-    const Frag8<T> a = src ? load_frag(src + (size_t)j * dm.Hkv * D + e) : zero_frag<T>();
-    const Frag8<T> ap = load_frag(pe + xx);
+    a = src ? load_frag(src + (size_t)j * dm.Hkv * D + e) : zero_frag<T>();
+    ap = load_frag(pe + xx);
+  };
+  Frag8<T> f, a, ap;
+  gload(k0, f, a, ap);
+  for (int kk = k0; kk < k1; kk += 32) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ws[(lc + e) * WS + lr] = frag_at(f, e);
+    __syncthreads();
+    const Frag8<T> ca = a, cp = ap;
+    if (kk + 32 < k1) gload(kk + 32, f, a, ap);
     const Frag8<T> bw = *reinterpret_cast<const Frag8<T>*>(ws + (wave * 16 + c16) * WS + qd * 8);
-    mma(acc, a, bw);
-    mma(acc, ap, bw);
+    mma(acc, ca, bw);
+    mma(acc, cp, bw);
     __syncthreads();
   }
   // acc[k]: row 4*qd + k of the tile, hidden unit n0 + 16*wave + c16
   const int n = n0 + wave * 16 + c16;
-  const float bias = to_f32(b1[n]);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int rr = blockIdx.y * 16 + qd * 4 + k;
-    if (rr >= R) continue;
-    const float av = acc[k] + bias;
-    h[(size_t)rr * H + n] = 0.5f * av * (1.f + erff(av * 0.70710678118654752f));
+    if (rr < R) part[((size_t)blockIdx.z * R + rr) * H + n] = acc[k];
   }
 }
 
-// MLP phi, second layer: out[b, i, g, e] = b2[e] + sum_n h[r, n] w2[n, e],
+// MLP phi, second layer: a = b1 + the sum of the first layer's slices (in
+// slice order), h = gelu(a), out[b, i, g, e] = b2[e] + sum_n h[n] w2[n, e],
 // fp32, one thread per feature.
 template <typename T>
-__global__ __launch_bounds__(256) void k_append_o(Dims dm, int D, int cap, const int* __restrict__ lens,
-                                                  const float* __restrict__ h, const T* __restrict__ w2,
-                                                  const T* __restrict__ b2, T* __restrict__ out) {
+__global__ __launch_bounds__(256) void k_append_o(Dims dm, int D, int cap, int nslice, const int* __restrict__ lens,
+                                                  const float* __restrict__ part, const T* __restrict__ b1,
+                                                  const T* __restrict__ w2, const T* __restrict__ b2,
+                                                  T* __restrict__ out) {
   extern __shared__ float hs[];
   const int r = blockIdx.x, b = r / dm.Hkv, g = r % dm.Hkv;
   const int i = append_block(append_slot(lens, b, dm.T), dm.l, dm.d);
   if (i < 0) return;
-  const int H = dm.hidden;
-  for (int n = threadIdx.x; n < H; n += blockDim.x) hs[n] = h[(size_t)r * H + n];
+  const int H = dm.hidden, R = dm.B * dm.Hkv;
+  for (int n = threadIdx.x; n < H; n += blockDim.x) {
+    float av = to_f32(b1[n]);
+#pragma unroll 8
+    for (int z = 0; z < nslice; ++z) av += part[((size_t)z * R + r) * H + n];
+    hs[n] = 0.5f * av * (1.f + erff(av * 0.70710678118654752f));
+  }
   __syncthreads();
   for (int e = threadIdx.x; e < D; e += blockDim.x) {
     float acc = to_f32(b2[e]);
+#pragma unroll 16
     for (int n = 0; n < H; ++n) acc = fmaf(hs[n], to_f32(w2[(size_t)n * D + e]), acc);
     out[((size_t)(b * cap + i) * dm.Hkv + g) * D + e] = from_f32<T>(acc);
   }
 }
 
+static int append_slices(const Dims& dm, int D) { return (dm.l * D + kAppendKS - 1) / kAppendKS; }
+
 size_t append_ws_bytes(const Dims& dm) {
-  return dm.hidden ? (size_t)dm.B * dm.Hkv * dm.hidden * sizeof(float) : 0;
+  const int D = dm.dk > dm.dv ? dm.dk : dm.dv;
+  return dm.hidden ? (size_t)append_slices(dm, D) * dm.B * dm.Hkv * dm.hidden * sizeof(float) : 0;
 }
 
 template <typename T, int D>
@@ -146,12 +164,13 @@ static hipError_t append_phi(const Dims& dm, const AppendArgs& a, const T* x, co
     k_append_mean<T><<<R, 64, 0, s>>>(dm, D, a.cap, a.lens, x, out);
     return hipGetLastError();
   }
-  dim3 grid(dm.hidden / 64, (R + 15) / 16);
-  k_append_h<T, D><<<grid, 256, 0, s>>>(dm, a.lens, x, (const T*)w.pe, (const T*)w.w1, (const T*)w.b1, a.h);
+  const int ns = append_slices(dm, D);
+  dim3 grid(dm.hidden / 64, (R + 15) / 16, ns);
+  k_append_h<T, D><<<grid, 256, 0, s>>>(dm, a.lens, x, (const T*)w.pe, (const T*)w.w1, a.h);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  k_append_o<T><<<R, 256, dm.hidden * sizeof(float), s>>>(dm, D, a.cap, a.lens, a.h, (const T*)w.w2,
-                                                          (const T*)w.b2, out);
+  k_append_o<T><<<R, 256, dm.hidden * sizeof(float), s>>>(dm, D, a.cap, ns, a.lens, a.h, (const T*)w.b1,
+                                                          (const T*)w.w2, (const T*)w.b2, out);
   return hipGetLastError();
 }
 

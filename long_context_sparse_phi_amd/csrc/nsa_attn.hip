@@ -211,10 +211,13 @@ __global__ __launch_bounds__(256, 2) void k_slc(Dims dm, SlcArgs a) {
     ls = ls * alpha + psum;
     m = mn;
     const Frag8<T> pf = to_frag<T>(p);
+    Frag8<T> plo;
+    if constexpr (kPrecisePV<T, OT>) plo = lo_frag(p, pf);
 #pragma unroll
     for (int dt = 0; dt < DV / 16; ++dt) {
       oacc[dt] *= alpha;
       mma(oacc[dt], tl.v[dt], pf);
+      if constexpr (kPrecisePV<T, OT>) mma(oacc[dt], tl.v[dt], plo);
     }
   };
 
@@ -331,7 +334,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_win(Dims dm, WinArgs a) {
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) mma(s[sub][ct], kf[ks], qf[ct][ks]);
     }
-    Frag8<T> pf[NCT];
+    Frag8<T> pf[NCT], plo[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       float v[8], mx = kNegInf;
@@ -356,6 +359,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_win(Dims dm, WinArgs a) {
       ls[ct] = ls[ct] * alpha + psum;
       m[ct] = mn;
       pf[ct] = to_frag<T>(p);
+      if constexpr (kPrecisePV<T, OT>) plo[ct] = lo_frag(p, pf[ct]);
 #pragma unroll
       for (int dt = 0; dt < DV / 16; ++dt) oacc[dt][ct] *= alpha;
     }
@@ -363,7 +367,10 @@ __global__ __launch_bounds__(NW * 64, 2) void k_win(Dims dm, WinArgs a) {
     for (int dt = 0; dt < DV / 16; ++dt) {
       const Frag8<T> vf = Tile::vfrag(tl_, dt * 16 + c16, h * 32, qd);
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) mma(oacc[dt][ct], vf, pf[ct]);
+      for (int ct = 0; ct < NCT; ++ct) {
+        mma(oacc[dt][ct], vf, pf[ct]);
+        if constexpr (kPrecisePV<T, OT>) mma(oacc[dt][ct], vf, plo[ct]);
+      }
     }
   };
 

@@ -62,6 +62,8 @@ struct BwdBufs {
   float* Dc;       // [3,B,T,Hq]
   float* dz;       // [B,T,Hq,3]
   void* fkv;       // fragment tiles of (k, v, k^T) over T (bwd_tile_ins instructions per 32 keys)
+                   // of the selected branch's keys/values
+  void* fkvw;      // the same for the window branch's own keys/values (independent K/V only)
   void* fckv;      // the same over the compressed keys (k_cmp, v_cmp, k_cmp^T)
   float* dkc;      // [B,Hkv,ncmp,dk]
   float* dvc;      // [B,Hkv,ncmp,dv]
@@ -102,6 +104,7 @@ static size_t bwd_carve(const Dims& dm, void* ws, BwdBufs* w) {
   w->Dc = (float*)take(3 * BTH * 4);
   w->dz = (float*)take(BTH * 3 * 4);
   w->fkv = take(frag_tiles_elems(dm, dm.T, bwd_tile_ins(dm)) * es);
+  w->fkvw = take(frag_tiles_elems(dm, dm.T, bwd_tile_ins(dm)) * es);
   w->fckv = take(frag_tiles_elems(dm, dm.ncmp, bwd_tile_ins(dm)) * es);
   w->dkc = (float*)take(BG * dm.ncmp * dm.dk * 4);
   w->dvc = (float*)take(BG * dm.ncmp * dm.dv * 4);
@@ -142,11 +145,20 @@ size_t bwd_ws_bytes(const Dims& dm) {
   return bwd_carve(dm, nullptr, &w);
 }
 
+// k, v feed phi (the compressed branch); ks, vs the selected and kw, vw the
+// window branch (all three the same tensors unless each branch has its own).
+// dk, dv receive the phi path, dks/dvs and dkw/dvw the other two branches'
+// key/value gradients (aliases of dk, dv when the tensors are shared).
 struct BwdArgs {
   const void *q, *k, *v, *x, *wg, *kc, *vc, *d_o;
+  const void *ks, *vs, *kw, *vw;
+  const void* fkv_win;  // fragment tiles the dq pass reads for the window branch
+  const float* ob;   // optional [3,B,T,Hq,dv] fp32 branch outputs saved by the forward
   const float* lse;  // [3,B,T,Hq] natural log
   const int* idx;    // [B,T,Hkv,n]
   float *dq, *dk, *dv, *dwg;
+  float *dks, *dvs, *dkw, *dvw;
+  bool split;
   BwdBufs w;
   BwdPlan pl;
 };
@@ -264,9 +276,10 @@ __global__ __launch_bounds__(256) void k_bwd_dq(Dims dm, BwdArgs a) {
   }
   // window branch
   {
+    const T* fw = (const T*)a.fkv_win + (size_t)(b * dm.Hkv + g) * ((dm.T + 31) / 32) * TI * 512 + lane * 8;
     const int lo = max(0, t - dm.w + 1);
     for (int kt = lo & ~31; kt <= t; kt += 32)
-      dq_tile<T, DK, DV, ROWSUM>(st, fb + (size_t)(kt / 32) * TI * 512, kt, lo, t + 1, c16, qd, sc2, lse2[2],
+      dq_tile<T, DK, DV, ROWSUM>(st, fw + (size_t)(kt / 32) * TI * 512, kt, lo, t + 1, c16, qd, sc2, lse2[2],
                                  gc[2], Dc[2]);
     rsum[2] = st.rs;
   }
@@ -288,6 +301,38 @@ __global__ __launch_bounds__(256) void k_bwd_dq(Dims dm, BwdArgs a) {
     for (int dt = 0; dt < DK / 16; ++dt)
       store4(out + dt * 16, dm.scale * st.dq[dt][0], dm.scale * st.dq[dt][1], dm.scale * st.dq[dt][2],
              dm.scale * st.dq[dt][3]);
+  }
+}
+
+// Row terms from the forward's saved fp32 branch outputs: dg_c = <dO, O_c>,
+// D_c = g_c dg_c, dz_c = dg_c g_c (1 - g_c).  Memory-bound: DV/4 lanes per
+// row, each reading 4 features of dO and of the three O_c.
+template <typename T, int DV>
+__global__ __launch_bounds__(256) void k_rowterms(Dims dm, BwdArgs a) {
+  constexpr int LPR = DV / 4, RPW = 64 / LPR;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t BTH = (size_t)dm.B * dm.T * dm.Hq;
+  const size_t row = ((size_t)blockIdx.x * 4 + wave) * RPW + lane / LPR;
+  const int f = (lane % LPR) * 4;
+  const bool live = row < BTH;
+  const size_t rr = live ? row : 0;
+  float d[4];
+  load4((const T*)a.d_o + rr * DV + f, d);
+  float v[3];
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    float o[4];
+    load4(a.ob + (c * BTH + rr) * DV + f, o);
+    v[c] = d[0] * o[0] + d[1] * o[1] + d[2] * o[2] + d[3] * o[3];
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off >>= 1) v[c] += __shfl_xor(v[c], off);
+  }
+  if (!live || lane % LPR != 0) return;
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    const float gc = a.w.gates[row * 3 + c];
+    a.w.Dc[c * BTH + row] = gc * v[c];
+    a.w.dz[row * 3 + c] = v[c] * gc * (1.f - gc);
   }
 }
 
@@ -416,8 +461,8 @@ __global__ __launch_bounds__(256) void k_bwd_kv(Dims dm, BwdArgs a) {
     kr = (const T*)a.kc + ((size_t)(b * dm.ncmp + kcl) * dm.Hkv + g) * DK;
     vr = (const T*)a.vc + ((size_t)(b * dm.ncmp + kcl) * dm.Hkv + g) * DV;
   } else {
-    kr = (const T*)a.k + ((size_t)(b * dm.T + kcl) * dm.Hkv + g) * DK;
-    vr = (const T*)a.v + ((size_t)(b * dm.T + kcl) * dm.Hkv + g) * DV;
+    kr = (const T*)(MODE == KV_WIN ? a.kw : a.ks) + ((size_t)(b * dm.T + kcl) * dm.Hkv + g) * DK;
+    vr = (const T*)(MODE == KV_WIN ? a.vw : a.vs) + ((size_t)(b * dm.T + kcl) * dm.Hkv + g) * DV;
   }
   Frag8<T> kf[DK / 32], vf[DV / 32];
 #pragma unroll
@@ -576,8 +621,8 @@ __global__ __launch_bounds__(256) void k_bwd_kv(Dims dm, BwdArgs a) {
   // write: lane holds key column c16, features dt*16 + 4qd + r
   if (MODE == KV_WIN) {
     if (!kvalid) return;
-    float* dkp = a.dk + ((size_t)(b * dm.T + key) * dm.Hkv + g) * DK + qd * 4;
-    float* dvp = a.dv + ((size_t)(b * dm.T + key) * dm.Hkv + g) * DV + qd * 4;
+    float* dkp = a.dkw + ((size_t)(b * dm.T + key) * dm.Hkv + g) * DK + qd * 4;
+    float* dvp = a.dvw + ((size_t)(b * dm.T + key) * dm.Hkv + g) * DV + qd * 4;
 #pragma unroll
     for (int dt = 0; dt < DK / 16; ++dt)
       store4(dkp + dt * 16, dm.scale * dk[dt][0], dm.scale * dk[dt][1], dm.scale * dk[dt][2], dm.scale * dk[dt][3]);
@@ -635,8 +680,8 @@ __global__ __launch_bounds__(256) void k_reduce_slc(Dims dm, BwdArgs a) {
     float s = 0.f;
     for (int sg = 0; sg < nseg; ++sg)
       s += a.w.part_slc[(((size_t)bg * pl.max_slc_seg + slot0 + sg) * dm.ls + kk) * W + e];
-    if (e < dm.dk) a.dk[((size_t)(b * dm.T + key) * dm.Hkv + g) * dm.dk + e] += s;
-    else a.dv[((size_t)(b * dm.T + key) * dm.Hkv + g) * dm.dv + e - dm.dk] += s;
+    if (e < dm.dk) a.dks[((size_t)(b * dm.T + key) * dm.Hkv + g) * dm.dk + e] += s;
+    else a.dvs[((size_t)(b * dm.T + key) * dm.Hkv + g) * dm.dv + e - dm.dk] += s;
   }
 }
 
@@ -1028,9 +1073,14 @@ static hipError_t bwd_impl(const Dims& dm, const nsa_bwd_args* args, BwdArgs& a,
   {
     const int ti = bwd_tile_ins(dm);
     const int n1 = 2 * DK / 32, n2 = n1 + 2 * DV / 32;
-    if ((e = launch_frag_pack(dm, DK, dm.T, a.k, a.w.fkv, ti, 0, false, s)) != hipSuccess ||
-        (e = launch_frag_pack(dm, DV, dm.T, a.v, a.w.fkv, ti, n1, false, s)) != hipSuccess ||
-        (e = launch_frag_pack(dm, DK, dm.T, a.k, a.w.fkv, ti, n2, true, s)) != hipSuccess)
+    if ((e = launch_frag_pack(dm, DK, dm.T, a.ks, a.w.fkv, ti, 0, false, s)) != hipSuccess ||
+        (e = launch_frag_pack(dm, DV, dm.T, a.vs, a.w.fkv, ti, n1, false, s)) != hipSuccess ||
+        (e = launch_frag_pack(dm, DK, dm.T, a.ks, a.w.fkv, ti, n2, true, s)) != hipSuccess)
+      return e;
+    if (a.split &&
+        ((e = launch_frag_pack(dm, DK, dm.T, a.kw, a.w.fkvw, ti, 0, false, s)) != hipSuccess ||
+         (e = launch_frag_pack(dm, DV, dm.T, a.vw, a.w.fkvw, ti, n1, false, s)) != hipSuccess ||
+         (e = launch_frag_pack(dm, DK, dm.T, a.kw, a.w.fkvw, ti, n2, true, s)) != hipSuccess))
       return e;
     if (dm.ncmp > 0 &&
         ((e = launch_frag_pack(dm, DK, dm.ncmp, a.kc, a.w.fckv, ti, 0, false, s)) != hipSuccess ||
@@ -1038,9 +1088,15 @@ static hipError_t bwd_impl(const Dims& dm, const nsa_bwd_args* args, BwdArgs& a,
          (e = launch_frag_pack(dm, DK, dm.ncmp, a.kc, a.w.fckv, ti, n2, true, s)) != hipSuccess))
       return e;
   }
-  // stage 2: row terms D_c, dz, then dq
+  // stage 2: row terms D_c, dz (from the saved branch outputs when given,
+  // else recomputed from the probabilities), then dq
   if ((e = mark()) != hipSuccess) return e;
-  k_bwd_dq<T, DK, DV, true><<<((dm.T + 3) / 4) * BG, 256, 0, s>>>(dm, a);
+  if (a.ob) {
+    const size_t rows = BTH, per_block = 4 * (64 / (DV / 4));
+    k_rowterms<T, DV><<<(unsigned)((rows + per_block - 1) / per_block), 256, 0, s>>>(dm, a);
+  } else {
+    k_bwd_dq<T, DK, DV, true><<<((dm.T + 3) / 4) * BG, 256, 0, s>>>(dm, a);
+  }
   k_bwd_dq<T, DK, DV, false><<<((dm.T + 3) / 4) * BG, 256, 0, s>>>(dm, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // stage 3: compressed keys
@@ -1056,11 +1112,18 @@ static hipError_t bwd_impl(const Dims& dm, const nsa_bwd_args* args, BwdArgs& a,
     k_reduce_cmp<<<BG * pl.nkg_cmp, 256, 0, s>>>(dm, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // stage 4: window keys (writes dk, dv)
+  // stage 4: window keys (writes dkw, dvw); with independent K/V per branch the
+  // selected branch's and phi's gradients start from zero instead of adding to it
   if ((e = mark()) != hipSuccess) return e;
+  if (a.split) {
+    const size_t nk = (size_t)dm.B * dm.T * dm.Hkv * DK, nv = (size_t)dm.B * dm.T * dm.Hkv * DV;
+    if ((e = zero_f32(a.dks, nk, s)) != hipSuccess || (e = zero_f32(a.dvs, nv, s)) != hipSuccess ||
+        (e = zero_f32(a.dk, nk, s)) != hipSuccess || (e = zero_f32(a.dv, nv, s)) != hipSuccess)
+      return e;
+  }
   k_bwd_kv<T, DK, DV, KV_WIN><<<BG * ((dm.T + 63) / 64), 256, klds, s>>>(dm, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // stage 5: selected blocks (adds into dk, dv)
+  // stage 5: selected blocks (adds into dks, dvs)
   if ((e = mark()) != hipSuccess) return e;
   k_rev_hist<<<BG * pl.nchunk, 64, dm.nsel * sizeof(int), s>>>(dm, a);
   k_rev_scan<<<BG, 256, 0, s>>>(dm, a);
@@ -1098,8 +1161,20 @@ hipError_t launch_bwd(const Dims& dm, const nsa_bwd_args* args, void* ws, hipStr
   a.q = args->q; a.k = args->k; a.v = args->v; a.x = args->x; a.wg = args->w_gate;
   a.kc = args->k_cmp; a.vc = args->v_cmp; a.d_o = args->d_o;
   a.lse = (const float*)args->lse; a.idx = (const int*)args->idx;
+  a.ob = (const float*)args->o_branch;
   a.dq = (float*)args->dq; a.dk = (float*)args->dk; a.dv = (float*)args->dv; a.dwg = (float*)args->dw_gate;
   bwd_carve(dm, ws, &a.w);
+  a.split = args->k_slc != nullptr;
+  if (a.split) {
+    a.ks = args->k_slc; a.vs = args->v_slc; a.kw = args->k_win; a.vw = args->v_win;
+    a.dks = (float*)args->dk_slc; a.dvs = (float*)args->dv_slc;
+    a.dkw = (float*)args->dk_win; a.dvw = (float*)args->dv_win;
+    a.fkv_win = a.w.fkvw;
+  } else {
+    a.ks = a.kw = a.k; a.vs = a.vw = a.v;
+    a.dks = a.dkw = a.dk; a.dvs = a.dvw = a.dv;
+    a.fkv_win = a.w.fkv;
+  }
   a.pl = bwd_plan(dm);
   const bool bf = dm.io == IO_BF16;
   if (dm.dk == 64 && dm.dv == 64) return bf ? bwd_impl<bf16, 64, 64>(dm, args, a, s, events) : bwd_impl<float, 64, 64>(dm, args, a, s, events);

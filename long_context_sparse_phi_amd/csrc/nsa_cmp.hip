@@ -201,7 +201,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
   auto pass_b = [&](const f32x4 (&s)[2][NCT], const T* vtile, int h, int kt, auto masked) {
     const int j0 = (kt / 32) * jstep;
     f32x4 cr[NCT][2];
-    Frag8<T> pf[NCT];
+    Frag8<T> pf[NCT], plo_all[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       float p[8];
@@ -217,6 +217,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
 #pragma unroll
         for (int e = 0; e < 8; ++e) plo.v[e] = (bf16)(p[e] - (float)pf[ct].v[e]);
       }
+      plo_all[ct] = plo;
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt) {
         cr[ct][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -226,12 +227,16 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
         }
       }
     }
-    // O^T += V^T P^T, value fragments shared by the column tiles
+    // O^T += V^T P^T, value fragments shared by the column tiles (P as hi + lo
+    // when O is kept in fp32 for the backward)
 #pragma unroll
     for (int dt = 0; dt < DV / 16; ++dt) {
       const Frag8<T> vf = *reinterpret_cast<const Frag8<T>*>(vtile + (dt * 16 + c16) * kCmpVS + h * 32 + qd * 8);
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) mma(oacc[dt][ct], vf, pf[ct]);
+      for (int ct = 0; ct < NCT; ++ct) {
+        mma(oacc[dt][ct], vf, pf[ct]);
+        if constexpr (kPrecisePV<T, OT>) mma(oacc[dt][ct], vf, plo_all[ct]);
+      }
     }
     // sum over the group's heads and accumulate the score rows in LDS
 #pragma unroll

@@ -136,6 +136,22 @@ __device__ __forceinline__ void split_bf16(const float* x, Frag8<bf16>& hi, Frag
   }
 }
 
+// Residual of rounding x to the bf16 fragment hi: lo = bf16(x - hi), so that
+// hi + lo carries ~16 significant bits of x.
+__device__ __forceinline__ Frag8<bf16> lo_frag(const float* x, const Frag8<bf16>& hi) {
+  Frag8<bf16> lo;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) lo.v[e] = (bf16)(x[e] - (float)hi.v[e]);
+  return lo;
+}
+__device__ __forceinline__ Frag8<float> lo_frag(const float*, const Frag8<float>&) { return Frag8<float>{}; }
+
+// Attention outputs kept in fp32 for the backward (OT = float) with bf16
+// inputs: P enters the P V product as hi + lo bf16 parts, so the saved branch
+// outputs carry P to ~16 bits instead of 8.
+template <typename T, typename OT>
+constexpr bool kPrecisePV = sizeof(T) == 2 && sizeof(OT) == 4;
+
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }

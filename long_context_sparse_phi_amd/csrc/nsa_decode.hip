@@ -110,6 +110,8 @@ struct DecArgs {
   float* lse;         // optional [3,B,Hq]
   void* o_branch;     // optional [3,B,Hq,dv]
   const int* lens;    // optional [B] tokens per sequence (NULL: S each)
+  const void* kwcache;  // window branch's caches (the same as kcache, vcache
+  const void* vwcache;  // unless each branch has its own keys and values)
   DecBufs w;
 };
 
@@ -462,8 +464,9 @@ __global__ __launch_bounds__(64) void k_dec_sw(Dims dm, DecArgs a, DecPlan pl) {
   const int ntile = r1 > r0 ? (r1 - kt0 + 31) / 32 : 0;
   const float sc2 = dm.scale * kLog2e;
   const size_t kstride = (size_t)dm.Hkv * DK, vstride = (size_t)dm.Hkv * DV;
-  const T* kbase = (const T*)a.kcache + ((size_t)b * pl.S * dm.Hkv + g) * DK;
-  const T* vbase = (const T*)a.vcache + ((size_t)b * pl.S * dm.Hkv + g) * DV;
+  const bool win_item = it >= pl.nis;
+  const T* kbase = (const T*)(win_item ? a.kwcache : a.kcache) + ((size_t)b * pl.S * dm.Hkv + g) * DK;
+  const T* vbase = (const T*)(win_item ? a.vwcache : a.vcache) + ((size_t)b * pl.S * dm.Hkv + g) * DV;
   const int krow = (c16 >> 2) * 8 + (c16 & 3);
   float m = kNegInf, ls = 0.f;
   f32x4 oacc[DV / 16];
@@ -640,6 +643,8 @@ hipError_t launch_decode(const Dims& dm, const nsa_decode_args* args, void* ws, 
   a.x = args->x; a.wg = args->w_gate; a.o = args->o;
   a.p_slc = (float*)args->p_slc; a.lse = (float*)args->lse; a.o_branch = args->o_branch;
   a.lens = args->seq_lens;
+  a.kwcache = args->k_win_cache ? args->k_win_cache : args->k_cache;
+  a.vwcache = args->v_win_cache ? args->v_win_cache : args->v_cache;
   dec_carve(dm, ws, &a.w);
   if (args->idx) a.w.idx = (int*)args->idx;
   const DecPlan pl = dec_plan(dm);

@@ -127,7 +127,7 @@ struct AppendArgs {
   void *kcmp, *vcmp;       // [B,cap,Hkv,dk], [B,cap,Hkv,dv]
   int cap;
   AppendPhi phi_k, phi_v;
-  float* h;                // workspace [B*Hkv, hidden]
+  float* h;                // workspace: first-layer slices [nslice, B*Hkv, hidden]
 };
 hipError_t launch_append(const Dims& dm, const AppendArgs& a, hipStream_t s);
 size_t append_ws_bytes(const Dims& dm);

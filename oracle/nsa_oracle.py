@@ -285,11 +285,12 @@ def decode_token_count(s: int, p: Params) -> int:
 # ---------------------------------------------------------------------------
 
 def _row(p: Params, t: int, q_t, k, v, kc, vc, g_t, n_sel: int,
-         sel: Optional[List[List[int]]] = None, tie_scores=None, W_full=None):
+         sel: Optional[List[List[int]]] = None, tie_scores=None, W_full=None, kv_win=None):
     """All NSA quantities at position t of one sequence.
 
-    q_t [Hq,dk]; k [*,Hkv,dk], v [*,Hkv,dv] raw keys/values (positions <= t used);
-    kc, vc compressed keys/values [*,Hkv,*]; g_t [Hq,3] gates.
+    q_t [Hq,dk]; k [*,Hkv,dk], v [*,Hkv,dv] raw keys/values of the selected
+    branch (positions <= t used); kv_win: the window branch's own (k, v), by
+    default the same; kc, vc compressed keys/values [*,Hkv,*]; g_t [Hq,3] gates.
     sel: optional fixed block sets per KV head.  tie_scores: optional [Hkv,n_sel]
     score rows used for selection instead of the oracle's own where the oracle's
     own row is a near tie.
@@ -324,7 +325,8 @@ def _row(p: Params, t: int, q_t, k, v, kc, vc, g_t, n_sel: int,
         ks = slc_keys(t, S, p)
         o_br[1, hs], lse[1, hs], _ = attend(q_t[hs], k[ks, g], v[ks, g], sc)
         kw = win_keys(t, p)
-        o_br[2, hs], lse[2, hs], _ = attend(q_t[hs], k[kw, g], v[kw, g], sc)
+        k_w, v_w = (k, v) if kv_win is None else kv_win
+        o_br[2, hs], lse[2, hs], _ = attend(q_t[hs], k_w[kw, g], v_w[kw, g], sc)
     o = (g_t[:, :, None] * np.transpose(o_br, (1, 0, 2))).sum(axis=1)
     return o, o_br, lse, p_slc, sets, retied
 
@@ -337,10 +339,14 @@ def _sets_to_idx(sets: List[List[int]], n: int) -> np.ndarray:
 
 
 def forward(p: Params, q, k, v, x, w_gate, phi_k=None, phi_v=None, rows=None,
-            idx=None, tie_scores=None, kc=None, vc=None) -> Dict[str, np.ndarray]:
+            idx=None, tie_scores=None, kc=None, vc=None, kv_slc=None, kv_win=None) -> Dict[str, np.ndarray]:
     """NSA prefill forward.
 
     q [B,T,Hq,dk], k [B,T,Hkv,dk], v [B,T,Hkv,dv], x [B,T,C], w_gate [C,Hq,3].
+    kv_slc, kv_win: optional (k, v) pairs of the selected and window branches
+    [YLY 滑动窗口: each branch may have its own keys and values so that the
+    branches' gradients do not interfere]; k, v then feed the compressed branch
+    only.  Default: one k, v for all three.
     rows: query positions to evaluate (default all).  idx: optional fixed block
     indices [B,T,Hkv,n] (-1 padded), used instead of top-n.  tie_scores: optional
     [B,T,Hkv,N_sel] score rows consulted only where the oracle's own row is a near
@@ -372,8 +378,10 @@ def forward(p: Params, q, k, v, x, w_gate, phi_k=None, phi_v=None, rows=None,
         for r, t in enumerate(rows):
             sel = None if idx is None else [list(idx[b, t, g]) for g in range(Hkv)]
             ts = None if tie_scores is None else tie_scores[b, t]
-            o, o_br, lse, ps, sets, ret = _row(p, int(t), q[b, t], k[b], v[b], kc[b], vc[b],
-                                               g_all[b, r], n_sel, sel, ts, W_full)
+            k_s, v_s = (k, v) if kv_slc is None else kv_slc
+            kvw = None if kv_win is None else (kv_win[0][b], kv_win[1][b])
+            o, o_br, lse, ps, sets, ret = _row(p, int(t), q[b, t], k_s[b], v_s[b], kc[b], vc[b],
+                                               g_all[b, r], n_sel, sel, ts, W_full, kvw)
             out["o"][b, r] = o
             out["o_branch"][:, b, r] = o_br
             out["lse"][:, b, r] = lse
@@ -384,7 +392,7 @@ def forward(p: Params, q, k, v, x, w_gate, phi_k=None, phi_v=None, rows=None,
 
 
 def decode(p: Params, q, k_cache, v_cache, kc_cache, vc_cache, x, w_gate,
-           tie_scores=None, seq_lens=None) -> Dict[str, np.ndarray]:
+           tie_scores=None, seq_lens=None, kv_win_cache=None) -> Dict[str, np.ndarray]:
     """One decode step: the query token sits at position S-1 of a length-S cache,
     its own key/value already stored there; compressed blocks come from the
     given compressed cache (complete blocks only), not from phi.
@@ -394,7 +402,9 @@ def decode(p: Params, q, k_cache, v_cache, kc_cache, vc_cache, x, w_gate,
     lse [3,B,Hq], p_slc [B,Hkv,N_sel], idx [B,Hkv,n], retied [B,Hkv].
     seq_lens [B] (optional): sequence b holds only its first seq_lens[b] cache
     rows, and its query sits at seq_lens[b]-1; p_slc keeps the width of the full
-    cache, zero beyond the sequence's own blocks.
+    cache, zero beyond the sequence's own blocks.  kv_win_cache: optional
+    (k, v) caches of the window branch when it has its own keys and values
+    (k_cache, v_cache then serve the selected branch only).
     """
     B, S = k_cache.shape[:2]
     Hq, dv = q.shape[1], v_cache.shape[3]
@@ -409,8 +419,9 @@ def decode(p: Params, q, k_cache, v_cache, kc_cache, vc_cache, x, w_gate,
         Sb = S if seq_lens is None else int(seq_lens[b])
         nb = -(-Sb // p.l_sel)
         ts = None if tie_scores is None else tie_scores[b]
+        kvw = None if kv_win_cache is None else (kv_win_cache[0][b, :Sb], kv_win_cache[1][b, :Sb])
         o, o_br, lse, ps, sets, ret = _row(p, Sb - 1, q[b], k_cache[b, :Sb], v_cache[b, :Sb], kc_cache[b],
-                                           vc_cache[b], g_all[b], nb, None, ts)
+                                           vc_cache[b], g_all[b], nb, None, ts, None, kvw)
         out["o"][b], out["o_branch"][:, b], out["lse"][:, b] = o, o_br, lse
         out["p_slc"][b, :, :nb], out["idx"][b], out["retied"][b] = ps, _sets_to_idx(sets, p.n), ret
     return out
@@ -521,12 +532,14 @@ def dense_causal(q, k, v, scale=None):
     return o, lse
 
 
-def dq_rows(p: Params, q_rows, k, v, kc, vc, g_rows, d_o_rows, idx_rows, rows) -> np.ndarray:
+def dq_rows(p: Params, q_rows, k, v, kc, vc, g_rows, d_o_rows, idx_rows, rows, kv_win=None) -> np.ndarray:
     """dq of the given query positions only (the same per-row arithmetic as
     backward(): dq_t depends on row t and the keys/values it attends).
 
     q_rows [B,R,Hq,dk], d_o_rows [B,R,Hq,dv], g_rows [B,R,Hq,3] gates, idx_rows
-    [B,R,Hkv,n]; k, v raw and kc, vc compressed keys/values of whole sequences.
+    [B,R,Hkv,n]; k, v raw and kc, vc compressed keys/values of whole sequences;
+    kv_win: optional own (k, v) of the window branch (k, v then serve the
+    selected branch).
     """
     B, R, Hq, dk_ = q_rows.shape
     Hkv = k.shape[2]
@@ -542,7 +555,8 @@ def dq_rows(p: Params, q_rows, k, v, kc, vc, g_rows, d_o_rows, idx_rows, rows) -
                 branches = [
                     (kc[b, :, g], vc[b, :, g], cmp_keys(t, p)),
                     (k[b, :, g], v[b, :, g], slc_keys(t, [j for j in idx_rows[b, r, g] if j >= 0], p)),
-                    (k[b, :, g], v[b, :, g], win_keys(t, p)),
+                    ((k if kv_win is None else kv_win[0])[b, :, g], (v if kv_win is None else kv_win[1])[b, :, g],
+                     win_keys(t, p)),
                 ]
                 for c, (KK, VV, keys) in enumerate(branches):
                     if len(keys) == 0:
@@ -554,10 +568,16 @@ def dq_rows(p: Params, q_rows, k, v, kc, vc, g_rows, d_o_rows, idx_rows, rows) -
     return dq
 
 
-def backward(p: Params, q, k, v, x, w_gate, phi_k, phi_v, d_o, idx) -> Dict[str, object]:
+def backward(p: Params, q, k, v, x, w_gate, phi_k, phi_v, d_o, idx, kv_slc=None, kv_win=None) -> Dict[str, object]:
     """Gradients of L = sum(d_o * O) with block indices idx [B,T,Hkv,n] fixed.
 
-    Returns dq, dk, dv, dw_gate, dphi_k, dphi_v (dicts keyed like phi).
+    Returns dq, dk, dv, dw_gate, dphi_k, dphi_v (dicts keyed like phi), and the
+    per-branch parts of the key/value gradients: dk_phi, dv_phi (through phi,
+    the compressed branch), dk_slc, dv_slc, dk_win, dv_win.  With one k, v for
+    all branches dk = dk_phi + dk_slc + dk_win (dv alike).  With kv_slc, kv_win
+    (independent keys/values per branch, as in forward) dk, dv are the
+    compressed branch's part only and the others are the gradients of the
+    branches' own tensors.
     """
     B, T, Hq, dk_ = q.shape
     Hkv, dv_ = k.shape[2], v.shape[3]
@@ -566,9 +586,11 @@ def backward(p: Params, q, k, v, x, w_gate, phi_k, phi_v, d_o, idx) -> Dict[str,
     kc = compress(k, phi_k, p)
     vc = compress(v, phi_v, p)
     g_all = gate(x, w_gate)
+    k_s, v_s = (k, v) if kv_slc is None else kv_slc
+    k_w, v_w = (k, v) if kv_win is None else kv_win
     dq = np.zeros_like(q)
-    dk = np.zeros_like(k)
-    dv = np.zeros_like(v)
+    dks, dvs = np.zeros_like(k_s), np.zeros_like(v_s)
+    dkw, dvw = np.zeros_like(k_w), np.zeros_like(v_w)
     dkc = np.zeros_like(kc)
     dvc = np.zeros_like(vc)
     dz = np.zeros_like(g_all)
@@ -589,8 +611,10 @@ def backward(p: Params, q, k, v, x, w_gate, phi_k, phi_v, d_o, idx) -> Dict[str,
                         continue
                     if name == "cmp":
                         K, V = kc[b, keys, g], vc[b, keys, g]
+                    elif name == "slc":
+                        K, V = k_s[b, keys, g], v_s[b, keys, g]
                     else:
-                        K, V = k[b, keys, g], v[b, keys, g]
+                        K, V = k_w[b, keys, g], v_w[b, keys, g]
                     O, _, P = attend(qh, K, V, sc)
                     dg = (dO * O).sum(axis=1)
                     dz[b, t, hs, c] = dg * gg[:, c] * (1.0 - gg[:, c])
@@ -600,11 +624,17 @@ def backward(p: Params, q, k, v, x, w_gate, phi_k, phi_v, d_o, idx) -> Dict[str,
                     if name == "cmp":
                         dkc[b, keys, g] += dK
                         dvc[b, keys, g] += dV
+                    elif name == "slc":
+                        np.add.at(dks[b, :, g], keys, dK)
+                        np.add.at(dvs[b, :, g], keys, dV)
                     else:
-                        np.add.at(dk[b, :, g], keys, dK)
-                        np.add.at(dv[b, :, g], keys, dV)
+                        np.add.at(dkw[b, :, g], keys, dK)
+                        np.add.at(dvw[b, :, g], keys, dV)
     dk_phi, dphi_k = _phi_bwd(k, phi_k, dkc, p)
     dv_phi, dphi_v = _phi_bwd(v, phi_v, dvc, p)
     dw_gate = np.einsum("btc,bthk->chk", x, dz)
-    return {"dq": dq, "dk": dk + dk_phi, "dv": dv + dv_phi, "dw_gate": dw_gate,
-            "dphi_k": dphi_k, "dphi_v": dphi_v, "dk_cmp": dkc, "dv_cmp": dvc}
+    split = kv_slc is not None or kv_win is not None
+    return {"dq": dq, "dk": dk_phi if split else dk_phi + dks + dkw,
+            "dv": dv_phi if split else dv_phi + dvs + dvw, "dw_gate": dw_gate,
+            "dphi_k": dphi_k, "dphi_v": dphi_v, "dk_cmp": dkc, "dv_cmp": dvc,
+            "dk_phi": dk_phi, "dv_phi": dv_phi, "dk_slc": dks, "dv_slc": dvs, "dk_win": dkw, "dv_win": dvw}

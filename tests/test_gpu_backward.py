@@ -25,7 +25,7 @@ CASES = {
 }
 
 
-def run_case(w, seed=0):
+def run_case(w, seed=0, recompute_row_terms=False):
     import long_context_sparse_phi_amd as nsa
     import oracle as O
     cfg = nsa.config_from_workload(w)
@@ -36,7 +36,7 @@ def run_case(w, seed=0):
           flush=True)
     fwd = nsa.nsa_fwd_prefill(cfg, d["q"], d["k"], d["v"], d["x"], d["w_gate"], d["phi_k"], d["phi_v"], debug=True)
     grads = nsa.nsa_bwd(cfg, d["q"], d["k"], d["v"], d["x"], d["w_gate"], d["phi_k"], d["phi_v"], fwd,
-                        d_o.to("cuda:0"))
+                        d_o.to("cuda:0"), recompute_row_terms=recompute_row_terms)
     torch.cuda.synchronize()
     a = NI.to_numpy64(inp)
     p = oracle_params(w)
@@ -48,10 +48,13 @@ def run_case(w, seed=0):
     return grads, ref
 
 
-@pytest.mark.parametrize("case", list(CASES))
+@pytest.mark.parametrize("case", list(CASES) + ["mlp_d128_selection/recompute", "mean_fp32_g4/recompute"])
 def test_backward_matches_oracle(case):
-    w = CASES[case]
-    g, ref = run_case(w)
+    # "/recompute": the softmax row terms are recomputed from the probabilities
+    # instead of read from the forward's saved branch outputs
+    name, _, mode = case.partition("/")
+    w = CASES[name]
+    g, ref = run_case(w, recompute_row_terms=mode == "recompute")
     for name in ("dq", "dk", "dv", "dw_gate"):
         err = assert_close(np64(g[name]), ref[name], name)
         print(f"[gpu] {case} {name}: max abs err {err:.3e}, max |ref| {np.abs(ref[name]).max():.3e}")

@@ -1,0 +1,124 @@
+"""GPU parity with independent keys/values per branch (the compressed branch
+compresses k, v; the selected and window branches attend their own pairs),
+against the fp64 oracle: prefill forward, backward (per-branch key/value
+gradients) and decode (a separate window cache).  Same bars as the shared
+case: indices bit-exact outside near ties, floats within 2e-2 absolute +
+1e-2 relative."""
+import numpy as np
+import pytest
+import torch
+
+import nsa_inputs as NI
+from tests.nsa_testutil import assert_close, np64, oracle_params, to_dev
+
+pytestmark = pytest.mark.gpu
+
+W = NI.workload
+DEV = "cuda:0"
+
+CASES = {
+    "mlp_d192_offsets": W("prefill_64k", T=900, H_kv=2, n=6, w=100, bias_std=0.02),
+    "mean_fp32_g4": W("tiny_fp32", T=520),
+}
+
+
+def branch_inputs(w):
+    """Own keys/values of the selected and window branches: the k, v draws of
+    other seeds of the same workload."""
+    s = NI.make_prefill_inputs(w, 11)
+    v = NI.make_prefill_inputs(w, 12)
+    return (s["k"], s["v"]), (v["k"], v["v"])
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_split_kv_prefill_and_backward(case):
+    import long_context_sparse_phi_amd as nsa
+    import oracle as O
+    w = CASES[case]
+    cfg = nsa.config_from_workload(w)
+    inp = NI.make_prefill_inputs(w, 0)
+    kv_s, kv_w = branch_inputs(w)
+    d_o = NI.make_grad_output(w, 0)
+    d = to_dev(inp)
+    ks, kw = tuple(t.to(DEV) for t in kv_s), tuple(t.to(DEV) for t in kv_w)
+    print(f"[gpu] split-kv prefill+backward {case} T={w.T}", flush=True)
+    fwd = nsa.nsa_fwd_prefill(cfg, d["q"], d["k"], d["v"], d["x"], d["w_gate"], d["phi_k"], d["phi_v"],
+                              debug=True, kv_slc=ks, kv_win=kw)
+    g = nsa.nsa_bwd(cfg, d["q"], d["k"], d["v"], d["x"], d["w_gate"], d["phi_k"], d["phi_v"], fwd, d_o.to(DEV),
+                    kv_slc=ks, kv_win=kw)
+    torch.cuda.synchronize()
+    a = NI.to_numpy64(inp)
+    s64 = tuple(np64(t) for t in kv_s)
+    w64 = tuple(np64(t) for t in kv_w)
+    p = oracle_params(w)
+    ref = O.forward(p, a["q"], a["k"], a["v"], a["x"], a["w_gate"], a["phi_k"], a["phi_v"],
+                    tie_scores=np64(fwd["p_slc"]), kv_slc=s64, kv_win=w64)
+    gi = fwd["idx"].cpu().numpy().astype(np.int64)
+    assert np.array_equal(gi, ref["idx"])
+    for c, name in enumerate(("cmp", "slc", "win")):
+        assert_close(np64(fwd["lse"][c]), ref["lse"][c], f"lse_{name}")
+        assert_close(np64(fwd["o_branch"][c]), ref["o_branch"][c], f"o_{name}")
+    assert_close(np64(fwd["o"]), ref["o"], "o")
+    rg = O.backward(p, a["q"], a["k"], a["v"], a["x"], a["w_gate"], a["phi_k"], a["phi_v"], np64(d_o),
+                    ref["idx"], kv_slc=s64, kv_win=w64)
+    for name in ("dq", "dk", "dv", "dk_slc", "dv_slc", "dk_win", "dv_win", "dw_gate"):
+        err = assert_close(np64(g[name]), rg[name], name)
+        print(f"[gpu] {case} {name}: max abs err {err:.3e}, max |ref| {np.abs(rg[name]).max():.3e}")
+    if w.phi == "mlp":
+        for key in ("pe", "w1", "b1", "w2", "b2"):
+            assert_close(np64(g["d_phi_k"][key]), rg["dphi_k"][key], f"dphi_k.{key}")
+            assert_close(np64(g["d_phi_v"][key]), rg["dphi_v"][key], f"dphi_v.{key}")
+
+
+def test_split_kv_with_shared_tensors_equals_shared_call():
+    # passing k, v as every branch's own pair gives the shared forward exactly,
+    # and per-branch gradients that add up to the shared ones
+    import long_context_sparse_phi_amd as nsa
+    w = CASES["mlp_d192_offsets"]
+    cfg = nsa.config_from_workload(w)
+    d = to_dev(NI.make_prefill_inputs(w, 1))
+    d_o = NI.make_grad_output(w, 1).to(DEV)
+    args = (cfg, d["q"], d["k"], d["v"], d["x"], d["w_gate"], d["phi_k"], d["phi_v"])
+    kv = (d["k"], d["v"])
+    print("[gpu] split-kv with shared tensors", flush=True)
+    f0 = nsa.nsa_fwd_prefill(*args, debug=True)
+    f1 = nsa.nsa_fwd_prefill(*args, debug=True, kv_slc=kv, kv_win=kv)
+    g0 = nsa.nsa_bwd(*args, f0, d_o)
+    g1 = nsa.nsa_bwd(*args, f1, d_o, kv_slc=kv, kv_win=kv)
+    torch.cuda.synchronize()
+    for key in ("o", "idx", "p_slc", "lse", "o_branch"):
+        assert torch.equal(f0[key], f1[key]), key
+    assert torch.equal(g0["dq"], g1["dq"])
+    for x in ("k", "v"):
+        tot = g1["d" + x] + g1[f"d{x}_slc"] + g1[f"d{x}_win"]
+        assert_close(np64(tot), np64(g0["d" + x]), "d" + x, atol=1e-4, rtol=1e-5)
+
+
+def test_split_kv_decode_window_cache():
+    import long_context_sparse_phi_amd as nsa
+    import oracle as O
+    w = W("decode_64k", B=3, T=1300, H_kv=2, bias_std=0.02)
+    p = oracle_params(w)
+    cfg = nsa.config_from_workload(w)
+    inp = NI.make_decode_inputs(w, 4)
+    other = NI.make_decode_inputs(w, 5)
+    a = NI.to_numpy64(inp)
+    kc = O.compress(a["k_cache"], a["phi_k"], p)
+    vc = O.compress(a["v_cache"], a["phi_v"], p)
+    dt = cfg.torch_dtype
+    lens = [1300, 700, 90]
+    print("[gpu] split-kv decode", flush=True)
+    res = nsa.nsa_fwd_decode(cfg, inp["q"].to(DEV), inp["k_cache"].to(DEV), inp["v_cache"].to(DEV),
+                             torch.from_numpy(kc).to(dt).to(DEV), torch.from_numpy(vc).to(dt).to(DEV),
+                             inp["x"].to(DEV), inp["w_gate"].to(DEV), debug=True,
+                             seq_lens=torch.tensor(lens, dtype=torch.int32, device=DEV),
+                             kv_win_cache=(other["k_cache"].to(DEV), other["v_cache"].to(DEV)))
+    torch.cuda.synchronize()
+    ref = O.decode(p, a["q"], a["k_cache"], a["v_cache"], kc, vc, a["x"], a["w_gate"],
+                   tie_scores=np64(res["p_slc"]), seq_lens=lens,
+                   kv_win_cache=(np64(other["k_cache"]), np64(other["v_cache"])))
+    assert np.array_equal(res["idx"].cpu().numpy().astype(np.int64), ref["idx"])
+    for c, name in enumerate(("cmp", "slc", "win")):
+        assert_close(np64(res["lse"][c]), ref["lse"][c], f"lse_{name}")
+        assert_close(np64(res["o_branch"][c]), ref["o_branch"][c], f"o_{name}")
+    assert_close(np64(res["o"]), ref["o"], "o")

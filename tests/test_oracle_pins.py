@@ -507,6 +507,60 @@ def test_backward_matches_finite_differences(phi):
             check(inp["phi_v"][key], gr["dphi_v"][key])
 
 
+def test_independent_kv_per_branch_reduces_to_shared():
+    # the same tensors passed as every branch's own keys/values: forward is
+    # unchanged and the per-branch gradients add up to the shared ones
+    p, inp = small_problem(T=70, phi="mlp", seed=4)
+    base = O.forward(p, **inp)
+    kv = (inp["k"], inp["v"])
+    split = O.forward(p, **inp, kv_slc=kv, kv_win=kv)
+    np.testing.assert_array_equal(split["o"], base["o"])
+    np.testing.assert_array_equal(split["idx"], base["idx"])
+    rng = np.random.default_rng(2)
+    d_o = rng.standard_normal(base["o"].shape)
+    g0 = O.backward(p, d_o=d_o, idx=base["idx"], **inp)
+    g1 = O.backward(p, d_o=d_o, idx=base["idx"], **inp, kv_slc=kv, kv_win=kv)
+    np.testing.assert_allclose(g1["dk"] + g1["dk_slc"] + g1["dk_win"], g0["dk"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(g1["dv"] + g1["dv_slc"] + g1["dv_win"], g0["dv"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(g1["dq"], g0["dq"])
+
+
+def test_independent_kv_backward_matches_finite_differences():
+    p, inp = small_problem(B=1, T=26, Hkv=2, G=2, dk=3, dv=2, C=4, phi="mlp", l=4, d=2,
+                           l_sel=8, n=3, w=5, hidden=4, seed=13)
+    p = O.Params(l=4, d=2, l_sel=8, n=3, w=5, phi="mlp", io=None)
+    rng = np.random.default_rng(6)
+    kv_s = (rng.standard_normal(inp["k"].shape), rng.standard_normal(inp["v"].shape))
+    kv_w = (rng.standard_normal(inp["k"].shape), rng.standard_normal(inp["v"].shape))
+    d_o = rng.standard_normal((1, 26, 4, 2))
+    idx = O.forward(p, **inp, kv_slc=kv_s, kv_win=kv_w)["idx"]
+    gr = O.backward(p, d_o=d_o, idx=idx, **inp, kv_slc=kv_s, kv_win=kv_w)
+    eps = 1e-6
+
+    def loss():
+        return float((O.forward(p, **inp, idx=idx, kv_slc=kv_s, kv_win=kv_w)["o"] * d_o).sum())
+
+    def check(arr, grad, n_pick=10):
+        flat = arr.reshape(-1)
+        for i in rng.choice(flat.size, size=min(n_pick, flat.size), replace=False):
+            old = flat[i]
+            flat[i] = old + eps
+            lp = loss()
+            flat[i] = old - eps
+            lm = loss()
+            flat[i] = old
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - grad.reshape(-1)[i]) < 1e-6 + 1e-6 * abs(fd), (i, fd, grad.reshape(-1)[i])
+
+    check(inp["k"], gr["dk"])
+    check(inp["v"], gr["dv"])
+    check(kv_s[0], gr["dk_slc"])
+    check(kv_s[1], gr["dv_slc"])
+    check(kv_w[0], gr["dk_win"])
+    check(kv_w[1], gr["dv_win"])
+    check(inp["q"], gr["dq"])
+
+
 def test_dq_rows_matches_finite_differences():
     """Per-row dq (used where the whole backward is too large for the oracle)
     against central differences of the loss in q at those rows."""
