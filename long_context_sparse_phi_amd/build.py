@@ -31,9 +31,15 @@ SOURCES = ["nsa_api.cpp", "nsa_phi.hip", "nsa_cmp.hip", "nsa_attn.hip", "nsa_dec
            "nsa_append.hip"]
 
 
+# Per-file additions.  The compressed-branch kernels never carry NaN through
+# their softmax (masked scores are -inf, never NaN), so max/min need no NaN
+# quieting there.
+FILE_FLAGS = {"nsa_cmp.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-8000:]}")

@@ -127,8 +127,14 @@ struct SlcCursor {
   int si, kt, lo, kend;
 };
 
+// Register tiles in flight per wave.  bf16 tiles are small enough for a ring
+// of four at one wave per SIMD (three tiles' loads in flight while one is
+// computed: the gather is bound by how many bytes are outstanding); fp32 keeps
+// two tiles at two waves per SIMD.
+template <typename T> constexpr int slc_depth() { return sizeof(T) == 2 ? 4 : 2; }
+
 template <typename T, int DK, int DV, typename OT>
-__global__ __launch_bounds__(256, 2) void k_slc(Dims dm, SlcArgs a) {
+__global__ __launch_bounds__(256, slc_depth<T>() > 2 ? 1 : 2) void k_slc(Dims dm, SlcArgs a) {
   constexpr int NK = kvf_nk<DK, DV>(), NI = kvf_ni<DK, DV>();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, qd = lane >> 4;
@@ -221,24 +227,38 @@ __global__ __launch_bounds__(256, 2) void k_slc(Dims dm, SlcArgs a) {
     }
   };
 
-  // Two register tiles in flight: the next tile's loads are issued before the
-  // current tile is computed, so memory latency overlaps the MFMA work.
-  SlcTile<T, DK, DV> ta, tb;
-  SlcCursor ca{0, 0, 0, 0};
-  open_block(ca);
-  if (ca.si < dm.n) load_tile(ta, ca);
-  while (ca.si < dm.n) {
-    SlcCursor cb = ca;
-    advance(cb);
-    if (cb.si < dm.n) load_tile(tb, cb);
-    __builtin_amdgcn_sched_barrier(0);
-    compute_tile(ta, ca);
-    if (cb.si >= dm.n) break;
-    ca = cb;
-    advance(ca);
-    if (ca.si < dm.n) load_tile(ta, ca);
-    __builtin_amdgcn_sched_barrier(0);
-    compute_tile(tb, cb);
+  // A ring of DEPTH register tiles, consumed in load order: after a slot's
+  // tile is computed the slot is refilled with the tile DEPTH positions
+  // further on, so DEPTH-1 tiles' loads are in flight during every compute.
+  constexpr int DEPTH = slc_depth<T>();
+  SlcTile<T, DK, DV> ring[DEPTH];
+  SlcCursor rc[DEPTH];
+  SlcCursor lc{0, 0, 0, 0};
+  open_block(lc);
+#pragma unroll
+  for (int r = 0; r < DEPTH; ++r) {
+    rc[r] = lc;
+    if (lc.si < dm.n) {
+      load_tile(ring[r], lc);
+      advance(lc);
+    }
+  }
+  bool more = rc[0].si < dm.n;
+  while (more) {
+#pragma unroll
+    for (int r = 0; r < DEPTH; ++r) {
+      if (more) {
+        __builtin_amdgcn_sched_barrier(0);
+        compute_tile(ring[r], rc[r]);
+        __builtin_amdgcn_sched_barrier(0);
+        rc[r] = lc;
+        if (lc.si < dm.n) {
+          load_tile(ring[r], lc);
+          advance(lc);
+        }
+        more = rc[(r + 1) % DEPTH].si < dm.n;
+      }
+    }
   }
   float tot = ls + xor16f(ls, lane);
   tot += xor32f(tot, lane);

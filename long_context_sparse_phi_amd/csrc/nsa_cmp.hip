@@ -13,9 +13,12 @@
 // log-sum-exp over the visible compressed keys; pass B recomputes the scores,
 // forms exact probabilities, accumulates O_cmp = P V_cmp, remaps P onto
 // selection blocks with one more MFMA (P times the constant 0/1/2 overlap
-// matrix, with P split into bf16 hi + lo parts so the scores keep ~16
-// significant bits), sums over heads with cross-lane adds, keeps each
-// position's score row in LDS and runs the top-n selection there.
+// matrix; for bf16 inputs P enters it in fp16, 11 significant bits, which
+// keeps a score's relative error near 1e-5 after the sums), sums over heads
+// with cross-lane adds, keeps each position's score row in LDS and runs the
+// top-n selection there.  Pass B evaluates P scaled by 2^14 (one exponent
+// offset) so that small probabilities stay in fp16's normal range; the scale
+// is removed from O and from the scores when they are stored.
 //
 // Layout of the work: a wave owns 16*NCT query columns = (positions x G heads
 // of one KV group); MFMA tiles compute S^T = K Q^T (16 keys x 16 columns) so
@@ -38,6 +41,8 @@ namespace nsa {
 // (in registers) while the current tile is computed from LDS.
 // ---------------------------------------------------------------------------
 constexpr int kCmpKT = 64;               // keys per LDS tile
+constexpr float kPScale2 = 14.f;         // pass B evaluates P * 2^kPScale2
+constexpr float kPScaleInv = 1.f / 16384.f;
 constexpr int kCmpVS = kCmpKT + 8;       // LDS row stride of the V^T tile (elements)
 
 // K tile rows are unpadded with XOR-swizzled 16-byte chunks (kchunk_off).
@@ -46,15 +51,18 @@ constexpr size_t cmp_tile_elems() {
   return (size_t)kCmpKT * DK + (PB ? (size_t)DV * kCmpVS : 0);
 }
 
-template <typename T, int DK, int DV, int NCT, int NW, bool PB, typename OT>
-__global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nselp, int njt) {
+// GS, NJ: group size and number of 16-block remap column tiles fixed at
+// compile time (0: read from the arguments).
+template <typename T, int DK, int DV, int NCT, int NW, bool PB, typename OT, int GS, int NJ>
+__global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nselp, int njt_arg) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   constexpr size_t TE = cmp_tile_elems<T, DK, DV, PB>();
   constexpr int NT = NW * 64;
   T* tiles = (T*)smem_raw;                                  // [2][TE]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, qd = lane >> 4;
-  const int G = dm.G, PW = 16 * NCT / G, PWG = NW * PW;
+  const int G = GS ? GS : dm.G, PW = 16 * NCT / G, PWG = NW * PW;
+  const int njt = NJ ? NJ : njt_arg;
   const int ntiles = (dm.T + PWG - 1) / PWG;
   int unit, tile;
   xcd_map(blockIdx.x, dm.B * dm.Hkv, ntiles, unit, tile);
@@ -82,19 +90,23 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
     const bool v = pos[ct] < dm.T;
     nvis[ct] = v ? ncmp_visible(pos[ct], dm.l, dm.d) : 0;
     const size_t row = (size_t)(b * dm.T + min(pos[ct], dm.T - 1)) * dm.Hq + hq[ct];
-    lse2[ct] = (PB && v && nvis[ct] > 0) ? a.lse[row] * kLog2e : 0.f;
+    lse2[ct] = (PB && v && nvis[ct] > 0) ? a.lse[row] * kLog2e - kPScale2 : 0.f;
     const T* qp = q + row * DK + qd * 8;
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) qf[ct][ks] = v ? load_frag(qp + ks * 32) : zero_frag<T>();
   }
+  // remap weights: fp16 operands for bf16 inputs, fp32 for fp32 inputs
+  constexpr bool kF16Remap = sizeof(T) == 2;
   Frag8<T> wf[2];
+  f16x8 wh[2];
   if (PB) {
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt) {
       float w[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) w[e] = jt < njt ? remap_weight(qd * 8 + e, jt * 16 + c16, dm.l, dm.d, dm.ls) : 0.f;
-      wf[jt] = to_frag<T>(w);
+      if constexpr (kF16Remap) wh[jt] = to_f16x8(w);
+      else wf[jt] = to_frag<T>(w);
     }
   }
   const float sc2 = dm.scale * kLog2e;
@@ -174,24 +186,25 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
     }
   };
 
-  // pass A: online max / sum of exp2 per column
+  // pass A: online max / sum of exp2 per column.  The maximum is taken over
+  // the raw scores and scaled once (sc2 > 0), and each exponent is one fma.
   auto pass_a = [&](const f32x4 (&s)[2][NCT], int kt, auto masked) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      float v[8], mx = kNegInf;
+      float v[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        v[e] = s[e >> 2][ct][e & 3] * sc2;
+        v[e] = s[e >> 2][ct][e & 3];
         if (masked) v[e] = kt + qd * 8 + e < nvis[ct] ? v[e] : kNegInf;
-        mx = fmaxf(mx, v[e]);
       }
+      float mx = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
       mx = fmaxf(mx, xor16f(mx, lane));
       mx = fmaxf(mx, xor32f(mx, lane));
-      const float mn = fmaxf(m[ct], mx);
+      const float mn = fmaxf(m[ct], mx * sc2);
       const float mref = mn == kNegInf ? 0.f : mn;
       float acc = ls[ct] * fast_exp2(m[ct] - mref);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc += fast_exp2(v[e] - mref);
+      for (int e = 0; e < 8; ++e) acc += fast_exp2(fmaf(v[e], sc2, -mref));
       ls[ct] = acc;
       m[ct] = mn;
     }
@@ -207,23 +220,24 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
       float p[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        p[e] = fast_exp2(s[e >> 2][ct][e & 3] * sc2 - lse2[ct]);
+        p[e] = fast_exp2(fmaf(s[e >> 2][ct][e & 3], sc2, -lse2[ct]));
         if (masked) p[e] = kt + qd * 8 + e < nvis[ct] ? p[e] : 0.f;
       }
       pf[ct] = to_frag<T>(p);
-      // remap onto selection blocks: P (hi + lo) times the overlap weights
-      Frag8<T> plo;
-      if constexpr (sizeof(T) == 2) {
+      if constexpr (kPrecisePV<T, OT>) plo_all[ct] = lo_frag(p, pf[ct]);
+      // remap onto selection blocks: P times the overlap weights
+      if constexpr (kF16Remap) {
+        const f16x8 ph = to_f16x8(p);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) plo.v[e] = (bf16)(p[e] - (float)pf[ct].v[e]);
-      }
-      plo_all[ct] = plo;
+        for (int jt = 0; jt < 2; ++jt) {
+          cr[ct][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (jt < njt) mma(cr[ct][jt], ph, wh[jt]);
+        }
+      } else {
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        cr[ct][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (jt < njt) {
-          mma(cr[ct][jt], pf[ct], wf[jt]);
-          if constexpr (sizeof(T) == 2) mma(cr[ct][jt], plo, wf[jt]);
+        for (int jt = 0; jt < 2; ++jt) {
+          cr[ct][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (jt < njt) mma(cr[ct][jt], pf[ct], wf[jt]);
         }
       }
     }
@@ -258,7 +272,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
         }
         if (writer) {
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) prow[rowoff[ct][0] + j] += v[ct];
+          for (int ct = 0; ct < NCT; ++ct) atomicAdd(prow + rowoff[ct][0] + j, v[ct]);
         }
       } else if (G == 2) {
 #pragma unroll
@@ -286,18 +300,27 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
     if (it + 1 < nkt) gload(kt0 + kCmpKT);
     const T* ktile = tiles + (size_t)(it & 1) * TE;
     const T* vtile = ktile + (size_t)kCmpKT * DK;
+    // With few column tiles both halves' scores are issued before either
+    // half's softmax work, so the second half's MFMAs run under the first
+    // half's VALU work (four column tiles have no registers for that).
+    constexpr bool kEarly = NCT <= 2;
+    f32x4 s[2][2][NCT];
+    if (kEarly) {
+      if (kt0 < nmax) scores(ktile, 0, s[0]);
+      if (kt0 + 32 < nmax) scores(ktile, 1, s[1]);
+    }
+#pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int kt = kt0 + h * 32;
       if (kt >= nmax) break;
-      f32x4 s[2][NCT];
-      scores(ktile, h, s);
+      if (!kEarly) scores(ktile, h, s[h]);
       const bool full = kt + 32 <= nfull;
       if constexpr (!PB) {
-        if (full) pass_a(s, kt, std::false_type{});
-        else pass_a(s, kt, std::true_type{});
+        if (full) pass_a(s[h], kt, std::false_type{});
+        else pass_a(s[h], kt, std::true_type{});
       } else {
-        if (full) pass_b(s, vtile, h, kt, std::false_type{});
-        else pass_b(s, vtile, h, kt, std::true_type{});
+        if (full) pass_b(s[h], vtile, h, kt, std::false_type{});
+        else pass_b(s[h], vtile, h, kt, std::true_type{});
       }
     }
     if (it + 1 < nkt) lstore((it + 1) & 1);
@@ -321,7 +344,8 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
       OT* op = o + ((size_t)(b * dm.T + pos[ct]) * dm.Hq + hq[ct]) * DV + qd * 4;
 #pragma unroll
       for (int dt = 0; dt < DV / 16; ++dt)
-        store4(op + dt * 16, oacc[dt][ct][0], oacc[dt][ct][1], oacc[dt][ct][2], oacc[dt][ct][3]);
+        store4(op + dt * 16, oacc[dt][ct][0] * kPScaleInv, oacc[dt][ct][1] * kPScaleInv,
+               oacc[dt][ct][2] * kPScaleInv, oacc[dt][ct][3] * kPScaleInv);
     }
     // top-n per position of this wave
     for (int pl = 0; pl < PW; ++pl) {
@@ -331,7 +355,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
       const size_t rbase = (size_t)(b * dm.T + t) * dm.Hkv + g;
       if (a.p_slc) {
         float* ps = a.p_slc + rbase * dm.nsel;
-        for (int j = lane; j < dm.nsel; j += 64) ps[j] = row[j];
+        for (int j = lane; j < dm.nsel; j += 64) ps[j] = row[j] * kPScaleInv;
       }
       wave_topn(row, t, dm.ls, dm.n, a.idx + rbase * dm.n, lane);
     }
@@ -349,7 +373,10 @@ static size_t cmp_lds(const Dims& dm, int nw, int nct, int nselp) {
 
 template <typename T, int DK, int DV, int NCT, int NW, bool PB, typename OT>
 static hipError_t cmp_launch(const Dims& dm, const CmpArgs& a, int nselp, int njt, size_t lds, hipStream_t s) {
-  auto kfn = k_cmp<T, DK, DV, NCT, NW, PB, OT>;
+  // the common configuration (16 heads per group, one remap column tile) is
+  // compiled with both fixed
+  auto kfn = (dm.G == 16 && njt == 1 && NCT > 1) ? k_cmp<T, DK, DV, NCT, NW, PB, OT, 16, 1>
+                                                 : k_cmp<T, DK, DV, NCT, NW, PB, OT, 0, 0>;
   if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   const int PWG = NW * 16 * NCT / dm.G;
   const int ntiles = (dm.T + PWG - 1) / PWG;

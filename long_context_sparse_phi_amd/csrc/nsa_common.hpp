@@ -111,6 +111,17 @@ __device__ __forceinline__ void mma(f32x4& c, const Frag8<float>& a, const Frag8
   for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[e], b.hi[e], c, 0, 0, 0);
 }
 
+// fp16 operands (v_mfma_f32_16x16x32_f16, same lane layout as bf16).
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x8v __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f16x8 to_f16x8(const float* x) {
+  const f32x8v v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+  return __builtin_convertvector(v, f16x8);
+}
+__device__ __forceinline__ void mma(f32x4& c, const f16x8& a, const f16x8& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
 // 8 fp32 values -> operand fragment of element type T (round to nearest even).
 __device__ __forceinline__ Frag8<bf16> to_frag_bf16(const float* x) {
   Frag8<bf16> f;
