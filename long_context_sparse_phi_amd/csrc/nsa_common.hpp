@@ -364,113 +364,110 @@ __device__ inline void wave_topn(float* row, int t, int ls, int n, int* out, int
   for (int e = cnt + lane; e < n; e += 64) out[e] = -1;
 }
 
-// The same selection by a whole workgroup of NW waves (NW*64 threads).
-// Stage 1: each wave keeps a contiguous slice of the candidates in registers
-// (KPL per lane) and extracts its local top (n-3) by repeated wave argmax;
-// stage 2: wave 0 takes the top (n-3) of the NW*(n-3) finalists (FPL per
-// lane).  The order is total (score, then index), so the result equals
-// wave_topn's.  fs/fj: LDS scratch of NW*(n-3) finalists.  The caller
-// synchronises the workgroup before (row complete) and after.
-template <int NW, int KPL, int FPL>
-__device__ inline void block_topn_impl(float* row, int jc, int n, int* out, float* fs, int* fj, int tid) {
-  const int lane = tid & 63, wave = tid >> 6;
-  const int R = (jc + 1 + NW - 1) / NW;
-  const int m = n - 3;
-  {
-    const int j0 = wave * R, j1 = min(jc + 1, j0 + R);
-    float ks[KPL];
-    int kj[KPL];
-    float ms = -__builtin_inff();
-    int mj = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-      const int j = j0 + lane + 64 * i;
-      const bool ok = j < j1 && j != 0 && j != jc - 1 && j != jc;
-      ks[i] = ok ? row[j] : -__builtin_inff();
-      kj[i] = j;
-      if (topn_better(ks[i], kj[i], ms, mj)) { ms = ks[i]; mj = kj[i]; }
-    }
-    for (int r = 0; r < m; ++r) {
-      float bs;
-      int bj;
-      wave_argmax(ms, mj, bs, bj);
-      if (lane == 0) { fs[wave * m + r] = bs; fj[wave * m + r] = bj; }
-      if (bs == -__builtin_inff()) continue;
-      if (mj == bj) {
-        ms = -__builtin_inff();
-        mj = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < KPL; ++i) {
-          if (kj[i] == bj) ks[i] = -__builtin_inff();
-          if (topn_better(ks[i], kj[i], ms, mj)) { ms = ks[i]; mj = kj[i]; }
-        }
-      }
-    }
-  }
-  __syncthreads();
-  if (wave != 0) return;
-  const int F = NW * m;
-  float gs[FPL];
-  int gj[FPL];
-  float ms = -__builtin_inff();
-  int mj = 0x7fffffff;
-#pragma unroll
-  for (int i = 0; i < FPL; ++i) {
-    const int e = lane + 64 * i;
-    gs[i] = e < F ? fs[e] : -__builtin_inff();
-    gj[i] = e < F ? fj[e] : 0x7fffffff;
-    if (topn_better(gs[i], gj[i], ms, mj)) { ms = gs[i]; mj = gj[i]; }
-  }
-  if (lane == 0) { row[0] = -1.f; row[jc - 1] = -1.f; row[jc] = -1.f; }
-  for (int r = 0; r < m; ++r) {
-    float bs;
-    int bj;
-    wave_argmax(ms, mj, bs, bj);
-    if (bs == -__builtin_inff()) break;
-    if (mj == bj) {
-      row[bj] = -1.f;
-      ms = -__builtin_inff();
-      mj = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < FPL; ++i) {
-        if (gj[i] == bj) gs[i] = -__builtin_inff();
-        if (topn_better(gs[i], gj[i], ms, mj)) { ms = gs[i]; mj = gj[i]; }
-      }
-    }
-  }
-  int cnt = 0;
-  for (int jb = 0; jb <= jc; jb += 64) {
-    const int j = jb + lane;
-    const bool sel = j <= jc && row[j] < 0.f;
-    const uint64_t mk = __ballot(sel);
-    if (sel) out[cnt + __popcll(mk & ((1ull << lane) - 1ull))] = j;
-    cnt += __popcll(mk);
-  }
-  for (int e = cnt + lane; e < n; e += 64) out[e] = -1;
-}
-
-// fs / fj: LDS scratch of NW*29 floats and ints (n <= 32).
+// The same selection by a whole workgroup of NW waves (NW*64 threads), by
+// radix select instead of repeated argmax.  Scores are >= 0, so their bit
+// patterns order like the values.  Four passes over 8-bit digits, most
+// significant first, narrow down the bit pattern K of the r-th largest
+// non-forced score (r = n - 3) and how many of the scores equal to K are still
+// needed; those are the lowest-indexed ones (ties go to the lower index).  The
+// selected set, forced blocks included, is then written in ascending order.
+// sh: LDS scratch of 256 + NW + 4 ints.  The caller synchronises the workgroup
+// before (row complete) and after.
 template <int NW>
-__device__ inline void block_topn(float* row, int t, int ls, int n, int* out, float* fs, int* fj, int tid) {
+__device__ inline void block_topn(const float* row, int t, int ls, int n, int* out, int* sh, int tid) {
+  constexpr int NT = NW * 64;
   const int jc = t / ls;
   if (jc + 1 <= n) {
-    for (int e = tid; e < n; e += NW * 64) out[e] = e <= jc ? e : -1;
+    for (int e = tid; e < n; e += NT) out[e] = e <= jc ? e : -1;
     return;
   }
-  const int R = (jc + 1 + NW - 1) / NW;
-  const bool f4 = NW * (n - 3) <= 4 * 64;
-  constexpr int FMAX = (NW * 29 + 63) / 64;
-  if (R <= 64) {
-    if (f4) block_topn_impl<NW, 1, 4>(row, jc, n, out, fs, fj, tid);
-    else block_topn_impl<NW, 1, FMAX>(row, jc, n, out, fs, fj, tid);
-  } else if (R <= 4 * 64) {
-    if (f4) block_topn_impl<NW, 4, 4>(row, jc, n, out, fs, fj, tid);
-    else block_topn_impl<NW, 4, FMAX>(row, jc, n, out, fs, fj, tid);
-  } else if (R <= 16 * 64) {
-    block_topn_impl<NW, 16, FMAX>(row, jc, n, out, fs, fj, tid);
-  } else if ((tid >> 6) == 0) {
-    wave_topn(row, t, ls, n, out, tid & 63);
+  const int lane = tid & 63, wave = tid >> 6;
+  int* hist = sh;              // [256]
+  int* wcnt = sh + 256;        // [NW] per-wave counts
+  int* ctl = wcnt + NW;        // [0] digit prefix, [1] still needed, [2] running total
+  auto key = [&](int j) { return __float_as_uint(row[j]); };
+  auto forced = [&](int j) { return j == 0 || j == jc - 1 || j == jc; };
+  unsigned prefix = 0, mask = 0;
+  int need = n - 3;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += NT) hist[i] = 0;
+    __syncthreads();
+    for (int j = tid; j <= jc; j += NT) {
+      if (forced(j)) continue;
+      const unsigned u = key(j);
+      if ((u & mask) == prefix) atomicAdd(hist + ((u >> shift) & 255), 1);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      // lane L holds bins 255-4L .. 252-4L; counts are summed from the top
+      int h[4], sum = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { h[i] = hist[255 - 4 * lane - i]; sum += h[i]; }
+      int incl = sum;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+      }
+      int run = incl - sum;   // bins above this lane's
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (run < need && run + h[i] >= need) {
+          ctl[0] = 255 - 4 * lane - i;
+          ctl[1] = need - run;
+        }
+        run += h[i];
+      }
+    }
+    __syncthreads();
+    prefix |= (unsigned)ctl[0] << shift;
+    mask |= 255u << shift;
+    need = ctl[1];
+    __syncthreads();
   }
+  // Selection in index order: a score above K, or equal to K among the first
+  // `need` such indices, or a forced block.  Two workgroup prefix counts (over
+  // 'equal to K', then over 'selected') walk the candidates in chunks of NT.
+  if (tid == 0) { ctl[1] = 0; ctl[2] = 0; }
+  __syncthreads();
+  for (int j0 = 0; j0 <= jc; j0 += NT) {
+    const int j = j0 + tid;
+    const bool valid = j <= jc;
+    const unsigned u = valid ? key(j) : 0u;
+    const bool eq = valid && !forced(j) && u == prefix;
+    // rank of j among the equal scores
+    uint64_t bal = __ballot(eq);
+    if (lane == 0) wcnt[wave] = __popcll(bal);
+    __syncthreads();
+    int before = ctl[1];
+    for (int w = 0; w < wave; ++w) before += wcnt[w];
+    const int rank = before + __popcll(bal & ((1ull << lane) - 1ull));
+    const bool sel = valid && (forced(j) || u > prefix || (eq && rank < need));
+    __syncthreads();
+    if (tid == NT - 1) {
+      int tot = ctl[1];
+      for (int w = 0; w < NW; ++w) tot += wcnt[w];
+      ctl[1] = tot;
+    }
+    // position of j among the selected blocks
+    bal = __ballot(sel);
+    __syncthreads();
+    if (lane == 0) wcnt[wave] = __popcll(bal);
+    __syncthreads();
+    int pos = ctl[2];
+    for (int w = 0; w < wave; ++w) pos += wcnt[w];
+    pos += __popcll(bal & ((1ull << lane) - 1ull));
+    if (sel && pos < n) out[pos] = j;
+    __syncthreads();
+    if (tid == NT - 1) {
+      int tot = ctl[2];
+      for (int w = 0; w < NW; ++w) tot += wcnt[w];
+      ctl[2] = tot;
+    }
+    __syncthreads();
+  }
+  const int cnt = ctl[2];
+  for (int e = cnt + tid; e < n; e += NT) out[e] = -1;
 }
 
 }  // namespace nsa

@@ -38,7 +38,7 @@ template <int DK, int DV> constexpr int dec_depth() { return DK + DV >= 320 ? 3 
 // Launch plan for the cache capacity S (grid sizes, workspace layout); every
 // sequence then works within its own length (DecSeq).
 struct DecPlan {
-  int S, t, ncmp, nc, nb, jstep, nis, niw, ni, wlen, ws0;
+  int S, t, ncmp, nc, cpw, nb, jstep, nis, niw, ni, wlen, ws0;
 };
 
 static DecPlan dec_plan(const Dims& dm) {
@@ -47,6 +47,10 @@ static DecPlan dec_plan(const Dims& dm) {
   p.t = dm.T - 1;
   p.ncmp = dm.ncmp;
   p.nc = (dm.ncmp + kDecCK - 1) / kDecCK;
+  // chunks per wave: about one wave per SIMD over the whole batch
+  const long long chunks = (long long)dm.B * dm.Hkv * p.nc;
+  p.cpw = 1;
+  while (p.nc % (2 * p.cpw) == 0 && chunks / (2 * p.cpw) >= 1024) p.cpw *= 2;
   p.nb = (31 * dm.d + dm.l - 1) / dm.ls + 1;
   p.jstep = 32 * dm.d / dm.ls;
   p.nis = dm.n;
@@ -198,19 +202,23 @@ struct DecTile {
   }
 };
 
-// Chunk of CK compressed keys per wave, one pass with an online softmax: per
-// tile the scores, the running per-head maximum, P V, and the remapped block
-// scores relative to that running maximum, stored with it; the combine scales
-// each tile's scores by exp2(max - lse).
+// Chunks of CK compressed keys, one pass with an online softmax: per tile the
+// scores, the running per-head maximum, P V, and the remapped block scores
+// relative to that running maximum, stored with it; the combine scales each
+// tile's scores by exp2(max - lse).  A wave streams pl.cpw consecutive chunks
+// of one (sequence, KV head) through a single ring of register tiles, so the
+// ring stays full across chunk boundaries; each chunk's softmax state is
+// written when its last tile is done.
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(64, 1) void k_dec_cmp(Dims dm, DecArgs a, DecPlan pl) {
   using Tile = DecTile<T, DK, DV>;
   __shared__ __align__(16) T tile[Tile::elems];
   const int lane = threadIdx.x, c16 = lane & 15, qd = lane >> 4;
-  const int c = blockIdx.x % pl.nc, bg = blockIdx.x / pl.nc;
+  const int wpb = pl.nc / pl.cpw;
+  const int c0 = (blockIdx.x % wpb) * pl.cpw, bg = blockIdx.x / wpb;
   const int b = bg / dm.Hkv, g = bg % dm.Hkv;
   const int ncmp = dec_seq(dm, a, b).ncmp;
-  const int k0 = c * kDecCK, k1 = min(k0 + kDecCK, ncmp);
+  const int k0 = c0 * kDecCK, k1 = min(k0 + pl.cpw * kDecCK, ncmp);
   const int ntile = k1 > k0 ? (k1 - k0 + 31) / 32 : 0;
   const bool cv = c16 < dm.G;
   Frag8<T> qf[DK / 32];
@@ -236,11 +244,29 @@ __global__ __launch_bounds__(64, 1) void k_dec_cmp(Dims dm, DecArgs a, DecPlan p
 #pragma unroll
   for (int dt = 0; dt < DV / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = kNegInf, lsum = 0.f;
-  float* ps = a.w.part_ps + ((size_t)bg * pl.nc + c) * kDecTPC * pl.nb * 16;
-  float* tm = a.w.part_tm + ((size_t)bg * pl.nc + c) * kDecTPC * 16;
-  // two tiles in flight in registers while the current one is computed from LDS
+  // softmax state of chunk c: maximum, sum and unnormalised P V; then reset
+  auto finish_chunk = [&](int c) {
+    float l = lsum + xor16f(lsum, lane);
+    l += xor32f(l, lane);
+    const size_t hb = ((size_t)bg * pl.nc + c) * 16 + c16;
+    if (qd == 0) {
+      a.w.part_ml[hb * 2 + 0] = m;
+      a.w.part_ml[hb * 2 + 1] = l;
+    }
+    float* op = a.w.part_o + hb * DV + qd * 4;
+#pragma unroll
+    for (int dt = 0; dt < DV / 16; ++dt) {
+      store4(op + dt * 16, oacc[dt][0], oacc[dt][1], oacc[dt][2], oacc[dt][3]);
+      oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    m = kNegInf;
+    lsum = 0.f;
+  };
   auto compute = [&](int i) {
     const int kt = k0 + 32 * i;
+    const int c = c0 + i / kDecTPC, ti = i % kDecTPC;
+    float* ps = a.w.part_ps + (((size_t)bg * pl.nc + c) * kDecTPC + ti) * pl.nb * 16;
+    float* tm = a.w.part_tm + (((size_t)bg * pl.nc + c) * kDecTPC + ti) * 16;
     f32x4 s[2];
     Tile::scores(s, tile, qf, krow, qd);
     float v[8], mx = kNegInf;
@@ -259,7 +285,7 @@ __global__ __launch_bounds__(64, 1) void k_dec_cmp(Dims dm, DecArgs a, DecPlan p
     for (int e = 0; e < 8; ++e) { p[e] = fast_exp2(v[e] - mref); psum += p[e]; }
     lsum = lsum * alpha + psum;
     m = mn;
-    if (qd == 0) tm[i * 16 + c16] = mn;
+    if (qd == 0) tm[c16] = mn;
     const Frag8<T> pf = to_frag<T>(p);
 #pragma unroll
     for (int dt = 0; dt < DV / 16; ++dt) {
@@ -275,10 +301,11 @@ __global__ __launch_bounds__(64, 1) void k_dec_cmp(Dims dm, DecArgs a, DecPlan p
       mma(cr, phi, wf[jt]);
       if constexpr (sizeof(T) == 2) mma(cr, plo, wf[jt]);
       const int jj = jt * 16 + c16;
-      if (jj < pl.nb) store4(ps + ((size_t)i * pl.nb + jj) * 16 + qd * 4, cr[0], cr[1], cr[2], cr[3]);
+      if (jj < pl.nb) store4(ps + (size_t)jj * 16 + qd * 4, cr[0], cr[1], cr[2], cr[3]);
     }
+    if (ti == kDecTPC - 1 || i == ntile - 1) finish_chunk(c);
   };
-  // a ring of kDecDepth tiles in flight in registers while the current one is
+  // a ring of DEPTH tiles in flight in registers while the current one is
   // computed from LDS (one wave per SIMD, most of its registers hold loads)
   constexpr int DEPTH = dec_depth<DK, DV>();
   auto step = [&](Tile& cur, int i) {
@@ -297,16 +324,8 @@ __global__ __launch_bounds__(64, 1) void k_dec_cmp(Dims dm, DecArgs a, DecPlan p
     for (int r = 0; r < DEPTH; ++r)
       if (i + r < ntile) step(ring[r], i + r);
   }
-  lsum += xor16f(lsum, lane);
-  lsum += xor32f(lsum, lane);
-  const size_t hb = ((size_t)bg * pl.nc + c) * 16 + c16;
-  if (qd == 0) {
-    a.w.part_ml[hb * 2 + 0] = m;
-    a.w.part_ml[hb * 2 + 1] = lsum;
-  }
-  float* op = a.w.part_o + hb * DV + qd * 4;
-#pragma unroll
-  for (int dt = 0; dt < DV / 16; ++dt) store4(op + dt * 16, oacc[dt][0], oacc[dt][1], oacc[dt][2], oacc[dt][3]);
+  // chunks past the sequence's compressed blocks hold an empty state
+  for (int c = c0 + (ntile + kDecTPC - 1) / kDecTPC; c < c0 + pl.cpw; ++c) finish_chunk(c);
 }
 
 // Element i of an I/O tensor as float.
@@ -314,22 +333,24 @@ __device__ __forceinline__ float load_elem(const void* p, int io, size_t i) {
   return io == IO_BF16 ? (float)((const bf16*)p)[i] : ((const float*)p)[i];
 }
 
+// Length of the combine's LDS score row.
+static __host__ __device__ int comb_row_len(const Dims& dm) { return (dm.nsel + 3) & ~3; }
+
 // One workgroup (1024 threads) per (sequence, KV head): per-head log-sum-exp
 // of the compressed branch, per-chunk scales, block scores and top-n.
 __global__ __launch_bounds__(1024) void k_dec_combine(Dims dm, DecArgs a, DecPlan pl) {
   extern __shared__ float smem[];
-  float* row = smem;                          // [nsel]
-  float* scl = row + ((dm.nsel + 3) & ~3);    // [nc][16]
+  float* row = smem;                          // [nsel] block scores
+  float* scl = row + comb_row_len(dm);        // [nc][16]
   float* lse2 = scl + pl.nc * 16;             // [16]
   float* mls = lse2 + 16;                     // [nc][16] chunk maxima
   float* lsl = mls + pl.nc * 16;              // [nc][16] chunk sums
-  float* fs = lsl + pl.nc * 16;               // [16*29] top-n finalists: scores
-  int* fj = (int*)(fs + 16 * 29);             // [16*29] and indices
+  int* tsh = (int*)(lsl + pl.nc * 16);        // [256 + 16 + 4] top-n scratch
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bg = blockIdx.x, b = bg / dm.Hkv, g = bg % dm.Hkv;
   const int G = dm.G;
   const DecSeq sq = dec_seq(dm, a, b);
-  // gate inputs of head `wave`, requested now and used at the end
+  // gate inputs of head `wave`, requested after the chunk states and used at the end
   float gx[4], gw[4][3];
   auto gate_load = [&](int k0) {
     const int h = g * G + min(wave, G - 1);
@@ -341,12 +362,12 @@ __global__ __launch_bounds__(1024) void k_dec_combine(Dims dm, DecArgs a, DecPla
       for (int c = 0; c < 3; ++c) gw[u][c] = k < dm.C ? load_elem(a.wg, dm.io, ((size_t)k * dm.Hq + h) * 3 + c) : 0.f;
     }
   };
-  gate_load(0);
   for (int i = tid; i < pl.nc * 16; i += 1024) {
     const size_t hb = (size_t)bg * pl.nc * 16 + i;
     mls[i] = a.w.part_ml[hb * 2];
     lsl[i] = a.w.part_ml[hb * 2 + 1];
   }
+  gate_load(0);
   __syncthreads();
   // per-head log-sum-exp: wave h reduces head h over the chunks
   {
@@ -411,7 +432,7 @@ __global__ __launch_bounds__(1024) void k_dec_combine(Dims dm, DecArgs a, DecPla
   if (a.p_slc)
     for (int j = tid; j < dm.nsel; j += 1024) a.p_slc[(size_t)bg * dm.nsel + j] = row[j];
   __syncthreads();
-  block_topn<16>(row, sq.t, dm.ls, dm.n, a.w.idx + (size_t)bg * dm.n, fs, fj, tid);
+  block_topn<16>(row, sq.t, dm.ls, dm.n, a.w.idx + (size_t)bg * dm.n, tsh, tid);
   // gates of the group's heads: wave h, lanes over the gate input, the three
   // branches together; the first 256 inputs were loaded at the start
   if (wave < G) {
@@ -615,13 +636,12 @@ static hipError_t decode_impl(const Dims& dm, const DecArgs& a, const DecPlan& p
   const int BG = dm.B * dm.Hkv;
   if ((e = mark()) != hipSuccess) return e;
   if (pl.nc > 0) {
-    k_dec_cmp<T, DK, DV><<<BG * pl.nc, 64, 0, s>>>(dm, a, pl);
+    k_dec_cmp<T, DK, DV><<<BG * (pl.nc / pl.cpw), 64, 0, s>>>(dm, a, pl);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = mark()) != hipSuccess) return e;
   {
-    const size_t lds = (((size_t)dm.nsel + 3) & ~(size_t)3) * 4 + (size_t)pl.nc * 16 * 4 * 3 + 16 * 4 +
-                       2 * 16 * 29 * 4;
+    const size_t lds = (size_t)comb_row_len(dm) * 4 + (size_t)pl.nc * 16 * 4 * 3 + 16 * 4 + (256 + 16 + 4) * 4;
     if (lds > 64 * 1024)
       hipFuncSetAttribute((const void*)k_dec_combine, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     k_dec_combine<<<BG, 1024, lds, s>>>(dm, a, pl);
