@@ -210,8 +210,10 @@ __device__ __forceinline__ void dq_tile(DqState<T, DK, DV>& st, const T* tb, int
 }
 
 // ROWSUM = true: per row and branch, dg_c = sum_k P_k (dO . v_k) = <dO, O_c>,
-// written as D_c = g_c dg_c and dz_c = dg_c g_c (1 - g_c).  ROWSUM = false: dq.
-template <typename T, int DK, int DV, bool ROWSUM>
+// written as D_c = g_c dg_c and dz_c = dg_c g_c (1 - g_c).  ROWSUM = false: dq
+// of the branches in BR (1 compressed, 2 selected, 4 window), added to dq when
+// ACC.
+template <typename T, int DK, int DV, bool ROWSUM, int BR = 7, bool ACC = false>
 __global__ __launch_bounds__(256) void k_bwd_dq(Dims dm, BwdArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c16 = lane & 15, qd = lane >> 4;
@@ -250,7 +252,7 @@ __global__ __launch_bounds__(256) void k_bwd_dq(Dims dm, BwdArgs a) {
   float rsum[3] = {0.f, 0.f, 0.f};
   const int TI = 2 * DK / 32 + 2 * DV / 32 + DK / 16;
   // compressed branch
-  {
+  if (BR & 1) {
     const int nv = ncmp_visible(t, dm.l, dm.d);
     const T* fb = (const T*)a.w.fckv + (size_t)(b * dm.Hkv + g) * ((dm.ncmp + 31) / 32) * TI * 512 + lane * 8;
     for (int kt = 0; kt < nv; kt += 32)
@@ -261,7 +263,7 @@ __global__ __launch_bounds__(256) void k_bwd_dq(Dims dm, BwdArgs a) {
   }
   const T* fb = (const T*)a.w.fkv + (size_t)(b * dm.Hkv + g) * ((dm.T + 31) / 32) * TI * 512 + lane * 8;
   // selected branch
-  {
+  if (BR & 2) {
     const int* ids = a.idx + ((size_t)(b * dm.T + t) * dm.Hkv + g) * dm.n;
     for (int si = 0; si < dm.n; ++si) {
       const int j = ids[si];
@@ -275,7 +277,7 @@ __global__ __launch_bounds__(256) void k_bwd_dq(Dims dm, BwdArgs a) {
     st.rs = 0.f;
   }
   // window branch
-  {
+  if (BR & 4) {
     const T* fw = (const T*)a.fkv_win + (size_t)(b * dm.Hkv + g) * ((dm.T + 31) / 32) * TI * 512 + lane * 8;
     const int lo = max(0, t - dm.w + 1);
     for (int kt = lo & ~31; kt <= t; kt += 32)
@@ -298,9 +300,346 @@ __global__ __launch_bounds__(256) void k_bwd_dq(Dims dm, BwdArgs a) {
   if (cv) {
     float* out = a.dq + row * DK + qd * 4;
 #pragma unroll
+    for (int dt = 0; dt < DK / 16; ++dt) {
+      float v[4] = {dm.scale * st.dq[dt][0], dm.scale * st.dq[dt][1], dm.scale * st.dq[dt][2],
+                    dm.scale * st.dq[dt][3]};
+      if (ACC) {
+        float o[4];
+        load4(out + dt * 16, o);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] += o[r];
+      }
+      store4(out + dt * 16, v[0], v[1], v[2], v[3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dq of the selected branch, added to dq: one wave per (b, t, g) as above, but
+// the (block, 32-key tile) sequence of the position runs through a ring of
+// DEPTH register tiles, so several tiles' gathers are in flight while one is
+// computed (the branch is bound by how many bytes are outstanding).
+// ---------------------------------------------------------------------------
+template <typename T, int DK, int DV>
+constexpr int dqs_depth() {
+  return (2 * DK / 32 + 2 * DV / 32 + DK / 16) * (sizeof(T) == 2 ? 4 : 8) * 3 <= 300 ? 3 : 2;
+}
+
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(256, 1) void k_bwd_dq_slc(Dims dm, BwdArgs a) {
+  constexpr int NKK = 2 * DK / 32, NKV = 2 * DV / 32, TI = NKK + NKV + DK / 16;
+  constexpr int DEPTH = dqs_depth<T, DK, DV>();
+  struct Tile { Frag8<T> f[TI]; };
+  struct Cur { int si, kt, lo, kend; };
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c16 = lane & 15, qd = lane >> 4;
+  const int ntiles = (dm.T + 3) / 4;
+  int unit, tile;
+  xcd_map(blockIdx.x, dm.B * dm.Hkv, ntiles, unit, tile);
+  const int b = unit / dm.Hkv, g = unit % dm.Hkv;
+  const int t = tile * 4 + wave;
+  if (t >= dm.T) return;
+  const int G = dm.G;
+  const bool cv = c16 < G;
+  const int hq = g * G + (cv ? c16 : 0);
+  const size_t BTH = (size_t)dm.B * dm.T * dm.Hq;
+  const size_t row = (size_t)(b * dm.T + t) * dm.Hq + hq;
+  Frag8<T> qf[DK / 32], dof[DV / 32];
+  f32x4 dq[DK / 16];
+  {
+    const T* qp = (const T*)a.q + row * DK + qd * 8;
+    const T* dp = (const T*)a.d_o + row * DV + qd * 8;
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) qf[ks] = cv ? load_frag(qp + ks * 32) : zero_frag<T>();
+#pragma unroll
+    for (int ks = 0; ks < DV / 32; ++ks) dof[ks] = cv ? load_frag(dp + ks * 32) : zero_frag<T>();
+#pragma unroll
+    for (int dt = 0; dt < DK / 16; ++dt) dq[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float sc2 = dm.scale * kLog2e;
+  const float lraw = cv ? a.lse[BTH + row] : 0.f;
+  const float lse2 = lraw == kNegInf ? 0.f : lraw * kLog2e;
+  const float gc = cv ? a.w.gates[row * 3 + 1] : 0.f;
+  const float Dc = cv ? a.w.Dc[BTH + row] : 0.f;
+  const int* ids = a.idx + ((size_t)(b * dm.T + t) * dm.Hkv + g) * dm.n;
+  const int myid = lane < dm.n ? ids[lane] : -1;
+  const T* fb = (const T*)a.w.fkv + (size_t)(b * dm.Hkv + g) * ((dm.T + 31) / 32) * TI * 512 + lane * 8;
+  auto open_block = [&](Cur& c) {
+    for (; c.si < dm.n; ++c.si) {
+      const int j = __builtin_amdgcn_readlane(myid, c.si);
+      if (j < 0) { c.si = dm.n; return; }
+      c.lo = j * dm.ls;
+      c.kt = c.lo & ~31;
+      c.kend = min((j + 1) * dm.ls, t + 1);
+      if (c.lo < c.kend) return;
+    }
+  };
+  auto advance = [&](Cur& c) {
+    c.kt += 32;
+    if (c.kt < c.kend) return;
+    ++c.si;
+    open_block(c);
+  };
+  auto load_tile = [&](Tile& tl, const Cur& c) {
+    const T* base = fb + (size_t)(c.kt / 32) * TI * 512;
+#pragma unroll
+    for (int i = 0; i < TI; ++i) tl.f[i] = load_frag(base + i * 512);
+  };
+  auto compute_tile = [&](const Tile& tl, const Cur& c) {
+    f32x4 sv[2], dp[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      sv[sub] = dp[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks) mma(sv[sub], tl.f[sub * (DK / 32) + ks], qf[ks]);
+#pragma unroll
+      for (int ks = 0; ks < DV / 32; ++ks) mma(dp[sub], tl.f[NKK + sub * (DV / 32) + ks], dof[ks]);
+    }
+    float ds[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int key = c.kt + qd * 8 + e;
+      const bool v = key >= c.lo && key < c.kend;
+      const float p = v ? fast_exp2(sv[e >> 2][e & 3] * sc2 - lse2) : 0.f;
+      ds[e] = p * (gc * dp[e >> 2][e & 3] - Dc);
+    }
+    const Frag8<T> dsf = to_frag<T>(ds);
+#pragma unroll
+    for (int dt = 0; dt < DK / 16; ++dt) mma(dq[dt], tl.f[NKK + NKV + dt], dsf);
+  };
+  Tile ring[DEPTH];
+  Cur rc[DEPTH];
+  Cur lc{0, 0, 0, 0};
+  open_block(lc);
+#pragma unroll
+  for (int r = 0; r < DEPTH; ++r) {
+    rc[r] = lc;
+    if (lc.si < dm.n) {
+      load_tile(ring[r], lc);
+      advance(lc);
+    }
+  }
+  bool more = rc[0].si < dm.n;
+  while (more) {
+#pragma unroll
+    for (int r = 0; r < DEPTH; ++r) {
+      if (more) {
+        __builtin_amdgcn_sched_barrier(0);
+        compute_tile(ring[r], rc[r]);
+        __builtin_amdgcn_sched_barrier(0);
+        rc[r] = lc;
+        if (lc.si < dm.n) {
+          load_tile(ring[r], lc);
+          advance(lc);
+        }
+        more = rc[(r + 1) % DEPTH].si < dm.n;
+      }
+    }
+  }
+  if (cv) {
+    float* out = a.dq + row * DK + qd * 4;
+#pragma unroll
+    for (int dt = 0; dt < DK / 16; ++dt) {
+      float o[4];
+      load4(out + dt * 16, o);
+      store4(out + dt * 16, o[0] + dm.scale * dq[dt][0], o[1] + dm.scale * dq[dt][1], o[2] + dm.scale * dq[dt][2],
+             o[3] + dm.scale * dq[dt][3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dq of the compressed and window branches, query-tile stationary: the query
+// positions of a workgroup share every key tile of these two branches, so
+// 64-key stages of the fragment-ordered tiles (key-row K, key-row V and K^T
+// fragments) are copied once into LDS, double-buffered through registers, and
+// each wave's columns (16*NCT (position, head) pairs) read their MFMA
+// operands there.  Per 32 keys and column tile: S^T = K Q^T, dP^T = V dO^T,
+// dS = P (g dP - D), dq^T += K^T dS^T.  BR: 1 compressed, 4 window.
+// ---------------------------------------------------------------------------
+template <typename T, int DK, int DV>
+constexpr int dqt_stage_elems() { return 2 * (2 * DK / 32 + 2 * DV / 32 + DK / 16) * 512; }
+
+template <typename T, int DK, int DV, int NCT, int NW, int BR>
+__global__ __launch_bounds__(NW * 64, 2) void k_dq_tiled(Dims dm, BwdArgs a) {
+  constexpr int NKK = 2 * DK / 32, NKV = 2 * DV / 32, TI = NKK + NKV + DK / 16;
+  constexpr int STAGE = dqt_stage_elems<T, DK, DV>();
+  constexpr int NT = NW * 64;
+  constexpr int CH = STAGE / 8 / NT;            // fragments of 8 elements per thread and stage
+  static_assert(CH * 8 * NT == STAGE, "stage must split evenly over the workgroup");
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* stg = (T*)smem_raw;                        // [2][STAGE]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15, qd = lane >> 4;
+  const int G = dm.G, PW = 16 * NCT / G, PWG = NW * PW;
+  const int ntiles = (dm.T + PWG - 1) / PWG;
+  int unit, tile;
+  xcd_map(blockIdx.x, dm.B * dm.Hkv, ntiles, unit, tile);
+  const int b = unit / dm.Hkv, g = unit % dm.Hkv;
+  const int twg = tile * PWG, tlast = min(dm.T - 1, twg + PWG - 1);
+  const int t0 = twg + wave * PW;
+  const size_t BTH = (size_t)dm.B * dm.T * dm.Hq;
+  Frag8<T> qf[NCT][DK / 32], dof[NCT][DV / 32];
+  int pos[NCT];
+  size_t row[NCT];
+  bool cvalid[NCT];
+  float lse2[NCT][2], gc[NCT][2], Dc[NCT][2];
+  f32x4 dq[NCT][DK / 16];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int col = ct * 16 + c16;
+    pos[ct] = t0 + col / G;
+    cvalid[ct] = pos[ct] < dm.T;
+    const int hq = g * G + col % G;
+    row[ct] = (size_t)(b * dm.T + min(pos[ct], dm.T - 1)) * dm.Hq + hq;
+    const T* qp = (const T*)a.q + row[ct] * DK + qd * 8;
+    const T* dp = (const T*)a.d_o + row[ct] * DV + qd * 8;
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) qf[ct][ks] = cvalid[ct] ? load_frag(qp + ks * 32) : zero_frag<T>();
+#pragma unroll
+    for (int ks = 0; ks < DV / 32; ++ks) dof[ct][ks] = cvalid[ct] ? load_frag(dp + ks * 32) : zero_frag<T>();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int c = k == 0 ? 0 : 2;
+      const float l = cvalid[ct] ? a.lse[c * BTH + row[ct]] : kNegInf;
+      lse2[ct][k] = l == kNegInf ? 0.f : l * kLog2e;
+      gc[ct][k] = cvalid[ct] ? a.w.gates[row[ct] * 3 + c] : 0.f;
+      Dc[ct][k] = cvalid[ct] ? a.w.Dc[c * BTH + row[ct]] : 0.f;
+    }
+#pragma unroll
+    for (int dt = 0; dt < DK / 16; ++dt) dq[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float sc2 = dm.scale * kLog2e;
+
+  // One key stream: keys [klo, khi) of the workgroup, fragment tiles `base`
+  // (nt tiles of this (b, g)); column ct sees keys [lo[ct], hi[ct]).
+  auto stream = [&](const T* base, int nt, int klo, int khi, const int (&lo)[NCT], const int (&hi)[NCT], int k) {
+    if (klo >= khi) return;
+    const int s_first = klo & ~63;
+    const int nst = (khi - s_first + 63) / 64;
+    Frag8<T> pre[CH];
+    auto gload = [&](int st) {
+      const int tile0 = (s_first + st * 64) / 32;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int e = (tid + c * NT) * 8;            // element offset in the stage
+        const int tl = tile0 + e / (TI * 512);
+        pre[c] = tl < nt ? load_frag(base + (size_t)tile0 * TI * 512 + e) : zero_frag<T>();
+      }
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        *reinterpret_cast<Frag8<T>*>(stg + (size_t)buf * STAGE + (tid + c * NT) * 8) = pre[c];
+    };
+    gload(0);
+    __syncthreads();   // the previous stream's last stage is no longer read
+    lstore(0);
+    __syncthreads();
+    for (int st = 0; st < nst; ++st) {
+      if (st + 1 < nst) gload(st + 1);
+      const T* sb = stg + (size_t)(st & 1) * STAGE + lane * 8;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kt = s_first + st * 64 + h * 32;
+        if (kt >= khi) break;
+        const T* tb = sb + (size_t)h * TI * 512;
+        f32x4 sacc[NCT][2], dpa[NCT][2];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+          for (int sub = 0; sub < 2; ++sub) sacc[ct][sub] = dpa[ct][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+          for (int ks = 0; ks < DK / 32; ++ks) {
+            const Frag8<T> kf = *reinterpret_cast<const Frag8<T>*>(tb + (sub * (DK / 32) + ks) * 512);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) mma(sacc[ct][sub], kf, qf[ct][ks]);
+          }
+#pragma unroll
+          for (int ks = 0; ks < DV / 32; ++ks) {
+            const Frag8<T> vf = *reinterpret_cast<const Frag8<T>*>(tb + (NKK + sub * (DV / 32) + ks) * 512);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) mma(dpa[ct][sub], vf, dof[ct][ks]);
+          }
+        }
+        Frag8<T> dsf[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          float ds[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int key = kt + qd * 8 + e;
+            const bool v = key >= lo[ct] && key < hi[ct];
+            const float pe = v ? fast_exp2(sacc[ct][e >> 2][e & 3] * sc2 - lse2[ct][k]) : 0.f;
+            ds[e] = pe * (gc[ct][k] * dpa[ct][e >> 2][e & 3] - Dc[ct][k]);
+          }
+          dsf[ct] = to_frag<T>(ds);
+        }
+#pragma unroll
+        for (int dt = 0; dt < DK / 16; ++dt) {
+          const Frag8<T> kt_f = *reinterpret_cast<const Frag8<T>*>(tb + (NKK + NKV + dt) * 512);
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) mma(dq[ct][dt], kt_f, dsf[ct]);
+        }
+      }
+      if (st + 1 < nst) {
+        lstore((st + 1) & 1);
+      }
+      __syncthreads();
+    }
+  };
+
+  const int BG = b * dm.Hkv + g;
+  if (BR & 1) {
+    int lo[NCT], hi[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      lo[ct] = 0;
+      hi[ct] = cvalid[ct] ? ncmp_visible(pos[ct], dm.l, dm.d) : 0;
+    }
+    const int nt = (dm.ncmp + 31) / 32;
+    stream((const T*)a.w.fckv + (size_t)BG * nt * TI * 512, nt, 0, ncmp_visible(tlast, dm.l, dm.d), lo, hi, 0);
+  }
+  if (BR & 4) {
+    int lo[NCT], hi[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      lo[ct] = max(0, pos[ct] - dm.w + 1);
+      hi[ct] = cvalid[ct] ? pos[ct] + 1 : 0;
+    }
+    const int nt = (dm.T + 31) / 32;
+    stream((const T*)a.fkv_win + (size_t)BG * nt * TI * 512, nt, max(0, twg - dm.w + 1), tlast + 1, lo, hi, 1);
+  }
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    if (!cvalid[ct]) continue;
+    float* out = a.dq + row[ct] * DK + qd * 4;
+#pragma unroll
     for (int dt = 0; dt < DK / 16; ++dt)
-      store4(out + dt * 16, dm.scale * st.dq[dt][0], dm.scale * st.dq[dt][1], dm.scale * st.dq[dt][2],
-             dm.scale * st.dq[dt][3]);
+      store4(out + dt * 16, dm.scale * dq[ct][dt][0], dm.scale * dq[ct][dt][1], dm.scale * dq[ct][dt][2],
+             dm.scale * dq[ct][dt][3]);
+  }
+}
+
+// Whether the query-tile dq kernel fits (its two stages in LDS).
+template <typename T, int DK, int DV>
+constexpr bool dq_tiled_fits() { return 2 * dqt_stage_elems<T, DK, DV>() * sizeof(T) <= 160 * 1024; }
+
+template <typename T, int DK, int DV, int BR>
+static hipError_t launch_dq_tiled(const Dims& dm, const BwdArgs& a, hipStream_t s) {
+  if constexpr (!dq_tiled_fits<T, DK, DV>()) {
+    return hipErrorInvalidValue;
+  } else {
+    constexpr int NCT = DK >= 192 ? 1 : 2, NW = 8;   // 192-wide rows: one column tile fits the registers
+    const size_t lds = 2 * (size_t)dqt_stage_elems<T, DK, DV>() * sizeof(T);
+    auto kfn = k_dq_tiled<T, DK, DV, NCT, NW, BR>;
+    if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const int PWG = NW * 16 * NCT / dm.G;
+    const int ntiles = (dm.T + PWG - 1) / PWG;
+    kfn<<<ntiles * dm.B * dm.Hkv, NW * 64, lds, s>>>(dm, a);
+    return hipGetLastError();
   }
 }
 
@@ -1097,7 +1436,14 @@ static hipError_t bwd_impl(const Dims& dm, const nsa_bwd_args* args, BwdArgs& a,
   } else {
     k_bwd_dq<T, DK, DV, true><<<((dm.T + 3) / 4) * BG, 256, 0, s>>>(dm, a);
   }
-  k_bwd_dq<T, DK, DV, false><<<((dm.T + 3) / 4) * BG, 256, 0, s>>>(dm, a);
+  if constexpr (dq_tiled_fits<T, DK, DV>()) {
+    // compressed and window branches query-tile stationary, then the selected
+    // branch per position, added
+    if ((e = launch_dq_tiled<T, DK, DV, 5>(dm, a, s)) != hipSuccess) return e;
+    k_bwd_dq_slc<T, DK, DV><<<((dm.T + 3) / 4) * BG, 256, 0, s>>>(dm, a);
+  } else {
+    k_bwd_dq<T, DK, DV, false><<<((dm.T + 3) / 4) * BG, 256, 0, s>>>(dm, a);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // stage 3: compressed keys
   const size_t klds = kv_lds<T, DK, DV>();
