@@ -535,7 +535,8 @@ def run_backward(steps, warmup, wname="train_16k"):
 
 # ---------------------------------------------------------------- dense baseline
 
-def run_dense_comparison(lengths=(8192, 16384, 32768, 65536), wname="prefill_64k", reps=2):
+def run_dense_comparison(lengths=(8192, 16384, 32768, 65536), wname="prefill_64k", reps=2,
+                         bwd_lengths=(8192, 16384, 32768, 65536)):
     """NSA prefill forward against dense causal attention on the same inputs
     (the comparison the pages' kernel-speed figures make), per sequence length:
     milliseconds of each (HIP events around the call, after one warmup) and the
@@ -560,7 +561,6 @@ def run_dense_comparison(lengths=(8192, 16384, 32768, 65536), wname="prefill_64k
         def timed(fn):
             fn()
             torch.cuda.synchronize()
-            a.k_new, a.v_new = kn[i].data_ptr(), vn[i].data_ptr()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             for _ in range(reps):
@@ -576,11 +576,31 @@ def run_dense_comparison(lengths=(8192, 16384, 32768, 65536), wname="prefill_64k
         del ws_n
         ws_d = torch.empty(nsa.workspace_size(cfg, nsa.NSA_OP_DENSE), dtype=torch.uint8, device=dev)
         t_dense = timed(lambda: nsa.nsa_dense_fwd(cfg, d["q"], d["k"], d["v"], out=o_n, workspace=ws_d))
-        del ws_d, d
-        log(f"T={T}: NSA {t_nsa:.2f} ms, dense {t_dense:.2f} ms")
-        out.append({"T": T, "nsa_ms": round(t_nsa, 3), "dense_ms": round(t_dense, 3),
-                    "speedup": round(t_dense / t_nsa, 2)})
-    return {"workload": wname, "pass": "forward", "per_length": out}
+        del ws_d
+        row = {"T": T, "nsa_ms": round(t_nsa, 3), "dense_ms": round(t_dense, 3),
+               "speedup": round(t_dense / t_nsa, 2)}
+        log(f"T={T}: forward NSA {t_nsa:.2f} ms, dense {t_dense:.2f} ms")
+        if T in bwd_lengths:
+            d_o = NI.make_grad_output(wt, 0).to(dev)
+            saved = nsa.nsa_fwd_prefill(cfg, d["q"], d["k"], d["v"], d["x"], d["w_gate"], d["phi_k"], d["phi_v"],
+                                        save_for_backward=True)
+            ws_b = torch.empty(nsa.workspace_size(cfg, nsa.NSA_OP_BWD), dtype=torch.uint8, device=dev)
+            t_nsa_b = timed(lambda: nsa.nsa_bwd(cfg, d["q"], d["k"], d["v"], d["x"], d["w_gate"], d["phi_k"],
+                                                d["phi_v"], saved, d_o, workspace=ws_b))
+            del ws_b, saved
+            dfw = nsa.nsa_dense_fwd(cfg, d["q"], d["k"], d["v"], want_lse=True)
+            ws_db = torch.empty(nsa.workspace_size(cfg, nsa.NSA_OP_DENSE_BWD), dtype=torch.uint8, device=dev)
+            t_dense_b = timed(lambda: nsa.nsa_dense_bwd(cfg, d["q"], d["k"], d["v"], dfw["o"], dfw["lse"], d_o,
+                                                        workspace=ws_db))
+            del ws_db, dfw, d_o
+            row.update({"nsa_bwd_ms": round(t_nsa_b, 3), "dense_bwd_ms": round(t_dense_b, 3),
+                        "bwd_speedup": round(t_dense_b / t_nsa_b, 2)})
+            log(f"T={T}: backward NSA {t_nsa_b:.2f} ms, dense {t_dense_b:.2f} ms")
+        del d
+        torch.cuda.empty_cache()
+        out.append(row)
+    return {"workload": wname, "passes": "forward; backward (NSA with the forward's saved tensors)",
+            "per_length": out}
 
 
 # ---------------------------------------------------------------- CPU oracle leg

@@ -64,7 +64,7 @@ typedef enum nsa_dtype { NSA_BF16 = 0, NSA_FP32 = 1 } nsa_dtype;
 typedef enum nsa_phi_kind { NSA_PHI_MEANPOOL = 0, NSA_PHI_MLP = 1 } nsa_phi_kind;
 typedef enum nsa_op {
   NSA_OP_FWD_PREFILL = 0, NSA_OP_FWD_DECODE = 1, NSA_OP_BWD = 2, NSA_OP_COMPRESS = 3,
-  NSA_OP_DENSE = 4, NSA_OP_APPEND = 5
+  NSA_OP_DENSE = 4, NSA_OP_APPEND = 5, NSA_OP_DENSE_BWD = 6
 } nsa_op;
 
 /* Shapes and hyper-parameters.
@@ -219,6 +219,19 @@ typedef struct nsa_dense_args {
   void *o, *lse;
 } nsa_dense_args;
 
+/* Backward of nsa_dense_fwd: with P the causal softmax probabilities and
+ * D = <dO, O> per row (the standard attention backward),
+ *   dV = P^T dO, dS = P (dO V^T - D), dq = scale dS K, dK = scale dS^T q,
+ * summed over the query heads of each KV head.  Inputs q, k, v, the forward's
+ * o (io_dtype) and lse ([B,T,Hq] fp32), d_o [B,T,Hq,dv] (io_dtype).  Outputs
+ * (fp32, overwritten) dq [B,T,Hq,dk], dk [B,T,Hkv,dk], dv [B,T,Hkv,dv].
+ * NSA_ERR_UNSUPPORTED for fp32 with d_k >= 128 (its key tiles do not fit the
+ * local memory).  Workspace: NSA_OP_DENSE_BWD. */
+typedef struct nsa_dense_bwd_args {
+  const void *q, *k, *v, *o, *lse, *d_o;
+  void *dq, *dk, *dv;
+} nsa_dense_bwd_args;
+
 /* Version of this header the library was built from (NSA_ABI_VERSION). */
 int nsa_abi_version(void);
 
@@ -243,6 +256,8 @@ nsa_status nsa_fwd_decode(const nsa_params* p, const nsa_decode_args* a, void* w
 nsa_status nsa_bwd(const nsa_params* p, const nsa_bwd_args* a, void* ws,
                    size_t ws_bytes, void* stream);
 nsa_status nsa_dense_fwd(const nsa_params* p, const nsa_dense_args* a, void* ws,
+                         size_t ws_bytes, void* stream);
+nsa_status nsa_dense_bwd(const nsa_params* p, const nsa_dense_bwd_args* a, void* ws,
                          size_t ws_bytes, void* stream);
 nsa_status nsa_decode_append(const nsa_params* p, const nsa_append_args* a, void* ws,
                              size_t ws_bytes, void* stream);

@@ -17,11 +17,11 @@ import torch
 
 from . import _lib
 from ._lib import (NSA_BF16, NSA_FP32, NSA_OP_APPEND, NSA_OP_BWD, NSA_OP_COMPRESS, NSA_OP_DENSE,
-                   NSA_OP_FWD_DECODE, NSA_OP_FWD_PREFILL,
+                   NSA_OP_DENSE_BWD, NSA_OP_FWD_DECODE, NSA_OP_FWD_PREFILL,
                    NSA_PHI_MEANPOOL, NSA_PHI_MLP, NSAError)
 
 __all__ = ["Config", "workspace_size", "nsa_compress", "nsa_fwd_prefill", "nsa_fwd_decode",
-           "nsa_decode_append", "nsa_bwd", "nsa_dense_fwd", "load_library", "NSAError"]
+           "nsa_decode_append", "nsa_bwd", "nsa_dense_fwd", "nsa_dense_bwd", "load_library", "NSAError"]
 
 load_library = _lib.load
 
@@ -364,6 +364,34 @@ def nsa_dense_fwd(cfg: Config, q, k, v, *, out=None, want_lse: bool = False,
     st = _lib.load().nsa_dense_fwd(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(), _stream(dev))
     if st != 0:
         raise NSAError("nsa_dense_fwd", st)
+    res["_workspace"] = ws
+    return res
+
+
+def nsa_dense_bwd(cfg: Config, q, k, v, o, lse, d_o, *,
+                  workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Backward of nsa_dense_fwd (o and lse as it returned them); fp32 gradients."""
+    dev = q.device
+    dt = cfg.torch_dtype
+    B, T, Hq, Hkv = cfg.B, cfg.T, cfg.H_q, cfg.H_kv
+    _check(q, "q", (B, T, Hq, cfg.d_k), dt, dev)
+    _check(k, "k", (B, T, Hkv, cfg.d_k), dt, dev)
+    _check(v, "v", (B, T, Hkv, cfg.d_v), dt, dev)
+    _check(o, "o", (B, T, Hq, cfg.d_v), dt, dev)
+    _check(lse, "lse", (B, T, Hq), torch.float32, dev)
+    _check(d_o, "d_o", (B, T, Hq, cfg.d_v), dt, dev)
+    f32 = torch.float32
+    res = {"dq": torch.empty(B, T, Hq, cfg.d_k, dtype=f32, device=dev),
+           "dk": torch.empty(B, T, Hkv, cfg.d_k, dtype=f32, device=dev),
+           "dv": torch.empty(B, T, Hkv, cfg.d_v, dtype=f32, device=dev)}
+    a = _lib.nsa_dense_bwd_args(q=q.data_ptr(), k=k.data_ptr(), v=v.data_ptr(), o=o.data_ptr(),
+                                lse=lse.data_ptr(), d_o=d_o.data_ptr(), dq=res["dq"].data_ptr(),
+                                dk=res["dk"].data_ptr(), dv=res["dv"].data_ptr())
+    ws = _workspace(cfg, NSA_OP_DENSE_BWD, dev, workspace)
+    p = cfg.params()
+    st = _lib.load().nsa_dense_bwd(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(), _stream(dev))
+    if st != 0:
+        raise NSAError("nsa_dense_bwd", st)
     res["_workspace"] = ws
     return res
 

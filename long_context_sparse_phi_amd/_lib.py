@@ -14,7 +14,8 @@ LIB_PATH = os.path.join(_PKG, "libnsa.so")
 NSA_OK, NSA_ERR_INVALID_ARG, NSA_ERR_UNSUPPORTED, NSA_ERR_WORKSPACE, NSA_ERR_HIP, NSA_ERR_INTERNAL = range(6)
 NSA_BF16, NSA_FP32 = 0, 1
 NSA_PHI_MEANPOOL, NSA_PHI_MLP = 0, 1
-NSA_OP_FWD_PREFILL, NSA_OP_FWD_DECODE, NSA_OP_BWD, NSA_OP_COMPRESS, NSA_OP_DENSE, NSA_OP_APPEND = range(6)
+(NSA_OP_FWD_PREFILL, NSA_OP_FWD_DECODE, NSA_OP_BWD, NSA_OP_COMPRESS, NSA_OP_DENSE, NSA_OP_APPEND,
+ NSA_OP_DENSE_BWD) = range(7)
 ABI_VERSION = 2
 
 _vp = ctypes.c_void_p
@@ -70,9 +71,13 @@ class nsa_dense_args(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("q", "k", "v", "o", "lse")]
 
 
+class nsa_dense_bwd_args(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("q", "k", "v", "o", "lse", "d_o", "dq", "dk", "dv")]
+
+
 EXPORTS = ("nsa_abi_version", "nsa_status_str", "nsa_workspace_size", "nsa_compress",
            "nsa_fwd_prefill", "nsa_fwd_decode", "nsa_bwd", "nsa_dense_fwd",
-           "nsa_decode_append")
+           "nsa_decode_append", "nsa_dense_bwd")
 
 _LIB = None
 
@@ -98,7 +103,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                  ctypes.c_size_t, _vp]
     for name, argt in (("nsa_fwd_prefill", nsa_prefill_args), ("nsa_fwd_decode", nsa_decode_args),
                        ("nsa_bwd", nsa_bwd_args), ("nsa_dense_fwd", nsa_dense_args),
-                       ("nsa_decode_append", nsa_append_args)):
+                       ("nsa_decode_append", nsa_append_args), ("nsa_dense_bwd", nsa_dense_bwd_args)):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [P(nsa_params), P(argt), _vp, ctypes.c_size_t, _vp]

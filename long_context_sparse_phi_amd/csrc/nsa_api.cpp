@@ -21,6 +21,9 @@ hipError_t launch_decode(const Dims& dm, const nsa_decode_args* a, void* ws, hip
 size_t decode_ws_bytes(const Dims& dm);
 hipError_t launch_bwd(const Dims& dm, const nsa_bwd_args* a, void* ws, hipStream_t s, void* const* events);
 size_t bwd_ws_bytes(const Dims& dm);
+size_t dense_bwd_ws_bytes(const Dims& dm);
+bool dense_bwd_supported(const Dims& dm);
+hipError_t launch_dense_bwd(const Dims& dm, const nsa_dense_bwd_args* a, void* ws, hipStream_t s);
 }  // namespace nsa
 
 using namespace nsa;
@@ -217,6 +220,7 @@ nsa_status nsa_workspace_size(const nsa_params* p, nsa_op op, size_t* bytes) {
       case NSA_OP_COMPRESS: *bytes = phi_ws(dm) > 0 ? phi_ws(dm) : 256; return NSA_OK;
       case NSA_OP_DENSE: *bytes = dense_ws_bytes(dm); return NSA_OK;
       case NSA_OP_APPEND: *bytes = append_ws_bytes(dm) > 0 ? append_ws_bytes(dm) : 256; return NSA_OK;
+      case NSA_OP_DENSE_BWD: *bytes = dense_bwd_ws_bytes(dm); return NSA_OK;
     }
     return NSA_ERR_INVALID_ARG;
   } catch (...) {
@@ -372,6 +376,25 @@ nsa_status nsa_decode_append(const nsa_params* p, const nsa_append_args* a, void
     aa.phi_v = {a->phi_v.pe, a->phi_v.w1, a->phi_v.b1, a->phi_v.w2, a->phi_v.b2};
     aa.h = (float*)ws;
     return hip_status(launch_append(dm, aa, (hipStream_t)stream));
+  } catch (...) {
+    return NSA_ERR_INTERNAL;
+  }
+}
+
+nsa_status nsa_dense_bwd(const nsa_params* p, const nsa_dense_bwd_args* a, void* ws, size_t ws_bytes,
+                         void* stream) {
+  try {
+    Dims dm;
+    nsa_status st = make_dims(p, &dm);
+    if (st != NSA_OK) return st;
+    if (!a) return NSA_ERR_INVALID_ARG;
+    const void* req[] = {a->q, a->k, a->v, a->o, a->lse, a->d_o, a->dq, a->dk, a->dv};
+    for (const void* r : req)
+      if (!r || !aligned16(r)) return NSA_ERR_INVALID_ARG;
+    if (!dense_bwd_supported(dm)) return NSA_ERR_UNSUPPORTED;
+    if (ws_bytes < dense_bwd_ws_bytes(dm) || !ws || !aligned16(ws)) return NSA_ERR_WORKSPACE;
+    if ((st = check_device()) != NSA_OK) return st;
+    return hip_status(launch_dense_bwd(dm, a, ws, (hipStream_t)stream));
   } catch (...) {
     return NSA_ERR_INTERNAL;
   }

@@ -1529,4 +1529,110 @@ hipError_t launch_bwd(const Dims& dm, const nsa_bwd_args* args, void* ws, hipStr
   return hipErrorInvalidValue;
 }
 
+// ---------------------------------------------------------------------------
+// Dense causal attention backward (the baseline's backward): the window
+// branch's kernels with a window over every key and unit gates.
+//   D = <dO, O> per row (O as the forward stored it), dq from the
+//   query-tile kernel, dK/dV from the key-stationary window kernel.
+// ---------------------------------------------------------------------------
+template <typename T, int DV>
+__global__ __launch_bounds__(256) void k_dense_rowterms(Dims dm, const T* __restrict__ o, const T* __restrict__ d_o,
+                                                        const float* __restrict__ lse, float* __restrict__ Dc,
+                                                        float* __restrict__ lse3, float* __restrict__ gates) {
+  constexpr int LPR = DV / 4, RPW = 64 / LPR;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t BTH = (size_t)dm.B * dm.T * dm.Hq;
+  const size_t row = ((size_t)blockIdx.x * 4 + wave) * RPW + lane / LPR;
+  const int f = (lane % LPR) * 4;
+  const bool live = row < BTH;
+  const size_t rr = live ? row : 0;
+  float d[4], x[4];
+  load4(d_o + rr * DV + f, d);
+  load4(o + rr * DV + f, x);
+  float v = d[0] * x[0] + d[1] * x[1] + d[2] * x[2] + d[3] * x[3];
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  if (!live || lane % LPR != 0) return;
+  Dc[2 * BTH + row] = v;
+  lse3[2 * BTH + row] = lse[row];
+#pragma unroll
+  for (int c = 0; c < 3; ++c) gates[row * 3 + c] = 1.f;
+}
+
+struct DenseBwdWs {
+  float *gates, *Dc, *lse3;
+  void* fkv;
+};
+
+static size_t dense_bwd_carve(const Dims& dm, void* ws, DenseBwdWs* w) {
+  char* base = (char*)ws;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { void* r = base ? base + off : nullptr; off += al256(bytes); return r; };
+  const size_t BTH = (size_t)dm.B * dm.T * dm.Hq, es = dm.io == IO_BF16 ? 2 : 4;
+  w->gates = (float*)take(BTH * 3 * 4);
+  w->Dc = (float*)take(3 * BTH * 4);
+  w->lse3 = (float*)take(3 * BTH * 4);
+  w->fkv = take(frag_tiles_elems(dm, dm.T, bwd_tile_ins(dm)) * es);
+  return off;
+}
+
+size_t dense_bwd_ws_bytes(const Dims& dm) {
+  DenseBwdWs w;
+  return dense_bwd_carve(dm, nullptr, &w);
+}
+
+template <typename T, int DK, int DV>
+static hipError_t dense_bwd_impl(Dims dm, const nsa_dense_bwd_args* args, void* ws, hipStream_t s) {
+  if constexpr (!dq_tiled_fits<T, DK, DV>()) {
+    return hipErrorInvalidValue;
+  } else {
+    dm.w = dm.T;
+    DenseBwdWs w;
+    dense_bwd_carve(dm, ws, &w);
+    BwdArgs a{};
+    a.q = args->q; a.k = args->k; a.v = args->v; a.d_o = args->d_o;
+    a.ks = a.kw = args->k; a.vs = a.vw = args->v;
+    a.lse = w.lse3;
+    a.dq = (float*)args->dq;
+    a.dk = a.dks = a.dkw = (float*)args->dk;
+    a.dv = a.dvs = a.dvw = (float*)args->dv;
+    a.w.gates = w.gates; a.w.Dc = w.Dc; a.w.fkv = w.fkv;
+    a.fkv_win = w.fkv;
+    hipError_t e;
+    const size_t BTH = (size_t)dm.B * dm.T * dm.Hq;
+    const size_t per_block = 4 * (64 / (DV / 4));
+    k_dense_rowterms<T, DV><<<(unsigned)((BTH + per_block - 1) / per_block), 256, 0, s>>>(
+        dm, (const T*)args->o, (const T*)args->d_o, (const float*)args->lse, w.Dc, w.lse3, w.gates);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int ti = bwd_tile_ins(dm);
+    const int n1 = 2 * DK / 32, n2 = n1 + 2 * DV / 32;
+    if ((e = launch_frag_pack(dm, DK, dm.T, a.k, w.fkv, ti, 0, false, s)) != hipSuccess ||
+        (e = launch_frag_pack(dm, DV, dm.T, a.v, w.fkv, ti, n1, false, s)) != hipSuccess ||
+        (e = launch_frag_pack(dm, DK, dm.T, a.k, w.fkv, ti, n2, true, s)) != hipSuccess)
+      return e;
+    if ((e = launch_dq_tiled<T, DK, DV, 4>(dm, a, s)) != hipSuccess) return e;
+    const size_t klds = kv_lds<T, DK, DV>();
+    if (klds > 64 * 1024)
+      hipFuncSetAttribute((const void*)k_bwd_kv<T, DK, DV, KV_WIN>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)klds);
+    k_bwd_kv<T, DK, DV, KV_WIN><<<dm.B * dm.Hkv * ((dm.T + 63) / 64), 256, klds, s>>>(dm, a);
+    return hipGetLastError();
+  }
+}
+
+bool dense_bwd_supported(const Dims& dm) {
+  const bool bf = dm.io == IO_BF16;
+  if (dm.dk == 64 && dm.dv == 64) return bf ? dq_tiled_fits<bf16, 64, 64>() : dq_tiled_fits<float, 64, 64>();
+  if (dm.dk == 128 && dm.dv == 128) return bf ? dq_tiled_fits<bf16, 128, 128>() : dq_tiled_fits<float, 128, 128>();
+  if (dm.dk == 192 && dm.dv == 128) return bf ? dq_tiled_fits<bf16, 192, 128>() : dq_tiled_fits<float, 192, 128>();
+  return false;
+}
+
+hipError_t launch_dense_bwd(const Dims& dm, const nsa_dense_bwd_args* a, void* ws, hipStream_t s) {
+  const bool bf = dm.io == IO_BF16;
+  if (dm.dk == 64 && dm.dv == 64) return bf ? dense_bwd_impl<bf16, 64, 64>(dm, a, ws, s) : dense_bwd_impl<float, 64, 64>(dm, a, ws, s);
+  if (dm.dk == 128 && dm.dv == 128) return bf ? dense_bwd_impl<bf16, 128, 128>(dm, a, ws, s) : dense_bwd_impl<float, 128, 128>(dm, a, ws, s);
+  if (dm.dk == 192 && dm.dv == 128) return bf ? dense_bwd_impl<bf16, 192, 128>(dm, a, ws, s) : dense_bwd_impl<float, 192, 128>(dm, a, ws, s);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace nsa

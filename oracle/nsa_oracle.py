@@ -42,7 +42,7 @@ from scipy.special import erf
 __all__ = [
     "Params", "gate", "compress", "remap_matrix", "attend", "n_cmp_visible",
     "candidate_blocks", "forced_blocks", "top_n", "is_near_tie", "forward",
-    "decode", "append_token", "backward", "dq_rows", "dense_causal", "round_io", "gelu", "gelu_grad", "sigmoid",
+    "decode", "append_token", "backward", "dq_rows", "dense_causal", "dense_causal_bwd", "round_io", "gelu", "gelu_grad", "sigmoid",
     "cmp_keys", "slc_keys", "win_keys", "decode_token_count",
 ]
 
@@ -530,6 +530,37 @@ def dense_causal(q, k, v, scale=None):
             o[b, :, h] = (e @ v[b, :, g]) / l_
             lse[b, :, h] = (m + np.log(l_))[:, 0]
     return o, lse
+
+
+def dense_causal_bwd(q, k, v, d_o, scale=None, o=None):
+    """Gradients of L = sum(d_o * O) for O = dense_causal(q, k, v): the
+    textbook attention backward per head, dV = P^T dO, dP = dO V^T,
+    D = rowsum(dO * O), dS = P (dP - D), dq = scale dS K, dK = scale dS^T q,
+    key/value gradients summed over the query heads of each KV head.
+    o: the forward output to form D from (default: the exact one).
+    Returns dq, dk, dv.
+    """
+    B, T, Hq, dk = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    sc = 1.0 / np.sqrt(dk) if scale is None else scale
+    if o is None:
+        o, _ = dense_causal(q, k, v, sc)
+    dq, dkk, dvv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    causal = np.tril(np.ones((T, T), dtype=bool))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            s = np.where(causal, sc * (q[b, :, h] @ k[b, :, g].T), -np.inf)
+            P = np.exp(s - s.max(axis=1, keepdims=True))
+            P /= P.sum(axis=1, keepdims=True)
+            dO = d_o[b, :, h]
+            dvv[b, :, g] += P.T @ dO
+            D = (dO * o[b, :, h]).sum(axis=1, keepdims=True)
+            dS = P * (dO @ v[b, :, g].T - D)
+            dq[b, :, h] = sc * dS @ k[b, :, g]
+            dkk[b, :, g] += sc * dS.T @ q[b, :, h]
+    return dq, dkk, dvv
 
 
 def dq_rows(p: Params, q_rows, k, v, kc, vc, g_rows, d_o_rows, idx_rows, rows, kv_win=None) -> np.ndarray:

@@ -63,3 +63,16 @@ def test_ctypes_mirror_matches_header_and_validation_runs_on_host():
     with pytest.raises(nsa.NSAError) as e:
         nsa.workspace_size(bad, _lib.NSA_OP_FWD_PREFILL)
     assert e.value.code == _lib.NSA_ERR_INVALID_ARG
+
+
+def test_dense_bwd_rejects_fp32_wide_heads_before_touching_memory():
+    # fp32 with d_k = 128: the key tiles do not fit the local memory, which is
+    # reported before any pointer is used (the pointers here are never valid)
+    import long_context_sparse_phi_amd as nsa
+    from long_context_sparse_phi_amd import _lib
+    lib = _lib.load()
+    cfg = nsa.Config(B=1, T=256, H_kv=1, G=4, d_k=128, d_v=128, phi="mean", dtype="fp32")
+    p = cfg.params()
+    a = _lib.nsa_dense_bwd_args(**{n: 4096 for n in ("q", "k", "v", "o", "lse", "d_o", "dq", "dk", "dv")})
+    st = lib.nsa_dense_bwd(ctypes.byref(p), ctypes.byref(a), None, 0, None)
+    assert st == _lib.NSA_ERR_UNSUPPORTED

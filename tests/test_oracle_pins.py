@@ -627,3 +627,22 @@ def test_dense_causal_matches_torch_sdpa():
     s = np.einsum("bthd,bjhd->bhtj", q, np.repeat(k, G, axis=2)) / np.sqrt(dk)
     s = np.where(np.tril(np.ones((T, T), dtype=bool)), s, -np.inf)
     np.testing.assert_allclose(lse, np.transpose(np.log(np.exp(s).sum(-1)), (0, 2, 1)), rtol=1e-12)
+
+
+def test_dense_causal_bwd_matches_torch_autograd():
+    """The dense baseline's backward against torch fp64 autograd through
+    scaled_dot_product_attention (causal, GQA by repeating the KV heads)."""
+    rng = np.random.default_rng(29)
+    B, T, Hkv, G, dk, dv = 2, 33, 2, 3, 5, 4
+    q = rng.standard_normal((B, T, Hkv * G, dk))
+    k = rng.standard_normal((B, T, Hkv, dk))
+    v = rng.standard_normal((B, T, Hkv, dv))
+    d_o = rng.standard_normal((B, T, Hkv * G, dv))
+    dq, dk_, dv_ = O.dense_causal_bwd(q, k, v, d_o)
+    tq, tk, tv = (torch.from_numpy(a).permute(0, 2, 1, 3).clone().requires_grad_(True) for a in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk.repeat_interleave(G, 1), tv.repeat_interleave(G, 1), is_causal=True)
+    (out * torch.from_numpy(d_o).permute(0, 2, 1, 3)).sum().backward()
+    np.testing.assert_allclose(dq, tq.grad.permute(0, 2, 1, 3).numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dk_, tk.grad.permute(0, 2, 1, 3).numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv_, tv.grad.permute(0, 2, 1, 3).numpy(), rtol=1e-10, atol=1e-12)
