@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define NSA_ABI_VERSION 2
+#define NSA_ABI_VERSION 3
 
 typedef enum nsa_status {
   NSA_OK = 0,
@@ -75,7 +75,12 @@ typedef enum nsa_op {
  *   16 | l', l' | 32*d, 31*d + l <= 32*l'); n_select n (3 <= n <= 32);
  *   window w >= 1; gate_dim C (gate input width); phi_hidden (MLP width,
  *   multiple of 64); phi (nsa_phi_kind); io_dtype (nsa_dtype);
- *   scale: 0 selects 1/sqrt(d_k). */
+ *   scale: 0 selects 1/sqrt(d_k);
+ *   gate_hidden: 0 for one linear gate layer, g = sigmoid(x w_gate); otherwise
+ *   the width Hg (1 .. 1024) of a two-layer gate MLP (youleyou page,
+ *   整体框架: gates from an MLP with a sigmoid),
+ *   g = sigmoid(gelu_erf(x w1 + b1) w_gate + b2), weights in nsa_gate_mlp and
+ *   w_gate [Hg,Hq,3]. */
 typedef struct nsa_params {
   int32_t batch, seqlen, n_kv_heads, group_size, d_k, d_v;
   int32_t cmp_block, cmp_stride, sel_block, n_select, window;
@@ -83,7 +88,14 @@ typedef struct nsa_params {
   int32_t phi;
   int32_t io_dtype;
   float scale;
+  int32_t gate_hidden;
 } nsa_params;
+
+/* First layer and biases of the gate MLP (io_dtype; used when gate_hidden > 0):
+ *   w1 [C, Hg], b1 [Hg], b2 [Hq, 3]. */
+typedef struct nsa_gate_mlp {
+  const void *w1, *b1, *b2;
+} nsa_gate_mlp;
 
 /* Compression MLP phi for keys (D = d_k) or values (D = d_v), io_dtype:
  *   pe [l, D], w1 [l*D, hidden], b1 [hidden], w2 [hidden, D], b2 [D];
@@ -119,6 +131,7 @@ typedef struct nsa_prefill_args {
   void *o;
   void *k_cmp, *v_cmp, *lse, *idx, *o_branch, *p_slc, *gates;
   const void *k_slc, *v_slc, *k_win, *v_win;
+  nsa_gate_mlp gate_mlp;
 } nsa_prefill_args;
 
 /* One decode step per sequence; the new token's key/value are already stored
@@ -149,6 +162,7 @@ typedef struct nsa_decode_args {
   void *idx, *p_slc, *lse, *o_branch;
   const int32_t *seq_lens;
   const void *k_win_cache, *v_win_cache;
+  nsa_gate_mlp gate_mlp;
 } nsa_decode_args;
 
 /* Decode-time cache maintenance: append one token per sequence to the raw
@@ -190,10 +204,18 @@ typedef struct nsa_append_args {
  *   (as in the forward), dk_slc, dv_slc, dk_win, dv_win [B,T,Hkv,dk|dv] fp32
  *   are required and receive those tensors' gradients, and dk, dv hold only
  *   the gradient through the compressed branch (phi).  Without them dk, dv
- *   are the sum over the three branches. */
+ *   are the sum over the three branches.
+ * Gates: dw_gate is the gradient of w_gate (the gate MLP's output layer when
+ *   gate_hidden > 0, then d_gate_mlp receives dw1 [C,Hg], db1 [Hg],
+ *   db2 [Hq,3], all required); dx (optional, NULL = not computed) [B,T,C]
+ *   fp32 is the gradient with respect to the gate input x. */
 typedef struct nsa_phi_grads {
   void *pe, *w1, *b1, *w2, *b2;
 } nsa_phi_grads;
+
+typedef struct nsa_gate_grads {
+  void *w1, *b1, *b2;
+} nsa_gate_grads;
 
 typedef struct nsa_bwd_args {
   const void *q, *k, *v, *x, *w_gate;
@@ -203,6 +225,9 @@ typedef struct nsa_bwd_args {
   nsa_phi_grads d_phi_k, d_phi_v;
   const void *k_slc, *v_slc, *k_win, *v_win;
   void *dk_slc, *dv_slc, *dk_win, *dv_win;
+  nsa_gate_mlp gate_mlp;
+  nsa_gate_grads d_gate_mlp;
+  void *dx;
 } nsa_bwd_args;
 
 /* Dense causal attention, the baseline the pages measure NSA against

@@ -45,6 +45,7 @@ class Config:
     phi: str = "mlp"          # "mlp" | "mean"
     dtype: str = "bf16"       # "bf16" | "fp32"
     scale: float = 0.0        # 0 => 1/sqrt(d_k)
+    gate_hidden: int = 0      # 0: one linear gate layer; else the gate MLP's hidden width
 
     @property
     def H_q(self) -> int:
@@ -59,6 +60,11 @@ class Config:
         return -(-self.T // self.l_sel)
 
     @property
+    def gate_in(self) -> int:
+        """Input width of the gate layer that w_gate holds."""
+        return self.gate_hidden if self.gate_hidden else self.gate_dim
+
+    @property
     def torch_dtype(self) -> torch.dtype:
         return torch.bfloat16 if self.dtype == "bf16" else torch.float32
 
@@ -69,7 +75,8 @@ class Config:
             sel_block=self.l_sel, n_select=self.n, window=self.w, gate_dim=self.gate_dim,
             phi_hidden=self.hidden if self.phi == "mlp" else 0,
             phi=NSA_PHI_MLP if self.phi == "mlp" else NSA_PHI_MEANPOOL,
-            io_dtype=NSA_BF16 if self.dtype == "bf16" else NSA_FP32, scale=self.scale)
+            io_dtype=NSA_BF16 if self.dtype == "bf16" else NSA_FP32, scale=self.scale,
+            gate_hidden=self.gate_hidden)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -123,6 +130,23 @@ def _phi_struct(cfg: Config, phi: Optional[Dict[str, torch.Tensor]], D: int, dev
     return w
 
 
+def _gate_struct(cfg: Config, gate_mlp: Optional[Dict[str, torch.Tensor]], dev) -> _lib.nsa_gate_mlp:
+    """First layer and biases of the gate MLP ({"w1", "b1", "b2"}), required
+    exactly when cfg.gate_hidden > 0."""
+    g = _lib.nsa_gate_mlp()
+    if not cfg.gate_hidden:
+        if gate_mlp is not None:
+            raise ValueError("gate_mlp given but cfg.gate_hidden is 0")
+        return g
+    if gate_mlp is None:
+        raise ValueError("cfg.gate_hidden > 0 needs gate_mlp = {w1, b1, b2}")
+    shapes = {"w1": (cfg.gate_dim, cfg.gate_hidden), "b1": (cfg.gate_hidden,), "b2": (cfg.H_q, 3)}
+    for k, shp in shapes.items():
+        _check(gate_mlp[k], f"gate_mlp.{k}", shp, cfg.torch_dtype, dev)
+        setattr(g, k, gate_mlp[k].data_ptr())
+    return g
+
+
 def nsa_compress(cfg: Config, x: torch.Tensor, phi: Optional[Dict[str, torch.Tensor]], is_value: bool,
                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Compressed keys (is_value=False) or values of x [B,T,Hkv,D] -> [B,Ncmp,Hkv,D]."""
@@ -155,12 +179,13 @@ def _branch_kv(cfg: Config, kv, tag: str, dev):
 
 def nsa_fwd_prefill(cfg: Config, q, k, v, x, w_gate, phi_k=None, phi_v=None, *, out=None,
                     save_for_backward: bool = False, debug: bool = False, kv_slc=None, kv_win=None,
-                    workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+                    gate_mlp=None, workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
     """NSA prefill forward.  Returns {"o": ...} plus, when save_for_backward,
     k_cmp, v_cmp, lse, idx, o_branch, and, when debug, also p_slc and gates.
     kv_slc, kv_win: (k, v) pairs of the selected and window branches when each
     branch has its own keys and values (both or neither); k, v then feed the
-    compressed branch only."""
+    compressed branch only.  With cfg.gate_hidden > 0, gate_mlp holds the gate
+    MLP's first layer and biases and w_gate its output layer [Hg, Hq, 3]."""
     dev = q.device
     dt = cfg.torch_dtype
     B, T, Hq, Hkv = cfg.B, cfg.T, cfg.H_q, cfg.H_kv
@@ -168,7 +193,7 @@ def nsa_fwd_prefill(cfg: Config, q, k, v, x, w_gate, phi_k=None, phi_v=None, *, 
     _check(k, "k", (B, T, Hkv, cfg.d_k), dt, dev)
     _check(v, "v", (B, T, Hkv, cfg.d_v), dt, dev)
     _check(x, "x", (B, T, cfg.gate_dim), dt, dev)
-    _check(w_gate, "w_gate", (cfg.gate_dim, Hq, 3), dt, dev)
+    _check(w_gate, "w_gate", (cfg.gate_in, Hq, 3), dt, dev)
     res = {"o": out if out is not None else torch.empty(B, T, Hq, cfg.d_v, dtype=dt, device=dev)}
     _check(res["o"], "o", (B, T, Hq, cfg.d_v), dt, dev)
     if save_for_backward or debug:
@@ -192,6 +217,7 @@ def nsa_fwd_prefill(cfg: Config, q, k, v, x, w_gate, phi_k=None, phi_v=None, *, 
         raise ValueError("kv_slc and kv_win go together")
     a.k_slc, a.v_slc = _branch_kv(cfg, kv_slc, "slc", dev)
     a.k_win, a.v_win = _branch_kv(cfg, kv_win, "win", dev)
+    a.gate_mlp = _gate_struct(cfg, gate_mlp, dev)
     ws = _workspace(cfg, NSA_OP_FWD_PREFILL, dev, workspace)
     p = cfg.params()
     st = _lib.load().nsa_fwd_prefill(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(), _stream(dev))
@@ -203,7 +229,7 @@ def nsa_fwd_prefill(cfg: Config, q, k, v, x, w_gate, phi_k=None, phi_v=None, *, 
 
 def nsa_fwd_decode(cfg: Config, q, k_cache, v_cache, k_cmp_cache, v_cmp_cache, x, w_gate, *,
                    out=None, debug: bool = False, seq_lens: Optional[torch.Tensor] = None,
-                   kv_win_cache=None, workspace: Optional[torch.Tensor] = None):
+                   kv_win_cache=None, gate_mlp=None, workspace: Optional[torch.Tensor] = None):
     """One decode step; cfg.T is the cache length S (query at position S-1).
     With seq_lens (int32 [B] on the device), cfg.T is the cache capacity and
     sequence b holds seq_lens[b] tokens, its query at position seq_lens[b]-1.
@@ -219,7 +245,7 @@ def nsa_fwd_decode(cfg: Config, q, k_cache, v_cache, k_cmp_cache, v_cmp_cache, x
     _check(k_cmp_cache, "k_cmp_cache", (B, cap, Hkv, cfg.d_k), dt, dev)
     _check(v_cmp_cache, "v_cmp_cache", (B, cap, Hkv, cfg.d_v), dt, dev)
     _check(x, "x", (B, cfg.gate_dim), dt, dev)
-    _check(w_gate, "w_gate", (cfg.gate_dim, Hq, 3), dt, dev)
+    _check(w_gate, "w_gate", (cfg.gate_in, Hq, 3), dt, dev)
     res = {"o": out if out is not None else torch.empty(B, Hq, cfg.d_v, dtype=dt, device=dev)}
     if debug:
         res["idx"] = torch.empty(B, Hkv, cfg.n, dtype=torch.int32, device=dev)
@@ -242,6 +268,7 @@ def nsa_fwd_decode(cfg: Config, q, k_cache, v_cache, k_cmp_cache, v_cmp_cache, x
         _check(kv_win_cache[0], "k_win_cache", (B, S, Hkv, cfg.d_k), dt, dev)
         _check(kv_win_cache[1], "v_win_cache", (B, S, Hkv, cfg.d_v), dt, dev)
         a.k_win_cache, a.v_win_cache = kv_win_cache[0].data_ptr(), kv_win_cache[1].data_ptr()
+    a.gate_mlp = _gate_struct(cfg, gate_mlp, dev)
     ws = _workspace(cfg, NSA_OP_FWD_DECODE, dev, workspace)
     p = cfg.params()
     st = _lib.load().nsa_fwd_decode(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(), _stream(dev))
@@ -285,14 +312,17 @@ def nsa_decode_append(cfg: Config, k_new, v_new, seq_lens, k_cache, v_cache, k_c
 
 
 def nsa_bwd(cfg: Config, q, k, v, x, w_gate, phi_k, phi_v, saved: Dict[str, torch.Tensor], d_o, *,
-            kv_slc=None, kv_win=None, recompute_row_terms: bool = False,
-            workspace: Optional[torch.Tensor] = None) -> Dict[str, object]:
+            kv_slc=None, kv_win=None, recompute_row_terms: bool = False, gate_mlp=None,
+            want_dx: bool = False, workspace: Optional[torch.Tensor] = None) -> Dict[str, object]:
     """Backward with the forward's selected blocks fixed.  `saved` is the dict
     nsa_fwd_prefill returned with save_for_backward=True.  Gradients are fp32.
     With kv_slc, kv_win (as passed to the forward) the result also holds
     dk_slc, dv_slc, dk_win, dv_win, and dk, dv are the compressed branch's part.
     The softmax row terms <dO, O_c> are read from saved["o_branch"] when it is
-    there, unless recompute_row_terms asks for them to be recomputed."""
+    there, unless recompute_row_terms asks for them to be recomputed.
+    With cfg.gate_hidden > 0 the result holds d_gate_mlp {w1, b1, b2}, and
+    dw_gate is the output layer's gradient; want_dx adds dx, the gradient
+    with respect to the gate input x."""
     dev = q.device
     dt = cfg.torch_dtype
     B, T, Hq, Hkv = cfg.B, cfg.T, cfg.H_q, cfg.H_kv
@@ -301,7 +331,7 @@ def nsa_bwd(cfg: Config, q, k, v, x, w_gate, phi_k, phi_v, saved: Dict[str, torc
     res = {"dq": torch.empty(B, T, Hq, cfg.d_k, dtype=f32, device=dev),
            "dk": torch.empty(B, T, Hkv, cfg.d_k, dtype=f32, device=dev),
            "dv": torch.empty(B, T, Hkv, cfg.d_v, dtype=f32, device=dev),
-           "dw_gate": torch.empty(cfg.gate_dim, Hq, 3, dtype=f32, device=dev)}
+           "dw_gate": torch.empty(cfg.gate_in, Hq, 3, dtype=f32, device=dev)}
     a = _lib.nsa_bwd_args()
     for name, t in (("q", q), ("k", k), ("v", v), ("x", x), ("w_gate", w_gate), ("d_o", d_o)):
         setattr(a, name, t.data_ptr())
@@ -335,6 +365,16 @@ def nsa_bwd(cfg: Config, q, k, v, x, w_gate, phi_k, phi_v, saved: Dict[str, torc
             gs = _lib.nsa_phi_grads(**{kk: vv.data_ptr() for kk, vv in g.items()})
             setattr(a, tag, gs)
             res[tag] = g
+    a.gate_mlp = _gate_struct(cfg, gate_mlp, dev)
+    if cfg.gate_hidden:
+        gg = {"w1": torch.empty(cfg.gate_dim, cfg.gate_hidden, dtype=f32, device=dev),
+              "b1": torch.empty(cfg.gate_hidden, dtype=f32, device=dev),
+              "b2": torch.empty(Hq, 3, dtype=f32, device=dev)}
+        a.d_gate_mlp = _lib.nsa_gate_grads(**{kk: vv.data_ptr() for kk, vv in gg.items()})
+        res["d_gate_mlp"] = gg
+    if want_dx:
+        res["dx"] = torch.empty(B, T, cfg.gate_dim, dtype=f32, device=dev)
+        a.dx = res["dx"].data_ptr()
     ws = _workspace(cfg, NSA_OP_BWD, dev, workspace)
     p = cfg.params()
     st = _lib.load().nsa_bwd(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(), _stream(dev))
@@ -399,5 +439,6 @@ def nsa_dense_bwd(cfg: Config, q, k, v, o, lse, d_o, *,
 def config_from_workload(w, **over) -> Config:
     """Config for a workload description of the shared input generator."""
     c = Config(B=w.B, T=w.T, H_kv=w.H_kv, G=w.G, d_k=w.d_k, d_v=w.d_v, l=w.l, d=w.d, l_sel=w.l_sel,
-               n=w.n, w=w.w, gate_dim=w.gate_dim, hidden=w.hidden, phi=w.phi, dtype=w.dtype)
+               n=w.n, w=w.w, gate_dim=w.gate_dim, hidden=w.hidden, phi=w.phi, dtype=w.dtype,
+               gate_hidden=getattr(w, "gate_hidden", 0))
     return dataclasses.replace(c, **over) if over else c

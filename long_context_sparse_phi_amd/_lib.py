@@ -16,7 +16,7 @@ NSA_BF16, NSA_FP32 = 0, 1
 NSA_PHI_MEANPOOL, NSA_PHI_MLP = 0, 1
 (NSA_OP_FWD_PREFILL, NSA_OP_FWD_DECODE, NSA_OP_BWD, NSA_OP_COMPRESS, NSA_OP_DENSE, NSA_OP_APPEND,
  NSA_OP_DENSE_BWD) = range(7)
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _vp = ctypes.c_void_p
 
@@ -25,7 +25,8 @@ class nsa_params(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "seqlen", "n_kv_heads", "group_size", "d_k", "d_v",
         "cmp_block", "cmp_stride", "sel_block", "n_select", "window",
-        "gate_dim", "phi_hidden", "phi", "io_dtype")] + [("scale", ctypes.c_float)]
+        "gate_dim", "phi_hidden", "phi", "io_dtype")] + [("scale", ctypes.c_float),
+                                                        ("gate_hidden", ctypes.c_int32)]
 
 
 class nsa_phi_weights(ctypes.Structure):
@@ -36,18 +37,28 @@ class nsa_phi_grads(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("pe", "w1", "b1", "w2", "b2")]
 
 
+class nsa_gate_mlp(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("w1", "b1", "b2")]
+
+
+class nsa_gate_grads(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("w1", "b1", "b2")]
+
+
 class nsa_prefill_args(ctypes.Structure):
     _fields_ = ([(n, _vp) for n in ("q", "k", "v", "x", "w_gate")] +
                 [("phi_k", nsa_phi_weights), ("phi_v", nsa_phi_weights)] +
                 [(n, _vp) for n in ("o", "k_cmp", "v_cmp", "lse", "idx", "o_branch", "p_slc", "gates",
-                                    "k_slc", "v_slc", "k_win", "v_win")])
+                                    "k_slc", "v_slc", "k_win", "v_win")] +
+                [("gate_mlp", nsa_gate_mlp)])
 
 
 class nsa_decode_args(ctypes.Structure):
     _fields_ = ([(n, _vp) for n in ("q", "k_cache", "v_cache", "k_cmp_cache", "v_cmp_cache", "x", "w_gate")] +
                 [("cmp_cache_cap", ctypes.c_int32)] +
                 [(n, _vp) for n in ("o", "idx", "p_slc", "lse", "o_branch", "seq_lens",
-                                    "k_win_cache", "v_win_cache")])
+                                    "k_win_cache", "v_win_cache")] +
+                [("gate_mlp", nsa_gate_mlp)])
 
 
 class nsa_append_args(ctypes.Structure):
@@ -64,7 +75,8 @@ class nsa_bwd_args(ctypes.Structure):
                                     "dq", "dk", "dv", "dw_gate")] +
                 [("d_phi_k", nsa_phi_grads), ("d_phi_v", nsa_phi_grads)] +
                 [(n, _vp) for n in ("k_slc", "v_slc", "k_win", "v_win",
-                                    "dk_slc", "dv_slc", "dk_win", "dv_win")])
+                                    "dk_slc", "dv_slc", "dk_win", "dv_win")] +
+                [("gate_mlp", nsa_gate_mlp), ("d_gate_mlp", nsa_gate_grads), ("dx", _vp)])
 
 
 class nsa_dense_args(ctypes.Structure):

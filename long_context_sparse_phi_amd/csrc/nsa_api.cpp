@@ -81,6 +81,7 @@ nsa_status make_dims(const nsa_params* p, Dims* dm) {
   if (p->window < 1) return NSA_ERR_INVALID_ARG;
   if (p->gate_dim < 1) return NSA_ERR_INVALID_ARG;
   if (p->gate_dim > 1024) return NSA_ERR_UNSUPPORTED;
+  if (p->gate_hidden < 0 || p->gate_hidden > 1024) return NSA_ERR_INVALID_ARG;
   if (p->phi != NSA_PHI_MEANPOOL && p->phi != NSA_PHI_MLP) return NSA_ERR_INVALID_ARG;
   if (p->phi == NSA_PHI_MLP && (p->phi_hidden < 64 || p->phi_hidden % 64 != 0)) return NSA_ERR_INVALID_ARG;
   if (p->io_dtype != NSA_BF16 && p->io_dtype != NSA_FP32) return NSA_ERR_UNSUPPORTED;
@@ -95,6 +96,7 @@ nsa_status make_dims(const nsa_params* p, Dims* dm) {
   D.nsel = (D.T + ls - 1) / ls;
   D.Tp = ((D.T + 63) & ~63) + 64;
   D.C = p->gate_dim;
+  D.Cg = p->gate_hidden;
   D.hidden = p->phi == NSA_PHI_MLP ? p->phi_hidden : 0;
   D.scale = p->scale > 0.f ? p->scale : 1.f / std::sqrt((float)p->d_k);
   D.io = p->io_dtype == NSA_BF16 ? IO_BF16 : IO_F32;
@@ -107,7 +109,7 @@ size_t esize(const Dims& dm) { return dm.io == IO_BF16 ? 2 : 4; }
 // Workspace plan of the prefill forward.  Every optional output the caller
 // leaves NULL is placed in the workspace; sizes assume all are NULL.
 struct PrefillWs {
-  void *gates, *kc, *vc, *vct, *vt, *kvf, *lse, *idx, *ob, *phi;
+  void *gates, *gh, *kc, *vc, *vct, *vt, *kvf, *lse, *idx, *ob, *phi;
 };
 
 size_t phi_ws(const Dims& dm) {
@@ -121,6 +123,7 @@ size_t plan_prefill(const Dims& dm, void* ws, PrefillWs* w) {
   const size_t BTH = (size_t)dm.B * dm.T * dm.Hq;
   const size_t es = esize(dm);
   w->gates = c.take(BTH * 3 * 4);
+  w->gh = c.take((size_t)dm.B * dm.T * dm.Cg * 4);
   w->kc = c.take((size_t)dm.B * dm.ncmp * dm.Hkv * dm.dk * es);
   w->vc = c.take((size_t)dm.B * dm.ncmp * dm.Hkv * dm.dv * es);
   w->vct = c.take((size_t)dm.B * dm.Hkv * dm.dv * dm.ncmp_pad * es);
@@ -179,6 +182,15 @@ bool all_or_none(std::initializer_list<const void*> ps, bool* present) {
   }
   *present = n > 0;
   return n == 0 || n == k;
+}
+
+// Gate MLP weights: required (aligned) when the gate has a hidden layer.
+bool gate_ok(const Dims& dm, const nsa_gate_mlp& g) {
+  if (dm.Cg == 0) return true;
+  const void* ps[3] = {g.w1, g.b1, g.b2};
+  for (const void* p : ps)
+    if (!p || !aligned16(p)) return false;
+  return true;
 }
 
 bool phi_ok(const nsa_phi_weights& w) {
@@ -261,6 +273,7 @@ static nsa_status prefill_impl(const nsa_params* p, const nsa_prefill_args* a, v
     for (const void* r : opt)
       if (r && !aligned16(r)) return NSA_ERR_INVALID_ARG;
     if (dm.hidden && (!phi_ok(a->phi_k) || !phi_ok(a->phi_v))) return NSA_ERR_INVALID_ARG;
+    if (!gate_ok(dm, a->gate_mlp)) return NSA_ERR_INVALID_ARG;
     bool split = false;
     if (!all_or_none({a->k_slc, a->v_slc, a->k_win, a->v_win}, &split)) return NSA_ERR_INVALID_ARG;
     PrefillWs w;
@@ -284,7 +297,10 @@ static nsa_status prefill_impl(const nsa_params* p, const nsa_prefill_args* a, v
     void* o_cmp = ob;
     void* o_slc = ob + BTH * dm.dv * obs;
     void* o_win = a->o_branch ? ob + 2 * BTH * dm.dv * obs : nullptr;
-    if (sg.mark() || launch_gate(dm, dm.B * dm.T, a->x, a->w_gate, gates, s) != hipSuccess) return NSA_ERR_HIP;
+    if (sg.mark() ||
+        launch_gate_mlp(dm, dm.B * dm.T, a->x, a->w_gate, GateMlp{a->gate_mlp.w1, a->gate_mlp.b1, a->gate_mlp.b2},
+                        (float*)w.gh, nullptr, gates, s) != hipSuccess)
+      return NSA_ERR_HIP;
     if (sg.mark() || run_compress(dm, dm.dk, a->k, &a->phi_k, kc, nullptr, w.phi, s) != hipSuccess)
       return NSA_ERR_HIP;
     if (sg.mark() || run_compress(dm, dm.dv, a->v, &a->phi_v, vc, w.vct, w.phi, s) != hipSuccess)
@@ -423,6 +439,7 @@ static nsa_status decode_impl(const nsa_params* p, const nsa_decode_args* a, voi
       if (r && !aligned16(r)) return NSA_ERR_INVALID_ARG;
     bool split = false;
     if (!all_or_none({a->k_win_cache, a->v_win_cache}, &split)) return NSA_ERR_INVALID_ARG;
+    if (!gate_ok(dm, a->gate_mlp)) return NSA_ERR_INVALID_ARG;
     const size_t need = decode_ws_bytes(dm);
     if (ws_bytes < need || !ws || !aligned16(ws)) return NSA_ERR_WORKSPACE;
     if ((st = check_device()) != NSA_OK) return st;
@@ -464,6 +481,11 @@ static nsa_status bwd_impl(const nsa_params* p, const nsa_bwd_args* a, void* ws,
       for (const void* r : g)
         if (!r || !aligned16(r)) return NSA_ERR_INVALID_ARG;
     }
+    if (!gate_ok(dm, a->gate_mlp)) return NSA_ERR_INVALID_ARG;
+    if (dm.Cg && (!a->d_gate_mlp.w1 || !a->d_gate_mlp.b1 || !a->d_gate_mlp.b2 || !aligned16(a->d_gate_mlp.w1) ||
+                  !aligned16(a->d_gate_mlp.b1) || !aligned16(a->d_gate_mlp.b2)))
+      return NSA_ERR_INVALID_ARG;
+    if (a->dx && !aligned16(a->dx)) return NSA_ERR_INVALID_ARG;
     bool split = false, split_out = false;
     if (!all_or_none({a->k_slc, a->v_slc, a->k_win, a->v_win}, &split) ||
         !all_or_none({a->dk_slc, a->dv_slc, a->dk_win, a->dv_win}, &split_out) || split != split_out)

@@ -59,6 +59,9 @@ static BwdPlan bwd_plan(const Dims& dm) {
 
 struct BwdBufs {
   float* gates;    // [B,T,Hq,3]
+  float* ghid;     // gate MLP: hidden layer gelu(x w1 + b1) [B*T, Cg]
+  float* gpre;     // gate MLP: the same before the GELU
+  float* gdh;      // gate MLP: gradient of the hidden layer [B*T, Cg]
   float* Dc;       // [3,B,T,Hq]
   float* dz;       // [B,T,Hq,3]
   void* fkv;       // fragment tiles of (k, v, k^T) over T (bwd_tile_ins instructions per 32 keys)
@@ -101,6 +104,9 @@ static size_t bwd_carve(const Dims& dm, void* ws, BwdBufs* w) {
   const size_t es = dm.io == IO_BF16 ? 2 : 4;
   const size_t BTH = (size_t)dm.B * dm.T * dm.Hq, BG = (size_t)dm.B * dm.Hkv;
   w->gates = (float*)take(BTH * 3 * 4);
+  w->ghid = (float*)take((size_t)dm.B * dm.T * dm.Cg * 4);
+  w->gpre = (float*)take((size_t)dm.B * dm.T * dm.Cg * 4);
+  w->gdh = (float*)take((size_t)dm.B * dm.T * dm.Cg * 4);
   w->Dc = (float*)take(3 * BTH * 4);
   w->dz = (float*)take(BTH * 3 * 4);
   w->fkv = take(frag_tiles_elems(dm, dm.T, bwd_tile_ins(dm)) * es);
@@ -122,6 +128,8 @@ static size_t bwd_carve(const Dims& dm, void* ws, BwdBufs* w) {
     size_t mn = (size_t)dm.C * 3 * dm.Hq;
     mn = mn > (size_t)dm.hidden * Dm ? mn : (size_t)dm.hidden * Dm;
     mn = mn > (size_t)dm.l * Dm ? mn : (size_t)dm.l * Dm;
+    mn = mn > (size_t)dm.Cg * 3 * dm.Hq ? mn : (size_t)dm.Cg * 3 * dm.Hq;
+    mn = mn > (size_t)dm.C * dm.Cg ? mn : (size_t)dm.C * dm.Cg;
     w->gpart = (float*)take(kMaxSplit * mn * 4);
   }
   if (dm.hidden) {
@@ -1406,7 +1414,9 @@ static hipError_t bwd_impl(const Dims& dm, const nsa_bwd_args* args, BwdArgs& a,
   const int BG = dm.B * dm.Hkv;
   // stage 0: gates, gate backward, row terms
   if ((e = mark()) != hipSuccess) return e;
-  if ((e = launch_gate(dm, dm.B * dm.T, a.x, a.wg, a.w.gates, s)) != hipSuccess) return e;
+  if ((e = launch_gate_mlp(dm, dm.B * dm.T, a.x, a.wg, GateMlp{args->gate_mlp.w1, args->gate_mlp.b1, args->gate_mlp.b2},
+                           a.w.ghid, a.w.gpre, a.w.gates, s)) != hipSuccess)
+    return e;
   // stage 1: fragment tiles of (k, v, k^T) and (k_cmp, v_cmp, k_cmp^T) for the dq passes
   if ((e = mark()) != hipSuccess) return e;
   {
@@ -1493,11 +1503,39 @@ static hipError_t bwd_impl(const Dims& dm, const nsa_bwd_args* args, BwdArgs& a,
     if ((e = phi_bwd<T, DK>(dm, a, args->phi_k, args->d_phi_k, a.k, a.w.dkc, a.dk, s)) != hipSuccess) return e;
     if ((e = phi_bwd<T, DV>(dm, a, args->phi_v, args->d_phi_v, a.v, a.w.dvc, a.dv, s)) != hipSuccess) return e;
   }
-  // stage 7: dW_g = x^T dz
+  // stage 7: gate weights (and the gate input's gradient when asked for)
   if ((e = mark()) != hipSuccess) return e;
   {
-    Gemm g{dm.C, 3 * dm.Hq, dm.B * dm.T, a.x, 1, dm.C, a.w.dz, 3 * dm.Hq, 1, a.dwg, 3 * dm.Hq, 0};
-    if ((e = gemm<T, float>(g, a.w.gpart, s)) != hipSuccess) return e;
+    const int ntok = dm.B * dm.T, HO = 3 * dm.Hq;
+    float* dx = (float*)args->dx;
+    if (dm.Cg == 0) {
+      // dW_g = x^T dz; dx = dz W_g^T
+      Gemm g{dm.C, HO, ntok, a.x, 1, dm.C, a.w.dz, HO, 1, a.dwg, HO, 0};
+      if ((e = gemm<T, float>(g, a.w.gpart, s)) != hipSuccess) return e;
+      if (dx) {
+        Gemm gx{ntok, dm.C, HO, a.w.dz, HO, 1, a.wg, 1, HO, dx, dm.C, 0};
+        if ((e = gemm<float, T>(gx, nullptr, s)) != hipSuccess) return e;
+      }
+    } else {
+      const nsa_gate_grads& gg = args->d_gate_mlp;
+      const int Cg = dm.Cg;
+      // output layer: dW2 = hid^T dz, db2 = colsum(dz), dhid = dz W2^T
+      Gemm g2{Cg, HO, ntok, a.w.ghid, 1, Cg, a.w.dz, HO, 1, a.dwg, HO, 0};
+      if ((e = gemm<float, float>(g2, a.w.gpart, s)) != hipSuccess) return e;
+      if ((e = colsum(ntok, HO, HO, a.w.dz, (float*)gg.b2, a.w.gpart, s)) != hipSuccess) return e;
+      Gemm gh{ntok, Cg, HO, a.w.dz, HO, 1, a.wg, 1, HO, a.w.gdh, Cg, 0};
+      if ((e = gemm<float, T>(gh, nullptr, s)) != hipSuccess) return e;
+      // GELU: da = dhid * gelu'(pre); first layer: dW1 = x^T da, db1 = colsum(da), dx = da W1^T
+      k_phi_dact<<<(unsigned)(((size_t)ntok * Cg + 255) / 256), 256, 0, s>>>((size_t)ntok * Cg, a.w.gpre, a.w.gdh);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = colsum(ntok, Cg, Cg, a.w.gdh, (float*)gg.b1, a.w.gpart, s)) != hipSuccess) return e;
+      Gemm g1{dm.C, Cg, ntok, a.x, 1, dm.C, a.w.gdh, Cg, 1, (float*)gg.w1, Cg, 0};
+      if ((e = gemm<T, float>(g1, a.w.gpart, s)) != hipSuccess) return e;
+      if (dx) {
+        Gemm gx{ntok, dm.C, Cg, a.w.gdh, Cg, 1, args->gate_mlp.w1, 1, Cg, dx, dm.C, 0};
+        if ((e = gemm<float, T>(gx, nullptr, s)) != hipSuccess) return e;
+      }
+    }
   }
   return mark();
 }

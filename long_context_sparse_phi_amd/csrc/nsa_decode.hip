@@ -116,6 +116,7 @@ struct DecArgs {
   const int* lens;    // optional [B] tokens per sequence (NULL: S each)
   const void* kwcache;  // window branch's caches (the same as kcache, vcache
   const void* vwcache;  // unless each branch has its own keys and values)
+  GateMlp gmlp;         // gate MLP first layer and biases (dm.Cg > 0)
   DecBufs w;
 };
 
@@ -333,8 +334,10 @@ __device__ __forceinline__ float load_elem(const void* p, int io, size_t i) {
   return io == IO_BF16 ? (float)((const bf16*)p)[i] : ((const float*)p)[i];
 }
 
-// Length of the combine's LDS score row.
-static __host__ __device__ int comb_row_len(const Dims& dm) { return (dm.nsel + 3) & ~3; }
+// Length of the combine's LDS score row (it later holds the gate input).
+static __host__ __device__ int comb_row_len(const Dims& dm) {
+  return ((dm.nsel > dm.C ? dm.nsel : dm.C) + 3) & ~3;
+}
 
 // One workgroup (1024 threads) per (sequence, KV head): per-head log-sum-exp
 // of the compressed branch, per-chunk scales, block scores and top-n.
@@ -346,6 +349,7 @@ __global__ __launch_bounds__(1024) void k_dec_combine(Dims dm, DecArgs a, DecPla
   float* mls = lse2 + 16;                     // [nc][16] chunk maxima
   float* lsl = mls + pl.nc * 16;              // [nc][16] chunk sums
   int* tsh = (int*)(lsl + pl.nc * 16);        // [256 + 16 + 4] top-n scratch
+  float* ghid = (float*)(tsh + 256 + 16 + 4); // [Cg] gate MLP hidden layer
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int bg = blockIdx.x, b = bg / dm.Hkv, g = bg % dm.Hkv;
   const int G = dm.G;
@@ -367,7 +371,7 @@ __global__ __launch_bounds__(1024) void k_dec_combine(Dims dm, DecArgs a, DecPla
     mls[i] = a.w.part_ml[hb * 2];
     lsl[i] = a.w.part_ml[hb * 2 + 1];
   }
-  gate_load(0);
+  if (dm.Cg == 0) gate_load(0);
   __syncthreads();
   // per-head log-sum-exp: wave h reduces head h over the chunks
   {
@@ -433,6 +437,39 @@ __global__ __launch_bounds__(1024) void k_dec_combine(Dims dm, DecArgs a, DecPla
     for (int j = tid; j < dm.nsel; j += 1024) a.p_slc[(size_t)bg * dm.nsel + j] = row[j];
   __syncthreads();
   block_topn<16>(row, sq.t, dm.ls, dm.n, a.w.idx + (size_t)bg * dm.n, tsh, tid);
+  // gate MLP: this sequence's hidden layer gelu(x w1 + b1) in LDS, then the
+  // output layer by the waves below over it
+  if (dm.Cg > 0) {
+    float* gx_s = row;   // the gate input of sequence b (the score row is no longer needed)
+    __syncthreads();
+    for (int k = tid; k < dm.C; k += 1024) gx_s[k] = load_elem(a.x, dm.io, (size_t)b * dm.C + k);
+    __syncthreads();
+    for (int j = tid; j < dm.Cg; j += 1024) {
+      float acc = load_elem(a.gmlp.b1, dm.io, j);
+#pragma unroll 8
+      for (int k = 0; k < dm.C; ++k) acc = fmaf(gx_s[k], load_elem(a.gmlp.w1, dm.io, (size_t)k * dm.Cg + j), acc);
+      ghid[j] = 0.5f * acc * (1.f + erff(acc * 0.70710678118654752f));
+    }
+    __syncthreads();
+    if (wave < G) {
+      const int h = g * G + wave;
+      float z[3] = {0.f, 0.f, 0.f};
+      for (int k = lane; k < dm.Cg; k += 64) {
+#pragma unroll
+        for (int c = 0; c < 3; ++c) z[c] = fmaf(ghid[k], load_elem(a.wg, dm.io, ((size_t)k * dm.Hq + h) * 3 + c), z[c]);
+      }
+#pragma unroll
+      for (int c = 0; c < 3; ++c) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) z[c] += __shfl_xor(z[c], off);
+      }
+      if (lane < 3) {
+        const float zz = (lane == 0 ? z[0] : (lane == 1 ? z[1] : z[2])) + load_elem(a.gmlp.b2, dm.io, (size_t)h * 3 + lane);
+        a.w.gates[((size_t)b * dm.Hq + h) * 3 + lane] = 1.f / (1.f + expf(-zz));
+      }
+    }
+    return;
+  }
   // gates of the group's heads: wave h, lanes over the gate input, the three
   // branches together; the first 256 inputs were loaded at the start
   if (wave < G) {
@@ -641,7 +678,8 @@ static hipError_t decode_impl(const Dims& dm, const DecArgs& a, const DecPlan& p
   }
   if ((e = mark()) != hipSuccess) return e;
   {
-    const size_t lds = (size_t)comb_row_len(dm) * 4 + (size_t)pl.nc * 16 * 4 * 3 + 16 * 4 + (256 + 16 + 4) * 4;
+    const size_t lds = (size_t)comb_row_len(dm) * 4 + (size_t)pl.nc * 16 * 4 * 3 + 16 * 4 + (256 + 16 + 4) * 4 +
+                       (size_t)dm.Cg * 4;
     if (lds > 64 * 1024)
       hipFuncSetAttribute((const void*)k_dec_combine, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     k_dec_combine<<<BG, 1024, lds, s>>>(dm, a, pl);
@@ -663,6 +701,7 @@ hipError_t launch_decode(const Dims& dm, const nsa_decode_args* args, void* ws, 
   a.x = args->x; a.wg = args->w_gate; a.o = args->o;
   a.p_slc = (float*)args->p_slc; a.lse = (float*)args->lse; a.o_branch = args->o_branch;
   a.lens = args->seq_lens;
+  a.gmlp = GateMlp{args->gate_mlp.w1, args->gate_mlp.b1, args->gate_mlp.b2};
   a.kwcache = args->k_win_cache ? args->k_win_cache : args->k_cache;
   a.vwcache = args->v_win_cache ? args->v_win_cache : args->v_cache;
   dec_carve(dm, ws, &a.w);

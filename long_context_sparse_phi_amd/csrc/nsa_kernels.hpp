@@ -18,6 +18,7 @@ struct Dims {
   int nsel;       // ceil(T / ls)
   int Tp;         // row stride of V^T: T rounded up to 64, plus 64
   int C;          // gate input width
+  int Cg;         // gate MLP hidden width (0: one linear gate layer)
   int hidden;     // phi MLP width
   float scale;    // softmax scale
   int io;         // IoType
@@ -114,6 +115,15 @@ struct WinArgs {
   int dense;           // o = window output alone (dense causal attention when w >= T)
 };
 hipError_t launch_win_combine(const Dims& dm, const WinArgs& a, hipStream_t s);
+
+// Gate MLP (dm.Cg > 0): hid = gelu(x w1 + b1) [ntok, Cg] (pre: before the
+// GELU, optional), gates = sigmoid(hid w_gate + b2).  dm.Cg == 0: gates =
+// sigmoid(x w_gate).
+struct GateMlp {
+  const void *w1, *b1, *b2;
+};
+hipError_t launch_gate_mlp(const Dims& dm, int ntok, const void* x, const void* w_gate, const GateMlp& g,
+                           float* hid, float* pre, float* gates, hipStream_t s);
 
 // Decode-time cache maintenance (nsa_append.hip).  dm.T is the raw cache
 // capacity; lens[b] the tokens sequence b held before the call.

@@ -17,11 +17,15 @@
 namespace nsa {
 
 // ---------------------------------------------------------------------------
-// Gate: gates[tok, h*3+c] = sigmoid(sum_i x[tok,i] w[i, h*3+c]), fp32 math.
+// Gate layers, fp32 math: out[tok, o] = act(sum_i x[tok,i] w[i, o] + bias[o]),
+// act = identity (0), exact GELU (1) or sigmoid (2); `pre` (optional) receives
+// the value before the activation.  One linear layer with a sigmoid gives the
+// gates g = sigmoid(x W_g); the gate MLP is a GELU layer followed by it.
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void k_gate(int ntok, int C, int HO, const T* __restrict__ x,
-                                              const T* __restrict__ w, float* __restrict__ gates) {
+template <typename TX, typename TW, int ACT>
+__global__ __launch_bounds__(256) void k_gate(int ntok, int C, int HO, const TX* __restrict__ x,
+                                              const TW* __restrict__ w, const TW* __restrict__ bias,
+                                              float* __restrict__ out, float* __restrict__ pre) {
   constexpr int TOK = 16;
   extern __shared__ float xs[];
   const int tok0 = blockIdx.x * TOK;
@@ -31,30 +35,53 @@ __global__ __launch_bounds__(256) void k_gate(int ntok, int C, int HO, const T* 
   }
   __syncthreads();
   for (int oc = threadIdx.x; oc < HO; oc += blockDim.x) {
+    const float b0 = bias ? to_f32(bias[oc]) : 0.f;
     float acc[TOK];
 #pragma unroll
-    for (int tk = 0; tk < TOK; ++tk) acc[tk] = 0.f;
+    for (int tk = 0; tk < TOK; ++tk) acc[tk] = b0;
     for (int i = 0; i < C; ++i) {
       float wv = to_f32(w[(size_t)i * HO + oc]);
 #pragma unroll
       for (int tk = 0; tk < TOK; ++tk) acc[tk] = fmaf(xs[tk * C + i], wv, acc[tk]);
     }
 #pragma unroll
-    for (int tk = 0; tk < TOK; ++tk)
-      if (tok0 + tk < ntok) gates[(size_t)(tok0 + tk) * HO + oc] = 1.f / (1.f + expf(-acc[tk]));
+    for (int tk = 0; tk < TOK; ++tk) {
+      if (tok0 + tk >= ntok) continue;
+      const size_t o = (size_t)(tok0 + tk) * HO + oc;
+      const float a = acc[tk];
+      if (pre) pre[o] = a;
+      out[o] = ACT == 2 ? 1.f / (1.f + expf(-a)) : (ACT == 1 ? 0.5f * a * (1.f + erff(a * 0.70710678118654752f)) : a);
+    }
   }
+}
+
+template <typename TX, typename TW, int ACT>
+static hipError_t gate_layer(int ntok, int C, int HO, const void* x, const void* w, const void* bias, float* out,
+                             float* pre, hipStream_t s) {
+  dim3 grid((ntok + 15) / 16);
+  k_gate<TX, TW, ACT><<<grid, 256, 16 * C * sizeof(float), s>>>(ntok, C, HO, (const TX*)x, (const TW*)w,
+                                                                 (const TW*)bias, out, pre);
+  return hipGetLastError();
 }
 
 hipError_t launch_gate(const Dims& dm, int ntok, const void* x, const void* w, float* gates,
                        hipStream_t s) {
-  int HO = dm.Hq * 3;
-  dim3 grid((ntok + 15) / 16);
-  size_t lds = 16 * dm.C * sizeof(float);
-  if (dm.io == IO_BF16)
-    k_gate<bf16><<<grid, 256, lds, s>>>(ntok, dm.C, HO, (const bf16*)x, (const bf16*)w, gates);
-  else
-    k_gate<float><<<grid, 256, lds, s>>>(ntok, dm.C, HO, (const float*)x, (const float*)w, gates);
-  return hipGetLastError();
+  const int HO = dm.Hq * 3;
+  if (dm.io == IO_BF16) return gate_layer<bf16, bf16, 2>(ntok, dm.C, HO, x, w, nullptr, gates, nullptr, s);
+  return gate_layer<float, float, 2>(ntok, dm.C, HO, x, w, nullptr, gates, nullptr, s);
+}
+
+hipError_t launch_gate_mlp(const Dims& dm, int ntok, const void* x, const void* w_gate, const GateMlp& g,
+                           float* hid, float* pre, float* gates, hipStream_t s) {
+  if (dm.Cg == 0) return launch_gate(dm, ntok, x, w_gate, gates, s);
+  const int HO = dm.Hq * 3;
+  hipError_t e;
+  if (dm.io == IO_BF16) {
+    if ((e = gate_layer<bf16, bf16, 1>(ntok, dm.C, dm.Cg, x, g.w1, g.b1, hid, pre, s)) != hipSuccess) return e;
+    return gate_layer<float, bf16, 2>(ntok, dm.Cg, HO, hid, w_gate, g.b2, gates, nullptr, s);
+  }
+  if ((e = gate_layer<float, float, 1>(ntok, dm.C, dm.Cg, x, g.w1, g.b1, hid, pre, s)) != hipSuccess) return e;
+  return gate_layer<float, float, 2>(ntok, dm.Cg, HO, hid, w_gate, g.b2, gates, nullptr, s);
 }
 
 // ---------------------------------------------------------------------------

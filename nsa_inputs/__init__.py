@@ -53,6 +53,7 @@ class Workload:
     phi_std: float = 0.02       # std of phi weights and the position embedding
     bias_std: float = 0.0       # std of phi biases (0: biases start at zero)
     gate_std: float = 0.02      # std of the gate projection weights
+    gate_hidden: int = 0        # 0: linear gate; else hidden width of a two-layer gate MLP
 
     @property
     def H_q(self) -> int:
@@ -136,6 +137,20 @@ def _phi(seed: int, tag: str, w: Workload, dim: int) -> Dict[str, torch.Tensor]:
     return out
 
 
+def _gate(seed: int, w: Workload) -> Dict[str, object]:
+    """Gate weights.  Linear gate: w_gate [gate_dim,Hq,3] ~ N(0, gate_std^2).
+    Two-layer gate MLP (gate_hidden = Hg > 0): w1 [gate_dim,Hg] ~ N(0, 1/gate_dim)
+    (unit-variance pre-activations for unit-variance x), b1 [Hg] and b2 [Hq,3]
+    ~ N(0, 0.1^2), output layer w_gate [Hg,Hq,3] ~ N(0, 1/Hg)."""
+    if not w.gate_hidden:
+        return {"w_gate": _normal(seed, "w_gate", (w.gate_dim, w.H_q, 3), w.gate_std)}
+    Hg = w.gate_hidden
+    return {"w_gate": _normal(seed, "gate.w2", (Hg, w.H_q, 3), Hg ** -0.5),
+            "gate_mlp": {"w1": _normal(seed, "gate.w1", (w.gate_dim, Hg), w.gate_dim ** -0.5),
+                         "b1": _normal(seed, "gate.b1", (Hg,), 0.1),
+                         "b2": _normal(seed, "gate.b2", (w.H_q, 3), 0.1)}}
+
+
 def _cast(d: Dict, dt: torch.dtype) -> Dict:
     res = {}
     for k, v in d.items():
@@ -147,7 +162,8 @@ def make_prefill_inputs(w: Workload, seed: int = 0) -> Dict[str, object]:
     """Inputs of one prefill / training forward call (CPU tensors in the I/O dtype).
 
     q [B,T,Hq,dk], k [B,T,Hkv,dk], v [B,T,Hkv,dv], x [B,T,gate_dim],
-    w_gate [gate_dim,Hq,3], phi_k / phi_v dicts (empty for mean-pool).
+    w_gate [gate_dim,Hq,3], phi_k / phi_v dicts (empty for mean-pool); with a
+    gate MLP, w_gate [Hg,Hq,3] and gate_mlp {w1, b1, b2}.
     """
     B, T = w.B, w.T
     d = {
@@ -155,10 +171,10 @@ def make_prefill_inputs(w: Workload, seed: int = 0) -> Dict[str, object]:
         "k": _kv(seed, "k", w, B, T, w.d_k),
         "v": _kv(seed, "v", w, B, T, w.d_v),
         "x": _normal(seed, "x", (B, T, w.gate_dim)),
-        "w_gate": _normal(seed, "w_gate", (w.gate_dim, w.H_q, 3), w.gate_std),
         "phi_k": _phi(seed, "phi_k", w, w.d_k),
         "phi_v": _phi(seed, "phi_v", w, w.d_v),
     }
+    d.update(_gate(seed, w))
     return _cast(d, w.torch_dtype)
 
 
@@ -176,10 +192,10 @@ def make_decode_inputs(w: Workload, seed: int = 0) -> Dict[str, object]:
         "k_cache": _kv(seed, "k", w, B, T, w.d_k),
         "v_cache": _kv(seed, "v", w, B, T, w.d_v),
         "x": _normal(seed, "dec.x", (B, w.gate_dim)),
-        "w_gate": _normal(seed, "w_gate", (w.gate_dim, w.H_q, 3), w.gate_std),
         "phi_k": _phi(seed, "phi_k", w, w.d_k),
         "phi_v": _phi(seed, "phi_v", w, w.d_v),
     }
+    d.update(_gate(seed, w))
     return _cast(d, w.torch_dtype)
 
 

@@ -40,7 +40,7 @@ import numpy as np
 from scipy.special import erf
 
 __all__ = [
-    "Params", "gate", "compress", "remap_matrix", "attend", "n_cmp_visible",
+    "Params", "gate", "gate_logits", "compress", "remap_matrix", "attend", "n_cmp_visible",
     "candidate_blocks", "forced_blocks", "top_n", "is_near_tie", "forward",
     "decode", "append_token", "backward", "dq_rows", "dense_causal", "dense_causal_bwd", "round_io", "gelu", "gelu_grad", "sigmoid",
     "cmp_keys", "slc_keys", "win_keys", "decode_token_count",
@@ -110,14 +110,28 @@ def _scale(p: Params, d_k: int) -> float:
 # ---------------------------------------------------------------------------
 # Gate  [YLY 整体框架: gate scores from the input features through an MLP and a
 # sigmoid; XK 三种注意力如何组合 §2: g = sigmoid(MLP(X))]
-# Reading: one gate per (token, query head, branch), a single linear layer
-# without bias: g[b,t,h,c] = sigmoid(x[b,t,:] . W_g[:,h,c]); c = (cmp, slc, win).
+# Reading: one gate per (token, query head, branch), c = (cmp, slc, win).  The
+# pages leave the MLP's depth open; two forms are computed:
+#   linear (default): g[b,t,h,c] = sigmoid(x[b,t,:] . W_g[:,h,c]), no bias;
+#   two-layer MLP:    a = x W1 + b1, u = gelu(a) (erf form, as the compression
+#                     MLP), g = sigmoid(u W_g + b2), W_g [Hg,Hq,3].
 # ---------------------------------------------------------------------------
 
-def gate(x, w_gate):
-    """x [B,T,C], w_gate [C,Hq,3] -> g [B,T,Hq,3]."""
-    z = np.einsum("btc,chk->bthk", x, w_gate)
-    return sigmoid(z)
+def gate_logits(x, w_gate, mlp: Optional[Dict[str, np.ndarray]] = None):
+    """Pre-sigmoid gate logits z [...,Hq,3] of x [...,C], and the MLP's hidden
+    pre-activation a [...,Hg] and activation u (None for the linear gate)."""
+    if mlp is None:
+        return np.einsum("...c,chk->...hk", x, w_gate), None, None
+    a = np.einsum("...c,cj->...j", x, mlp["w1"]) + mlp["b1"]
+    u = gelu(a)
+    z = np.einsum("...j,jhk->...hk", u, w_gate) + mlp["b2"]
+    return z, a, u
+
+
+def gate(x, w_gate, mlp: Optional[Dict[str, np.ndarray]] = None):
+    """x [B,T,C], w_gate [C,Hq,3] (linear) or [Hg,Hq,3] with mlp = {w1 [C,Hg],
+    b1 [Hg], b2 [Hq,3]} -> g [B,T,Hq,3]."""
+    return sigmoid(gate_logits(x, w_gate, mlp)[0])
 
 
 # ---------------------------------------------------------------------------
@@ -339,7 +353,8 @@ def _sets_to_idx(sets: List[List[int]], n: int) -> np.ndarray:
 
 
 def forward(p: Params, q, k, v, x, w_gate, phi_k=None, phi_v=None, rows=None,
-            idx=None, tie_scores=None, kc=None, vc=None, kv_slc=None, kv_win=None) -> Dict[str, np.ndarray]:
+            idx=None, tie_scores=None, kc=None, vc=None, kv_slc=None, kv_win=None,
+            gate_mlp=None) -> Dict[str, np.ndarray]:
     """NSA prefill forward.
 
     q [B,T,Hq,dk], k [B,T,Hkv,dk], v [B,T,Hkv,dv], x [B,T,C], w_gate [C,Hq,3].
@@ -350,7 +365,9 @@ def forward(p: Params, q, k, v, x, w_gate, phi_k=None, phi_v=None, rows=None,
     rows: query positions to evaluate (default all).  idx: optional fixed block
     indices [B,T,Hkv,n] (-1 padded), used instead of top-n.  tie_scores: optional
     [B,T,Hkv,N_sel] score rows consulted only where the oracle's own row is a near
-    tie.  kc, vc: optional precomputed compressed keys/values.
+    tie.  kc, vc: optional precomputed compressed keys/values.  gate_mlp:
+    optional {w1, b1, b2} of a two-layer gate MLP (w_gate is then its output
+    layer [Hg,Hq,3]).
 
     Returns o [B,R,Hq,dv], o_branch [3,B,R,Hq,dv], lse [3,B,R,Hq],
     p_slc [B,R,Hkv,N_sel], idx [B,R,Hkv,n], retied [B,R,Hkv], gates [B,R,Hq,3],
@@ -365,7 +382,7 @@ def forward(p: Params, q, k, v, x, w_gate, phi_k=None, phi_v=None, rows=None,
         kc = compress(k, phi_k, p)
     if vc is None:
         vc = compress(v, phi_v, p)
-    g_all = gate(x[:, rows], w_gate)
+    g_all = gate(x[:, rows], w_gate, gate_mlp)
     W_full = remap_matrix(kc.shape[1], n_sel, p)
     out = {
         "o": np.zeros((B, R, Hq, dv)), "o_branch": np.zeros((3, B, R, Hq, dv)),
@@ -392,7 +409,7 @@ def forward(p: Params, q, k, v, x, w_gate, phi_k=None, phi_v=None, rows=None,
 
 
 def decode(p: Params, q, k_cache, v_cache, kc_cache, vc_cache, x, w_gate,
-           tie_scores=None, seq_lens=None, kv_win_cache=None) -> Dict[str, np.ndarray]:
+           tie_scores=None, seq_lens=None, kv_win_cache=None, gate_mlp=None) -> Dict[str, np.ndarray]:
     """One decode step: the query token sits at position S-1 of a length-S cache,
     its own key/value already stored there; compressed blocks come from the
     given compressed cache (complete blocks only), not from phi.
@@ -404,13 +421,14 @@ def decode(p: Params, q, k_cache, v_cache, kc_cache, vc_cache, x, w_gate,
     rows, and its query sits at seq_lens[b]-1; p_slc keeps the width of the full
     cache, zero beyond the sequence's own blocks.  kv_win_cache: optional
     (k, v) caches of the window branch when it has its own keys and values
-    (k_cache, v_cache then serve the selected branch only).
+    (k_cache, v_cache then serve the selected branch only).  gate_mlp: as in
+    forward.
     """
     B, S = k_cache.shape[:2]
     Hq, dv = q.shape[1], v_cache.shape[3]
     Hkv = k_cache.shape[2]
     n_sel = -(-S // p.l_sel)
-    g_all = gate(x[:, None], w_gate)[:, 0]
+    g_all = gate(x[:, None], w_gate, gate_mlp)[:, 0]
     out = {"o": np.zeros((B, Hq, dv)), "o_branch": np.zeros((3, B, Hq, dv)),
            "lse": np.zeros((3, B, Hq)), "p_slc": np.zeros((B, Hkv, n_sel)),
            "idx": np.full((B, Hkv, p.n), -1, dtype=np.int64),
@@ -461,7 +479,9 @@ def append_token(p: Params, k_cache, v_cache, kc_cache, vc_cache, k_new, v_new, 
 # scores or the discrete selection).  Per branch c, with dO_c = g_c * dO:
 #   dV += P^T dO_c;  dP = dO_c V^T;  D = rowsum(dO_c * O_c);  dS = P * (dP - D)
 #   dq += scale * dS K;  dK += scale * dS^T q
-# Gate: dg_c = <dO, O_c>, dW_g = sum_{b,t} x (x) (dg * g * (1 - g)).
+# Gate: dg_c = <dO, O_c>, dz = dg * g * (1 - g); linear gate: dW_g = x^T dz,
+# dx = dz W_g^T; gate MLP: dW_g = u^T dz, db2 = sum dz, du = dz W_g^T,
+# da = du * gelu'(a), dW1 = x^T da, db1 = sum da, dx = da W1^T.
 # Compressed-branch dK_cmp / dV_cmp flow back through phi to k / v and to the
 # phi parameters.  Rounding of the stored compressed tensors is not
 # differentiated (use io=None when comparing with finite differences).
@@ -599,7 +619,8 @@ def dq_rows(p: Params, q_rows, k, v, kc, vc, g_rows, d_o_rows, idx_rows, rows, k
     return dq
 
 
-def backward(p: Params, q, k, v, x, w_gate, phi_k, phi_v, d_o, idx, kv_slc=None, kv_win=None) -> Dict[str, object]:
+def backward(p: Params, q, k, v, x, w_gate, phi_k, phi_v, d_o, idx, kv_slc=None, kv_win=None,
+             gate_mlp=None) -> Dict[str, object]:
     """Gradients of L = sum(d_o * O) with block indices idx [B,T,Hkv,n] fixed.
 
     Returns dq, dk, dv, dw_gate, dphi_k, dphi_v (dicts keyed like phi), and the
@@ -608,7 +629,9 @@ def backward(p: Params, q, k, v, x, w_gate, phi_k, phi_v, d_o, idx, kv_slc=None,
     all branches dk = dk_phi + dk_slc + dk_win (dv alike).  With kv_slc, kv_win
     (independent keys/values per branch, as in forward) dk, dv are the
     compressed branch's part only and the others are the gradients of the
-    branches' own tensors.
+    branches' own tensors.  Gate: dw_gate (the output layer's gradient when
+    gate_mlp is given, which adds dgate_mlp = {w1, b1, b2}) and dx, the
+    gradient with respect to the gate input x.
     """
     B, T, Hq, dk_ = q.shape
     Hkv, dv_ = k.shape[2], v.shape[3]
@@ -616,7 +639,8 @@ def backward(p: Params, q, k, v, x, w_gate, phi_k, phi_v, d_o, idx, kv_slc=None,
     sc = _scale(p, dk_)
     kc = compress(k, phi_k, p)
     vc = compress(v, phi_v, p)
-    g_all = gate(x, w_gate)
+    z_all, a_gate, u_gate = gate_logits(x, w_gate, gate_mlp)
+    g_all = sigmoid(z_all)
     k_s, v_s = (k, v) if kv_slc is None else kv_slc
     k_w, v_w = (k, v) if kv_win is None else kv_win
     dq = np.zeros_like(q)
@@ -663,9 +687,20 @@ def backward(p: Params, q, k, v, x, w_gate, phi_k, phi_v, d_o, idx, kv_slc=None,
                         np.add.at(dvw[b, :, g], keys, dV)
     dk_phi, dphi_k = _phi_bwd(k, phi_k, dkc, p)
     dv_phi, dphi_v = _phi_bwd(v, phi_v, dvc, p)
-    dw_gate = np.einsum("btc,bthk->chk", x, dz)
+    if gate_mlp is None:
+        dw_gate = np.einsum("btc,bthk->chk", x, dz)
+        dx = np.einsum("bthk,chk->btc", dz, w_gate)
+        dgate_mlp = None
+    else:
+        dw_gate = np.einsum("btj,bthk->jhk", u_gate, dz)
+        du = np.einsum("bthk,jhk->btj", dz, w_gate)
+        da = du * gelu_grad(a_gate)
+        dgate_mlp = {"w1": np.einsum("btc,btj->cj", x, da), "b1": da.sum(axis=(0, 1)),
+                     "b2": dz.sum(axis=(0, 1))}
+        dx = np.einsum("btj,cj->btc", da, gate_mlp["w1"])
     split = kv_slc is not None or kv_win is not None
     return {"dq": dq, "dk": dk_phi if split else dk_phi + dks + dkw,
             "dv": dv_phi if split else dv_phi + dvs + dvw, "dw_gate": dw_gate,
+            "dx": dx, "dgate_mlp": dgate_mlp,
             "dphi_k": dphi_k, "dphi_v": dphi_v, "dk_cmp": dkc, "dv_cmp": dvc,
             "dk_phi": dk_phi, "dv_phi": dv_phi, "dk_slc": dks, "dv_slc": dvs, "dk_win": dkw, "dv_win": dvw}

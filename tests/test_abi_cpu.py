@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_abi_version_and_status_strings(lib):
     lib.nsa_abi_version.restype = ctypes.c_int
-    assert lib.nsa_abi_version() == 2
+    assert lib.nsa_abi_version() == 3
     lib.nsa_status_str.restype = ctypes.c_char_p
     lib.nsa_status_str.argtypes = [ctypes.c_int]
     assert lib.nsa_status_str(0) == b"ok"
@@ -48,7 +48,7 @@ def test_ctypes_mirror_matches_header_and_validation_runs_on_host():
     import long_context_sparse_phi_amd as nsa
     from long_context_sparse_phi_amd import _lib
     # nsa_params: 15 int32 + 1 float
-    assert ctypes.sizeof(_lib.nsa_params) == 64
+    assert ctypes.sizeof(_lib.nsa_params) == 68
     cfg = nsa.Config(B=1, T=1024, H_kv=1, G=4, d_k=64, d_v=64, n=4, w=128, phi="mean", dtype="fp32")
     assert nsa.workspace_size(cfg, _lib.NSA_OP_FWD_PREFILL) > 0
     bad = nsa.Config(B=1, T=1024, H_kv=1, G=3, d_k=64, d_v=64)
@@ -76,3 +76,16 @@ def test_dense_bwd_rejects_fp32_wide_heads_before_touching_memory():
     a = _lib.nsa_dense_bwd_args(**{n: 4096 for n in ("q", "k", "v", "o", "lse", "d_o", "dq", "dk", "dv")})
     st = lib.nsa_dense_bwd(ctypes.byref(p), ctypes.byref(a), None, 0, None)
     assert st == _lib.NSA_ERR_UNSUPPORTED
+
+
+def test_gate_hidden_width_is_validated_on_host():
+    import long_context_sparse_phi_amd as nsa
+    from long_context_sparse_phi_amd import _lib
+    ok = nsa.Config(B=1, T=512, H_kv=1, G=4, d_k=64, d_v=64, n=4, w=128, phi="mean", gate_hidden=64)
+    assert nsa.workspace_size(ok, _lib.NSA_OP_BWD) > nsa.workspace_size(
+        nsa.Config(B=1, T=512, H_kv=1, G=4, d_k=64, d_v=64, n=4, w=128, phi="mean"), _lib.NSA_OP_BWD)
+    for bad_width in (-1, 1025):
+        bad = nsa.Config(B=1, T=512, H_kv=1, G=4, d_k=64, d_v=64, n=4, w=128, phi="mean", gate_hidden=bad_width)
+        with pytest.raises(nsa.NSAError) as e:
+            nsa.workspace_size(bad, _lib.NSA_OP_FWD_PREFILL)
+        assert e.value.code == _lib.NSA_ERR_INVALID_ARG

@@ -94,6 +94,36 @@ def test_gate_zero_weights_is_half_and_matches_loops():
     assert np.all((g > 0) & (g < 1))
 
 
+def gate_mlp_weights(C, Hg, Hq, seed):
+    rng = np.random.default_rng(seed)
+    mlp = {"w1": rng.standard_normal((C, Hg)) / math.sqrt(C), "b1": 0.3 * rng.standard_normal(Hg),
+           "b2": 0.3 * rng.standard_normal((Hq, 3))}
+    return mlp, rng.standard_normal((Hg, Hq, 3)) / math.sqrt(Hg)
+
+
+def test_gate_mlp_matches_torch_gelu_sigmoid():
+    """Two-layer gate against torch's fp64 erf-GELU, linear and sigmoid."""
+    x = rand(2, 7, 9)
+    mlp, w2 = gate_mlp_weights(9, 11, 4, seed=3)
+    t = lambda a: torch.from_numpy(a)
+    h = torch.nn.functional.gelu(t(x) @ t(mlp["w1"]) + t(mlp["b1"]), approximate="none")
+    ref = torch.sigmoid(torch.einsum("btj,jhk->bthk", h, t(w2)) + t(mlp["b2"])).numpy()
+    np.testing.assert_allclose(O.gate(x, w2, mlp), ref, rtol=1e-13, atol=1e-15)
+
+
+def test_gate_mlp_reduces_to_linear_gate_on_the_gelu_identity_range():
+    """With the hidden pre-activations shifted far positive (gelu(a) = a to
+    double precision there) and the shift cancelled by b2, the MLP gate is the
+    linear gate with weights W1 W_g."""
+    x = rand(3, 5, 6)
+    mlp, w2 = gate_mlp_weights(6, 8, 4, seed=4)
+    c = 60.0
+    mlp["b1"] = np.full(8, c)
+    mlp["b2"] = -c * w2.sum(axis=0)
+    lin = O.gate(x, np.einsum("cj,jhk->chk", mlp["w1"], w2))
+    np.testing.assert_allclose(O.gate(x, w2, mlp), lin, rtol=1e-11, atol=1e-12)
+
+
 # ---------------------------------------------------------------- compression
 
 def test_n_cmp_visible_closed_form():
@@ -609,6 +639,78 @@ def test_backward_dense_case_matches_torch_autograd():
     np.testing.assert_allclose(gr["dk"], tk.grad.numpy(), rtol=1e-10, atol=1e-11)
     np.testing.assert_allclose(gr["dv"], tv.grad.numpy(), rtol=1e-10, atol=1e-11)
     np.testing.assert_allclose(gr["dw_gate"], tw.grad.numpy(), rtol=1e-10, atol=1e-11)
+
+
+@pytest.mark.parametrize("mlp_gate", [False, True])
+def test_backward_gate_and_gate_input_match_torch_autograd(mlp_gate):
+    """Dense case (every branch attends all past keys) with torch fp64 autograd
+    through a linear or two-layer gate: dw_gate, the gate MLP's weights and
+    dx, the gradient with respect to the gate input."""
+    T, C, Hg, Hq = 36, 5, 7, 4
+    p, inp = small_problem(B=2, T=T, Hkv=2, G=2, dk=6, dv=5, C=C, l=1, d=1, l_sel=8,
+                           n=5, w=T, phi="mean", seed=21)
+    mlp = None
+    if mlp_gate:
+        mlp, inp["w_gate"] = gate_mlp_weights(C, Hg, Hq, seed=22)
+    rng = np.random.default_rng(23)
+    d_o = rng.standard_normal((2, T, Hq, 5))
+    idx = O.forward(p, **inp, gate_mlp=mlp)["idx"]
+    gr = O.backward(p, d_o=d_o, idx=idx, **inp, gate_mlp=mlp)
+    tq, tk, tv, tx, tw = (torch.tensor(inp[n], requires_grad=True) for n in ("q", "k", "v", "x", "w_gate"))
+    dense = torch.nn.functional.scaled_dot_product_attention(
+        tq.permute(0, 2, 1, 3), tk.permute(0, 2, 1, 3).repeat_interleave(2, 1),
+        tv.permute(0, 2, 1, 3).repeat_interleave(2, 1), is_causal=True).permute(0, 2, 1, 3)
+    if mlp_gate:
+        tm = {k: torch.tensor(v, requires_grad=True) for k, v in mlp.items()}
+        h = torch.nn.functional.gelu(tx @ tm["w1"] + tm["b1"], approximate="none")
+        z = torch.einsum("btj,jhk->bthk", h, tw) + tm["b2"]
+    else:
+        z = torch.einsum("btc,chk->bthk", tx, tw)
+    out = torch.sigmoid(z).sum(-1, keepdim=True) * dense
+    (out * torch.from_numpy(d_o)).sum().backward()
+    tol = dict(rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(gr["dq"], tq.grad.numpy(), **tol)
+    np.testing.assert_allclose(gr["dk"], tk.grad.numpy(), **tol)
+    np.testing.assert_allclose(gr["dw_gate"], tw.grad.numpy(), **tol)
+    np.testing.assert_allclose(gr["dx"], tx.grad.numpy(), **tol)
+    if mlp_gate:
+        for key in ("w1", "b1", "b2"):
+            np.testing.assert_allclose(gr["dgate_mlp"][key], tm[key].grad.numpy(), **tol)
+    else:
+        assert gr["dgate_mlp"] is None
+
+
+def test_gate_mlp_backward_matches_finite_differences_with_real_selection():
+    p, inp = small_problem(B=1, T=26, Hkv=2, G=2, dk=3, dv=2, C=4, phi="mlp", l=4, d=2,
+                           l_sel=8, n=3, w=5, hidden=4, seed=31)
+    p = O.Params(l=4, d=2, l_sel=8, n=3, w=5, phi="mlp", io=None)
+    mlp, inp["w_gate"] = gate_mlp_weights(4, 6, 4, seed=32)
+    rng = np.random.default_rng(33)
+    d_o = rng.standard_normal((1, 26, 4, 2))
+    idx = O.forward(p, **inp, gate_mlp=mlp)["idx"]
+    gr = O.backward(p, d_o=d_o, idx=idx, **inp, gate_mlp=mlp)
+    eps = 1e-6
+
+    def loss():
+        return float((O.forward(p, **inp, idx=idx, gate_mlp=mlp)["o"] * d_o).sum())
+
+    def check(arr, grad, n_pick=10):
+        flat = arr.reshape(-1)
+        for i in rng.choice(flat.size, size=min(n_pick, flat.size), replace=False):
+            old = flat[i]
+            flat[i] = old + eps
+            lp = loss()
+            flat[i] = old - eps
+            lm = loss()
+            flat[i] = old
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - grad.reshape(-1)[i]) < 1e-6 + 1e-6 * abs(fd), (i, fd, grad.reshape(-1)[i])
+
+    check(inp["x"], gr["dx"])
+    check(inp["w_gate"], gr["dw_gate"])
+    for key in ("w1", "b1", "b2"):
+        check(mlp[key], gr["dgate_mlp"][key])
+    check(inp["q"], gr["dq"])
 
 
 def test_dense_causal_matches_torch_sdpa():
