@@ -533,6 +533,58 @@ def run_backward(steps, warmup, wname="train_16k"):
             "training_forward_ms": round(fwd_ms, 4)}
 
 
+# ---------------------------------------------------------------- projection layer
+
+def run_layer(reps=5, wname="train_16k"):
+    """The projection layer around the operator (q/k/v/o projections as rocBLAS
+    GEMMs, layer width C = gate_dim) at the training shape: layer forward and
+    backward against the operator's own forward and backward on the same
+    projected inputs, so that the difference is the projections' cost."""
+    import torch
+    import long_context_sparse_phi_amd as nsa
+    import nsa_inputs as NI
+
+    w = NI.workload(wname)
+    cfg = nsa.config_from_workload(w)
+    log(f"generating layer inputs for {wname}")
+    d = {k: ({kk: vv.to("cuda:0") for kk, vv in v.items()} if isinstance(v, dict) else v.to("cuda:0"))
+         for k, v in NI.make_layer_inputs(w, 0).items()}
+    args = (cfg, d["h"], d["proj"], d["w_gate"], d["phi_k"], d["phi_v"])
+    f = nsa.nsa_layer_fwd(*args)
+    g = nsa.nsa_layer_bwd(*args, f, d["dy"])
+    d_o = NI.make_grad_output(w, 0).to("cuda:0")
+    op_args = (cfg, f["q"], f["k"], f["v"], d["h"], d["w_gate"], d["phi_k"], d["phi_v"])
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ev = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            ev.append((e0, e1))
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ev) / reps
+
+    fws, bws = f["_workspace"], g["_workspace"]
+    layer_f = timed(lambda: nsa.nsa_layer_fwd(*args, workspace=fws))
+    layer_b = timed(lambda: nsa.nsa_layer_bwd(*args, f, d["dy"], workspace=bws))
+    op_f = timed(lambda: nsa.nsa_fwd_prefill(*op_args, save_for_backward=True, workspace=fws))
+    op_b = timed(lambda: nsa.nsa_bwd(*op_args, f, d_o, want_dx=True))
+    ntok, C = w.B * w.T, w.gate_dim
+    proj_fwd = 2.0 * ntok * C * (w.H_q * w.d_k + w.H_kv * (w.d_k + w.d_v) + w.H_q * w.d_v)
+    pf, pb = max(layer_f - op_f, 1e-9), max(layer_b - op_b, 1e-9)
+    return {"workload": wname, "C": C, "reps": reps,
+            "layer_fwd_ms": round(layer_f, 4), "layer_bwd_ms": round(layer_b, 4),
+            "operator_fwd_ms": round(op_f, 4), "operator_bwd_ms": round(op_b, 4),
+            "projection_tflop_fwd": round(proj_fwd / 1e12, 4), "projection_tflop_bwd": round(2 * proj_fwd / 1e12, 4),
+            "projection_fwd_tflops": round(proj_fwd / (pf * 1e-3) / 1e12, 1),
+            "projection_bwd_tflops": round(2 * proj_fwd / (pb * 1e-3) / 1e12, 1)}
+
+
 # ---------------------------------------------------------------- dense baseline
 
 def run_dense_comparison(lengths=(8192, 16384, 32768, 65536), wname="prefill_64k", reps=2,
@@ -665,6 +717,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--bwd-steps", type=int, default=5)
     ap.add_argument("--no-dense", action="store_true", help="skip the NSA-vs-dense comparison")
+    ap.add_argument("--no-layer", action="store_true", help="skip the projection-layer leg")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the 1 GiB elementwise kernel used to scale the PMC byte counters")
     ap.add_argument("--traffic-from", nargs=4, metavar=("CAL_FETCH", "CAL_WRITE", "RUN_FETCH", "RUN_WRITE"),
@@ -708,6 +761,8 @@ def main():
         out["decode"] = run_decode(args.decode_steps, 3)
     if not args.no_backward:
         out["backward"] = run_backward(args.bwd_steps, 2)
+    if not args.no_layer:
+        out["layer"] = run_layer()
     if not args.no_dense:
         out["dense_baseline"] = run_dense_comparison()
     if not args.no_cpu_baseline:

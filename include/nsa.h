@@ -57,14 +57,16 @@ typedef enum nsa_status {
   NSA_ERR_UNSUPPORTED = 2,  /* valid but not built: device, dtype, head dims */
   NSA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
   NSA_ERR_HIP = 4,          /* a HIP runtime call failed */
-  NSA_ERR_INTERNAL = 5
+  NSA_ERR_INTERNAL = 5,
+  NSA_ERR_BLAS = 6          /* a rocBLAS call of the projection layer failed */
 } nsa_status;
 
 typedef enum nsa_dtype { NSA_BF16 = 0, NSA_FP32 = 1 } nsa_dtype;
 typedef enum nsa_phi_kind { NSA_PHI_MEANPOOL = 0, NSA_PHI_MLP = 1 } nsa_phi_kind;
 typedef enum nsa_op {
   NSA_OP_FWD_PREFILL = 0, NSA_OP_FWD_DECODE = 1, NSA_OP_BWD = 2, NSA_OP_COMPRESS = 3,
-  NSA_OP_DENSE = 4, NSA_OP_APPEND = 5, NSA_OP_DENSE_BWD = 6
+  NSA_OP_DENSE = 4, NSA_OP_APPEND = 5, NSA_OP_DENSE_BWD = 6, NSA_OP_LAYER_FWD = 7,
+  NSA_OP_LAYER_BWD = 8
 } nsa_op;
 
 /* Shapes and hyper-parameters.
@@ -257,6 +259,49 @@ typedef struct nsa_dense_bwd_args {
   void *dq, *dk, *dv;
 } nsa_dense_bwd_args;
 
+/* One attention layer around the operator: projections of the layer input to
+ * queries, keys and values, NSA with the layer input as the gate input, and
+ * the output projection (the module shape of the xookee explainer's
+ * 三种注意力如何组合 §2; the youleyou page, 整体框架, derives q, k, v and the
+ * gates from the same input):
+ *   q = h w_q, k = h w_k, v = h w_v (rounded to io_dtype),
+ *   o = NSA(q, k, v; gate input h), y = o w_o (io_dtype).
+ * gate_dim C is the layer width.  Inputs (io_dtype, 16-byte aligned):
+ *   h [B,T,C], w_q [C, Hq*dk], w_k [C, Hkv*dk], w_v [C, Hkv*dv], w_o [Hq*dv, C],
+ *   w_gate, gate_mlp, phi_k, phi_v as for nsa_fwd_prefill.
+ * Outputs: y [B,T,C]; q [B,T,Hq,dk], k [B,T,Hkv,dk], v [B,T,Hkv,dv] and
+ *   o [B,T,Hq,dv] (io_dtype, required: the backward reads them);
+ *   k_cmp, v_cmp, lse, idx, o_branch as nsa_fwd_prefill's (optional; the
+ *   backward needs k_cmp, v_cmp, lse and idx).
+ * The projections run as rocBLAS GEMMs with fp32 accumulation on the stream.
+ * Workspace: NSA_OP_LAYER_FWD. */
+typedef struct nsa_layer_args {
+  const void *h, *w_q, *w_k, *w_v, *w_o, *w_gate;
+  nsa_gate_mlp gate_mlp;
+  nsa_phi_weights phi_k, phi_v;
+  void *y, *q, *k, *v, *o;
+  void *k_cmp, *v_cmp, *lse, *idx, *o_branch;
+} nsa_layer_args;
+
+/* Backward of nsa_layer_fwd with the selected blocks fixed.  Inputs: the
+ * forward's inputs, its saved q, k, v, o, k_cmp, v_cmp, lse, idx (o_branch
+ * optional, as for nsa_bwd), and dy [B,T,C] io_dtype.  dO = dy w_o^T is
+ * rounded to io_dtype (the operator's backward takes dO in io_dtype).
+ * Outputs (fp32, overwritten): dh [B,T,C] (through q, k, v and the gate),
+ * dw_q, dw_k, dw_v, dw_o (the weights' shapes), dw_gate, d_gate_mlp
+ * (gate_hidden > 0), d_phi_k, d_phi_v (NSA_PHI_MLP).
+ * Workspace: NSA_OP_LAYER_BWD. */
+typedef struct nsa_layer_bwd_args {
+  const void *h, *w_q, *w_k, *w_v, *w_o, *w_gate;
+  nsa_gate_mlp gate_mlp;
+  nsa_phi_weights phi_k, phi_v;
+  const void *q, *k, *v, *o, *k_cmp, *v_cmp, *lse, *idx, *o_branch;
+  const void *dy;
+  void *dh, *dw_q, *dw_k, *dw_v, *dw_o, *dw_gate;
+  nsa_gate_grads d_gate_mlp;
+  nsa_phi_grads d_phi_k, d_phi_v;
+} nsa_layer_bwd_args;
+
 /* Version of this header the library was built from (NSA_ABI_VERSION). */
 int nsa_abi_version(void);
 
@@ -286,6 +331,10 @@ nsa_status nsa_dense_bwd(const nsa_params* p, const nsa_dense_bwd_args* a, void*
                          size_t ws_bytes, void* stream);
 nsa_status nsa_decode_append(const nsa_params* p, const nsa_append_args* a, void* ws,
                              size_t ws_bytes, void* stream);
+nsa_status nsa_layer_fwd(const nsa_params* p, const nsa_layer_args* a, void* ws,
+                         size_t ws_bytes, void* stream);
+nsa_status nsa_layer_bwd(const nsa_params* p, const nsa_layer_bwd_args* a, void* ws,
+                         size_t ws_bytes, void* stream);
 
 /* Timed variants, for measurement.  Identical work to the entry points
  * above; in addition hipEventRecord(events[i], stream) is issued before stage

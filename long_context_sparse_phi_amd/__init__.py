@@ -17,11 +17,12 @@ import torch
 
 from . import _lib
 from ._lib import (NSA_BF16, NSA_FP32, NSA_OP_APPEND, NSA_OP_BWD, NSA_OP_COMPRESS, NSA_OP_DENSE,
-                   NSA_OP_DENSE_BWD, NSA_OP_FWD_DECODE, NSA_OP_FWD_PREFILL,
-                   NSA_PHI_MEANPOOL, NSA_PHI_MLP, NSAError)
+                   NSA_OP_DENSE_BWD, NSA_OP_FWD_DECODE, NSA_OP_FWD_PREFILL, NSA_OP_LAYER_BWD,
+                   NSA_OP_LAYER_FWD, NSA_PHI_MEANPOOL, NSA_PHI_MLP, NSAError)
 
 __all__ = ["Config", "workspace_size", "nsa_compress", "nsa_fwd_prefill", "nsa_fwd_decode",
-           "nsa_decode_append", "nsa_bwd", "nsa_dense_fwd", "nsa_dense_bwd", "load_library", "NSAError"]
+           "nsa_decode_append", "nsa_bwd", "nsa_dense_fwd", "nsa_dense_bwd", "nsa_layer_fwd", "nsa_layer_bwd",
+           "load_library", "NSAError"]
 
 load_library = _lib.load
 
@@ -432,6 +433,104 @@ def nsa_dense_bwd(cfg: Config, q, k, v, o, lse, d_o, *,
     st = _lib.load().nsa_dense_bwd(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(), _stream(dev))
     if st != 0:
         raise NSAError("nsa_dense_bwd", st)
+    res["_workspace"] = ws
+    return res
+
+
+def _layer_weights(cfg: Config, proj: Dict[str, torch.Tensor], dev):
+    C, dt = cfg.gate_dim, cfg.torch_dtype
+    shapes = {"w_q": (C, cfg.H_q * cfg.d_k), "w_k": (C, cfg.H_kv * cfg.d_k), "w_v": (C, cfg.H_kv * cfg.d_v),
+              "w_o": (cfg.H_q * cfg.d_v, C)}
+    for k, shp in shapes.items():
+        _check(proj[k], f"proj.{k}", shp, dt, dev)
+    return {k: proj[k].data_ptr() for k in shapes}
+
+
+def nsa_layer_fwd(cfg: Config, h, proj: Dict[str, torch.Tensor], w_gate, phi_k=None, phi_v=None, *,
+                  gate_mlp=None, workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+    """Attention layer around the operator: q, k, v = h w_q, h w_k, h w_v;
+    o = NSA(q, k, v) with h as the gate input; y = o w_o.  h [B,T,C] with
+    C = cfg.gate_dim; proj = {w_q [C,Hq*dk], w_k [C,Hkv*dk], w_v [C,Hkv*dv],
+    w_o [Hq*dv,C]}.  Returns y and what nsa_layer_bwd needs (q, k, v, o,
+    k_cmp, v_cmp, lse, idx, o_branch)."""
+    dev = h.device
+    dt = cfg.torch_dtype
+    B, T, Hq, Hkv = cfg.B, cfg.T, cfg.H_q, cfg.H_kv
+    _check(h, "h", (B, T, cfg.gate_dim), dt, dev)
+    _check(w_gate, "w_gate", (cfg.gate_in, Hq, 3), dt, dev)
+    a = _lib.nsa_layer_args(h=h.data_ptr(), w_gate=w_gate.data_ptr(), **_layer_weights(cfg, proj, dev))
+    res = {"y": torch.empty(B, T, cfg.gate_dim, dtype=dt, device=dev),
+           "q": torch.empty(B, T, Hq, cfg.d_k, dtype=dt, device=dev),
+           "k": torch.empty(B, T, Hkv, cfg.d_k, dtype=dt, device=dev),
+           "v": torch.empty(B, T, Hkv, cfg.d_v, dtype=dt, device=dev),
+           "o": torch.empty(B, T, Hq, cfg.d_v, dtype=dt, device=dev),
+           "k_cmp": torch.empty(B, cfg.n_cmp, Hkv, cfg.d_k, dtype=dt, device=dev),
+           "v_cmp": torch.empty(B, cfg.n_cmp, Hkv, cfg.d_v, dtype=dt, device=dev),
+           "lse": torch.empty(3, B, T, Hq, dtype=torch.float32, device=dev),
+           "idx": torch.empty(B, T, Hkv, cfg.n, dtype=torch.int32, device=dev),
+           "o_branch": torch.empty(3, B, T, Hq, cfg.d_v, dtype=torch.float32, device=dev)}
+    for name, t in res.items():
+        setattr(a, name, t.data_ptr() if t.numel() else None)
+    a.phi_k = _phi_struct(cfg, phi_k, cfg.d_k, dev)
+    a.phi_v = _phi_struct(cfg, phi_v, cfg.d_v, dev)
+    a.gate_mlp = _gate_struct(cfg, gate_mlp, dev)
+    ws = _workspace(cfg, NSA_OP_LAYER_FWD, dev, workspace)
+    p = cfg.params()
+    st = _lib.load().nsa_layer_fwd(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(), _stream(dev))
+    if st != 0:
+        raise NSAError("nsa_layer_fwd", st)
+    res["_workspace"] = ws
+    return res
+
+
+def nsa_layer_bwd(cfg: Config, h, proj: Dict[str, torch.Tensor], w_gate, phi_k, phi_v,
+                  saved: Dict[str, torch.Tensor], dy, *, gate_mlp=None,
+                  workspace: Optional[torch.Tensor] = None) -> Dict[str, object]:
+    """Backward of nsa_layer_fwd (saved = its result) for dy [B,T,C]: dh,
+    dw_q, dw_k, dw_v, dw_o, dw_gate, and d_gate_mlp / d_phi_k / d_phi_v where
+    those weights exist; all fp32."""
+    dev = h.device
+    dt = cfg.torch_dtype
+    B, T, Hq = cfg.B, cfg.T, cfg.H_q
+    C = cfg.gate_dim
+    _check(h, "h", (B, T, C), dt, dev)
+    _check(dy, "dy", (B, T, C), dt, dev)
+    _check(w_gate, "w_gate", (cfg.gate_in, Hq, 3), dt, dev)
+    f32 = torch.float32
+    a = _lib.nsa_layer_bwd_args(h=h.data_ptr(), w_gate=w_gate.data_ptr(), dy=dy.data_ptr(),
+                                **_layer_weights(cfg, proj, dev))
+    for name in ("q", "k", "v", "o", "k_cmp", "v_cmp", "lse", "idx", "o_branch"):
+        t = saved[name]
+        setattr(a, name, t.data_ptr() if t.numel() else None)
+    res = {"dh": torch.empty(B, T, C, dtype=f32, device=dev),
+           "dw_gate": torch.empty(cfg.gate_in, Hq, 3, dtype=f32, device=dev)}
+    for k, t in proj.items():
+        res["d" + k] = torch.empty(t.shape, dtype=f32, device=dev)
+    for name in ("dh", "dw_gate", "dw_q", "dw_k", "dw_v", "dw_o"):
+        setattr(a, name, res[name].data_ptr())
+    a.phi_k = _phi_struct(cfg, phi_k, cfg.d_k, dev)
+    a.phi_v = _phi_struct(cfg, phi_v, cfg.d_v, dev)
+    a.gate_mlp = _gate_struct(cfg, gate_mlp, dev)
+    if cfg.gate_hidden:
+        gg = {"w1": torch.empty(C, cfg.gate_hidden, dtype=f32, device=dev),
+              "b1": torch.empty(cfg.gate_hidden, dtype=f32, device=dev),
+              "b2": torch.empty(Hq, 3, dtype=f32, device=dev)}
+        a.d_gate_mlp = _lib.nsa_gate_grads(**{kk: vv.data_ptr() for kk, vv in gg.items()})
+        res["d_gate_mlp"] = gg
+    if cfg.phi == "mlp":
+        for tag, D in (("d_phi_k", cfg.d_k), ("d_phi_v", cfg.d_v)):
+            g = {"pe": torch.empty(cfg.l, D, dtype=f32, device=dev),
+                 "w1": torch.empty(cfg.l * D, cfg.hidden, dtype=f32, device=dev),
+                 "b1": torch.empty(cfg.hidden, dtype=f32, device=dev),
+                 "w2": torch.empty(cfg.hidden, D, dtype=f32, device=dev),
+                 "b2": torch.empty(D, dtype=f32, device=dev)}
+            setattr(a, tag, _lib.nsa_phi_grads(**{kk: vv.data_ptr() for kk, vv in g.items()}))
+            res[tag] = g
+    ws = _workspace(cfg, NSA_OP_LAYER_BWD, dev, workspace)
+    p = cfg.params()
+    st = _lib.load().nsa_layer_bwd(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(), _stream(dev))
+    if st != 0:
+        raise NSAError("nsa_layer_bwd", st)
     res["_workspace"] = ws
     return res
 

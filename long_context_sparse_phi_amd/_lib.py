@@ -11,11 +11,12 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libnsa.so")
 
-NSA_OK, NSA_ERR_INVALID_ARG, NSA_ERR_UNSUPPORTED, NSA_ERR_WORKSPACE, NSA_ERR_HIP, NSA_ERR_INTERNAL = range(6)
+(NSA_OK, NSA_ERR_INVALID_ARG, NSA_ERR_UNSUPPORTED, NSA_ERR_WORKSPACE, NSA_ERR_HIP, NSA_ERR_INTERNAL,
+ NSA_ERR_BLAS) = range(7)
 NSA_BF16, NSA_FP32 = 0, 1
 NSA_PHI_MEANPOOL, NSA_PHI_MLP = 0, 1
 (NSA_OP_FWD_PREFILL, NSA_OP_FWD_DECODE, NSA_OP_BWD, NSA_OP_COMPRESS, NSA_OP_DENSE, NSA_OP_APPEND,
- NSA_OP_DENSE_BWD) = range(7)
+ NSA_OP_DENSE_BWD, NSA_OP_LAYER_FWD, NSA_OP_LAYER_BWD) = range(9)
 ABI_VERSION = 3
 
 _vp = ctypes.c_void_p
@@ -87,9 +88,23 @@ class nsa_dense_bwd_args(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("q", "k", "v", "o", "lse", "d_o", "dq", "dk", "dv")]
 
 
+class nsa_layer_args(ctypes.Structure):
+    _fields_ = ([(n, _vp) for n in ("h", "w_q", "w_k", "w_v", "w_o", "w_gate")] +
+                [("gate_mlp", nsa_gate_mlp), ("phi_k", nsa_phi_weights), ("phi_v", nsa_phi_weights)] +
+                [(n, _vp) for n in ("y", "q", "k", "v", "o", "k_cmp", "v_cmp", "lse", "idx", "o_branch")])
+
+
+class nsa_layer_bwd_args(ctypes.Structure):
+    _fields_ = ([(n, _vp) for n in ("h", "w_q", "w_k", "w_v", "w_o", "w_gate")] +
+                [("gate_mlp", nsa_gate_mlp), ("phi_k", nsa_phi_weights), ("phi_v", nsa_phi_weights)] +
+                [(n, _vp) for n in ("q", "k", "v", "o", "k_cmp", "v_cmp", "lse", "idx", "o_branch", "dy",
+                                    "dh", "dw_q", "dw_k", "dw_v", "dw_o", "dw_gate")] +
+                [("d_gate_mlp", nsa_gate_grads), ("d_phi_k", nsa_phi_grads), ("d_phi_v", nsa_phi_grads)])
+
+
 EXPORTS = ("nsa_abi_version", "nsa_status_str", "nsa_workspace_size", "nsa_compress",
            "nsa_fwd_prefill", "nsa_fwd_decode", "nsa_bwd", "nsa_dense_fwd",
-           "nsa_decode_append", "nsa_dense_bwd")
+           "nsa_decode_append", "nsa_dense_bwd", "nsa_layer_fwd", "nsa_layer_bwd")
 
 _LIB = None
 
@@ -115,7 +130,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                  ctypes.c_size_t, _vp]
     for name, argt in (("nsa_fwd_prefill", nsa_prefill_args), ("nsa_fwd_decode", nsa_decode_args),
                        ("nsa_bwd", nsa_bwd_args), ("nsa_dense_fwd", nsa_dense_args),
-                       ("nsa_decode_append", nsa_append_args), ("nsa_dense_bwd", nsa_dense_bwd_args)):
+                       ("nsa_decode_append", nsa_append_args), ("nsa_dense_bwd", nsa_dense_bwd_args),
+                       ("nsa_layer_fwd", nsa_layer_args), ("nsa_layer_bwd", nsa_layer_bwd_args)):
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [P(nsa_params), P(argt), _vp, ctypes.c_size_t, _vp]

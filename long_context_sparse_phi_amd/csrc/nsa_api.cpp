@@ -2,8 +2,10 @@
 // launch sequence of each entry point.  Nothing is enqueued until every check
 // has passed.
 #include <hip/hip_runtime.h>
+#include <rocblas/rocblas.h>
 
 #include <atomic>
+#include <mutex>
 #include <initializer_list>
 #include <cmath>
 #include <cstring>
@@ -200,6 +202,71 @@ bool phi_ok(const nsa_phi_weights& w) {
   return true;
 }
 
+// ---------------------------------------------------------------------------
+// Projection layer: rocBLAS GEMMs around the operator.
+// ---------------------------------------------------------------------------
+
+// One rocBLAS handle per device, created on first use with that device
+// current; the mutex serialises setting the stream and enqueuing the GEMMs.
+std::mutex g_blas_mu;
+rocblas_handle g_blas[64];
+
+nsa_status blas_handle(rocblas_handle* h) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return NSA_ERR_HIP;
+  if (dev < 0 || dev >= 64) return NSA_ERR_UNSUPPORTED;
+  if (!g_blas[dev] && rocblas_create_handle(&g_blas[dev]) != rocblas_status_success) {
+    g_blas[dev] = nullptr;
+    return NSA_ERR_BLAS;
+  }
+  *h = g_blas[dev];
+  return NSA_OK;
+}
+
+// Row-major C[M,N] (leading dim ldc) = op(A) op(B) + beta C, with op(A) [M,K]
+// and op(B) [K,N]; ta / tb say that A / B are stored transposed ([K,M], [N,K]).
+// rocBLAS is column-major, where a row-major matrix reads as its transpose, so
+// the call computes C^T = op(B)^T op(A)^T with the operands swapped.
+bool rm_gemm(rocblas_handle h, bool ta, bool tb, int M, int N, int K, const void* A, rocblas_datatype at, int lda,
+             const void* B, rocblas_datatype bt, int ldb, float beta, void* C, rocblas_datatype ct, int ldc) {
+  if (M == 0 || N == 0) return true;
+  const float alpha = 1.f;
+  return rocblas_gemm_ex(h, tb ? rocblas_operation_transpose : rocblas_operation_none,
+                         ta ? rocblas_operation_transpose : rocblas_operation_none, N, M, K, &alpha, B, bt, ldb, A,
+                         at, lda, &beta, C, ct, ldc, C, ct, ldc, rocblas_datatype_f32_r, rocblas_gemm_algo_standard,
+                         0, 0) == rocblas_status_success;
+}
+
+struct LayerBwdWs {
+  void* op_ws;    // the operator's backward workspace
+  void* d_o;      // dO = dy w_o^T, io dtype [B*T, Hq*dv]
+  float *dq, *dk, *dv;
+  float* h32;     // the layer input in fp32 (bf16 I/O only)
+  float* w32;     // one projection weight in fp32 at a time
+};
+
+size_t plan_layer_bwd(const Dims& dm, void* ws, LayerBwdWs* w) {
+  Carve c(ws);
+  LayerBwdWs t;
+  if (!w) w = &t;
+  const size_t ntok = (size_t)dm.B * dm.T, es = esize(dm);
+  w->op_ws = c.take(bwd_ws_bytes(dm));
+  w->d_o = c.take(ntok * dm.Hq * dm.dv * es);
+  w->dq = (float*)c.take(ntok * dm.Hq * dm.dk * 4);
+  w->dk = (float*)c.take(ntok * dm.Hkv * dm.dk * 4);
+  w->dv = (float*)c.take(ntok * dm.Hkv * dm.dv * 4);
+  w->h32 = dm.io == IO_BF16 ? (float*)c.take(ntok * dm.C * 4) : nullptr;
+  const size_t wmax = (size_t)dm.C * (dm.Hq * dm.dk > dm.Hkv * dm.dv ? dm.Hq * dm.dk : dm.Hkv * dm.dv);
+  w->w32 = dm.io == IO_BF16 ? (float*)c.take(wmax * 4) : nullptr;
+  return c.off;
+}
+
+bool layer_weights_ok(const void* const* ps, int n) {
+  for (int i = 0; i < n; ++i)
+    if (!ps[i] || !aligned16(ps[i])) return false;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -214,6 +281,7 @@ const char* nsa_status_str(nsa_status s) {
     case NSA_ERR_WORKSPACE: return "workspace missing or too small";
     case NSA_ERR_HIP: return "HIP runtime error";
     case NSA_ERR_INTERNAL: return "internal error";
+    case NSA_ERR_BLAS: return "rocBLAS error";
   }
   return "unknown status";
 }
@@ -233,6 +301,8 @@ nsa_status nsa_workspace_size(const nsa_params* p, nsa_op op, size_t* bytes) {
       case NSA_OP_DENSE: *bytes = dense_ws_bytes(dm); return NSA_OK;
       case NSA_OP_APPEND: *bytes = append_ws_bytes(dm) > 0 ? append_ws_bytes(dm) : 256; return NSA_OK;
       case NSA_OP_DENSE_BWD: *bytes = dense_bwd_ws_bytes(dm); return NSA_OK;
+      case NSA_OP_LAYER_FWD: *bytes = plan_prefill(dm, nullptr, &w); return NSA_OK;
+      case NSA_OP_LAYER_BWD: *bytes = plan_layer_bwd(dm, nullptr, nullptr); return NSA_OK;
     }
     return NSA_ERR_INVALID_ARG;
   } catch (...) {
@@ -258,8 +328,10 @@ nsa_status nsa_compress(const nsa_params* p, int is_value, const void* x, const 
   }
 }
 
+// check_only: run every check (the device's included) and return without
+// enqueuing anything.
 static nsa_status prefill_impl(const nsa_params* p, const nsa_prefill_args* a, void* ws, size_t ws_bytes,
-                               void* stream, void* const* events, int n_events) {
+                               void* stream, void* const* events, int n_events, bool check_only = false) {
   try {
     Dims dm;
     nsa_status st = make_dims(p, &dm);
@@ -280,6 +352,7 @@ static nsa_status prefill_impl(const nsa_params* p, const nsa_prefill_args* a, v
     const size_t need = plan_prefill(dm, nullptr, &w);
     if (ws_bytes < need || !ws || !aligned16(ws)) return NSA_ERR_WORKSPACE;
     if ((st = check_device()) != NSA_OK) return st;
+    if (check_only) return NSA_OK;
     plan_prefill(dm, ws, &w);
     hipStream_t s = (hipStream_t)stream;
     Stages sg(events, s);
@@ -461,7 +534,7 @@ nsa_status nsa_fwd_decode_timed(const nsa_params* p, const nsa_decode_args* a, v
 }
 
 static nsa_status bwd_impl(const nsa_params* p, const nsa_bwd_args* a, void* ws, size_t ws_bytes, void* stream,
-                           void* const* events, int n_events) {
+                           void* const* events, int n_events, bool check_only = false) {
   try {
     Dims dm;
     nsa_status st = make_dims(p, &dm);
@@ -493,6 +566,7 @@ static nsa_status bwd_impl(const nsa_params* p, const nsa_bwd_args* a, void* ws,
     const size_t need = bwd_ws_bytes(dm);
     if (ws_bytes < need || !ws || !aligned16(ws)) return NSA_ERR_WORKSPACE;
     if ((st = check_device()) != NSA_OK) return st;
+    if (check_only) return NSA_OK;
     return hip_status(launch_bwd(dm, a, ws, (hipStream_t)stream, events));
   } catch (...) {
     return NSA_ERR_INTERNAL;
@@ -507,6 +581,111 @@ nsa_status nsa_bwd_timed(const nsa_params* p, const nsa_bwd_args* a, void* ws, s
                          void* const* events, int n_events) {
   if (!events) return NSA_ERR_INVALID_ARG;
   return bwd_impl(p, a, ws, ws_bytes, stream, events, n_events);
+}
+
+nsa_status nsa_layer_fwd(const nsa_params* p, const nsa_layer_args* a, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    Dims dm;
+    nsa_status st = make_dims(p, &dm);
+    if (st != NSA_OK) return st;
+    if (!a) return NSA_ERR_INVALID_ARG;
+    const void* req[] = {a->h, a->w_q, a->w_k, a->w_v, a->w_o, a->y, a->q, a->k, a->v, a->o};
+    if (!layer_weights_ok(req, 10)) return NSA_ERR_INVALID_ARG;
+    nsa_prefill_args pa{};
+    pa.q = a->q; pa.k = a->k; pa.v = a->v; pa.x = a->h; pa.w_gate = a->w_gate;
+    pa.phi_k = a->phi_k; pa.phi_v = a->phi_v; pa.o = a->o;
+    pa.k_cmp = a->k_cmp; pa.v_cmp = a->v_cmp; pa.lse = a->lse; pa.idx = a->idx; pa.o_branch = a->o_branch;
+    pa.gate_mlp = a->gate_mlp;
+    if ((st = prefill_impl(p, &pa, ws, ws_bytes, stream, nullptr, 0, true)) != NSA_OK) return st;
+    const rocblas_datatype T = dm.io == IO_BF16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
+    const int ntok = dm.B * dm.T, C = dm.C;
+    const int nq = dm.Hq * dm.dk, nk = dm.Hkv * dm.dk, nv = dm.Hkv * dm.dv, no = dm.Hq * dm.dv;
+    {
+      std::lock_guard<std::mutex> lk(g_blas_mu);
+      rocblas_handle h;
+      if ((st = blas_handle(&h)) != NSA_OK) return st;
+      if (rocblas_set_stream(h, (hipStream_t)stream) != rocblas_status_success) return NSA_ERR_BLAS;
+      if (!rm_gemm(h, false, false, ntok, nq, C, a->h, T, C, a->w_q, T, nq, 0.f, a->q, T, nq) ||
+          !rm_gemm(h, false, false, ntok, nk, C, a->h, T, C, a->w_k, T, nk, 0.f, a->k, T, nk) ||
+          !rm_gemm(h, false, false, ntok, nv, C, a->h, T, C, a->w_v, T, nv, 0.f, a->v, T, nv))
+        return NSA_ERR_BLAS;
+    }
+    if ((st = prefill_impl(p, &pa, ws, ws_bytes, stream, nullptr, 0)) != NSA_OK) return st;
+    std::lock_guard<std::mutex> lk(g_blas_mu);
+    rocblas_handle h;
+    if ((st = blas_handle(&h)) != NSA_OK) return st;
+    if (rocblas_set_stream(h, (hipStream_t)stream) != rocblas_status_success) return NSA_ERR_BLAS;
+    if (!rm_gemm(h, false, false, ntok, C, no, a->o, T, no, a->w_o, T, C, 0.f, a->y, T, C)) return NSA_ERR_BLAS;
+    return NSA_OK;
+  } catch (...) {
+    return NSA_ERR_INTERNAL;
+  }
+}
+
+nsa_status nsa_layer_bwd(const nsa_params* p, const nsa_layer_bwd_args* a, void* ws, size_t ws_bytes,
+                         void* stream) {
+  try {
+    Dims dm;
+    nsa_status st = make_dims(p, &dm);
+    if (st != NSA_OK) return st;
+    if (!a) return NSA_ERR_INVALID_ARG;
+    const void* req[] = {a->h, a->w_q, a->w_k, a->w_v, a->w_o, a->q, a->k, a->v, a->o, a->dy,
+                         a->dh, a->dw_q, a->dw_k, a->dw_v, a->dw_o};
+    if (!layer_weights_ok(req, 15)) return NSA_ERR_INVALID_ARG;
+    const size_t need = plan_layer_bwd(dm, nullptr, nullptr);
+    if (ws_bytes < need || !ws || !aligned16(ws)) return NSA_ERR_WORKSPACE;
+    LayerBwdWs w;
+    plan_layer_bwd(dm, ws, &w);
+    nsa_bwd_args ba{};
+    ba.q = a->q; ba.k = a->k; ba.v = a->v; ba.x = a->h; ba.w_gate = a->w_gate;
+    ba.phi_k = a->phi_k; ba.phi_v = a->phi_v;
+    ba.k_cmp = a->k_cmp; ba.v_cmp = a->v_cmp; ba.lse = a->lse; ba.idx = a->idx; ba.o_branch = a->o_branch;
+    ba.d_o = w.d_o; ba.dq = w.dq; ba.dk = w.dk; ba.dv = w.dv; ba.dw_gate = a->dw_gate;
+    ba.d_phi_k = a->d_phi_k; ba.d_phi_v = a->d_phi_v;
+    ba.gate_mlp = a->gate_mlp; ba.d_gate_mlp = a->d_gate_mlp; ba.dx = a->dh;
+    const size_t op_bytes = bwd_ws_bytes(dm);
+    if ((st = bwd_impl(p, &ba, w.op_ws, op_bytes, stream, nullptr, 0, true)) != NSA_OK) return st;
+    const bool bf = dm.io == IO_BF16;
+    const rocblas_datatype T = bf ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
+    const rocblas_datatype F = rocblas_datatype_f32_r;
+    const int ntok = dm.B * dm.T, C = dm.C;
+    const int nq = dm.Hq * dm.dk, nk = dm.Hkv * dm.dk, nv = dm.Hkv * dm.dv, no = dm.Hq * dm.dv;
+    hipStream_t s = (hipStream_t)stream;
+    {
+      // dO = dy w_o^T (io dtype), dW_o = o^T dy
+      std::lock_guard<std::mutex> lk(g_blas_mu);
+      rocblas_handle h;
+      if ((st = blas_handle(&h)) != NSA_OK) return st;
+      if (rocblas_set_stream(h, s) != rocblas_status_success) return NSA_ERR_BLAS;
+      if (!rm_gemm(h, false, true, ntok, no, C, a->dy, T, C, a->w_o, T, C, 0.f, w.d_o, T, no) ||
+          !rm_gemm(h, true, false, no, C, ntok, a->o, T, no, a->dy, T, C, 0.f, a->dw_o, F, C))
+        return NSA_ERR_BLAS;
+    }
+    // the operator's backward; its dx (the gate path) initialises dh
+    if ((st = bwd_impl(p, &ba, w.op_ws, op_bytes, stream, nullptr, 0)) != NSA_OK) return st;
+    const float* h32 = (const float*)a->h;
+    if (bf && launch_to_f32(a->h, (size_t)ntok * C, w.h32, s) != hipSuccess) return NSA_ERR_HIP;
+    if (bf) h32 = w.h32;
+    struct Proj { const void* w; const float* d; int n; void* dw; };
+    const Proj pr[3] = {{a->w_q, w.dq, nq, a->dw_q}, {a->w_k, w.dk, nk, a->dw_k}, {a->w_v, w.dv, nv, a->dw_v}};
+    std::lock_guard<std::mutex> lk(g_blas_mu);
+    rocblas_handle h;
+    if ((st = blas_handle(&h)) != NSA_OK) return st;
+    if (rocblas_set_stream(h, s) != rocblas_status_success) return NSA_ERR_BLAS;
+    for (const Proj& j : pr) {
+      // dW = h^T d; dh += d W^T (fp32 operands; the weight is widened first)
+      if (!rm_gemm(h, true, false, C, j.n, ntok, h32, F, C, j.d, F, j.n, 0.f, j.dw, F, j.n)) return NSA_ERR_BLAS;
+      const float* w32 = (const float*)j.w;
+      if (bf) {
+        if (launch_to_f32(j.w, (size_t)C * j.n, w.w32, s) != hipSuccess) return NSA_ERR_HIP;
+        w32 = w.w32;
+      }
+      if (!rm_gemm(h, false, true, ntok, C, j.n, j.d, F, j.n, w32, F, j.n, 1.f, a->dh, F, C)) return NSA_ERR_BLAS;
+    }
+    return NSA_OK;
+  } catch (...) {
+    return NSA_ERR_INTERNAL;
+  }
 }
 
 }  // extern "C"

@@ -122,6 +122,8 @@ hipError_t launch_win_combine(const Dims& dm, const WinArgs& a, hipStream_t s);
 struct GateMlp {
   const void *w1, *b1, *b2;
 };
+// dst[i] = float(src[i]) for a bf16 array of n elements.
+hipError_t launch_to_f32(const void* src, size_t n, float* dst, hipStream_t s);
 hipError_t launch_gate_mlp(const Dims& dm, int ntok, const void* x, const void* w_gate, const GateMlp& g,
                            float* hid, float* pre, float* gates, hipStream_t s);
 

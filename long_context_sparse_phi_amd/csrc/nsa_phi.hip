@@ -84,6 +84,23 @@ hipError_t launch_gate_mlp(const Dims& dm, int ntok, const void* x, const void* 
   return gate_layer<float, float, 2>(ntok, dm.Cg, HO, hid, w_gate, g.b2, gates, nullptr, s);
 }
 
+__global__ __launch_bounds__(256) void k_to_f32(size_t n, const bf16* __restrict__ src, float* __restrict__ dst) {
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i + 8 <= n) {
+    const Frag8<bf16> f = load_frag(src + i);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dst[i + e] = to_f32(frag_at(f, e));
+  } else {
+    for (size_t j = i; j < n; ++j) dst[j] = to_f32(src[j]);
+  }
+}
+
+hipError_t launch_to_f32(const void* src, size_t n, float* dst, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  k_to_f32<<<(unsigned)((n + 2047) / 2048), 256, 0, s>>>(n, (const bf16*)src, dst);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Transposes.
 // ---------------------------------------------------------------------------

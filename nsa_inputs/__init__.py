@@ -20,7 +20,7 @@ from typing import Dict, Optional
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "workload", "make_prefill_inputs",
-           "make_decode_inputs", "make_grad_output", "tensor_seed"]
+           "make_decode_inputs", "make_grad_output", "make_layer_inputs", "tensor_seed"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -194,6 +194,27 @@ def make_decode_inputs(w: Workload, seed: int = 0) -> Dict[str, object]:
         "x": _normal(seed, "dec.x", (B, w.gate_dim)),
         "phi_k": _phi(seed, "phi_k", w, w.d_k),
         "phi_v": _phi(seed, "phi_v", w, w.d_v),
+    }
+    d.update(_gate(seed, w))
+    return _cast(d, w.torch_dtype)
+
+
+def make_layer_inputs(w: Workload, seed: int = 0) -> Dict[str, object]:
+    """Inputs of the projection layer around the operator (layer width
+    C = gate_dim): h [B,T,C] ~ N(0,1); proj = {w_q [C,Hq*dk], w_k [C,Hkv*dk],
+    w_v [C,Hkv*dv]} ~ N(0, 1/C), so that q, k, v have unit variance like the
+    operator's own inputs, and w_o [Hq*dv,C] ~ N(0, 1/(Hq*dv)); gate and phi
+    weights as for the operator; dy [B,T,C] ~ N(0,1)."""
+    B, T, C = w.B, w.T, w.gate_dim
+    d = {
+        "h": _normal(seed, "layer.h", (B, T, C)),
+        "proj": {"w_q": _normal(seed, "layer.w_q", (C, w.H_q * w.d_k), C ** -0.5),
+                 "w_k": _normal(seed, "layer.w_k", (C, w.H_kv * w.d_k), C ** -0.5),
+                 "w_v": _normal(seed, "layer.w_v", (C, w.H_kv * w.d_v), C ** -0.5),
+                 "w_o": _normal(seed, "layer.w_o", (w.H_q * w.d_v, C), (w.H_q * w.d_v) ** -0.5)},
+        "phi_k": _phi(seed, "phi_k", w, w.d_k),
+        "phi_v": _phi(seed, "phi_v", w, w.d_v),
+        "dy": _normal(seed, "layer.dy", (B, T, C)),
     }
     d.update(_gate(seed, w))
     return _cast(d, w.torch_dtype)

@@ -42,7 +42,7 @@ from scipy.special import erf
 __all__ = [
     "Params", "gate", "gate_logits", "compress", "remap_matrix", "attend", "n_cmp_visible",
     "candidate_blocks", "forced_blocks", "top_n", "is_near_tie", "forward",
-    "decode", "append_token", "backward", "dq_rows", "dense_causal", "dense_causal_bwd", "round_io", "gelu", "gelu_grad", "sigmoid",
+    "decode", "append_token", "backward", "layer_forward", "layer_backward", "dq_rows", "dense_causal", "dense_causal_bwd", "round_io", "gelu", "gelu_grad", "sigmoid",
     "cmp_keys", "slc_keys", "win_keys", "decode_token_count",
 ]
 
@@ -523,6 +523,61 @@ def _phi_bwd(kv, phi, dout, p: Params):
         dkv[:, i * p.d: i * p.d + p.l] += du
         grads["pe"] += du.sum(axis=(0, 2))
     return dkv, grads
+
+
+# ---------------------------------------------------------------------------
+# Projection layer around the operator [XK 三种注意力如何组合 §2: the module
+# projects its input to queries, keys and values, runs the three branches,
+# gates them from the same input and projects the result; YLY 整体框架].
+# Reading: q = h W_q, k = h W_k, v = h W_v and the attention output o are
+# stored tensors, rounded to the I/O dtype (R16); the gate input is h;
+# y = o W_o, rounded likewise.  Backward: dO = dy W_o^T rounded to the I/O
+# dtype (the operator takes dO as a stored tensor), dW_o = o^T dy, then the
+# operator's backward, dW_p = h^T d_p and dh = dx + sum_p d_p W_p^T for
+# p in (q, k, v).
+# ---------------------------------------------------------------------------
+
+def layer_forward(p: Params, h, proj: Dict[str, np.ndarray], w_gate, n_heads, phi_k=None, phi_v=None,
+                  gate_mlp=None, tie_scores=None) -> Dict[str, np.ndarray]:
+    """h [B,T,C]; proj = {w_q [C,Hq*dk], w_k [C,Hkv*dk], w_v [C,Hkv*dv],
+    w_o [Hq*dv,C]}; n_heads = (Hq, Hkv).  Returns y [B,T,C], q, k, v, o (as
+    stored) and the operator's forward result under "nsa"."""
+    B, T, C = h.shape
+    Hq, Hkv = n_heads
+    dk = proj["w_q"].shape[1] // Hq
+    dv = proj["w_o"].shape[0] // Hq
+    q = round_io(h @ proj["w_q"], p.io).reshape(B, T, Hq, dk)
+    k = round_io(h @ proj["w_k"], p.io).reshape(B, T, Hkv, dk)
+    v = round_io(h @ proj["w_v"], p.io).reshape(B, T, Hkv, dv)
+    f = forward(p, q, k, v, h, w_gate, phi_k, phi_v, tie_scores=tie_scores, gate_mlp=gate_mlp)
+    o = round_io(f["o"], p.io)
+    y = round_io(o.reshape(B, T, Hq * dv) @ proj["w_o"], p.io)
+    return {"y": y, "q": q, "k": k, "v": v, "o": o, "nsa": f}
+
+
+def layer_backward(p: Params, h, proj: Dict[str, np.ndarray], w_gate, n_heads, phi_k, phi_v, dy, idx,
+                   gate_mlp=None) -> Dict[str, object]:
+    """Gradients of L = sum(dy * y) with the block indices idx fixed: dh,
+    dw_q, dw_k, dw_v, dw_o, and the operator's own (dw_gate, dgate_mlp,
+    dphi_k, dphi_v)."""
+    B, T, C = h.shape
+    f = layer_forward(p, h, proj, w_gate, n_heads, phi_k, phi_v, gate_mlp)
+    Hq = n_heads[0]
+    dv = proj["w_o"].shape[0] // Hq
+    o2 = f["o"].reshape(B * T, -1)
+    dy2 = dy.reshape(B * T, C)
+    d_o = round_io(dy2 @ proj["w_o"].T, p.io).reshape(B, T, Hq, dv)
+    g = backward(p, f["q"], f["k"], f["v"], h, w_gate, phi_k, phi_v, d_o, idx, gate_mlp=gate_mlp)
+    h2 = h.reshape(B * T, C)
+    out = {"dw_o": o2.T @ dy2, "dw_gate": g["dw_gate"], "dgate_mlp": g["dgate_mlp"],
+           "dphi_k": g["dphi_k"], "dphi_v": g["dphi_v"]}
+    dh = g["dx"].reshape(B * T, C).copy()
+    for name, d in (("q", g["dq"]), ("k", g["dk"]), ("v", g["dv"])):
+        d2 = d.reshape(B * T, -1)
+        out["dw_" + name] = h2.T @ d2
+        dh += d2 @ proj["w_" + name].T
+    out["dh"] = dh.reshape(B, T, C)
+    return out
 
 
 def dense_causal(q, k, v, scale=None):

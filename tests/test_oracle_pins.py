@@ -713,6 +713,89 @@ def test_gate_mlp_backward_matches_finite_differences_with_real_selection():
     check(inp["q"], gr["dq"])
 
 
+def layer_problem(T, C, Hkv, G, dk, dv, seed, phi="mean", **kw):
+    rng = np.random.default_rng(seed)
+    Hq = Hkv * G
+    h = rng.standard_normal((1, T, C))
+    proj = {"w_q": rng.standard_normal((C, Hq * dk)) / math.sqrt(C),
+            "w_k": rng.standard_normal((C, Hkv * dk)) / math.sqrt(C),
+            "w_v": rng.standard_normal((C, Hkv * dv)) / math.sqrt(C),
+            "w_o": rng.standard_normal((Hq * dv, C)) / math.sqrt(Hq * dv)}
+    w_gate = 0.3 * rng.standard_normal((C, Hq, 3))
+    return h, proj, w_gate, rng
+
+
+def test_layer_matches_torch_autograd_in_the_dense_case():
+    """Projections + operator + output projection against torch fp64 autograd
+    where all three branches are dense causal attention (l = d = 1, mean phi,
+    n covering all blocks, w >= T)."""
+    T, C, Hkv, G, dk, dv = 30, 6, 2, 2, 4, 3
+    h, proj, w_gate, rng = layer_problem(T, C, Hkv, G, dk, dv, seed=41)
+    p = O.Params(l=1, d=1, l_sel=8, n=4, w=T, phi="mean", io=None)
+    dy = rng.standard_normal((1, T, C))
+    f = O.layer_forward(p, h, proj, w_gate, (Hkv * G, Hkv))
+    g = O.layer_backward(p, h, proj, w_gate, (Hkv * G, Hkv), None, None, dy, f["nsa"]["idx"])
+    th = torch.tensor(h, requires_grad=True)
+    tw = {k: torch.tensor(v, requires_grad=True) for k, v in proj.items()}
+    tg = torch.tensor(w_gate, requires_grad=True)
+    q = (th @ tw["w_q"]).reshape(1, T, Hkv * G, dk).permute(0, 2, 1, 3)
+    k = (th @ tw["w_k"]).reshape(1, T, Hkv, dk).permute(0, 2, 1, 3).repeat_interleave(G, 1)
+    v = (th @ tw["w_v"]).reshape(1, T, Hkv, dv).permute(0, 2, 1, 3).repeat_interleave(G, 1)
+    dense = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True).permute(0, 2, 1, 3)
+    gates = torch.sigmoid(torch.einsum("btc,chk->bthk", th, tg))
+    o = gates.sum(-1, keepdim=True) * dense
+    y = o.reshape(1, T, -1) @ tw["w_o"]
+    np.testing.assert_allclose(f["y"], y.detach().numpy(), rtol=1e-11, atol=1e-12)
+    (y * torch.from_numpy(dy)).sum().backward()
+    tol = dict(rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(g["dh"], th.grad.numpy(), **tol)
+    np.testing.assert_allclose(g["dw_gate"], tg.grad.numpy(), **tol)
+    for key in proj:
+        np.testing.assert_allclose(g["d" + key], tw[key].grad.numpy(), **tol)
+
+
+def test_layer_backward_matches_finite_differences_with_real_selection():
+    T, C, Hkv, G, dk, dv = 26, 4, 2, 2, 3, 2
+    h, proj, w_gate, rng = layer_problem(T, C, Hkv, G, dk, dv, seed=43)
+    p = O.Params(l=4, d=2, l_sel=8, n=3, w=5, phi="mlp", io=None)
+    hid = 4
+    phi = {D: {"pe": 0.2 * rng.standard_normal((4, D)), "w1": 0.2 * rng.standard_normal((4 * D, hid)),
+               "b1": 0.2 * rng.standard_normal(hid), "w2": 0.2 * rng.standard_normal((hid, D)),
+               "b2": 0.2 * rng.standard_normal(D)} for D in (dk, dv)}
+    mlp, w_gate = gate_mlp_weights(C, 5, Hkv * G, seed=44)
+    heads = (Hkv * G, Hkv)
+    dy = rng.standard_normal((1, T, C))
+    idx = O.layer_forward(p, h, proj, w_gate, heads, phi[dk], phi[dv], mlp)["nsa"]["idx"]
+    g = O.layer_backward(p, h, proj, w_gate, heads, phi[dk], phi[dv], dy, idx, gate_mlp=mlp)
+    eps = 1e-6
+
+    def loss():
+        B = 1
+        q = (h @ proj["w_q"]).reshape(B, T, heads[0], dk)
+        k = (h @ proj["w_k"]).reshape(B, T, Hkv, dk)
+        v = (h @ proj["w_v"]).reshape(B, T, Hkv, dv)
+        o = O.forward(p, q, k, v, h, w_gate, phi[dk], phi[dv], idx=idx, gate_mlp=mlp)["o"]
+        return float(((o.reshape(B, T, -1) @ proj["w_o"]) * dy).sum())
+
+    def check(arr, grad, n_pick=8):
+        flat = arr.reshape(-1)
+        for i in rng.choice(flat.size, size=min(n_pick, flat.size), replace=False):
+            old = flat[i]
+            flat[i] = old + eps
+            lp = loss()
+            flat[i] = old - eps
+            lm = loss()
+            flat[i] = old
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - grad.reshape(-1)[i]) < 1e-6 + 1e-6 * abs(fd), (i, fd, grad.reshape(-1)[i])
+
+    check(h, g["dh"])
+    for key in proj:
+        check(proj[key], g["d" + key])
+    check(mlp["w1"], g["dgate_mlp"]["w1"])
+    check(phi[dk]["w1"], g["dphi_k"]["w1"])
+
+
 def test_dense_causal_matches_torch_sdpa():
     """The dense baseline against torch's fp64 scaled-dot-product attention
     (causal, GQA by repeating the KV heads)."""
