@@ -34,29 +34,32 @@
 namespace nsa {
 
 // ---------------------------------------------------------------------------
-// One kernel for both passes.  A workgroup of 4 waves owns PWG consecutive
+// One kernel for both passes.  A workgroup of NW waves owns PWG consecutive
 // positions of one (batch, KV head); all waves need the same compressed keys,
-// so 64-key tiles of K_cmp (and, in pass B, of V_cmp^T) are staged once in LDS
+// so KT-key tiles of K_cmp (and, in pass B, of V_cmp^T) are staged once in LDS
 // per workgroup, double-buffered: the next tile's global loads are in flight
 // (in registers) while the current tile is computed from LDS.
 // ---------------------------------------------------------------------------
-constexpr int kCmpKT = 64;               // keys per LDS tile
 constexpr float kPScale2 = 14.f;         // pass B evaluates P * 2^kPScale2
 constexpr float kPScaleInv = 1.f / 16384.f;
-constexpr int kCmpVS = kCmpKT + 8;       // LDS row stride of the V^T tile (elements)
+// LDS row stride of the V^T tile (elements)
+template <int KT>
+constexpr int cmp_vs() { return KT + 8; }
 
 // K tile rows are unpadded with XOR-swizzled 16-byte chunks (kchunk_off).
-template <typename T, int DK, int DV, bool PB>
+template <typename T, int DK, int DV, bool PB, int KT>
 constexpr size_t cmp_tile_elems() {
-  return (size_t)kCmpKT * DK + (PB ? (size_t)DV * kCmpVS : 0);
+  return (size_t)KT * DK + (PB ? (size_t)DV * cmp_vs<KT>() : 0);
 }
 
 // GS, NJ: group size and number of 16-block remap column tiles fixed at
 // compile time (0: read from the arguments).
-template <typename T, int DK, int DV, int NCT, int NW, bool PB, typename OT, int GS, int NJ>
+template <typename T, int DK, int DV, int NCT, int NW, bool PB, typename OT, int GS, int NJ, int KT>
 __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nselp, int njt_arg) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  constexpr size_t TE = cmp_tile_elems<T, DK, DV, PB>();
+  constexpr size_t TE = cmp_tile_elems<T, DK, DV, PB, KT>();
+  constexpr int VS = cmp_vs<KT>();
+  constexpr int NH = KT / 32;                               // 32-key halves per tile
   constexpr int NT = NW * 64;
   T* tiles = (T*)smem_raw;                                  // [2][TE]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -121,10 +124,10 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
   }
 
   // cooperative tile loader
-  constexpr int KCH = kCmpKT * DK / 8 / NT;        // 16-byte chunks per thread (K)
-  constexpr int VCH = PB ? DV * kCmpKT / 8 / NT : 0;
-  static_assert(KCH * NT == kCmpKT * DK / 8, "K tile must split evenly over the workgroup");
-  static_assert(!PB || VCH * NT == DV * kCmpKT / 8, "V tile must split evenly over the workgroup");
+  constexpr int KCH = KT * DK / 8 / NT;            // 16-byte chunks per thread (K)
+  constexpr int VCH = PB ? DV * KT / 8 / NT : 0;
+  static_assert(KCH * NT == KT * DK / 8, "K tile must split evenly over the workgroup");
+  static_assert(!PB || VCH * NT == DV * KT / 8, "V tile must split evenly over the workgroup");
   Frag8<T> kr[KCH], vr[VCH > 0 ? VCH : 1];
   const T* kcb = (const T*)a.kc + ((size_t)b * dm.ncmp * dm.Hkv + g) * DK;
   const T* vtb = (const T*)a.vct + (size_t)(b * dm.Hkv + g) * DV * dm.ncmp_pad;
@@ -137,13 +140,13 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
     }
 #pragma unroll
     for (int c = 0; c < VCH; ++c) {
-      const int idx = threadIdx.x + NT * c, row = idx / (kCmpKT / 8), c8 = idx % (kCmpKT / 8);
+      const int idx = threadIdx.x + NT * c, row = idx / (KT / 8), c8 = idx % (KT / 8);
       vr[c] = load_frag(vtb + (size_t)row * dm.ncmp_pad + kt + c8 * 8);
     }
   };
   auto lstore = [&](int buf) {
     T* kt_ = tiles + (size_t)buf * TE;
-    T* vt_ = kt_ + (size_t)kCmpKT * DK;
+    T* vt_ = kt_ + (size_t)KT * DK;
 #pragma unroll
     for (int c = 0; c < KCH; ++c) {
       const int idx = threadIdx.x + NT * c, row = idx / (DK / 8), c8 = idx % (DK / 8);
@@ -151,8 +154,8 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
     }
 #pragma unroll
     for (int c = 0; c < VCH; ++c) {
-      const int idx = threadIdx.x + NT * c, row = idx / (kCmpKT / 8), c8 = idx % (kCmpKT / 8);
-      *reinterpret_cast<Frag8<T>*>(vt_ + row * kCmpVS + c8 * 8) = vr[c];
+      const int idx = threadIdx.x + NT * c, row = idx / (KT / 8), c8 = idx % (KT / 8);
+      *reinterpret_cast<Frag8<T>*>(vt_ + row * VS + c8 * 8) = vr[c];
     }
   };
 
@@ -245,7 +248,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
     // when O is kept in fp32 for the backward)
 #pragma unroll
     for (int dt = 0; dt < DV / 16; ++dt) {
-      const Frag8<T> vf = *reinterpret_cast<const Frag8<T>*>(vtile + (dt * 16 + c16) * kCmpVS + h * 32 + qd * 8);
+      const Frag8<T> vf = *reinterpret_cast<const Frag8<T>*>(vtile + (dt * 16 + c16) * VS + h * 32 + qd * 8);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         mma(oacc[dt][ct], vf, pf[ct]);
@@ -289,28 +292,28 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
     }
   };
 
-  const int nkt = (nmax_wg + kCmpKT - 1) / kCmpKT;
+  const int nkt = (nmax_wg + KT - 1) / KT;
   if (nkt > 0) {
     gload(0);
     lstore(0);
   }
   __syncthreads();
   for (int it = 0; it < nkt; ++it) {
-    const int kt0 = it * kCmpKT;
-    if (it + 1 < nkt) gload(kt0 + kCmpKT);
+    const int kt0 = it * KT;
+    if (it + 1 < nkt) gload(kt0 + KT);
     const T* ktile = tiles + (size_t)(it & 1) * TE;
-    const T* vtile = ktile + (size_t)kCmpKT * DK;
+    const T* vtile = ktile + (size_t)KT * DK;
     // With few column tiles both halves' scores are issued before either
     // half's softmax work, so the second half's MFMAs run under the first
     // half's VALU work (four column tiles have no registers for that).
-    constexpr bool kEarly = NCT <= 2;
-    f32x4 s[2][2][NCT];
-    if (kEarly) {
+    constexpr bool kEarly = NCT <= 2 && NH == 2;
+    f32x4 s[NH][2][NCT];
+    if constexpr (kEarly) {
       if (kt0 < nmax) scores(ktile, 0, s[0]);
-      if (kt0 + 32 < nmax) scores(ktile, 1, s[1]);
+      if (kt0 + 32 < nmax) scores(ktile, 1, s[NH - 1]);
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < NH; ++h) {
       const int kt = kt0 + h * 32;
       if (kt >= nmax) break;
       if (!kEarly) scores(ktile, h, s[h]);
@@ -347,36 +350,49 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
         store4(op + dt * 16, oacc[dt][ct][0] * kPScaleInv, oacc[dt][ct][1] * kPScaleInv,
                oacc[dt][ct][2] * kPScaleInv, oacc[dt][ct][3] * kPScaleInv);
     }
-    // top-n per position of this wave
-    for (int pl = 0; pl < PW; ++pl) {
-      const int t = t0 + pl;
-      if (t >= dm.T) break;
-      float* row = prow + pl * nselp;
-      const size_t rbase = (size_t)(b * dm.T + t) * dm.Hkv + g;
-      if (a.p_slc) {
-        float* ps = a.p_slc + rbase * dm.nsel;
-        for (int j = lane; j < dm.nsel; j += 64) ps[j] = row[j] * kPScaleInv;
+    // top-n per position of this wave, two positions at a time
+    for (int pl = 0; pl < PW; pl += 2) {
+      const float* rows[2];
+      int ts[2];
+      int* outs[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int t = t0 + pl + r;
+        const bool live = pl + r < PW && t < dm.T;
+        ts[r] = live ? t : -1;
+        rows[r] = prow + (pl + r) * nselp;
+        const size_t rbase = (size_t)(b * dm.T + (live ? t : 0)) * dm.Hkv + g;
+        outs[r] = a.idx + rbase * dm.n;
+        if (live && a.p_slc) {
+          float* ps = a.p_slc + rbase * dm.nsel;
+          for (int j = lane; j < dm.nsel; j += 64) ps[j] = rows[r][j] * kPScaleInv;
+        }
       }
-      wave_topn(row, t, dm.ls, dm.n, a.idx + rbase * dm.n, lane);
+      if (dm.nsel <= 1024) {
+        wave_topn_rows<16, 2>(rows, ts, dm.ls, dm.n, outs, lane);
+      } else {
+        for (int r = 0; r < 2; ++r)
+          if (ts[r] >= 0) wave_topn(prow + (pl + r) * nselp, ts[r], dm.ls, dm.n, outs[r], lane);
+      }
     }
   }
 }
 
 int cmp_out_nselp(const Dims& dm) { return (dm.nsel + 15) & ~15; }
 
-template <typename T, int DK, int DV, bool PB>
+template <typename T, int DK, int DV, bool PB, int KT>
 static size_t cmp_lds(const Dims& dm, int nw, int nct, int nselp) {
-  size_t b = 2 * cmp_tile_elems<T, DK, DV, PB>() * sizeof(T);
+  size_t b = 2 * cmp_tile_elems<T, DK, DV, PB, KT>() * sizeof(T);
   if (PB) b += (size_t)nw * (16 * nct / dm.G) * nselp * sizeof(float);
   return b;
 }
 
-template <typename T, int DK, int DV, int NCT, int NW, bool PB, typename OT>
+template <typename T, int DK, int DV, int NCT, int NW, bool PB, typename OT, int KT = 64>
 static hipError_t cmp_launch(const Dims& dm, const CmpArgs& a, int nselp, int njt, size_t lds, hipStream_t s) {
   // the common configuration (16 heads per group, one remap column tile) is
   // compiled with both fixed
-  auto kfn = (dm.G == 16 && njt == 1 && NCT > 1) ? k_cmp<T, DK, DV, NCT, NW, PB, OT, 16, 1>
-                                                 : k_cmp<T, DK, DV, NCT, NW, PB, OT, 0, 0>;
+  auto kfn = (dm.G == 16 && njt == 1 && NCT > 1) ? k_cmp<T, DK, DV, NCT, NW, PB, OT, 16, 1, KT>
+                                                 : k_cmp<T, DK, DV, NCT, NW, PB, OT, 0, 0, KT>;
   if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   const int PWG = NW * 16 * NCT / dm.G;
   const int ntiles = (dm.T + PWG - 1) / PWG;
@@ -384,9 +400,11 @@ static hipError_t cmp_launch(const Dims& dm, const CmpArgs& a, int nselp, int nj
   return hipGetLastError();
 }
 
-// Pass A: 4 waves x 4 column tiles.  Pass B: 8 waves x 2 column tiles, so two
-// waves share each SIMD; with the score rows it falls back to 4 waves x 1
-// column tile when LDS is short.
+// Pass A: 4 waves x 4 column tiles, 64-key tiles.  Pass B: 4 waves x 2
+// column tiles with 32-key tiles, so that two independent workgroups share a
+// compute unit (two waves per SIMD that are not tied by one barrier); else 8
+// waves x 2 column tiles with 64-key tiles, and with long score rows 4 waves x
+// 1 column tile.
 template <typename T, int DK, int DV, bool PB>
 static hipError_t cmp_impl(const Dims& dm, const CmpArgs& a, hipStream_t s) {
   const int nselp = cmp_out_nselp(dm);
@@ -394,16 +412,21 @@ static hipError_t cmp_impl(const Dims& dm, const CmpArgs& a, hipStream_t s) {
   const int njt = (nblk + 15) / 16;
   const size_t lim = 160 * 1024;
   if constexpr (!PB) {
-    const size_t lds = cmp_lds<T, DK, DV, PB>(dm, 4, 4, nselp);
+    const size_t lds = cmp_lds<T, DK, DV, PB, 64>(dm, 4, 4, nselp);
     return a.o_f32 ? cmp_launch<T, DK, DV, 4, 4, PB, float>(dm, a, nselp, njt, lds, s)
                    : cmp_launch<T, DK, DV, 4, 4, PB, T>(dm, a, nselp, njt, lds, s);
   } else {
-  if (cmp_lds<T, DK, DV, PB>(dm, 8, 2, nselp) <= lim) {
-    const size_t lds = cmp_lds<T, DK, DV, PB>(dm, 8, 2, nselp);
+  if (2 * cmp_lds<T, DK, DV, PB, 32>(dm, 4, 2, nselp) <= lim) {
+    const size_t lds = cmp_lds<T, DK, DV, PB, 32>(dm, 4, 2, nselp);
+    return a.o_f32 ? cmp_launch<T, DK, DV, 2, 4, PB, float, 32>(dm, a, nselp, njt, lds, s)
+                   : cmp_launch<T, DK, DV, 2, 4, PB, T, 32>(dm, a, nselp, njt, lds, s);
+  }
+  if (cmp_lds<T, DK, DV, PB, 64>(dm, 8, 2, nselp) <= lim) {
+    const size_t lds = cmp_lds<T, DK, DV, PB, 64>(dm, 8, 2, nselp);
     return a.o_f32 ? cmp_launch<T, DK, DV, 2, 8, PB, float>(dm, a, nselp, njt, lds, s)
                    : cmp_launch<T, DK, DV, 2, 8, PB, T>(dm, a, nselp, njt, lds, s);
   }
-  const size_t lds = cmp_lds<T, DK, DV, PB>(dm, 4, 1, nselp);
+  const size_t lds = cmp_lds<T, DK, DV, PB, 64>(dm, 4, 1, nselp);
   if (lds > lim) return hipErrorInvalidValue;
   return a.o_f32 ? cmp_launch<T, DK, DV, 1, 4, PB, float>(dm, a, nselp, njt, lds, s)
                  : cmp_launch<T, DK, DV, 1, 4, PB, T>(dm, a, nselp, njt, lds, s);
@@ -424,7 +447,7 @@ hipError_t launch_cmp_out_topn(const Dims& dm, const CmpArgs& a, hipStream_t s) 
 
 bool cmp_out_fits(const Dims& dm) {
   // pass B with one column tile per wave: tiles (largest case: fp32, 192/128) + score rows
-  const size_t tiles = 2 * ((size_t)kCmpKT * dm.dk + (size_t)dm.dv * kCmpVS) * (dm.io == IO_BF16 ? 2 : 4);
+  const size_t tiles = 2 * ((size_t)64 * dm.dk + (size_t)dm.dv * cmp_vs<64>()) * (dm.io == IO_BF16 ? 2 : 4);
   return tiles + (size_t)4 * (16 / dm.G) * cmp_out_nselp(dm) * sizeof(float) <= 160 * 1024;
 }
 

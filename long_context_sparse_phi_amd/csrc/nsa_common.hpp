@@ -364,6 +364,85 @@ __device__ inline void wave_topn(float* row, int t, int ls, int n, int* out, int
   for (int e = cnt + lane; e < n; e += 64) out[e] = -1;
 }
 
+// The same selection for R rows at once, each held in registers (rows of at
+// most 64*KV blocks): lane L owns blocks L + 64 i (i < KV), read from LDS
+// once, as 64-bit keys (score bits << 32 | ~j) so that one integer maximum
+// orders by score and then by lower index (scores are >= 0, so their bits
+// order like their values).  Each lane keeps its three best unselected keys,
+// sorted; a pick is one wave maximum per row (the R chains are independent),
+// after which the winning lane shifts its three keys and re-ranks its blocks
+// only when all three were taken.  t[r] < 0 marks an absent row.
+template <int KV, int R>
+__device__ inline void wave_topn_rows(const float* const* row, const int* t, int ls, int n, int* const* out,
+                                      int lane) {
+  int jc[R];
+  bool live[R];
+  uint64_t key[R][KV];   // 0: not a candidate
+  uint32_t taken[R];     // bit i: block lane + 64 i selected
+  uint64_t k1[R], k2[R], k3[R];
+  auto rank3 = [&](int r) {
+    uint64_t a = 0, b = 0, c = 0;
+#pragma unroll
+    for (int i = 0; i < KV; ++i) {
+      const uint64_t x = (taken[r] >> i) & 1u ? 0ull : key[r][i];
+      const bool g1 = x > a, g2 = x > b, g3 = x > c;
+      c = g2 ? b : (g3 ? x : c);
+      b = g1 ? a : (g2 ? x : b);
+      a = g1 ? x : a;
+    }
+    k1[r] = a;
+    k2[r] = b;
+    k3[r] = c;
+  };
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    jc[r] = t[r] >= 0 ? t[r] / ls : -1;
+    live[r] = t[r] >= 0 && jc[r] + 1 > n;
+    taken[r] = 0;
+    if (t[r] >= 0 && !live[r])
+      for (int e = lane; e < n; e += 64) out[r][e] = e <= jc[r] ? e : -1;
+#pragma unroll
+    for (int i = 0; i < KV; ++i) {
+      const int j = lane + 64 * i;
+      const bool cand = live[r] && j <= jc[r] && j != 0 && j != jc[r] - 1 && j != jc[r];
+      key[r][i] = cand ? ((uint64_t)(__float_as_uint(row[r][j]) & 0x7fffffffu) << 32) | (0xffffffffu - (uint32_t)j)
+                       : 0ull;
+    }
+    rank3(r);
+  }
+  for (int it = 0; it < n - 3; ++it) {
+    uint64_t b[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) b[r] = wave_max_u64(k1[r]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (b[r] != 0ull && k1[r] == b[r]) {
+        const int j = (int)(0xffffffffu - (uint32_t)b[r]);
+        taken[r] |= 1u << (j >> 6);
+        k1[r] = k2[r];
+        k2[r] = k3[r];
+        k3[r] = 0ull;
+        if (k1[r] == 0ull) rank3(r);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (!live[r]) continue;
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < KV; ++i) {
+      if (64 * i > jc[r]) break;
+      const int j = lane + 64 * i;
+      const bool sel = j <= jc[r] && (((taken[r] >> i) & 1u) || j == 0 || j == jc[r] - 1 || j == jc[r]);
+      const uint64_t mk = __ballot(sel);
+      if (sel) out[r][cnt + __popcll(mk & ((1ull << lane) - 1ull))] = j;
+      cnt += __popcll(mk);
+    }
+    for (int e = cnt + lane; e < n; e += 64) out[r][e] = -1;
+  }
+}
+
 // The same selection by a whole workgroup of NW waves (NW*64 threads), by
 // radix select instead of repeated argmax.  Scores are >= 0, so their bit
 // patterns order like the values.  Four passes over 8-bit digits, most
