@@ -199,29 +199,48 @@ __global__ __launch_bounds__(256, slc_depth<T>() > 2 ? 1 : 2) void k_slc(Dims dm
 #pragma unroll
       for (int ks = 0; ks < DK / 32; ++ks) mma(sacc[sub], tl.k[sub][ks], qf[ks]);
     }
-    float v[8], mx = kNegInf;
+    // Scores in units of log2, masked only in tiles that cross the block's
+    // range (the causal end of the current block).
+    float v[8];
+    if (c.kt >= c.lo && c.kt + 32 <= c.kend) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int key = c.kt + qd * 8 + e;
-      v[e] = (key >= c.lo && key < c.kend) ? sacc[e >> 2][e & 3] * sc2 : kNegInf;
-      mx = fmaxf(mx, v[e]);
+      for (int e = 0; e < 8; ++e) v[e] = sacc[e >> 2][e & 3] * sc2;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int key = c.kt + qd * 8 + e;
+        v[e] = (key >= c.lo && key < c.kend) ? sacc[e >> 2][e & 3] * sc2 : kNegInf;
+      }
     }
+    float mx = fmaxf(fmaxf(fmaxf(v[0], v[1]), v[2]), fmaxf(fmaxf(v[3], v[4]), v[5]));
+    mx = fmaxf(mx, fmaxf(v[6], v[7]));
     mx = fmaxf(mx, xor16f(mx, lane));
     mx = fmaxf(mx, xor32f(mx, lane));
-    const float mn = fmaxf(m, mx);
-    const float mref = mn == kNegInf ? 0.f : mn;
-    const float alpha = fast_exp2(m - mref);
+    // Lazy rescaling: the reference m of a column moves only when the tile's
+    // maximum exceeds it by more than 8 (so p <= 2^8); the move rescales the
+    // accumulators, and is decided for the whole wave so that the common case
+    // skips the multiplications.
+    if (__builtin_amdgcn_ballot_w64(mx > m + 8.f) != 0) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = mn == kNegInf ? 1.f : fast_exp2(m - mn);
+      ls *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt) oacc[dt] *= alpha;
+      m = mn;
+    }
+    const float mref = m == kNegInf ? 0.f : m;
     float p[8], psum = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) { p[e] = fast_exp2(v[e] - mref); psum += p[e]; }
-    ls = ls * alpha + psum;
-    m = mn;
+    for (int e = 0; e < 8; ++e) {
+      p[e] = fast_exp2(v[e] - mref);
+      psum += p[e];
+    }
+    ls += psum;
     const Frag8<T> pf = to_frag<T>(p);
     Frag8<T> plo;
     if constexpr (kPrecisePV<T, OT>) plo = lo_frag(p, pf);
 #pragma unroll
     for (int dt = 0; dt < DV / 16; ++dt) {
-      oacc[dt] *= alpha;
       mma(oacc[dt], tl.v[dt], pf);
       if constexpr (kPrecisePV<T, OT>) mma(oacc[dt], tl.v[dt], plo);
     }

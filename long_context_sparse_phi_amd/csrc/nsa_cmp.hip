@@ -42,14 +42,42 @@ namespace nsa {
 // ---------------------------------------------------------------------------
 constexpr float kPScale2 = 14.f;         // pass B evaluates P * 2^kPScale2
 constexpr float kPScaleInv = 1.f / 16384.f;
-// LDS row stride of the V^T tile (elements)
+// LDS row stride of the padded (fp32) V^T tile (elements)
 template <int KT>
 constexpr int cmp_vs() { return KT + 8; }
+
+// V^T tile layout.  fp32: rows of KT keys padded to KT + 8.  bf16: rows of
+// 128 bytes (8 chunks of 8 keys) without padding, chunk c of row R stored at
+// c ^ ((R >> 1) & 7); with 32-key tiles a 128-byte row holds dv rows R and
+// R + DV/2 (chunks 0-3 and 4-7).  Measured on gfx950, both the 16-lane
+// fragment reads (16 consecutive rows, one chunk column) and the stores
+// (8 lanes per row) of this layout are free of bank conflicts, while padded
+// 32- and 64-key rows are not.
+template <typename T, int KT>
+struct VtLayout {
+  static constexpr bool kSwz = sizeof(T) == 2;
+  static constexpr int CPR = KT / 8;                  // chunks per dv row
+  template <int DV>
+  static constexpr int rows() { return kSwz ? DV * CPR / 8 : DV; }
+  // element offset of chunk c (8 keys) of dv row r
+  template <int DV>
+  __device__ static int off(int r, int c) {
+    if constexpr (kSwz) {
+      constexpr int NR = rows<DV>();
+      const int R = r % NR, cc = (r / NR) * CPR + c;
+      return R * 64 + ((cc ^ ((R >> 1) & 7)) << 3);
+    } else {
+      return r * cmp_vs<KT>() + c * 8;
+    }
+  }
+  template <int DV>
+  static constexpr size_t elems() { return kSwz ? (size_t)DV * KT : (size_t)DV * cmp_vs<KT>(); }
+};
 
 // K tile rows are unpadded with XOR-swizzled 16-byte chunks (kchunk_off).
 template <typename T, int DK, int DV, bool PB, int KT>
 constexpr size_t cmp_tile_elems() {
-  return (size_t)KT * DK + (PB ? (size_t)DV * cmp_vs<KT>() : 0);
+  return (size_t)KT * DK + (PB ? VtLayout<T, KT>::template elems<DV>() : 0);
 }
 
 // GS, NJ: group size and number of 16-block remap column tiles fixed at
@@ -58,7 +86,7 @@ template <typename T, int DK, int DV, int NCT, int NW, bool PB, typename OT, int
 __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nselp, int njt_arg) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   constexpr size_t TE = cmp_tile_elems<T, DK, DV, PB, KT>();
-  constexpr int VS = cmp_vs<KT>();
+  using VL = VtLayout<T, KT>;
   constexpr int NH = KT / 32;                               // 32-key halves per tile
   constexpr int NT = NW * 64;
   T* tiles = (T*)smem_raw;                                  // [2][TE]
@@ -131,32 +159,59 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
   Frag8<T> kr[KCH], vr[VCH > 0 ? VCH : 1];
   const T* kcb = (const T*)a.kc + ((size_t)b * dm.ncmp * dm.Hkv + g) * DK;
   const T* vtb = (const T*)a.vct + (size_t)(b * dm.Hkv + g) * DV * dm.ncmp_pad;
+  // per-thread chunk offsets, the same for every tile: global (elements from
+  // the tile's first key) and LDS (swizzled K rows, padded V^T rows)
+  const int kstride = dm.Hkv * DK;
+  int kgo[KCH], klo[KCH], krw[KCH], vgo[VCH > 0 ? VCH : 1], vlo[VCH > 0 ? VCH : 1];
+#pragma unroll
+  for (int c = 0; c < KCH; ++c) {
+    const int idx = threadIdx.x + NT * c, row = idx / (DK / 8), c8 = idx % (DK / 8);
+    krw[c] = row;
+    kgo[c] = row * kstride + c8 * 8;
+    klo[c] = kchunk_off<DK>(row, c8);
+  }
+#pragma unroll
+  for (int c = 0; c < VCH; ++c) {
+    const int idx = threadIdx.x + NT * c;
+    int row, c8;
+    if constexpr (VL::kSwz) {
+      // 8 consecutive threads fill one 128-byte LDS row
+      constexpr int NR = VL::template rows<DV>();
+      const int R = idx >> 3, cc = idx & 7;
+      row = R + NR * (cc / VL::CPR);
+      c8 = cc % VL::CPR;
+    } else {
+      row = idx / (KT / 8);
+      c8 = idx % (KT / 8);
+    }
+    vgo[c] = row * dm.ncmp_pad + c8 * 8;
+    vlo[c] = VL::template off<DV>(row, c8);
+  }
   auto gload = [&](int kt) {
+    const T* kb = kcb + (size_t)kt * kstride;
+    if (kt + KT <= dm.ncmp) {
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int idx = threadIdx.x + NT * c, row = idx / (DK / 8), c8 = idx % (DK / 8);
-      const int key = min(kt + row, dm.ncmp - 1);
-      kr[c] = load_frag(kcb + (size_t)key * dm.Hkv * DK + c8 * 8);
-    }
+      for (int c = 0; c < KCH; ++c) kr[c] = load_frag(kb + kgo[c]);
+    } else {
+      // the last tile: keys past the end repeat the last key (never used)
 #pragma unroll
-    for (int c = 0; c < VCH; ++c) {
-      const int idx = threadIdx.x + NT * c, row = idx / (KT / 8), c8 = idx % (KT / 8);
-      vr[c] = load_frag(vtb + (size_t)row * dm.ncmp_pad + kt + c8 * 8);
+      for (int c = 0; c < KCH; ++c) {
+        const int over = max(kt + krw[c] - (dm.ncmp - 1), 0);
+        kr[c] = load_frag(kb + kgo[c] - over * kstride);
+      }
     }
+    // V^T rows are padded past the last key (zeros), so no tile needs a clamp
+    const T* vb = vtb + kt;
+#pragma unroll
+    for (int c = 0; c < VCH; ++c) vr[c] = load_frag(vb + vgo[c]);
   };
   auto lstore = [&](int buf) {
     T* kt_ = tiles + (size_t)buf * TE;
     T* vt_ = kt_ + (size_t)KT * DK;
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int idx = threadIdx.x + NT * c, row = idx / (DK / 8), c8 = idx % (DK / 8);
-      *reinterpret_cast<Frag8<T>*>(kt_ + kchunk_off<DK>(row, c8)) = kr[c];
-    }
+    for (int c = 0; c < KCH; ++c) *reinterpret_cast<Frag8<T>*>(kt_ + klo[c]) = kr[c];
 #pragma unroll
-    for (int c = 0; c < VCH; ++c) {
-      const int idx = threadIdx.x + NT * c, row = idx / (KT / 8), c8 = idx % (KT / 8);
-      *reinterpret_cast<Frag8<T>*>(vt_ + row * VS + c8 * 8) = vr[c];
-    }
+    for (int c = 0; c < VCH; ++c) *reinterpret_cast<Frag8<T>*>(vt_ + vlo[c]) = vr[c];
   };
 
   const int krow = (c16 >> 2) * 8 + (c16 & 3);
@@ -248,7 +303,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
     // when O is kept in fp32 for the backward)
 #pragma unroll
     for (int dt = 0; dt < DV / 16; ++dt) {
-      const Frag8<T> vf = *reinterpret_cast<const Frag8<T>*>(vtile + (dt * 16 + c16) * VS + h * 32 + qd * 8);
+      const Frag8<T> vf = *reinterpret_cast<const Frag8<T>*>(vtile + VL::template off<DV>(dt * 16 + c16, h * 4 + qd));
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         mma(oacc[dt][ct], vf, pf[ct]);
@@ -299,6 +354,8 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
   }
   __syncthreads();
   for (int it = 0; it < nkt; ++it) {
+    // the next tile's loads go out first, the current tile is computed from
+    // LDS, then the next tile's registers are stored to the other buffer
     const int kt0 = it * KT;
     if (it + 1 < nkt) gload(kt0 + KT);
     const T* ktile = tiles + (size_t)(it & 1) * TE;
@@ -447,7 +504,7 @@ hipError_t launch_cmp_out_topn(const Dims& dm, const CmpArgs& a, hipStream_t s) 
 
 bool cmp_out_fits(const Dims& dm) {
   // pass B with one column tile per wave: tiles (largest case: fp32, 192/128) + score rows
-  const size_t tiles = 2 * ((size_t)64 * dm.dk + (size_t)dm.dv * cmp_vs<64>()) * (dm.io == IO_BF16 ? 2 : 4);
+  const size_t tiles = 2 * ((size_t)64 * dm.dk + (size_t)dm.dv * cmp_vs<64>()) * (dm.io == IO_BF16 ? 2 : 4);  // an upper bound
   return tiles + (size_t)4 * (16 / dm.G) * cmp_out_nselp(dm) * sizeof(float) <= 160 * 1024;
 }
 
