@@ -141,11 +141,12 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
     }
   }
   const float sc2 = dm.scale * kLog2e;
-  float m[NCT], ls[NCT];
+  float m[NCT], mr[NCT], ls[NCT];
   f32x4 oacc[PB ? DV / 16 : 1][NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
     m[ct] = kNegInf;
+    mr[ct] = kNegInf;
     ls[ct] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < (PB ? DV / 16 : 1); ++dt) oacc[dt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -244,8 +245,11 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
     }
   };
 
-  // pass A: online max / sum of exp2 per column.  The maximum is taken over
-  // the raw scores and scaled once (sc2 > 0), and each exponent is one fma.
+  // pass A: online max / sum of exp2.  Each lane keeps its own state over the
+  // keys it holds (8 of every 32) and the four lanes of a column are merged
+  // once at the end, so the loop has no cross-lane traffic.  The running
+  // maximum is kept raw (mr) and scaled (m, log2 units; sc2 > 0); each
+  // exponent is one fma.
   auto pass_a = [&](const f32x4 (&s)[2][NCT], int kt, auto masked) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
@@ -255,16 +259,19 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
         v[e] = s[e >> 2][ct][e & 3];
         if (masked) v[e] = kt + qd * 8 + e < nvis[ct] ? v[e] : kNegInf;
       }
-      float mx = fmaxf(fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])), fmaxf(fmaxf(v[4], v[5]), fmaxf(v[6], v[7])));
-      mx = fmaxf(mx, xor16f(mx, lane));
-      mx = fmaxf(mx, xor32f(mx, lane));
-      const float mn = fmaxf(m[ct], mx * sc2);
-      const float mref = mn == kNegInf ? 0.f : mn;
+      float mx = fmaxf(fmaxf(mr[ct], v[0]), v[1]);
+      mx = fmaxf(fmaxf(mx, v[2]), v[3]);
+      mx = fmaxf(fmaxf(mx, v[4]), v[5]);
+      mx = fmaxf(fmaxf(mx, v[6]), v[7]);
+      const float mn = mx * sc2;
+      float mref = mn;
+      if (masked) mref = mn == kNegInf ? 0.f : mn;   // nothing visible to this lane yet
       float acc = ls[ct] * fast_exp2(m[ct] - mref);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc += fast_exp2(fmaf(v[e], sc2, -mref));
       ls[ct] = acc;
       m[ct] = mn;
+      mr[ct] = mx;
     }
   };
 
@@ -390,9 +397,11 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
   if constexpr (!PB) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      float tot = ls[ct] + xor16f(ls[ct], lane);
-      tot += xor32f(tot, lane);
-      const float lse = m[ct] == kNegInf ? kNegInf : (m[ct] + __log2f(tot)) * kLn2;
+      // merge the four lane states of each column
+      const float M = colmax4(m[ct], lane);
+      const float part = m[ct] == kNegInf ? 0.f : ls[ct] * fast_exp2(m[ct] - M);
+      const float tot = colsum4(part, lane);
+      const float lse = M == kNegInf ? kNegInf : (M + __log2f(tot)) * kLn2;
       if (qd == 0 && pos[ct] < dm.T) a.lse[(size_t)(b * dm.T + pos[ct]) * dm.Hq + hq[ct]] = lse;
     }
   } else {
