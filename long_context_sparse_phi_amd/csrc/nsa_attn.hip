@@ -374,33 +374,48 @@ __global__ __launch_bounds__(NW * 64, 2) void k_win(Dims dm, WinArgs a) {
         for (int ct = 0; ct < NCT; ++ct) mma(s[sub][ct], kf[ks], qf[ct][ks]);
     }
     Frag8<T> pf[NCT], plo[NCT];
+    float v[NCT][8], mx[NCT];
+    bool grow = false;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      float v[8], mx = kNegInf;
       const int lo = pos[ct] - dm.w + 1;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        v[e] = s[e >> 2][ct][e & 3] * sc2;
+        v[ct][e] = s[e >> 2][ct][e & 3] * sc2;
         if (masked) {
           const int key = kt + qd * 8 + e;
-          v[e] = (key >= lo && key <= pos[ct]) ? v[e] : kNegInf;
+          v[ct][e] = (key >= lo && key <= pos[ct]) ? v[ct][e] : kNegInf;
         }
-        mx = fmaxf(mx, v[e]);
       }
-      mx = fmaxf(mx, xor16f(mx, lane));
-      mx = fmaxf(mx, xor32f(mx, lane));
-      const float mn = fmaxf(m[ct], mx);
-      const float mref = mn == kNegInf ? 0.f : mn;
-      const float alpha = fast_exp2(m[ct] - mref);
+      float x = fmaxf(fmaxf(fmaxf(v[ct][0], v[ct][1]), v[ct][2]), fmaxf(fmaxf(v[ct][3], v[ct][4]), v[ct][5]));
+      x = fmaxf(x, fmaxf(v[ct][6], v[ct][7]));
+      x = fmaxf(x, xor16f(x, lane));
+      mx[ct] = fmaxf(x, xor32f(x, lane));
+      grow |= mx[ct] > m[ct] + 8.f;
+    }
+    // Lazy rescaling: a column's reference m moves only when the half tile's
+    // maximum exceeds it by more than 8 (so p <= 2^8), decided for the whole
+    // wave so that the common case skips the accumulator multiplications.
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const float mn = fmaxf(m[ct], mx[ct]);
+        const float alpha = mn == kNegInf ? 1.f : fast_exp2(m[ct] - mn);
+        ls[ct] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DV / 16; ++dt) oacc[dt][ct] *= alpha;
+        m[ct] = mn;
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const float mref = m[ct] == kNegInf ? 0.f : m[ct];
       float p[8], psum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { p[e] = fast_exp2(v[e] - mref); psum += p[e]; }
-      ls[ct] = ls[ct] * alpha + psum;
-      m[ct] = mn;
+      for (int e = 0; e < 8; ++e) { p[e] = fast_exp2(v[ct][e] - mref); psum += p[e]; }
+      ls[ct] += psum;
       pf[ct] = to_frag<T>(p);
       if constexpr (kPrecisePV<T, OT>) plo[ct] = lo_frag(p, pf[ct]);
-#pragma unroll
-      for (int dt = 0; dt < DV / 16; ++dt) oacc[dt][ct] *= alpha;
     }
 #pragma unroll
     for (int dt = 0; dt < DV / 16; ++dt) {

@@ -1,13 +1,16 @@
 // Cooperative staging of 64-key attention tiles in LDS for a workgroup of NT
-// threads: a K tile [64 keys][DK] and a V^T tile [DV][64 keys] (rows padded
-// to 72 elements).  Global loads go to registers first (gload) so they can be
-// in flight while the previous tile is computed, then to LDS (lstore).
+// threads: a K tile [64 keys][DK] and a V^T tile [DV][64 keys].  Global loads
+// go to registers first (gload) so they can be in flight while the previous
+// tile is computed, then to LDS (lstore).
 //
 // K rows are unpadded; their 16-byte chunks are XOR-swizzled by row
 // (kswz) so that the 16 key rows one MFMA fragment read touches land in 16
 // different 4-bank groups.  The rows read together are the permuted key rows
 // (c/4)*8 + c%4 (+4), c = 0..15; kswz is a bijection on the chunks of a row.
-// The V^T rows are padded to 72 elements, which already spreads them.
+// bf16 V^T rows (128 bytes) are unpadded with chunk c of row r stored at
+// c ^ ((r >> 1) & 7): measured on gfx950, the 16-row fragment reads and the
+// 8-lanes-per-row stores of this layout are free of bank conflicts, while
+// rows padded to 72 elements are not.  fp32 V^T rows stay padded.
 #pragma once
 #include "nsa_common.hpp"
 
@@ -33,8 +36,14 @@ __device__ __forceinline__ int kchunk_off(int r, int chunk) {
 
 template <typename T, int DK, int DV, bool WITH_V, int NT = 256>
 struct KVTile {
+  static constexpr bool kVSwz = sizeof(T) == 2;
   static constexpr size_t kElems = (size_t)kTileKeys * DK;
-  static constexpr size_t elems = kElems + (WITH_V ? (size_t)DV * kTileVS : 0);
+  static constexpr size_t elems = kElems + (WITH_V ? (size_t)DV * (kVSwz ? kTileKeys : kTileVS) : 0);
+  // element offset of chunk c (8 keys) of V^T row r
+  static __device__ __forceinline__ int voff(int r, int c) {
+    if constexpr (kVSwz) return r * kTileKeys + ((c ^ ((r >> 1) & 7)) << 3);
+    else return r * kTileVS + c * 8;
+  }
   static constexpr int KCH = kTileKeys * DK / 8 / NT;
   static constexpr int VCH = WITH_V ? DV * kTileKeys / 8 / NT : 0;
   static_assert(KCH * NT == kTileKeys * DK / 8, "K tile must split evenly over the workgroup");
@@ -67,7 +76,7 @@ struct KVTile {
 #pragma unroll
     for (int c = 0; c < VCH; ++c) {
       const int idx = threadIdx.x + NT * c, row = idx / (kTileKeys / 8), c8 = idx % (kTileKeys / 8);
-      *reinterpret_cast<Frag8<T>*>(vt + row * kTileVS + c8 * 8) = vr[c];
+      *reinterpret_cast<Frag8<T>*>(vt + voff(row, c8)) = vr[c];
     }
   }
   // MFMA A operand from the staged K tile: row r of the tile, features ks*32 + qd*8 ..
@@ -76,7 +85,7 @@ struct KVTile {
   }
   // MFMA A operand of O^T += V^T P^T: V^T row dv, keys k0 + qd*8 ..
   static __device__ __forceinline__ Frag8<T> vfrag(const T* tile, int dv, int k0, int qd) {
-    return *reinterpret_cast<const Frag8<T>*>(tile + kElems + dv * kTileVS + k0 + qd * 8);
+    return *reinterpret_cast<const Frag8<T>*>(tile + kElems + voff(dv, k0 / 8 + qd));
   }
 };
 
