@@ -160,13 +160,26 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
   Frag8<T> kr[KCH], vr[VCH > 0 ? VCH : 1];
   const T* kcb = (const T*)a.kc + ((size_t)b * dm.ncmp * dm.Hkv + g) * DK;
   const T* vtb = (const T*)a.vct + (size_t)(b * dm.Hkv + g) * DV * dm.ncmp_pad;
+  // bf16 tiles go from global memory straight into LDS (one 16-byte chunk
+  // per lane and load, lane i of a load writing chunk i of a 1 KB window), so
+  // each thread loads the chunk that belongs at its LDS position under the
+  // swizzled layouts; fp32 tiles pass through registers.
+  constexpr bool kDMA = sizeof(T) == 2;
   // per-thread chunk offsets, the same for every tile: global (elements from
-  // the tile's first key) and LDS (swizzled K rows, padded V^T rows)
+  // the tile's first key) and LDS
   const int kstride = dm.Hkv * DK;
   int kgo[KCH], klo[KCH], krw[KCH], vgo[VCH > 0 ? VCH : 1], vlo[VCH > 0 ? VCH : 1];
 #pragma unroll
   for (int c = 0; c < KCH; ++c) {
-    const int idx = threadIdx.x + NT * c, row = idx / (DK / 8), c8 = idx % (DK / 8);
+    const int idx = threadIdx.x + NT * c;
+    int row, c8;
+    if constexpr (kDMA) {
+      row = idx / (DK / 8);
+      c8 = (idx % (DK / 8)) ^ kswz<DK>(row);   // the logical chunk stored at this position
+    } else {
+      row = idx / (DK / 8);
+      c8 = idx % (DK / 8);
+    }
     krw[c] = row;
     kgo[c] = row * kstride + c8 * 8;
     klo[c] = kchunk_off<DK>(row, c8);
@@ -176,9 +189,9 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
     const int idx = threadIdx.x + NT * c;
     int row, c8;
     if constexpr (VL::kSwz) {
-      // 8 consecutive threads fill one 128-byte LDS row
+      // position idx of the V^T region: 128-byte LDS row R, chunk slot idx % 8
       constexpr int NR = VL::template rows<DV>();
-      const int R = idx >> 3, cc = idx & 7;
+      const int R = idx >> 3, cc = (idx & 7) ^ ((R >> 1) & 7);
       row = R + NR * (cc / VL::CPR);
       c8 = cc % VL::CPR;
     } else {
@@ -188,6 +201,29 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
     vgo[c] = row * dm.ncmp_pad + c8 * 8;
     vlo[c] = VL::template off<DV>(row, c8);
   }
+  static_assert(!kDMA || VL::kSwz, "direct loads need the unpadded V^T layout");
+  const int wave_pos = (threadIdx.x >> 6) * 64;      // first position of this wave's window
+  // direct-to-LDS loads of the tile at key kt into buffer buf
+  auto dma = [&](int kt, int buf) {
+    T* kdst = tiles + (size_t)buf * TE;
+    T* vdst = kdst + (size_t)KT * DK;
+    const T* kb = kcb + (size_t)kt * kstride;
+    const bool full = kt + KT <= dm.ncmp;
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+      // the last tile: keys past the end repeat the last key (never used)
+      const int over = full ? 0 : max(kt + krw[c] - (dm.ncmp - 1), 0);
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(kb + kgo[c] - over * kstride),
+                                       (void __attribute__((address_space(3)))*)(kdst + (NT * c + wave_pos) * 8), 16,
+                                       0, 0);
+    }
+    const T* vb = vtb + kt;
+#pragma unroll
+    for (int c = 0; c < VCH; ++c)
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(vb + vgo[c]),
+                                       (void __attribute__((address_space(3)))*)(vdst + (NT * c + wave_pos) * 8), 16,
+                                       0, 0);
+  };
   auto gload = [&](int kt) {
     const T* kb = kcb + (size_t)kt * kstride;
     if (kt + KT <= dm.ncmp) {
@@ -356,15 +392,24 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
 
   const int nkt = (nmax_wg + KT - 1) / KT;
   if (nkt > 0) {
-    gload(0);
-    lstore(0);
+    if constexpr (kDMA) {
+      dma(0, 0);
+      __builtin_amdgcn_s_waitcnt(0);
+    } else {
+      gload(0);
+      lstore(0);
+    }
   }
   __syncthreads();
   for (int it = 0; it < nkt; ++it) {
     // the next tile's loads go out first, the current tile is computed from
-    // LDS, then the next tile's registers are stored to the other buffer
+    // LDS, then the next tile lands in the other buffer (directly, or from
+    // registers)
     const int kt0 = it * KT;
-    if (it + 1 < nkt) gload(kt0 + KT);
+    if (it + 1 < nkt) {
+      if constexpr (kDMA) dma(kt0 + KT, (it + 1) & 1);
+      else gload(kt0 + KT);
+    }
     const T* ktile = tiles + (size_t)(it & 1) * TE;
     const T* vtile = ktile + (size_t)KT * DK;
     // With few column tiles both halves' scores are issued before either
@@ -390,7 +435,11 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
         else pass_b(s[h], vtile, h, kt, std::true_type{});
       }
     }
-    if (it + 1 < nkt) lstore((it + 1) & 1);
+    if constexpr (kDMA) {
+      __builtin_amdgcn_s_waitcnt(0);   // this wave's direct loads have landed
+    } else {
+      if (it + 1 < nkt) lstore((it + 1) & 1);
+    }
     __syncthreads();
   }
   if (!wave_live) return;
