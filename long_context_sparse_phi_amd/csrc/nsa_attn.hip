@@ -359,7 +359,9 @@ __global__ __launch_bounds__(NW * 64, 2) void k_win(Dims dm, WinArgs a) {
   const int kfull0 = (wave_live && t0 + PW - 1 < dm.T) ? max(0, t0 + PW - 1 - dm.w + 1) : 0x7fffffff;
   const int kfull1 = t0;
 
+  // both MFMA blocks ask the scheduler to interleave LDS reads with MFMAs
   auto half_tile = [&](const T* tl_, int h, int kt, auto masked) {
+    __builtin_amdgcn_iglp_opt(0);
     f32x4 s[2][NCT];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -417,6 +419,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_win(Dims dm, WinArgs a) {
       pf[ct] = to_frag<T>(p);
       if constexpr (kPrecisePV<T, OT>) plo[ct] = lo_frag(p, pf[ct]);
     }
+    __builtin_amdgcn_iglp_opt(0);
 #pragma unroll
     for (int dt = 0; dt < DV / 16; ++dt) {
       const Frag8<T> vf = Tile::vfrag(tl_, dt * 16 + c16, h * 32, qd);
