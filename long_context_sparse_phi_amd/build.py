@@ -27,7 +27,7 @@ FLAGS = [
     "-Wno-unused-result", "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"),
 ]
-SOURCES = ["nsa_api.cpp", "nsa_phi.hip", "nsa_cmp.hip", "nsa_attn.hip", "nsa_decode.hip", "nsa_bwd.hip",
+SOURCES = ["nsa_api.cpp", "nsa_blas.cpp", "nsa_phi.hip", "nsa_cmp.hip", "nsa_attn.hip", "nsa_decode.hip", "nsa_bwd.hip",
            "nsa_append.hip"]
 
 

@@ -2,10 +2,8 @@
 // launch sequence of each entry point.  Nothing is enqueued until every check
 // has passed.
 #include <hip/hip_runtime.h>
-#include <rocblas/rocblas.h>
 
 #include <atomic>
-#include <mutex>
 #include <initializer_list>
 #include <cmath>
 #include <cstring>
@@ -153,7 +151,7 @@ hipError_t run_compress(const Dims& dm, int D, const void* x, const nsa_phi_weig
   const size_t es = esize(dm);
   const int R = dm.l / dm.d;
   const int nsub = dm.ncmp > 0 ? dm.ncmp + R - 1 : 0;
-  a.w1t = c.take((size_t)dm.hidden * dm.l * D * es);
+  a.arows = c.take(((size_t)dm.B * dm.Hkv * nsub + R) * dm.d * D * es);
   a.w2t = c.take((size_t)D * dm.hidden * es);
   a.cvec = (float*)c.take((size_t)dm.hidden * 4);
   a.y = (float*)c.take(((size_t)dm.B * dm.Hkv * nsub + R) * R * dm.hidden * 4);
@@ -206,36 +204,8 @@ bool phi_ok(const nsa_phi_weights& w) {
 // Projection layer: rocBLAS GEMMs around the operator.
 // ---------------------------------------------------------------------------
 
-// One rocBLAS handle per device, created on first use with that device
-// current; the mutex serialises setting the stream and enqueuing the GEMMs.
-std::mutex g_blas_mu;
-rocblas_handle g_blas[64];
-
-nsa_status blas_handle(rocblas_handle* h) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return NSA_ERR_HIP;
-  if (dev < 0 || dev >= 64) return NSA_ERR_UNSUPPORTED;
-  if (!g_blas[dev] && rocblas_create_handle(&g_blas[dev]) != rocblas_status_success) {
-    g_blas[dev] = nullptr;
-    return NSA_ERR_BLAS;
-  }
-  *h = g_blas[dev];
-  return NSA_OK;
-}
-
-// Row-major C[M,N] (leading dim ldc) = op(A) op(B) + beta C, with op(A) [M,K]
-// and op(B) [K,N]; ta / tb say that A / B are stored transposed ([K,M], [N,K]).
-// rocBLAS is column-major, where a row-major matrix reads as its transpose, so
-// the call computes C^T = op(B)^T op(A)^T with the operands swapped.
-bool rm_gemm(rocblas_handle h, bool ta, bool tb, int M, int N, int K, const void* A, rocblas_datatype at, int lda,
-             const void* B, rocblas_datatype bt, int ldb, float beta, void* C, rocblas_datatype ct, int ldc) {
-  if (M == 0 || N == 0) return true;
-  const float alpha = 1.f;
-  return rocblas_gemm_ex(h, tb ? rocblas_operation_transpose : rocblas_operation_none,
-                         ta ? rocblas_operation_transpose : rocblas_operation_none, N, M, K, &alpha, B, bt, ldb, A,
-                         at, lda, &beta, C, ct, ldc, C, ct, ldc, rocblas_datatype_f32_r, rocblas_gemm_algo_standard,
-                         0, 0) == rocblas_status_success;
-}
+// rocBLAS status of a layer GEMM as an API status
+nsa_status blas_status(int r) { return r == 0 ? NSA_OK : (r == 1 ? NSA_ERR_BLAS : NSA_ERR_HIP); }
 
 struct LayerBwdWs {
   void* op_ws;    // the operator's backward workspace
@@ -597,26 +567,19 @@ nsa_status nsa_layer_fwd(const nsa_params* p, const nsa_layer_args* a, void* ws,
     pa.k_cmp = a->k_cmp; pa.v_cmp = a->v_cmp; pa.lse = a->lse; pa.idx = a->idx; pa.o_branch = a->o_branch;
     pa.gate_mlp = a->gate_mlp;
     if ((st = prefill_impl(p, &pa, ws, ws_bytes, stream, nullptr, 0, true)) != NSA_OK) return st;
-    const rocblas_datatype T = dm.io == IO_BF16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
+    const BlasType T = dm.io == IO_BF16 ? kBlasBF16 : kBlasF32;
     const int ntok = dm.B * dm.T, C = dm.C;
     const int nq = dm.Hq * dm.dk, nk = dm.Hkv * dm.dk, nv = dm.Hkv * dm.dv, no = dm.Hq * dm.dv;
-    {
-      std::lock_guard<std::mutex> lk(g_blas_mu);
-      rocblas_handle h;
-      if ((st = blas_handle(&h)) != NSA_OK) return st;
-      if (rocblas_set_stream(h, (hipStream_t)stream) != rocblas_status_success) return NSA_ERR_BLAS;
-      if (!rm_gemm(h, false, false, ntok, nq, C, a->h, T, C, a->w_q, T, nq, 0.f, a->q, T, nq) ||
-          !rm_gemm(h, false, false, ntok, nk, C, a->h, T, C, a->w_k, T, nk, 0.f, a->k, T, nk) ||
-          !rm_gemm(h, false, false, ntok, nv, C, a->h, T, C, a->w_v, T, nv, 0.f, a->v, T, nv))
-        return NSA_ERR_BLAS;
-    }
+    hipStream_t s = (hipStream_t)stream;
+    if ((st = blas_status(blas_gemm(s, false, false, ntok, nq, C, a->h, T, C, a->w_q, T, nq, 0.f, a->q, T, nq))) !=
+            NSA_OK ||
+        (st = blas_status(blas_gemm(s, false, false, ntok, nk, C, a->h, T, C, a->w_k, T, nk, 0.f, a->k, T, nk))) !=
+            NSA_OK ||
+        (st = blas_status(blas_gemm(s, false, false, ntok, nv, C, a->h, T, C, a->w_v, T, nv, 0.f, a->v, T, nv))) !=
+            NSA_OK)
+      return st;
     if ((st = prefill_impl(p, &pa, ws, ws_bytes, stream, nullptr, 0)) != NSA_OK) return st;
-    std::lock_guard<std::mutex> lk(g_blas_mu);
-    rocblas_handle h;
-    if ((st = blas_handle(&h)) != NSA_OK) return st;
-    if (rocblas_set_stream(h, (hipStream_t)stream) != rocblas_status_success) return NSA_ERR_BLAS;
-    if (!rm_gemm(h, false, false, ntok, C, no, a->o, T, no, a->w_o, T, C, 0.f, a->y, T, C)) return NSA_ERR_BLAS;
-    return NSA_OK;
+    return blas_status(blas_gemm(s, false, false, ntok, C, no, a->o, T, no, a->w_o, T, C, 0.f, a->y, T, C));
   } catch (...) {
     return NSA_ERR_INTERNAL;
   }
@@ -646,20 +609,18 @@ nsa_status nsa_layer_bwd(const nsa_params* p, const nsa_layer_bwd_args* a, void*
     const size_t op_bytes = bwd_ws_bytes(dm);
     if ((st = bwd_impl(p, &ba, w.op_ws, op_bytes, stream, nullptr, 0, true)) != NSA_OK) return st;
     const bool bf = dm.io == IO_BF16;
-    const rocblas_datatype T = bf ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
-    const rocblas_datatype F = rocblas_datatype_f32_r;
+    const BlasType T = bf ? kBlasBF16 : kBlasF32;
+    const BlasType F = kBlasF32;
     const int ntok = dm.B * dm.T, C = dm.C;
     const int nq = dm.Hq * dm.dk, nk = dm.Hkv * dm.dk, nv = dm.Hkv * dm.dv, no = dm.Hq * dm.dv;
     hipStream_t s = (hipStream_t)stream;
     {
       // dO = dy w_o^T (io dtype), dW_o = o^T dy
-      std::lock_guard<std::mutex> lk(g_blas_mu);
-      rocblas_handle h;
-      if ((st = blas_handle(&h)) != NSA_OK) return st;
-      if (rocblas_set_stream(h, s) != rocblas_status_success) return NSA_ERR_BLAS;
-      if (!rm_gemm(h, false, true, ntok, no, C, a->dy, T, C, a->w_o, T, C, 0.f, w.d_o, T, no) ||
-          !rm_gemm(h, true, false, no, C, ntok, a->o, T, no, a->dy, T, C, 0.f, a->dw_o, F, C))
-        return NSA_ERR_BLAS;
+      if ((st = blas_status(blas_gemm(s, false, true, ntok, no, C, a->dy, T, C, a->w_o, T, C, 0.f, w.d_o, T, no))) !=
+              NSA_OK ||
+          (st = blas_status(blas_gemm(s, true, false, no, C, ntok, a->o, T, no, a->dy, T, C, 0.f, a->dw_o, F, C))) !=
+              NSA_OK)
+        return st;
     }
     // the operator's backward; its dx (the gate path) initialises dh
     if ((st = bwd_impl(p, &ba, w.op_ws, op_bytes, stream, nullptr, 0)) != NSA_OK) return st;
@@ -668,19 +629,19 @@ nsa_status nsa_layer_bwd(const nsa_params* p, const nsa_layer_bwd_args* a, void*
     if (bf) h32 = w.h32;
     struct Proj { const void* w; const float* d; int n; void* dw; };
     const Proj pr[3] = {{a->w_q, w.dq, nq, a->dw_q}, {a->w_k, w.dk, nk, a->dw_k}, {a->w_v, w.dv, nv, a->dw_v}};
-    std::lock_guard<std::mutex> lk(g_blas_mu);
-    rocblas_handle h;
-    if ((st = blas_handle(&h)) != NSA_OK) return st;
-    if (rocblas_set_stream(h, s) != rocblas_status_success) return NSA_ERR_BLAS;
     for (const Proj& j : pr) {
       // dW = h^T d; dh += d W^T (fp32 operands; the weight is widened first)
-      if (!rm_gemm(h, true, false, C, j.n, ntok, h32, F, C, j.d, F, j.n, 0.f, j.dw, F, j.n)) return NSA_ERR_BLAS;
+      if ((st = blas_status(blas_gemm(s, true, false, C, j.n, ntok, h32, F, C, j.d, F, j.n, 0.f, j.dw, F, j.n))) !=
+          NSA_OK)
+        return st;
       const float* w32 = (const float*)j.w;
       if (bf) {
         if (launch_to_f32(j.w, (size_t)C * j.n, w.w32, s) != hipSuccess) return NSA_ERR_HIP;
         w32 = w.w32;
       }
-      if (!rm_gemm(h, false, true, ntok, C, j.n, j.d, F, j.n, w32, F, j.n, 1.f, a->dh, F, C)) return NSA_ERR_BLAS;
+      if ((st = blas_status(blas_gemm(s, false, true, ntok, C, j.n, j.d, F, j.n, w32, F, j.n, 1.f, a->dh, F, C))) !=
+          NSA_OK)
+        return st;
     }
     return NSA_OK;
   } catch (...) {

@@ -81,7 +81,7 @@ struct BwdBufs {
   float* part_slc; // [B*Hkv*max_slc_seg][ls][dk+dv]
   float* gpart;    // split-K GEMM / column-sum partials
   // phi
-  void* w1t;       // [H, l*D]   io
+  void* arows;     // [B*Hkv*nsub + l/d, d*D] io: phi GEMM1 rows
   void* w2t;       // [D, H]     io
   float* y;        // GEMM1 output
   float* act;      // [R,H] pre-activation
@@ -137,7 +137,7 @@ static size_t bwd_carve(const Dims& dm, void* ws, BwdBufs* w) {
     const int R = dm.l / dm.d;
     const size_t rows = BG * dm.ncmp;
     const size_t nsub = dm.ncmp > 0 ? dm.ncmp + R - 1 : 0;
-    w->w1t = take((size_t)dm.hidden * dm.l * D * es);
+    w->arows = take((BG * nsub + R) * dm.d * D * es);
     w->w2t = take((size_t)D * dm.hidden * es);
     w->y = (float*)take((BG * nsub + R) * R * dm.hidden * 4);
     w->act = (float*)take(rows * dm.hidden * 4);
@@ -1357,8 +1357,7 @@ static hipError_t phi_bwd(const Dims& dm, const BwdArgs& a, const nsa_phi_weight
   const int H = dm.hidden, R = dm.l / dm.d;
   const int nsub = dm.ncmp + R - 1;
   // recompute the forward pre-activations
-  if ((e = launch_transpose_2d(dm, dm.l * D, H, w.w1, a.w.w1t, s)) != hipSuccess) return e;
-  if ((e = launch_phi_gemm1(dm, D, nsub, xsrc, w.pe, a.w.w1t, a.w.y, s)) != hipSuccess) return e;
+  if ((e = launch_phi_gemm1(dm, D, nsub, xsrc, w.pe, w.w1, a.w.arows, a.w.y, s)) != hipSuccess) return e;
   k_phi_act<T><<<(unsigned)((rows * H + 255) / 256), 256, 0, s>>>(dm, a.w.y, (const T*)w.b1, a.w.act, a.w.hid);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // db2 = colsum(dout); dW2 = hid^T dout

@@ -49,7 +49,7 @@ struct PhiMlpArgs {
   const void* b1;        // [hidden]
   const void* w2;        // [hidden, D]
   const void* b2;        // [D]
-  void* w1t;             // ws: [hidden, l*D]   (io type)
+  void* arows;           // ws: [B*Hkv*nsub + l/d, d*D] sub-block rows (io type)
   void* w2t;             // ws: [D, hidden]     (io type)
   float* cvec;           // ws: [hidden]  b1 + sum_j pe[j] . w1[j]
   float* y;              // ws: [B*Hkv*nsub, (l/d)*hidden] sub-block products
@@ -58,9 +58,10 @@ struct PhiMlpArgs {
   void* outT;            // optional [B,Hkv,D,ncmp_pad]
 };
 hipError_t launch_phi_mlp(const Dims& dm, const PhiMlpArgs& a, hipStream_t s);
-// First phi GEMM alone (sub-block products y, see nsa_phi.hip); w1t = w1 transposed.
-hipError_t launch_phi_gemm1(const Dims& dm, int D, int nsub, const void* x, const void* pe, const void* w1t,
-                            float* y, hipStream_t s);
+// First phi GEMM alone (sub-block products y, see nsa_phi.hip); arows:
+// workspace of (B*Hkv*nsub + l/d) * d*D io elements.
+hipError_t launch_phi_gemm1(const Dims& dm, int D, int nsub, const void* x, const void* pe, const void* w1,
+                            void* arows, float* y, hipStream_t s);
 size_t phi_mlp_ws_bytes(const Dims& dm, int D);
 
 // ---- compressed attention ----
@@ -122,6 +123,14 @@ hipError_t launch_win_combine(const Dims& dm, const WinArgs& a, hipStream_t s);
 struct GateMlp {
   const void *w1, *b1, *b2;
 };
+// Row-major GEMM through rocBLAS on stream s: C[M,N] (leading dim ldc) =
+// op(A) op(B) + beta C with op(A) [M,K], op(B) [K,N]; ta / tb: A / B stored
+// transposed ([K,M], [N,K]).  fp32 accumulation.  Returns 0 on success, 1 when
+// rocBLAS reports an error, 2 when the device or its handle is unavailable.
+enum BlasType { kBlasBF16 = 0, kBlasF32 = 1 };
+int blas_gemm(hipStream_t s, bool ta, bool tb, int M, int N, int K, const void* A, BlasType at, int lda,
+              const void* B, BlasType bt, int ldb, float beta, void* C, BlasType ct, int ldc);
+
 // dst[i] = float(src[i]) for a bf16 array of n elements.
 hipError_t launch_to_f32(const void* src, size_t n, float* dst, hipStream_t s);
 hipError_t launch_gate_mlp(const Dims& dm, int ntok, const void* x, const void* w_gate, const GateMlp& g,

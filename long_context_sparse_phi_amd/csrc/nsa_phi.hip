@@ -227,64 +227,33 @@ hipError_t launch_meanpool(const Dims& dm, int D, const void* x, void* out, void
 //          rows Mmain + r: A = pe rows r*d .. r*d+d-1 (flattened)
 //   hidden: a = b1 + sum_r y[Mmain + r, r*H + o] + sum_r y[(bg, i + r), r*H + o]; h = gelu(a)
 //   GEMM2: out[b, i, g, :] = h w2 + b2, rounded to the I/O type.
-// Each wave owns a 32x32 output tile (2x2 MFMA 16x16 tiles); a workgroup of
-// four waves owns 64x64.
+// GEMM1 is a plain dense GEMM once the rows of A are laid out contiguously
+// (k_phi_arows): it runs through rocBLAS, one call per W1 chunk r, with fp32
+// accumulation and output.  GEMM2 (small) is k_phi_gemm2: each wave owns a
+// 32x32 output tile (2x2 MFMA 16x16 tiles), a workgroup of four waves 64x64.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
-__global__ __launch_bounds__(256) void k_phi_gemm1(Dims dm, int nsub, const T* __restrict__ x,
-                                                   const T* __restrict__ pe,
-                                                   const T* __restrict__ w1t, float* __restrict__ y) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c16 = lane & 15, qd = lane >> 4;
-  const int H = dm.hidden, R = dm.l / dm.d, KK = dm.d * D, N = R * H;
-  const int Mmain = dm.B * dm.Hkv * nsub, M = Mmain + R;
-  const int mbase = blockIdx.y * 64 + (wave >> 1) * 32;
-  const int nbase = blockIdx.x * 64 + (wave & 1) * 32;
-  const T* arow[2];
-  bool aval[2];
-  for (int i = 0; i < 2; ++i) {
-    int m = mbase + i * 16 + c16;
-    aval[i] = m < M;
-    if (m < Mmain) {
-      int s = m % nsub, bg = m / nsub, g = bg % dm.Hkv, b = bg / dm.Hkv;
-      arow[i] = x + ((size_t)(b * dm.T + s * dm.d) * dm.Hkv + g) * D;
-    } else {
-      int r = aval[i] ? m - Mmain : 0;
-      arow[i] = pe + (size_t)r * dm.d * D;
-    }
+// A rows: sub-block s of (b, g) as d*D contiguous elements, then the R
+// position-embedding rows (pe rows r*d .. r*d+d-1).  8 elements per thread.
+template <typename T>
+__global__ __launch_bounds__(256) void k_phi_arows(Dims dm, int D, int nsub, const T* __restrict__ x,
+                                                   const T* __restrict__ pe, T* __restrict__ arows) {
+  const int KK = dm.d * D, R = dm.l / dm.d;
+  const size_t Mmain = (size_t)dm.B * dm.Hkv * nsub;
+  const size_t id = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= (Mmain + R) * (KK / 8)) return;
+  const size_t m = id / (KK / 8);
+  const int k = (int)(id % (KK / 8)) * 8;
+  const T* src;
+  if (m < Mmain) {
+    const int bg = (int)(m / nsub), sidx = (int)(m % nsub), b = bg / dm.Hkv, g = bg % dm.Hkv;
+    const int j = k / D, e = k % D;
+    src = x + ((size_t)(b * dm.T + sidx * dm.d + j) * dm.Hkv + g) * D + e;
+  } else {
+    src = pe + (size_t)(m - Mmain) * KK + k;
   }
-  const bool amain[2] = {mbase + c16 < Mmain, mbase + 16 + c16 < Mmain};
-  const T* brow[2];
-  for (int j = 0; j < 2; ++j) {
-    int n = nbase + j * 16 + c16;  // n < N always: N is a multiple of 64
-    int r = n / H, o = n % H;
-    brow[j] = w1t + (size_t)o * (dm.l * D) + (size_t)r * KK;
-  }
-  f32x4 acc[2][2];
-  for (int i = 0; i < 2; ++i)
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int kk = 0; kk < KK; kk += 32) {
-    const int xx = kk + qd * 8;
-    const int jt = xx / D, e = xx % D;
-    Frag8<T> af[2], bfr[2];
-    for (int i = 0; i < 2; ++i) {
-      if (!aval[i]) { af[i] = zero_frag<T>(); continue; }
-      const T* p = amain[i] ? arow[i] + (size_t)jt * dm.Hkv * D + e : arow[i] + xx;
-      af[i] = load_frag(p);
-    }
-    for (int j = 0; j < 2; ++j) bfr[j] = load_frag(brow[j] + xx);
-    for (int i = 0; i < 2; ++i)
-      for (int j = 0; j < 2; ++j) mma(acc[i][j], af[i], bfr[j]);
-  }
-  for (int i = 0; i < 2; ++i)
-    for (int j = 0; j < 2; ++j) {
-      int n = nbase + j * 16 + c16;
-      for (int r = 0; r < 4; ++r) {
-        int m = mbase + i * 16 + qd * 4 + r;
-        if (m < M) y[(size_t)m * N + n] = acc[i][j][r];
-      }
-    }
+  *reinterpret_cast<Frag8<T>*>(arows + m * KK + k) = load_frag(src);
 }
+
 
 // h rows: (b*Hkv + g)*ncmp + i.  bf16 I/O: h holds hi rows then lo rows (bf16);
 // fp32 I/O: h is fp32.
@@ -387,7 +356,7 @@ size_t phi_mlp_ws_bytes(const Dims& dm, int D) {
   const int nsub = dm.ncmp > 0 ? dm.ncmp + R - 1 : 0;
   size_t b = 0;
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  b += al((size_t)dm.hidden * dm.l * D * es);                       // w1t
+  b += al(((size_t)dm.B * dm.Hkv * nsub + R) * dm.d * D * es);      // arows
   b += al((size_t)D * dm.hidden * es);                              // w2t
   b += al((size_t)dm.hidden * 4);                                   // cvec (unused slot)
   b += al(((size_t)dm.B * dm.Hkv * nsub + R) * R * dm.hidden * 4);  // y
@@ -400,14 +369,8 @@ static hipError_t phi_mlp_impl(const Dims& dm, const PhiMlpArgs& a, hipStream_t 
   const int R = dm.l / dm.d;
   const int nsub = dm.ncmp + R - 1;
   hipError_t e;
-  if ((e = launch_transpose_2d(dm, dm.l * D, dm.hidden, a.w1, a.w1t, s)) != hipSuccess) return e;
   if ((e = launch_transpose_2d(dm, dm.hidden, D, a.w2, a.w2t, s)) != hipSuccess) return e;
-  {
-    const int M = dm.B * dm.Hkv * nsub + R, N = R * dm.hidden;
-    dim3 grid(N / 64, (M + 63) / 64);
-    k_phi_gemm1<T, D><<<grid, 256, 0, s>>>(dm, nsub, (const T*)a.x, (const T*)a.pe, (const T*)a.w1t, a.y);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
+  if ((e = launch_phi_gemm1(dm, D, nsub, a.x, a.pe, a.w1, a.arows, a.y, s)) != hipSuccess) return e;
   {
     size_t total = (size_t)dm.B * dm.Hkv * dm.ncmp * dm.hidden;
     k_phi_hidden<T><<<(unsigned)((total + 255) / 256), 256, 0, s>>>(dm, nsub, a.y, (const T*)a.b1, a.h);
@@ -427,25 +390,29 @@ static hipError_t phi_mlp_impl(const Dims& dm, const PhiMlpArgs& a, hipStream_t 
   return hipSuccess;
 }
 
-template <typename T, int D>
-static hipError_t gemm1_impl(const Dims& dm, int nsub, const void* x, const void* pe, const void* w1t, float* y,
-                             hipStream_t s) {
-  const int R = dm.l / dm.d;
-  const int M = dm.B * dm.Hkv * nsub + R, N = R * dm.hidden;
-  dim3 grid(N / 64, (M + 63) / 64);
-  k_phi_gemm1<T, D><<<grid, 256, 0, s>>>(dm, nsub, (const T*)x, (const T*)pe, (const T*)w1t, y);
-  return hipGetLastError();
-}
-
-hipError_t launch_phi_gemm1(const Dims& dm, int D, int nsub, const void* x, const void* pe, const void* w1t,
-                            float* y, hipStream_t s) {
+hipError_t launch_phi_gemm1(const Dims& dm, int D, int nsub, const void* x, const void* pe, const void* w1,
+                            void* arows, float* y, hipStream_t s) {
+  const int R = dm.l / dm.d, KK = dm.d * D, H = dm.hidden;
+  const size_t M = (size_t)dm.B * dm.Hkv * nsub + R;
+  const size_t total = M * (KK / 8);
   const bool bf = dm.io == IO_BF16;
-  switch (D) {
-    case 64: return bf ? gemm1_impl<bf16, 64>(dm, nsub, x, pe, w1t, y, s) : gemm1_impl<float, 64>(dm, nsub, x, pe, w1t, y, s);
-    case 128: return bf ? gemm1_impl<bf16, 128>(dm, nsub, x, pe, w1t, y, s) : gemm1_impl<float, 128>(dm, nsub, x, pe, w1t, y, s);
-    case 192: return bf ? gemm1_impl<bf16, 192>(dm, nsub, x, pe, w1t, y, s) : gemm1_impl<float, 192>(dm, nsub, x, pe, w1t, y, s);
+  if (bf)
+    k_phi_arows<bf16><<<(unsigned)((total + 255) / 256), 256, 0, s>>>(dm, D, nsub, (const bf16*)x, (const bf16*)pe,
+                                                                       (bf16*)arows);
+  else
+    k_phi_arows<float><<<(unsigned)((total + 255) / 256), 256, 0, s>>>(dm, D, nsub, (const float*)x,
+                                                                        (const float*)pe, (float*)arows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // y[:, r*H : (r+1)*H] = A * w1[r*KK : (r+1)*KK, :]
+  const BlasType t = bf ? kBlasBF16 : kBlasF32;
+  const size_t es = bf ? 2 : 4;
+  for (int r = 0; r < R; ++r) {
+    const void* br = (const char*)w1 + (size_t)r * KK * H * es;
+    if (blas_gemm(s, false, false, (int)M, H, KK, arows, t, KK, br, t, H, 0.f, y + (size_t)r * H, kBlasF32, R * H))
+      return hipErrorUnknown;
   }
-  return hipErrorInvalidValue;
+  return hipSuccess;
 }
 
 hipError_t launch_phi_mlp(const Dims& dm, const PhiMlpArgs& a, hipStream_t s) {
