@@ -84,10 +84,12 @@ struct BwdBufs {
   void* arows;     // [B*Hkv*nsub + l/d, d*D] io: phi GEMM1 rows
   void* w2t;       // [D, H]     io
   float* y;        // GEMM1 output
-  float* act;      // [R,H] pre-activation
-  float* hid;      // [R,H] gelu(act)
-  float* dh;       // [R,H]
-  float* du;       // [R,l*D]
+  float* act;      // [rows,H] pre-activation (rows = B*Hkv*ncmp compressed keys)
+  float* hid;      // [rows,H] gelu(act)
+  float* dh;       // [rows,H]
+  void* dap;       // [B*Hkv*nsub + l/d - 1, H] dh * gelu'(act) in the sub-block row layout:
+                   // bf16 I/O a hi plane then a lo plane, fp32 I/O one fp32 plane
+  float* dxs;      // [B*Hkv*nsub, d*D] token gradient of phi per sub-block
 };
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -143,7 +145,8 @@ static size_t bwd_carve(const Dims& dm, void* ws, BwdBufs* w) {
     w->act = (float*)take(rows * dm.hidden * 4);
     w->hid = (float*)take(rows * dm.hidden * 4);
     w->dh = (float*)take(rows * dm.hidden * 4);
-    w->du = (float*)take(rows * dm.l * D * 4);
+    w->dap = take((nsub ? BG * nsub + R - 1 : 0) * dm.hidden * 4);
+    w->dxs = (float*)take(BG * nsub * dm.d * D * 4);
   }
   return off;
 }
@@ -1266,59 +1269,69 @@ __global__ __launch_bounds__(256) void k_phi_dact(size_t n, const float* __restr
   dh[id] *= cdf + a * pdf;
 }
 
-// dW1[r*d*D + x][o] = sum_{bg,i} (x_tok[bg, (i+r)*d + j][e] + pe[r*d + j][e]) * da[(bg,i)][o],
-// x = j*D + e.  64 x 64 output tile per workgroup, rows in steps of 32.
+// The MLP gradient da = dh * gelu'(act), moved to the sub-block row layout of
+// the GEMM1 rows: compressed key i of head (b, g) goes to row bg*nsub + R-1 + i,
+// and rows bg*nsub .. bg*nsub + R-2 (and R-1 rows past the last head) hold
+// zeros.  Key i reads sub-blocks i .. i+R-1, one per W1 chunk r, so the rows
+// that pair with sub-block row m under chunk r are this layout shifted by
+// R-1-r rows, for every head at once.  bf16 I/O splits da into a bf16 hi part
+// and the bf16 rounding of the remainder (hi + lo carries ~16 mantissa bits),
+// so the GEMMs run on bf16 operands at close to fp32 accuracy.  dh is
+// overwritten with da (its column sum is db1).
 template <typename T>
-__global__ __launch_bounds__(256) void k_phi_dw1(Dims dm, int D, const T* __restrict__ xs, const T* __restrict__ pe,
-                                                 const float* __restrict__ da, float* __restrict__ dw1) {
-  __shared__ float As[32][64 + 4];
-  __shared__ float Bs[32][64 + 4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c16 = lane & 15, kq = lane >> 4;
-  const int H = dm.hidden, dD = dm.d * D;
-  const int r = blockIdx.z;
-  const int x0 = blockIdx.y * 64, o0 = blockIdx.x * 64;
-  const int rows = dm.B * dm.Hkv * dm.ncmp;
-  f32x4 acc[2][2];
-  for (int i = 0; i < 2; ++i)
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < rows; k0 += 32) {
-    for (int i = tid; i < 64 * 32; i += 256) {
-      const int xx = i & 63, kk = i >> 6, row = k0 + kk, xg = x0 + xx;
-      float v = 0.f;
-      if (row < rows && xg < dD) {
-        const int ii = row % dm.ncmp, bg = row / dm.ncmp, b = bg / dm.Hkv, g = bg % dm.Hkv;
-        const int j = xg / D, e = xg % D;
-        const int tok = (ii + r) * dm.d + j;
-        v = to_f32(xs[((size_t)(b * dm.T + tok) * dm.Hkv + g) * D + e]) + to_f32(pe[(size_t)(r * dm.d + j) * D + e]);
-      }
-      As[kk][xx] = v;
-      const int oo = i & 63, o = o0 + oo;
-      Bs[kk][oo] = (row < rows && o < H) ? da[(size_t)row * H + o] : 0.f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 32; kk += 4) {
-      float af[2], bfv[2];
-      for (int i = 0; i < 2; ++i) af[i] = As[kk + kq][(wave >> 1) * 32 + i * 16 + c16];
-      for (int j = 0; j < 2; ++j) bfv[j] = Bs[kk + kq][(wave & 1) * 32 + j * 16 + c16];
-      for (int i = 0; i < 2; ++i)
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], bfv[j], acc[i][j], 0, 0, 0);
-    }
-    __syncthreads();
+__global__ __launch_bounds__(256) void k_phi_da_split(Dims dm, int nsub, const float* __restrict__ act,
+                                                      float* __restrict__ dh, T* __restrict__ dap) {
+  const int H = dm.hidden, R = dm.l / dm.d;
+  const size_t BG = (size_t)dm.B * dm.Hkv, rows_p = BG * nsub + R - 1;
+  const size_t id = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= rows_p * H) return;
+  const size_t p = id / H;
+  const int o = (int)(id % H);
+  const size_t bg = p / nsub;
+  const int i = (int)(p % nsub) - (R - 1);
+  float v = 0.f;
+  if (bg < BG && i >= 0) {
+    const size_t k = (bg * dm.ncmp + i) * H + o;
+    const float x = act[k];
+    const float cdf = 0.5f * (1.f + erff(x * 0.70710678118654752f));
+    const float pdf = 0.3989422804014327f * expf(-0.5f * x * x);
+    v = dh[k] * (cdf + x * pdf);
+    dh[k] = v;
   }
-  for (int i = 0; i < 2; ++i)
-    for (int j = 0; j < 2; ++j) {
-      const int o = o0 + (wave & 1) * 32 + j * 16 + c16;
-      for (int rr = 0; rr < 4; ++rr) {
-        const int xg = x0 + (wave >> 1) * 32 + i * 16 + kq * 4 + rr;
-        if (xg < dD && o < H) dw1[((size_t)r * dD + xg) * H + o] = acc[i][j][rr];
-      }
-    }
+  if constexpr (sizeof(T) == 2) {
+    const T hi = from_f32<T>(v);
+    dap[id] = hi;
+    dap[rows_p * H + id] = from_f32<T>(v - to_f32(hi));
+  } else {
+    dap[id] = v;
+  }
 }
 
-// Token gradient from phi: dx[b, tok, g, e] += sum over blocks i covering tok of
-// du[(bg, i)][(tok - i*d)*D + e]   (MLP), or of dcmp[(bg,i)][e] / l (mean).
+// Position-embedding part of dW1: every compressed key adds pe to its sub-block
+// rows, so dW1[x][o] gains pe[x] * sum of da[., o] = pe[x] * db1[o].
+template <typename T>
+__global__ __launch_bounds__(256) void k_phi_dw1_pe(size_t n, int H, const T* __restrict__ pe,
+                                                    const float* __restrict__ db1, float* __restrict__ dw1) {
+  const size_t id = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (id >= n) return;
+  dw1[id] += to_f32(pe[id / H]) * db1[id % H];
+}
+
+// dpe = sum over keys of da W1^T = db1 W1^T: one wave per pe element.
+template <typename T>
+__global__ __launch_bounds__(256) void k_phi_dpe(int n, int H, const T* __restrict__ w1,
+                                                 const float* __restrict__ db1, float* __restrict__ dpe) {
+  const int x = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (x >= n) return;
+  float acc = 0.f;
+  for (int o = lane; o < H; o += 64) acc += db1[o] * to_f32(w1[(size_t)x * H + o]);
+  for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (lane == 0) dpe[x] = acc;
+}
+
+// Token gradient from phi: dx[b, tok, g, e] += dxs[bg*nsub + tok/d][(tok%d)*D + e]
+// (MLP: the GEMMs already summed the blocks covering each sub-block), or the
+// sum over blocks i covering tok of dcmp[(bg,i)][e] / l (mean).
 __global__ __launch_bounds__(256) void k_phi_dx(Dims dm, int D, const float* __restrict__ src, int mlp,
                                                 float* __restrict__ dx) {
   const size_t total = (size_t)dm.B * dm.T * dm.Hkv * D;
@@ -1330,16 +1343,18 @@ __global__ __launch_bounds__(256) void k_phi_dx(Dims dm, int D, const float* __r
   r /= dm.Hkv;
   const int tok = r % dm.T, b = r / dm.T;
   const int bg = b * dm.Hkv + g;
+  if (mlp) {
+    const int nsub = dm.ncmp + dm.l / dm.d - 1;
+    if (tok < nsub * dm.d)
+      dx[id] += src[((size_t)bg * nsub + tok / dm.d) * dm.d * D + (size_t)(tok % dm.d) * D + e];
+    return;
+  }
   // blocks i with i*d <= tok < i*d + l, 0 <= i < ncmp
   int ilo = tok - dm.l + 1;
   ilo = ilo <= 0 ? 0 : (ilo + dm.d - 1) / dm.d;
   const int ihi = min(tok / dm.d, dm.ncmp - 1);
   float s = 0.f;
-  for (int i = ilo; i <= ihi; ++i) {
-    const size_t row = (size_t)bg * dm.ncmp + i;
-    if (mlp) s += src[row * dm.l * D + (size_t)(tok - i * dm.d) * D + e];
-    else s += src[row * D + e] / (float)dm.l;
-  }
+  for (int i = ilo; i <= ihi; ++i) s += src[((size_t)bg * dm.ncmp + i) * D + e] / (float)dm.l;
   dx[id] += s;
 }
 
@@ -1371,24 +1386,40 @@ static hipError_t phi_bwd(const Dims& dm, const BwdArgs& a, const nsa_phi_weight
     Gemm g{(int)rows, H, D, dcmp, D, 1, w.w2, 1, D, a.w.dh, H, 0};
     if ((e = gemm<float, T>(g, nullptr, s)) != hipSuccess) return e;
   }
-  k_phi_dact<<<(unsigned)((rows * H + 255) / 256), 256, 0, s>>>(rows * H, a.w.act, a.w.dh);
+  const size_t Mmain = (size_t)dm.B * dm.Hkv * nsub, rows_p = Mmain + R - 1;
+  k_phi_da_split<T><<<(unsigned)((rows_p * H + 255) / 256), 256, 0, s>>>(dm, nsub, a.w.act, a.w.dh, (T*)a.w.dap);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = colsum((int)rows, H, H, a.w.dh, (float*)gr.b1, a.w.gpart, s)) != hipSuccess) return e;
-  // dW1 chunks
+  const bool bf = sizeof(T) == 2;
+  const BlasType t = bf ? kBlasBF16 : kBlasF32;
+  const int planes = bf ? 2 : 1, dD = dm.d * D;
+  auto da_rows = [&](int pl, int shift) {
+    return (const char*)a.w.dap + ((size_t)pl * rows_p + shift) * H * sizeof(T);
+  };
+  // dW1 chunk r = (sub-block rows)^T (da shifted by R-1-r), plus the pe part
+  for (int r = 0; r < R; ++r)
+    for (int pl = 0; pl < planes; ++pl)
+      if (blas_gemm(s, true, false, dD, H, (int)Mmain, a.w.arows, t, dD, da_rows(pl, R - 1 - r), t, H,
+                    pl ? 1.f : 0.f, (float*)gr.w1 + (size_t)r * dD * H, kBlasF32, H))
+        return hipErrorUnknown;
   {
-    dim3 grid((H + 63) / 64, (dm.d * D + 63) / 64, R);
-    k_phi_dw1<T><<<grid, 256, 0, s>>>(dm, D, (const T*)xsrc, (const T*)w.pe, a.w.dh, (float*)gr.w1);
+    const size_t n = (size_t)dm.l * D * H;
+    k_phi_dw1_pe<T><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(n, H, (const T*)w.pe, (const float*)gr.b1,
+                                                                 (float*)gr.w1);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // du = da W1^T -> token gradient and dpe
-  {
-    Gemm g{(int)rows, dm.l * D, H, a.w.dh, H, 1, w.w1, 1, H, a.w.du, (long long)dm.l * D, 0};
-    if ((e = gemm<float, T>(g, nullptr, s)) != hipSuccess) return e;
-  }
-  if ((e = colsum((int)rows, dm.l * D, (long long)dm.l * D, a.w.du, (float*)gr.pe, a.w.gpart, s)) != hipSuccess)
-    return e;
+  // token gradient per sub-block: sum over chunks of (da shifted by R-1-r) W1_r^T
+  for (int r = 0; r < R; ++r)
+    for (int pl = 0; pl < planes; ++pl)
+      if (blas_gemm(s, false, true, (int)Mmain, dD, H, da_rows(pl, R - 1 - r), t, H,
+                    (const char*)w.w1 + (size_t)r * dD * H * sizeof(T), t, H, (r | pl) ? 1.f : 0.f, a.w.dxs,
+                    kBlasF32, dD))
+        return hipErrorUnknown;
+  k_phi_dpe<T><<<(unsigned)((dm.l * D + 3) / 4), 256, 0, s>>>(dm.l * D, H, (const T*)w.w1, (const float*)gr.b1,
+                                                              (float*)gr.pe);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   const size_t total = (size_t)dm.B * dm.T * dm.Hkv * D;
-  k_phi_dx<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(dm, D, a.w.du, 1, dx);
+  k_phi_dx<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(dm, D, a.w.dxs, 1, dx);
   return hipGetLastError();
 }
 
