@@ -24,6 +24,11 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # packed fp32 VALU forms are disabled: only plain scalar fp32 ops are emitted
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: with the AGPR form the compiler copied
+    # loop-carried accumulators into AGPRs and back on every iteration
+    # (hundreds of v_accvgpr moves per tile in the dK/dV, selected-branch and
+    # decode loops)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-result", "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"),
 ]
