@@ -122,11 +122,22 @@ __device__ __forceinline__ void mma(f32x4& c, const f16x8& a, const f16x8& b) {
   c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// Two fp32 values -> two bf16 (round to nearest even) in one packed convert.
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x2v cvt2_bf16(float a, float b) {
+  return __builtin_convertvector((f32x2v){a, b}, bf16x2v);
+}
+
 // 8 fp32 values -> operand fragment of element type T (round to nearest even).
 __device__ __forceinline__ Frag8<bf16> to_frag_bf16(const float* x) {
   Frag8<bf16> f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) f.v[e] = (bf16)x[e];
+  for (int e = 0; e < 8; e += 2) {
+    const bf16x2v h = cvt2_bf16(x[e], x[e + 1]);
+    f.v[e] = h[0];
+    f.v[e + 1] = h[1];
+  }
   return f;
 }
 template <typename T> __device__ __forceinline__ Frag8<T> to_frag(const float* x);
@@ -138,12 +149,17 @@ template <> __device__ __forceinline__ Frag8<float> to_frag<float>(const float* 
   return f;
 }
 // x = hi + lo with hi, lo in bf16: the pair carries ~16 significant bits.
+// Pairs are converted together and hi is widened back to fp32 by bit shifts.
 __device__ __forceinline__ void split_bf16(const float* x, Frag8<bf16>& hi, Frag8<bf16>& lo) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    bf16 h = (bf16)x[e];
-    hi.v[e] = h;
-    lo.v[e] = (bf16)(x[e] - (float)h);
+  for (int e = 0; e < 8; e += 2) {
+    const bf16x2v h = cvt2_bf16(x[e], x[e + 1]);
+    const unsigned hb = __builtin_bit_cast(unsigned, h);
+    const bf16x2v l = cvt2_bf16(x[e] - __uint_as_float(hb << 16), x[e + 1] - __uint_as_float(hb & 0xffff0000u));
+    hi.v[e] = h[0];
+    hi.v[e + 1] = h[1];
+    lo.v[e] = l[0];
+    lo.v[e + 1] = l[1];
   }
 }
 
@@ -152,7 +168,11 @@ __device__ __forceinline__ void split_bf16(const float* x, Frag8<bf16>& hi, Frag
 __device__ __forceinline__ Frag8<bf16> lo_frag(const float* x, const Frag8<bf16>& hi) {
   Frag8<bf16> lo;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) lo.v[e] = (bf16)(x[e] - (float)hi.v[e]);
+  for (int e = 0; e < 8; e += 2) {
+    const bf16x2v l = cvt2_bf16(x[e] - (float)hi.v[e], x[e + 1] - (float)hi.v[e + 1]);
+    lo.v[e] = l[0];
+    lo.v[e + 1] = l[1];
+  }
   return lo;
 }
 __device__ __forceinline__ Frag8<float> lo_frag(const float*, const Frag8<float>&) { return Frag8<float>{}; }
