@@ -24,6 +24,8 @@
 //   * The reverse index (positions that selected each block, ascending) is
 //     built by a per-chunk histogram, a scan and an ordered fill.
 //   * phi and the gate projection go through a strided fp32 MFMA GEMM.
+#include <type_traits>
+
 #include "../../include/nsa.h"
 #include "nsa_common.hpp"
 #include "nsa_kernels.hpp"
@@ -826,9 +828,16 @@ __global__ __launch_bounds__(256) void k_bwd_kv(Dims dm, BwdArgs a) {
   for (int dt = 0; dt < DV / 16; ++dt) dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float sc2 = dm.scale * kLog2e;
 
-  St reg;
+  // Two register stages when they fit the register budget (one staging chunk
+  // per thread, DK + DV <= 256): the rows of a position pair are requested two
+  // pairs ahead of their compute and one pair ahead of their copy into LDS.
+  // Otherwise one pair ahead, copied into LDS at the end of the same step
+  // (the two stages are then never live together).
+  constexpr bool kTwo = St::NCH == 1;
+  St rg[2];
   // global -> registers for the position pair (pp0, pp1): rows r = i*16 + h
-  auto gload = [&](int pp0, int pp1) {
+  auto gload = [&](auto S, int pp0, int pp1) {
+    St& reg = rg[decltype(S)::value];
 #pragma unroll
     for (int cc = 0; cc < St::NCH; ++cc) {
       const int u = tid + 256 * cc;
@@ -856,7 +865,8 @@ __global__ __launch_bounds__(256) void k_bwd_kv(Dims dm, BwdArgs a) {
     }
   };
   // registers -> LDS buffer: row-major and transposed copies
-  auto lstore = [&](int buf) {
+  auto lstore = [&](auto S, int buf) {
+    const St& reg = rg[decltype(S)::value];
     T* Qr = (T*)(smem_raw + (size_t)buf * St::bytes);
     T* Qt = Qr + 32 * QS;
     T* Dr = Qt + DK * TS;
@@ -885,14 +895,23 @@ __global__ __launch_bounds__(256) void k_bwd_kv(Dims dm, BwdArgs a) {
     }
   };
 
-  gload(position(0), position(1));
-  lstore(0);
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  gload(S0{}, position(0), position(1));
+  if (kTwo && 2 < npos) gload(S1{}, position(2), position(3));
+  lstore(S0{}, 0);
   __syncthreads();
-  for (int pi = 0; pi < npos; pi += 2) {
-    const int buf = (pi >> 1) & 1;
+  // Pair pi/2 is computed from LDS buffer buf = (pi/2) & 1.  With two stages
+  // its registers were stage buf (a compile-time index: that loop is unrolled
+  // by two pairs); with one stage everything goes through stage 0.
+  auto step = [&](auto RS, int buf, int pi) {
+    constexpr int rs = decltype(RS)::value;
     int pos[2] = {position(pi), position(pi + 1)};
-    const bool more = pi + 2 < npos;
-    if (more) gload(position(pi + 2), position(pi + 3));
+    if constexpr (kTwo) {
+      if (pi + 4 < npos) gload(RS, position(pi + 4), position(pi + 5));
+    } else {
+      if (pi + 2 < npos) gload(S0{}, position(pi + 2), position(pi + 3));
+    }
     const T* Qr = (const T*)(smem_raw + (size_t)buf * St::bytes);
     const T* Qt = Qr + 32 * QS;
     const T* Dr = Qt + DK * TS;
@@ -964,8 +983,19 @@ __global__ __launch_bounds__(256) void k_bwd_kv(Dims dm, BwdArgs a) {
         if constexpr (sizeof(T) == 2) mma(dk[dt], xf, dslo);
       }
     }
-    if (more) lstore(buf ^ 1);
+    if (pi + 2 < npos) {
+      if constexpr (kTwo) lstore(std::integral_constant<int, rs ^ 1>{}, buf ^ 1);
+      else lstore(S0{}, buf ^ 1);
+    }
     __syncthreads();
+  };
+  if constexpr (kTwo) {
+    for (int pi = 0; pi < npos; pi += 4) {
+      step(S0{}, 0, pi);
+      if (pi + 2 < npos) step(S1{}, 1, pi + 2);
+    }
+  } else {
+    for (int pi = 0; pi < npos; pi += 2) step(S0{}, (pi >> 1) & 1, pi);
   }
   if (!wave_live) return;
   // write: lane holds key column c16, features dt*16 + 4qd + r
