@@ -23,7 +23,10 @@
 //     segments whose partial sums are added in a fixed order afterwards.
 //   * The reverse index (positions that selected each block, ascending) is
 //     built by a per-chunk histogram, a scan and an ordered fill.
-//   * phi and the gate projection go through a strided fp32 MFMA GEMM.
+//   * phi's first layer: recomputed through rocBLAS; its weight and token
+//     gradients are rocBLAS GEMMs over the sub-block rows (da shifted into
+//     the same row layout, see phi_bwd).  phi's second layer and the gate
+//     projection go through a strided fp32 MFMA GEMM.
 #include <type_traits>
 
 #include "../../include/nsa.h"
