@@ -1026,45 +1026,65 @@ static size_t kv_lds() {
   return 2 * KvStage<T, DK, DV>::bytes + kSegSlc * sizeof(int);
 }
 
-// Sum the compressed-key segments in order: dkc/dvc [B,Hkv,ncmp,D].
+// Segment sums of the dK/dV partials, in segment order (deterministic).  A
+// thread owns kRedVec vectors of 4 consecutive features of one key; grid.y
+// splits a 64-key group's (dk+dv)/4-vector rows over workgroups, so every
+// thread's loads are independent and can be in flight together.
+constexpr int kRedVec = 4;
+
+// compressed keys: dkc/dvc [B,Hkv,ncmp,D] = sum over the query segments
 __global__ __launch_bounds__(256) void k_reduce_cmp(Dims dm, BwdArgs a) {
   const BwdPlan& pl = a.pl;
-  const int W = dm.dk + dm.dv;
+  const int W4 = (dm.dk + dm.dv) / 4;
   const int r = blockIdx.x;              // (bg, kg)
   const int kg = r % pl.nkg_cmp, bg = r / pl.nkg_cmp;
   // segments of this key group start at its first key's first visible position
   const int pf = (kg * 64) * dm.d + dm.l - 1;
-  for (int i = threadIdx.x; i < 64 * W; i += 256) {
-    const int kk = i / W, e = i % W, key = kg * 64 + kk;
-    if (key >= dm.ncmp) continue;
-    float s = 0.f;
-    for (int seg = 0; seg < pl.nseg_cmp; ++seg) {
-      if (pf + seg * kSegCmp >= dm.T) break;
-      s += a.w.part_cmp[(((size_t)r * pl.nseg_cmp + seg) * 64 + kk) * W + e];
-    }
-    if (e < dm.dk) a.w.dkc[((size_t)bg * dm.ncmp + key) * dm.dk + e] = s;
-    else a.w.dvc[((size_t)bg * dm.ncmp + key) * dm.dv + e - dm.dk] = s;
+  const int nseg = pf < dm.T ? min(pl.nseg_cmp, (dm.T - pf + kSegCmp - 1) / kSegCmp) : 0;
+  const f32x4* __restrict__ part = reinterpret_cast<const f32x4*>(a.w.part_cmp) + (size_t)r * pl.nseg_cmp * 64 * W4;
+  const size_t sstride = (size_t)64 * W4;
+  float* __restrict__ dkc = a.w.dkc;
+  float* __restrict__ dvc = a.w.dvc;
+#pragma unroll
+  for (int q = 0; q < kRedVec; ++q) {
+    const int v = (blockIdx.y * kRedVec + q) * 256 + threadIdx.x;
+    const int kk = v / W4, e = (v % W4) * 4, key = kg * 64 + kk;
+    if (kk >= 64 || key >= dm.ncmp) continue;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int seg = 0; seg < nseg; ++seg) acc += part[seg * sstride + v];
+    float* dst = e < dm.dk ? dkc + ((size_t)bg * dm.ncmp + key) * dm.dk + e
+                           : dvc + ((size_t)bg * dm.ncmp + key) * dm.dv + (e - dm.dk);
+    *reinterpret_cast<f32x4*>(dst) = acc;
   }
 }
 
-// Add the selected-block segments, in order, into dk / dv.
+// selected blocks: dks/dvs += sum over the block's list segments
 __global__ __launch_bounds__(256) void k_reduce_slc(Dims dm, BwdArgs a) {
   const BwdPlan& pl = a.pl;
-  const int W = dm.dk + dm.dv;
+  const int W4 = (dm.dk + dm.dv) / 4;
   const int j = blockIdx.x % dm.nsel, bg = blockIdx.x / dm.nsel;
   const int b = bg / dm.Hkv, g = bg % dm.Hkv;
   const int cnt = a.w.cnt[(size_t)bg * dm.nsel + j];
   if (cnt == 0) return;
   const int nseg = (cnt + kSegSlc - 1) / kSegSlc;
   const int slot0 = a.w.segoff[(size_t)bg * dm.nsel + j];
-  for (int i = threadIdx.x; i < dm.ls * W; i += 256) {
-    const int kk = i / W, e = i % W, key = j * dm.ls + kk;
-    if (key >= dm.T) continue;
-    float s = 0.f;
-    for (int sg = 0; sg < nseg; ++sg)
-      s += a.w.part_slc[(((size_t)bg * pl.max_slc_seg + slot0 + sg) * dm.ls + kk) * W + e];
-    if (e < dm.dk) a.dks[((size_t)(b * dm.T + key) * dm.Hkv + g) * dm.dk + e] += s;
-    else a.dvs[((size_t)(b * dm.T + key) * dm.Hkv + g) * dm.dv + e - dm.dk] += s;
+  const f32x4* __restrict__ part =
+      reinterpret_cast<const f32x4*>(a.w.part_slc) + ((size_t)bg * pl.max_slc_seg + slot0) * dm.ls * W4;
+  const size_t sstride = (size_t)dm.ls * W4;
+  float* __restrict__ dks = a.dks;
+  float* __restrict__ dvs = a.dvs;
+#pragma unroll
+  for (int q = 0; q < kRedVec; ++q) {
+    const int v = (blockIdx.y * kRedVec + q) * 256 + threadIdx.x;
+    const int kk = v / W4, e = (v % W4) * 4, key = j * dm.ls + kk;
+    if (kk >= dm.ls || key >= dm.T) continue;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int sg = 0; sg < nseg; ++sg) acc += part[sg * sstride + v];
+    float* dst = e < dm.dk ? dks + ((size_t)(b * dm.T + key) * dm.Hkv + g) * dm.dk + e
+                           : dvs + ((size_t)(b * dm.T + key) * dm.Hkv + g) * dm.dv + (e - dm.dk);
+    f32x4 d = *reinterpret_cast<const f32x4*>(dst);
+    d += acc;
+    *reinterpret_cast<f32x4*>(dst) = d;
   }
 }
 
@@ -1528,7 +1548,10 @@ static hipError_t bwd_impl(const Dims& dm, const nsa_bwd_args* args, BwdArgs& a,
   if ((e = mark()) != hipSuccess) return e;
   if (dm.ncmp > 0) {
     k_bwd_kv<T, DK, DV, KV_CMP><<<BG * pl.nkg_cmp * pl.nseg_cmp, 256, klds, s>>>(dm, a);
-    k_reduce_cmp<<<BG * pl.nkg_cmp, 256, 0, s>>>(dm, a);
+    {
+      const int nv = 64 * ((dm.dk + dm.dv) / 4);
+      k_reduce_cmp<<<dim3(BG * pl.nkg_cmp, (nv + 256 * kRedVec - 1) / (256 * kRedVec)), 256, 0, s>>>(dm, a);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // stage 4: window keys (writes dkw, dvw); with independent K/V per branch the
@@ -1548,7 +1571,10 @@ static hipError_t bwd_impl(const Dims& dm, const nsa_bwd_args* args, BwdArgs& a,
   k_rev_scan<<<BG, 256, 0, s>>>(dm, a);
   k_rev_fill<<<BG * pl.nchunk, 64, dm.nsel * sizeof(int), s>>>(dm, a);
   k_bwd_kv<T, DK, DV, KV_SLC><<<BG * pl.max_slc_seg * pl.nkc_slc, 256, klds, s>>>(dm, a);
-  k_reduce_slc<<<BG * dm.nsel, 256, 0, s>>>(dm, a);
+  {
+    const int nv = dm.ls * ((dm.dk + dm.dv) / 4);
+    k_reduce_slc<<<dim3(BG * dm.nsel, (nv + 256 * kRedVec - 1) / (256 * kRedVec)), 256, 0, s>>>(dm, a);
+  }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // stage 6: phi
   if ((e = mark()) != hipSuccess) return e;
