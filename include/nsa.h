@@ -23,9 +23,9 @@
  *   device memory the kernels need is the caller's workspace of
  *   nsa_workspace_size() bytes.  The library allocates nothing itself, with
  *   one exception: the first call on a device that runs a rocBLAS GEMM (the
- *   MLP form of phi, in the forward and the backward, and the projection
- *   layer) creates that device's rocBLAS handle, which keeps a workspace of
- *   its own until the process ends.
+ *   gate projection and the MLP form of phi in the forward and the backward,
+ *   the projection layer) creates that device's rocBLAS handle, which keeps
+ *   a workspace of its own until the process ends.
  * - Tensors are dense, row-major, in the order their shapes are written.
  *   Query head h belongs to KV head h / group_size.
  * - io_dtype (NSA_BF16 or NSA_FP32) is the element type of every input and
@@ -63,8 +63,9 @@ typedef enum nsa_status {
   NSA_ERR_HIP = 4,          /* a HIP runtime call failed */
   NSA_ERR_INTERNAL = 5,
   NSA_ERR_BLAS = 6          /* a rocBLAS call of the projection layer failed
-                               (a failed rocBLAS call inside phi is reported
-                               as NSA_ERR_HIP) */
+                               (a failed rocBLAS call inside the operator,
+                               in the gates or phi, is reported as
+                               NSA_ERR_HIP) */
 } nsa_status;
 
 typedef enum nsa_dtype { NSA_BF16 = 0, NSA_FP32 = 1 } nsa_dtype;

@@ -64,11 +64,23 @@ static hipError_t gate_layer(int ntok, int C, int HO, const void* x, const void*
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void k_sigmoid(size_t n, float* __restrict__ g) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) g[i] = 1.f / (1.f + expf(-g[i]));
+}
+
+// The linear gate is a plain GEMM (x and W_g share the I/O type): rocBLAS with
+// fp32 accumulation and output, then the sigmoid in place.
 hipError_t launch_gate(const Dims& dm, int ntok, const void* x, const void* w, float* gates,
                        hipStream_t s) {
   const int HO = dm.Hq * 3;
-  if (dm.io == IO_BF16) return gate_layer<bf16, bf16, 2>(ntok, dm.C, HO, x, w, nullptr, gates, nullptr, s);
-  return gate_layer<float, float, 2>(ntok, dm.C, HO, x, w, nullptr, gates, nullptr, s);
+  if (ntok == 0) return hipSuccess;
+  const BlasType t = dm.io == IO_BF16 ? kBlasBF16 : kBlasF32;
+  if (blas_gemm(s, false, false, ntok, HO, dm.C, x, t, dm.C, w, t, HO, 0.f, gates, kBlasF32, HO))
+    return hipErrorUnknown;
+  const size_t n = (size_t)ntok * HO;
+  k_sigmoid<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(n, gates);
+  return hipGetLastError();
 }
 
 hipError_t launch_gate_mlp(const Dims& dm, int ntok, const void* x, const void* w_gate, const GateMlp& g,
