@@ -21,6 +21,11 @@ CASES = {
     "few_blocks": W("decode_64k", B=2, T=300, H_kv=1),
     "no_cmp_block": W("decode_64k", B=1, T=20, H_kv=2),
     "g8_window_larger_than_cache": W("tiny_fp32", mode="decode", dtype="bf16", B=2, T=700, G=8, H_kv=2, w=1000),
+    # more than 1024 selection blocks in the score row (l = l' = d = 16)
+    "long_score_row_g16": W("decode_64k", B=2, T=16400, H_kv=1, d_k=64, d_v=64, l=16, d=16, l_sel=16, n=8,
+                            w=128, hidden=64, bias_std=0.02),
+    "long_score_row_g4": W("tiny_fp32", mode="decode", dtype="bf16", B=2, T=16400, l=16, d=16, l_sel=16, n=8,
+                           w=128),
 }
 
 
