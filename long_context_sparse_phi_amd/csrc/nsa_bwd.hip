@@ -37,8 +37,8 @@ namespace nsa {
 
 int bwd_stage_count() { return 8; }
 
-constexpr int kSegCmp = 1024;    // query positions per compressed-key segment
-constexpr int kSegSlc = 1024;    // list entries per selected-block segment
+constexpr int kSegCmp = 512;     // query positions per compressed-key segment
+constexpr int kSegSlc = 512;     // list entries per selected-block segment
 constexpr int kRevChunk = 256;   // positions per reverse-index chunk
 constexpr int kMaxSplit = 64;    // split-K factor bound of the reduction GEMMs
 

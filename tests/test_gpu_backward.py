@@ -22,13 +22,13 @@ CASES = {
     "small_blocks_g4_b2": W("tiny_fp32", mode="train", dtype="bf16", B=2, T=300, l=8, d=4, l_sel=16, n=5, w=24),
     "g8_mlp_d64": W("train_16k", T=400, G=8, H_kv=2, d_k=64, d_v=64, hidden=64, n=5, w=60, bias_std=0.05),
     "short_no_cmp_block": W("train_16k", T=20, H_kv=1),
-    # more than 1024 query positions per key: the dK/dV partials span several
-    # segments (block 0 is selected by every position; the first compressed
-    # keys are seen by all later ones), so the ordered segment sums run
+    # thousands of query positions per key: the dK/dV partials span several
+    # 512-position segments (block 0 is selected by every position; the first
+    # compressed keys are seen by all later ones), so the ordered segment sums run
     "multi_segment_bf16_d64": W("tiny_fp32", mode="train", dtype="bf16", T=2200),
     "multi_segment_mlp_d128": W("train_16k", B=1, T=2100, H_kv=1, n=6, w=128, bias_std=0.02),
     # more than 1024 selection blocks (l = l' = d = 16): the reverse index over
-    # 1025 blocks, 17 segments for block 0 (the oracle takes about 30 s)
+    # 1025 blocks, 33 segments for block 0 (the oracle takes about 30 s)
     "long_score_rows_t16400": W("tiny_fp32", mode="train", dtype="bf16", T=16400, l=16, d=16, l_sel=16, n=8,
                                 w=128),
 }
