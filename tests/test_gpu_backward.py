@@ -27,6 +27,8 @@ CASES = {
     # compressed keys are seen by all later ones), so the ordered segment sums run
     "multi_segment_bf16_d64": W("tiny_fp32", mode="train", dtype="bf16", T=2200),
     "multi_segment_mlp_d128": W("train_16k", B=1, T=2100, H_kv=1, n=6, w=128, bias_std=0.02),
+    # several segments per key for each of four (sequence, KV head) pairs
+    "multi_segment_b2_hkv2": W("tiny_fp32", mode="train", dtype="bf16", B=2, T=1500, H_kv=2),
     # more than 1024 selection blocks (l = l' = d = 16): the reverse index over
     # 1025 blocks, 33 segments for block 0 (the oracle takes about 30 s)
     "long_score_rows_t16400": W("tiny_fp32", mode="train", dtype="bf16", T=16400, l=16, d=16, l_sel=16, n=8,
