@@ -41,7 +41,7 @@ from scipy.special import erf
 
 __all__ = [
     "Params", "gate", "gate_logits", "compress", "remap_matrix", "attend", "n_cmp_visible",
-    "candidate_blocks", "forced_blocks", "top_n", "is_near_tie", "forward",
+    "candidate_blocks", "forced_blocks", "top_n", "is_near_tie", "SCORE_FLOOR", "forward",
     "decode", "append_token", "backward", "layer_forward", "layer_backward", "dq_rows", "dense_causal", "dense_causal_bwd", "round_io", "gelu", "gelu_grad", "sigmoid",
     "cmp_keys", "slc_keys", "win_keys", "decode_token_count",
 ]
@@ -273,9 +273,16 @@ def top_n(scores, t: int, p: Params) -> List[int]:
     return sorted(F + _ranked_rest(scores, t, p)[:r])
 
 
-def is_near_tie(scores, t: int, p: Params, rel: float = 1e-3) -> bool:
+# Smallest score an fp32 kernel still resolves to 1e-3: scores are sums of
+# probabilities (each head's row sums to 1); below 2^-100 a score's terms sit
+# at or under fp32's normal range, so two such scores count as a tie.
+SCORE_FLOOR = 2.0 ** -100
+
+
+def is_near_tie(scores, t: int, p: Params, rel: float = 1e-3, floor: float = SCORE_FLOOR) -> bool:
     """True when the last selected and first unselected ranked scores are within
-    ``rel`` of the larger one, so that rounding may legitimately swap them."""
+    ``rel`` of the larger one, so that rounding may legitimately swap them, or
+    when both lie below ``floor`` (indistinguishable from 0 in fp32 arithmetic)."""
     J = candidate_blocks(t, p)
     if len(J) <= p.n:
         return False
@@ -284,7 +291,8 @@ def is_near_tie(scores, t: int, p: Params, rel: float = 1e-3) -> bool:
     if r <= 0 or len(rest) <= r:
         return False
     a, b = scores[rest[r - 1]], scores[rest[r]]
-    return abs(a - b) <= rel * max(abs(a), abs(b))
+    big = max(abs(a), abs(b))
+    return abs(a - b) <= rel * big or big < floor
 
 
 def decode_token_count(s: int, p: Params) -> int:

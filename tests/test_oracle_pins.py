@@ -314,6 +314,13 @@ def test_top_n_ties_prefer_lower_index_and_forced_blocks():
     assert O.is_near_tie(s, t, p)
     s[3] = 0.7 * (1 - 5e-3)
     assert not O.is_near_tie(s, t, p)
+    # below the fp32 score floor two scores tie whatever their ratio; above it
+    # the relative rule alone decides
+    s[:] = 0.0
+    s[3], s[5] = 2.0 ** -101, 2.0 ** -130
+    assert O.is_near_tie(s, t, p)
+    s[3], s[5] = 2.0 ** -90, 2.0 ** -95
+    assert not O.is_near_tie(s, t, p)
 
 
 # ---------------------------------------------------------------- selected / window branches
