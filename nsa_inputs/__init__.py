@@ -54,6 +54,7 @@ class Workload:
     bias_std: float = 0.0       # std of phi biases (0: biases start at zero)
     gate_std: float = 0.02      # std of the gate projection weights
     gate_hidden: int = 0        # 0: linear gate; else hidden width of a two-layer gate MLP
+    q_group_corr: float = 0.0   # correlation between the query heads of one KV group (each stays N(0,1))
 
     @property
     def H_q(self) -> int:
@@ -115,6 +116,18 @@ def _kv(seed: int, name: str, w: Workload, B: int, T: int, dim: int) -> torch.Te
     return t
 
 
+def _queries(seed: int, name: str, w: Workload, lead) -> torch.Tensor:
+    """Query heads [*lead, Hq, dk], each N(0,1).  With q_group_corr = c > 0 the
+    G heads of a KV group share a component: q = sqrt(c) * s_group + sqrt(1-c) * z_head,
+    so heads of one group favour the same keys (peaked group-shared scores)."""
+    q = _normal(seed, name, (*lead, w.H_q, w.d_k))
+    c = w.q_group_corr
+    if c > 0:
+        s = _normal(seed, name + "_group", (*lead, w.H_kv, w.d_k))
+        q.mul_((1.0 - c) ** 0.5).add_(s.repeat_interleave(w.G, dim=-2), alpha=c ** 0.5)
+    return q
+
+
 def _phi(seed: int, tag: str, w: Workload, dim: int) -> Dict[str, torch.Tensor]:
     """Random-init parameters of the compression MLP phi for K (dim=d_k) or V (dim=d_v).
 
@@ -167,7 +180,7 @@ def make_prefill_inputs(w: Workload, seed: int = 0) -> Dict[str, object]:
     """
     B, T = w.B, w.T
     d = {
-        "q": _normal(seed, "q", (B, T, w.H_q, w.d_k)),
+        "q": _queries(seed, "q", w, (B, T)),
         "k": _kv(seed, "k", w, B, T, w.d_k),
         "v": _kv(seed, "v", w, B, T, w.d_v),
         "x": _normal(seed, "x", (B, T, w.gate_dim)),
@@ -188,7 +201,7 @@ def make_decode_inputs(w: Workload, seed: int = 0) -> Dict[str, object]:
     """
     B, T = w.B, w.T
     d = {
-        "q": _normal(seed, "dec.q", (B, w.H_q, w.d_k)),
+        "q": _queries(seed, "dec.q", w, (B,)),
         "k_cache": _kv(seed, "k", w, B, T, w.d_k),
         "v_cache": _kv(seed, "v", w, B, T, w.d_v),
         "x": _normal(seed, "dec.x", (B, w.gate_dim)),

@@ -52,3 +52,16 @@ class SampledRows:
     def __getitem__(self, idx):
         b, t = idx
         return self.data[b, self.pos[int(t)]]
+
+
+# Input recipes whose compressed-branch scores are peaked: the G query heads of
+# a KV group share a component (so they favour the same blocks) and phi's
+# weights are larger than the workloads' 0.02, so compressed keys spread the
+# logits over tens to hundreds of nats.  "extreme" also offsets every
+# selection block's keys and values (std 3), which widens the selected and
+# window branches' logits.
+PEAKED = {
+    "peaked": dict(phi_std=0.15, q_group_corr=0.9, bias_std=0.02),
+    "steep": dict(phi_std=0.20, q_group_corr=0.95, bias_std=0.02),
+    "extreme": dict(phi_std=0.25, q_group_corr=0.95, bias_std=0.02, kv_offset_std=3.0),
+}
