@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define NSA_ABI_VERSION 3
+#define NSA_ABI_VERSION 4
 
 typedef enum nsa_status {
   NSA_OK = 0,
@@ -133,7 +133,13 @@ typedef struct nsa_phi_weights {
  * gets its own keys and values so that their gradients do not interfere):
  *   k_slc, v_slc [B,T,Hkv,dk|dv] for the selected branch and k_win, v_win for
  *   the window branch, all four set or all NULL.  When set, k and v feed the
- *   compressed branch (phi) only.  NULL: one k, v for all three branches. */
+ *   compressed branch (phi) only.  NULL: one k, v for all three branches.
+ * Precomputed compressed keys/values (optional, both or neither; the
+ * decode step takes its compressed cache the same way):
+ *   k_cmp_in [B,Ncmp,Hkv,dk], v_cmp_in [B,Ncmp,Hkv,dv] in io_dtype.  When
+ *   set, phi is not run (phi_k, phi_v are not read) and these feed the
+ *   compressed branch and the importance scores; k_cmp / v_cmp, if given,
+ *   receive a copy of them. */
 typedef struct nsa_prefill_args {
   const void *q, *k, *v, *x, *w_gate;
   nsa_phi_weights phi_k, phi_v;
@@ -141,6 +147,7 @@ typedef struct nsa_prefill_args {
   void *k_cmp, *v_cmp, *lse, *idx, *o_branch, *p_slc, *gates;
   const void *k_slc, *v_slc, *k_win, *v_win;
   nsa_gate_mlp gate_mlp;
+  const void *k_cmp_in, *v_cmp_in;
 } nsa_prefill_args;
 
 /* One decode step per sequence; the new token's key/value are already stored

@@ -180,13 +180,15 @@ def _branch_kv(cfg: Config, kv, tag: str, dev):
 
 def nsa_fwd_prefill(cfg: Config, q, k, v, x, w_gate, phi_k=None, phi_v=None, *, out=None,
                     save_for_backward: bool = False, debug: bool = False, kv_slc=None, kv_win=None,
-                    gate_mlp=None, workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
+                    gate_mlp=None, kv_cmp=None, workspace: Optional[torch.Tensor] = None) -> Dict[str, torch.Tensor]:
     """NSA prefill forward.  Returns {"o": ...} plus, when save_for_backward,
     k_cmp, v_cmp, lse, idx, o_branch, and, when debug, also p_slc and gates.
     kv_slc, kv_win: (k, v) pairs of the selected and window branches when each
     branch has its own keys and values (both or neither); k, v then feed the
     compressed branch only.  With cfg.gate_hidden > 0, gate_mlp holds the gate
-    MLP's first layer and biases and w_gate its output layer [Hg, Hq, 3]."""
+    MLP's first layer and biases and w_gate its output layer [Hg, Hq, 3].
+    kv_cmp: precomputed compressed (k_cmp [B,Ncmp,Hkv,dk], v_cmp [B,Ncmp,Hkv,dv])
+    used instead of running phi (phi_k, phi_v are then not needed)."""
     dev = q.device
     dt = cfg.torch_dtype
     B, T, Hq, Hkv = cfg.B, cfg.T, cfg.H_q, cfg.H_kv
@@ -209,8 +211,15 @@ def nsa_fwd_prefill(cfg: Config, q, k, v, x, w_gate, phi_k=None, phi_v=None, *, 
     a = _lib.nsa_prefill_args()
     for name, t in (("q", q), ("k", k), ("v", v), ("x", x), ("w_gate", w_gate)):
         setattr(a, name, t.data_ptr())
-    a.phi_k = _phi_struct(cfg, phi_k, cfg.d_k, dev)
-    a.phi_v = _phi_struct(cfg, phi_v, cfg.d_v, dev)
+    if kv_cmp is None:
+        a.phi_k = _phi_struct(cfg, phi_k, cfg.d_k, dev)
+        a.phi_v = _phi_struct(cfg, phi_v, cfg.d_v, dev)
+    else:
+        kc, vc = kv_cmp
+        _check(kc, "k_cmp_in", (B, cfg.n_cmp, Hkv, cfg.d_k), dt, dev)
+        _check(vc, "v_cmp_in", (B, cfg.n_cmp, Hkv, cfg.d_v), dt, dev)
+        a.k_cmp_in = kc.data_ptr() if kc.numel() else None
+        a.v_cmp_in = vc.data_ptr() if vc.numel() else None
     for name in ("o", "k_cmp", "v_cmp", "lse", "idx", "o_branch", "p_slc", "gates"):
         t = res.get(name)
         setattr(a, name, t.data_ptr() if (t is not None and t.numel()) else None)
@@ -539,5 +548,6 @@ def config_from_workload(w, **over) -> Config:
     """Config for a workload description of the shared input generator."""
     c = Config(B=w.B, T=w.T, H_kv=w.H_kv, G=w.G, d_k=w.d_k, d_v=w.d_v, l=w.l, d=w.d, l_sel=w.l_sel,
                n=w.n, w=w.w, gate_dim=w.gate_dim, hidden=w.hidden, phi=w.phi, dtype=w.dtype,
-               gate_hidden=getattr(w, "gate_hidden", 0))
+               gate_hidden=getattr(w, "gate_hidden", 0),
+               scale=0.0 if getattr(w, "scale_mult", 1.0) == 1.0 else w.scale_mult / math.sqrt(w.d_k))
     return dataclasses.replace(c, **over) if over else c

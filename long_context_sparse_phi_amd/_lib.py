@@ -17,7 +17,7 @@ NSA_BF16, NSA_FP32 = 0, 1
 NSA_PHI_MEANPOOL, NSA_PHI_MLP = 0, 1
 (NSA_OP_FWD_PREFILL, NSA_OP_FWD_DECODE, NSA_OP_BWD, NSA_OP_COMPRESS, NSA_OP_DENSE, NSA_OP_APPEND,
  NSA_OP_DENSE_BWD, NSA_OP_LAYER_FWD, NSA_OP_LAYER_BWD) = range(9)
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _vp = ctypes.c_void_p
 
@@ -51,7 +51,8 @@ class nsa_prefill_args(ctypes.Structure):
                 [("phi_k", nsa_phi_weights), ("phi_v", nsa_phi_weights)] +
                 [(n, _vp) for n in ("o", "k_cmp", "v_cmp", "lse", "idx", "o_branch", "p_slc", "gates",
                                     "k_slc", "v_slc", "k_win", "v_win")] +
-                [("gate_mlp", nsa_gate_mlp)])
+                [("gate_mlp", nsa_gate_mlp)] +
+                [(n, _vp) for n in ("k_cmp_in", "v_cmp_in")])
 
 
 class nsa_decode_args(ctypes.Structure):

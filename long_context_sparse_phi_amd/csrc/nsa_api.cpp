@@ -314,7 +314,11 @@ static nsa_status prefill_impl(const nsa_params* p, const nsa_prefill_args* a, v
     const void* opt[] = {a->k_cmp, a->v_cmp, a->lse, a->idx, a->o_branch, a->p_slc, a->gates};
     for (const void* r : opt)
       if (r && !aligned16(r)) return NSA_ERR_INVALID_ARG;
-    if (dm.hidden && (!phi_ok(a->phi_k) || !phi_ok(a->phi_v))) return NSA_ERR_INVALID_ARG;
+    bool given_cmp = false;
+    if (!all_or_none({a->k_cmp_in, a->v_cmp_in}, &given_cmp)) return NSA_ERR_INVALID_ARG;
+    // phi runs when there is a complete block and no compressed keys are given
+    const bool run_phi = dm.ncmp > 0 && !given_cmp;
+    if (dm.hidden && run_phi && (!phi_ok(a->phi_k) || !phi_ok(a->phi_v))) return NSA_ERR_INVALID_ARG;
     if (!gate_ok(dm, a->gate_mlp)) return NSA_ERR_INVALID_ARG;
     bool split = false;
     if (!all_or_none({a->k_slc, a->v_slc, a->k_win, a->v_win}, &split)) return NSA_ERR_INVALID_ARG;
@@ -329,8 +333,8 @@ static nsa_status prefill_impl(const nsa_params* p, const nsa_prefill_args* a, v
     const size_t BTH = (size_t)dm.B * dm.T * dm.Hq;
     const size_t es = esize(dm);
     float* gates = a->gates ? (float*)a->gates : (float*)w.gates;
-    void* kc = a->k_cmp ? a->k_cmp : w.kc;
-    void* vc = a->v_cmp ? a->v_cmp : w.vc;
+    const void* kc = given_cmp ? a->k_cmp_in : (a->k_cmp ? a->k_cmp : w.kc);
+    const void* vc = given_cmp ? a->v_cmp_in : (a->v_cmp ? a->v_cmp : w.vc);
     float* lse = a->lse ? (float*)a->lse : (float*)w.lse;
     int* idx = a->idx ? (int*)a->idx : (int*)w.idx;
     // branch outputs: fp32 when saved for the backward, else I/O type in the workspace
@@ -344,10 +348,22 @@ static nsa_status prefill_impl(const nsa_params* p, const nsa_prefill_args* a, v
         launch_gate_mlp(dm, dm.B * dm.T, a->x, a->w_gate, GateMlp{a->gate_mlp.w1, a->gate_mlp.b1, a->gate_mlp.b2},
                         (float*)w.gh, nullptr, gates, s) != hipSuccess)
       return NSA_ERR_HIP;
-    if (sg.mark() || run_compress(dm, dm.dk, a->k, &a->phi_k, kc, nullptr, w.phi, s) != hipSuccess)
-      return NSA_ERR_HIP;
-    if (sg.mark() || run_compress(dm, dm.dv, a->v, &a->phi_v, vc, w.vct, w.phi, s) != hipSuccess)
-      return NSA_ERR_HIP;
+    if (run_phi) {
+      if (sg.mark() || run_compress(dm, dm.dk, a->k, &a->phi_k, (void*)kc, nullptr, w.phi, s) != hipSuccess)
+        return NSA_ERR_HIP;
+      if (sg.mark() || run_compress(dm, dm.dv, a->v, &a->phi_v, (void*)vc, w.vct, w.phi, s) != hipSuccess)
+        return NSA_ERR_HIP;
+    } else {
+      // the caller's compressed keys and values (or none: no block is
+      // complete): V_cmp^T for the compressed pass, copies for the saved
+      // outputs
+      const size_t kb = (size_t)dm.B * dm.ncmp * dm.Hkv * dm.dk * es, vb = (size_t)dm.B * dm.ncmp * dm.Hkv * dm.dv * es;
+      if (sg.mark() || (a->k_cmp && kb && hipMemcpyAsync(a->k_cmp, kc, kb, hipMemcpyDeviceToDevice, s) != hipSuccess))
+        return NSA_ERR_HIP;
+      if (sg.mark() || (a->v_cmp && vb && hipMemcpyAsync(a->v_cmp, vc, vb, hipMemcpyDeviceToDevice, s) != hipSuccess) ||
+          (vb && launch_transpose_seq(dm, dm.B, dm.ncmp, dm.Hkv, dm.dv, dm.ncmp_pad, vc, w.vct, s) != hipSuccess))
+        return NSA_ERR_HIP;
+    }
     const void* ks = split ? a->k_slc : a->k;
     const void* vs = split ? a->v_slc : a->v;
     const void* kw = split ? a->k_win : a->k;

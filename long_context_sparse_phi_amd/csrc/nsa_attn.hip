@@ -157,6 +157,7 @@ __global__ __launch_bounds__(256, slc_depth<T>() > 2 ? 1 : 2) void k_slc(Dims dm
   // the n block indices of this position, one per lane (n <= 32)
   const int* ids = a.idx + ((size_t)(b * dm.T + t) * dm.Hkv + g) * dm.n;
   const int myid = lane < dm.n ? ids[lane] : -1;
+  const int nrow = wave_sel_row_len(myid, lane, dm.n, t, dm.ls);
   const float sc2 = dm.scale * kLog2e;
   float m = kNegInf, ls = 0.f;
   f32x4 oacc[DV / 16];
@@ -167,14 +168,14 @@ __global__ __launch_bounds__(256, slc_depth<T>() > 2 ? 1 : 2) void k_slc(Dims dm
 
   // first tile of block slot si at or after it, or si = n when none is left
   auto open_block = [&](SlcCursor& c) {
-    for (; c.si < dm.n; ++c.si) {
+    for (; c.si < nrow; ++c.si) {
       const int j = __builtin_amdgcn_readlane(myid, c.si);
-      if (j < 0) { c.si = dm.n; return; }
       c.lo = j * dm.ls;
       c.kt = c.lo & ~31;
       c.kend = min((j + 1) * dm.ls, t + 1);
       if (c.lo < c.kend) return;
     }
+    c.si = dm.n;
   };
   auto advance = [&](SlcCursor& c) {
     c.kt += 32;

@@ -219,9 +219,16 @@ __device__ __forceinline__ void dq_tile(DqState<T, DK, DV>& st, const T* tb, int
     else ds[e] = p * (gc * dp[e >> 2][e & 3] - Dc);
   }
   if (!ROWSUM) {
-    Frag8<T> dsf = to_frag<T>(ds);
+    // dS as a bf16 hi + lo pair: a row of dS sums to zero, so dq = dS K
+    // cancels and a single bf16 rounding of dS would show in it
+    Frag8<T> dsf = to_frag<T>(ds), dslo;
+    if constexpr (sizeof(T) == 2) split_bf16(ds, dsf, dslo);
 #pragma unroll
-    for (int dt = 0; dt < DK / 16; ++dt) mma(st.dq[dt], load_frag(tb + (NKK + NKV + dt) * 512), dsf);
+    for (int dt = 0; dt < DK / 16; ++dt) {
+      const Frag8<T> kf = load_frag(tb + (NKK + NKV + dt) * 512);
+      mma(st.dq[dt], kf, dsf);
+      if constexpr (sizeof(T) == 2) mma(st.dq[dt], kf, dslo);
+    }
   }
 }
 
@@ -281,9 +288,10 @@ __global__ __launch_bounds__(256) void k_bwd_dq(Dims dm, BwdArgs a) {
   // selected branch
   if (BR & 2) {
     const int* ids = a.idx + ((size_t)(b * dm.T + t) * dm.Hkv + g) * dm.n;
-    for (int si = 0; si < dm.n; ++si) {
-      const int j = ids[si];
-      if (j < 0) break;
+    const int myid = lane < dm.n ? ids[lane] : -1;
+    const int nrow = wave_sel_row_len(myid, lane, dm.n, t, dm.ls);
+    for (int si = 0; si < nrow; ++si) {
+      const int j = __builtin_amdgcn_readlane(myid, si);
       const int lo = j * dm.ls, kend = min((j + 1) * dm.ls, t + 1);
       for (int kt = lo & ~31; kt < kend; kt += 32)
         dq_tile<T, DK, DV, ROWSUM>(st, fb + (size_t)(kt / 32) * TI * 512, kt, lo, kend, c16, qd, sc2, lse2[1],
@@ -379,16 +387,17 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq_slc(Dims dm, BwdArgs a) {
   const float Dc = cv ? a.w.Dc[BTH + row] : 0.f;
   const int* ids = a.idx + ((size_t)(b * dm.T + t) * dm.Hkv + g) * dm.n;
   const int myid = lane < dm.n ? ids[lane] : -1;
+  const int nrow = wave_sel_row_len(myid, lane, dm.n, t, dm.ls);
   const T* fb = (const T*)a.w.fkv + (size_t)(b * dm.Hkv + g) * ((dm.T + 31) / 32) * TI * 512 + lane * 8;
   auto open_block = [&](Cur& c) {
-    for (; c.si < dm.n; ++c.si) {
+    for (; c.si < nrow; ++c.si) {
       const int j = __builtin_amdgcn_readlane(myid, c.si);
-      if (j < 0) { c.si = dm.n; return; }
       c.lo = j * dm.ls;
       c.kt = c.lo & ~31;
       c.kend = min((j + 1) * dm.ls, t + 1);
       if (c.lo < c.kend) return;
     }
+    c.si = dm.n;
   };
   auto advance = [&](Cur& c) {
     c.kt += 32;
@@ -419,9 +428,14 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq_slc(Dims dm, BwdArgs a) {
       const float p = v ? fast_exp2(sv[e >> 2][e & 3] * sc2 - lse2) : 0.f;
       ds[e] = p * (gc * dp[e >> 2][e & 3] - Dc);
     }
-    const Frag8<T> dsf = to_frag<T>(ds);
+    // dS as a bf16 hi + lo pair (dq = dS K cancels; see dq_tile)
+    Frag8<T> dsf = to_frag<T>(ds), dslo;
+    if constexpr (sizeof(T) == 2) split_bf16(ds, dsf, dslo);
 #pragma unroll
-    for (int dt = 0; dt < DK / 16; ++dt) mma(dq[dt], tl.f[NKK + NKV + dt], dsf);
+    for (int dt = 0; dt < DK / 16; ++dt) {
+      mma(dq[dt], tl.f[NKK + NKV + dt], dsf);
+      if constexpr (sizeof(T) == 2) mma(dq[dt], tl.f[NKK + NKV + dt], dslo);
+    }
   };
   Tile ring[DEPTH];
   Cur rc[DEPTH];
@@ -580,7 +594,8 @@ __global__ __launch_bounds__(NW * 64, 2) void k_dq_tiled(Dims dm, BwdArgs a) {
             for (int ct = 0; ct < NCT; ++ct) mma(dpa[ct][sub], vf, dof[ct][ks]);
           }
         }
-        Frag8<T> dsf[NCT];
+        // dS as a bf16 hi + lo pair (dq = dS K cancels; see dq_tile)
+        Frag8<T> dsf[NCT], dslo[NCT];
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           float ds[8];
@@ -592,12 +607,16 @@ __global__ __launch_bounds__(NW * 64, 2) void k_dq_tiled(Dims dm, BwdArgs a) {
             ds[e] = pe * (gc[ct][k] * dpa[ct][e >> 2][e & 3] - Dc[ct][k]);
           }
           dsf[ct] = to_frag<T>(ds);
+          if constexpr (sizeof(T) == 2) split_bf16(ds, dsf[ct], dslo[ct]);
         }
 #pragma unroll
         for (int dt = 0; dt < DK / 16; ++dt) {
           const Frag8<T> kt_f = *reinterpret_cast<const Frag8<T>*>(tb + (NKK + NKV + dt) * 512);
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) mma(dq[ct][dt], kt_f, dsf[ct]);
+          for (int ct = 0; ct < NCT; ++ct) {
+            mma(dq[ct][dt], kt_f, dsf[ct]);
+            if constexpr (sizeof(T) == 2) mma(dq[ct][dt], kt_f, dslo[ct]);
+          }
         }
       }
       if (st + 1 < nst) {
@@ -1099,11 +1118,11 @@ __global__ __launch_bounds__(64) void k_rev_hist(Dims dm, BwdArgs a) {
   for (int j = threadIdx.x; j < dm.nsel; j += 64) hist[j] = 0;
   __syncthreads();
   const int t0 = ch * kRevChunk, t1 = min(dm.T, t0 + kRevChunk);
+  const int lane = threadIdx.x;
   for (int t = t0; t < t1; ++t) {
-    if (threadIdx.x < dm.n) {
-      const int j = a.idx[((size_t)(b * dm.T + t) * dm.Hkv + g) * dm.n + threadIdx.x];
-      if (j >= 0) hist[j] += 1;
-    }
+    // only the row's usable prefix counts (distinct, causal blocks)
+    const int j = lane < dm.n ? a.idx[((size_t)(b * dm.T + t) * dm.Hkv + g) * dm.n + lane] : -1;
+    if (lane < wave_sel_row_len(j, lane, dm.n, t, dm.ls)) hist[j] += 1;
     __syncthreads();
   }
   for (int j = threadIdx.x; j < dm.nsel; j += 64)
@@ -1155,11 +1174,10 @@ __global__ __launch_bounds__(64) void k_rev_fill(Dims dm, BwdArgs a) {
   __syncthreads();
   int* list = a.w.list + (size_t)bg * dm.T * dm.n;
   const int t0 = ch * kRevChunk, t1 = min(dm.T, t0 + kRevChunk);
+  const int lane = threadIdx.x;
   for (int t = t0; t < t1; ++t) {
-    if (threadIdx.x < dm.n) {
-      const int j = a.idx[((size_t)(b * dm.T + t) * dm.Hkv + g) * dm.n + threadIdx.x];
-      if (j >= 0) list[cur[j]++] = t;
-    }
+    const int j = lane < dm.n ? a.idx[((size_t)(b * dm.T + t) * dm.Hkv + g) * dm.n + lane] : -1;
+    if (lane < wave_sel_row_len(j, lane, dm.n, t, dm.ls)) list[cur[j]++] = t;
     __syncthreads();
   }
 }

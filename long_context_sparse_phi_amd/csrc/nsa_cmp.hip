@@ -13,12 +13,11 @@
 // log-sum-exp over the visible compressed keys; pass B recomputes the scores,
 // forms exact probabilities, accumulates O_cmp = P V_cmp, remaps P onto
 // selection blocks with one more MFMA (P times the constant 0/1/2 overlap
-// matrix; for bf16 inputs P enters it in fp16, 11 significant bits, which
-// keeps a score's relative error near 1e-5 after the sums), sums over heads
-// with cross-lane adds, keeps each position's score row in LDS and runs the
-// top-n selection there.  Pass B evaluates P scaled by 2^14 (one exponent
-// offset) so that small probabilities stay in fp16's normal range; the scale
-// is removed from O and from the scores when they are stored.
+// matrix; for bf16 inputs P enters it as a bf16 hi + lo pair, about 16
+// significant bits with fp32's exponent range, so a block 80 nats below the
+// row maximum still ranks by its own value), sums over heads with cross-lane
+// adds, keeps each position's score row in LDS and runs the top-n selection
+// there.
 //
 // Layout of the work: a wave owns 16*NCT query columns = (positions x G heads
 // of one KV group); MFMA tiles compute S^T = K Q^T (16 keys x 16 columns) so
@@ -40,8 +39,6 @@ namespace nsa {
 // per workgroup, double-buffered: the next tile's global loads are in flight
 // (in registers) while the current tile is computed from LDS.
 // ---------------------------------------------------------------------------
-constexpr float kPScale2 = 14.f;         // pass B evaluates P * 2^kPScale2
-constexpr float kPScaleInv = 1.f / 16384.f;
 // LDS row stride of the padded (fp32) V^T tile (elements)
 template <int KT>
 constexpr int cmp_vs() { return KT + 8; }
@@ -121,23 +118,22 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
     const bool v = pos[ct] < dm.T;
     nvis[ct] = v ? ncmp_visible(pos[ct], dm.l, dm.d) : 0;
     const size_t row = (size_t)(b * dm.T + min(pos[ct], dm.T - 1)) * dm.Hq + hq[ct];
-    lse2[ct] = (PB && v && nvis[ct] > 0) ? a.lse[row] * kLog2e - kPScale2 : 0.f;
+    lse2[ct] = (PB && v && nvis[ct] > 0) ? a.lse[row] * kLog2e : 0.f;
     const T* qp = q + row * DK + qd * 8;
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) qf[ct][ks] = v ? load_frag(qp + ks * 32) : zero_frag<T>();
   }
-  // remap weights: fp16 operands for bf16 inputs, fp32 for fp32 inputs
-  constexpr bool kF16Remap = sizeof(T) == 2;
+  // remap weights (small integers, exact in bf16); bf16 inputs remap P as a
+  // hi + lo pair
+  constexpr bool kSplitRemap = sizeof(T) == 2;
   Frag8<T> wf[2];
-  f16x8 wh[2];
   if (PB) {
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt) {
       float w[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) w[e] = jt < njt ? remap_weight(qd * 8 + e, jt * 16 + c16, dm.l, dm.d, dm.ls) : 0.f;
-      if constexpr (kF16Remap) wh[jt] = to_f16x8(w);
-      else wf[jt] = to_frag<T>(w);
+      wf[jt] = to_frag<T>(w);
     }
   }
   const float sc2 = dm.scale * kLog2e;
@@ -328,20 +324,14 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
         if (masked) p[e] = kt + qd * 8 + e < nvis[ct] ? p[e] : 0.f;
       }
       pf[ct] = to_frag<T>(p);
-      if constexpr (kPrecisePV<T, OT>) plo_all[ct] = lo_frag(p, pf[ct]);
-      // remap onto selection blocks: P times the overlap weights
-      if constexpr (kF16Remap) {
-        const f16x8 ph = to_f16x8(p);
+      if constexpr (kSplitRemap) plo_all[ct] = lo_frag(p, pf[ct]);
+      // remap onto selection blocks: P (hi + lo) times the overlap weights
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          cr[ct][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (jt < njt) mma(cr[ct][jt], ph, wh[jt]);
-        }
-      } else {
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          cr[ct][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (jt < njt) mma(cr[ct][jt], pf[ct], wf[jt]);
+      for (int jt = 0; jt < 2; ++jt) {
+        cr[ct][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (jt < njt) {
+          mma(cr[ct][jt], pf[ct], wf[jt]);
+          if constexpr (kSplitRemap) mma(cr[ct][jt], plo_all[ct], wf[jt]);
         }
       }
     }
@@ -466,8 +456,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
       OT* op = o + ((size_t)(b * dm.T + pos[ct]) * dm.Hq + hq[ct]) * DV + qd * 4;
 #pragma unroll
       for (int dt = 0; dt < DV / 16; ++dt)
-        store4(op + dt * 16, oacc[dt][ct][0] * kPScaleInv, oacc[dt][ct][1] * kPScaleInv,
-               oacc[dt][ct][2] * kPScaleInv, oacc[dt][ct][3] * kPScaleInv);
+        store4(op + dt * 16, oacc[dt][ct][0], oacc[dt][ct][1], oacc[dt][ct][2], oacc[dt][ct][3]);
     }
     // top-n per position of this wave, two positions at a time
     for (int pl = 0; pl < PW; pl += 2) {
@@ -484,7 +473,7 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
         outs[r] = a.idx + rbase * dm.n;
         if (live && a.p_slc) {
           float* ps = a.p_slc + rbase * dm.nsel;
-          for (int j = lane; j < dm.nsel; j += 64) ps[j] = rows[r][j] * kPScaleInv;
+          for (int j = lane; j < dm.nsel; j += 64) ps[j] = rows[r][j];
         }
       }
       if (dm.nsel <= 1024) {

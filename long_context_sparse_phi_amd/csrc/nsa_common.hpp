@@ -111,17 +111,6 @@ __device__ __forceinline__ void mma(f32x4& c, const Frag8<float>& a, const Frag8
   for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[e], b.hi[e], c, 0, 0, 0);
 }
 
-// fp16 operands (v_mfma_f32_16x16x32_f16, same lane layout as bf16).
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x8v __attribute__((ext_vector_type(8)));
-__device__ __forceinline__ f16x8 to_f16x8(const float* x) {
-  const f32x8v v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
-  return __builtin_convertvector(v, f16x8);
-}
-__device__ __forceinline__ void mma(f32x4& c, const f16x8& a, const f16x8& b) {
-  c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
 // Two fp32 values -> two bf16 (round to nearest even) in one packed convert.
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef float f32x2v __attribute__((ext_vector_type(2)));
@@ -223,6 +212,26 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ int ncmp_visible(int t, int l, int d) {
   int s = t + 1;
   return s < l ? 0 : (s - l) / d + 1;
+}
+
+// Selected-block rows (n entries per position and KV head, ascending, -1
+// padded) are read in order while each entry is above the previous one (the
+// first above -1) and causal (its first token j*ls <= t).  Every kernel that
+// reads a row caller-side (the backward takes the forward's rows back from the
+// caller) applies this rule, so entries after padding, a repeated or
+// descending entry, or a block past t are never used to address memory, and
+// all kernels use the same entries.
+__host__ __device__ __forceinline__ bool sel_slot_ok(int j, int prev, int t, int ls) {
+  return j > prev && j >= 0 && j <= t / ls;
+}
+
+// Length of the usable prefix of a row whose entry si sits in lane si (-1 in
+// lanes si >= n); one wave, every lane gets the same count.
+__device__ __forceinline__ int wave_sel_row_len(int myid, int lane, int n, int t, int ls) {
+  const int prev = __shfl_up(myid, 1);
+  const bool bad = lane < n && !sel_slot_ok(myid, lane == 0 ? -1 : prev, t, ls);
+  const uint64_t stop = __ballot(bad || lane >= n);
+  return stop ? __builtin_ctzll(stop) : 64;
 }
 
 // ---------------------------------------------------------------------------

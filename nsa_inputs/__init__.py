@@ -55,6 +55,7 @@ class Workload:
     gate_std: float = 0.02      # std of the gate projection weights
     gate_hidden: int = 0        # 0: linear gate; else hidden width of a two-layer gate MLP
     q_group_corr: float = 0.0   # correlation between the query heads of one KV group (each stays N(0,1))
+    scale_mult: float = 1.0     # softmax scale = scale_mult / sqrt(d_k)
 
     @property
     def H_q(self) -> int:

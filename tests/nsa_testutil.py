@@ -11,7 +11,8 @@ ATOL, RTOL = 2e-2, 1e-2   # |gpu - oracle| <= ATOL + RTOL * |oracle|
 def oracle_params(w):
     import oracle as O
     return O.Params(l=w.l, d=w.d, l_sel=w.l_sel, n=w.n, w=w.w, phi=w.phi,
-                    io="bf16" if w.dtype == "bf16" else "fp32")
+                    io="bf16" if w.dtype == "bf16" else "fp32",
+                    scale=None if w.scale_mult == 1.0 else w.scale_mult / np.sqrt(w.d_k))
 
 
 def to_dev(d, dev="cuda:0"):
@@ -55,13 +56,15 @@ class SampledRows:
 
 
 # Input recipes whose compressed-branch scores are peaked: the G query heads of
-# a KV group share a component (so they favour the same blocks) and phi's
-# weights are larger than the workloads' 0.02, so compressed keys spread the
-# logits over tens to hundreds of nats.  "extreme" also offsets every
-# selection block's keys and values (std 3), which widens the selected and
-# window branches' logits.
+# a KV group share a component (so they favour the same blocks), phi's weights
+# are somewhat larger than the workloads' 0.02 and the softmax scale is a
+# multiple of 1/sqrt(d_k), so the logits spread over tens to hundreds of nats
+# while keys, values and compressed keys keep magnitudes near 1.  The scale
+# multiplies all three branches' logits, so the selected and window softmaxes
+# are peaked too.  "extreme" also offsets every selection block's keys and
+# values (std 1).
 PEAKED = {
-    "peaked": dict(phi_std=0.15, q_group_corr=0.9, bias_std=0.02),
-    "steep": dict(phi_std=0.20, q_group_corr=0.95, bias_std=0.02),
-    "extreme": dict(phi_std=0.25, q_group_corr=0.95, bias_std=0.02, kv_offset_std=3.0),
+    "peaked": dict(phi_std=0.05, q_group_corr=0.9, scale_mult=8.0, bias_std=0.02),
+    "steep": dict(phi_std=0.05, q_group_corr=0.95, scale_mult=16.0, bias_std=0.02),
+    "extreme": dict(phi_std=0.05, q_group_corr=0.95, scale_mult=24.0, bias_std=0.02, kv_offset_std=1.0),
 }

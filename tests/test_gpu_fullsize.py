@@ -31,30 +31,47 @@ def sample_rows(T, ls, w, seed, n_random=6):
     return np.array(sorted({int(t) for t in base + extra if 0 <= t < T}), dtype=np.int64)
 
 
-def test_prefill_64k_sampled_rows():
+def check_prefill_sampled_rows(w, row_seed=1, seed=0, feed_oracle_cmp=False):
+    """Run the full-size prefill of workload w and compare every compressed key
+    and value, and all outputs of sampled positions, with the oracle, both for
+    the debug launch (every intermediate exported) and for the launch that
+    writes o alone (the configuration the benchmark times).  With
+    feed_oracle_cmp the oracle's compressed keys and values are the GPU's
+    input (phi is not run on the GPU), so that peaked score rows are compared
+    on identical compressed keys.  Returns the fraction of (position, KV head)
+    rows that were near ties."""
     import long_context_sparse_phi_amd as nsa
     import oracle as O
-    w = NI.workload("prefill_64k")
     cfg = nsa.config_from_workload(w)
-    inp = NI.make_prefill_inputs(w, 0)
-    d = to_dev(inp)
-    print(f"[gpu] full-size prefill T={w.T} Hkv={w.H_kv} G={w.G} dk={w.d_k}", flush=True)
-    res = nsa.nsa_fwd_prefill(cfg, d["q"], d["k"], d["v"], d["x"], d["w_gate"], d["phi_k"], d["phi_v"], debug=True)
-    torch.cuda.synchronize()
-    del d
-    rows = sample_rows(w.T, w.l_sel, w.w, seed=1)
-    rt = torch.from_numpy(rows).to("cuda:0")
-    g = {"o": np64(res["o"][:, rt]), "o_branch": np64(res["o_branch"][:, :, rt]), "lse": np64(res["lse"][:, :, rt]),
-         "p_slc": np64(res["p_slc"][:, rt]), "idx": res["idx"][:, rt].cpu().numpy().astype(np.int64),
-         "gates": np64(res["gates"][:, rt]), "k_cmp": np64(res["k_cmp"]), "v_cmp": np64(res["v_cmp"])}
-    del res
-    torch.cuda.empty_cache()
+    inp = NI.make_prefill_inputs(w, seed)
     p = oracle_params(w)
     k = inp["k"].double().numpy()
     v = inp["v"].double().numpy()
     phi_k, phi_v = NI.to_numpy64(inp["phi_k"]), NI.to_numpy64(inp["phi_v"])
     kc = O.compress(k, phi_k, p)
     vc = O.compress(v, phi_v, p)
+    d = to_dev(inp)
+    kv_cmp = None
+    if feed_oracle_cmp:
+        kv_cmp = tuple(torch.from_numpy(x).to(cfg.torch_dtype).contiguous().to("cuda:0") for x in (kc, vc))
+    print(f"[gpu] full-size prefill T={w.T} Hkv={w.H_kv} G={w.G} dk={w.d_k} phi_std={w.phi_std} "
+          f"q_group_corr={w.q_group_corr} oracle_cmp={feed_oracle_cmp}", flush=True)
+    res = nsa.nsa_fwd_prefill(cfg, d["q"], d["k"], d["v"], d["x"], d["w_gate"], d["phi_k"], d["phi_v"], debug=True,
+                              kv_cmp=kv_cmp)
+    torch.cuda.synchronize()
+    rows = sample_rows(w.T, w.l_sel, w.w, seed=row_seed)
+    rt = torch.from_numpy(rows).to("cuda:0")
+    g = {"o": np64(res["o"][:, rt]), "o_branch": np64(res["o_branch"][:, :, rt]), "lse": np64(res["lse"][:, :, rt]),
+         "p_slc": np64(res["p_slc"][:, rt]), "idx": res["idx"][:, rt].cpu().numpy().astype(np.int64),
+         "gates": np64(res["gates"][:, rt]), "k_cmp": np64(res["k_cmp"]), "v_cmp": np64(res["v_cmp"])}
+    del res
+    torch.cuda.empty_cache()
+    # the launch that writes o alone
+    res = nsa.nsa_fwd_prefill(cfg, d["q"], d["k"], d["v"], d["x"], d["w_gate"], d["phi_k"], d["phi_v"], kv_cmp=kv_cmp)
+    torch.cuda.synchronize()
+    g["o_only"] = np64(res["o"][:, rt])
+    del res, d, kv_cmp
+    torch.cuda.empty_cache()
     assert_close(g["k_cmp"], kc, "k_cmp")
     assert_close(g["v_cmp"], vc, "v_cmp")
     ref = O.forward(p, SampledRows(inp["q"][:, rows].double().numpy(), rows, w.T), k, v,
@@ -68,29 +85,51 @@ def test_prefill_64k_sampled_rows():
         assert_close(g["lse"][c], ref["lse"][c], f"lse_{name}")
         assert_close(g["o_branch"][c], ref["o_branch"][c], f"o_{name}")
     assert_close(g["o"], ref["o"], "o")
-    print(f"[gpu] 64K prefill: {len(rows)} rows checked, near ties re-selected: {int(ref['retied'].sum())}")
+    assert_close(g["o_only"], ref["o"], "o (o-only launch)")
+    frac = float(ref["retied"].mean())
+    print(f"[gpu] prefill T={w.T}: {len(rows)} rows checked, near-tie fraction {frac:.3f}", flush=True)
+    return frac
 
 
-def test_decode_64k_sampled_sequences():
+def test_prefill_64k_sampled_rows():
+    check_prefill_sampled_rows(NI.workload("prefill_64k"))
+
+
+def check_decode_sequences(w, seqs, seed=0, feed_oracle_cmp=False):
+    """Full-size decode of workload w: the compressed caches and all outputs of
+    the sequences seqs against the oracle.  The compressed caches are the GPU's
+    own compression of the raw caches, or, with feed_oracle_cmp, the oracle's
+    (then every sequence is compressed on the CPU and seqs must cover them).
+    Returns the near-tie fraction."""
     import long_context_sparse_phi_amd as nsa
     import oracle as O
-    w = NI.workload("decode_64k")
     cfg = nsa.config_from_workload(w)
-    inp = NI.make_decode_inputs(w, 0)
-    d = to_dev(inp)
-    print(f"[gpu] full-size decode B={w.B} S={w.T} Hkv={w.H_kv} G={w.G} dk={w.d_k}", flush=True)
-    kct = nsa.nsa_compress(cfg, d["k_cache"], d["phi_k"], False)
-    vct = nsa.nsa_compress(cfg, d["v_cache"], d["phi_v"], True)
-    res = nsa.nsa_fwd_decode(cfg, d["q"], d["k_cache"], d["v_cache"], kct, vct, d["x"], d["w_gate"], debug=True)
-    torch.cuda.synchronize()
+    inp = NI.make_decode_inputs(w, seed)
     p = oracle_params(w)
     phi_k, phi_v = NI.to_numpy64(inp["phi_k"]), NI.to_numpy64(inp["phi_v"])
-    for b in (0, 13, w.B - 1):
+    ocmp = {}
+    for b in seqs:
+        sl = slice(b, b + 1)
+        ocmp[b] = (O.compress(inp["k_cache"][sl].double().numpy(), phi_k, p),
+                   O.compress(inp["v_cache"][sl].double().numpy(), phi_v, p))
+    d = to_dev(inp)
+    print(f"[gpu] full-size decode B={w.B} S={w.T} Hkv={w.H_kv} G={w.G} dk={w.d_k} phi_std={w.phi_std} "
+          f"q_group_corr={w.q_group_corr} oracle_cmp={feed_oracle_cmp}", flush=True)
+    if feed_oracle_cmp:
+        assert sorted(seqs) == list(range(w.B))
+        kct = torch.cat([torch.from_numpy(ocmp[b][0]) for b in range(w.B)]).to(cfg.torch_dtype).to("cuda:0")
+        vct = torch.cat([torch.from_numpy(ocmp[b][1]) for b in range(w.B)]).to(cfg.torch_dtype).to("cuda:0")
+    else:
+        kct = nsa.nsa_compress(cfg, d["k_cache"], d["phi_k"], False)
+        vct = nsa.nsa_compress(cfg, d["v_cache"], d["phi_v"], True)
+    res = nsa.nsa_fwd_decode(cfg, d["q"], d["k_cache"], d["v_cache"], kct, vct, d["x"], d["w_gate"], debug=True)
+    torch.cuda.synchronize()
+    retied = []
+    for b in seqs:
         sl = slice(b, b + 1)
         kcache = inp["k_cache"][sl].double().numpy()
         vcache = inp["v_cache"][sl].double().numpy()
-        kc = O.compress(kcache, phi_k, p)
-        vc = O.compress(vcache, phi_v, p)
+        kc, vc = ocmp[b]
         assert_close(np64(kct[sl, :kc.shape[1]]), kc, f"k_cmp_cache[{b}]")
         assert_close(np64(vct[sl, :vc.shape[1]]), vc, f"v_cmp_cache[{b}]")
         ref = O.decode(p, inp["q"][sl].double().numpy(), kcache, vcache, kc, vc, inp["x"][sl].double().numpy(),
@@ -102,7 +141,14 @@ def test_decode_64k_sampled_sequences():
             assert_close(np64(res["lse"][c][sl]), ref["lse"][c], f"lse_{name}[{b}]")
             assert_close(np64(res["o_branch"][c][sl]), ref["o_branch"][c], f"o_{name}[{b}]")
         assert_close(np64(res["o"][sl]), ref["o"], f"o[{b}]")
-        print(f"[gpu] 64K decode sequence {b} checked", flush=True)
+        retied.append(ref["retied"])
+        print(f"[gpu] decode S={w.T} sequence {b} checked", flush=True)
+    return float(np.mean(retied))
+
+
+def test_decode_64k_sampled_sequences():
+    w = NI.workload("decode_64k")
+    check_decode_sequences(w, (0, 13, w.B - 1))
 
 
 def test_train_16k_sampled_dq():

@@ -5,12 +5,16 @@ probabilities, remapped to selection blocks and summed over a GQA group's heads
 (youleyou NSA page, 重要性分数计算 and Top-n块选择).  Selection is meant for rows
 on which a few blocks dominate.  The workload recipe (random-init phi weights at
 std 0.02, independent query heads) gives nearly flat rows, so the parity tests
-add recipes in which the heads of a group share a query component and phi's
-weights are larger:
+add recipes in which the heads of a group share a query component and the
+softmax scale is a multiple of 1/sqrt(d_k):
 
-* peaked:  phi std 0.15, head correlation 0.9  (about 70 nats of logit range)
-* steep:   phi std 0.20, head correlation 0.95 (about 130 nats)
-* extreme: phi std 0.25, head correlation 0.95, block offsets of std 3
+* peaked:  softmax scale 8/sqrt(d_k), head correlation 0.9  (about 60 nats of
+  logit range)
+* steep:   scale 16/sqrt(d_k), head correlation 0.95 (about 130 nats)
+* extreme: scale 24/sqrt(d_k), head correlation 0.95, block offsets of std 1
+  (about 200 nats)
+(phi weights at std 0.05 in all three, so compressed keys and values stay
+near 1 in magnitude).
 
 These tests check, without a GPU, that the recipes really reach that regime,
 and that the steep rows tell a score path of full fp32 range apart from one
@@ -34,7 +38,7 @@ def _group_rows(w, rows, seed=0):
     p = oracle_params(w)
     kc = O.compress(a["k"], a["phi_k"], p)
     vc = O.compress(a["v"], a["phi_v"], p)
-    sc = 1.0 / np.sqrt(w.d_k)
+    sc = p.scale
     out = []
     for t in rows:
         nv = O.n_cmp_visible(t, w.l, w.d)
