@@ -62,10 +62,13 @@ typedef enum nsa_status {
   NSA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
   NSA_ERR_HIP = 4,          /* a HIP runtime call failed */
   NSA_ERR_INTERNAL = 5,
-  NSA_ERR_BLAS = 6          /* a rocBLAS call of the projection layer failed
+  NSA_ERR_BLAS = 6,         /* a rocBLAS call of the projection layer failed
                                (a failed rocBLAS call inside the operator,
                                in the gates or phi, is reported as
                                NSA_ERR_HIP) */
+  NSA_ERR_SCRATCH = 7       /* the problem needs more scratch memory than the
+                               library's static per-GPU buffer holds
+                               (nsa_fwd_decode_noalloc) */
 } nsa_status;
 
 typedef enum nsa_dtype { NSA_BF16 = 0, NSA_FP32 = 1 } nsa_dtype;
@@ -337,6 +340,25 @@ nsa_status nsa_fwd_prefill(const nsa_params* p, const nsa_prefill_args* a, void*
                            size_t ws_bytes, void* stream);
 nsa_status nsa_fwd_decode(const nsa_params* p, const nsa_decode_args* a, void* ws,
                           size_t ws_bytes, void* stream);
+
+/* The decode step without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, serving loops and
+ * harnesses that forbid allocation.  Same arguments, kernels and results as
+ * nsa_fwd_decode; the scratch memory those kernels need (per-chunk softmax
+ * states, block scores, selected/window partials) lives in a buffer the
+ * library holds in device memory, NSA_DECODE_STATIC_SCRATCH_BYTES per GPU,
+ * from the first call on that GPU until the process ends.  The call itself
+ * allocates nothing.  A problem whose decode workspace
+ * (nsa_workspace_size(p, NSA_OP_FWD_DECODE, ...)) exceeds that size is
+ * rejected with NSA_ERR_SCRATCH before anything is enqueued (the 64K-token
+ * decode of 32 sequences x 4 KV heads x 16 query heads, d_k = 192, needs
+ * about 53 MB).  Every call on one GPU shares that GPU's buffer: calls that
+ * may overlap on one GPU (different streams, or different host threads)
+ * race and must be ordered by the caller.  Nothing in the buffer needs to
+ * start at any value: every value a call reads was written earlier in the
+ * same call. */
+#define NSA_DECODE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+nsa_status nsa_fwd_decode_noalloc(const nsa_params* p, const nsa_decode_args* a, void* stream);
 nsa_status nsa_bwd(const nsa_params* p, const nsa_bwd_args* a, void* ws,
                    size_t ws_bytes, void* stream);
 nsa_status nsa_dense_fwd(const nsa_params* p, const nsa_dense_args* a, void* ws,

@@ -239,12 +239,16 @@ def nsa_fwd_prefill(cfg: Config, q, k, v, x, w_gate, phi_k=None, phi_v=None, *, 
 
 def nsa_fwd_decode(cfg: Config, q, k_cache, v_cache, k_cmp_cache, v_cmp_cache, x, w_gate, *,
                    out=None, debug: bool = False, seq_lens: Optional[torch.Tensor] = None,
-                   kv_win_cache=None, gate_mlp=None, workspace: Optional[torch.Tensor] = None):
+                   kv_win_cache=None, gate_mlp=None, workspace: Optional[torch.Tensor] = None,
+                   no_alloc: bool = False):
     """One decode step; cfg.T is the cache length S (query at position S-1).
     With seq_lens (int32 [B] on the device), cfg.T is the cache capacity and
     sequence b holds seq_lens[b] tokens, its query at position seq_lens[b]-1.
     kv_win_cache: the window branch's own (k, v) caches when each branch has
-    independent keys and values (k_cache, v_cache then serve the selected one)."""
+    independent keys and values (k_cache, v_cache then serve the selected one).
+    no_alloc: call nsa_fwd_decode_noalloc, which takes no workspace (the
+    library's static per-GPU scratch buffer; calls on one GPU must not
+    overlap)."""
     dev = q.device
     dt = cfg.torch_dtype
     B, S, Hq, Hkv = cfg.B, cfg.T, cfg.H_q, cfg.H_kv
@@ -279,8 +283,13 @@ def nsa_fwd_decode(cfg: Config, q, k_cache, v_cache, k_cmp_cache, v_cmp_cache, x
         _check(kv_win_cache[1], "v_win_cache", (B, S, Hkv, cfg.d_v), dt, dev)
         a.k_win_cache, a.v_win_cache = kv_win_cache[0].data_ptr(), kv_win_cache[1].data_ptr()
     a.gate_mlp = _gate_struct(cfg, gate_mlp, dev)
-    ws = _workspace(cfg, NSA_OP_FWD_DECODE, dev, workspace)
     p = cfg.params()
+    if no_alloc:
+        st = _lib.load().nsa_fwd_decode_noalloc(ctypes.byref(p), ctypes.byref(a), _stream(dev))
+        if st != 0:
+            raise NSAError("nsa_fwd_decode_noalloc", st)
+        return res
+    ws = _workspace(cfg, NSA_OP_FWD_DECODE, dev, workspace)
     st = _lib.load().nsa_fwd_decode(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(), _stream(dev))
     if st != 0:
         raise NSAError("nsa_fwd_decode", st)

@@ -105,7 +105,7 @@ class nsa_layer_bwd_args(ctypes.Structure):
 
 EXPORTS = ("nsa_abi_version", "nsa_status_str", "nsa_workspace_size", "nsa_compress",
            "nsa_fwd_prefill", "nsa_fwd_decode", "nsa_bwd", "nsa_dense_fwd",
-           "nsa_decode_append", "nsa_dense_bwd", "nsa_layer_fwd", "nsa_layer_bwd")
+           "nsa_decode_append", "nsa_dense_bwd", "nsa_layer_fwd", "nsa_layer_bwd", "nsa_fwd_decode_noalloc")
 
 _LIB = None
 
@@ -136,6 +136,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = ctypes.c_int
         fn.argtypes = [P(nsa_params), P(argt), _vp, ctypes.c_size_t, _vp]
+    lib.nsa_fwd_decode_noalloc.restype = ctypes.c_int
+    lib.nsa_fwd_decode_noalloc.argtypes = [P(nsa_params), P(nsa_decode_args), _vp]
     if lib.nsa_abi_version() != ABI_VERSION:
         raise RuntimeError("libnsa.so ABI version mismatch")
     _LIB = lib

@@ -19,6 +19,7 @@ bool cmp_out_fits(const Dims& dm);
 hipError_t launch_decode(const Dims& dm, const nsa_decode_args* a, void* ws, hipStream_t s,
                          void* const* events);
 size_t decode_ws_bytes(const Dims& dm);
+hipError_t decode_static_scratch(void** out);
 hipError_t launch_bwd(const Dims& dm, const nsa_bwd_args* a, void* ws, hipStream_t s, void* const* events);
 size_t bwd_ws_bytes(const Dims& dm);
 size_t dense_bwd_ws_bytes(const Dims& dm);
@@ -252,6 +253,7 @@ const char* nsa_status_str(nsa_status s) {
     case NSA_ERR_HIP: return "HIP runtime error";
     case NSA_ERR_INTERNAL: return "internal error";
     case NSA_ERR_BLAS: return "rocBLAS error";
+    case NSA_ERR_SCRATCH: return "problem larger than the library's static scratch buffer";
   }
   return "unknown status";
 }
@@ -479,8 +481,10 @@ int nsa_prefill_stage_count(void) { return kPrefillStages; }
 int nsa_decode_stage_count(void) { return kDecodeStages; }
 int nsa_bwd_stage_count(void) { return bwd_stage_count(); }
 
+// static_scratch: run in the library's per-GPU static buffer instead of the
+// caller's workspace (ws, ws_bytes unused).
 static nsa_status decode_impl(const nsa_params* p, const nsa_decode_args* a, void* ws, size_t ws_bytes,
-                              void* stream, void* const* events, int n_events) {
+                              void* stream, void* const* events, int n_events, bool static_scratch = false) {
   try {
     Dims dm;
     nsa_status st = make_dims(p, &dm);
@@ -500,8 +504,13 @@ static nsa_status decode_impl(const nsa_params* p, const nsa_decode_args* a, voi
     if (!all_or_none({a->k_win_cache, a->v_win_cache}, &split)) return NSA_ERR_INVALID_ARG;
     if (!gate_ok(dm, a->gate_mlp)) return NSA_ERR_INVALID_ARG;
     const size_t need = decode_ws_bytes(dm);
-    if (ws_bytes < need || !ws || !aligned16(ws)) return NSA_ERR_WORKSPACE;
+    if (static_scratch) {
+      if (need > NSA_DECODE_STATIC_SCRATCH_BYTES) return NSA_ERR_SCRATCH;
+    } else if (ws_bytes < need || !ws || !aligned16(ws)) {
+      return NSA_ERR_WORKSPACE;
+    }
     if ((st = check_device()) != NSA_OK) return st;
+    if (static_scratch && decode_static_scratch(&ws) != hipSuccess) return NSA_ERR_HIP;
     return hip_status(launch_decode(dm, a, ws, (hipStream_t)stream, events));
   } catch (...) {
     return NSA_ERR_INTERNAL;
@@ -511,6 +520,10 @@ static nsa_status decode_impl(const nsa_params* p, const nsa_decode_args* a, voi
 nsa_status nsa_fwd_decode(const nsa_params* p, const nsa_decode_args* a, void* ws, size_t ws_bytes,
                           void* stream) {
   return decode_impl(p, a, ws, ws_bytes, stream, nullptr, 0);
+}
+
+nsa_status nsa_fwd_decode_noalloc(const nsa_params* p, const nsa_decode_args* a, void* stream) {
+  return decode_impl(p, a, nullptr, 0, stream, nullptr, 0, true);
 }
 
 nsa_status nsa_fwd_decode_timed(const nsa_params* p, const nsa_decode_args* a, void* ws, size_t ws_bytes,

@@ -22,6 +22,8 @@
 // request pattern that streams at full rate) into registers, one tile ahead,
 // then writes it to LDS: keys row-major with XOR-swizzled chunks, values
 // transposed ([feature][key]) so both MFMA operands are single 16-byte reads.
+#include <mutex>
+
 #include "../../include/nsa.h"
 #include "nsa_common.hpp"
 #include "nsa_kernels.hpp"
@@ -98,6 +100,33 @@ static size_t dec_carve(const Dims& dm, void* ws, DecBufs* b) {
 size_t decode_ws_bytes(const Dims& dm) {
   DecBufs b;
   return dec_carve(dm, nullptr, &b);
+}
+
+// Scratch of the allocation-free decode entry point: one copy per GPU,
+// created with the code object and held until the process ends.  In host code
+// `scratch` is only a stand-in for the symbol; its device address differs per
+// GPU and comes from hipGetSymbolAddress with that GPU current.
+static __device__ __align__(256) unsigned char scratch[NSA_DECODE_STATIC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device, looked up once per
+// device and kept.
+hipError_t decode_static_scratch(void** out) {
+  static std::mutex mu;
+  static void* addr[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 struct DecArgs {
