@@ -536,8 +536,8 @@ def run_backward(steps, warmup, wname="train_16k"):
 # ---------------------------------------------------------------- projection layer
 
 def run_layer(reps=5, wname="train_16k"):
-    """The projection layer around the operator (q/k/v/o projections as rocBLAS
-    GEMMs, layer width C = gate_dim) at the training shape: layer forward and
+    """The projection layer around the operator (q/k/v/o projections as the
+    library's MFMA GEMMs, layer width C = gate_dim) at the training shape: layer forward and
     backward against the operator's own forward and backward on the same
     projected inputs, so that the difference is the projections' cost."""
     import torch

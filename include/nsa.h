@@ -21,11 +21,10 @@
  * Conventions shared by every entry point
  * - All tensor pointers are device pointers owned by the caller.  Extra
  *   device memory the kernels need is the caller's workspace of
- *   nsa_workspace_size() bytes.  The library allocates nothing itself, with
- *   one exception: the first call on a device that runs a rocBLAS GEMM (the
- *   gate projection and the MLP form of phi in the forward and the backward,
- *   the projection layer) creates that device's rocBLAS handle, which keeps
- *   a workspace of its own until the process ends.
+ *   nsa_workspace_size() bytes.  The library allocates nothing itself; every
+ *   kernel, the GEMMs included, is the library's own HIP code (no BLAS
+ *   library is called).  The one buffer it holds is the static scratch of
+ *   nsa_fwd_decode_noalloc (below), part of the library's code object.
  * - Tensors are dense, row-major, in the order their shapes are written.
  *   Query head h belongs to KV head h / group_size.
  * - io_dtype (NSA_BF16 or NSA_FP32) is the element type of every input and
@@ -40,8 +39,10 @@
  *   then undefined.  No C++ exception crosses this interface.
  * - Every pointer must be 16-byte aligned.
  * - The device is the caller's current HIP device; it must be gfx950.
- * - No global mutable state: calls on different streams may run
- *   concurrently as long as their buffers do not overlap.
+ * - Calls on different streams may run concurrently as long as their
+ *   buffers do not overlap (nsa_fwd_decode_noalloc excepted, below).  The
+ *   only process-wide state is read-only once set: per device, whether it is
+ *   a gfx950 and the address of the static scratch buffer.
  */
 #ifndef NSA_H_
 #define NSA_H_
@@ -62,10 +63,7 @@ typedef enum nsa_status {
   NSA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
   NSA_ERR_HIP = 4,          /* a HIP runtime call failed */
   NSA_ERR_INTERNAL = 5,
-  NSA_ERR_BLAS = 6,         /* a rocBLAS call of the projection layer failed
-                               (a failed rocBLAS call inside the operator,
-                               in the gates or phi, is reported as
-                               NSA_ERR_HIP) */
+  /* 6 is not used */
   NSA_ERR_SCRATCH = 7       /* the problem needs more scratch memory than the
                                library's static per-GPU buffer holds
                                (nsa_fwd_decode_noalloc) */
@@ -290,7 +288,9 @@ typedef struct nsa_dense_bwd_args {
  *   o [B,T,Hq,dv] (io_dtype, required: the backward reads them);
  *   k_cmp, v_cmp, lse, idx, o_branch as nsa_fwd_prefill's (optional; the
  *   backward needs k_cmp, v_cmp, lse and idx).
- * The projections run as rocBLAS GEMMs with fp32 accumulation on the stream.
+ * The projections run as the library's bf16 MFMA GEMMs (fp32 accumulation;
+ * fp32 I/O: fp32 MFMA) on the stream; with bf16 I/O the width C must be a
+ * multiple of 8 (else NSA_ERR_UNSUPPORTED).
  * Workspace: NSA_OP_LAYER_FWD. */
 typedef struct nsa_layer_args {
   const void *h, *w_q, *w_k, *w_v, *w_o, *w_gate;

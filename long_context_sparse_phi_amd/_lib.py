@@ -11,8 +11,9 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libnsa.so")
 
-(NSA_OK, NSA_ERR_INVALID_ARG, NSA_ERR_UNSUPPORTED, NSA_ERR_WORKSPACE, NSA_ERR_HIP, NSA_ERR_INTERNAL,
- NSA_ERR_BLAS) = range(7)
+(NSA_OK, NSA_ERR_INVALID_ARG, NSA_ERR_UNSUPPORTED, NSA_ERR_WORKSPACE, NSA_ERR_HIP,
+ NSA_ERR_INTERNAL) = range(6)
+NSA_ERR_SCRATCH = 7
 NSA_BF16, NSA_FP32 = 0, 1
 NSA_PHI_MEANPOOL, NSA_PHI_MLP = 0, 1
 (NSA_OP_FWD_PREFILL, NSA_OP_FWD_DECODE, NSA_OP_BWD, NSA_OP_COMPRESS, NSA_OP_DENSE, NSA_OP_APPEND,

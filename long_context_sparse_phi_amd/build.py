@@ -32,7 +32,7 @@ FLAGS = [
     "-Wno-unused-result", "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"),
 ]
-SOURCES = ["nsa_api.cpp", "nsa_blas.cpp", "nsa_phi.hip", "nsa_cmp.hip", "nsa_attn.hip", "nsa_decode.hip", "nsa_bwd.hip",
+SOURCES = ["nsa_api.cpp", "nsa_gemm.hip", "nsa_phi.hip", "nsa_cmp.hip", "nsa_attn.hip", "nsa_decode.hip", "nsa_bwd.hip",
            "nsa_append.hip"]
 
 
@@ -57,9 +57,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = OUT + ".tmp"
-    # rocBLAS serves the plain GEMMs of the projection layer
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-L/opt/rocm/lib", "-lrocblas",
-           "-Wl,-rpath,/opt/rocm/lib", "-o", tmp]
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr[-8000:]}")

@@ -154,7 +154,7 @@ hipError_t run_compress(const Dims& dm, int D, const void* x, const nsa_phi_weig
   const int nsub = dm.ncmp > 0 ? dm.ncmp + R - 1 : 0;
   a.arows = c.take(((size_t)dm.B * dm.Hkv * nsub + R) * dm.d * D * es);
   a.w2t = c.take((size_t)D * dm.hidden * es);
-  a.cvec = (float*)c.take((size_t)dm.hidden * 4);
+  a.pe_part = (float*)c.take(phi_pe_part_floats(dm) * 4);
   a.y = (float*)c.take(((size_t)dm.B * dm.Hkv * nsub + R) * R * dm.hidden * 4);
   a.h = c.take((size_t)dm.B * dm.Hkv * dm.ncmp * dm.hidden * 4);
   a.out = out; a.outT = outT;
@@ -202,18 +202,17 @@ bool phi_ok(const nsa_phi_weights& w) {
 }
 
 // ---------------------------------------------------------------------------
-// Projection layer: rocBLAS GEMMs around the operator.
+// Projection layer: hand-written GEMMs (nsa_gemm.hip) around the operator.
 // ---------------------------------------------------------------------------
 
-// rocBLAS status of a layer GEMM as an API status
-nsa_status blas_status(int r) { return r == 0 ? NSA_OK : (r == 1 ? NSA_ERR_BLAS : NSA_ERR_HIP); }
+// split-K bound of the layer's weight-gradient GEMMs (sums over every token)
+constexpr int kLayerSplit = 8;
 
 struct LayerBwdWs {
   void* op_ws;    // the operator's backward workspace
   void* d_o;      // dO = dy w_o^T, io dtype [B*T, Hq*dv]
   float *dq, *dk, *dv;
-  float* h32;     // the layer input in fp32 (bf16 I/O only)
-  float* w32;     // one projection weight in fp32 at a time
+  float* part;    // split-K partials of the weight gradients
 };
 
 size_t plan_layer_bwd(const Dims& dm, void* ws, LayerBwdWs* w) {
@@ -226,11 +225,24 @@ size_t plan_layer_bwd(const Dims& dm, void* ws, LayerBwdWs* w) {
   w->dq = (float*)c.take(ntok * dm.Hq * dm.dk * 4);
   w->dk = (float*)c.take(ntok * dm.Hkv * dm.dk * 4);
   w->dv = (float*)c.take(ntok * dm.Hkv * dm.dv * 4);
-  w->h32 = dm.io == IO_BF16 ? (float*)c.take(ntok * dm.C * 4) : nullptr;
-  const size_t wmax = (size_t)dm.C * (dm.Hq * dm.dk > dm.Hkv * dm.dv ? dm.Hq * dm.dk : dm.Hkv * dm.dv);
-  w->w32 = dm.io == IO_BF16 ? (float*)c.take(wmax * 4) : nullptr;
+  const size_t wmax = (size_t)dm.C * (dm.Hq * dm.dk > dm.Hq * dm.dv ? dm.Hq * dm.dk : dm.Hq * dm.dv);
+  w->part = (float*)c.take(wmax * (dm.io == IO_BF16 ? kLayerSplit : kGemmMaxSplit) * 4);
   return c.off;
 }
+
+// One layer GEMM: C = A B (+ C), bf16 MFMA for bf16 I/O (fp32 operands as
+// hi + lo parts), exact fp32 MFMA for fp32 I/O.  a_f32 / b_f32: the operand is
+// fp32 whatever the I/O type.  split: the sum runs over many tokens.
+hipError_t layer_gemm(const Dims& dm, const MmArgs& g, bool a_f32, bool b_f32, bool split, float* part,
+                      hipStream_t s) {
+  if (dm.io == IO_BF16) return mm(g, a_f32, b_f32, split ? mm_split(g, kLayerSplit) : 1, part, s);
+  const Gemm e{g.M, g.N, g.K, g.A, g.sam, g.sak, g.B, g.sbk, g.sbn, (float*)g.C, g.ldc, g.accumulate};
+  return gemm_exact(e, true, true, split ? part : nullptr, s);
+}
+
+// The layer's GEMMs take 16-byte rows: with bf16 I/O the width C must be a
+// multiple of 8 (the head widths always are).
+bool layer_shapes_ok(const Dims& dm) { return dm.io != IO_BF16 || dm.C % 8 == 0; }
 
 bool layer_weights_ok(const void* const* ps, int n) {
   for (int i = 0; i < n; ++i)
@@ -252,7 +264,6 @@ const char* nsa_status_str(nsa_status s) {
     case NSA_ERR_WORKSPACE: return "workspace missing or too small";
     case NSA_ERR_HIP: return "HIP runtime error";
     case NSA_ERR_INTERNAL: return "internal error";
-    case NSA_ERR_BLAS: return "rocBLAS error";
     case NSA_ERR_SCRATCH: return "problem larger than the library's static scratch buffer";
   }
   return "unknown status";
@@ -596,19 +607,22 @@ nsa_status nsa_layer_fwd(const nsa_params* p, const nsa_layer_args* a, void* ws,
     pa.k_cmp = a->k_cmp; pa.v_cmp = a->v_cmp; pa.lse = a->lse; pa.idx = a->idx; pa.o_branch = a->o_branch;
     pa.gate_mlp = a->gate_mlp;
     if ((st = prefill_impl(p, &pa, ws, ws_bytes, stream, nullptr, 0, true)) != NSA_OK) return st;
-    const BlasType T = dm.io == IO_BF16 ? kBlasBF16 : kBlasF32;
-    const int ntok = dm.B * dm.T, C = dm.C;
+    if (!layer_shapes_ok(dm)) return NSA_ERR_UNSUPPORTED;
+    const int ntok = dm.B * dm.T, C = dm.C, bo = dm.io == IO_BF16;
     const int nq = dm.Hq * dm.dk, nk = dm.Hkv * dm.dk, nv = dm.Hkv * dm.dv, no = dm.Hq * dm.dv;
     hipStream_t s = (hipStream_t)stream;
-    if ((st = blas_status(blas_gemm(s, false, false, ntok, nq, C, a->h, T, C, a->w_q, T, nq, 0.f, a->q, T, nq))) !=
-            NSA_OK ||
-        (st = blas_status(blas_gemm(s, false, false, ntok, nk, C, a->h, T, C, a->w_k, T, nk, 0.f, a->k, T, nk))) !=
-            NSA_OK ||
-        (st = blas_status(blas_gemm(s, false, false, ntok, nv, C, a->h, T, C, a->w_v, T, nv, 0.f, a->v, T, nv))) !=
-            NSA_OK)
-      return st;
+    // q = h w_q, k = h w_k, v = h w_v (outputs in the I/O type)
+    const MmArgs gq{ntok, nq, C, a->h, C, 1, a->w_q, nq, 1, a->q, nq, 0, bo};
+    const MmArgs gk{ntok, nk, C, a->h, C, 1, a->w_k, nk, 1, a->k, nk, 0, bo};
+    const MmArgs gv{ntok, nv, C, a->h, C, 1, a->w_v, nv, 1, a->v, nv, 0, bo};
+    if (layer_gemm(dm, gq, false, false, false, nullptr, s) != hipSuccess ||
+        layer_gemm(dm, gk, false, false, false, nullptr, s) != hipSuccess ||
+        layer_gemm(dm, gv, false, false, false, nullptr, s) != hipSuccess)
+      return NSA_ERR_HIP;
     if ((st = prefill_impl(p, &pa, ws, ws_bytes, stream, nullptr, 0)) != NSA_OK) return st;
-    return blas_status(blas_gemm(s, false, false, ntok, C, no, a->o, T, no, a->w_o, T, C, 0.f, a->y, T, C));
+    // y = o w_o
+    const MmArgs gy{ntok, C, no, a->o, no, 1, a->w_o, C, 1, a->y, C, 0, bo};
+    return hip_status(layer_gemm(dm, gy, false, false, false, nullptr, s));
   } catch (...) {
     return NSA_ERR_INTERNAL;
   }
@@ -637,40 +651,27 @@ nsa_status nsa_layer_bwd(const nsa_params* p, const nsa_layer_bwd_args* a, void*
     ba.gate_mlp = a->gate_mlp; ba.d_gate_mlp = a->d_gate_mlp; ba.dx = a->dh;
     const size_t op_bytes = bwd_ws_bytes(dm);
     if ((st = bwd_impl(p, &ba, w.op_ws, op_bytes, stream, nullptr, 0, true)) != NSA_OK) return st;
-    const bool bf = dm.io == IO_BF16;
-    const BlasType T = bf ? kBlasBF16 : kBlasF32;
-    const BlasType F = kBlasF32;
-    const int ntok = dm.B * dm.T, C = dm.C;
+    if (!layer_shapes_ok(dm)) return NSA_ERR_UNSUPPORTED;
+    const int ntok = dm.B * dm.T, C = dm.C, bo = dm.io == IO_BF16;
     const int nq = dm.Hq * dm.dk, nk = dm.Hkv * dm.dk, nv = dm.Hkv * dm.dv, no = dm.Hq * dm.dv;
     hipStream_t s = (hipStream_t)stream;
-    {
-      // dO = dy w_o^T (io dtype), dW_o = o^T dy
-      if ((st = blas_status(blas_gemm(s, false, true, ntok, no, C, a->dy, T, C, a->w_o, T, C, 0.f, w.d_o, T, no))) !=
-              NSA_OK ||
-          (st = blas_status(blas_gemm(s, true, false, no, C, ntok, a->o, T, no, a->dy, T, C, 0.f, a->dw_o, F, C))) !=
-              NSA_OK)
-        return st;
-    }
+    // dO = dy w_o^T (I/O type), dW_o = o^T dy (fp32)
+    const MmArgs gdo{ntok, no, C, a->dy, C, 1, a->w_o, 1, C, w.d_o, no, 0, bo};
+    const MmArgs gwo{no, C, ntok, a->o, 1, no, a->dy, C, 1, a->dw_o, C, 0, 0};
+    if (layer_gemm(dm, gdo, false, false, false, nullptr, s) != hipSuccess ||
+        layer_gemm(dm, gwo, false, false, true, w.part, s) != hipSuccess)
+      return NSA_ERR_HIP;
     // the operator's backward; its dx (the gate path) initialises dh
     if ((st = bwd_impl(p, &ba, w.op_ws, op_bytes, stream, nullptr, 0)) != NSA_OK) return st;
-    const float* h32 = (const float*)a->h;
-    if (bf && launch_to_f32(a->h, (size_t)ntok * C, w.h32, s) != hipSuccess) return NSA_ERR_HIP;
-    if (bf) h32 = w.h32;
     struct Proj { const void* w; const float* d; int n; void* dw; };
     const Proj pr[3] = {{a->w_q, w.dq, nq, a->dw_q}, {a->w_k, w.dk, nk, a->dw_k}, {a->w_v, w.dv, nv, a->dw_v}};
     for (const Proj& j : pr) {
-      // dW = h^T d; dh += d W^T (fp32 operands; the weight is widened first)
-      if ((st = blas_status(blas_gemm(s, true, false, C, j.n, ntok, h32, F, C, j.d, F, j.n, 0.f, j.dw, F, j.n))) !=
-          NSA_OK)
-        return st;
-      const float* w32 = (const float*)j.w;
-      if (bf) {
-        if (launch_to_f32(j.w, (size_t)C * j.n, w.w32, s) != hipSuccess) return NSA_ERR_HIP;
-        w32 = w.w32;
-      }
-      if ((st = blas_status(blas_gemm(s, false, true, ntok, C, j.n, j.d, F, j.n, w32, F, j.n, 1.f, a->dh, F, C))) !=
-          NSA_OK)
-        return st;
+      // dW = h^T d (fp32); dh += d W^T (d is fp32)
+      const MmArgs gw{C, j.n, ntok, a->h, 1, C, j.d, j.n, 1, j.dw, j.n, 0, 0};
+      const MmArgs gh{ntok, C, j.n, j.d, j.n, 1, j.w, 1, j.n, a->dh, C, 1, 0};
+      if (layer_gemm(dm, gw, false, true, true, w.part, s) != hipSuccess ||
+          layer_gemm(dm, gh, true, false, false, nullptr, s) != hipSuccess)
+        return NSA_ERR_HIP;
     }
     return NSA_OK;
   } catch (...) {

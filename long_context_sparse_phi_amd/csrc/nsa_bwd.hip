@@ -23,10 +23,10 @@
 //     segments whose partial sums are added in a fixed order afterwards.
 //   * The reverse index (positions that selected each block, ascending) is
 //     built by a per-chunk histogram, a scan and an ordered fill.
-//   * phi's first layer: recomputed through rocBLAS; its weight and token
-//     gradients are rocBLAS GEMMs over the sub-block rows (da shifted into
-//     the same row layout, see phi_bwd).  phi's second layer and the gate
-//     projection go through a strided fp32 MFMA GEMM.
+//   * phi's first layer: recomputed with the bf16 MFMA GEMM; its weight and
+//     token gradients are the same GEMM over the sub-block rows (da shifted
+//     into the same row layout, see phi_bwd).  phi's second layer and the
+//     gate projection go through the strided fp32 MFMA GEMM.
 #include <type_traits>
 
 #include "../../include/nsa.h"
@@ -41,6 +41,7 @@ constexpr int kSegCmp = 512;     // query positions per compressed-key segment
 constexpr int kSegSlc = 512;     // list entries per selected-block segment
 constexpr int kRevChunk = 256;   // positions per reverse-index chunk
 constexpr int kMaxSplit = 64;    // split-K factor bound of the reduction GEMMs
+constexpr int kW1Split = 16;     // split-K factor bound of phi's dW1 GEMM (bf16 I/O)
 
 struct BwdPlan {
   int nkg_cmp;     // 64-key groups of the compressed keys
@@ -92,9 +93,9 @@ struct BwdBufs {
   float* act;      // [rows,H] pre-activation (rows = B*Hkv*ncmp compressed keys)
   float* hid;      // [rows,H] gelu(act)
   float* dh;       // [rows,H]
-  void* dap;       // [B*Hkv*nsub + l/d - 1, H] dh * gelu'(act) in the sub-block row layout:
-                   // bf16 I/O a hi plane then a lo plane, fp32 I/O one fp32 plane
+  float* dap;      // [B*Hkv*nsub + l/d - 1, H] dh * gelu'(act) in the sub-block row layout
   float* dxs;      // [B*Hkv*nsub, d*D] token gradient of phi per sub-block
+  float* pe_part;  // position-embedding rows' partial sums (launch_phi_gemm1)
 };
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -137,7 +138,9 @@ static size_t bwd_carve(const Dims& dm, void* ws, BwdBufs* w) {
     mn = mn > (size_t)dm.l * Dm ? mn : (size_t)dm.l * Dm;
     mn = mn > (size_t)dm.Cg * 3 * dm.Hq ? mn : (size_t)dm.Cg * 3 * dm.Hq;
     mn = mn > (size_t)dm.C * dm.Cg ? mn : (size_t)dm.C * dm.Cg;
-    w->gpart = (float*)take(kMaxSplit * mn * 4);
+    // phi's dW1 chunks (d*D x hidden), split over the sub-block rows
+    const size_t w1 = (size_t)dm.d * Dm * dm.hidden * (dm.io == IO_BF16 ? kW1Split : kGemmMaxSplit);
+    w->gpart = (float*)take((kMaxSplit * mn > w1 ? kMaxSplit * mn : w1) * 4);
   }
   if (dm.hidden) {
     const int D = dm.dk > dm.dv ? dm.dk : dm.dv;
@@ -147,10 +150,11 @@ static size_t bwd_carve(const Dims& dm, void* ws, BwdBufs* w) {
     w->arows = take((BG * nsub + R) * dm.d * D * es);
     w->w2t = take((size_t)D * dm.hidden * es);
     w->y = (float*)take((BG * nsub + R) * R * dm.hidden * 4);
+    w->pe_part = (float*)take(phi_pe_part_floats(dm) * 4);
     w->act = (float*)take(rows * dm.hidden * 4);
     w->hid = (float*)take(rows * dm.hidden * 4);
     w->dh = (float*)take(rows * dm.hidden * 4);
-    w->dap = take((nsub ? BG * nsub + R - 1 : 0) * dm.hidden * 4);
+    w->dap = (float*)take((nsub ? BG * nsub + R - 1 : 0) * dm.hidden * 4);
     w->dxs = (float*)take(BG * nsub * dm.d * D * 4);
   }
   return off;
@@ -1186,99 +1190,6 @@ __global__ __launch_bounds__(64) void k_rev_fill(Dims dm, BwdArgs a) {
 // Strided fp32 GEMM on MFMA: C[m,n] (+)= sum_k A[m*sam + k*sak] * B[k*sbk + n*sbn].
 // 64x64 output tile per workgroup, k steps of 32 staged through LDS.
 // ---------------------------------------------------------------------------
-struct Gemm {
-  int M, N, K;
-  const void* A; long long sam, sak;
-  const void* B; long long sbk, sbn;
-  float* C; long long ldc;
-  int accumulate;
-};
-
-// blockIdx.z = split index: k range [z*kc, (z+1)*kc); with a split the result
-// goes to part[z][M][N] and is summed afterwards in split order.
-template <typename TA, typename TB>
-__global__ __launch_bounds__(256) void k_gemm(Gemm gm, int kc, float* part) {
-  __shared__ float As[32][64 + 4];
-  __shared__ float Bs[32][64 + 4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c16 = lane & 15, kq = lane >> 4;
-  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
-  const int kbeg = blockIdx.z * kc, kend = min(gm.K, kbeg + kc);
-  const TA* A = (const TA*)gm.A;
-  const TB* B = (const TB*)gm.B;
-  f32x4 acc[2][2];
-  for (int i = 0; i < 2; ++i)
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const bool a_k_fast = gm.sak == 1, b_n_fast = gm.sbn == 1;
-  for (int k0 = kbeg; k0 < kend; k0 += 32) {
-    for (int i = tid; i < 64 * 32; i += 256) {
-      int mm, kk;
-      if (a_k_fast) { kk = i & 31; mm = i >> 5; } else { mm = i & 63; kk = i >> 6; }
-      const int m = m0 + mm, k = k0 + kk;
-      As[kk][mm] = (m < gm.M && k < kend) ? to_f32(A[m * gm.sam + k * gm.sak]) : 0.f;
-      int nn, kb;
-      if (b_n_fast) { nn = i & 63; kb = i >> 6; } else { kb = i & 31; nn = i >> 5; }
-      const int n = n0 + nn, k2 = k0 + kb;
-      Bs[kb][nn] = (n < gm.N && k2 < kend) ? to_f32(B[k2 * gm.sbk + n * gm.sbn]) : 0.f;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 32; kk += 4) {
-      float af[2], bfv[2];
-      for (int i = 0; i < 2; ++i) af[i] = As[kk + kq][(wave >> 1) * 32 + i * 16 + c16];
-      for (int j = 0; j < 2; ++j) bfv[j] = Bs[kk + kq][(wave & 1) * 32 + j * 16 + c16];
-      for (int i = 0; i < 2; ++i)
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[i], bfv[j], acc[i][j], 0, 0, 0);
-    }
-    __syncthreads();
-  }
-  for (int i = 0; i < 2; ++i)
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + (wave & 1) * 32 + j * 16 + c16;
-      if (n >= gm.N) continue;
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + (wave >> 1) * 32 + i * 16 + kq * 4 + r;
-        if (m >= gm.M) continue;
-        if (part) {
-          part[((size_t)blockIdx.z * gm.M + m) * gm.N + n] = acc[i][j][r];
-        } else {
-          float* cp = gm.C + (long long)m * gm.ldc + n;
-          *cp = gm.accumulate ? *cp + acc[i][j][r] : acc[i][j][r];
-        }
-      }
-    }
-}
-
-__global__ __launch_bounds__(256) void k_gemm_reduce(Gemm gm, int nsplit, const float* __restrict__ part) {
-  const size_t id = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (id >= (size_t)gm.M * gm.N) return;
-  const int m = id / gm.N, n = id % gm.N;
-  float s = 0.f;
-  for (int z = 0; z < nsplit; ++z) s += part[(size_t)z * gm.M * gm.N + id];
-  float* cp = gm.C + (long long)m * gm.ldc + n;
-  *cp = gm.accumulate ? *cp + s : s;
-}
-
-// Splits K so that about 512 workgroups run; partials need nsplit*M*N floats of part.
-template <typename TA, typename TB>
-static hipError_t gemm(const Gemm& g, float* part, hipStream_t s) {
-  if (g.M <= 0 || g.N <= 0) return hipSuccess;
-  const int tiles = ((g.N + 63) / 64) * ((g.M + 63) / 64);
-  int nsplit = part ? (512 + tiles - 1) / tiles : 1;
-  nsplit = min(nsplit, min(kMaxSplit, max(1, g.K / 256)));
-  const int kc = ((g.K + nsplit - 1) / nsplit + 31) & ~31;
-  nsplit = (g.K + kc - 1) / kc;
-  dim3 grid((g.N + 63) / 64, (g.M + 63) / 64, nsplit);
-  if (nsplit == 1) {
-    k_gemm<TA, TB><<<grid, 256, 0, s>>>(g, kc, nullptr);
-    return hipGetLastError();
-  }
-  k_gemm<TA, TB><<<grid, 256, 0, s>>>(g, kc, part);
-  const size_t mn = (size_t)g.M * g.N;
-  k_gemm_reduce<<<(unsigned)((mn + 255) / 256), 256, 0, s>>>(g, nsplit, part);
-  return hipGetLastError();
-}
-
 // Column sums out[c] = sum_r in[r*ld + c] in two stages with a fixed order:
 // row split z sums rows z, z + nsplit, ...; then the splits are added in order.
 __global__ __launch_bounds__(256) void k_colsum_part(int R, int Cn, long long ld, int nsplit,
@@ -1345,13 +1256,11 @@ __global__ __launch_bounds__(256) void k_phi_dact(size_t n, const float* __restr
 // and rows bg*nsub .. bg*nsub + R-2 (and R-1 rows past the last head) hold
 // zeros.  Key i reads sub-blocks i .. i+R-1, one per W1 chunk r, so the rows
 // that pair with sub-block row m under chunk r are this layout shifted by
-// R-1-r rows, for every head at once.  bf16 I/O splits da into a bf16 hi part
-// and the bf16 rounding of the remainder (hi + lo carries ~16 mantissa bits),
-// so the GEMMs run on bf16 operands at close to fp32 accuracy.  dh is
-// overwritten with da (its column sum is db1).
-template <typename T>
-__global__ __launch_bounds__(256) void k_phi_da_split(Dims dm, int nsub, const float* __restrict__ act,
-                                                      float* __restrict__ dh, T* __restrict__ dap) {
+// R-1-r rows, for every head at once.  da is kept in fp32; with bf16 I/O the
+// GEMMs take it as a bf16 hi part plus the bf16 rounding of the remainder
+// (~16 mantissa bits).  dh is overwritten with da (its column sum is db1).
+__global__ __launch_bounds__(256) void k_phi_da(Dims dm, int nsub, const float* __restrict__ act,
+                                                float* __restrict__ dh, float* __restrict__ dap) {
   const int H = dm.hidden, R = dm.l / dm.d;
   const size_t BG = (size_t)dm.B * dm.Hkv, rows_p = BG * nsub + R - 1;
   const size_t id = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -1369,13 +1278,7 @@ __global__ __launch_bounds__(256) void k_phi_da_split(Dims dm, int nsub, const f
     v = dh[k] * (cdf + x * pdf);
     dh[k] = v;
   }
-  if constexpr (sizeof(T) == 2) {
-    const T hi = from_f32<T>(v);
-    dap[id] = hi;
-    dap[rows_p * H + id] = from_f32<T>(v - to_f32(hi));
-  } else {
-    dap[id] = v;
-  }
+  dap[id] = v;
 }
 
 // Position-embedding part of dW1: every compressed key adds pe to its sub-block
@@ -1443,36 +1346,41 @@ static hipError_t phi_bwd(const Dims& dm, const BwdArgs& a, const nsa_phi_weight
   const int H = dm.hidden, R = dm.l / dm.d;
   const int nsub = dm.ncmp + R - 1;
   // recompute the forward pre-activations
-  if ((e = launch_phi_gemm1(dm, D, nsub, xsrc, w.pe, w.w1, a.w.arows, a.w.y, s)) != hipSuccess) return e;
+  if ((e = launch_phi_gemm1(dm, D, nsub, xsrc, w.pe, w.w1, a.w.arows, a.w.y, a.w.pe_part, s)) != hipSuccess)
+    return e;
   k_phi_act<T><<<(unsigned)((rows * H + 255) / 256), 256, 0, s>>>(dm, a.w.y, (const T*)w.b1, a.w.act, a.w.hid);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // db2 = colsum(dout); dW2 = hid^T dout
   if ((e = colsum((int)rows, D, D, dcmp, (float*)gr.b2, a.w.gpart, s)) != hipSuccess) return e;
   {
     Gemm g{H, D, (int)rows, a.w.hid, 1, H, dcmp, D, 1, (float*)gr.w2, D, 0};
-    if ((e = gemm<float, float>(g, a.w.gpart, s)) != hipSuccess) return e;
+    if ((e = gemm_exact(g, true, true, a.w.gpart, s)) != hipSuccess) return e;
   }
   // dh = dout W2^T; da = dh * gelu'(act)
   {
     Gemm g{(int)rows, H, D, dcmp, D, 1, w.w2, 1, D, a.w.dh, H, 0};
-    if ((e = gemm<float, T>(g, nullptr, s)) != hipSuccess) return e;
+    if ((e = gemm_exact(g, true, sizeof(T) == 4, nullptr, s)) != hipSuccess) return e;
   }
   const size_t Mmain = (size_t)dm.B * dm.Hkv * nsub, rows_p = Mmain + R - 1;
-  k_phi_da_split<T><<<(unsigned)((rows_p * H + 255) / 256), 256, 0, s>>>(dm, nsub, a.w.act, a.w.dh, (T*)a.w.dap);
+  k_phi_da<<<(unsigned)((rows_p * H + 255) / 256), 256, 0, s>>>(dm, nsub, a.w.act, a.w.dh, a.w.dap);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = colsum((int)rows, H, H, a.w.dh, (float*)gr.b1, a.w.gpart, s)) != hipSuccess) return e;
   const bool bf = sizeof(T) == 2;
-  const BlasType t = bf ? kBlasBF16 : kBlasF32;
-  const int planes = bf ? 2 : 1, dD = dm.d * D;
-  auto da_rows = [&](int pl, int shift) {
-    return (const char*)a.w.dap + ((size_t)pl * rows_p + shift) * H * sizeof(T);
-  };
-  // dW1 chunk r = (sub-block rows)^T (da shifted by R-1-r), plus the pe part
-  for (int r = 0; r < R; ++r)
-    for (int pl = 0; pl < planes; ++pl)
-      if (blas_gemm(s, true, false, dD, H, (int)Mmain, a.w.arows, t, dD, da_rows(pl, R - 1 - r), t, H,
-                    pl ? 1.f : 0.f, (float*)gr.w1 + (size_t)r * dD * H, kBlasF32, H))
-        return hipErrorUnknown;
+  const int dD = dm.d * D;
+  auto da_rows = [&](int shift) { return a.w.dap + (size_t)shift * H; };
+  // dW1 chunk r = (sub-block rows)^T (da shifted by R-1-r), plus the pe part;
+  // the sum runs over the sub-block rows, split for parallelism
+  for (int r = 0; r < R; ++r) {
+    float* dw1 = (float*)gr.w1 + (size_t)r * dD * H;
+    if (bf) {
+      const MmArgs g{dD, H, (int)Mmain, a.w.arows, 1, dD, da_rows(R - 1 - r), H, 1, dw1, H, 0, 0};
+      e = mm(g, false, true, mm_split(g, kW1Split), a.w.gpart, s);
+    } else {
+      const Gemm g{dD, H, (int)Mmain, a.w.arows, 1, dD, da_rows(R - 1 - r), H, 1, dw1, H, 0};
+      e = gemm_exact(g, true, true, a.w.gpart, s);
+    }
+    if (e != hipSuccess) return e;
+  }
   {
     const size_t n = (size_t)dm.l * D * H;
     k_phi_dw1_pe<T><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(n, H, (const T*)w.pe, (const float*)gr.b1,
@@ -1480,12 +1388,17 @@ static hipError_t phi_bwd(const Dims& dm, const BwdArgs& a, const nsa_phi_weight
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // token gradient per sub-block: sum over chunks of (da shifted by R-1-r) W1_r^T
-  for (int r = 0; r < R; ++r)
-    for (int pl = 0; pl < planes; ++pl)
-      if (blas_gemm(s, false, true, (int)Mmain, dD, H, da_rows(pl, R - 1 - r), t, H,
-                    (const char*)w.w1 + (size_t)r * dD * H * sizeof(T), t, H, (r | pl) ? 1.f : 0.f, a.w.dxs,
-                    kBlasF32, dD))
-        return hipErrorUnknown;
+  for (int r = 0; r < R; ++r) {
+    const void* w1r = (const char*)w.w1 + (size_t)r * dD * H * sizeof(T);
+    if (bf) {
+      const MmArgs g{(int)Mmain, dD, H, da_rows(R - 1 - r), H, 1, w1r, 1, H, a.w.dxs, dD, r > 0, 0};
+      e = mm(g, true, false, 1, nullptr, s);
+    } else {
+      const Gemm g{(int)Mmain, dD, H, da_rows(R - 1 - r), H, 1, w1r, 1, H, a.w.dxs, dD, r > 0};
+      e = gemm_exact(g, true, true, nullptr, s);
+    }
+    if (e != hipSuccess) return e;
+  }
   k_phi_dpe<T><<<(unsigned)((dm.l * D + 3) / 4), 256, 0, s>>>(dm.l * D, H, (const T*)w.w1, (const float*)gr.b1,
                                                               (float*)gr.pe);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1618,29 +1531,29 @@ static hipError_t bwd_impl(const Dims& dm, const nsa_bwd_args* args, BwdArgs& a,
     if (dm.Cg == 0) {
       // dW_g = x^T dz; dx = dz W_g^T
       Gemm g{dm.C, HO, ntok, a.x, 1, dm.C, a.w.dz, HO, 1, a.dwg, HO, 0};
-      if ((e = gemm<T, float>(g, a.w.gpart, s)) != hipSuccess) return e;
+      if ((e = gemm_exact(g, sizeof(T) == 4, true, a.w.gpart, s)) != hipSuccess) return e;
       if (dx) {
         Gemm gx{ntok, dm.C, HO, a.w.dz, HO, 1, a.wg, 1, HO, dx, dm.C, 0};
-        if ((e = gemm<float, T>(gx, nullptr, s)) != hipSuccess) return e;
+        if ((e = gemm_exact(gx, true, sizeof(T) == 4, nullptr, s)) != hipSuccess) return e;
       }
     } else {
       const nsa_gate_grads& gg = args->d_gate_mlp;
       const int Cg = dm.Cg;
       // output layer: dW2 = hid^T dz, db2 = colsum(dz), dhid = dz W2^T
       Gemm g2{Cg, HO, ntok, a.w.ghid, 1, Cg, a.w.dz, HO, 1, a.dwg, HO, 0};
-      if ((e = gemm<float, float>(g2, a.w.gpart, s)) != hipSuccess) return e;
+      if ((e = gemm_exact(g2, true, true, a.w.gpart, s)) != hipSuccess) return e;
       if ((e = colsum(ntok, HO, HO, a.w.dz, (float*)gg.b2, a.w.gpart, s)) != hipSuccess) return e;
       Gemm gh{ntok, Cg, HO, a.w.dz, HO, 1, a.wg, 1, HO, a.w.gdh, Cg, 0};
-      if ((e = gemm<float, T>(gh, nullptr, s)) != hipSuccess) return e;
+      if ((e = gemm_exact(gh, true, sizeof(T) == 4, nullptr, s)) != hipSuccess) return e;
       // GELU: da = dhid * gelu'(pre); first layer: dW1 = x^T da, db1 = colsum(da), dx = da W1^T
       k_phi_dact<<<(unsigned)(((size_t)ntok * Cg + 255) / 256), 256, 0, s>>>((size_t)ntok * Cg, a.w.gpre, a.w.gdh);
       if ((e = hipGetLastError()) != hipSuccess) return e;
       if ((e = colsum(ntok, Cg, Cg, a.w.gdh, (float*)gg.b1, a.w.gpart, s)) != hipSuccess) return e;
       Gemm g1{dm.C, Cg, ntok, a.x, 1, dm.C, a.w.gdh, Cg, 1, (float*)gg.w1, Cg, 0};
-      if ((e = gemm<T, float>(g1, a.w.gpart, s)) != hipSuccess) return e;
+      if ((e = gemm_exact(g1, sizeof(T) == 4, true, a.w.gpart, s)) != hipSuccess) return e;
       if (dx) {
         Gemm gx{ntok, dm.C, Cg, a.w.gdh, Cg, 1, args->gate_mlp.w1, 1, Cg, dx, dm.C, 0};
-        if ((e = gemm<float, T>(gx, nullptr, s)) != hipSuccess) return e;
+        if ((e = gemm_exact(gx, true, sizeof(T) == 4, nullptr, s)) != hipSuccess) return e;
       }
     }
   }

@@ -51,7 +51,7 @@ struct PhiMlpArgs {
   const void* b2;        // [D]
   void* arows;           // ws: [B*Hkv*nsub + l/d, d*D] sub-block rows (io type)
   void* w2t;             // ws: [D, hidden]     (io type)
-  float* cvec;           // ws: [hidden]  b1 + sum_j pe[j] . w1[j]
+  float* pe_part;        // ws: position-embedding rows' partial sums (phi_pe_part_floats)
   float* y;              // ws: [B*Hkv*nsub, (l/d)*hidden] sub-block products
   void* h;               // ws: hidden activations [B*Hkv*ncmp, hidden]: bf16 hi,lo pair or fp32
   void* out;             // [B,ncmp,Hkv,D]
@@ -61,7 +61,9 @@ hipError_t launch_phi_mlp(const Dims& dm, const PhiMlpArgs& a, hipStream_t s);
 // First phi GEMM alone (sub-block products y, see nsa_phi.hip); arows:
 // workspace of (B*Hkv*nsub + l/d) * d*D io elements.
 hipError_t launch_phi_gemm1(const Dims& dm, int D, int nsub, const void* x, const void* pe, const void* w1,
-                            void* arows, float* y, hipStream_t s);
+                            void* arows, float* y, float* pe_part, hipStream_t s);
+// floats of pe_part that launch_phi_gemm1 needs
+size_t phi_pe_part_floats(const Dims& dm);
 size_t phi_mlp_ws_bytes(const Dims& dm, int D);
 
 // ---- compressed attention ----
@@ -123,13 +125,40 @@ hipError_t launch_win_combine(const Dims& dm, const WinArgs& a, hipStream_t s);
 struct GateMlp {
   const void *w1, *b1, *b2;
 };
-// Row-major GEMM through rocBLAS on stream s: C[M,N] (leading dim ldc) =
-// op(A) op(B) + beta C with op(A) [M,K], op(B) [K,N]; ta / tb: A / B stored
-// transposed ([K,M], [N,K]).  fp32 accumulation.  Returns 0 on success, 1 when
-// rocBLAS reports an error, 2 when the device or its handle is unavailable.
-enum BlasType { kBlasBF16 = 0, kBlasF32 = 1 };
-int blas_gemm(hipStream_t s, bool ta, bool tb, int M, int N, int K, const void* A, BlasType at, int lda,
-              const void* B, BlasType bt, int ldb, float beta, void* C, BlasType ct, int ldc);
+// Hand-written MFMA GEMM (nsa_gemm.hip): C[m, n] (+)= sum_k A(m, k) B(k, n),
+// A(m, k) = A[m*sam + k*sak], B(k, n) = B[k*sbk + n*sbn]; each operand
+// k-contiguous or contiguous along its other index, bf16 or fp32 (fp32
+// operands enter as bf16 hi + lo parts); C fp32 (optionally accumulated) or
+// bf16.  batch independent products, operand and result b offset by b*bsa,
+// b*bsb, b*bsc elements.  nsplit > 1 splits k, with batch * nsplit * M * N
+// floats of part.
+struct MmArgs {
+  int M, N, K;
+  const void* A; long long sam, sak;
+  const void* B; long long sbk, sbn;
+  void* C; long long ldc;
+  int accumulate;
+  int c_bf16;
+  int batch = 1;
+  long long bsa = 0, bsb = 0, bsc = 0;
+};
+bool mm_supported(const MmArgs& g, bool a_f32, bool b_f32);
+// Exact fp32 GEMM (v_mfma_f32_16x16x4_f32, operands converted to fp32) for
+// fp32 I/O and small reductions: C[m*ldc + n] (+)= sum_k A(m, k) B(k, n),
+// split over k (at most kGemmMaxSplit ways, nsplit * M * N floats of part)
+// when part is given.
+struct Gemm {
+  int M, N, K;
+  const void* A; long long sam, sak;
+  const void* B; long long sbk, sbn;
+  float* C; long long ldc;
+  int accumulate;
+};
+constexpr int kGemmMaxSplit = 64;
+hipError_t gemm_exact(const Gemm& g, bool a_f32, bool b_f32, float* part, hipStream_t s);
+int mm_split(const MmArgs& g, int max_split);
+hipError_t mm(const MmArgs& g, bool a_f32, bool b_f32, int nsplit, float* part, hipStream_t s);
+
 
 // dst[i] = float(src[i]) for a bf16 array of n elements.
 hipError_t launch_to_f32(const void* src, size_t n, float* dst, hipStream_t s);

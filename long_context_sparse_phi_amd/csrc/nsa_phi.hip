@@ -69,18 +69,25 @@ __global__ __launch_bounds__(256) void k_sigmoid(size_t n, float* __restrict__ g
   if (i < n) g[i] = 1.f / (1.f + expf(-g[i]));
 }
 
-// The linear gate is a plain GEMM (x and W_g share the I/O type): rocBLAS with
-// fp32 accumulation and output, then the sigmoid in place.
+// The linear gate: with bf16 I/O a bf16 MFMA GEMM (fp32 accumulation and
+// output), then the sigmoid in place; fp32 I/O, or a gate width the GEMM's
+// 16-byte loads cannot take, runs the fp32 gate layer.
 hipError_t launch_gate(const Dims& dm, int ntok, const void* x, const void* w, float* gates,
                        hipStream_t s) {
   const int HO = dm.Hq * 3;
   if (ntok == 0) return hipSuccess;
-  const BlasType t = dm.io == IO_BF16 ? kBlasBF16 : kBlasF32;
-  if (blas_gemm(s, false, false, ntok, HO, dm.C, x, t, dm.C, w, t, HO, 0.f, gates, kBlasF32, HO))
-    return hipErrorUnknown;
-  const size_t n = (size_t)ntok * HO;
-  k_sigmoid<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(n, gates);
-  return hipGetLastError();
+  if (dm.io == IO_BF16) {
+    const MmArgs g{ntok, HO, dm.C, x, dm.C, 1, w, HO, 1, gates, HO, 0, 0};
+    if (mm_supported(g, false, false)) {
+      hipError_t e = mm(g, false, false, 1, nullptr, s);
+      if (e != hipSuccess) return e;
+      const size_t n = (size_t)ntok * HO;
+      k_sigmoid<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(n, gates);
+      return hipGetLastError();
+    }
+    return gate_layer<bf16, bf16, 2>(ntok, dm.C, HO, x, w, nullptr, gates, nullptr, s);
+  }
+  return gate_layer<float, float, 2>(ntok, dm.C, HO, x, w, nullptr, gates, nullptr, s);
 }
 
 hipError_t launch_gate_mlp(const Dims& dm, int ntok, const void* x, const void* w_gate, const GateMlp& g,
@@ -240,7 +247,7 @@ hipError_t launch_meanpool(const Dims& dm, int D, const void* x, void* out, void
 //   hidden: a = b1 + sum_r y[Mmain + r, r*H + o] + sum_r y[(bg, i + r), r*H + o]; h = gelu(a)
 //   GEMM2: out[b, i, g, :] = h w2 + b2, rounded to the I/O type.
 // GEMM1 is a plain dense GEMM once the rows of A are laid out contiguously
-// (k_phi_arows): it runs through rocBLAS, one call per W1 chunk r, with fp32
+// (k_phi_arows): one bf16 MFMA GEMM per W1 chunk r (nsa_gemm.hip), fp32
 // accumulation and output.  GEMM2 (small) is k_phi_gemm2: each wave owns a
 // 32x32 output tile (2x2 MFMA 16x16 tiles), a workgroup of four waves 64x64.
 // ---------------------------------------------------------------------------
@@ -266,6 +273,48 @@ __global__ __launch_bounds__(256) void k_phi_arows(Dims dm, int D, int nsub, con
   *reinterpret_cast<Frag8<T>*>(arows + m * KK + k) = load_frag(src);
 }
 
+
+// The position-embedding rows of y: y[Mmain + r, r*H + o] = pe_r . W1_r[:, o]
+// (pe_r: the d rows of pe that chunk r covers, KK = d*D values), the same
+// for every block.  Stage 1: workgroup (o chunk of 64, r, slice z) sums the
+// kPeSlices-th part z of the KK products, four waves a quarter of it each;
+// stage 2 adds the slices in order (deterministic, no atomics).
+constexpr int kPeSlices = 16;
+
+size_t phi_pe_part_floats(const Dims& dm) { return (size_t)kPeSlices * (dm.l / dm.d) * dm.hidden; }
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_phi_pe_part(Dims dm, int D, const T* __restrict__ pe,
+                                                     const T* __restrict__ w1, float* __restrict__ part) {
+  __shared__ float red[4][64];
+  const int H = dm.hidden, KK = dm.d * D;
+  const int r = blockIdx.y, z = blockIdx.z, o = blockIdx.x * 64 + (threadIdx.x & 63), q = threadIdx.x >> 6;
+  const int len = (KK + kPeSlices * 4 - 1) / (kPeSlices * 4);
+  const int k0 = (z * 4 + q) * len, k1 = min(KK, k0 + len);
+  float s = 0.f;
+  if (o < H) {
+#pragma unroll 8
+    for (int k = k0; k < k1; ++k)
+      s = fmaf(to_f32(pe[(size_t)r * KK + k]), to_f32(w1[((size_t)r * KK + k) * H + o]), s);
+  }
+  red[q][threadIdx.x & 63] = s;
+  __syncthreads();
+  if (q == 0 && o < H) {
+    const int t = threadIdx.x;
+    part[((size_t)r * kPeSlices + z) * H + o] = red[0][t] + red[1][t] + red[2][t] + red[3][t];
+  }
+}
+
+__global__ __launch_bounds__(256) void k_phi_pe_fin(Dims dm, size_t Mmain, const float* __restrict__ part,
+                                                    float* __restrict__ y) {
+  const int H = dm.hidden, R = dm.l / dm.d;
+  const int id = blockIdx.x * 256 + threadIdx.x;
+  if (id >= R * H) return;
+  const int r = id / H, o = id % H;
+  float s = 0.f;
+  for (int z = 0; z < kPeSlices; ++z) s += part[((size_t)r * kPeSlices + z) * H + o];
+  y[(Mmain + r) * (size_t)(R * H) + (size_t)r * H + o] = s;
+}
 
 // h rows: (b*Hkv + g)*ncmp + i.  bf16 I/O: h holds hi rows then lo rows (bf16);
 // fp32 I/O: h is fp32.
@@ -370,7 +419,7 @@ size_t phi_mlp_ws_bytes(const Dims& dm, int D) {
   auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
   b += al(((size_t)dm.B * dm.Hkv * nsub + R) * dm.d * D * es);      // arows
   b += al((size_t)D * dm.hidden * es);                              // w2t
-  b += al((size_t)dm.hidden * 4);                                   // cvec (unused slot)
+  b += al(phi_pe_part_floats(dm) * 4);                              // pe-row partial sums
   b += al(((size_t)dm.B * dm.Hkv * nsub + R) * R * dm.hidden * 4);  // y
   b += al((size_t)dm.B * dm.Hkv * dm.ncmp * dm.hidden * (dm.io == IO_BF16 ? 4 : 4));  // h
   return b;
@@ -382,7 +431,7 @@ static hipError_t phi_mlp_impl(const Dims& dm, const PhiMlpArgs& a, hipStream_t 
   const int nsub = dm.ncmp + R - 1;
   hipError_t e;
   if ((e = launch_transpose_2d(dm, dm.hidden, D, a.w2, a.w2t, s)) != hipSuccess) return e;
-  if ((e = launch_phi_gemm1(dm, D, nsub, a.x, a.pe, a.w1, a.arows, a.y, s)) != hipSuccess) return e;
+  if ((e = launch_phi_gemm1(dm, D, nsub, a.x, a.pe, a.w1, a.arows, a.y, a.pe_part, s)) != hipSuccess) return e;
   {
     size_t total = (size_t)dm.B * dm.Hkv * dm.ncmp * dm.hidden;
     k_phi_hidden<T><<<(unsigned)((total + 255) / 256), 256, 0, s>>>(dm, nsub, a.y, (const T*)a.b1, a.h);
@@ -403,7 +452,7 @@ static hipError_t phi_mlp_impl(const Dims& dm, const PhiMlpArgs& a, hipStream_t 
 }
 
 hipError_t launch_phi_gemm1(const Dims& dm, int D, int nsub, const void* x, const void* pe, const void* w1,
-                            void* arows, float* y, hipStream_t s) {
+                            void* arows, float* y, float* pe_part, hipStream_t s) {
   const int R = dm.l / dm.d, KK = dm.d * D, H = dm.hidden;
   const size_t M = (size_t)dm.B * dm.Hkv * nsub + R;
   const size_t total = M * (KK / 8);
@@ -416,13 +465,35 @@ hipError_t launch_phi_gemm1(const Dims& dm, int D, int nsub, const void* x, cons
                                                                         (const float*)pe, (float*)arows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // y[:, r*H : (r+1)*H] = A * w1[r*KK : (r+1)*KK, :]
-  const BlasType t = bf ? kBlasBF16 : kBlasF32;
+  // the position-embedding rows, then the sub-block rows:
+  // y[:, r*H : (r+1)*H] = A * w1[r*KK : (r+1)*KK, :], with bf16 I/O one
+  // launch over the R chunks
+  const size_t Mmain = M - R;
+  {
+    const dim3 grid((H + 63) / 64, R, kPeSlices);
+    if (bf)
+      k_phi_pe_part<bf16><<<grid, 256, 0, s>>>(dm, D, (const bf16*)pe, (const bf16*)w1, pe_part);
+    else
+      k_phi_pe_part<float><<<grid, 256, 0, s>>>(dm, D, (const float*)pe, (const float*)w1, pe_part);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    k_phi_pe_fin<<<(R * H + 255) / 256, 256, 0, s>>>(dm, Mmain, pe_part, y);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const size_t es = bf ? 2 : 4;
+  if (bf) {
+    MmArgs g{(int)Mmain, H, KK, arows, KK, 1, w1, H, 1, y, R * H, 0, 0};
+    g.batch = R;
+    g.bsb = (long long)KK * H;
+    g.bsc = H;
+    return mm(g, false, false, 1, nullptr, s);
+  }
   for (int r = 0; r < R; ++r) {
     const void* br = (const char*)w1 + (size_t)r * KK * H * es;
-    if (blas_gemm(s, false, false, (int)M, H, KK, arows, t, KK, br, t, H, 0.f, y + (size_t)r * H, kBlasF32, R * H))
-      return hipErrorUnknown;
+    {
+      const Gemm g{(int)Mmain, H, KK, arows, KK, 1, br, H, 1, y + (size_t)r * H, R * H, 0};
+      e = gemm_exact(g, true, true, nullptr, s);
+    }
+    if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
