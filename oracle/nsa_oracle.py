@@ -43,7 +43,7 @@ __all__ = [
     "Params", "gate", "gate_logits", "compress", "remap_matrix", "attend", "n_cmp_visible",
     "candidate_blocks", "forced_blocks", "top_n", "is_near_tie", "SCORE_FLOOR", "forward",
     "decode", "append_token", "backward", "layer_forward", "layer_backward", "dq_rows", "dense_causal", "dense_causal_bwd", "round_io", "gelu", "gelu_grad", "sigmoid",
-    "cmp_keys", "slc_keys", "win_keys", "decode_token_count",
+    "cmp_keys", "slc_keys", "win_keys", "decode_token_count", "dkv_keys",
 ]
 
 
@@ -680,6 +680,113 @@ def dq_rows(p: Params, q_rows, k, v, kc, vc, g_rows, d_o_rows, idx_rows, rows, k
                     dqh, _, _ = _attend_bwd(qh, K, V, P, O, gg[:, c:c + 1] * dO, sc)
                     dq[b, r, hs] += dqh
     return dq
+
+
+def dkv_keys(p: Params, q, k, v, g_all, d_o, idx, keys, phi_k=None, phi_v=None, pairs=None, tie_scores=None):
+    """Key/value gradients at the sampled token positions ``keys`` of the
+    (sequence, KV head) pairs ``pairs`` (None: every pair), plus phi's
+    parameter gradients: the same per-row arithmetic as backward(), restricted
+    to the rows that reach those tokens.
+
+    Every row contributes its compressed branch: every block's dK_cmp, dV_cmp
+    is needed, since phi's gradients sum over all blocks and a token's gradient
+    through phi comes from the blocks that contain it.  Rows that see the same
+    compressed blocks (the d consecutive positions between two block ends) are
+    stacked into one product; each row's softmax is still its own.  The
+    selected branch is evaluated for the rows that selected a block holding a
+    sampled token at or before the row; the window branch for the rows whose
+    window holds one.
+
+    q [B,T,Hq,dk], k, v [B,T,Hkv,*], g_all [B,T,Hq,3] gates, d_o [B,T,Hq,dv],
+    idx [B,T,Hkv,n] the selected blocks, or None: then every row's selection is
+    made here from the compressed branch's probabilities, as forward() does
+    (tie_scores [B,T,Hkv,N_sel] consulted on near ties only), and returned.
+    Returns dk, dv [B,len(keys),Hkv,*] (the sum over the three branches, as
+    backward()'s dk, dv at those tokens; NaN for pairs not asked for), dk_cmp,
+    dv_cmp [B,Ncmp,Hkv,*], dphi_k, dphi_v and idx (-1 rows for pairs not asked
+    for when the selection was made here).
+    """
+    B, T, Hq, dk_ = q.shape
+    Hkv = k.shape[2]
+    G = Hq // Hkv
+    sc = _scale(p, dk_)
+    keys = [int(s) for s in keys]
+    pairs = {(b, g) for b in range(B) for g in range(Hkv)} if pairs is None else {tuple(x) for x in pairs}
+    pos = {s: r for r, s in enumerate(keys)}
+    kc = compress(k, phi_k, p)
+    vc = compress(v, phi_v, p)
+    dkc, dvc = np.zeros_like(kc), np.zeros_like(vc)
+    dk_s = np.zeros((B, len(keys), Hkv, k.shape[3]))
+    dv_s = np.zeros((B, len(keys), Hkv, v.shape[3]))
+    blocks_of = {}
+    for s in keys:
+        blocks_of.setdefault(s // p.l_sel, []).append(s)
+    own_sel = idx is None
+    if own_sel:
+        idx = np.full((B, T, Hkv, p.n), -1, dtype=np.int64)
+        for b, g in pairs:
+            for t in range(T):
+                if n_cmp_visible(t, p.l, p.d) == 0:
+                    # no complete compressed block: every causal block (at most
+                    # one, so fewer than n candidates)
+                    idx[b, t, g] = _sets_to_idx([top_n(np.zeros(t // p.l_sel + 1), t, p)], p.n)[0]
+    # compressed branch: runs of rows with the same visible blocks
+    runs = {}
+    for t in range(T):
+        runs.setdefault(n_cmp_visible(t, p.l, p.d), []).append(t)
+    for b in range(B):
+        for g in range(Hkv):
+            hs = slice(g * G, (g + 1) * G)
+            for nv, ts in runs.items():
+                if nv == 0:
+                    continue
+                K, V = kc[b, :nv, g], vc[b, :nv, g]
+                qh = q[b, ts, hs].reshape(-1, dk_)
+                dOc = (g_all[b, ts, hs, 0:1] * d_o[b, ts, hs]).reshape(len(ts) * G, -1)
+                O, _, P = attend(qh, K, V, sc)
+                _, dK, dV = _attend_bwd(qh, K, V, P, O, dOc, sc)
+                dkc[b, :nv, g] += dK
+                dvc[b, :nv, g] += dV
+                if own_sel and (b, g) in pairs:
+                    # importance scores and top-n of each row, as in forward()
+                    W = remap_matrix(nv, ts[-1] // p.l_sel + 1, p)
+                    for r, t in enumerate(ts):
+                        ns = t // p.l_sel + 1
+                        scores = (P[r * G:(r + 1) * G] @ W[:, :ns]).sum(axis=0)
+                        if tie_scores is not None and is_near_tie(scores, t, p):
+                            S = top_n(tie_scores[b, t, g], t, p)
+                        else:
+                            S = top_n(scores, t, p)
+                        idx[b, t, g] = _sets_to_idx([S], p.n)[0]
+    # selected and window branches of the asked pairs
+    for b, g in sorted(pairs):
+        hs = slice(g * G, (g + 1) * G)
+        for t in range(T):
+            qh, dO, gg = q[b, t, hs], d_o[b, t, hs], g_all[b, t, hs]
+            sel = [j for j in idx[b, t, g] if j >= 0]
+            in_slc = [s for j in sel for s in blocks_of.get(j, []) if s <= t]
+            in_win = [s for s in keys if t - p.w + 1 <= s <= t]
+            for c, kidx, wanted in ((1, slc_keys(t, sel, p), in_slc), (2, win_keys(t, p), in_win)):
+                if not wanted:
+                    continue
+                K, V = k[b, kidx, g], v[b, kidx, g]
+                O, _, P = attend(qh, K, V, sc)
+                _, dK, dV = _attend_bwd(qh, K, V, P, O, gg[:, c:c + 1] * dO, sc)
+                at = np.searchsorted(kidx, wanted)     # key lists are ascending
+                for s, i in zip(wanted, at):
+                    dk_s[b, pos[s], g] += dK[i]
+                    dv_s[b, pos[s], g] += dV[i]
+    dk_phi, dphi_k = _phi_bwd(k, phi_k, dkc, p)
+    dv_phi, dphi_v = _phi_bwd(v, phi_v, dvc, p)
+    dk_s += dk_phi[:, keys]
+    dv_s += dv_phi[:, keys]
+    for b in range(B):
+        for g in range(Hkv):
+            if (b, g) not in pairs:
+                dk_s[b, :, g] = np.nan
+                dv_s[b, :, g] = np.nan
+    return {"dk": dk_s, "dv": dv_s, "dk_cmp": dkc, "dv_cmp": dvc, "dphi_k": dphi_k, "dphi_v": dphi_v,
+            "idx": idx}
 
 
 def backward(p: Params, q, k, v, x, w_gate, phi_k, phi_v, d_o, idx, kv_slc=None, kv_win=None,

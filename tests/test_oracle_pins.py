@@ -626,6 +626,73 @@ def test_dq_rows_matches_finite_differences():
                 assert abs(fd - dq[0, r, h, e]) < 1e-6 + 1e-6 * abs(fd), (t, h, e, fd, dq[0, r, h, e])
 
 
+def test_dkv_keys_matches_finite_differences():
+    """Key/value gradients at sampled tokens (used where the whole backward is
+    too large for the oracle) against central differences of the loss in k
+    and v at those tokens, through all three branches and phi, and phi's
+    parameter gradients against the same differences in its parameters."""
+    for phi in ("mlp", "mean"):
+        p, inp = small_problem(B=2, T=30, Hkv=2, G=2, dk=3, dv=2, C=4, phi=phi, l=4, d=2,
+                               l_sel=8, n=3, w=5, hidden=4, seed=21)
+        p = O.Params(l=4, d=2, l_sel=8, n=3, w=5, phi=phi, io=None)
+        rng = np.random.default_rng(23)
+        d_o = rng.standard_normal((2, 30, 4, 2))
+        idx = O.forward(p, **inp)["idx"]
+        keys = [0, 1, 7, 8, 13, 24, 29]
+        g_all = O.gate(inp["x"], inp["w_gate"])
+        got = O.dkv_keys(p, inp["q"], inp["k"], inp["v"], g_all, d_o, idx, keys, inp["phi_k"], inp["phi_v"])
+        eps = 1e-6
+
+        def fd(arr, i):
+            old = arr[i]
+            arr[i] = old + eps
+            lp = _loss(p, inp, d_o, idx)
+            arr[i] = old - eps
+            lm = _loss(p, inp, d_o, idx)
+            arr[i] = old
+            return (lp - lm) / (2 * eps)
+
+        for name, g_name in (("k", "dk"), ("v", "dv")):
+            for b in range(2):
+                for r, s in enumerate(keys):
+                    for g in range(2):
+                        for e in range(inp[name].shape[3]):
+                            want = fd(inp[name], (b, s, g, e))
+                            have = got[g_name][b, r, g, e]
+                            assert abs(want - have) < 1e-6 + 1e-6 * abs(want), (phi, name, b, s, g, e, want, have)
+        if phi == "mlp":
+            for tag, gk in (("phi_k", "dphi_k"), ("phi_v", "dphi_v")):
+                for key in ("pe", "w1", "b1", "w2", "b2"):
+                    flat = inp[tag][key].reshape(-1)
+                    for i in rng.choice(flat.size, size=min(4, flat.size), replace=False):
+                        want = fd(flat, i)
+                        have = got[gk][key].reshape(-1)[i]
+                        assert abs(want - have) < 1e-6 + 1e-6 * abs(want), (tag, key, i, want, have)
+
+
+def test_dkv_keys_equals_the_full_backward_at_every_token():
+    p, inp = small_problem(B=1, T=70, Hkv=2, G=3, dk=5, dv=4, C=4, phi="mlp", l=8, d=4,
+                           l_sel=16, n=3, w=9, hidden=6, seed=4)
+    rng = np.random.default_rng(2)
+    d_o = rng.standard_normal((1, 70, 6, 4))
+    idx = O.forward(p, **inp)["idx"]
+    full = O.backward(p, d_o=d_o, idx=idx, **inp)
+    got = O.dkv_keys(p, inp["q"], inp["k"], inp["v"], O.gate(inp["x"], inp["w_gate"]), d_o, idx, range(70),
+                     inp["phi_k"], inp["phi_v"])
+    np.testing.assert_allclose(got["dk"], full["dk"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(got["dv"], full["dv"], rtol=1e-12, atol=1e-12)
+    for key in ("pe", "w1", "b1", "w2", "b2"):
+        np.testing.assert_allclose(got["dphi_k"][key], full["dphi_k"][key], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(got["dphi_v"][key], full["dphi_v"][key], rtol=1e-12, atol=1e-12)
+    # selecting the blocks itself from its own scores gives forward()'s indices
+    # and the same gradients; pairs not asked for are left out
+    own = O.dkv_keys(p, inp["q"], inp["k"], inp["v"], O.gate(inp["x"], inp["w_gate"]), d_o, None, range(70),
+                     inp["phi_k"], inp["phi_v"], pairs=[(0, 1)])
+    np.testing.assert_array_equal(own["idx"][:, :, 1], idx[:, :, 1])
+    np.testing.assert_allclose(own["dk"][:, :, 1], full["dk"][:, :, 1], rtol=1e-12, atol=1e-12)
+    assert np.isnan(own["dk"][:, :, 0]).all()
+
+
 def test_backward_dense_case_matches_torch_autograd():
     T = 40
     p, inp = small_problem(B=1, T=T, Hkv=2, G=2, dk=6, dv=5, C=5, l=1, d=1, l_sel=8,
