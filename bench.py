@@ -263,6 +263,23 @@ def prefill_roofline(w, stage_ms):
             "launch_ms": round(stage_ms[i], 4), "algorithmic_flops_per_launch": work[name]}
 
 
+def prefill_leg(steps, warmup, wname):
+    """Another prefill workload measured like the headline one (tokens/s from
+    the wall clock, stage times from HIP events) with its MFMA fraction on
+    useful FLOPs and the time 50 % of the bf16 peak would take."""
+    w, wall, stage_ms, gpu_ms = run_prefill(steps, warmup, wname)
+    ms = wall * 1e3 / steps
+    fl = useful_flops(w)
+    useful = fl["cmp"] + fl["slc"] + fl["win"] + fl["phi"] + fl["gate"]
+    return {"workload": wname, "B": w.B, "T": w.T, "H_kv": w.H_kv, "G": w.G, "d_k": w.d_k, "d_v": w.d_v,
+            "steps": steps, "ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
+            "gpu_ms_per_step": round(gpu_ms, 4), "useful_tflop_per_step": round(useful / 1e12, 4),
+            "mfma_frac_useful": round(useful / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "ms_at_half_peak": round(useful / (0.5 * PEAK_BF16_TFLOPS * 1e12) * 1e3, 4),
+            "stages_ms": {name: round(x, 4) for (name, _), x in zip(PREFILL_STAGES, stage_ms)},
+            "roofline": prefill_roofline(w, stage_ms)}
+
+
 def selected_gather(w, stage_ms):
     """The selected branch as a gather: K/V bytes of every (position, KV head)'s
     selected tokens (16 FLOP/B at G = 16, served mostly by L2 and MALL), per
@@ -718,6 +735,7 @@ def main():
     ap.add_argument("--bwd-steps", type=int, default=5)
     ap.add_argument("--no-dense", action="store_true", help="skip the NSA-vs-dense comparison")
     ap.add_argument("--no-layer", action="store_true", help="skip the projection-layer leg")
+    ap.add_argument("--no-prefill-8k", action="store_true", help="skip the 8K prefill leg")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the 1 GiB elementwise kernel used to scale the PMC byte counters")
     ap.add_argument("--traffic-from", nargs=4, metavar=("CAL_FETCH", "CAL_WRITE", "RUN_FETCH", "RUN_WRITE"),
@@ -757,6 +775,8 @@ def main():
         "roofline": prefill_roofline(w, stage_ms),
         "selected_gather": selected_gather(w, stage_ms),
     }
+    if not args.no_prefill_8k:
+        out["prefill_8k"] = prefill_leg(args.steps, args.warmup, "prefill_8k")
     if not args.no_decode:
         out["decode"] = run_decode(args.decode_steps, 3)
     if not args.no_backward:

@@ -8,7 +8,9 @@ benchmark times, on outputs the fp64 oracle can compute one by one:
 * 64K decode (32 sequences): the compressed caches and the decode outputs of
   sampled sequences;
 * 16K training shape (B=2, T=16384, d=128): dq of sampled positions, with the
-  selected indices checked first.
+  selected indices checked first; for two (sequence, KV head) pairs the
+  selection of every position and dk, dv at sampled key tokens; phi's
+  parameter gradients.
 
 Tolerances as in the small-size tests: indices bit-exact (near ties re-selected
 from the GPU's exported scores), floating outputs within 2e-2 absolute + 1e-2
@@ -151,7 +153,12 @@ def test_decode_64k_sampled_sequences():
     check_decode_sequences(w, (0, 13, w.B - 1))
 
 
-def test_train_16k_sampled_dq():
+def test_train_16k_sampled_dq_dk_dv_and_dphi():
+    """Backward at the training shape: dq of sampled positions; for two
+    (sequence, KV head) pairs the selected blocks of every position and dk, dv
+    at sampled key tokens (block 0, which every position selects, block and
+    window edges, the last tokens); and phi's parameter gradients, which sum
+    over every compressed block of the batch."""
     import long_context_sparse_phi_amd as nsa
     import oracle as O
     w = NI.workload("train_16k")
@@ -166,23 +173,52 @@ def test_train_16k_sampled_dq():
     torch.cuda.synchronize()
     rows = sample_rows(w.T, w.l_sel, w.w, seed=2, n_random=4)
     rt = torch.from_numpy(rows).to("cuda:0")
+    T = w.T
+    keys = sorted({0, 1, 31, 32, 63, 64, 100, 511, 512, 1000, 4001, T // 2, T - w.w - 1, T - w.w, T - 65, T - 64,
+                   T - 2, T - 1} | set(np.random.default_rng(5).integers(0, T, 3).tolist()))
+    kt = torch.tensor(keys, device="cuda:0")
     g_dq = np64(grads["dq"][:, rt])
-    g_idx = fwd["idx"][:, rt].cpu().numpy().astype(np.int64)
-    g_ps = np64(fwd["p_slc"][:, rt])
+    g_dk, g_dv = np64(grads["dk"][:, kt]), np64(grads["dv"][:, kt])
+    g_dphi = {tag: {k2: np64(t) for k2, t in grads[tag].items()} for tag in ("d_phi_k", "d_phi_v")}
+    g_idx = fwd["idx"].cpu().numpy().astype(np.int64)
+    g_ps = np64(fwd["p_slc"])
     del grads, fwd, d
     torch.cuda.empty_cache()
     p = oracle_params(w)
+    q = inp["q"].double().numpy()
     k = inp["k"].double().numpy()
     v = inp["v"].double().numpy()
     phi_k, phi_v = NI.to_numpy64(inp["phi_k"]), NI.to_numpy64(inp["phi_v"])
     kc = O.compress(k, phi_k, p)
     vc = O.compress(v, phi_v, p)
-    q_rows = inp["q"][:, rows].double().numpy()
     x = inp["x"].double().numpy()
     wg = inp["w_gate"].double().numpy()
+    dO = d_o.double().numpy()
+    # dq of sampled positions
+    q_rows = q[:, rows]
     ref_f = O.forward(p, SampledRows(q_rows, rows, w.T), k, v, x, wg, phi_k, phi_v, rows=rows,
-                      tie_scores=SampledRows(g_ps, rows, w.T), kc=kc, vc=vc)
-    assert np.array_equal(ref_f["idx"], g_idx)
-    dq = O.dq_rows(p, q_rows, k, v, kc, vc, ref_f["gates"], d_o[:, rows].double().numpy(), ref_f["idx"], rows)
+                      tie_scores=SampledRows(g_ps[:, rows], rows, w.T), kc=kc, vc=vc)
+    assert np.array_equal(ref_f["idx"], g_idx[:, rows])
+    dq = O.dq_rows(p, q_rows, k, v, kc, vc, ref_f["gates"], dO[:, rows], ref_f["idx"], rows)
     assert_close(g_dq, dq, "dq")
     print(f"[gpu] 16K backward: dq of {len(rows)} rows x {w.B} sequences checked", flush=True)
+    # key-side gradients
+    pairs = [(0, 0), (1, w.H_kv - 1)]
+    ref = O.dkv_keys(p, q, k, v, O.gate(x, wg), dO, None, keys, phi_k, phi_v, pairs=pairs, tie_scores=g_ps)
+    for b, g in pairs:
+        mism = np.argwhere(np.any(ref["idx"][b, :, g] != g_idx[b, :, g], axis=-1))
+        assert len(mism) == 0, f"idx of (b={b}, g={g}) differs at {len(mism)} positions, first {mism[:3].ravel()}"
+        assert_close(g_dk[b, :, g], ref["dk"][b, :, g], f"dk (b={b}, g={g})")
+        assert_close(g_dv[b, :, g], ref["dv"][b, :, g], f"dv (b={b}, g={g})")
+    for tag, rtag in (("d_phi_k", "dphi_k"), ("d_phi_v", "dphi_v")):
+        for key in ("pe", "w1", "b1", "w2", "b2"):
+            err = assert_close(g_dphi[tag][key], ref[rtag][key], f"{rtag}.{key}")
+            print(f"[gpu] 16K {rtag}.{key}: max abs err {err:.3e}, max |ref| {np.abs(ref[rtag][key]).max():.3e}")
+    print(f"[gpu] 16K backward: selection of every position, dk and dv at {len(keys)} tokens of {pairs}, "
+          f"and phi's gradients checked", flush=True)
+
+
+def test_prefill_8k_sampled_rows():
+    # the 8K prefill workload at its own size (B=1, T=8192, 4 KV x 16 query
+    # heads, d_k = d_v = 128, MLP phi), both launches, more sampled rows
+    check_prefill_sampled_rows(NI.workload("prefill_8k"), row_seed=3)
