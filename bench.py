@@ -687,7 +687,7 @@ class _SampledRows:
         return self.data[b, self.pos[int(t)]]
 
 
-def cpu_baseline(wname="prefill_64k", nrows=192):
+def cpu_baseline(wname="prefill_64k", nrows=1536):
     """fp64 oracle on a bounded sample of the workload: the compression of the
     whole sequence plus `nrows` query positions spread evenly over [0, T);
     tokens/s = T / (t_compress + t_rows * T / nrows)."""
@@ -718,6 +718,78 @@ def cpu_baseline(wname="prefill_64k", nrows=192):
     return {"value": round(w.B * w.T / est, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{wname}: phi compression of all {kc.shape[1]} blocks ({t_cmp:.1f} s) + {nrows} query "
                       f"rows evenly spaced over [0,{w.T}) ({t_rows:.1f} s), scaled to {w.T} rows"}
+
+
+def cpu_baseline_decode(wname="decode_64k", nseq=2, reps=10):
+    """fp64 oracle decode step on `nseq` of the workload's sequences, averaged
+    over `reps` repetitions (their compressed caches are built first by the
+    oracle's compression and are not timed: the step takes them as an input);
+    scaled to all B sequences."""
+    import numpy as np
+    import torch
+    import nsa_inputs as NI
+    import oracle as O
+
+    w = NI.workload(wname)
+    cores = len(os.sched_getaffinity(0))
+    torch.set_num_threads(cores)
+    inp = NI.make_decode_inputs(w.replace(B=nseq), 0)
+    a = NI.to_numpy64(inp)
+    del inp
+    p = O.Params(l=w.l, d=w.d, l_sel=w.l_sel, n=w.n, w=w.w, phi=w.phi, io="bf16")
+    kc = O.compress(a["k_cache"], a["phi_k"], p)
+    vc = O.compress(a["v_cache"], a["phi_v"], p)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        O.decode(p, a["q"], a["k_cache"], a["v_cache"], kc, vc, a["x"], a["w_gate"])
+    t = (time.perf_counter() - t0) / reps
+    us = t * 1e6 * w.B / nseq
+    return {"value": round(us, 1), "unit": "us/step", "cores": cores, "kind": "oracle",
+            "sample": f"{wname}: the decode step of {nseq} of the {w.B} sequences ({t:.2f} s, mean of {reps}), "
+                      f"scaled to {w.B}; compressed caches built beforehand, untimed"}
+
+
+def cpu_baseline_backward(wname="train_16k", nrows=384):
+    """fp64 oracle backward on a bounded sample: phi's forward and backward
+    over every compressed block, plus the per-row backward arithmetic (each
+    branch's softmax and its gradients, what backward() does for every row) of
+    `nrows` positions spread evenly over each sequence; tokens/s = B*T /
+    (t_phi + t_rows * B*T / (B*nrows))."""
+    import numpy as np
+    import torch
+    import nsa_inputs as NI
+    import oracle as O
+
+    w = NI.workload(wname)
+    cores = len(os.sched_getaffinity(0))
+    torch.set_num_threads(cores)
+    inp = NI.make_prefill_inputs(w, 0)
+    d_o = NI.make_grad_output(w, 0)
+    rows = np.linspace(0, w.T - 1, nrows).astype(np.int64)
+    q_rows = inp["q"][:, rows].double().numpy()
+    k, v = inp["k"].double().numpy(), inp["v"].double().numpy()
+    phi_k, phi_v = NI.to_numpy64(inp["phi_k"]), NI.to_numpy64(inp["phi_v"])
+    x = inp["x"].double().numpy()
+    wg = inp["w_gate"].double().numpy()
+    d_o_rows = d_o[:, rows].double().numpy()
+    del inp, d_o
+    p = O.Params(l=w.l, d=w.d, l_sel=w.l_sel, n=w.n, w=w.w, phi=w.phi, io="bf16")
+    t0 = time.perf_counter()
+    kc = O.compress(k, phi_k, p)
+    vc = O.compress(v, phi_v, p)
+    from oracle import nsa_oracle as ON
+    ON._phi_bwd(k, phi_k, np.ones_like(kc), p)
+    ON._phi_bwd(v, phi_v, np.ones_like(vc), p)
+    t_phi = time.perf_counter() - t0
+    f = O.forward(p, _SampledRows(q_rows, rows, w.T), k, v, x, wg, phi_k, phi_v, rows=rows, kc=kc, vc=vc)
+    t0 = time.perf_counter()
+    O.dq_rows(p, q_rows, k, v, kc, vc, f["gates"], d_o_rows, f["idx"], rows)
+    t_rows = time.perf_counter() - t0
+    est = t_phi + t_rows * w.T / nrows
+    return {"value": round(w.B * w.T / est, 2), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{wname}: phi forward and backward over all {kc.shape[1]} blocks of {w.B} sequences "
+                      f"({t_phi:.1f} s) + the per-row backward of {nrows} positions evenly spaced over each "
+                      f"sequence ({t_rows:.1f} s), scaled to {w.T} rows"}
 
 
 # ---------------------------------------------------------------- main
@@ -788,6 +860,12 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(args.workload)
+        if "decode" in out:
+            log("timing the fp64 oracle's decode step on a sample")
+            out["decode"]["cpu_baseline"] = cpu_baseline_decode()
+        if "backward" in out:
+            log("timing the fp64 oracle's backward on a sample")
+            out["backward"]["cpu_baseline"] = cpu_baseline_backward()
     print(json.dumps(out))
 
 
