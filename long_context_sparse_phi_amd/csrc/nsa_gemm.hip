@@ -237,30 +237,57 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs g, int kc, int nsplit, float*
     step(I0{}, t);
     if (t + 1 < nk) step(I1{}, t + 1);
   }
-  // C tile (or this split's partial tile)
-  float* pz = part ? part + (size_t)blockIdx.z * g.M * g.N : nullptr;
-  const long long cb = bat * g.bsc;
+  // C tile (or this split's partial tile) through LDS: each wave writes its
+  // 64 x 64 fp32 tile (row stride 68 floats: the four row groups of a write
+  // land on distinct banks), then stores it row by row, four consecutive
+  // values per lane.  The k loop's last barrier has freed the LDS.
+  float* ep = (float*)smem_raw + (size_t)wave * 64 * 68;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wn + j * 16 + c16;
-      if (n >= g.N) continue;
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm + i * 16 + qd * 4 + r;
-        if (m >= g.M) continue;
-        const float v = acc[i][j][r];
-        if (pz) {
-          pz[(size_t)m * g.N + n] = v;
-        } else if (g.c_bf16) {
-          ((bf16*)g.C)[cb + (long long)m * g.ldc + n] = (bf16)v;
-        } else {
-          float* cp = (float*)g.C + cb + (long long)m * g.ldc + n;
-          *cp = g.accumulate ? *cp + v : v;
+      for (int r = 0; r < 4; ++r) ep[(i * 16 + qd * 4 + r) * 68 + j * 16 + c16] = acc[i][j][r];
+  __syncthreads();
+  const bool to_part = part != nullptr;
+  float* pz = to_part ? part + (size_t)blockIdx.z * g.M * g.N : nullptr;
+  const long long ld = to_part ? g.N : g.ldc;
+  const long long cb = to_part ? 0 : bat * g.bsc;
+  const bool c16b = !to_part && g.c_bf16;
+  const bool acc_c = !to_part && g.accumulate;
+  const uintptr_t cbase = to_part ? (uintptr_t)pz : (uintptr_t)g.C + (uintptr_t)cb * (c16b ? 2 : 4);
+  // four-value vectors need 16-byte (fp32) or 8-byte (bf16) aligned rows
+  const bool vec = ld % 4 == 0 && cbase % (c16b ? 8 : 16) == 0;
+  const int col = (lane & 15) * 4;
+  const int n = n0 + wn + col;
+#pragma unroll 4
+  for (int it = 0; it < 16; ++it) {
+    const int row = it * 4 + (lane >> 4);
+    const int m = m0 + wm + row;
+    if (m >= g.M || n >= g.N) continue;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(ep + row * 68 + col);
+    const long long o = (long long)m * ld + n;
+    if (c16b) {
+      bf16* cp = (bf16*)g.C + cb + o;
+      if (vec && n + 4 <= g.N) {
+        store_col4(cp, (bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]);
+      } else {
+        for (int e = 0; e < 4 && n + e < g.N; ++e) cp[e] = (bf16)v[e];
+      }
+    } else {
+      float* cp = to_part ? pz + o : (float*)g.C + cb + o;
+      if (vec && n + 4 <= g.N) {
+        f32x4 w = v;
+        if (acc_c) {
+          const f32x4 old = *reinterpret_cast<const f32x4*>(cp);
+          w = f32x4{old[0] + v[0], old[1] + v[1], old[2] + v[2], old[3] + v[3]};
         }
+        *reinterpret_cast<f32x4*>(cp) = w;
+      } else {
+        for (int e = 0; e < 4 && n + e < g.N; ++e) cp[e] = acc_c ? cp[e] + v[e] : v[e];
       }
     }
+  }
 }
 
 // Sums the split partials of each batch in split order into C.
@@ -284,7 +311,9 @@ __global__ __launch_bounds__(256) void k_mm_reduce(MmArgs g, int nsplit, const f
 template <typename TA, typename TB, bool AKC, bool BKC>
 hipError_t mm_launch(const MmArgs& g, int nsplit, int kc, float* part, hipStream_t s) {
   constexpr int PA = sizeof(TA) == 4 ? 2 : 1, PB = sizeof(TB) == 4 ? 2 : 1;
-  const size_t lds = 2 * (size_t)(PA + PB) * kTileElems * sizeof(bf16);
+  // the operand pipeline, or the epilogue's four 64 x 68 fp32 wave tiles
+  const size_t pipe = 2 * (size_t)(PA + PB) * kTileElems * sizeof(bf16), epi = (size_t)4 * 64 * 68 * sizeof(float);
+  const size_t lds = pipe > epi ? pipe : epi;
   auto kfn = k_mm<TA, TB, AKC, BKC>;
   if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   dim3 grid((g.N + kBN - 1) / kBN, (g.M + kBM - 1) / kBM, nsplit * g.batch);
