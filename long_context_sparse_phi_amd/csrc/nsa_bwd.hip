@@ -728,23 +728,25 @@ __device__ __forceinline__ bool kv_task(const Dims& dm, const BwdArgs& a, int& b
   const BwdPlan& pl = a.pl;
   plist = nullptr;
   outp = nullptr;
-  // Consecutive workgroups go to different XCDs, so the (b, g) index runs
-  // fastest: every XCD then receives an even share of the heavy tasks.
+  // Selected blocks: consecutive workgroups go to different XCDs, so the
+  // (b, g) index runs fastest and every XCD receives an even share.
   const int BG = dm.B * dm.Hkv;
   if (MODE == KV_CMP) {
-    bg = blockIdx.x % BG;
-    const int r = blockIdx.x / BG;
-    const int kg = r % pl.nkg_cmp;
-    const int seg = r / pl.nkg_cmp;
+    // tasks in order of their first query position on each XCD (64*d keys'
+    // worth of positions per group step, kSegCmp per segment)
+    int kg, seg;
+    span_task_order(blockIdx.x, BG, pl.nkg_cmp, pl.nseg_cmp, 64 * dm.d, kSegCmp, bg, kg, seg);
     k0 = kg * 64;
     klim = dm.ncmp;
     p0 = k0 * dm.d + dm.l - 1 + seg * kSegCmp;
     npos = max(0, min(dm.T, p0 + kSegCmp) - p0);
     outp = a.w.part_cmp + (((size_t)bg * pl.nkg_cmp + kg) * pl.nseg_cmp + seg) * 64 * W;
   } else if (MODE == KV_WIN) {
+    // each XCD walks contiguous key groups of its (b, g): the groups running
+    // together on it read nearly the same query rows, which its L2 then holds
     const int nkg = (dm.T + 63) / 64;
-    const int kg = blockIdx.x % nkg;
-    bg = blockIdx.x / nkg;
+    int kg;
+    xcd_map(blockIdx.x, BG, nkg, bg, kg);
     k0 = kg * 64;
     klim = dm.T;
     p0 = k0;
@@ -873,10 +875,16 @@ __global__ __launch_bounds__(256) void k_bwd_kv(Dims dm, BwdArgs a) {
       const int D = m.is_q ? DK : DV;
       const T* src = (const T*)(m.is_q ? a.q : a.d_o);
       const bool ok = u < St::NTASK && pp >= 0;
-      const size_t rb = ((size_t)(b * dm.T + (ok ? pp : 0)) * dm.Hq + g * G + h0) * D + m.c8 * 8;
+      // loads from a clamped row (position 0, the group's last head, feature
+      // chunk 0 for threads without a task) that is always in the tensor, then
+      // a select: no branch per row
+      const size_t rb = ((size_t)(b * dm.T + (ok ? pp : 0)) * dm.Hq + g * G) * D + (ok ? m.c8 * 8 : 0);
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        reg.r[cc][k] = (ok && h0 + k < G) ? load_frag(src + rb + (size_t)k * D) : zero_frag<T>();
+      for (int k = 0; k < 4; ++k) {
+        const bool hv = ok && h0 + k < G;
+        const Frag8<T> f = load_frag(src + rb + (size_t)min(h0 + k, G - 1) * D);
+        reg.r[cc][k] = hv ? f : zero_frag<T>();
+      }
     }
     if (tid < 32) {
       const int h = tid & 15, pp = (tid >> 4) ? pp1 : pp0;
@@ -947,32 +955,43 @@ __global__ __launch_bounds__(256) void k_bwd_kv(Dims dm, BwdArgs a) {
     const float* sg = sD + 32;
     if (wave_live) {
       float pg[2][4], dsv[2][4];
+      // S and dP of both 16-row tiles first: four independent MFMA chains
+      f32x4 sacc[2], dpacc[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f}, dpacc = f32x4{0.f, 0.f, 0.f, 0.f};
+        sacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dpacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
-        for (int ks = 0; ks < DK / 32; ++ks)
-          mma(sacc, *reinterpret_cast<const Frag8<T>*>(Qr + (i * 16 + c16) * QS + ks * 32 + qd * 8), kf[ks]);
+      for (int ks = 0; ks < DK / 32; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < DV / 32; ++ks)
-          mma(dpacc, *reinterpret_cast<const Frag8<T>*>(Dr + (i * 16 + c16) * DS + ks * 32 + qd * 8), vf[ks]);
+        for (int i = 0; i < 2; ++i)
+          mma(sacc[i], *reinterpret_cast<const Frag8<T>*>(Qr + (i * 16 + c16) * QS + ks * 32 + qd * 8), kf[ks]);
+#pragma unroll
+      for (int ks = 0; ks < DV / 32; ++ks)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          mma(dpacc[i], *reinterpret_cast<const Frag8<T>*>(Dr + (i * 16 + c16) * DS + ks * 32 + qd * 8), vf[ks]);
+      // Row terms without branches: a lane's four rows are consecutive in the
+      // staged log-sum-exp, D_c and gate arrays.  Staged rows past the
+      // positions or heads hold 0 there and zero q / dO, so every lane
+      // evaluates finite values and the mask only selects them.
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
         const int t = pos[i];
         bool pv = t >= 0 && kvalid;
         if (MODE == KV_CMP) pv = pv && key < ncmp_visible(t, dm.l, dm.d);
         else if (MODE == KV_WIN) pv = pv && key <= t && t <= key + dm.w - 1;
         else pv = pv && key <= t;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(slse + i * 16 + qd * 4);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(sD + i * 16 + qd * 4);
+        const f32x4 g4 = *reinterpret_cast<const f32x4*>(sg + i * 16 + qd * 4);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int rr = i * 16 + qd * 4 + r;
           const bool v = pv && (qd * 4 + r) < G;
-          float p = 0.f, ds = 0.f;
-          if (v) {
-            p = fast_exp2(sacc[r] * sc2 - slse[rr]);
-            ds = p * (sg[rr] * dpacc[r] - sD[rr]);
-            p *= sg[rr];
-          }
-          pg[i][r] = p;
-          dsv[i][r] = ds;
+          const float p = fast_exp2(sacc[i][r] * sc2 - l4[r]);
+          pg[i][r] = v ? p * g4[r] : 0.f;
+          dsv[i][r] = v ? p * (g4[r] * dpacc[i][r] - d4[r]) : 0.f;
         }
       }
       float pv8[8], ds8[8];

@@ -240,7 +240,7 @@ __device__ __forceinline__ int wave_sel_row_len(int myid, int lane, int n, int t
 // unit when there are at most 8 units (so that unit's keys stay in that
 // XCD's L2), and hands out the most expensive tiles (late positions) first.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void xcd_map(int id, int units, int ntiles, int& unit, int& tile) {
+__host__ __device__ __forceinline__ void xcd_map(int id, int units, int ntiles, int& unit, int& tile) {
   if (units <= 8 && 8 % units == 0 && ntiles % (8 / units) == 0) {
     int per = 8 / units, x = id & 7, k = id >> 3;
     unit = x / per;
@@ -253,6 +253,40 @@ __device__ __forceinline__ void xcd_map(int id, int units, int ntiles, int& unit
     unit = id / ntiles;
     tile = ntiles - 1 - id % ntiles;
   }
+}
+
+// Task (group kg, segment seg) of workgroup id, for units x ngroup x nseg
+// tasks whose query rows start at kg*span + seg*seglen (plus a constant).
+// When span is a multiple of seglen, the tasks with equal a = R*kg + seg
+// (R = span / seglen) read the same rows: each XCD then takes one unit's
+// tasks in increasing a (xcd_map), so the tasks running together on it share
+// their rows in L2.  Otherwise the unit index runs fastest.  A bijection of
+// [0, units*ngroup*nseg) onto the tasks either way.
+__host__ __device__ __forceinline__ void span_task_order(int id, int units, int ngroup, int nseg, int span,
+                                                         int seglen, int& unit, int& kg, int& seg) {
+  if (span % seglen == 0) {
+    const int R = span / seglen;
+    int tile;
+    xcd_map(id, units, ngroup * nseg, unit, tile);
+    int r = ngroup * nseg - 1 - tile;   // rank among the unit's tasks
+    const int amax = R * (ngroup - 1) + nseg - 1;
+    for (int a = 0; a <= amax; ++a) {
+      // groups kg < ngroup with 0 <= a - R*kg < nseg
+      const int hi = a / R < ngroup - 1 ? a / R : ngroup - 1;
+      const int lo = a - nseg + 1 <= 0 ? 0 : (a - nseg + R) / R;
+      const int cnt = hi >= lo ? hi - lo + 1 : 0;
+      if (r < cnt) {
+        kg = lo + r;
+        seg = a - R * kg;
+        return;
+      }
+      r -= cnt;
+    }
+  }
+  unit = id % units;
+  const int r = id / units;
+  kg = r % ngroup;
+  seg = r / ngroup;
 }
 
 // Weight of compression block kr (row of a 32-key tile) in selection block jc

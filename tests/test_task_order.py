@@ -1,0 +1,98 @@
+"""CPU test of the workgroup -> task mappings of the backward's dK/dV kernels.
+
+Every workgroup of a launch must receive a distinct task and every task a
+workgroup, or a key group's gradient segment is computed twice and another
+never.  The mappings are the kernels' own (nsa_common.hpp, compiled
+host-only): xcd_map for the window keys' (unit, key group) tasks and
+span_task_order for the compressed keys' (unit, key group, segment) tasks.
+Beyond the bijection, the test checks the order the mapping exists for: on
+each XCD (workgroup id mod 8) one unit's tasks come in nondecreasing first
+query position.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "long_context_sparse_phi_amd", "csrc")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+PROGRAM = r"""
+#include "nsa_common.hpp"
+#include <cstdio>
+int main() {
+  int kind, units, ngroup, nseg, span, seglen;
+  while (std::scanf("%d %d %d %d %d %d", &kind, &units, &ngroup, &nseg, &span, &seglen) == 6) {
+    const int n = units * ngroup * nseg;
+    for (int id = 0; id < n; ++id) {
+      int u = -1, kg = -1, seg = 0;
+      if (kind == 0) nsa::xcd_map(id, units, ngroup, u, kg);
+      else nsa::span_task_order(id, units, ngroup, nseg, span, seglen, u, kg, seg);
+      std::printf("%d %d %d\n", u, kg, seg);
+    }
+  }
+  return 0;
+}
+"""
+
+
+@pytest.fixture(scope="module")
+def order_binary(tmp_path_factory):
+    if not os.path.exists(HIPCC) and shutil.which("hipcc") is None:
+        pytest.skip("hipcc not available")
+    d = tmp_path_factory.mktemp("taskorder")
+    src, exe = d / "order.cpp", d / "order"
+    src.write_text(PROGRAM)
+    subprocess.run([HIPCC, "-x", "hip", "--offload-host-only", "-O1", "-std=c++17", "-I", CSRC,
+                    "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True,
+                   capture_output=True)
+    return str(exe)
+
+
+def run(binary, cases):
+    text = "".join(" ".join(map(str, c)) + "\n" for c in cases)
+    out = subprocess.run([binary], input=text, capture_output=True, text=True, check=True).stdout.split("\n")
+    res, i = [], 0
+    for kind, units, ngroup, nseg, _, _ in cases:
+        n = units * ngroup * nseg
+        res.append([tuple(int(x) for x in line.split()) for line in out[i:i + n]])
+        i += n
+    return res
+
+
+# (units, key groups, segments, group span in positions, segment length)
+CMP_SHAPES = [
+    (8, 16, 32, 1024, 512),    # train_16k: B=2, Hkv=4, d=16
+    (4, 64, 128, 1024, 512),   # 64K, B=1, Hkv=4
+    (1, 3, 5, 1024, 512),
+    (2, 7, 9, 512, 512),       # d=8: one segment per group step
+    (3, 5, 4, 2048, 512),      # units not dividing 8
+    (16, 4, 6, 1024, 512),
+    (8, 5, 7, 768, 512),       # d=12: span not a multiple of the segment
+    (6, 2, 3, 320, 512),
+]
+WIN_SHAPES = [(8, 256), (4, 1024), (1, 33), (2, 64), (3, 10), (16, 5), (12, 7), (8, 1)]
+
+
+def test_compressed_task_order_is_a_bijection_in_position_order(order_binary):
+    res = run(order_binary, [(1,) + s for s in CMP_SHAPES])
+    for (units, ngroup, nseg, span, seglen), tasks in zip(CMP_SHAPES, res):
+        assert sorted(tasks) == [(u, k, s) for u in range(units) for k in range(ngroup) for s in range(nseg)]
+        if span % seglen:
+            continue
+        R = span // seglen
+        # dispatch order on each XCD, per unit: nondecreasing a = R*kg + seg
+        last = {}
+        for wid, (u, kg, seg) in enumerate(tasks):
+            key = (wid % 8, u)
+            a = R * kg + seg
+            assert a >= last.get(key, -1), (units, ngroup, nseg, wid)
+            last[key] = a
+
+
+def test_window_task_map_is_a_bijection(order_binary):
+    res = run(order_binary, [(0, u, n, 1, 1, 1) for u, n in WIN_SHAPES])
+    for (units, ntiles), tasks in zip(WIN_SHAPES, res):
+        assert sorted((u, k) for u, k, _ in tasks) == [(u, k) for u in range(units) for k in range(ntiles)]
