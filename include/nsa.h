@@ -79,8 +79,9 @@ typedef enum nsa_op {
 
 /* Shapes and hyper-parameters.
  *   batch B; seqlen T (prefill/backward) or cache length S (decode);
- *   n_kv_heads H_kv; group_size G (query heads per KV head, H_q = H_kv*G,
- *   G in {1,2,4,8,16}); d_k, d_v head dims ((64,64), (128,128), (192,128));
+ *   n_kv_heads H_kv (H_kv * max(d_k, d_v) < 2^24); group_size G (query heads
+ *   per KV head, H_q = H_kv*G, G in {1,2,4,8,16}); d_k, d_v head dims
+ *   ((64,64), (128,128), (192,128));
  *   cmp_block l, cmp_stride d (d | l), sel_block l' (d | l', l <= l',
  *   16 | l', l' | 32*d, 31*d + l <= 32*l'); n_select n (3 <= n <= 32);
  *   window w >= 1; gate_dim C (gate input width); phi_hidden (MLP width,

@@ -74,6 +74,8 @@ nsa_status make_dims(const nsa_params* p, Dims* dm) {
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return NSA_ERR_UNSUPPORTED;
   if (p->d_k < 1 || p->d_v < 1) return NSA_ERR_INVALID_ARG;
   if (!shapes_supported(p->d_k, p->d_v)) return NSA_ERR_UNSUPPORTED;
+  // one key row of every KV head: a 24-bit element count (decode tile addressing)
+  if ((long long)p->n_kv_heads * (p->d_k > p->d_v ? p->d_k : p->d_v) >= (1ll << 24)) return NSA_ERR_UNSUPPORTED;
   const int l = p->cmp_block, d = p->cmp_stride, ls = p->sel_block;
   if (l < 1 || d < 1 || ls < 1 || l % d != 0 || ls % d != 0 || l > ls) return NSA_ERR_INVALID_ARG;
   if (ls % 16 != 0 || (32 * d) % ls != 0) return NSA_ERR_UNSUPPORTED;

@@ -170,10 +170,14 @@ __device__ __forceinline__ DecSeq dec_seq(const Dims& dm, const DecArgs& a, int 
 
 // 32-key tile of one KV head: global -> registers (gload, one tile ahead of
 // the compute) -> LDS (lstore).  Keys: 32 rows x DK, chunks swizzled by
-// kchunk_off.  Values: V^T [DV][kVS]; a lane moves 4 consecutive key rows x 8
-// features and writes them as 8-byte columns.  Lanes vary the feature chunk
-// fastest within groups of 4, then the row quad, which spreads both the
-// global requests (64 contiguous bytes per lane quad) and the LDS banks.
+// kchunk_off; load c moves rows 8*(c%4) .. +7, 8 consecutive 16-byte chunks
+// of each (128 contiguous bytes per row).  Values: V^T [DV][kVS]; a lane
+// moves 4 consecutive key rows x 8 features and writes them as 8-byte
+// columns.  Lanes vary the feature chunk fastest within groups of 4, then the
+// row quad, which spreads both the global requests (64 contiguous bytes per
+// lane quad) and the LDS banks.  Addresses are a wave-uniform tile base plus
+// a 24-bit row product per lane, so a load costs a few full-rate VALU
+// operations.
 template <typename T, int DK, int DV>
 struct DecTile {
   static constexpr int kVS = 40;                     // V^T row stride (elements)
@@ -181,30 +185,33 @@ struct DecTile {
   static constexpr int VTK = DV / 64;                // value tasks (4 rows x 8 features) per lane
   static constexpr size_t kElems = (size_t)32 * DK;
   static constexpr size_t elems = kElems + (size_t)DV * kVS;
+  static_assert(DK % 64 == 0, "key rows are moved in groups of 8 chunks");
   Frag8<T> kr[KCH];
   Frag8<T> vr[VTK][4];
+  static __device__ __forceinline__ int krow(int c, int lane) { return (c & 3) * 8 + (lane >> 3); }
+  static __device__ __forceinline__ int kchunk(int c, int lane) { return (c >> 2) * 8 + (lane & 7); }
 
+  // rows past klim - 1 (the tail of the last tile) read row klim - 1
   __device__ __forceinline__ void gload(const T* kbase, const T* vbase, size_t kstride, size_t vstride, int key0,
                                         int klim, int lane) {
+    const T* kt = kbase + (size_t)key0 * kstride;
+    const T* vt = vbase + (size_t)key0 * vstride;
+    const int rmax = klim - 1 - key0;
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int i = lane + 64 * c, row = i / (DK / 8), c8 = i % (DK / 8);
-      kr[c] = load_frag(kbase + (size_t)min(key0 + row, klim - 1) * kstride + c8 * 8);
-    }
+    for (int c = 0; c < KCH; ++c)
+      kr[c] = load_frag(kt + __umul24((unsigned)min(krow(c, lane), rmax), (unsigned)kstride) + kchunk(c, lane) * 8);
 #pragma unroll
     for (int c = 0; c < VTK; ++c) {
       const int u = lane + 64 * c, c8 = (u & 3) + 4 * (u >> 5), rq = (u >> 2) & 7;
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        vr[c][k] = load_frag(vbase + (size_t)min(key0 + 4 * rq + k, klim - 1) * vstride + c8 * 8);
+        vr[c][k] = load_frag(vt + __umul24((unsigned)min(4 * rq + k, rmax), (unsigned)vstride) + c8 * 8);
     }
   }
   __device__ __forceinline__ void lstore(T* tile, int lane) {
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int i = lane + 64 * c, row = i / (DK / 8), c8 = i % (DK / 8);
-      *reinterpret_cast<Frag8<T>*>(tile + kchunk_off<DK>(row, c8)) = kr[c];
-    }
+    for (int c = 0; c < KCH; ++c)
+      *reinterpret_cast<Frag8<T>*>(tile + kchunk_off<DK>(krow(c, lane), kchunk(c, lane))) = kr[c];
     T* vt = tile + kElems;
 #pragma unroll
     for (int c = 0; c < VTK; ++c) {
@@ -238,18 +245,22 @@ struct DecTile {
 // tile's scores by exp2(max - lse).  A wave streams pl.cpw consecutive chunks
 // of one (sequence, KV head) through a single ring of register tiles, so the
 // ring stays full across chunk boundaries; each chunk's softmax state is
-// written when its last tile is done.
+// written when its last tile is done.  The chunk's per-tile block scores
+// and reference maxima are kept in LDS and written with that state: global
+// stores issued between the ring's loads would make the loads' completion
+// count ambiguous, and every tile would then wait for all loads in flight.
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(64, 1) void k_dec_cmp(Dims dm, DecArgs a, DecPlan pl) {
   using Tile = DecTile<T, DK, DV>;
   __shared__ __align__(16) T tile[Tile::elems];
+  __shared__ __align__(16) float sps[kDecTPC * 32 * 16];   // [tile][block][head], nb <= 32
+  __shared__ __align__(16) float stm[kDecTPC * 16];        // [tile][head]
   const int lane = threadIdx.x, c16 = lane & 15, qd = lane >> 4;
   const int wpb = pl.nc / pl.cpw;
   const int c0 = (blockIdx.x % wpb) * pl.cpw, bg = blockIdx.x / wpb;
   const int b = bg / dm.Hkv, g = bg % dm.Hkv;
   const int ncmp = dec_seq(dm, a, b).ncmp;
   const int k0 = c0 * kDecCK, k1 = min(k0 + pl.cpw * kDecCK, ncmp);
-  const int ntile = k1 > k0 ? (k1 - k0 + 31) / 32 : 0;
   const bool cv = c16 < dm.G;
   Frag8<T> qf[DK / 32];
   {
@@ -274,8 +285,18 @@ __global__ __launch_bounds__(64, 1) void k_dec_cmp(Dims dm, DecArgs a, DecPlan p
 #pragma unroll
   for (int dt = 0; dt < DV / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = kNegInf, lsum = 0.f;
-  // softmax state of chunk c: maximum, sum and unnormalised P V; then reset
-  auto finish_chunk = [&](int c) {
+  // softmax state of chunk c (nt tiles): maximum, sum and unnormalised P V,
+  // and the tiles' block scores and maxima; then reset
+  auto finish_chunk = [&](int c, int nt) {
+    if (nt > 0) {
+      __syncthreads();
+      const size_t tb = ((size_t)bg * pl.nc + c) * kDecTPC;
+      float* gps = a.w.part_ps + tb * pl.nb * 16;
+      for (int e = lane * 4; e < nt * pl.nb * 16; e += 256)
+        *reinterpret_cast<f32x4*>(gps + e) = *reinterpret_cast<const f32x4*>(sps + e);
+      for (int e = lane * 4; e < nt * 16; e += 256)
+        *reinterpret_cast<f32x4*>(a.w.part_tm + tb * 16 + e) = *reinterpret_cast<const f32x4*>(stm + e);
+    }
     float l = lsum + xor16f(lsum, lane);
     l += xor32f(l, lane);
     const size_t hb = ((size_t)bg * pl.nc + c) * 16 + c16;
@@ -292,11 +313,11 @@ __global__ __launch_bounds__(64, 1) void k_dec_cmp(Dims dm, DecArgs a, DecPlan p
     m = kNegInf;
     lsum = 0.f;
   };
-  auto compute = [&](int i) {
-    const int kt = k0 + 32 * i;
-    const int c = c0 + i / kDecTPC, ti = i % kDecTPC;
-    float* ps = a.w.part_ps + (((size_t)bg * pl.nc + c) * kDecTPC + ti) * pl.nb * 16;
-    float* tm = a.w.part_tm + (((size_t)bg * pl.nc + c) * kDecTPC + ti) * 16;
+  // tile ti of the chunk starting at key kc0
+  auto compute = [&](int kc0, int ti) {
+    const int kt = kc0 + 32 * ti;
+    float* ps = sps + ti * pl.nb * 16;
+    float* tm = stm + ti * 16;
     f32x4 s[2];
     Tile::scores(s, tile, qf, krow, qd);
     float v[8], mx = kNegInf;
@@ -307,21 +328,27 @@ __global__ __launch_bounds__(64, 1) void k_dec_cmp(Dims dm, DecArgs a, DecPlan p
     }
     mx = fmaxf(mx, xor16f(mx, lane));
     mx = fmaxf(mx, xor32f(mx, lane));
-    const float mn = fmaxf(m, mx);
-    const float mref = mn == kNegInf ? 0.f : mn;
-    const float alpha = fast_exp2(m - mref);
+    // Lazy rescaling: a head's reference m moves only when the tile's maximum
+    // exceeds it by more than 8 (so p <= 2^8), decided for the whole wave.
+    // The tile's probabilities and remapped scores are relative to m, which
+    // is what part_tm records.
+    if (__builtin_amdgcn_ballot_w64(mx > m + 8.f) != 0) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = mn == kNegInf ? 1.f : fast_exp2(m - mn);
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt) oacc[dt] *= alpha;
+      m = mn;
+    }
+    const float mref = m == kNegInf ? 0.f : m;
     float p[8], psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) { p[e] = fast_exp2(v[e] - mref); psum += p[e]; }
-    lsum = lsum * alpha + psum;
-    m = mn;
-    if (qd == 0) tm[c16] = mn;
+    lsum += psum;
+    if (qd == 0) tm[c16] = m;
     const Frag8<T> pf = to_frag<T>(p);
 #pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt) {
-      oacc[dt] *= alpha;
-      mma(oacc[dt], Tile::vfrag(tile, dt, c16, qd), pf);
-    }
+    for (int dt = 0; dt < DV / 16; ++dt) mma(oacc[dt], Tile::vfrag(tile, dt, c16, qd), pf);
     Frag8<T> phi = pf, plo;
     if constexpr (sizeof(T) == 2) split_bf16(p, phi, plo);
 #pragma unroll
@@ -333,29 +360,42 @@ __global__ __launch_bounds__(64, 1) void k_dec_cmp(Dims dm, DecArgs a, DecPlan p
       const int jj = jt * 16 + c16;
       if (jj < pl.nb) store4(ps + (size_t)jj * 16 + qd * 4, cr[0], cr[1], cr[2], cr[3]);
     }
-    if (ti == kDecTPC - 1 || i == ntile - 1) finish_chunk(c);
   };
-  // a ring of DEPTH tiles in flight in registers while the current one is
-  // computed from LDS (one wave per SIMD, most of its registers hold loads)
+  // Each chunk streams through a ring of DEPTH register tiles, computed from
+  // LDS one at a time (one wave per SIMD, most of its registers hold loads).
+  // Every full round of DEPTH tiles issues DEPTH tiles' loads (past the
+  // chunk's last tile they re-read it, which the L2 serves), so the wait for
+  // a tile covers that tile's loads only; the chunk's global stores follow
+  // its ring and are complete before the next chunk's loads are issued.
   constexpr int DEPTH = dec_depth<DK, DV>();
-  auto step = [&](Tile& cur, int i) {
-    __syncthreads();
-    cur.lstore(tile, lane);
-    __syncthreads();
-    if (i + DEPTH < ntile) cur.gload(kbase, vbase, kstride, vstride, k0 + 32 * (i + DEPTH), ncmp, lane);
-    compute(i);
-  };
   Tile ring[DEPTH];
+  for (int cc = 0; cc < pl.cpw; ++cc) {
+    const int c = c0 + cc, kc0 = k0 + cc * kDecCK;
+    const int nt = kc0 < k1 ? min(kDecTPC, (k1 - kc0 + 31) / 32) : 0;
+    if (nt > 0) {
+      auto tkey = [&](int ti) { return kc0 + 32 * min(ti, nt - 1); };
+      auto step = [&](Tile& cur, int ti, bool refill) {
+        __syncthreads();
+        cur.lstore(tile, lane);
+        __syncthreads();
+        if (refill) cur.gload(kbase, vbase, kstride, vstride, tkey(ti + DEPTH), ncmp, lane);
+        compute(kc0, ti);
+      };
 #pragma unroll
-  for (int r = 0; r < DEPTH; ++r)
-    if (r < ntile) ring[r].gload(kbase, vbase, kstride, vstride, k0 + 32 * r, ncmp, lane);
-  for (int i = 0; i < ntile; i += DEPTH) {
+      for (int r = 0; r < DEPTH; ++r) ring[r].gload(kbase, vbase, kstride, vstride, tkey(r), ncmp, lane);
+      int i0 = 0;
+      for (; i0 + DEPTH <= nt; i0 += DEPTH) {
 #pragma unroll
-    for (int r = 0; r < DEPTH; ++r)
-      if (i + r < ntile) step(ring[r], i + r);
+        for (int r = 0; r < DEPTH; ++r) step(ring[r], i0 + r, true);
+      }
+#pragma unroll
+      for (int r = 0; r < DEPTH; ++r)
+        if (i0 + r < nt) step(ring[r], i0 + r, false);
+    }
+    finish_chunk(c, nt);
+    // vmcnt(0): the chunk's stores are done before the next chunk's loads
+    __builtin_amdgcn_s_waitcnt(0x0F70);
   }
-  // chunks past the sequence's compressed blocks hold an empty state
-  for (int c = c0 + (ntile + kDecTPC - 1) / kDecTPC; c < c0 + pl.cpw; ++c) finish_chunk(c);
 }
 
 // Element i of an I/O tensor as float.
@@ -572,20 +612,23 @@ __global__ __launch_bounds__(64) void k_dec_sw(Dims dm, DecArgs a, DecPlan pl) {
     }
     mx = fmaxf(mx, xor16f(mx, lane));
     mx = fmaxf(mx, xor32f(mx, lane));
-    const float mn = fmaxf(m, mx);
-    const float mref = mn == kNegInf ? 0.f : mn;
-    const float alpha = fast_exp2(m - mref);
+    // lazy rescaling, as in k_dec_cmp: m is the reference of the state
+    if (__builtin_amdgcn_ballot_w64(mx > m + 8.f) != 0) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = mn == kNegInf ? 1.f : fast_exp2(m - mn);
+      ls *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DV / 16; ++dt) oacc[dt] *= alpha;
+      m = mn;
+    }
+    const float mref = m == kNegInf ? 0.f : m;
     float p[8], psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) { p[e] = fast_exp2(v[e] - mref); psum += p[e]; }
-    ls = ls * alpha + psum;
-    m = mn;
+    ls += psum;
     const Frag8<T> pf = to_frag<T>(p);
 #pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt) {
-      oacc[dt] *= alpha;
-      mma(oacc[dt], Tile::vfrag(tile, dt, c16, qd), pf);
-    }
+    for (int dt = 0; dt < DV / 16; ++dt) mma(oacc[dt], Tile::vfrag(tile, dt, c16, qd), pf);
   };
   // a ring of two tiles in flight (a 64-token block or aligned window chunk
   // is two tiles, so all of it is requested up front)

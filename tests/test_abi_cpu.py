@@ -63,6 +63,11 @@ def test_ctypes_mirror_matches_header_and_validation_runs_on_host():
     with pytest.raises(nsa.NSAError) as e:
         nsa.workspace_size(bad, _lib.NSA_OP_FWD_PREFILL)
     assert e.value.code == _lib.NSA_ERR_INVALID_ARG
+    # a key row of every KV head must stay below 2^24 elements
+    bad = nsa.Config(B=1, T=64, H_kv=(1 << 24) // 192 + 1, G=1, d_k=192, d_v=128)
+    with pytest.raises(nsa.NSAError) as e:
+        nsa.workspace_size(bad, _lib.NSA_OP_FWD_DECODE)
+    assert e.value.code == _lib.NSA_ERR_UNSUPPORTED
 
 
 def test_dense_bwd_rejects_fp32_wide_heads_before_touching_memory():
