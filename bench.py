@@ -190,7 +190,12 @@ def write_traffic(cal_fetch, cal_write, run_fetch, run_write, out_path, command)
 
 # ---------------------------------------------------------------- prefill leg
 
-def run_prefill(steps, warmup, wname="prefill_64k"):
+def run_prefill(steps, warmup, wname="prefill_64k", calibrate=False):
+    """Times `steps` prefill calls (per-stage HIP events inside each).  With
+    calibrate, three further calls (outside the timed steps) carry one more
+    event, behind which the library runs the selected branch's gather alone:
+    the walk of k_slc over the same index rows and tiles without its
+    arithmetic.  Returns (workload, wall s, stage ms, GPU ms, calibration)."""
     import torch
     import long_context_sparse_phi_amd as nsa
     from long_context_sparse_phi_amd import _lib
@@ -246,7 +251,17 @@ def run_prefill(steps, warmup, wname="prefill_64k"):
     stage_ms = [sum(ev.elapsed_ms(events[i][s], events[i][s + 1]) for i in range(steps)) / steps
                 for s in range(nst)]
     gpu_ms = sum(ev.elapsed_ms(events[i][0], events[i][nst]) for i in range(steps)) / steps
-    return w, wall, stage_ms, gpu_ms
+    cal = None
+    if calibrate:
+        ncal = 3
+        cev = [ev.create(nst + 2) for _ in range(ncal)]
+        for i in range(ncal):
+            step(cev[i])
+        torch.cuda.synchronize()
+        isel = [n for n, _ in PREFILL_STAGES].index("selected")
+        cal = {"selected_ms": sum(ev.elapsed_ms(e[isel], e[isel + 1]) for e in cev) / ncal,
+               "gather_only_ms": sum(ev.elapsed_ms(e[nst], e[nst + 1]) for e in cev) / ncal}
+    return w, wall, stage_ms, gpu_ms, cal
 
 
 def prefill_roofline(w, stage_ms):
@@ -267,7 +282,7 @@ def prefill_leg(steps, warmup, wname):
     """Another prefill workload measured like the headline one (tokens/s from
     the wall clock, stage times from HIP events) with its MFMA fraction on
     useful FLOPs and the time 50 % of the bf16 peak would take."""
-    w, wall, stage_ms, gpu_ms = run_prefill(steps, warmup, wname)
+    w, wall, stage_ms, gpu_ms, _ = run_prefill(steps, warmup, wname)
     ms = wall * 1e3 / steps
     fl = useful_flops(w)
     useful = fl["cmp"] + fl["slc"] + fl["win"] + fl["phi"] + fl["gate"]
@@ -280,15 +295,25 @@ def prefill_leg(steps, warmup, wname):
             "roofline": prefill_roofline(w, stage_ms)}
 
 
-def selected_gather(w, stage_ms):
+def selected_gather(w, stage_ms, cal=None):
     """The selected branch as a gather: K/V bytes of every (position, KV head)'s
     selected tokens (16 FLOP/B at G = 16, served mostly by L2 and MALL), per
-    second of the selected-attention stage."""
+    second of the selected-attention stage.  With the calibration of
+    run_prefill, the same bytes per second of the gather alone (k_slc's walk
+    over the same tiles without its arithmetic) are the ceiling this access
+    stream reaches on the device, and frac is k_slc's rate against it."""
     _, n_slc, _ = key_counts(w)
     nbytes = int(n_slc.sum()) * w.B * w.H_kv * (w.d_k + w.d_v) * 2
     i = [n for n, _ in PREFILL_STAGES].index("selected")
-    return {"kernel": "k_slc", "block_fetch_bytes": nbytes,
-            "TB_per_s": round(nbytes / (stage_ms[i] * 1e-3) / 1e12, 2)}
+    out = {"kernel": "k_slc", "block_fetch_bytes": nbytes,
+           "TB_per_s": round(nbytes / (stage_ms[i] * 1e-3) / 1e12, 2)}
+    if cal:
+        ceil = nbytes / (cal["gather_only_ms"] * 1e-3) / 1e12
+        rate = nbytes / (cal["selected_ms"] * 1e-3) / 1e12
+        out["gather_ceiling"] = {"kernel": "k_slc_gather", "gather_only_ms": round(cal["gather_only_ms"], 4),
+                                 "selected_ms": round(cal["selected_ms"], 4), "ceiling_TB_per_s": round(ceil, 2),
+                                 "k_slc_TB_per_s": round(rate, 2), "frac": round(rate / ceil, 4)}
+    return out
 
 
 # ---------------------------------------------------------------- decode leg
@@ -826,7 +851,7 @@ def main():
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
-    w, wall, stage_ms, gpu_ms = run_prefill(args.steps, args.warmup, args.workload)
+    w, wall, stage_ms, gpu_ms, cal = run_prefill(args.steps, args.warmup, args.workload, calibrate=True)
     ms_per_step = wall * 1e3 / args.steps
     fl = useful_flops(w)
     useful = fl["cmp"] + fl["slc"] + fl["win"] + fl["phi"] + fl["gate"]
@@ -845,7 +870,7 @@ def main():
         "mfma_frac_useful": round(useful / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "stages_ms": {name: round(ms, 4) for (name, _), ms in zip(PREFILL_STAGES, stage_ms)},
         "roofline": prefill_roofline(w, stage_ms),
-        "selected_gather": selected_gather(w, stage_ms),
+        "selected_gather": selected_gather(w, stage_ms, cal),
     }
     if not args.no_prefill_8k:
         out["prefill_8k"] = prefill_leg(args.steps, args.warmup, "prefill_8k")

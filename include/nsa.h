@@ -383,6 +383,11 @@ nsa_status nsa_layer_bwd(const nsa_params* p, const nsa_layer_bwd_args* a, void*
  *   and fragment-ordered K/V copies,
  *   4 compressed log-sum-exp, 5 compressed output + scores + top-n,
  *   6 selected attention, 7 window attention + gated combine.
+ *   With n_events >= stage count + 2, after the last stage the prefill also
+ *   runs a gather calibration, timed by events[9]: the selected branch's walk
+ *   over the same index rows and fragment-ordered K/V tiles without its
+ *   arithmetic (what the memory system takes to deliver that access stream).
+ *   It writes only internal workspace; the outputs are those of the stages.
  * Decode stages (3): 0 compressed-cache partial softmax states and scores,
  *   1 combine + group scores + top-n + gates, 2 selected/window attention +
  *   merge + gated combine.

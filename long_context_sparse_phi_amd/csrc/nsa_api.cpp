@@ -399,6 +399,13 @@ static nsa_status prefill_impl(const nsa_params* p, const nsa_prefill_args* a, v
     wa.o_win = o_win; wa.lse = lse + 2 * BTH; wa.o = a->o; wa.o_f32 = o_f32;
     if (sg.mark() || launch_win_combine(dm, wa, s) != hipSuccess) return NSA_ERR_HIP;
     if (sg.mark()) return NSA_ERR_HIP;
+    // measurement only: the selected branch's gather without its arithmetic,
+    // timed by one more event; its one word per wave goes to the V^T copy,
+    // which no stage reads any more
+    if (events && n_events >= kPrefillStages + 2) {
+      if (slc_gather_sink_bytes(dm) > (size_t)dm.B * dm.Hkv * dm.dv * dm.Tp * es) return NSA_ERR_INTERNAL;
+      if (launch_slc_gather(dm, sa, w.vt, s) != hipSuccess || sg.mark()) return NSA_ERR_HIP;
+    }
     return NSA_OK;
   } catch (...) {
     return NSA_ERR_INTERNAL;

@@ -133,39 +133,19 @@ struct SlcCursor {
 // two tiles at two waves per SIMD.
 template <typename T> constexpr int slc_depth() { return sizeof(T) == 2 ? 4 : 2; }
 
-template <typename T, int DK, int DV, typename OT>
-__global__ __launch_bounds__(256, slc_depth<T>() > 2 ? 1 : 2) void k_slc(Dims dm, SlcArgs a) {
+// The selection of position t for KV head g of sequence b, walked tile by
+// tile: every 32-key tile of its valid block slots goes through a ring of
+// register tiles and is handed to consume(tile, cursor) in load order.
+template <typename T, int DK, int DV, typename Consume>
+__device__ __forceinline__ void slc_walk(const Dims& dm, const T* kvf, const int* idx, int b, int g, int t,
+                                         int lane, Consume&& consume) {
   constexpr int NK = kvf_nk<DK, DV>(), NI = kvf_ni<DK, DV>();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int c16 = lane & 15, qd = lane >> 4;
-  const int ntiles = (dm.T + 3) / 4;
-  int unit, tile;
-  xcd_map(blockIdx.x, dm.B * dm.Hkv, ntiles, unit, tile);
-  const int b = unit / dm.Hkv, g = unit % dm.Hkv;
-  const int t = tile * 4 + wave;
-  if (t >= dm.T) return;
-  const int G = dm.G;
-  const bool cv = c16 < G;
-  const int hq = g * G + (cv ? c16 : 0);
-  const size_t qrow = (size_t)(b * dm.T + t) * dm.Hq + hq;
-  Frag8<T> qf[DK / 32];
-  {
-    const T* qp = (const T*)a.q + qrow * DK + qd * 8;
-#pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks) qf[ks] = cv ? load_frag_nt(qp + ks * 32) : zero_frag<T>();
-  }
   // the n block indices of this position, one per lane (n <= 32)
-  const int* ids = a.idx + ((size_t)(b * dm.T + t) * dm.Hkv + g) * dm.n;
+  const int* ids = idx + ((size_t)(b * dm.T + t) * dm.Hkv + g) * dm.n;
   const int myid = lane < dm.n ? ids[lane] : -1;
   const int nrow = wave_sel_row_len(myid, lane, dm.n, t, dm.ls);
-  const float sc2 = dm.scale * kLog2e;
-  float m = kNegInf, ls = 0.f;
-  f32x4 oacc[DV / 16];
-#pragma unroll
-  for (int dt = 0; dt < DV / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int nt = (dm.T + 31) / 32;
-  const T* kvt = (const T*)a.kvf + (size_t)(b * dm.Hkv + g) * nt * NI * 512 + lane * 8;
-
+  const T* kvt = kvf + (size_t)(b * dm.Hkv + g) * nt * NI * 512 + lane * 8;
   // first tile of block slot si at or after it, or si = n when none is left
   auto open_block = [&](SlcCursor& c) {
     for (; c.si < nrow; ++c.si) {
@@ -192,6 +172,66 @@ __global__ __launch_bounds__(256, slc_depth<T>() > 2 ? 1 : 2) void k_slc(Dims dm
 #pragma unroll
     for (int dt = 0; dt < DV / 16; ++dt) tl.v[dt] = load_frag(base + (NK + dt) * 512);
   };
+  // A ring of DEPTH register tiles, consumed in load order: after a slot's
+  // tile is computed the slot is refilled with the tile DEPTH positions
+  // further on, so DEPTH-1 tiles' loads are in flight during every compute.
+  constexpr int DEPTH = slc_depth<T>();
+  SlcTile<T, DK, DV> ring[DEPTH];
+  SlcCursor rc[DEPTH];
+  SlcCursor lc{0, 0, 0, 0};
+  open_block(lc);
+#pragma unroll
+  for (int r = 0; r < DEPTH; ++r) {
+    rc[r] = lc;
+    if (lc.si < dm.n) {
+      load_tile(ring[r], lc);
+      advance(lc);
+    }
+  }
+  bool more = rc[0].si < dm.n;
+  while (more) {
+#pragma unroll
+    for (int r = 0; r < DEPTH; ++r) {
+      if (more) {
+        __builtin_amdgcn_sched_barrier(0);
+        consume(ring[r], rc[r]);
+        __builtin_amdgcn_sched_barrier(0);
+        rc[r] = lc;
+        if (lc.si < dm.n) {
+          load_tile(ring[r], lc);
+          advance(lc);
+        }
+        more = rc[(r + 1) % DEPTH].si < dm.n;
+      }
+    }
+  }
+}
+
+template <typename T, int DK, int DV, typename OT>
+__global__ __launch_bounds__(256, slc_depth<T>() > 2 ? 1 : 2) void k_slc(Dims dm, SlcArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c16 = lane & 15, qd = lane >> 4;
+  const int ntiles = (dm.T + 3) / 4;
+  int unit, tile;
+  xcd_map(blockIdx.x, dm.B * dm.Hkv, ntiles, unit, tile);
+  const int b = unit / dm.Hkv, g = unit % dm.Hkv;
+  const int t = tile * 4 + wave;
+  if (t >= dm.T) return;
+  const int G = dm.G;
+  const bool cv = c16 < G;
+  const int hq = g * G + (cv ? c16 : 0);
+  const size_t qrow = (size_t)(b * dm.T + t) * dm.Hq + hq;
+  Frag8<T> qf[DK / 32];
+  {
+    const T* qp = (const T*)a.q + qrow * DK + qd * 8;
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) qf[ks] = cv ? load_frag_nt(qp + ks * 32) : zero_frag<T>();
+  }
+  const float sc2 = dm.scale * kLog2e;
+  float m = kNegInf, ls = 0.f;
+  f32x4 oacc[DV / 16];
+#pragma unroll
+  for (int dt = 0; dt < DV / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto compute_tile = [&](const SlcTile<T, DK, DV>& tl, const SlcCursor& c) {
     f32x4 sacc[2];
 #pragma unroll
@@ -247,39 +287,7 @@ __global__ __launch_bounds__(256, slc_depth<T>() > 2 ? 1 : 2) void k_slc(Dims dm
     }
   };
 
-  // A ring of DEPTH register tiles, consumed in load order: after a slot's
-  // tile is computed the slot is refilled with the tile DEPTH positions
-  // further on, so DEPTH-1 tiles' loads are in flight during every compute.
-  constexpr int DEPTH = slc_depth<T>();
-  SlcTile<T, DK, DV> ring[DEPTH];
-  SlcCursor rc[DEPTH];
-  SlcCursor lc{0, 0, 0, 0};
-  open_block(lc);
-#pragma unroll
-  for (int r = 0; r < DEPTH; ++r) {
-    rc[r] = lc;
-    if (lc.si < dm.n) {
-      load_tile(ring[r], lc);
-      advance(lc);
-    }
-  }
-  bool more = rc[0].si < dm.n;
-  while (more) {
-#pragma unroll
-    for (int r = 0; r < DEPTH; ++r) {
-      if (more) {
-        __builtin_amdgcn_sched_barrier(0);
-        compute_tile(ring[r], rc[r]);
-        __builtin_amdgcn_sched_barrier(0);
-        rc[r] = lc;
-        if (lc.si < dm.n) {
-          load_tile(ring[r], lc);
-          advance(lc);
-        }
-        more = rc[(r + 1) % DEPTH].si < dm.n;
-      }
-    }
-  }
+  slc_walk<T, DK, DV>(dm, (const T*)a.kvf, a.idx, b, g, t, lane, compute_tile);
   float tot = ls + xor16f(ls, lane);
   tot += xor32f(tot, lane);
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
@@ -298,6 +306,62 @@ static hipError_t slc_impl(const Dims& dm, const SlcArgs& a, hipStream_t s) {
   if (a.o_f32) k_slc<T, DK, DV, float><<<grid, 256, 0, s>>>(dm, a);
   else k_slc<T, DK, DV, T><<<grid, 256, 0, s>>>(dm, a);
   return hipGetLastError();
+}
+
+// Calibration of the selected branch's gather: the walk of k_slc over the
+// same index rows and fragment tiles, with the same launch shape, folding
+// every loaded register into one word per wave instead of the attention
+// arithmetic.  Its time is what the memory system takes to deliver exactly
+// that access stream.
+template <typename T>
+__device__ __forceinline__ unsigned fold_frag(const Frag8<T>& f) {
+  typedef unsigned int uv __attribute__((ext_vector_type(sizeof(Frag8<T>) / 4)));
+  const uv w = __builtin_bit_cast(uv, f);
+  unsigned x = 0;
+#pragma unroll
+  for (int e = 0; e < (int)(sizeof(Frag8<T>) / 4); ++e) x ^= w[e];
+  return x;
+}
+
+template <typename T, int DK, int DV>
+__global__ __launch_bounds__(256, slc_depth<T>() > 2 ? 1 : 2) void k_slc_gather(Dims dm, SlcArgs a, unsigned* sink) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ntiles = (dm.T + 3) / 4;
+  int unit, tile;
+  xcd_map(blockIdx.x, dm.B * dm.Hkv, ntiles, unit, tile);
+  const int b = unit / dm.Hkv, g = unit % dm.Hkv;
+  const int t = tile * 4 + wave;
+  if (t >= dm.T) return;
+  unsigned acc = 0;
+  slc_walk<T, DK, DV>(dm, (const T*)a.kvf, a.idx, b, g, t, lane,
+                      [&](const SlcTile<T, DK, DV>& tl, const SlcCursor&) {
+#pragma unroll
+                        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                          for (int ks = 0; ks < DK / 32; ++ks) acc ^= fold_frag(tl.k[sub][ks]);
+#pragma unroll
+                        for (int dt = 0; dt < DV / 16; ++dt) acc ^= fold_frag(tl.v[dt]);
+                      });
+  if (lane == 0) sink[(size_t)blockIdx.x * 4 + wave] = acc;
+}
+
+template <typename T, int DK, int DV>
+static hipError_t slc_gather_impl(const Dims& dm, const SlcArgs& a, unsigned* sink, hipStream_t s) {
+  k_slc_gather<T, DK, DV><<<((dm.T + 3) / 4) * dm.B * dm.Hkv, 256, 0, s>>>(dm, a, sink);
+  return hipGetLastError();
+}
+
+size_t slc_gather_sink_bytes(const Dims& dm) { return (size_t)((dm.T + 3) / 4) * dm.B * dm.Hkv * 4 * sizeof(unsigned); }
+
+hipError_t launch_slc_gather(const Dims& dm, const SlcArgs& a, void* sink, hipStream_t s) {
+  const bool bf = dm.io == IO_BF16;
+  unsigned* u = (unsigned*)sink;
+  if (dm.dk == 64 && dm.dv == 64) return bf ? slc_gather_impl<bf16, 64, 64>(dm, a, u, s) : slc_gather_impl<float, 64, 64>(dm, a, u, s);
+  if (dm.dk == 128 && dm.dv == 128)
+    return bf ? slc_gather_impl<bf16, 128, 128>(dm, a, u, s) : slc_gather_impl<float, 128, 128>(dm, a, u, s);
+  if (dm.dk == 192 && dm.dv == 128)
+    return bf ? slc_gather_impl<bf16, 192, 128>(dm, a, u, s) : slc_gather_impl<float, 192, 128>(dm, a, u, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_slc(const Dims& dm, const SlcArgs& a, hipStream_t s) {

@@ -102,6 +102,10 @@ struct SlcArgs {
   int o_f32;        // o is fp32 instead of the I/O type
 };
 hipError_t launch_slc(const Dims& dm, const SlcArgs& a, hipStream_t s);
+// Gather calibration: k_slc's walk over the same tiles without its arithmetic
+// (one word per wave into sink, slc_gather_sink_bytes).
+size_t slc_gather_sink_bytes(const Dims& dm);
+hipError_t launch_slc_gather(const Dims& dm, const SlcArgs& a, void* sink, hipStream_t s);
 
 // ---- sliding window + gated combine ----
 struct WinArgs {
