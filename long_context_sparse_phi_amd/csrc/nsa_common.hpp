@@ -255,6 +255,22 @@ __host__ __device__ __forceinline__ void xcd_map(int id, int units, int ntiles, 
   }
 }
 
+// Output tile (row tile mt, column tile nt) of GEMM workgroup lid in an
+// ncol x nrow grid.  Workgroups are dispatched to the 8 XCDs in turn: with a
+// multiple of 8 row tiles, XCD x takes row tiles x, x+8, ... and each one's
+// column tiles back to back, so the A rows of a row tile are fetched into one
+// L2 while its column tiles run; otherwise tiles go in launch order.
+__host__ __device__ __forceinline__ void gemm_tile_order(int lid, int ncol, int nrow, int& mt, int& nt) {
+  if (nrow % 8 == 0) {
+    const int x = lid & 7, k = lid >> 3;
+    mt = (k / ncol) * 8 + x;
+    nt = k % ncol;
+  } else {
+    mt = lid / ncol;
+    nt = lid % ncol;
+  }
+}
+
 // Task (group kg, segment seg) of workgroup id, for units x ngroup x nseg
 // tasks whose query rows start at kg*span + seg*seglen (plus a constant).
 // When span is a multiple of seglen, the tasks with equal a = R*kg + seg

@@ -155,7 +155,9 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs g, int kc, int nsplit, float*
   bf16* lds = (bf16*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, qd = lane >> 4;
-  const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
+  int mt, nt;
+  gemm_tile_order(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x, gridDim.y, mt, nt);
+  const int m0 = mt * kBM, n0 = nt * kBN;
   const int split = blockIdx.z % nsplit, bat = blockIdx.z / nsplit;
   const int kbeg = split * kc, kend = min(g.K, kbeg + kc);
   const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;

@@ -1,10 +1,11 @@
-"""CPU test of the workgroup -> task mappings of the backward's dK/dV kernels.
+"""CPU test of the workgroup -> task mappings of the dK/dV kernels and the GEMM.
 
 Every workgroup of a launch must receive a distinct task and every task a
 workgroup, or a key group's gradient segment is computed twice and another
 never.  The mappings are the kernels' own (nsa_common.hpp, compiled
-host-only): xcd_map for the window keys' (unit, key group) tasks and
-span_task_order for the compressed keys' (unit, key group, segment) tasks.
+host-only): xcd_map for the window keys' (unit, key group) tasks,
+span_task_order for the compressed keys' (unit, key group, segment) tasks and
+gemm_tile_order for the MFMA GEMM's output tiles.
 Beyond the bijection, the test checks the order the mapping exists for: on
 each XCD (workgroup id mod 8) one unit's tasks come in nondecreasing first
 query position.
@@ -29,7 +30,8 @@ int main() {
     for (int id = 0; id < n; ++id) {
       int u = -1, kg = -1, seg = 0;
       if (kind == 0) nsa::xcd_map(id, units, ngroup, u, kg);
-      else nsa::span_task_order(id, units, ngroup, nseg, span, seglen, u, kg, seg);
+      else if (kind == 1) nsa::span_task_order(id, units, ngroup, nseg, span, seglen, u, kg, seg);
+      else nsa::gemm_tile_order(id, ngroup, units, u, kg);   // row tile, column tile
       std::printf("%d %d %d\n", u, kg, seg);
     }
   }
@@ -96,3 +98,18 @@ def test_window_task_map_is_a_bijection(order_binary):
     res = run(order_binary, [(0, u, n, 1, 1, 1) for u, n in WIN_SHAPES])
     for (units, ntiles), tasks in zip(WIN_SHAPES, res):
         assert sorted((u, k) for u, k, _ in tasks) == [(u, k) for u in range(units) for k in range(ntiles)]
+
+
+# (row tiles, column tiles) of the layer and phi GEMMs and odd shapes
+GEMM_GRIDS = [(256, 64), (256, 2), (256, 4), (8, 1), (16, 3), (5, 7), (12, 2), (1, 1)]
+
+
+def test_gemm_tile_order_is_a_bijection_with_rows_grouped_per_xcd(order_binary):
+    res = run(order_binary, [(2, rows, cols, 1, 1, 1) for rows, cols in GEMM_GRIDS])
+    for (rows, cols), tasks in zip(GEMM_GRIDS, res):
+        assert sorted((m, n) for m, n, _ in tasks) == [(m, n) for m in range(rows) for n in range(cols)]
+        if rows % 8 == 0:
+            # every row tile is served by a single XCD (workgroup id mod 8)
+            xcd = {}
+            for wid, (m, n, _) in enumerate(tasks):
+                assert xcd.setdefault(m, wid % 8) == wid % 8
