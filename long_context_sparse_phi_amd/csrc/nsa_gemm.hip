@@ -10,8 +10,10 @@
 // four waves computes a 128 x 128 tile of C with v_mfma_f32_16x16x32_bf16,
 // each wave 64 x 64 (4 x 4 MFMA tiles), stepping k by 64.  Operand tiles are
 // staged in LDS as 128 rows of 64 k (128-byte rows, 16-byte chunk c of row r
-// stored at chunk c ^ ((r >> 1) & 7): neither the 16-lane fragment reads nor
-// the row stores conflict on banks), double-buffered: the next tile's global
+// stored at chunk c ^ (((r >> 1) ^ (r >> 4)) & 7): the 16 rows of a fragment
+// read reach 64 distinct banks, and so do the 4-byte stores of an operand
+// contiguous along m or n, which write element e ^ (g & 1) of row group g),
+// double-buffered: the next tile's global
 // loads are in flight in registers while the current one is multiplied.  An
 // fp32 operand is staged as two bf16 planes, hi = bf16(x) and lo = bf16(x -
 // hi), and enters the products as hi and lo (about 16 significant bits);
@@ -29,7 +31,7 @@ namespace {
 constexpr int kBM = 128, kBN = 128, kBK = 64;
 constexpr int kTileElems = 128 * kBK;          // one operand plane (bf16 elements)
 
-__device__ __forceinline__ int mm_off(int r, int c) { return r * kBK + ((c ^ ((r >> 1) & 7)) << 3); }
+__device__ __forceinline__ int mm_off(int r, int c) { return r * kBK + ((c ^ (((r >> 1) ^ (r >> 4)) & 7)) << 3); }
 
 // Eight consecutive elements of an operand, as loaded (bf16 or fp32); the
 // conversion to bf16 hi / lo parts waits until the LDS store, so that the
@@ -123,18 +125,21 @@ struct Stage {
         Frag8<bf16> hi[2], lo[2];
         split8<T>(raw[i][0], hi[0], lo[0]);
         split8<T>(raw[i][1], hi[1], lo[1]);
+        // store e writes row rgp*8 + (e ^ odd): rows of both parities in every
+        // store instruction, which with the swizzle spreads it over all banks
+        const bool odd = rgp & 1;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int r = rgp * 8 + e;
+          const int r = rgp * 8 + (e ^ (int)odd);
           const int o = mm_off(r, k >> 3) + (k & 7);
           bf16x2v v;
-          v[0] = hi[0].v[e];
-          v[1] = hi[1].v[e];
+          v[0] = odd ? hi[0].v[e ^ 1] : hi[0].v[e];
+          v[1] = odd ? hi[1].v[e ^ 1] : hi[1].v[e];
           *reinterpret_cast<bf16x2v*>(phi + o) = v;
           if constexpr (SPLIT) {
             bf16x2v w;
-            w[0] = lo[0].v[e];
-            w[1] = lo[1].v[e];
+            w[0] = odd ? lo[0].v[e ^ 1] : lo[0].v[e];
+            w[1] = odd ? lo[1].v[e ^ 1] : lo[1].v[e];
             *reinterpret_cast<bf16x2v*>(plo + o) = w;
           }
         }
