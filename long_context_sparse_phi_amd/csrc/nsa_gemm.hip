@@ -160,140 +160,148 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs g, int kc, int nsplit, float*
   bf16* lds = (bf16*)smem_raw;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, qd = lane >> 4;
-  int mt, nt;
-  gemm_tile_order(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x, gridDim.y, mt, nt);
-  const int m0 = mt * kBM, n0 = nt * kBN;
-  const int split = blockIdx.z % nsplit, bat = blockIdx.z / nsplit;
-  const int kbeg = split * kc, kend = min(g.K, kbeg + kc);
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-  const TA* A = (const TA*)g.A + bat * g.bsa;
-  const TB* B = (const TB*)g.B + bat * g.bsb;
-  // A rows are m (stride sam) and B rows are n (stride sbn); k-contiguous
-  // operands step rows by their row stride, the others step k by theirs
-  const long long as = AKC ? g.sam : g.sak, bs = BKC ? g.sbn : g.sbk;
-  Stage<TA, AKC> sa[2];
-  Stage<TB, BKC> sb[2];
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Persistent: the workgroups of a (batch, split) plane walk its output
+  // tiles with a stride of the grid width, which is a multiple of 8 when
+  // the grid is smaller than the tile count (so tile lid keeps XCD lid % 8).
+  const int ncol = (g.N + kBN - 1) / kBN, nrow = (g.M + kBM - 1) / kBM;
+  for (int lid = blockIdx.x; lid < ncol * nrow; lid += gridDim.x) {
+    int mt, nt;
+    gemm_tile_order(lid, ncol, nrow, mt, nt);
+    const int m0 = mt * kBM, n0 = nt * kBN;
+    const int split = blockIdx.z % nsplit, bat = blockIdx.z / nsplit;
+    const int kbeg = split * kc, kend = min(g.K, kbeg + kc);
+    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
+    const TA* A = (const TA*)g.A + bat * g.bsa;
+    const TB* B = (const TB*)g.B + bat * g.bsb;
+    // A rows are m (stride sam) and B rows are n (stride sbn); k-contiguous
+    // operands step rows by their row stride, the others step k by theirs
+    const long long as = AKC ? g.sam : g.sak, bs = BKC ? g.sbn : g.sbk;
+    Stage<TA, AKC> sa[2];
+    Stage<TB, BKC> sb[2];
+    f32x4 acc[4][4];
+  #pragma unroll
+    for (int i = 0; i < 4; ++i)
+  #pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = kend > kbeg ? (kend - kbeg + kBK - 1) / kBK : 0;
-  auto gload = [&](auto set, int t) {
-    constexpr int S = decltype(set)::value;
-    const int k0 = kbeg + t * kBK;
-    sa[S].load(A, as, m0, g.M, k0, kend, tid);
-    sb[S].load(B, bs, n0, g.N, k0, kend, tid);
-  };
-  auto lstore = [&](auto set) {
-    constexpr int S = decltype(set)::value;
-    bf16* base = lds + (size_t)S * BUF;
-    sa[S].store(base, base + kTileElems, tid);
-    sb[S].store(base + PA * kTileElems, base + (PA + 1) * kTileElems, tid);
-  };
-  auto compute = [&](auto set) {
-    constexpr int S = decltype(set)::value;
-    const bf16* base = lds + (size_t)S * BUF;
-    const bf16* ah = base;
-    const bf16* al = base + kTileElems;
-    const bf16* bh = base + PA * kTileElems;
-    const bf16* bl = bh + kTileElems;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      Frag8<bf16> af[4], bfr[4], alo[SA ? 4 : 1], blo[SB ? 4 : 1];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int o = mm_off(wm + i * 16 + c16, kk * 4 + qd);
-        af[i] = *reinterpret_cast<const Frag8<bf16>*>(ah + o);
-        if constexpr (SA) alo[i] = *reinterpret_cast<const Frag8<bf16>*>(al + o);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int o = mm_off(wn + j * 16 + c16, kk * 4 + qd);
-        bfr[j] = *reinterpret_cast<const Frag8<bf16>*>(bh + o);
-        if constexpr (SB) blo[j] = *reinterpret_cast<const Frag8<bf16>*>(bl + o);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
+    const int nk = kend > kbeg ? (kend - kbeg + kBK - 1) / kBK : 0;
+    auto gload = [&](auto set, int t) {
+      constexpr int S = decltype(set)::value;
+      const int k0 = kbeg + t * kBK;
+      sa[S].load(A, as, m0, g.M, k0, kend, tid);
+      sb[S].load(B, bs, n0, g.N, k0, kend, tid);
+    };
+    auto lstore = [&](auto set) {
+      constexpr int S = decltype(set)::value;
+      bf16* base = lds + (size_t)S * BUF;
+      sa[S].store(base, base + kTileElems, tid);
+      sb[S].store(base + PA * kTileElems, base + (PA + 1) * kTileElems, tid);
+    };
+    auto compute = [&](auto set) {
+      constexpr int S = decltype(set)::value;
+      const bf16* base = lds + (size_t)S * BUF;
+      const bf16* ah = base;
+      const bf16* al = base + kTileElems;
+      const bf16* bh = base + PA * kTileElems;
+      const bf16* bl = bh + kTileElems;
+  #pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        Frag8<bf16> af[4], bfr[4], alo[SA ? 4 : 1], blo[SB ? 4 : 1];
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int o = mm_off(wm + i * 16 + c16, kk * 4 + qd);
+          af[i] = *reinterpret_cast<const Frag8<bf16>*>(ah + o);
+          if constexpr (SA) alo[i] = *reinterpret_cast<const Frag8<bf16>*>(al + o);
+        }
+  #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          mma(acc[i][j], af[i], bfr[j]);
-          if constexpr (SA) mma(acc[i][j], alo[i], bfr[j]);
-          if constexpr (SB) mma(acc[i][j], af[i], blo[j]);
+          const int o = mm_off(wn + j * 16 + c16, kk * 4 + qd);
+          bfr[j] = *reinterpret_cast<const Frag8<bf16>*>(bh + o);
+          if constexpr (SB) blo[j] = *reinterpret_cast<const Frag8<bf16>*>(bl + o);
         }
-    }
-  };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  // step t: set S holds nothing pending (its tile t is in LDS buffer S), the
-  // other set holds tile t+1; tile t+2 is requested into set S
-  auto step = [&](auto set, int t) {
-    constexpr int S = decltype(set)::value;
-    using O = std::integral_constant<int, 1 - S>;
-    if (t + 2 < nk) gload(set, t + 2);
-    compute(set);
-    if (t + 1 < nk) lstore(O{});
+  #pragma unroll
+        for (int i = 0; i < 4; ++i)
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            mma(acc[i][j], af[i], bfr[j]);
+            if constexpr (SA) mma(acc[i][j], alo[i], bfr[j]);
+            if constexpr (SB) mma(acc[i][j], af[i], blo[j]);
+          }
+      }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    // step t: set S holds nothing pending (its tile t is in LDS buffer S), the
+    // other set holds tile t+1; tile t+2 is requested into set S
+    auto step = [&](auto set, int t) {
+      constexpr int S = decltype(set)::value;
+      using O = std::integral_constant<int, 1 - S>;
+      if (t + 2 < nk) gload(set, t + 2);
+      compute(set);
+      if (t + 1 < nk) lstore(O{});
+      __syncthreads();
+    };
+    if (nk > 0) gload(I0{}, 0);
+    if (nk > 1) gload(I1{}, 1);
+    if (nk > 0) lstore(I0{});
     __syncthreads();
-  };
-  if (nk > 0) gload(I0{}, 0);
-  if (nk > 1) gload(I1{}, 1);
-  if (nk > 0) lstore(I0{});
-  __syncthreads();
-  for (int t = 0; t < nk; t += 2) {
-    step(I0{}, t);
-    if (t + 1 < nk) step(I1{}, t + 1);
-  }
-  // C tile (or this split's partial tile) through LDS: each wave writes its
-  // 64 x 64 fp32 tile (row stride 68 floats: the four row groups of a write
-  // land on distinct banks), then stores it row by row, four consecutive
-  // values per lane.  The k loop's last barrier has freed the LDS.
-  float* ep = (float*)smem_raw + (size_t)wave * 64 * 68;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) ep[(i * 16 + qd * 4 + r) * 68 + j * 16 + c16] = acc[i][j][r];
-  __syncthreads();
-  const bool to_part = part != nullptr;
-  float* pz = to_part ? part + (size_t)blockIdx.z * g.M * g.N : nullptr;
-  const long long ld = to_part ? g.N : g.ldc;
-  const long long cb = to_part ? 0 : bat * g.bsc;
-  const bool c16b = !to_part && g.c_bf16;
-  const bool acc_c = !to_part && g.accumulate;
-  const uintptr_t cbase = to_part ? (uintptr_t)pz : (uintptr_t)g.C + (uintptr_t)cb * (c16b ? 2 : 4);
-  // four-value vectors need 16-byte (fp32) or 8-byte (bf16) aligned rows
-  const bool vec = ld % 4 == 0 && cbase % (c16b ? 8 : 16) == 0;
-  const int col = (lane & 15) * 4;
-  const int n = n0 + wn + col;
-#pragma unroll 4
-  for (int it = 0; it < 16; ++it) {
-    const int row = it * 4 + (lane >> 4);
-    const int m = m0 + wm + row;
-    if (m >= g.M || n >= g.N) continue;
-    const f32x4 v = *reinterpret_cast<const f32x4*>(ep + row * 68 + col);
-    const long long o = (long long)m * ld + n;
-    if (c16b) {
-      bf16* cp = (bf16*)g.C + cb + o;
-      if (vec && n + 4 <= g.N) {
-        store_col4(cp, (bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]);
-      } else {
-        for (int e = 0; e < 4 && n + e < g.N; ++e) cp[e] = (bf16)v[e];
-      }
-    } else {
-      float* cp = to_part ? pz + o : (float*)g.C + cb + o;
-      if (vec && n + 4 <= g.N) {
-        f32x4 w = v;
-        if (acc_c) {
-          const f32x4 old = *reinterpret_cast<const f32x4*>(cp);
-          w = f32x4{old[0] + v[0], old[1] + v[1], old[2] + v[2], old[3] + v[3]};
+    for (int t = 0; t < nk; t += 2) {
+      step(I0{}, t);
+      if (t + 1 < nk) step(I1{}, t + 1);
+    }
+    // C tile (or this split's partial tile) through LDS: each wave writes its
+    // 64 x 64 fp32 tile (row stride 68 floats: the four row groups of a write
+    // land on distinct banks), then stores it row by row, four consecutive
+    // values per lane.  The k loop's last barrier has freed the LDS.
+    float* ep = (float*)smem_raw + (size_t)wave * 64 * 68;
+  #pragma unroll
+    for (int i = 0; i < 4; ++i)
+  #pragma unroll
+      for (int j = 0; j < 4; ++j)
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) ep[(i * 16 + qd * 4 + r) * 68 + j * 16 + c16] = acc[i][j][r];
+    __syncthreads();
+    const bool to_part = part != nullptr;
+    float* pz = to_part ? part + (size_t)blockIdx.z * g.M * g.N : nullptr;
+    const long long ld = to_part ? g.N : g.ldc;
+    const long long cb = to_part ? 0 : bat * g.bsc;
+    const bool c16b = !to_part && g.c_bf16;
+    const bool acc_c = !to_part && g.accumulate;
+    const uintptr_t cbase = to_part ? (uintptr_t)pz : (uintptr_t)g.C + (uintptr_t)cb * (c16b ? 2 : 4);
+    // four-value vectors need 16-byte (fp32) or 8-byte (bf16) aligned rows
+    const bool vec = ld % 4 == 0 && cbase % (c16b ? 8 : 16) == 0;
+    const int col = (lane & 15) * 4;
+    const int n = n0 + wn + col;
+  #pragma unroll 4
+    for (int it = 0; it < 16; ++it) {
+      const int row = it * 4 + (lane >> 4);
+      const int m = m0 + wm + row;
+      if (m >= g.M || n >= g.N) continue;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(ep + row * 68 + col);
+      const long long o = (long long)m * ld + n;
+      if (c16b) {
+        bf16* cp = (bf16*)g.C + cb + o;
+        if (vec && n + 4 <= g.N) {
+          store_col4(cp, (bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]);
+        } else {
+          for (int e = 0; e < 4 && n + e < g.N; ++e) cp[e] = (bf16)v[e];
         }
-        *reinterpret_cast<f32x4*>(cp) = w;
       } else {
-        for (int e = 0; e < 4 && n + e < g.N; ++e) cp[e] = acc_c ? cp[e] + v[e] : v[e];
+        float* cp = to_part ? pz + o : (float*)g.C + cb + o;
+        if (vec && n + 4 <= g.N) {
+          f32x4 w = v;
+          if (acc_c) {
+            const f32x4 old = *reinterpret_cast<const f32x4*>(cp);
+            w = f32x4{old[0] + v[0], old[1] + v[1], old[2] + v[2], old[3] + v[3]};
+          }
+          *reinterpret_cast<f32x4*>(cp) = w;
+        } else {
+          for (int e = 0; e < 4 && n + e < g.N; ++e) cp[e] = acc_c ? cp[e] + v[e] : v[e];
+        }
       }
     }
+    // the epilogue's LDS reads are done before the next tile is staged
+    __syncthreads();
   }
 }
 
@@ -323,7 +331,11 @@ hipError_t mm_launch(const MmArgs& g, int nsplit, int kc, float* part, hipStream
   const size_t lds = pipe > epi ? pipe : epi;
   auto kfn = k_mm<TA, TB, AKC, BKC>;
   if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  dim3 grid((g.N + kBN - 1) / kBN, (g.M + kBM - 1) / kBM, nsplit * g.batch);
+  // two workgroups per CU over all planes; below the tile count the width is
+  // rounded down to a multiple of 8 (the XCD count)
+  const int ntile = ((g.N + kBN - 1) / kBN) * ((g.M + kBM - 1) / kBM), planes = nsplit * g.batch;
+  const int cap = 512 / planes > 8 ? (512 / planes) & ~7 : 8;
+  dim3 grid(ntile > cap ? cap : ntile, 1, planes);
   kfn<<<grid, 256, lds, s>>>(g, kc, nsplit, nsplit > 1 ? part : nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
