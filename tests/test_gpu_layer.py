@@ -84,3 +84,42 @@ def test_layer_equals_projections_plus_operator():
         assert torch.equal(f[key], op[key]), key
     y = (f["o"].float().reshape(w.B * w.T, -1) @ d["proj"]["w_o"].float()).reshape(f["y"].shape)
     assert_close(np64(f["y"]), np64(y), "y", atol=2e-2, rtol=1e-2)
+
+
+# Projection GEMMs with more output tiles than the persistent grid has
+# workgroups: 8192 tokens (64 row tiles, grouped per XCD) and 8002 tokens
+# (63 row tiles, launch order, a ragged last row tile).  The projections are
+# checked against their fp64 products: q, k, v = h W; y = o W_o on the GPU's
+# own o; dW_o = o^T dy.
+WIDE = {
+    "tokens_8192": W("train_16k", B=2, T=4096),
+    "tokens_8002_ragged": W("train_16k", B=2, T=4001),
+}
+
+
+@pytest.mark.parametrize("case", list(WIDE))
+def test_layer_projections_with_many_tiles(case):
+    import long_context_sparse_phi_amd as nsa
+    import oracle as O
+    w = WIDE[case]
+    cfg = nsa.config_from_workload(w)
+    inp = NI.make_layer_inputs(w, 2)
+    d = to_dev(inp)
+    print(f"[gpu] layer projections {case} B={w.B} T={w.T} C={w.gate_dim}", flush=True)
+    f = nsa.nsa_layer_fwd(cfg, d["h"], d["proj"], d["w_gate"], d["phi_k"], d["phi_v"])
+    g = nsa.nsa_layer_bwd(cfg, d["h"], d["proj"], d["w_gate"], d["phi_k"], d["phi_v"], f, d["dy"])
+    torch.cuda.synchronize()
+    a = NI.to_numpy64(inp)
+    p = oracle_params(w)
+    ntok = w.B * w.T
+    h = a["h"].reshape(ntok, w.gate_dim)
+    for n in ("q", "k", "v"):
+        ref = O.round_io(h @ a["proj"]["w_" + n], p.io)
+        assert_close(np64(f[n]).reshape(ref.shape), ref, n, atol=1e-2, rtol=1e-2)
+    o = np64(f["o"]).reshape(ntok, w.H_q * w.d_v)
+    ref_y = O.round_io(o @ a["proj"]["w_o"], p.io)
+    assert_close(np64(f["y"]).reshape(ref_y.shape), ref_y, "y", atol=1e-2, rtol=1e-2)
+    dy = a["dy"].reshape(ntok, w.gate_dim)
+    ref_dwo = o.T @ dy
+    err = assert_close(np64(g["dw_o"]), ref_dwo, "dw_o")
+    print(f"[gpu] {case} dw_o: max abs err {err:.3e}, max |ref| {np.abs(ref_dwo).max():.3e}")
