@@ -209,7 +209,9 @@ __device__ __forceinline__ void slc_walk(const Dims& dm, const T* kvf, const int
 
 template <typename T, int DK, int DV, typename OT>
 __global__ __launch_bounds__(256, slc_depth<T>() > 2 ? 1 : 2) void k_slc(Dims dm, SlcArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index (hence the position t and the walk's block bounds) is
+  // made visibly uniform, so the ring's control flow runs on scalar registers
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15, qd = lane >> 4;
   const int ntiles = (dm.T + 3) / 4;
   int unit, tile;
@@ -325,7 +327,7 @@ __device__ __forceinline__ unsigned fold_frag(const Frag8<T>& f) {
 
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(256, slc_depth<T>() > 2 ? 1 : 2) void k_slc_gather(Dims dm, SlcArgs a, unsigned* sink) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ntiles = (dm.T + 3) / 4;
   int unit, tile;
   xcd_map(blockIdx.x, dm.B * dm.Hkv, ntiles, unit, tile);

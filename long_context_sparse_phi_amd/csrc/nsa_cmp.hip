@@ -87,7 +87,15 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
   constexpr int NH = KT / 32;                               // 32-key halves per tile
   constexpr int NT = NW * 64;
   T* tiles = (T*)smem_raw;                                  // [2][TE]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // With bf16 tiles, the group size fixed at compile time and four waves,
+  // the wave index is read through readfirstlane so that the compiler knows
+  // it is uniform: everything derived from it (positions, loop bounds, tile
+  // addresses, LDS destinations) then lives in scalar registers.  The other
+  // instances keep the per-lane form, which is what fits their register
+  // budget.
+  constexpr bool kScalarWave = GS != 0 && NW == 4 && sizeof(T) == 2;
+  const int lane = threadIdx.x & 63;
+  const int wave = kScalarWave ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : threadIdx.x >> 6;
   const int c16 = lane & 15, qd = lane >> 4;
   const int G = GS ? GS : dm.G, PW = 16 * NCT / G, PWG = NW * PW;
   const int njt = NJ ? NJ : njt_arg;
@@ -198,25 +206,41 @@ __global__ __launch_bounds__(NW * 64, 2) void k_cmp(Dims dm, CmpArgs a, int nsel
     vlo[c] = VL::template off<DV>(row, c8);
   }
   static_assert(!kDMA || VL::kSwz, "direct loads need the unpadded V^T layout");
-  const int wave_pos = (threadIdx.x >> 6) * 64;      // first position of this wave's window
+  // the same offsets in bytes (a K tile spans KT rows of the key array, a V^T
+  // tile DV rows of the padded key axis; both far below 4 GiB)
+  uint32_t kgb[KCH], vgb[VCH > 0 ? VCH : 1];
+#pragma unroll
+  for (int c = 0; c < KCH; ++c) kgb[c] = (uint32_t)kgo[c] * (uint32_t)sizeof(T);
+#pragma unroll
+  for (int c = 0; c < VCH; ++c) vgb[c] = (uint32_t)vgo[c] * (uint32_t)sizeof(T);
+  const int wave_pos = wave * 64;      // first position of this wave's window
   // direct-to-LDS loads of the tile at key kt into buffer buf
+  // Full tiles address each chunk as the tile's (uniform) base plus the
+  // thread's fixed 32-bit byte offset, the scalar-base form of the load.
   auto dma = [&](int kt, int buf) {
     T* kdst = tiles + (size_t)buf * TE;
     T* vdst = kdst + (size_t)KT * DK;
     const T* kb = kcb + (size_t)kt * kstride;
-    const bool full = kt + KT <= dm.ncmp;
+    if (kt + KT <= dm.ncmp) {
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      // the last tile: keys past the end repeat the last key (never used)
-      const int over = full ? 0 : max(kt + krw[c] - (dm.ncmp - 1), 0);
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(kb + kgo[c] - over * kstride),
-                                       (void __attribute__((address_space(3)))*)(kdst + (NT * c + wave_pos) * 8), 16,
-                                       0, 0);
+      for (int c = 0; c < KCH; ++c)
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)((const char*)kb + kgb[c]),
+                                         (void __attribute__((address_space(3)))*)(kdst + (NT * c + wave_pos) * 8),
+                                         16, 0, 0);
+    } else {
+#pragma unroll
+      for (int c = 0; c < KCH; ++c) {
+        // the last tile: keys past the end repeat the last key (never used)
+        const int over = max(kt + krw[c] - (dm.ncmp - 1), 0);
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(kb + kgo[c] - over * kstride),
+                                         (void __attribute__((address_space(3)))*)(kdst + (NT * c + wave_pos) * 8),
+                                         16, 0, 0);
+      }
     }
-    const T* vb = vtb + kt;
+    const char* vb = (const char*)(vtb + kt);
 #pragma unroll
     for (int c = 0; c < VCH; ++c)
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(vb + vgo[c]),
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(vb + vgb[c]),
                                        (void __attribute__((address_space(3)))*)(vdst + (NT * c + wave_pos) * 8), 16,
                                        0, 0);
   };
