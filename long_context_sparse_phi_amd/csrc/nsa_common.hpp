@@ -336,25 +336,6 @@ __device__ __forceinline__ float colsum4(float v, int lane) {
   return v + xor32f(v, lane);
 }
 
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, ROWMASK, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, ROWMASK, 0xf, false);
-  return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
-}
-// Maximum of a 64-bit key over the wave (DPP prefix max ends in lane 63), broadcast.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
-  uint64_t t;
-  t = dpp_u64<0x111, 0xf>(k); k = t > k ? t : k;   // row_shr:1
-  t = dpp_u64<0x112, 0xf>(k); k = t > k ? t : k;   // row_shr:2
-  t = dpp_u64<0x114, 0xf>(k); k = t > k ? t : k;   // row_shr:4
-  t = dpp_u64<0x118, 0xf>(k); k = t > k ? t : k;   // row_shr:8
-  t = dpp_u64<0x142, 0xa>(k); k = t > k ? t : k;   // row_bcast:15
-  t = dpp_u64<0x143, 0xc>(k); k = t > k ? t : k;   // row_bcast:31
-  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)k, 63);
-  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 63);
-  return ((uint64_t)hi << 32) | lo;
-}
 // Wave-wide max (float) and min (int) by the same DPP pattern, broadcast.
 template <int CTRL, int ROWMASK>
 __device__ __forceinline__ float dpp_f32(float v, float ident) {
@@ -384,6 +365,16 @@ __device__ __forceinline__ int wave_min_i32(int v) {
   v = min(v, dpp_i32<0x142, 0xa>(v, id));
   v = min(v, dpp_i32<0x143, 0xc>(v, id));
   return __builtin_amdgcn_readlane(v, 63);
+}
+// Wave-wide maximum of an unsigned value (0 is the identity), broadcast.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)dpp_i32<0x111, 0xf>((int)v, 0));
+  v = max(v, (uint32_t)dpp_i32<0x112, 0xf>((int)v, 0));
+  v = max(v, (uint32_t)dpp_i32<0x114, 0xf>((int)v, 0));
+  v = max(v, (uint32_t)dpp_i32<0x118, 0xf>((int)v, 0));
+  v = max(v, (uint32_t)dpp_i32<0x142, 0xa>((int)v, 0));
+  v = max(v, (uint32_t)dpp_i32<0x143, 0xc>((int)v, 0));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 // Selection order: larger score first, the lower index winning a tie.  Each
 // lane offers its best (s, j); the wave's best is returned in every lane
@@ -445,33 +436,45 @@ __device__ inline void wave_topn(float* row, int t, int ls, int n, int* out, int
 
 // The same selection for R rows at once, each held in registers (rows of at
 // most 64*KV blocks): lane L owns blocks L + 64 i (i < KV), read from LDS
-// once, as 64-bit keys (score bits << 32 | ~j) so that one integer maximum
-// orders by score and then by lower index (scores are >= 0, so their bits
-// order like their values).  Each lane keeps its three best unselected keys,
-// sorted; a pick is one wave maximum per row (the R chains are independent),
-// after which the winning lane shifts its three keys and re-ranks its blocks
-// only when all three were taken.  t[r] < 0 marks an absent row.
+// once, as 32-bit keys: the score's bits plus one (scores are >= 0, so their
+// bits order like their values; 0 marks a block that is not a candidate).
+// Each lane keeps its three best unselected keys with their slots i, sorted
+// by key and, among equal keys, by lower slot (a lane's blocks ascend with i).
+// A pick is one 32-bit wave maximum per row (the R chains are independent);
+// the lanes holding it are found by ballot, and when several lanes hold equal
+// keys the lowest block index among them wins, as in the selection rule.  The
+// winning lane shifts its three keys and re-ranks its blocks only when all
+// three were taken.  t[r] < 0 marks an absent row.
 template <int KV, int R>
 __device__ inline void wave_topn_rows(const float* const* row, const int* t, int ls, int n, int* const* out,
                                       int lane) {
   int jc[R];
   bool live[R];
-  uint64_t key[R][KV];   // 0: not a candidate
+  uint32_t key[R][KV];
   uint32_t taken[R];     // bit i: block lane + 64 i selected
-  uint64_t k1[R], k2[R], k3[R];
+  uint32_t k1[R], k2[R], k3[R];
+  int i1[R], i2[R], i3[R];
   auto rank3 = [&](int r) {
-    uint64_t a = 0, b = 0, c = 0;
+    uint32_t a = 0, b = 0, c = 0;
+    int ia = 0, ib = 0, ic = 0;
 #pragma unroll
     for (int i = 0; i < KV; ++i) {
-      const uint64_t x = (taken[r] >> i) & 1u ? 0ull : key[r][i];
+      const uint32_t x = (taken[r] >> i) & 1u ? 0u : key[r][i];
+      // strict: of two equal keys the one met first (lower block) stays ahead
       const bool g1 = x > a, g2 = x > b, g3 = x > c;
       c = g2 ? b : (g3 ? x : c);
+      ic = g2 ? ib : (g3 ? i : ic);
       b = g1 ? a : (g2 ? x : b);
+      ib = g1 ? ia : (g2 ? i : ib);
       a = g1 ? x : a;
+      ia = g1 ? i : ia;
     }
     k1[r] = a;
     k2[r] = b;
     k3[r] = c;
+    i1[r] = ia;
+    i2[r] = ib;
+    i3[r] = ic;
   };
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -484,24 +487,33 @@ __device__ inline void wave_topn_rows(const float* const* row, const int* t, int
     for (int i = 0; i < KV; ++i) {
       const int j = lane + 64 * i;
       const bool cand = live[r] && j <= jc[r] && j != 0 && j != jc[r] - 1 && j != jc[r];
-      key[r][i] = cand ? ((uint64_t)(__float_as_uint(row[r][j]) & 0x7fffffffu) << 32) | (0xffffffffu - (uint32_t)j)
-                       : 0ull;
+      key[r][i] = cand ? (__float_as_uint(row[r][j]) & 0x7fffffffu) + 1u : 0u;
     }
     rank3(r);
   }
   for (int it = 0; it < n - 3; ++it) {
-    uint64_t b[R];
+    uint32_t best[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) b[r] = wave_max_u64(k1[r]);
+    for (int r = 0; r < R; ++r) best[r] = wave_max_u32(k1[r]);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      if (b[r] != 0ull && k1[r] == b[r]) {
-        const int j = (int)(0xffffffffu - (uint32_t)b[r]);
-        taken[r] |= 1u << (j >> 6);
+      if (best[r] == 0u) continue;   // no candidate left in this row
+      const uint64_t holders = __ballot(k1[r] == best[r]);
+      int win;
+      if (__popcll(holders) == 1) {
+        win = __builtin_ctzll(holders);
+      } else {
+        // equal keys in several lanes: the lowest block index j = lane + 64 i
+        win = wave_min_i32(k1[r] == best[r] ? lane + 64 * i1[r] : 0x7fffffff) & 63;
+      }
+      if (lane == win) {
+        taken[r] |= 1u << i1[r];
         k1[r] = k2[r];
+        i1[r] = i2[r];
         k2[r] = k3[r];
-        k3[r] = 0ull;
-        if (k1[r] == 0ull) rank3(r);
+        i2[r] = i3[r];
+        k3[r] = 0u;
+        if (k1[r] == 0u) rank3(r);
       }
     }
   }

@@ -72,6 +72,38 @@ def test_prefill_matches_oracle(case):
     print(f"[gpu] {case}: near-tie rows re-selected from GPU scores: {int(ref['retied'].sum())}")
 
 
+# All-zero queries give every visible compressed key the same probability, so
+# interior selection blocks receive exactly equal scores: the selection then
+# rests on the tie rule alone (the lower block index first), inside one lane's
+# blocks and across lanes.  Rows reach past 128 blocks (three blocks per lane).
+TIE_CASES = {
+    "zero_q_g16_bf16": W("prefill_8k", T=2100, H_kv=1, l=8, d=4, l_sel=16, n=8, w=24),
+    "zero_q_g4_fp32": W("tiny_fp32", T=2100, l=8, d=4, l_sel=16, n=6, w=24),
+}
+
+
+@pytest.mark.parametrize("case", list(TIE_CASES))
+def test_prefill_exact_score_ties(case):
+    import long_context_sparse_phi_amd as nsa
+    import oracle as O
+    w = TIE_CASES[case]
+    cfg = nsa.config_from_workload(w)
+    inp = NI.make_prefill_inputs(w, 0)
+    inp["q"] = torch.zeros_like(inp["q"])
+    d = to_dev(inp)
+    print(f"[gpu] prefill exact ties {case} T={w.T} G={w.G}", flush=True)
+    res = nsa.nsa_fwd_prefill(cfg, d["q"], d["k"], d["v"], d["x"], d["w_gate"], d["phi_k"], d["phi_v"],
+                              debug=True)
+    torch.cuda.synchronize()
+    a = NI.to_numpy64(inp)
+    ref = O.forward(oracle_params(w), a["q"], a["k"], a["v"], a["x"], a["w_gate"], a["phi_k"], a["phi_v"],
+                    tie_scores=np64(res["p_slc"]))
+    # the scores really tie: most rows past the first n blocks are re-selected
+    # from the GPU's scores, whose equal entries decide by index
+    assert ref["retied"].mean() > 0.5, float(ref["retied"].mean())
+    compare(w, inp, res, ref)
+
+
 def test_prefill_is_deterministic():
     w = CASES["mlp_d192_offsets"]
     _, r1 = run_gpu(w)
