@@ -82,6 +82,8 @@ class HipEvents:
         lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         lib.hipEventElapsedTime.restype = ctypes.c_int
         lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        lib.hipEventRecord.restype = ctypes.c_int
 
     def create(self, n):
         out = []
@@ -91,6 +93,10 @@ class HipEvents:
                 raise RuntimeError("hipEventCreate failed")
             out.append(e.value)
         return out
+
+    def record(self, e, stream):
+        if self.lib.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
@@ -191,11 +197,14 @@ def write_traffic(cal_fetch, cal_write, run_fetch, run_write, out_path, command)
 # ---------------------------------------------------------------- prefill leg
 
 def run_prefill(steps, warmup, wname="prefill_64k", calibrate=False):
-    """Times `steps` prefill calls (per-stage HIP events inside each).  With
-    calibrate, three further calls (outside the timed steps) carry one more
-    event, behind which the library runs the selected branch's gather alone:
-    the walk of k_slc over the same index rows and tiles without its
-    arithmetic.  Returns (workload, wall s, stage ms, GPU ms, calibration)."""
+    """Times `steps` calls of the plain entry point (wall clock, and a HIP
+    event pair around each call), then `steps` calls of the timed entry
+    point for the per-stage split (its events between stages are
+    instrumentation, so they stay out of the step time).  With calibrate,
+    three further calls carry one more event, behind which the library runs
+    the selected branch's gather alone: the walk of k_slc over the same index
+    rows and tiles without its arithmetic.  Returns (workload, wall s, stage
+    ms, GPU ms, calibration)."""
     import torch
     import long_context_sparse_phi_amd as nsa
     from long_context_sparse_phi_amd import _lib
@@ -243,14 +252,21 @@ def run_prefill(steps, warmup, wname="prefill_64k", calibrate=False):
         step()
     torch.cuda.synchronize()
     log(f"prefill timed {steps}")
+    pair = [ev.create(2) for _ in range(steps)]
     t0 = time.perf_counter()
+    for i in range(steps):
+        ev.record(pair[i][0], stream)
+        step()
+        ev.record(pair[i][1], stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = sum(ev.elapsed_ms(e0, e1) for e0, e1 in pair) / steps
+    log(f"prefill stage split {steps}")
     for i in range(steps):
         step(events[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     stage_ms = [sum(ev.elapsed_ms(events[i][s], events[i][s + 1]) for i in range(steps)) / steps
                 for s in range(nst)]
-    gpu_ms = sum(ev.elapsed_ms(events[i][0], events[i][nst]) for i in range(steps)) / steps
     cal = None
     if calibrate:
         ncal = 3
@@ -387,9 +403,10 @@ def run_decode(steps, warmup, wname="decode_64k"):
     ev = HipEvents(lib)
     events = [ev.create(nst + 1) for _ in range(steps)]
 
-    def step(evs=None):
-        flush.fill_(1.0)
-        flush.sum()
+    def step(evs=None, flush_first=True):
+        if flush_first:
+            flush.fill_(1.0)
+            flush.sum()
         if evs is None:
             st = lib.nsa_fwd_decode(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(), stream)
         else:
@@ -402,15 +419,27 @@ def run_decode(steps, warmup, wname="decode_64k"):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    # the step time: an event pair around each call of the plain entry point
+    # (after the cache flush); the stage split: further calls of the timed
+    # entry point, whose events between stages add a few microseconds each
     log(f"decode timed {steps}")
+    pair = [ev.create(2) for _ in range(steps)]
     t0 = time.perf_counter()
+    for i in range(steps):
+        flush.fill_(1.0)
+        flush.sum()
+        ev.record(pair[i][0], stream)
+        step(flush_first=False)
+        ev.record(pair[i][1], stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = sum(ev.elapsed_ms(e0, e1) for e0, e1 in pair) / steps
     for i in range(steps):
         step(events[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     stage_ms = [sum(ev.elapsed_ms(events[i][s], events[i][s + 1]) for i in range(steps)) / steps
                 for s in range(nst)]
-    step_ms = sum(ev.elapsed_ms(events[i][0], events[i][nst]) for i in range(steps)) / steps
+    staged_ms = sum(ev.elapsed_ms(events[i][0], events[i][nst]) for i in range(steps)) / steps
     append = run_append(w, cfg, d, kc, vc)
     nbytes = decode_bytes(w, idx)
     ncmp = (w.T - w.l) // w.d + 1
@@ -422,6 +451,7 @@ def run_decode(steps, warmup, wname="decode_64k"):
         "algorithmic_bytes": nbytes, "GB_per_s": round(nbytes / (step_ms * 1e-3) / 1e9, 1),
         "frac_hbm_peak": round(nbytes / (step_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "stages_us": {n: round(ms * 1e3, 2) for (n, _), ms in zip(DECODE_STAGES, stage_ms)},
+        "staged_call_us": round(staged_ms * 1e3, 2),
         "roofline": {"kernel": "k_dec_cmp", "stage": "cmp_partials", "bound": "hbm", "achieved": round(gbs, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                      "traffic": traffic_for("k_dec_cmp"),
@@ -546,9 +576,13 @@ def run_backward(steps, warmup, wname="train_16k"):
     log(f"backward timed {steps}")
     t0 = time.perf_counter()
     for i in range(steps):
-        step(events[i])
+        step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # the stage split from further calls of the timed entry point
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
     stage_ms = [sum(ev.elapsed_ms(events[i][s], events[i][s + 1]) for i in range(steps)) / steps
                 for s in range(nst)]
     # the training-mode forward that saves the fp32 branch outputs (and with

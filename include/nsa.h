@@ -172,7 +172,10 @@ typedef struct nsa_prefill_args {
  *   o_branch [3,B,Hq,dv] fp32.
  * k_win_cache, v_win_cache: the window branch's own caches [B,S,Hkv,dk|dv]
  *   when each branch has independent keys/values (both set or both NULL);
- *   k_cache, v_cache then serve the selected branch only. */
+ *   k_cache, v_cache then serve the selected branch only.
+ * A capacity S whose per-(sequence, KV head) score row and per-tile score
+ * partials do not fit one compute unit's 160 KB of LDS together returns
+ * NSA_ERR_UNSUPPORTED before anything is launched. */
 typedef struct nsa_decode_args {
   const void *q, *k_cache, *v_cache, *k_cmp_cache, *v_cmp_cache, *x, *w_gate;
   int32_t cmp_cache_cap;

@@ -19,6 +19,7 @@ bool cmp_out_fits(const Dims& dm);
 hipError_t launch_decode(const Dims& dm, const nsa_decode_args* a, void* ws, hipStream_t s,
                          void* const* events);
 size_t decode_ws_bytes(const Dims& dm);
+bool decode_fits(const Dims& dm);
 hipError_t decode_static_scratch(void** out);
 hipError_t launch_bwd(const Dims& dm, const nsa_bwd_args* a, void* ws, hipStream_t s, void* const* events);
 size_t bwd_ws_bytes(const Dims& dm);
@@ -509,6 +510,7 @@ static nsa_status decode_impl(const nsa_params* p, const nsa_decode_args* a, voi
     Dims dm;
     nsa_status st = make_dims(p, &dm);
     if (st != NSA_OK) return st;
+    if (!decode_fits(dm)) return NSA_ERR_UNSUPPORTED;
     if (!a) return NSA_ERR_INVALID_ARG;
     if (events && n_events < kDecodeStages + 1) return NSA_ERR_INVALID_ARG;
     const void* req[] = {a->q, a->k_cache, a->v_cache, a->x, a->w_gate, a->o};

@@ -242,13 +242,13 @@ struct DecTile {
 // Chunks of CK compressed keys, one pass with an online softmax: per tile the
 // scores, the running per-head maximum, P V, and the remapped block scores
 // relative to that running maximum, stored with it; the combine scales each
-// tile's scores by exp2(max - lse).  A wave streams pl.cpw consecutive chunks
-// of one (sequence, KV head) through a single ring of register tiles, so the
-// ring stays full across chunk boundaries; each chunk's softmax state is
-// written when its last tile is done.  The chunk's per-tile block scores
-// and reference maxima are kept in LDS and written with that state: global
-// stores issued between the ring's loads would make the loads' completion
-// count ambiguous, and every tile would then wait for all loads in flight.
+// tile's scores by exp2(max - lse).  A wave takes pl.cpw consecutive chunks
+// of one (sequence, KV head); each chunk streams through the ring of register
+// tiles and its softmax state is written when its last tile is done.  The
+// chunk's per-tile block scores and reference maxima are kept in LDS and
+// written with that state, after the chunk's loads: global stores issued
+// between the ring's loads would make the loads' completion count ambiguous,
+// and every tile would then wait for all loads in flight.
 template <typename T, int DK, int DV>
 __global__ __launch_bounds__(64, 1) void k_dec_cmp(Dims dm, DecArgs a, DecPlan pl) {
   using Tile = DecTile<T, DK, DV>;
@@ -403,13 +403,27 @@ __device__ __forceinline__ float load_elem(const void* p, int io, size_t i) {
   return io == IO_BF16 ? (float)((const bf16*)p)[i] : ((const float*)p)[i];
 }
 
-// Length of the combine's LDS score row (it later holds the gate input).
+// Length of the combine's LDS score row (it later holds the gate input, or the
+// 16 waves' partial gate sums).
 static __host__ __device__ int comb_row_len(const Dims& dm) {
-  return ((dm.nsel > dm.C ? dm.nsel : dm.C) + 3) & ~3;
+  const int n = dm.nsel > dm.C ? dm.nsel : dm.C;
+  return ((n > 16 * 64 ? n : 16 * 64) + 3) & ~3;
+}
+// Per-(tile, block offset) contributions to the block scores: [nc*TPC][nb].
+static __host__ __device__ int comb_contrib_len(const DecPlan& pl) { return (pl.nc * kDecTPC * pl.nb + 3) & ~3; }
+
+// Dynamic LDS of the combine: score row, chunk scales and states, top-n
+// scratch, gate MLP hidden layer, tile contributions.
+static size_t comb_lds_bytes(const Dims& dm, const DecPlan& pl) {
+  return (size_t)comb_row_len(dm) * 4 + (size_t)pl.nc * 16 * 4 * 3 + 16 * 4 + (256 + 16 + 4) * 4 + (size_t)dm.Cg * 4 +
+         (size_t)comb_contrib_len(pl) * 4;
 }
 
 // One workgroup (1024 threads) per (sequence, KV head): per-head log-sum-exp
-// of the compressed branch, per-chunk scales, block scores and top-n.
+// of the compressed branch, per-chunk scales, block scores, top-n and gates.
+// Global reads are laid out so that consecutive lanes read consecutive 16-byte
+// pieces: the gate weights of the group's heads are contiguous per input row,
+// and the per-tile score partials are read as one float4 per lane.
 __global__ __launch_bounds__(1024) void k_dec_combine(Dims dm, DecArgs a, DecPlan pl) {
   extern __shared__ float smem[];
   float* row = smem;                          // [nsel] block scores
@@ -419,20 +433,22 @@ __global__ __launch_bounds__(1024) void k_dec_combine(Dims dm, DecArgs a, DecPla
   float* lsl = mls + pl.nc * 16;              // [nc][16] chunk sums
   int* tsh = (int*)(lsl + pl.nc * 16);        // [256 + 16 + 4] top-n scratch
   float* ghid = (float*)(tsh + 256 + 16 + 4); // [Cg] gate MLP hidden layer
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float* ctb = ghid + dm.Cg;                  // [nc*TPC][nb] tile contributions
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bg = blockIdx.x, b = bg / dm.Hkv, g = bg % dm.Hkv;
-  const int G = dm.G;
+  const int G = dm.G, G3 = 3 * G;
   const DecSeq sq = dec_seq(dm, a, b);
-  // gate inputs of head `wave`, requested after the chunk states and used at the end
-  float gx[4], gw[4][3];
+  // linear gate: wave w takes the inputs k = k0 + w + 16 u (u < 16) and lane
+  // e < 3G output e of the group (head e / 3, branch e % 3), whose weights are
+  // contiguous in each input row; requested now, used at the end
+  float gx[16], gw[16];
   auto gate_load = [&](int k0) {
-    const int h = g * G + min(wave, G - 1);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int k = k0 + u * 64 + lane;
-      gx[u] = k < dm.C ? load_elem(a.x, dm.io, (size_t)b * dm.C + k) : 0.f;
-#pragma unroll
-      for (int c = 0; c < 3; ++c) gw[u][c] = k < dm.C ? load_elem(a.wg, dm.io, ((size_t)k * dm.Hq + h) * 3 + c) : 0.f;
+    for (int u = 0; u < 16; ++u) {
+      const int k = k0 + wave + 16 * u;
+      const bool ok = k < dm.C;
+      gx[u] = ok ? load_elem(a.x, dm.io, (size_t)b * dm.C + k) : 0.f;
+      gw[u] = ok && lane < G3 ? load_elem(a.wg, dm.io, (size_t)k * dm.Hq * 3 + g * G3 + lane) : 0.f;
     }
   };
   for (int i = tid; i < pl.nc * 16; i += 1024) {
@@ -467,45 +483,60 @@ __global__ __launch_bounds__(1024) void k_dec_combine(Dims dm, DecArgs a, DecPla
     scl[i] = v;
     a.w.cmp_scl[(size_t)bg * pl.nc * 16 + i] = v;
   }
-  __syncthreads();
-  // block scores: sum over heads of exact probabilities remapped to blocks
+  // block scores: sum over heads of exact probabilities remapped to blocks.
+  // Tile kg's partial for block offset jj (block kg * jstep + jj) is 16
+  // heads' remapped scores relative to the tile's running maxima; four lanes
+  // take its four float4s, scale them to probabilities and sum over heads.
   const int ntiles = (sq.ncmp + 31) / 32;
+  {
+    const float4* ps4 = reinterpret_cast<const float4*>(a.w.part_ps) + (size_t)bg * pl.nc * kDecTPC * pl.nb * 4;
+    const float4* tm4 = reinterpret_cast<const float4*>(a.w.part_tm) + (size_t)bg * pl.nc * kDecTPC * 4;
+    const int nf = ntiles * pl.nb * 4;
+    for (int f0 = 0; f0 < nf; f0 += 1024) {   // uniform trip count: the shuffles below need every lane
+      const int f = f0 + tid;
+      const int kg = f / (pl.nb * 4), h4 = f & 3;
+      float part = 0.f;
+      if (f < nf) {
+        const float4 x = ps4[f], m = tm4[kg * 4 + h4];
+        const float xs[4] = {x.x, x.y, x.z, x.w}, ms[4] = {m.x, m.y, m.z, m.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int h = h4 * 4 + e;
+          const float l2 = lse2[h];
+          if (h < G && ms[e] != kNegInf && l2 != kNegInf) part += xs[e] * fast_exp2(ms[e] - l2);
+        }
+      }
+      part += __shfl_xor(part, 1);
+      part += __shfl_xor(part, 2);
+      if (f < nf && h4 == 0) ctb[f >> 2] = part;
+    }
+  }
+  __syncthreads();
+  // each block adds the (at most a few) tiles that touch it, in tile order
   for (int j = tid; j < dm.nsel; j += 1024) {
     float val = 0.f;
     int klo = j - pl.nb + 1;
     klo = klo <= 0 ? 0 : (klo + pl.jstep - 1) / pl.jstep;
     const int khi = j < sq.nsel ? min(j / pl.jstep, ntiles - 1) : -1;
-    // at most a few tiles touch a block; all their loads are issued together
-    for (int kb = klo; kb <= khi; kb += 2) {
-      float x[2][16], mt[2][16];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int kg = kb + q;
-        if (kg > khi) break;
-        const int c = kg / kDecTPC, i = kg % kDecTPC, jj = j - kg * pl.jstep;
-        const float* ps = a.w.part_ps + ((((size_t)bg * pl.nc + c) * kDecTPC + i) * pl.nb + jj) * 16;
-        const float* tm = a.w.part_tm + (((size_t)bg * pl.nc + c) * kDecTPC + i) * 16;
-#pragma unroll
-        for (int h4 = 0; h4 < 16; h4 += 4) {
-          load4(ps + h4, x[q] + h4);
-          load4(tm + h4, mt[q] + h4);
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        if (kb + q > khi) break;
-#pragma unroll
-        for (int h = 0; h < 16; ++h)
-          if (h < G && mt[q][h] != kNegInf && lse2[h] != kNegInf) val += x[q][h] * fast_exp2(mt[q][h] - lse2[h]);
-      }
-    }
+    for (int kg = klo; kg <= khi; ++kg) val += ctb[kg * pl.nb + (j - kg * pl.jstep)];
     row[j] = val;
   }
   __syncthreads();
   if (a.p_slc)
     for (int j = tid; j < dm.nsel; j += 1024) a.p_slc[(size_t)bg * dm.nsel + j] = row[j];
-  __syncthreads();
-  block_topn<16>(row, sq.t, dm.ls, dm.n, a.w.idx + (size_t)bg * dm.n, tsh, tid);
+  int* out = a.w.idx + (size_t)bg * dm.n;
+  if (dm.nsel <= 1024) {
+    // rows of up to 1024 blocks: one wave, the row held in registers
+    if (wave == 0) {
+      const float* rows[1] = {row};
+      const int ts[1] = {sq.t};
+      int* outs[1] = {out};
+      wave_topn_rows<16, 1>(rows, ts, dm.ls, dm.n, outs, lane);
+    }
+  } else {
+    __syncthreads();
+    block_topn<16>(row, sq.t, dm.ls, dm.n, out, tsh, tid);
+  }
   // gate MLP: this sequence's hidden layer gelu(x w1 + b1) in LDS, then the
   // output layer by the waves below over it
   if (dm.Cg > 0) {
@@ -539,27 +570,22 @@ __global__ __launch_bounds__(1024) void k_dec_combine(Dims dm, DecArgs a, DecPla
     }
     return;
   }
-  // gates of the group's heads: wave h, lanes over the gate input, the three
-  // branches together; the first 256 inputs were loaded at the start
-  if (wave < G) {
-    const int h = g * G + wave;
-    float z[3] = {0.f, 0.f, 0.f};
-    for (int k0 = 0; k0 < dm.C; k0 += 4 * 64) {
-      if (k0 > 0) gate_load(k0);
+  // linear gate: per-wave partial sums over its inputs, then the 16 waves'
+  // sums in a fixed order (the score row's space holds them)
+  float z = 0.f;
+  for (int k0 = 0; k0 < dm.C; k0 += 16 * 16) {
+    if (k0 > 0) gate_load(k0);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < 16; ++u) z = fmaf(gx[u], gw[u], z);
+  }
+  __syncthreads();   // the top-n has read the row
+  row[wave * 64 + lane] = z;
+  __syncthreads();
+  if (tid < G3) {
+    float zz = 0.f;
 #pragma unroll
-        for (int c = 0; c < 3; ++c) z[c] += gx[u] * gw[u][c];
-    }
-#pragma unroll
-    for (int c = 0; c < 3; ++c) {
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) z[c] += __shfl_xor(z[c], off);
-    }
-    if (lane < 3) {
-      const float zz = lane == 0 ? z[0] : (lane == 1 ? z[1] : z[2]);
-      a.w.gates[((size_t)b * dm.Hq + h) * 3 + lane] = 1.f / (1.f + expf(-zz));
-    }
+    for (int w = 0; w < 16; ++w) zz += row[w * 64 + tid];
+    a.w.gates[((size_t)b * dm.Hq + g * G + tid / 3) * 3 + tid % 3] = 1.f / (1.f + expf(-zz));
   }
 }
 
@@ -750,8 +776,7 @@ static hipError_t decode_impl(const Dims& dm, const DecArgs& a, const DecPlan& p
   }
   if ((e = mark()) != hipSuccess) return e;
   {
-    const size_t lds = (size_t)comb_row_len(dm) * 4 + (size_t)pl.nc * 16 * 4 * 3 + 16 * 4 + (256 + 16 + 4) * 4 +
-                       (size_t)dm.Cg * 4;
+    const size_t lds = comb_lds_bytes(dm, pl);
     if (lds > 64 * 1024)
       hipFuncSetAttribute((const void*)k_dec_combine, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     k_dec_combine<<<BG, 1024, lds, s>>>(dm, a, pl);
@@ -763,6 +788,14 @@ static hipError_t decode_impl(const Dims& dm, const DecArgs& a, const DecPlan& p
   k_dec_merge<T, DV><<<BG * 8, 256, ((size_t)pl.ni * 2 + (size_t)pl.nc * 2 + 8) * sizeof(float), s>>>(dm, a, pl);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return mark();
+}
+
+// Whether the decode's workgroups fit a compute unit's 160 KB of LDS (the
+// combine's score row and per-tile contributions grow with the cache length).
+bool decode_fits(const Dims& dm) {
+  const DecPlan pl = dec_plan(dm);
+  const size_t merge = ((size_t)pl.ni * 2 + (size_t)pl.nc * 2 + 8) * sizeof(float);
+  return comb_lds_bytes(dm, pl) <= 160 * 1024 && merge <= 160 * 1024;
 }
 
 hipError_t launch_decode(const Dims& dm, const nsa_decode_args* args, void* ws, hipStream_t s,
