@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define NSA_ABI_VERSION 4
+#define NSA_ABI_VERSION 5
 
 typedef enum nsa_status {
   NSA_OK = 0,
@@ -201,6 +201,15 @@ typedef struct nsa_decode_args {
  * In/out: k_cache [B,S,Hkv,dk], v_cache [B,S,Hkv,dv] (S = p->seqlen),
  *   k_cmp_cache [B,cmp_cache_cap,Hkv,dk], v_cmp_cache [B,cmp_cache_cap,Hkv,dv]
  *   with cmp_cache_cap >= Ncmp(S) (NSA_ERR_INVALID_ARG otherwise).
+ * Independent keys/values per branch (optional, each quartet all set or all
+ *   NULL, else NSA_ERR_INVALID_ARG): k_slc_new [B,Hkv,dk], v_slc_new
+ *   [B,Hkv,dv] with k_slc_cache [B,S,Hkv,dk], v_slc_cache [B,S,Hkv,dv] are the
+ *   selected branch's token and caches, written as k_slc_cache[b, L] =
+ *   k_slc_new[b] (and v); the k_win_* / v_win_* quartet does the same for
+ *   the window branch.  k_cache, v_cache then hold the compressed branch's
+ *   keys and values, the rows phi reads.  A decode step over such caches takes
+ *   k_slc_cache, v_slc_cache as its k_cache, v_cache and k_win_cache,
+ *   v_win_cache as its window caches.
  * A sequence whose L is outside [0, S-1] (full cache) is left untouched.
  * No other cache row is written.  Workspace: NSA_OP_APPEND. */
 typedef struct nsa_append_args {
@@ -209,6 +218,10 @@ typedef struct nsa_append_args {
   void *k_cache, *v_cache, *k_cmp_cache, *v_cmp_cache;
   int32_t cmp_cache_cap;
   nsa_phi_weights phi_k, phi_v;
+  const void *k_slc_new, *v_slc_new;
+  void *k_slc_cache, *v_slc_cache;
+  const void *k_win_new, *v_win_new;
+  void *k_win_cache, *v_win_cache;
 } nsa_append_args;
 
 /* Backward with the selected blocks held fixed (no gradient through the

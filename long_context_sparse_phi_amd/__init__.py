@@ -298,10 +298,15 @@ def nsa_fwd_decode(cfg: Config, q, k_cache, v_cache, k_cmp_cache, v_cmp_cache, x
 
 
 def nsa_decode_append(cfg: Config, k_new, v_new, seq_lens, k_cache, v_cache, k_cmp_cache, v_cmp_cache,
-                      phi_k=None, phi_v=None, *, workspace: Optional[torch.Tensor] = None) -> None:
+                      phi_k=None, phi_v=None, *, kv_slc=None, kv_win=None,
+                      workspace: Optional[torch.Tensor] = None) -> None:
     """Append one token per sequence at slot seq_lens[b] of the raw caches
     (cfg.T = their capacity) and write the compressed block it completes, if
-    any.  seq_lens (int32 [B], device) is read only; advance it afterwards."""
+    any.  seq_lens (int32 [B], device) is read only; advance it afterwards.
+    With independent keys/values per branch, kv_slc and kv_win are each
+    (k_new, v_new, k_cache, v_cache) of the selected and window branches,
+    appended at the same slot; k_cache, v_cache are then the compressed
+    branch's (the rows phi reads)."""
     dev = k_cache.device
     dt = cfg.torch_dtype
     B, S, Hkv = cfg.B, cfg.T, cfg.H_kv
@@ -322,6 +327,16 @@ def nsa_decode_append(cfg: Config, k_new, v_new, seq_lens, k_cache, v_cache, k_c
     a.cmp_cache_cap = cap
     a.phi_k = _phi_struct(cfg, phi_k, cfg.d_k, dev)
     a.phi_v = _phi_struct(cfg, phi_v, cfg.d_v, dev)
+    for tag, quad in (("slc", kv_slc), ("win", kv_win)):
+        if quad is None:
+            continue
+        kn, vn, kc, vc = quad
+        _check(kn, f"k_{tag}_new", (B, Hkv, cfg.d_k), dt, dev)
+        _check(vn, f"v_{tag}_new", (B, Hkv, cfg.d_v), dt, dev)
+        _check(kc, f"k_{tag}_cache", (B, S, Hkv, cfg.d_k), dt, dev)
+        _check(vc, f"v_{tag}_cache", (B, S, Hkv, cfg.d_v), dt, dev)
+        for n, t in ((f"k_{tag}_new", kn), (f"v_{tag}_new", vn), (f"k_{tag}_cache", kc), (f"v_{tag}_cache", vc)):
+            setattr(a, n, t.data_ptr())
     ws = _workspace(cfg, NSA_OP_APPEND, dev, workspace)
     p = cfg.params()
     st = _lib.load().nsa_decode_append(ctypes.byref(p), ctypes.byref(a), ws.data_ptr(), ws.numel(),

@@ -18,7 +18,7 @@ NSA_BF16, NSA_FP32 = 0, 1
 NSA_PHI_MEANPOOL, NSA_PHI_MLP = 0, 1
 (NSA_OP_FWD_PREFILL, NSA_OP_FWD_DECODE, NSA_OP_BWD, NSA_OP_COMPRESS, NSA_OP_DENSE, NSA_OP_APPEND,
  NSA_OP_DENSE_BWD, NSA_OP_LAYER_FWD, NSA_OP_LAYER_BWD) = range(9)
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _vp = ctypes.c_void_p
 
@@ -68,7 +68,9 @@ class nsa_append_args(ctypes.Structure):
     _fields_ = ([(n, _vp) for n in ("k_new", "v_new", "seq_lens", "k_cache", "v_cache",
                                     "k_cmp_cache", "v_cmp_cache")] +
                 [("cmp_cache_cap", ctypes.c_int32)] +
-                [("phi_k", nsa_phi_weights), ("phi_v", nsa_phi_weights)])
+                [("phi_k", nsa_phi_weights), ("phi_v", nsa_phi_weights)] +
+                [(n, _vp) for n in ("k_slc_new", "v_slc_new", "k_slc_cache", "v_slc_cache",
+                                    "k_win_new", "v_win_new", "k_win_cache", "v_win_cache")])
 
 
 class nsa_bwd_args(ctypes.Structure):

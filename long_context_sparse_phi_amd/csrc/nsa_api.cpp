@@ -464,11 +464,17 @@ nsa_status nsa_decode_append(const nsa_params* p, const nsa_append_args* a, void
                         !aligned16(a->v_cmp_cache) || a->cmp_cache_cap < dm.ncmp))
       return NSA_ERR_INVALID_ARG;
     if (dm.hidden && (!phi_ok(a->phi_k) || !phi_ok(a->phi_v))) return NSA_ERR_INVALID_ARG;
+    bool slc = false, win = false;
+    if (!all_or_none({a->k_slc_new, a->v_slc_new, a->k_slc_cache, a->v_slc_cache}, &slc) ||
+        !all_or_none({a->k_win_new, a->v_win_new, a->k_win_cache, a->v_win_cache}, &win))
+      return NSA_ERR_INVALID_ARG;
     const size_t need = append_ws_bytes(dm);
     if (ws_bytes < need || (need && !ws) || !aligned16(ws)) return NSA_ERR_WORKSPACE;
     if ((st = check_device()) != NSA_OK) return st;
     AppendArgs aa;
     aa.lens = a->seq_lens; aa.kn = a->k_new; aa.vn = a->v_new; aa.kc = a->k_cache; aa.vc = a->v_cache;
+    aa.kn_slc = a->k_slc_new; aa.vn_slc = a->v_slc_new; aa.kc_slc = a->k_slc_cache; aa.vc_slc = a->v_slc_cache;
+    aa.kn_win = a->k_win_new; aa.vn_win = a->v_win_new; aa.kc_win = a->k_win_cache; aa.vc_win = a->v_win_cache;
     aa.kcmp = a->k_cmp_cache; aa.vcmp = a->v_cmp_cache; aa.cap = a->cmp_cache_cap;
     aa.phi_k = {a->phi_k.pe, a->phi_k.w1, a->phi_k.b1, a->phi_k.w2, a->phi_k.b2};
     aa.phi_v = {a->phi_v.pe, a->phi_v.w1, a->phi_v.b1, a->phi_v.w2, a->phi_v.b2};

@@ -33,14 +33,18 @@ __device__ __forceinline__ int append_block(int L, int l, int d) {
   return (n >= 0 && n % d == 0) ? n / d : -1;
 }
 
-// Raw caches: k_cache[b, L, g] = k_new[b, g] and the same for v.
+// Raw caches: k_cache[b, L, g] = k_new[b, g] and the same for v, for the
+// compressed branch's pair (blockIdx.y = 0) and, when given, the selected
+// (1) and window (2) branches' own pairs.
 template <typename T>
-__global__ __launch_bounds__(64) void k_append_store(Dims dm, const int* __restrict__ lens,
-                                                     const T* __restrict__ kn, const T* __restrict__ vn,
-                                                     T* __restrict__ kc, T* __restrict__ vc) {
+__global__ __launch_bounds__(64) void k_append_store(Dims dm, AppendArgs a) {
   const int bg = blockIdx.x, b = bg / dm.Hkv, g = bg % dm.Hkv;
-  const int L = append_slot(lens, b, dm.T);
-  if (L < 0) return;
+  const T* kn = (const T*)(blockIdx.y == 0 ? a.kn : blockIdx.y == 1 ? a.kn_slc : a.kn_win);
+  const T* vn = (const T*)(blockIdx.y == 0 ? a.vn : blockIdx.y == 1 ? a.vn_slc : a.vn_win);
+  T* kc = (T*)(blockIdx.y == 0 ? a.kc : blockIdx.y == 1 ? a.kc_slc : a.kc_win);
+  T* vc = (T*)(blockIdx.y == 0 ? a.vc : blockIdx.y == 1 ? a.vc_slc : a.vc_win);
+  const int L = append_slot(a.lens, b, dm.T);
+  if (L < 0 || !kc) return;
   const size_t rk = (size_t)(b * dm.T + L) * dm.Hkv + g;
   for (int e = threadIdx.x; e < dm.dk; e += 64) kc[rk * dm.dk + e] = kn[(size_t)bg * dm.dk + e];
   for (int e = threadIdx.x; e < dm.dv; e += 64) vc[rk * dm.dv + e] = vn[(size_t)bg * dm.dv + e];
@@ -176,7 +180,8 @@ static hipError_t append_phi(const Dims& dm, const AppendArgs& a, const T* x, co
 
 template <typename T, int DK, int DV>
 static hipError_t append_impl(const Dims& dm, const AppendArgs& a, hipStream_t s) {
-  k_append_store<T><<<dm.B * dm.Hkv, 64, 0, s>>>(dm, a.lens, (const T*)a.kn, (const T*)a.vn, (T*)a.kc, (T*)a.vc);
+  const unsigned pairs = a.kc_win ? 3 : (a.kc_slc ? 2 : 1);
+  k_append_store<T><<<dim3(dm.B * dm.Hkv, pairs), 64, 0, s>>>(dm, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (dm.ncmp == 0) return hipSuccess;   // no block can complete within the capacity

@@ -178,6 +178,10 @@ struct AppendArgs {
   const int* lens;         // [B]
   const void *kn, *vn;     // [B,Hkv,dk], [B,Hkv,dv]
   void *kc, *vc;           // [B,T,Hkv,dk], [B,T,Hkv,dv]
+  // optional per-branch pairs (selected, window): token and raw caches
+  // shaped as kn/vn and kc/vc, or all NULL
+  const void *kn_slc, *vn_slc, *kn_win, *vn_win;
+  void *kc_slc, *vc_slc, *kc_win, *vc_win;
   void *kcmp, *vcmp;       // [B,cap,Hkv,dk], [B,cap,Hkv,dv]
   int cap;
   AppendPhi phi_k, phi_v;

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_abi_version_and_status_strings(lib):
     lib.nsa_abi_version.restype = ctypes.c_int
-    assert lib.nsa_abi_version() == 4
+    assert lib.nsa_abi_version() == 5
     lib.nsa_status_str.restype = ctypes.c_char_p
     lib.nsa_status_str.argtypes = [ctypes.c_int]
     assert lib.nsa_status_str(0) == b"ok"
@@ -94,3 +94,27 @@ def test_gate_hidden_width_is_validated_on_host():
         with pytest.raises(nsa.NSAError) as e:
             nsa.workspace_size(bad, _lib.NSA_OP_FWD_PREFILL)
         assert e.value.code == _lib.NSA_ERR_INVALID_ARG
+
+
+def test_append_args_mirror_and_partial_branch_pairs_rejected_on_host():
+    """nsa_append_args keeps its earlier fields in place and adds the selected
+    and window branches' quartets; a quartet given in part is rejected before
+    any pointer is used (the pointers here are never valid)."""
+    import long_context_sparse_phi_amd as nsa
+    from long_context_sparse_phi_amd import _lib
+    A = _lib.nsa_append_args
+    ptr = ctypes.sizeof(ctypes.c_void_p)
+    assert A.k_new.offset == 0 and A.cmp_cache_cap.offset == 7 * ptr
+    assert A.k_slc_new.offset == A.phi_v.offset + ctypes.sizeof(_lib.nsa_phi_weights)
+    assert A.v_win_cache.offset == A.k_slc_new.offset + 7 * ptr
+    lib = _lib.load()
+    cfg = nsa.Config(B=1, T=256, H_kv=1, G=4, d_k=64, d_v=64, n=4, w=64, phi="mean")
+    p = cfg.params()
+    base = {n: 4096 for n in ("k_new", "v_new", "seq_lens", "k_cache", "v_cache", "k_cmp_cache", "v_cmp_cache")}
+    ws = nsa.workspace_size(cfg, _lib.NSA_OP_APPEND)
+    for partial in ({"k_slc_new": 4096}, {"k_slc_new": 4096, "v_slc_new": 4096, "k_slc_cache": 4096},
+                    {"v_win_cache": 4096}, {"k_win_new": 4096, "v_win_new": 4096, "k_win_cache": 4096}):
+        a = A(cmp_cache_cap=64, **base, **partial)
+        st = lib.nsa_decode_append(ctypes.byref(p), ctypes.byref(a), ctypes.c_void_p(4096), ws, None)
+        assert st == _lib.NSA_ERR_INVALID_ARG, partial
+

@@ -1,7 +1,8 @@
 """GPU parity with independent keys/values per branch (the compressed branch
 compresses k, v; the selected and window branches attend their own pairs),
 against the fp64 oracle: prefill forward, backward (per-branch key/value
-gradients) and decode (a separate window cache).  Same bars as the shared
+gradients), decode (a separate window cache) and decode-time cache maintenance
+of all three pairs.  Same bars as the shared
 case: indices bit-exact outside near ties, floats within 2e-2 absolute +
 1e-2 relative."""
 import numpy as np
@@ -122,3 +123,76 @@ def test_split_kv_decode_window_cache():
         assert_close(np64(res["lse"][c]), ref["lse"][c], f"lse_{name}")
         assert_close(np64(res["o_branch"][c]), ref["o_branch"][c], f"o_{name}")
     assert_close(np64(res["o"]), ref["o"], "o")
+
+
+def test_split_kv_append_then_decode():
+    """nsa_decode_append with the selected and window branches' own pairs:
+    all three raw caches hold exactly the appended tokens, the compressed
+    caches the oracle's phi over the compressed branch's rows, and a decode
+    over the maintained caches matches the oracle with three pairs."""
+    import long_context_sparse_phi_amd as nsa
+    import oracle as O
+    w = W("decode_64k", B=3, T=700, H_kv=2, bias_std=0.02)
+    S, B = w.T, w.B
+    p = oracle_params(w)
+    cfg = nsa.config_from_workload(w)
+    dt = cfg.torch_dtype
+    src = NI.make_decode_inputs(w, 6)                      # compressed branch's rows, q, x, weights
+    sel = NI.make_decode_inputs(w, 7)                      # selected branch's rows
+    win = NI.make_decode_inputs(w, 8)                      # window branch's rows
+    a = NI.to_numpy64(src)
+    ncmp = lambda L: O.n_cmp_visible(L - 1, w.l, w.d)
+    kc_ref = O.compress(a["k_cache"], a["phi_k"], p)
+    vc_ref = O.compress(a["v_cache"], a["phi_v"], p)
+    start, steps = [0, 45, S - 3], 40
+
+    def nan_beyond(t, n_of):
+        t = t.clone()
+        for b, L in enumerate(start):
+            t[b, n_of(L):] = float("nan")
+        return t.to(DEV)
+
+    full = {n: (d["k_cache"].to(DEV), d["v_cache"].to(DEV)) for n, d in (("cmp", src), ("slc", sel), ("win", win))}
+    caches = {n: (nan_beyond(d["k_cache"], lambda L: L), nan_beyond(d["v_cache"], lambda L: L))
+              for n, d in (("cmp", src), ("slc", sel), ("win", win))}
+    kcmp = nan_beyond(torch.from_numpy(kc_ref).to(dt), ncmp)
+    vcmp = nan_beyond(torch.from_numpy(vc_ref).to(dt), ncmp)
+    phi_k, phi_v = to_dev(src["phi_k"]), to_dev(src["phi_v"])
+    lens = torch.tensor(start, dtype=torch.int32, device=DEV)
+    rows = torch.arange(B, device=DEV)
+    print(f"[gpu] split-kv append: {steps} steps from {start}", flush=True)
+    for _ in range(steps):
+        slot = lens.clamp(max=S - 1).long()
+        new = {n: (full[n][0][rows, slot].contiguous(), full[n][1][rows, slot].contiguous()) for n in full}
+        nsa.nsa_decode_append(cfg, *new["cmp"], lens, *caches["cmp"], kcmp, vcmp, phi_k, phi_v,
+                              kv_slc=(*new["slc"], *caches["slc"]), kv_win=(*new["win"], *caches["win"]))
+        lens += 1
+    torch.cuda.synchronize()
+    final = [min(L + steps, S) for L in start]
+    for n in caches:
+        for b, L in enumerate(final):
+            for c in (0, 1):
+                assert torch.equal(caches[n][c][b, :L], full[n][c][b, :L]), (n, b, c)
+                assert torch.isnan(caches[n][c][b, L:]).all(), (n, b, c)
+    for b, L in enumerate(final):
+        m = ncmp(L)
+        assert_close(np64(kcmp[b, :m]), kc_ref[b, :m], f"k_cmp[{b}]")
+        assert_close(np64(vcmp[b, :m]), vc_ref[b, :m], f"v_cmp[{b}]")
+        assert torch.isnan(kcmp[b, m:].float()).all() and torch.isnan(vcmp[b, m:].float()).all()
+    res = nsa.nsa_fwd_decode(cfg, src["q"].to(DEV), *caches["slc"], kcmp, vcmp, src["x"].to(DEV),
+                             src["w_gate"].to(DEV), debug=True, seq_lens=lens, kv_win_cache=caches["win"])
+    torch.cuda.synchronize()
+    ks, vs = np64(sel["k_cache"]), np64(sel["v_cache"])
+    kw, vw = np64(win["k_cache"]), np64(win["v_cache"])
+    kcr, vcr = kc_ref.copy(), vc_ref.copy()
+    for b, L in enumerate(final):
+        ks[b, L:] = vs[b, L:] = kw[b, L:] = vw[b, L:] = np.nan
+        kcr[b, ncmp(L):] = vcr[b, ncmp(L):] = np.nan
+    ref = O.decode(p, a["q"], ks, vs, kcr, vcr, a["x"], a["w_gate"], tie_scores=np64(res["p_slc"]),
+                   seq_lens=final, kv_win_cache=(kw, vw))
+    assert np.array_equal(res["idx"].cpu().numpy().astype(np.int64), ref["idx"])
+    for c, name in enumerate(("cmp", "slc", "win")):
+        assert_close(np64(res["lse"][c]), ref["lse"][c], f"lse_{name}")
+        assert_close(np64(res["o_branch"][c]), ref["o_branch"][c], f"o_{name}")
+    assert_close(np64(res["o"]), ref["o"], "o")
+
