@@ -398,10 +398,6 @@ __global__ __launch_bounds__(64, 1) void k_dec_cmp(Dims dm, DecArgs a, DecPlan p
   }
 }
 
-// Element i of an I/O tensor as float.
-__device__ __forceinline__ float load_elem(const void* p, int io, size_t i) {
-  return io == IO_BF16 ? (float)((const bf16*)p)[i] : ((const float*)p)[i];
-}
 
 // Length of the combine's LDS score row (it later holds the gate input, or the
 // 16 waves' partial gate sums).
@@ -423,7 +419,10 @@ static size_t comb_lds_bytes(const Dims& dm, const DecPlan& pl) {
 // of the compressed branch, per-chunk scales, block scores, top-n and gates.
 // Global reads are laid out so that consecutive lanes read consecutive 16-byte
 // pieces: the gate weights of the group's heads are contiguous per input row,
-// and the per-tile score partials are read as one float4 per lane.
+// and the per-tile score partials are read as one float4 per lane.  Loads are
+// typed (T is the I/O element type) and unconditional (indices clamped, the
+// result selected), so a thread's loads are all in flight together.
+template <typename T>
 __global__ __launch_bounds__(1024) void k_dec_combine(Dims dm, DecArgs a, DecPlan pl) {
   extern __shared__ float smem[];
   float* row = smem;                          // [nsel] block scores
@@ -442,13 +441,15 @@ __global__ __launch_bounds__(1024) void k_dec_combine(Dims dm, DecArgs a, DecPla
   // e < 3G output e of the group (head e / 3, branch e % 3), whose weights are
   // contiguous in each input row; requested now, used at the end
   float gx[16], gw[16];
+  const T* xrow = (const T*)a.x + (size_t)b * dm.C;
+  const T* wcol = (const T*)a.wg + g * G3 + min(lane, G3 - 1);
   auto gate_load = [&](int k0) {
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
-      const int k = k0 + wave + 16 * u;
-      const bool ok = k < dm.C;
-      gx[u] = ok ? load_elem(a.x, dm.io, (size_t)b * dm.C + k) : 0.f;
-      gw[u] = ok && lane < G3 ? load_elem(a.wg, dm.io, (size_t)k * dm.Hq * 3 + g * G3 + lane) : 0.f;
+      const int k = k0 + wave + 16 * u, kk = min(k, dm.C - 1);
+      const float xv = to_f32(xrow[kk]), wv = to_f32(wcol[(size_t)kk * dm.Hq * 3]);
+      gx[u] = k < dm.C ? xv : 0.f;
+      gw[u] = k < dm.C && lane < G3 ? wv : 0.f;
     }
   };
   for (int i = tid; i < pl.nc * 16; i += 1024) {
@@ -531,23 +532,25 @@ __global__ __launch_bounds__(1024) void k_dec_combine(Dims dm, DecArgs a, DecPla
       const float* rows[1] = {row};
       const int ts[1] = {sq.t};
       int* outs[1] = {out};
-      wave_topn_rows<16, 1>(rows, ts, dm.ls, dm.n, outs, lane);
+      // inlined (a call would put the pointer arrays on a scratch stack)
+      [[clang::always_inline]] wave_topn_rows<16, 1>(rows, ts, dm.ls, dm.n, outs, lane);
     }
   } else {
     __syncthreads();
-    block_topn<16>(row, sq.t, dm.ls, dm.n, out, tsh, tid);
+    [[clang::always_inline]] block_topn<16>(row, sq.t, dm.ls, dm.n, out, tsh, tid);
   }
   // gate MLP: this sequence's hidden layer gelu(x w1 + b1) in LDS, then the
   // output layer by the waves below over it
   if (dm.Cg > 0) {
     float* gx_s = row;   // the gate input of sequence b (the score row is no longer needed)
     __syncthreads();
-    for (int k = tid; k < dm.C; k += 1024) gx_s[k] = load_elem(a.x, dm.io, (size_t)b * dm.C + k);
+    for (int k = tid; k < dm.C; k += 1024) gx_s[k] = to_f32(xrow[k]);
     __syncthreads();
     for (int j = tid; j < dm.Cg; j += 1024) {
-      float acc = load_elem(a.gmlp.b1, dm.io, j);
+      const T* w1 = (const T*)a.gmlp.w1 + j;
+      float acc = to_f32(((const T*)a.gmlp.b1)[j]);
 #pragma unroll 8
-      for (int k = 0; k < dm.C; ++k) acc = fmaf(gx_s[k], load_elem(a.gmlp.w1, dm.io, (size_t)k * dm.Cg + j), acc);
+      for (int k = 0; k < dm.C; ++k) acc = fmaf(gx_s[k], to_f32(w1[(size_t)k * dm.Cg]), acc);
       ghid[j] = 0.5f * acc * (1.f + erff(acc * 0.70710678118654752f));
     }
     __syncthreads();
@@ -556,7 +559,7 @@ __global__ __launch_bounds__(1024) void k_dec_combine(Dims dm, DecArgs a, DecPla
       float z[3] = {0.f, 0.f, 0.f};
       for (int k = lane; k < dm.Cg; k += 64) {
 #pragma unroll
-        for (int c = 0; c < 3; ++c) z[c] = fmaf(ghid[k], load_elem(a.wg, dm.io, ((size_t)k * dm.Hq + h) * 3 + c), z[c]);
+        for (int c = 0; c < 3; ++c) z[c] = fmaf(ghid[k], to_f32(((const T*)a.wg)[((size_t)k * dm.Hq + h) * 3 + c]), z[c]);
       }
 #pragma unroll
       for (int c = 0; c < 3; ++c) {
@@ -564,7 +567,7 @@ __global__ __launch_bounds__(1024) void k_dec_combine(Dims dm, DecArgs a, DecPla
         for (int off = 32; off >= 1; off >>= 1) z[c] += __shfl_xor(z[c], off);
       }
       if (lane < 3) {
-        const float zz = (lane == 0 ? z[0] : (lane == 1 ? z[1] : z[2])) + load_elem(a.gmlp.b2, dm.io, (size_t)h * 3 + lane);
+        const float zz = (lane == 0 ? z[0] : (lane == 1 ? z[1] : z[2])) + to_f32(((const T*)a.gmlp.b2)[(size_t)h * 3 + lane]);
         a.w.gates[((size_t)b * dm.Hq + h) * 3 + lane] = 1.f / (1.f + expf(-zz));
       }
     }
@@ -778,8 +781,8 @@ static hipError_t decode_impl(const Dims& dm, const DecArgs& a, const DecPlan& p
   {
     const size_t lds = comb_lds_bytes(dm, pl);
     if (lds > 64 * 1024)
-      hipFuncSetAttribute((const void*)k_dec_combine, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    k_dec_combine<<<BG, 1024, lds, s>>>(dm, a, pl);
+      hipFuncSetAttribute((const void*)k_dec_combine<T>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    k_dec_combine<T><<<BG, 1024, lds, s>>>(dm, a, pl);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = mark()) != hipSuccess) return e;
