@@ -1133,6 +1133,13 @@ __global__ __launch_bounds__(256) void k_reduce_slc(Dims dm, BwdArgs a) {
 // ---------------------------------------------------------------------------
 // Reverse index: positions that selected each block, ascending.
 // ---------------------------------------------------------------------------
+// The two per-chunk kernels below run one wave per workgroup: its LDS updates
+// happen in program order, so the chunk's positions follow one another
+// without a barrier, and the index rows of kRevBatch positions are requested
+// together (the position clamped to the chunk, the slot to the row, so every
+// load is in bounds and unconditional).
+constexpr int kRevBatch = 8;
+
 __global__ __launch_bounds__(64) void k_rev_hist(Dims dm, BwdArgs a) {
   extern __shared__ int hist[];
   const BwdPlan& pl = a.pl;
@@ -1141,49 +1148,83 @@ __global__ __launch_bounds__(64) void k_rev_hist(Dims dm, BwdArgs a) {
   for (int j = threadIdx.x; j < dm.nsel; j += 64) hist[j] = 0;
   __syncthreads();
   const int t0 = ch * kRevChunk, t1 = min(dm.T, t0 + kRevChunk);
-  const int lane = threadIdx.x;
-  for (int t = t0; t < t1; ++t) {
-    // only the row's usable prefix counts (distinct, causal blocks)
-    const int j = lane < dm.n ? a.idx[((size_t)(b * dm.T + t) * dm.Hkv + g) * dm.n + lane] : -1;
-    if (lane < wave_sel_row_len(j, lane, dm.n, t, dm.ls)) hist[j] += 1;
-    __syncthreads();
+  const int lane = threadIdx.x, slot = min(lane, dm.n - 1);
+  for (int tb = t0; tb < t1; tb += kRevBatch) {
+    int jv[kRevBatch];
+#pragma unroll
+    for (int u = 0; u < kRevBatch; ++u)
+      jv[u] = a.idx[((size_t)(b * dm.T + min(tb + u, t1 - 1)) * dm.Hkv + g) * dm.n + slot];
+#pragma unroll
+    for (int u = 0; u < kRevBatch; ++u) {
+      const int t = tb + u;
+      if (t >= t1) break;
+      // only the row's usable prefix counts (distinct, causal blocks)
+      const int j = lane < dm.n ? jv[u] : -1;
+      if (lane < wave_sel_row_len(j, lane, dm.n, t, dm.ls)) hist[j] += 1;
+    }
   }
+  __syncthreads();
   for (int j = threadIdx.x; j < dm.nsel; j += 64)
     a.w.hist[((size_t)bg * pl.nchunk + ch) * dm.nsel + j] = hist[j];
 }
 
+// Per (b, g): each block's count, first list entry and first segment slot,
+// the segment-slot -> (block, segment) table, and each chunk's offset into
+// every block's list.  The counts stay in LDS; every thread takes a
+// contiguous range of blocks, and an exclusive scan over the threads gives
+// each range its first entry and slot, so the table is in block order as a
+// serial walk would write it.  LDS: nsel + 512 ints.
 __global__ __launch_bounds__(256) void k_rev_scan(Dims dm, BwdArgs a) {
+  extern __shared__ int sc[];
   const BwdPlan& pl = a.pl;
-  const int bg = blockIdx.x;
-  for (int j = threadIdx.x; j < dm.nsel; j += 256) {
+  const int bg = blockIdx.x, tid = threadIdx.x;
+  int* cnt_s = sc;                                   // [nsel] counts, then list starts
+  int* part_c = sc + ((dm.nsel + 3) & ~3);           // [256] entries per thread range
+  int* part_s = part_c + 256;                        // [256] segments per thread range
+  for (int j = tid; j < dm.nsel; j += 256) {
     int tot = 0;
     for (int ch = 0; ch < pl.nchunk; ++ch) tot += a.w.hist[((size_t)bg * pl.nchunk + ch) * dm.nsel + j];
     a.w.cnt[(size_t)bg * dm.nsel + j] = tot;
+    cnt_s[j] = tot;
   }
   __syncthreads();
-  __shared__ int nslots;
+  const int per = (dm.nsel + 255) / 256;
+  const int j0 = min(tid * per, dm.nsel), j1 = min(j0 + per, dm.nsel);
+  int c = 0, ns = 0;
+  for (int j = j0; j < j1; ++j) {
+    c += cnt_s[j];
+    ns += (cnt_s[j] + kSegSlc - 1) / kSegSlc;
+  }
+  part_c[tid] = c;
+  part_s[tid] = ns;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {   // inclusive scan over the threads
+    const int vc = tid >= off ? part_c[tid - off] : 0, vs = tid >= off ? part_s[tid - off] : 0;
+    __syncthreads();
+    part_c[tid] += vc;
+    part_s[tid] += vs;
+    __syncthreads();
+  }
+  int run = part_c[tid] - c, srun = part_s[tid] - ns;
+  const int nslots = part_s[255];
   int* task = a.w.task + (size_t)bg * pl.max_slc_seg;
-  if (threadIdx.x == 0) {
-    int run = 0, srun = 0;
-    for (int j = 0; j < dm.nsel; ++j) {
-      const int c = a.w.cnt[(size_t)bg * dm.nsel + j];
-      const int ns = (c + kSegSlc - 1) / kSegSlc;
-      a.w.lstart[(size_t)bg * dm.nsel + j] = run;
-      a.w.segoff[(size_t)bg * dm.nsel + j] = srun;
-      for (int sg = 0; sg < ns; ++sg) task[srun + sg] = j * pl.nseg_slc + sg;
-      run += c;
-      srun += ns;
-    }
-    nslots = srun;
+  for (int j = j0; j < j1; ++j) {
+    const int cj = cnt_s[j], nsj = (cj + kSegSlc - 1) / kSegSlc;
+    a.w.lstart[(size_t)bg * dm.nsel + j] = run;
+    a.w.segoff[(size_t)bg * dm.nsel + j] = srun;
+    for (int sg = 0; sg < nsj; ++sg) task[srun + sg] = j * pl.nseg_slc + sg;
+    cnt_s[j] = run;   // this thread's own block: its list start from here on
+    run += cj;
+    srun += nsj;
   }
+  for (int i = nslots + tid; i < pl.max_slc_seg; i += 256) task[i] = -1;
   __syncthreads();
-  for (int i = nslots + threadIdx.x; i < pl.max_slc_seg; i += 256) task[i] = -1;
-  for (int j = threadIdx.x; j < dm.nsel; j += 256) {
-    int run = a.w.lstart[(size_t)bg * dm.nsel + j];
+  for (int j = tid; j < dm.nsel; j += 256) {
+    int r = cnt_s[j];
     for (int ch = 0; ch < pl.nchunk; ++ch) {
       const size_t o = ((size_t)bg * pl.nchunk + ch) * dm.nsel + j;
-      a.w.offc[o] = run;
-      run += a.w.hist[o];
+      a.w.offc[o] = r;
+      r += a.w.hist[o];
     }
   }
 }
@@ -1197,11 +1238,20 @@ __global__ __launch_bounds__(64) void k_rev_fill(Dims dm, BwdArgs a) {
   __syncthreads();
   int* list = a.w.list + (size_t)bg * dm.T * dm.n;
   const int t0 = ch * kRevChunk, t1 = min(dm.T, t0 + kRevChunk);
-  const int lane = threadIdx.x;
-  for (int t = t0; t < t1; ++t) {
-    const int j = lane < dm.n ? a.idx[((size_t)(b * dm.T + t) * dm.Hkv + g) * dm.n + lane] : -1;
-    if (lane < wave_sel_row_len(j, lane, dm.n, t, dm.ls)) list[cur[j]++] = t;
-    __syncthreads();
+  const int lane = threadIdx.x, slot = min(lane, dm.n - 1);
+  for (int tb = t0; tb < t1; tb += kRevBatch) {
+    int jv[kRevBatch];
+#pragma unroll
+    for (int u = 0; u < kRevBatch; ++u)
+      jv[u] = a.idx[((size_t)(b * dm.T + min(tb + u, t1 - 1)) * dm.Hkv + g) * dm.n + slot];
+#pragma unroll
+    for (int u = 0; u < kRevBatch; ++u) {
+      const int t = tb + u;
+      if (t >= t1) break;
+      const int j = lane < dm.n ? jv[u] : -1;
+      // positions enter each block's list in increasing order
+      if (lane < wave_sel_row_len(j, lane, dm.n, t, dm.ls)) list[cur[j]++] = t;
+    }
   }
 }
 
@@ -1518,7 +1568,11 @@ static hipError_t bwd_impl(const Dims& dm, const nsa_bwd_args* args, BwdArgs& a,
   // stage 5: selected blocks (adds into dks, dvs)
   if ((e = mark()) != hipSuccess) return e;
   k_rev_hist<<<BG * pl.nchunk, 64, dm.nsel * sizeof(int), s>>>(dm, a);
-  k_rev_scan<<<BG, 256, 0, s>>>(dm, a);
+  {
+    const size_t lds = ((size_t)((dm.nsel + 3) & ~3) + 512) * sizeof(int);
+    if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)k_rev_scan, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    k_rev_scan<<<BG, 256, lds, s>>>(dm, a);
+  }
   k_rev_fill<<<BG * pl.nchunk, 64, dm.nsel * sizeof(int), s>>>(dm, a);
   k_bwd_kv<T, DK, DV, KV_SLC><<<BG * pl.max_slc_seg * pl.nkc_slc, 256, klds, s>>>(dm, a);
   {
