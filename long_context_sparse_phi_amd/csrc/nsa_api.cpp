@@ -228,7 +228,9 @@ size_t plan_layer_bwd(const Dims& dm, void* ws, LayerBwdWs* w) {
   w->dq = (float*)c.take(ntok * dm.Hq * dm.dk * 4);
   w->dk = (float*)c.take(ntok * dm.Hkv * dm.dk * 4);
   w->dv = (float*)c.take(ntok * dm.Hkv * dm.dv * 4);
-  const size_t wmax = (size_t)dm.C * (dm.Hq * dm.dk > dm.Hq * dm.dv ? dm.Hq * dm.dk : dm.Hq * dm.dv);
+  // partials of dW_o [Hq*dv, C] or of dW_q|dW_k|dW_v [C, Hq*dk + Hkv*(dk + dv)]
+  const size_t nqkv = (size_t)dm.Hq * dm.dk + (size_t)dm.Hkv * (dm.dk + dm.dv);
+  const size_t wmax = (size_t)dm.C * (nqkv > (size_t)dm.Hq * dm.dv ? nqkv : (size_t)dm.Hq * dm.dv);
   w->part = (float*)c.take(wmax * (dm.io == IO_BF16 ? kLayerSplit : kGemmMaxSplit) * 4);
   return c.off;
 }
@@ -241,6 +243,24 @@ hipError_t layer_gemm(const Dims& dm, const MmArgs& g, bool a_f32, bool b_f32, b
   if (dm.io == IO_BF16) return mm(g, a_f32, b_f32, split ? mm_split(g, kLayerSplit) : 1, part, s);
   const Gemm e{g.M, g.N, g.K, g.A, g.sam, g.sak, g.B, g.sbk, g.sbn, (float*)g.C, g.ldc, g.accumulate};
   return gemm_exact(e, true, true, split ? part : nullptr, s);
+}
+
+// The q|k|v products of the layer as one launch over three segments (see
+// MmArgs).  With fp32 I/O the exact fp32 GEMM runs once per segment.
+hipError_t layer_gemm_seg(const Dims& dm, const MmArgs& g, bool a_f32, bool b_f32, bool split, float* part,
+                          hipStream_t s) {
+  if (dm.io == IO_BF16) return mm(g, a_f32, b_f32, split ? mm_split(g, kLayerSplit) : 1, part, s);
+  for (int i = 0; i < g.nseg; ++i) {
+    const MmSeg& q = g.seg[i];
+    const int end = i + 1 < g.nseg ? g.seg[i + 1].off : (g.seg_k ? g.K : g.N);
+    const Gemm e = g.seg_k ? Gemm{g.M, g.N, end - q.off, q.A, q.sam, q.sak, q.B, q.sbk, q.sbn, (float*)g.C, g.ldc,
+                                  g.accumulate || i > 0}
+                           : Gemm{g.M, end - q.off, g.K, g.A, g.sam, g.sak, q.B, q.sbk, q.sbn, (float*)q.C, q.ldc,
+                                  g.accumulate};
+    const hipError_t r = gemm_exact(e, true, true, split ? part : nullptr, s);
+    if (r != hipSuccess) return r;
+  }
+  return hipSuccess;
 }
 
 // The layer's GEMMs take 16-byte rows: with bf16 I/O the width C must be a
@@ -628,14 +648,13 @@ nsa_status nsa_layer_fwd(const nsa_params* p, const nsa_layer_args* a, void* ws,
     const int ntok = dm.B * dm.T, C = dm.C, bo = dm.io == IO_BF16;
     const int nq = dm.Hq * dm.dk, nk = dm.Hkv * dm.dk, nv = dm.Hkv * dm.dv, no = dm.Hq * dm.dv;
     hipStream_t s = (hipStream_t)stream;
-    // q = h w_q, k = h w_k, v = h w_v (outputs in the I/O type)
-    const MmArgs gq{ntok, nq, C, a->h, C, 1, a->w_q, nq, 1, a->q, nq, 0, bo};
-    const MmArgs gk{ntok, nk, C, a->h, C, 1, a->w_k, nk, 1, a->k, nk, 0, bo};
-    const MmArgs gv{ntok, nv, C, a->h, C, 1, a->w_v, nv, 1, a->v, nv, 0, bo};
-    if (layer_gemm(dm, gq, false, false, false, nullptr, s) != hipSuccess ||
-        layer_gemm(dm, gk, false, false, false, nullptr, s) != hipSuccess ||
-        layer_gemm(dm, gv, false, false, false, nullptr, s) != hipSuccess)
-      return NSA_ERR_HIP;
+    // [q | k | v] = h [w_q | w_k | w_v] in one launch (outputs in the I/O type)
+    MmArgs gx{ntok, nq + nk + nv, C, a->h, C, 1, nullptr, nq, 1, nullptr, 0, 0, bo};
+    gx.nseg = 3;
+    gx.seg[0] = MmSeg{nullptr, 0, 0, a->w_q, nq, 1, a->q, nq, 0};
+    gx.seg[1] = MmSeg{nullptr, 0, 0, a->w_k, nk, 1, a->k, nk, nq};
+    gx.seg[2] = MmSeg{nullptr, 0, 0, a->w_v, nv, 1, a->v, nv, nq + nk};
+    if (layer_gemm_seg(dm, gx, false, false, false, nullptr, s) != hipSuccess) return NSA_ERR_HIP;
     if ((st = prefill_impl(p, &pa, ws, ws_bytes, stream, nullptr, 0)) != NSA_OK) return st;
     // y = o w_o
     const MmArgs gy{ntok, C, no, a->o, no, 1, a->w_o, C, 1, a->y, C, 0, bo};
@@ -680,16 +699,24 @@ nsa_status nsa_layer_bwd(const nsa_params* p, const nsa_layer_bwd_args* a, void*
       return NSA_ERR_HIP;
     // the operator's backward; its dx (the gate path) initialises dh
     if ((st = bwd_impl(p, &ba, w.op_ws, op_bytes, stream, nullptr, 0)) != NSA_OK) return st;
-    struct Proj { const void* w; const float* d; int n; void* dw; };
-    const Proj pr[3] = {{a->w_q, w.dq, nq, a->dw_q}, {a->w_k, w.dk, nk, a->dw_k}, {a->w_v, w.dv, nv, a->dw_v}};
-    for (const Proj& j : pr) {
-      // dW = h^T d (fp32); dh += d W^T (d is fp32)
-      const MmArgs gw{C, j.n, ntok, a->h, 1, C, j.d, j.n, 1, j.dw, j.n, 0, 0};
-      const MmArgs gh{ntok, C, j.n, j.d, j.n, 1, j.w, 1, j.n, a->dh, C, 1, 0};
-      if (layer_gemm(dm, gw, false, true, true, w.part, s) != hipSuccess ||
-          layer_gemm(dm, gh, true, false, false, nullptr, s) != hipSuccess)
-        return NSA_ERR_HIP;
-    }
+    // [dW_q | dW_k | dW_v] = h^T [dq | dk | dv] (fp32) in one launch, split
+    // over the tokens
+    MmArgs gw{C, nq + nk + nv, ntok, a->h, 1, C, nullptr, nq, 1, nullptr, 0, 0, 0};
+    gw.nseg = 3;
+    gw.seg[0] = MmSeg{nullptr, 0, 0, w.dq, nq, 1, a->dw_q, nq, 0};
+    gw.seg[1] = MmSeg{nullptr, 0, 0, w.dk, nk, 1, a->dw_k, nk, nq};
+    gw.seg[2] = MmSeg{nullptr, 0, 0, w.dv, nv, 1, a->dw_v, nv, nq + nk};
+    // dh += [dq | dk | dv] [w_q | w_k | w_v]^T in one launch, the contraction
+    // running over the three segments (dq, dk, dv are fp32)
+    MmArgs gh{ntok, C, nq + nk + nv, nullptr, nq, 1, nullptr, 1, nq, a->dh, C, 1, 0};
+    gh.nseg = 3;
+    gh.seg_k = 1;
+    gh.seg[0] = MmSeg{w.dq, nq, 1, a->w_q, 1, nq, nullptr, 0, 0};
+    gh.seg[1] = MmSeg{w.dk, nk, 1, a->w_k, 1, nk, nullptr, 0, nq};
+    gh.seg[2] = MmSeg{w.dv, nv, 1, a->w_v, 1, nv, nullptr, 0, nq + nk};
+    if (layer_gemm_seg(dm, gw, false, true, true, w.part, s) != hipSuccess ||
+        layer_gemm_seg(dm, gh, true, false, false, nullptr, s) != hipSuccess)
+      return NSA_ERR_HIP;
     return NSA_OK;
   } catch (...) {
     return NSA_ERR_INTERNAL;

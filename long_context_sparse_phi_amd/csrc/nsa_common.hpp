@@ -271,6 +271,29 @@ __host__ __device__ __forceinline__ void gemm_tile_order(int lid, int ncol, int 
   }
 }
 
+// A GEMM whose n range is cut into nseg segments (segment s holds columns
+// [off[s], off[s + 1]), the last one ending at N), each padded to whole tiles
+// of tw columns, so that no tile spans two segments.  seg_tiles: the column
+// tile count; seg_tile: segment s of column tile nt and that tile's first
+// column inside the segment.
+__host__ __device__ __forceinline__ int seg_width(int s, int nseg, const int* off, int N) {
+  return (s + 1 < nseg ? off[s + 1] : N) - off[s];
+}
+__host__ __device__ __forceinline__ int seg_tiles(int nseg, const int* off, int N, int tw) {
+  int t = 0;
+  for (int s = 0; s < nseg; ++s) t += (seg_width(s, nseg, off, N) + tw - 1) / tw;
+  return t;
+}
+__host__ __device__ __forceinline__ void seg_tile(int nt, int nseg, const int* off, int N, int tw, int& s, int& n0) {
+  int t0 = 0;
+  for (s = 0; s + 1 < nseg; ++s) {
+    const int tc = (seg_width(s, nseg, off, N) + tw - 1) / tw;
+    if (nt < t0 + tc) break;
+    t0 += tc;
+  }
+  n0 = (nt - t0) * tw;
+}
+
 // Task (group kg, segment seg) of workgroup id, for units x ngroup x nseg
 // tasks whose query rows start at kg*span + seg*seglen (plus a constant).
 // When span is a multiple of seglen, the tasks with equal a = R*kg + seg

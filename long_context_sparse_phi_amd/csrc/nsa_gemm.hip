@@ -31,6 +31,11 @@ namespace {
 constexpr int kBM = 128, kBN = 128, kBK = 64;
 constexpr int kTileElems = 128 * kBK;          // one operand plane (bf16 elements)
 
+// Value of segment s out of three, chosen by selects rather than an indexed
+// read of the argument block.
+template <typename V>
+__device__ __forceinline__ V seg_pick(int s, V a, V b, V c) { return s == 0 ? a : (s == 1 ? b : c); }
+
 __device__ __forceinline__ int mm_off(int r, int c) { return r * kBK + ((c ^ (((r >> 1) ^ (r >> 4)) & 7)) << 3); }
 
 // Eight consecutive elements of an operand, as loaded (bf16 or fp32); the
@@ -163,19 +168,32 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs g, int kc, int nsplit, float*
   // Persistent: the workgroups of a (batch, split) plane walk its output
   // tiles with a stride of the grid width, which is a multiple of 8 when
   // the grid is smaller than the tile count (so tile lid keeps XCD lid % 8).
-  const int ncol = (g.N + kBN - 1) / kBN, nrow = (g.M + kBM - 1) / kBM;
+  // segments: n segments pick B and C per column tile, k segments pick A
+  // and B per k step (seg_pick keeps the choice in scalar registers)
+  const bool nsegs = g.nseg > 1 && !g.seg_k, ksegs = g.nseg > 1 && g.seg_k;
+  const int soff[3] = {g.seg[0].off, g.seg[1].off, g.seg[2].off};
+  const int ncol = nsegs ? seg_tiles(g.nseg, soff, g.N, kBN) : (g.N + kBN - 1) / kBN;
+  const int nrow = (g.M + kBM - 1) / kBM;
   for (int lid = blockIdx.x; lid < ncol * nrow; lid += gridDim.x) {
     int mt, nt;
     gemm_tile_order(lid, ncol, nrow, mt, nt);
-    const int m0 = mt * kBM, n0 = nt * kBN;
+    int sn = 0, n0 = nt * kBN, Nl = g.N;     // segment, first column in it, its width
+    if (nsegs) {
+      seg_tile(nt, g.nseg, soff, g.N, kBN, sn, n0);
+      Nl = seg_width(sn, g.nseg, soff, g.N);
+    }
+    const int m0 = mt * kBM;
     const int split = blockIdx.z % nsplit, bat = blockIdx.z / nsplit;
     const int kbeg = split * kc, kend = min(g.K, kbeg + kc);
     const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
     const TA* A = (const TA*)g.A + bat * g.bsa;
-    const TB* B = (const TB*)g.B + bat * g.bsb;
+    const TB* B = nsegs ? (const TB*)seg_pick(sn, g.seg[0].B, g.seg[1].B, g.seg[2].B) : (const TB*)g.B + bat * g.bsb;
     // A rows are m (stride sam) and B rows are n (stride sbn); k-contiguous
     // operands step rows by their row stride, the others step k by theirs
-    const long long as = AKC ? g.sam : g.sak, bs = BKC ? g.sbn : g.sbk;
+    const long long as = AKC ? g.sam : g.sak;
+    const long long bs = nsegs ? (BKC ? seg_pick(sn, g.seg[0].sbn, g.seg[1].sbn, g.seg[2].sbn)
+                                      : seg_pick(sn, g.seg[0].sbk, g.seg[1].sbk, g.seg[2].sbk))
+                               : (BKC ? g.sbn : g.sbk);
     Stage<TA, AKC> sa[2];
     Stage<TB, BKC> sb[2];
     f32x4 acc[4][4];
@@ -187,9 +205,25 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs g, int kc, int nsplit, float*
     const int nk = kend > kbeg ? (kend - kbeg + kBK - 1) / kBK : 0;
     auto gload = [&](auto set, int t) {
       constexpr int S = decltype(set)::value;
-      const int k0 = kbeg + t * kBK;
-      sa[S].load(A, as, m0, g.M, k0, kend, tid);
-      sb[S].load(B, bs, n0, g.N, k0, kend, tid);
+      int k0 = kbeg + t * kBK, kl = kend;
+      const TA* Ap = A;
+      const TB* Bp = B;
+      long long ap = as, bp = bs;
+      if (ksegs) {
+        // the k segment holding this step, and k relative to its start
+        const int sk = (g.nseg > 2 && k0 >= soff[2]) ? 2 : (k0 >= soff[1] ? 1 : 0);
+        const int ko = seg_pick(sk, soff[0], soff[1], soff[2]);
+        kl = min(kend, ko + seg_width(sk, g.nseg, soff, g.K)) - ko;
+        k0 -= ko;
+        Ap = (const TA*)seg_pick(sk, g.seg[0].A, g.seg[1].A, g.seg[2].A);
+        Bp = (const TB*)seg_pick(sk, g.seg[0].B, g.seg[1].B, g.seg[2].B);
+        ap = AKC ? seg_pick(sk, g.seg[0].sam, g.seg[1].sam, g.seg[2].sam)
+                 : seg_pick(sk, g.seg[0].sak, g.seg[1].sak, g.seg[2].sak);
+        bp = BKC ? seg_pick(sk, g.seg[0].sbn, g.seg[1].sbn, g.seg[2].sbn)
+                 : seg_pick(sk, g.seg[0].sbk, g.seg[1].sbk, g.seg[2].sbk);
+      }
+      sa[S].load(Ap, ap, m0, g.M, k0, kl, tid);
+      sb[S].load(Bp, bp, n0, Nl, k0, kl, tid);
     };
     auto lstore = [&](auto set) {
       constexpr int S = decltype(set)::value;
@@ -263,11 +297,16 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs g, int kc, int nsplit, float*
     __syncthreads();
     const bool to_part = part != nullptr;
     float* pz = to_part ? part + (size_t)blockIdx.z * g.M * g.N : nullptr;
-    const long long ld = to_part ? g.N : g.ldc;
+    // an n segment's columns go to its own C, or at their place in the
+    // full-width partial rows
+    void* Cs = nsegs ? seg_pick(sn, g.seg[0].C, g.seg[1].C, g.seg[2].C) : g.C;
+    const long long ldc = nsegs ? seg_pick(sn, g.seg[0].ldc, g.seg[1].ldc, g.seg[2].ldc) : g.ldc;
+    const int pcol = to_part && nsegs ? seg_pick(sn, soff[0], soff[1], soff[2]) : 0;
+    const long long ld = to_part ? g.N : ldc;
     const long long cb = to_part ? 0 : bat * g.bsc;
     const bool c16b = !to_part && g.c_bf16;
     const bool acc_c = !to_part && g.accumulate;
-    const uintptr_t cbase = to_part ? (uintptr_t)pz : (uintptr_t)g.C + (uintptr_t)cb * (c16b ? 2 : 4);
+    const uintptr_t cbase = to_part ? (uintptr_t)(pz + pcol) : (uintptr_t)Cs + (uintptr_t)cb * (c16b ? 2 : 4);
     // four-value vectors need 16-byte (fp32) or 8-byte (bf16) aligned rows
     const bool vec = ld % 4 == 0 && cbase % (c16b ? 8 : 16) == 0;
     const int col = (lane & 15) * 4;
@@ -276,19 +315,19 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs g, int kc, int nsplit, float*
     for (int it = 0; it < 16; ++it) {
       const int row = it * 4 + (lane >> 4);
       const int m = m0 + wm + row;
-      if (m >= g.M || n >= g.N) continue;
+      if (m >= g.M || n >= Nl) continue;
       const f32x4 v = *reinterpret_cast<const f32x4*>(ep + row * 68 + col);
-      const long long o = (long long)m * ld + n;
+      const long long o = (long long)m * ld + pcol + n;
       if (c16b) {
-        bf16* cp = (bf16*)g.C + cb + o;
-        if (vec && n + 4 <= g.N) {
+        bf16* cp = (bf16*)Cs + cb + o;
+        if (vec && n + 4 <= Nl) {
           store_col4(cp, (bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]);
         } else {
-          for (int e = 0; e < 4 && n + e < g.N; ++e) cp[e] = (bf16)v[e];
+          for (int e = 0; e < 4 && n + e < Nl; ++e) cp[e] = (bf16)v[e];
         }
       } else {
-        float* cp = to_part ? pz + o : (float*)g.C + cb + o;
-        if (vec && n + 4 <= g.N) {
+        float* cp = to_part ? pz + o : (float*)Cs + cb + o;
+        if (vec && n + 4 <= Nl) {
           f32x4 w = v;
           if (acc_c) {
             const f32x4 old = *reinterpret_cast<const f32x4*>(cp);
@@ -296,7 +335,7 @@ __global__ __launch_bounds__(256) void k_mm(MmArgs g, int kc, int nsplit, float*
           }
           *reinterpret_cast<f32x4*>(cp) = w;
         } else {
-          for (int e = 0; e < 4 && n + e < g.N; ++e) cp[e] = acc_c ? cp[e] + v[e] : v[e];
+          for (int e = 0; e < 4 && n + e < Nl; ++e) cp[e] = acc_c ? cp[e] + v[e] : v[e];
         }
       }
     }
@@ -314,11 +353,18 @@ __global__ __launch_bounds__(256) void k_mm_reduce(MmArgs g, int nsplit, const f
   const int m = (int)(id / g.N), n = (int)(id % g.N);
   float s = 0.f;
   for (int z = 0; z < nsplit; ++z) s += part[((size_t)bat * nsplit + z) * mn + id];
-  const long long o = bat * g.bsc + (long long)m * g.ldc + n;
+  // n segments: the column's segment and its place in that segment's C
+  int sn = 0;
+  if (g.nseg > 1 && !g.seg_k) sn = (g.nseg > 2 && n >= g.seg[2].off) ? 2 : (n >= g.seg[1].off ? 1 : 0);
+  const bool segs = g.nseg > 1 && !g.seg_k;
+  void* C = segs ? seg_pick(sn, g.seg[0].C, g.seg[1].C, g.seg[2].C) : g.C;
+  const long long ldc = segs ? seg_pick(sn, g.seg[0].ldc, g.seg[1].ldc, g.seg[2].ldc) : g.ldc;
+  const int nl = segs ? n - seg_pick(sn, g.seg[0].off, g.seg[1].off, g.seg[2].off) : n;
+  const long long o = bat * g.bsc + (long long)m * ldc + nl;
   if (g.c_bf16) {
-    ((bf16*)g.C)[o] = (bf16)s;
+    ((bf16*)C)[o] = (bf16)s;
   } else {
-    float* cp = (float*)g.C + o;
+    float* cp = (float*)C + o;
     *cp = g.accumulate ? *cp + s : s;
   }
 }
@@ -333,7 +379,9 @@ hipError_t mm_launch(const MmArgs& g, int nsplit, int kc, float* part, hipStream
   if (lds > 64 * 1024) (void)hipFuncSetAttribute((const void*)kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   // two workgroups per CU over all planes; below the tile count the width is
   // rounded down to a multiple of 8 (the XCD count)
-  const int ntile = ((g.N + kBN - 1) / kBN) * ((g.M + kBM - 1) / kBM), planes = nsplit * g.batch;
+  int soff[3] = {g.seg[0].off, g.seg[1].off, g.seg[2].off};
+  const int ncol = g.nseg > 1 && !g.seg_k ? seg_tiles(g.nseg, soff, g.N, kBN) : (g.N + kBN - 1) / kBN;
+  const int ntile = ncol * ((g.M + kBM - 1) / kBM), planes = nsplit * g.batch;
   const int cap = 512 / planes > 8 ? (512 / planes) & ~7 : 8;
   dim3 grid(ntile > cap ? cap : ntile, 1, planes);
   kfn<<<grid, 256, lds, s>>>(g, kc, nsplit, nsplit > 1 ? part : nullptr);
@@ -466,7 +514,24 @@ bool mm_supported(const MmArgs& g, bool a_f32, bool b_f32) {
   const bool akc = g.sak == 1, bkc = g.sbk == 1;
   if (!akc && g.sam != 1) return false;
   if (!bkc && g.sbn != 1) return false;
-  return aligned_elems(g.A, akc ? g.sam : g.sak, ea) && aligned_elems(g.B, bkc ? g.sbn : g.sbk, eb);
+  if (g.nseg <= 1) return aligned_elems(g.A, akc ? g.sam : g.sak, ea) && aligned_elems(g.B, bkc ? g.sbn : g.sbk, eb);
+  // segments: batch 1, increasing offsets from 0, every segment's operands in
+  // the top-level layout, k segments in whole 64-wide k steps
+  if (g.nseg > 3 || g.batch != 1 || g.seg[0].off != 0) return false;
+  const int ext = g.seg_k ? g.K : g.N;
+  for (int s = 0; s < g.nseg; ++s) {
+    const MmSeg& q = g.seg[s];
+    const int end = s + 1 < g.nseg ? g.seg[s + 1].off : ext;
+    if (end <= q.off) return false;
+    if (g.seg_k && s + 1 < g.nseg && (end - q.off) % kBK != 0) return false;
+    if ((q.sbk == 1) != bkc || (!bkc && q.sbn != 1)) return false;
+    if (!aligned_elems(q.B, bkc ? q.sbn : q.sbk, eb)) return false;
+    if (g.seg_k) {
+      if ((q.sak == 1) != akc || (!akc && q.sam != 1)) return false;
+      if (!aligned_elems(q.A, akc ? q.sam : q.sak, ea)) return false;
+    }
+  }
+  return g.seg_k || aligned_elems(g.A, akc ? g.sam : g.sak, ea);
 }
 
 hipError_t mm(const MmArgs& g, bool a_f32, bool b_f32, int nsplit, float* part, hipStream_t s) {

@@ -136,6 +136,24 @@ struct GateMlp {
 // bf16.  batch independent products, operand and result b offset by b*bsa,
 // b*bsb, b*bsc elements.  nsplit > 1 splits k, with batch * nsplit * M * N
 // floats of part.
+//
+// Segments (nseg = 2 or 3, batch 1) make one launch of several products that
+// share an operand, the projection layer's q|k|v:
+// - along n (seg_k = 0): columns [off, next off) of the product take their B
+//   and C from the segment (B(k, n') = B[k*sbk + n'*sbn], C[m*ldc + n'] with
+//   n' the column inside the segment); A is the shared operand;
+// - along k (seg_k = 1): k in [off, next off) takes A and B from the segment
+//   (k' inside the segment); every segment but the last spans a multiple of
+//   64, so no k step crosses two; C is shared.
+// Every segment's operands have the layout (which index is contiguous) of the
+// top-level fields, whose pointers are then unused.  seg[0].off is 0.  With a
+// split of k, part holds nsplit * M * N floats, N the total width.
+struct MmSeg {
+  const void* A; long long sam, sak;
+  const void* B; long long sbk, sbn;
+  void* C; long long ldc;
+  int off;
+};
 struct MmArgs {
   int M, N, K;
   const void* A; long long sam, sak;
@@ -145,6 +163,9 @@ struct MmArgs {
   int c_bf16;
   int batch = 1;
   long long bsa = 0, bsb = 0, bsc = 0;
+  int nseg = 0;
+  int seg_k = 0;
+  MmSeg seg[3] = {};
 };
 bool mm_supported(const MmArgs& g, bool a_f32, bool b_f32);
 // Exact fp32 GEMM (v_mfma_f32_16x16x4_f32, operands converted to fp32) for

@@ -26,6 +26,19 @@ PROGRAM = r"""
 int main() {
   int kind, units, ngroup, nseg, span, seglen;
   while (std::scanf("%d %d %d %d %d %d", &kind, &units, &ngroup, &nseg, &span, &seglen) == 6) {
+    if (kind == 3) {
+      // segmented GEMM columns: units = segment count, ngroup = N, nseg and
+      // span = the second and third segments' offsets, seglen = tile width
+      const int off[3] = {0, nseg, span};
+      const int nt = nsa::seg_tiles(units, off, ngroup, seglen);
+      for (int t = 0; t < nt; ++t) {
+        int s = -1, n0 = -1;
+        nsa::seg_tile(t, units, off, ngroup, seglen, s, n0);
+        std::printf("%d %d %d\n", s, n0, nsa::seg_width(s, units, off, ngroup));
+      }
+      std::printf("end\n");
+      continue;
+    }
     const int n = units * ngroup * nseg;
     for (int id = 0; id < n; ++id) {
       int u = -1, kg = -1, seg = 0;
@@ -113,3 +126,31 @@ def test_gemm_tile_order_is_a_bijection_with_rows_grouped_per_xcd(order_binary):
             xcd = {}
             for wid, (m, n, _) in enumerate(tasks):
                 assert xcd.setdefault(m, wid % 8) == wid % 8
+
+
+# (segment count, N, second offset, third offset, tile width): q|k|v widths of
+# the layer shapes and ragged ones
+SEG_CASES = [
+    (3, 9216, 8192, 8704, 128),    # train_16k: 64 x 128 | 4 x 128 | 4 x 128
+    (3, 13568, 12288, 13056, 128),  # 64 query heads x 192 | 4 x 192 | 4 x 128
+    (3, 448, 256, 384, 128),       # one KV head of 64: 64-wide segments
+    (2, 200, 72, 0, 128),
+    (3, 3, 1, 2, 128),
+    (3, 640, 128, 256, 64),
+]
+
+
+def test_segment_tiles_cover_every_column_once(order_binary):
+    text = "".join(f"3 {n} {w} {o1} {o2} {tw}\n" for n, w, o1, o2, tw in SEG_CASES)
+    out = subprocess.run([order_binary], input=text, capture_output=True, text=True, check=True).stdout
+    blocks = out.split("end\n")[:-1]
+    assert len(blocks) == len(SEG_CASES)
+    for (nsg, N, o1, o2, tw), blk in zip(SEG_CASES, blocks):
+        offs = [0, o1, o2][:nsg]
+        widths = [(offs[i + 1] if i + 1 < nsg else N) - offs[i] for i in range(nsg)]
+        tiles = [tuple(int(x) for x in line.split()) for line in blk.strip().splitlines()]
+        # segments in order, each one's tiles from its first column in steps of tw
+        expect = [(s, n0, widths[s]) for s in range(nsg) for n0 in range(0, widths[s], tw)]
+        assert tiles == expect, (nsg, N, o1, o2, tw)
+        cols = sorted(c for s, n0, w in tiles for c in range(offs[s] + n0, offs[s] + min(n0 + tw, w)))
+        assert cols == list(range(N))
