@@ -6,15 +6,15 @@
 // once, by many waves in parallel:
 //   1. k_dec_cmp: the compressed cache of each (sequence, KV group) is split
 //      into chunks of CK blocks; a wave computes the group's 16 head scores for
-//      its chunk, its partial softmax state (max m, sum l, unnormalised P V)
-//      and its per-head partial importance scores remapped onto selection
-//      blocks (same remap MFMA as the prefill).
-//   2. k_dec_combine: merges the chunks' softmax states into exact per-head
+//      its consecutive chunks, their partial softmax state (max m, sum l,
+//      unnormalised P V) and the per-head partial importance scores of each
+//      tile remapped onto selection blocks (same remap MFMA as the prefill).
+//   2. k_dec_combine: merges the waves' softmax states into exact per-head
 //      probabilities, sums the group's heads into the block scores and runs
 //      top-n.
 //   3. k_dec_sw: one selected block or one 64-token window chunk per wave,
 //      each a partial softmax state.
-//   4. k_dec_merge: evaluates the gates, merges the compressed chunks and the
+//   4. k_dec_merge: evaluates the gates, merges the compressed states and the
 //      selected and window partial states, and writes
 //      o = g_cmp O_cmp + g_slc O_slc + g_win O_win.
 // All caches are stored [key][Hkv][feature].  A wave reads each 32-key tile of
@@ -40,7 +40,7 @@ template <int DK, int DV> constexpr int dec_depth() { return DK + DV >= 320 ? 3 
 // Launch plan for the cache capacity S (grid sizes, workspace layout); every
 // sequence then works within its own length (DecSeq).
 struct DecPlan {
-  int S, t, ncmp, nc, cpw, nb, jstep, nis, niw, ni, wlen, ws0;
+  int S, t, ncmp, nc, cpw, ns, nb, jstep, nis, niw, ni, wlen, ws0;
 };
 
 static DecPlan dec_plan(const Dims& dm) {
@@ -53,6 +53,7 @@ static DecPlan dec_plan(const Dims& dm) {
   const long long chunks = (long long)dm.B * dm.Hkv * p.nc;
   p.cpw = 1;
   while (p.nc % (2 * p.cpw) == 0 && chunks / (2 * p.cpw) >= 1024) p.cpw *= 2;
+  p.ns = p.nc / p.cpw;   // softmax states per (sequence, KV head): one per wave
   p.nb = (31 * dm.d + dm.l - 1) / dm.ls + 1;
   p.jstep = 32 * dm.d / dm.ls;
   p.nis = dm.n;
@@ -64,11 +65,11 @@ static DecPlan dec_plan(const Dims& dm) {
 }
 
 struct DecBufs {
-  float* part_o;    // [B,Hkv,nc,16,dv]
-  float* part_ml;   // [B,Hkv,nc,16,2]
+  float* part_o;    // [B,Hkv,ns,16,dv] unnormalised P V of each wave's chunks
+  float* part_ml;   // [B,Hkv,ns,16,2]
   float* part_ps;   // [B,Hkv,nc,TPC,nb,16] remapped scores, relative to the tile's running max
   float* part_tm;   // [B,Hkv,nc,TPC,16] running max (log2 units) after each tile
-  float* cmp_scl;   // [B,Hkv,nc,16] exp2(m_chunk - lse) per chunk and head
+  float* cmp_scl;   // [B,Hkv,ns,16] exp2(m_wave - lse) per wave and head
   float* lse_cmp;   // [B,Hq] (log2 units)
   float* gates;     // [B,Hq,3]
   int* idx;         // [B,Hkv,n]
@@ -84,11 +85,11 @@ static size_t dec_carve(const Dims& dm, void* ws, DecBufs* b) {
   size_t off = 0;
   auto take = [&](size_t bytes) { void* r = base ? base + off : nullptr; off += al256(bytes); return r; };
   const size_t BG = (size_t)dm.B * dm.Hkv;
-  b->part_o = (float*)take(BG * p.nc * 16 * dm.dv * 4);
-  b->part_ml = (float*)take(BG * p.nc * 16 * 2 * 4);
+  b->part_o = (float*)take(BG * p.ns * 16 * dm.dv * 4);
+  b->part_ml = (float*)take(BG * p.ns * 16 * 2 * 4);
   b->part_ps = (float*)take(BG * p.nc * 16 * kDecTPC * p.nb * 4);
   b->part_tm = (float*)take(BG * p.nc * 16 * kDecTPC * 4);
-  b->cmp_scl = (float*)take(BG * (p.nc > 0 ? p.nc : 1) * 16 * 4);
+  b->cmp_scl = (float*)take(BG * (p.ns > 0 ? p.ns : 1) * 16 * 4);
   b->lse_cmp = (float*)take((size_t)dm.B * dm.Hq * 4);
   b->gates = (float*)take((size_t)dm.B * dm.Hq * 3 * 4);
   b->idx = (int*)take(BG * dm.n * 4);
@@ -244,9 +245,10 @@ struct DecTile {
 // relative to that running maximum, stored with it; the combine scales each
 // tile's scores by exp2(max - lse).  A wave takes pl.cpw consecutive chunks
 // of one (sequence, KV head); each chunk streams through the ring of register
-// tiles and its softmax state is written when its last tile is done.  The
-// chunk's per-tile block scores and reference maxima are kept in LDS and
-// written with that state, after the chunk's loads: global stores issued
+// tiles, one online softmax runs through all of them, and the wave writes its
+// softmax state once, after its last chunk.  A chunk's per-tile block scores
+// and reference maxima are kept in LDS and written after the chunk's loads
+// (one round of the ring per chunk): global stores issued
 // between the ring's loads would make the loads' completion count ambiguous,
 // and every tile would then wait for all loads in flight.
 template <typename T, int DK, int DV>
@@ -285,8 +287,7 @@ __global__ __launch_bounds__(64, 1) void k_dec_cmp(Dims dm, DecArgs a, DecPlan p
 #pragma unroll
   for (int dt = 0; dt < DV / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = kNegInf, lsum = 0.f;
-  // softmax state of chunk c (nt tiles): maximum, sum and unnormalised P V,
-  // and the tiles' block scores and maxima; then reset
+  // the tiles' block scores and maxima of chunk c (nt tiles)
   auto finish_chunk = [&](int c, int nt) {
     if (nt > 0) {
       __syncthreads();
@@ -297,21 +298,20 @@ __global__ __launch_bounds__(64, 1) void k_dec_cmp(Dims dm, DecArgs a, DecPlan p
       for (int e = lane * 4; e < nt * 16; e += 256)
         *reinterpret_cast<f32x4*>(a.w.part_tm + tb * 16 + e) = *reinterpret_cast<const f32x4*>(stm + e);
     }
+  };
+  // the softmax state of all of the wave's chunks (one online softmax runs
+  // through them): maximum, sum and unnormalised P V
+  auto finish_wave = [&]() {
     float l = lsum + xor16f(lsum, lane);
     l += xor32f(l, lane);
-    const size_t hb = ((size_t)bg * pl.nc + c) * 16 + c16;
+    const size_t hb = ((size_t)bg * pl.ns + blockIdx.x % wpb) * 16 + c16;
     if (qd == 0) {
       a.w.part_ml[hb * 2 + 0] = m;
       a.w.part_ml[hb * 2 + 1] = l;
     }
     float* op = a.w.part_o + hb * DV + qd * 4;
 #pragma unroll
-    for (int dt = 0; dt < DV / 16; ++dt) {
-      store4(op + dt * 16, oacc[dt][0], oacc[dt][1], oacc[dt][2], oacc[dt][3]);
-      oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    m = kNegInf;
-    lsum = 0.f;
+    for (int dt = 0; dt < DV / 16; ++dt) store4(op + dt * 16, oacc[dt][0], oacc[dt][1], oacc[dt][2], oacc[dt][3]);
   };
   // tile ti of the chunk starting at key kc0
   auto compute = [&](int kc0, int ti) {
@@ -396,6 +396,7 @@ __global__ __launch_bounds__(64, 1) void k_dec_cmp(Dims dm, DecArgs a, DecPlan p
     // vmcnt(0): the chunk's stores are done before the next chunk's loads
     __builtin_amdgcn_s_waitcnt(0x0F70);
   }
+  finish_wave();
 }
 
 
@@ -408,15 +409,15 @@ static __host__ __device__ int comb_row_len(const Dims& dm) {
 // Per-(tile, block offset) contributions to the block scores: [nc*TPC][nb].
 static __host__ __device__ int comb_contrib_len(const DecPlan& pl) { return (pl.nc * kDecTPC * pl.nb + 3) & ~3; }
 
-// Dynamic LDS of the combine: score row, chunk scales and states, top-n
+// Dynamic LDS of the combine: score row, wave scales and states, top-n
 // scratch, gate MLP hidden layer, tile contributions.
 static size_t comb_lds_bytes(const Dims& dm, const DecPlan& pl) {
-  return (size_t)comb_row_len(dm) * 4 + (size_t)pl.nc * 16 * 4 * 3 + 16 * 4 + (256 + 16 + 4) * 4 + (size_t)dm.Cg * 4 +
+  return (size_t)comb_row_len(dm) * 4 + (size_t)pl.ns * 16 * 4 * 3 + 16 * 4 + (256 + 16 + 4) * 4 + (size_t)dm.Cg * 4 +
          (size_t)comb_contrib_len(pl) * 4;
 }
 
 // One workgroup (1024 threads) per (sequence, KV head): per-head log-sum-exp
-// of the compressed branch, per-chunk scales, block scores, top-n and gates.
+// of the compressed branch, per-wave scales, block scores, top-n and gates.
 // Global reads are laid out so that consecutive lanes read consecutive 16-byte
 // pieces: the gate weights of the group's heads are contiguous per input row,
 // and the per-tile score partials are read as one float4 per lane.  Loads are
@@ -426,11 +427,11 @@ template <typename T>
 __global__ __launch_bounds__(1024) void k_dec_combine(Dims dm, DecArgs a, DecPlan pl) {
   extern __shared__ float smem[];
   float* row = smem;                          // [nsel] block scores
-  float* scl = row + comb_row_len(dm);        // [nc][16]
-  float* lse2 = scl + pl.nc * 16;             // [16]
-  float* mls = lse2 + 16;                     // [nc][16] chunk maxima
-  float* lsl = mls + pl.nc * 16;              // [nc][16] chunk sums
-  int* tsh = (int*)(lsl + pl.nc * 16);        // [256 + 16 + 4] top-n scratch
+  float* scl = row + comb_row_len(dm);        // [ns][16]
+  float* lse2 = scl + pl.ns * 16;             // [16]
+  float* mls = lse2 + 16;                     // [ns][16] wave maxima
+  float* lsl = mls + pl.ns * 16;              // [ns][16] wave sums
+  int* tsh = (int*)(lsl + pl.ns * 16);        // [256 + 16 + 4] top-n scratch
   float* ghid = (float*)(tsh + 256 + 16 + 4); // [Cg] gate MLP hidden layer
   float* ctb = ghid + dm.Cg;                  // [nc*TPC][nb] tile contributions
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -452,23 +453,23 @@ __global__ __launch_bounds__(1024) void k_dec_combine(Dims dm, DecArgs a, DecPla
       gw[u] = k < dm.C && lane < G3 ? wv : 0.f;
     }
   };
-  for (int i = tid; i < pl.nc * 16; i += 1024) {
-    const size_t hb = (size_t)bg * pl.nc * 16 + i;
+  for (int i = tid; i < pl.ns * 16; i += 1024) {
+    const size_t hb = (size_t)bg * pl.ns * 16 + i;
     mls[i] = a.w.part_ml[hb * 2];
     lsl[i] = a.w.part_ml[hb * 2 + 1];
   }
   if (dm.Cg == 0) gate_load(0);
   __syncthreads();
-  // per-head log-sum-exp: wave h reduces head h over the chunks
+  // per-head log-sum-exp: wave h reduces head h over the waves' states
   {
     const int h = wave;
     float M = kNegInf;
-    for (int c = lane; c < pl.nc; c += 64) M = fmaxf(M, mls[c * 16 + h]);
+    for (int c = lane; c < pl.ns; c += 64) M = fmaxf(M, mls[c * 16 + h]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     const float Mr = M == kNegInf ? 0.f : M;
     float L = 0.f;
-    for (int c = lane; c < pl.nc; c += 64) L += lsl[c * 16 + h] * fast_exp2(mls[c * 16 + h] - Mr);
+    for (int c = lane; c < pl.ns; c += 64) L += lsl[c * 16 + h] * fast_exp2(mls[c * 16 + h] - Mr);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
     if (lane == 0) {
@@ -478,11 +479,11 @@ __global__ __launch_bounds__(1024) void k_dec_combine(Dims dm, DecArgs a, DecPla
     }
   }
   __syncthreads();
-  for (int i = tid; i < pl.nc * 16; i += 1024) {
+  for (int i = tid; i < pl.ns * 16; i += 1024) {
     const float mc = mls[i], l2 = lse2[i % 16];
     const float v = (mc == kNegInf || l2 == kNegInf) ? 0.f : fast_exp2(mc - l2);
     scl[i] = v;
-    a.w.cmp_scl[(size_t)bg * pl.nc * 16 + i] = v;
+    a.w.cmp_scl[(size_t)bg * pl.ns * 16 + i] = v;
   }
   // block scores: sum over heads of exact probabilities remapped to blocks.
   // Tile kg's partial for block offset jj (block kg * jstep + jj) is 16
@@ -690,13 +691,13 @@ __global__ __launch_bounds__(64) void k_dec_sw(Dims dm, DecArgs a, DecPlan pl) {
 }
 
 // One workgroup per (sequence, KV head, pair of query heads): gates, merge of
-// the compressed chunks and of the selected/window partial states, output.
+// the compressed states and of the selected/window partial states, output.
 template <typename T, int DV>
 __global__ __launch_bounds__(256) void k_dec_merge(Dims dm, DecArgs a, DecPlan pl) {
   extern __shared__ float sm[];
   float* swscl = sm;                  // [ni][2]
-  float* cscl = swscl + pl.ni * 2;    // [nc][2]
-  float* gts = cscl + pl.nc * 2;      // [2][3]
+  float* cscl = swscl + pl.ni * 2;    // [ns][2]
+  float* gts = cscl + pl.ns * 2;      // [2][3]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hp = blockIdx.x % 8, bg = blockIdx.x / 8;
   const int b = bg / dm.Hkv, g = bg % dm.Hkv;
@@ -739,14 +740,14 @@ __global__ __launch_bounds__(256) void k_dec_merge(Dims dm, DecArgs a, DecPlan p
       }
     }
   }
-  for (int i = tid; i < pl.nc * 2; i += 256) cscl[i] = a.w.cmp_scl[((size_t)bg * pl.nc + i / 2) * 16 + h0 + i % 2];
+  for (int i = tid; i < pl.ns * 2; i += 256) cscl[i] = a.w.cmp_scl[((size_t)bg * pl.ns + i / 2) * 16 + h0 + i % 2];
   __syncthreads();
   const int hh = h0 + tid / DV, e = tid % DV;   // 2 heads x DV features (DV <= 128)
   if (tid >= 2 * DV || hh >= G) return;
   const int hl = hh - h0;
   float oc = 0.f;
 #pragma unroll 8
-  for (int c = 0; c < pl.nc; ++c) oc += a.w.part_o[(((size_t)bg * pl.nc + c) * 16 + hh) * DV + e] * cscl[c * 2 + hl];
+  for (int c = 0; c < pl.ns; ++c) oc += a.w.part_o[(((size_t)bg * pl.ns + c) * 16 + hh) * DV + e] * cscl[c * 2 + hl];
   float ob[2] = {0.f, 0.f};
 #pragma unroll 8
   for (int it = 0; it < pl.nis; ++it)
@@ -788,7 +789,7 @@ static hipError_t decode_impl(const Dims& dm, const DecArgs& a, const DecPlan& p
   if ((e = mark()) != hipSuccess) return e;
   k_dec_sw<T, DK, DV><<<BG * pl.ni, 64, 0, s>>>(dm, a, pl);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  k_dec_merge<T, DV><<<BG * 8, 256, ((size_t)pl.ni * 2 + (size_t)pl.nc * 2 + 8) * sizeof(float), s>>>(dm, a, pl);
+  k_dec_merge<T, DV><<<BG * 8, 256, ((size_t)pl.ni * 2 + (size_t)pl.ns * 2 + 8) * sizeof(float), s>>>(dm, a, pl);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return mark();
 }
@@ -797,7 +798,7 @@ static hipError_t decode_impl(const Dims& dm, const DecArgs& a, const DecPlan& p
 // combine's score row and per-tile contributions grow with the cache length).
 bool decode_fits(const Dims& dm) {
   const DecPlan pl = dec_plan(dm);
-  const size_t merge = ((size_t)pl.ni * 2 + (size_t)pl.nc * 2 + 8) * sizeof(float);
+  const size_t merge = ((size_t)pl.ni * 2 + (size_t)pl.ns * 2 + 8) * sizeof(float);
   return comb_lds_bytes(dm, pl) <= 160 * 1024 && merge <= 160 * 1024;
 }
 
