@@ -56,10 +56,12 @@ static DecPlan dec_plan(const Dims& dm) {
   p.ns = p.nc / p.cpw;   // softmax states per (sequence, KV head): one per wave
   p.nb = (31 * dm.d + dm.l - 1) / dm.ls + 1;
   p.jstep = 32 * dm.d / dm.ls;
-  p.nis = dm.n;
+  // work items of the selected/window pass: two selected blocks, or two
+  // 64-token window chunks, each
+  p.nis = (dm.n + 1) / 2;
   p.wlen = dm.w < dm.T ? dm.w : dm.T;
   p.ws0 = dm.T - p.wlen;
-  p.niw = (p.wlen + kDecWinChunk - 1) / kDecWinChunk;
+  p.niw = ((p.wlen + kDecWinChunk - 1) / kDecWinChunk + 1) / 2;
   p.ni = p.nis + p.niw;
   return p;
 }
@@ -607,21 +609,29 @@ __global__ __launch_bounds__(64) void k_dec_sw(Dims dm, DecArgs a, DecPlan pl) {
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks) qf[ks] = cv ? load_frag(qp + ks * 32) : zero_frag<T>();
   }
-  // key range of this work item: one selected block or one window chunk
+  // key ranges of this work item: two selected blocks or two window chunks
+  // (either may be empty); one online softmax runs over both
   const DecSeq sq = dec_seq(dm, a, b);
-  int r0 = 0, r1 = 0;
-  if (it < pl.nis) {
-    const int j = it < dm.n ? a.w.idx[(size_t)bg * dm.n + it] : -1;
-    if (j >= 0) { r0 = j * dm.ls; r1 = min((j + 1) * dm.ls, sq.S); }
-  } else if (it - pl.nis < sq.niw) {
-    r0 = sq.ws0 + (it - pl.nis) * kDecWinChunk;
-    r1 = min(r0 + kDecWinChunk, sq.S);
+  const bool win_item = it >= pl.nis;
+  int r0[2] = {0, 0}, r1[2] = {0, 0};
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    if (!win_item) {
+      const int slot = 2 * it + u;
+      const int j = slot < dm.n ? a.w.idx[(size_t)bg * dm.n + slot] : -1;
+      if (j >= 0) { r0[u] = j * dm.ls; r1[u] = min((j + 1) * dm.ls, sq.S); }
+    } else {
+      const int c = 2 * (it - pl.nis) + u;
+      if (c < sq.niw) { r0[u] = sq.ws0 + c * kDecWinChunk; r1[u] = min(r0[u] + kDecWinChunk, sq.S); }
+    }
   }
-  const int kt0 = r0 & ~31;
-  const int ntile = r1 > r0 ? (r1 - kt0 + 31) / 32 : 0;
+  const int kta = r0[0] & ~31, ktb = r0[1] & ~31;
+  const int nta = r1[0] > r0[0] ? (r1[0] - kta + 31) / 32 : 0;
+  const int ntile = nta + (r1[1] > r0[1] ? (r1[1] - ktb + 31) / 32 : 0);
+  // first key of tile i: the first range's tiles, then the second's
+  auto tkey = [&](int i) { return i < nta ? kta + 32 * i : ktb + 32 * (i - nta); };
   const float sc2 = dm.scale * kLog2e;
   const size_t kstride = (size_t)dm.Hkv * DK, vstride = (size_t)dm.Hkv * DV;
-  const bool win_item = it >= pl.nis;
   const T* kbase = (const T*)(win_item ? a.kwcache : a.kcache) + ((size_t)b * pl.S * dm.Hkv + g) * DK;
   const T* vbase = (const T*)(win_item ? a.vwcache : a.vcache) + ((size_t)b * pl.S * dm.Hkv + g) * DV;
   const int krow = (c16 >> 2) * 8 + (c16 & 3);
@@ -630,14 +640,15 @@ __global__ __launch_bounds__(64) void k_dec_sw(Dims dm, DecArgs a, DecPlan pl) {
 #pragma unroll
   for (int dt = 0; dt < DV / 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int i) {
-    const int kt = kt0 + 32 * i;
+    const int kt = tkey(i);
+    const int lo = i < nta ? r0[0] : r0[1], hi = i < nta ? r1[0] : r1[1];
     f32x4 s[2];
     Tile::scores(s, tile, qf, krow, qd);
     float v[8], mx = kNegInf;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int key = kt + qd * 8 + e;
-      v[e] = (key >= r0 && key < r1) ? s[e >> 2][e & 3] * sc2 : kNegInf;
+      v[e] = (key >= lo && key < hi) ? s[e >> 2][e & 3] * sc2 : kNegInf;
       mx = fmaxf(mx, v[e]);
     }
     mx = fmaxf(mx, xor16f(mx, lane));
@@ -661,18 +672,19 @@ __global__ __launch_bounds__(64) void k_dec_sw(Dims dm, DecArgs a, DecPlan pl) {
     for (int dt = 0; dt < DV / 16; ++dt) mma(oacc[dt], Tile::vfrag(tile, dt, c16, qd), pf);
   };
   // a ring of two tiles in flight (a 64-token block or aligned window chunk
-  // is two tiles, so all of it is requested up front)
+  // is two tiles: the first range is requested up front, the second while
+  // the first is computed)
   auto step = [&](Tile& cur, int i) {
     __syncthreads();
     cur.lstore(tile, lane);
     __syncthreads();
-    if (i + 2 < ntile) cur.gload(kbase, vbase, kstride, vstride, kt0 + 32 * (i + 2), sq.S, lane);
+    if (i + 2 < ntile) cur.gload(kbase, vbase, kstride, vstride, tkey(i + 2), sq.S, lane);
     compute(i);
   };
   Tile ring[2];
 #pragma unroll
   for (int r = 0; r < 2; ++r)
-    if (r < ntile) ring[r].gload(kbase, vbase, kstride, vstride, kt0 + 32 * r, sq.S, lane);
+    if (r < ntile) ring[r].gload(kbase, vbase, kstride, vstride, tkey(r), sq.S, lane);
   for (int i = 0; i < ntile; i += 2) {
 #pragma unroll
     for (int r = 0; r < 2; ++r)
