@@ -369,7 +369,7 @@ nsa_status nsa_fwd_decode(const nsa_params* p, const nsa_decode_args* a, void* w
  * (nsa_workspace_size(p, NSA_OP_FWD_DECODE, ...)) exceeds that size is
  * rejected with NSA_ERR_SCRATCH before anything is enqueued (the 64K-token
  * decode of 32 sequences x 4 KV heads x 16 query heads, d_k = 192, needs
- * about 53 MB).  Every call on one GPU shares that GPU's buffer: calls that
+ * about 32 MB).  Every call on one GPU shares that GPU's buffer: calls that
  * may overlap on one GPU (different streams, or different host threads)
  * race and must be ordered by the caller.  Nothing in the buffer needs to
  * start at any value: every value a call reads was written earlier in the
