@@ -747,6 +747,10 @@ __device__ __forceinline__ bool kv_task(const Dims& dm, const BwdArgs& a, int& b
     const int nkg = (dm.T + 63) / 64;
     int kg;
     xcd_map(blockIdx.x, BG, nkg, bg, kg);
+    // xcd_map hands out the last groups first; with a window over the whole
+    // sequence (the dense baseline) the first key groups carry the most query
+    // positions, so they go first instead
+    if (dm.w >= dm.T) kg = nkg - 1 - kg;
     k0 = kg * 64;
     klim = dm.T;
     p0 = k0;
