@@ -546,10 +546,11 @@ def _phi_bwd(kv, phi, dout, p: Params):
 # ---------------------------------------------------------------------------
 
 def layer_forward(p: Params, h, proj: Dict[str, np.ndarray], w_gate, n_heads, phi_k=None, phi_v=None,
-                  gate_mlp=None, tie_scores=None) -> Dict[str, np.ndarray]:
+                  gate_mlp=None, tie_scores=None, idx=None) -> Dict[str, np.ndarray]:
     """h [B,T,C]; proj = {w_q [C,Hq*dk], w_k [C,Hkv*dk], w_v [C,Hkv*dv],
-    w_o [Hq*dv,C]}; n_heads = (Hq, Hkv).  Returns y [B,T,C], q, k, v, o (as
-    stored) and the operator's forward result under "nsa"."""
+    w_o [Hq*dv,C]}; n_heads = (Hq, Hkv).  idx: optional fixed block indices
+    (as in forward).  Returns y [B,T,C], q, k, v, o (as stored) and the
+    operator's forward result under "nsa"."""
     B, T, C = h.shape
     Hq, Hkv = n_heads
     dk = proj["w_q"].shape[1] // Hq
@@ -557,7 +558,7 @@ def layer_forward(p: Params, h, proj: Dict[str, np.ndarray], w_gate, n_heads, ph
     q = round_io(h @ proj["w_q"], p.io).reshape(B, T, Hq, dk)
     k = round_io(h @ proj["w_k"], p.io).reshape(B, T, Hkv, dk)
     v = round_io(h @ proj["w_v"], p.io).reshape(B, T, Hkv, dv)
-    f = forward(p, q, k, v, h, w_gate, phi_k, phi_v, tie_scores=tie_scores, gate_mlp=gate_mlp)
+    f = forward(p, q, k, v, h, w_gate, phi_k, phi_v, idx=idx, tie_scores=tie_scores, gate_mlp=gate_mlp)
     o = round_io(f["o"], p.io)
     y = round_io(o.reshape(B, T, Hq * dv) @ proj["w_o"], p.io)
     return {"y": y, "q": q, "k": k, "v": v, "o": o, "nsa": f}
@@ -567,9 +568,10 @@ def layer_backward(p: Params, h, proj: Dict[str, np.ndarray], w_gate, n_heads, p
                    gate_mlp=None) -> Dict[str, object]:
     """Gradients of L = sum(dy * y) with the block indices idx fixed: dh,
     dw_q, dw_k, dw_v, dw_o, and the operator's own (dw_gate, dgate_mlp,
-    dphi_k, dphi_v)."""
+    dphi_k, dphi_v).  The forward that gives o for dw_o runs with the same
+    fixed idx, the selection the whole backward holds fixed."""
     B, T, C = h.shape
-    f = layer_forward(p, h, proj, w_gate, n_heads, phi_k, phi_v, gate_mlp)
+    f = layer_forward(p, h, proj, w_gate, n_heads, phi_k, phi_v, gate_mlp, idx=idx)
     Hq = n_heads[0]
     dv = proj["w_o"].shape[0] // Hq
     o2 = f["o"].reshape(B * T, -1)

@@ -19,6 +19,10 @@ CASES = {
     "mlp_d128": W("train_16k", B=1, T=600, H_kv=2, G=4, n=6, w=128, bias_std=0.02),
     "mean_fp32_gate_mlp": W("tiny_fp32", mode="train", B=2, T=300, gate_hidden=64),
     "mlp_d192_g16_gate_mlp": W("prefill_64k", mode="train", T=400, H_kv=1, n=5, w=100, gate_hidden=128),
+    # 1100 tokens: the q|k|v weight gradients' launch splits its token sum in
+    # two (a ragged second part), so the split partials of the three segments
+    # are summed into their own dW
+    "mlp_d128_split_k": W("train_16k", B=1, T=1100, H_kv=2, G=4, n=6, w=128, bias_std=0.02),
 }
 
 
