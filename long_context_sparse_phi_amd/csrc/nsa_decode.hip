@@ -194,21 +194,28 @@ struct DecTile {
   static __device__ __forceinline__ int krow(int c, int lane) { return (c & 3) * 8 + (lane >> 3); }
   static __device__ __forceinline__ int kchunk(int c, int lane) { return (c >> 2) * 8 + (lane & 7); }
 
-  // rows past klim - 1 (the tail of the last tile) read row klim - 1
+  // rows past klim - 1 (the tail of the last tile) read row klim - 1.  NT:
+  // non-temporal loads, for data read once (the compressed cache streams
+  // through once per step; the selected blocks and window chunks overlap)
+  template <bool NT = false>
   __device__ __forceinline__ void gload(const T* kbase, const T* vbase, size_t kstride, size_t vstride, int key0,
                                         int klim, int lane) {
+    auto ld = [](const T* p) {
+      if constexpr (NT) return load_frag_nt(p);
+      else return load_frag(p);
+    };
     const T* kt = kbase + (size_t)key0 * kstride;
     const T* vt = vbase + (size_t)key0 * vstride;
     const int rmax = klim - 1 - key0;
 #pragma unroll
     for (int c = 0; c < KCH; ++c)
-      kr[c] = load_frag(kt + __umul24((unsigned)min(krow(c, lane), rmax), (unsigned)kstride) + kchunk(c, lane) * 8);
+      kr[c] = ld(kt + __umul24((unsigned)min(krow(c, lane), rmax), (unsigned)kstride) + kchunk(c, lane) * 8);
 #pragma unroll
     for (int c = 0; c < VTK; ++c) {
       const int u = lane + 64 * c, c8 = (u & 3) + 4 * (u >> 5), rq = (u >> 2) & 7;
 #pragma unroll
       for (int k = 0; k < 4; ++k)
-        vr[c][k] = load_frag(vt + __umul24((unsigned)min(4 * rq + k, rmax), (unsigned)vstride) + c8 * 8);
+        vr[c][k] = ld(vt + __umul24((unsigned)min(4 * rq + k, rmax), (unsigned)vstride) + c8 * 8);
     }
   }
   __device__ __forceinline__ void lstore(T* tile, int lane) {
@@ -366,9 +373,10 @@ __global__ __launch_bounds__(64, 1) void k_dec_cmp(Dims dm, DecArgs a, DecPlan p
   // Each chunk streams through a ring of DEPTH register tiles, computed from
   // LDS one at a time (one wave per SIMD, most of its registers hold loads).
   // Every full round of DEPTH tiles issues DEPTH tiles' loads (past the
-  // chunk's last tile they re-read it, which the L2 serves), so the wait for
-  // a tile covers that tile's loads only; the chunk's global stores follow
-  // its ring and are complete before the next chunk's loads are issued.
+  // chunk's last tile they re-read it), so the wait for a tile covers that
+  // tile's loads only; the chunk's global stores follow its ring and are
+  // complete before the next chunk's loads are issued.  The cache is read
+  // once per step, with non-temporal loads.
   constexpr int DEPTH = dec_depth<DK, DV>();
   Tile ring[DEPTH];
   for (int cc = 0; cc < pl.cpw; ++cc) {
@@ -380,11 +388,11 @@ __global__ __launch_bounds__(64, 1) void k_dec_cmp(Dims dm, DecArgs a, DecPlan p
         __syncthreads();
         cur.lstore(tile, lane);
         __syncthreads();
-        if (refill) cur.gload(kbase, vbase, kstride, vstride, tkey(ti + DEPTH), ncmp, lane);
+        if (refill) cur.template gload<true>(kbase, vbase, kstride, vstride, tkey(ti + DEPTH), ncmp, lane);
         compute(kc0, ti);
       };
 #pragma unroll
-      for (int r = 0; r < DEPTH; ++r) ring[r].gload(kbase, vbase, kstride, vstride, tkey(r), ncmp, lane);
+      for (int r = 0; r < DEPTH; ++r) ring[r].template gload<true>(kbase, vbase, kstride, vstride, tkey(r), ncmp, lane);
       int i0 = 0;
       for (; i0 + DEPTH <= nt; i0 += DEPTH) {
 #pragma unroll
