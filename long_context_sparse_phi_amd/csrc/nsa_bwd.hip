@@ -1264,23 +1264,52 @@ __global__ __launch_bounds__(64) void k_rev_fill(Dims dm, BwdArgs a) {
 // 64x64 output tile per workgroup, k steps of 32 staged through LDS.
 // ---------------------------------------------------------------------------
 // Column sums out[c] = sum_r in[r*ld + c] in two stages with a fixed order:
-// row split z sums rows z, z + nsplit, ...; then the splits are added in order.
+// row split z sums rows z, z + nsplit, ...; then the splits are added in
+// order.  Each stage keeps eight running sums (rows 8 apart in its sequence,
+// so that eight loads are in flight), added pairwise at the end.
+__device__ __forceinline__ float sum8(const float (&acc)[8]) {
+  return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+}
+
 __global__ __launch_bounds__(256) void k_colsum_part(int R, int Cn, long long ld, int nsplit,
                                                      const float* __restrict__ in, float* __restrict__ part) {
   const int c = blockIdx.x * 256 + threadIdx.x, z = blockIdx.y;
   if (c >= Cn) return;
-  float s = 0.f;
-  for (int r = z; r < R; r += nsplit) s += in[(long long)r * ld + c];
-  part[(size_t)z * Cn + c] = s;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int r = z;
+  for (; r + 7 * nsplit < R; r += 8 * nsplit) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] += in[(long long)(r + u * nsplit) * ld + c];
+  }
+  for (; r < R; r += nsplit) acc[0] += in[(long long)r * ld + c];
+  part[(size_t)z * Cn + c] = sum8(acc);
 }
 
 __global__ __launch_bounds__(256) void k_colsum_fin(int Cn, int nsplit, const float* __restrict__ part,
                                                     float* __restrict__ out) {
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= Cn) return;
-  float s = 0.f;
-  for (int z = 0; z < nsplit; ++z) s += part[(size_t)z * Cn + c];
-  out[c] = s;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int z = 0;
+  for (; z + 8 <= nsplit; z += 8) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] += part[(size_t)(z + u) * Cn + c];
+  }
+  for (; z < nsplit; ++z) acc[0] += part[(size_t)z * Cn + c];
+  out[c] = sum8(acc);
+}
+
+// A reduction GEMM of the backward: with bf16 I/O the library's bf16 MFMA
+// GEMM (fp32 operands as bf16 hi + lo parts, fp32 accumulation; split over
+// k when `split`, at most kMaxSplit ways), when the operand layouts suit it;
+// otherwise, and with fp32 I/O, the exact fp32 GEMM.
+template <typename T>
+static hipError_t bwd_gemm(const Gemm& g, bool a_f32, bool b_f32, bool split, float* part, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    const MmArgs m{g.M, g.N, g.K, g.A, g.sam, g.sak, g.B, g.sbk, g.sbn, g.C, g.ldc, g.accumulate, 0};
+    if (mm_supported(m, a_f32, b_f32)) return mm(m, a_f32, b_f32, split ? mm_split(m, kMaxSplit) : 1, part, s);
+  }
+  return gemm_exact(g, a_f32, b_f32, split ? part : nullptr, s);
 }
 
 static hipError_t colsum(int R, int Cn, long long ld, const float* in, float* out, float* part, hipStream_t s) {
@@ -1427,12 +1456,12 @@ static hipError_t phi_bwd(const Dims& dm, const BwdArgs& a, const nsa_phi_weight
   if ((e = colsum((int)rows, D, D, dcmp, (float*)gr.b2, a.w.gpart, s)) != hipSuccess) return e;
   {
     Gemm g{H, D, (int)rows, a.w.hid, 1, H, dcmp, D, 1, (float*)gr.w2, D, 0};
-    if ((e = gemm_exact(g, true, true, a.w.gpart, s)) != hipSuccess) return e;
+    if ((e = bwd_gemm<T>(g, true, true, true, a.w.gpart, s)) != hipSuccess) return e;
   }
   // dh = dout W2^T; da = dh * gelu'(act)
   {
     Gemm g{(int)rows, H, D, dcmp, D, 1, w.w2, 1, D, a.w.dh, H, 0};
-    if ((e = gemm_exact(g, true, sizeof(T) == 4, nullptr, s)) != hipSuccess) return e;
+    if ((e = bwd_gemm<T>(g, true, sizeof(T) == 4, false, nullptr, s)) != hipSuccess) return e;
   }
   const size_t Mmain = (size_t)dm.B * dm.Hkv * nsub, rows_p = Mmain + R - 1;
   k_phi_da<<<(unsigned)((rows_p * H + 255) / 256), 256, 0, s>>>(dm, nsub, a.w.act, a.w.dh, a.w.dap);
@@ -1608,7 +1637,7 @@ static hipError_t bwd_impl(const Dims& dm, const nsa_bwd_args* args, BwdArgs& a,
     if (dm.Cg == 0) {
       // dW_g = x^T dz; dx = dz W_g^T
       Gemm g{dm.C, HO, ntok, a.x, 1, dm.C, a.w.dz, HO, 1, a.dwg, HO, 0};
-      if ((e = gemm_exact(g, sizeof(T) == 4, true, a.w.gpart, s)) != hipSuccess) return e;
+      if ((e = bwd_gemm<T>(g, sizeof(T) == 4, true, true, a.w.gpart, s)) != hipSuccess) return e;
       if (dx) {
         Gemm gx{ntok, dm.C, HO, a.w.dz, HO, 1, a.wg, 1, HO, dx, dm.C, 0};
         if ((e = gemm_exact(gx, true, sizeof(T) == 4, nullptr, s)) != hipSuccess) return e;
